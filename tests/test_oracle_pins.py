@@ -1,0 +1,292 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: the pages' printed worked
+example, an invariant the pages state, a closed form, brute force on tiny
+inputs, central finite differences, or an independent library routine.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from lora_inputs import bf16_bits_of, gen_linear, gen_mlp, to_bf16_values
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def _lin(T=5, k=7, n=6, r=3, seed=1, b_std=0.5):
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((T, k))
+    W = g.standard_normal((n, k)) * 0.3
+    A = g.uniform(-1, 1, (r, k))
+    B = g.standard_normal((n, r)) * b_std
+    dY = g.standard_normal((T, n))
+    return X, W, A, B, dY
+
+
+def _mlp(T=3, d=4, f=6, r=2, seed=2):
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((T, d))
+    shp = {"gate": (f, d), "up": (f, d), "down": (d, f)}
+    W = {k: g.standard_normal(v) * 0.4 for k, v in shp.items()}
+    A = {k: g.uniform(-1, 1, (r, v[1])) for k, v in shp.items()}
+    B = {k: g.standard_normal((v[0], r)) * 0.5 for k, v in shp.items()}
+    dY = g.standard_normal((T, d))
+    return X, W, A, B, dY
+
+
+# ----------------------------------------------------------------- printed
+def test_trainable_params_printed_example():
+    fx = json.load(open(os.path.join(GOLDEN, "trainable_params.json")))
+    n, k, r = fx["n"], fx["k"], fx["r"]
+    assert n * k == fx["full_params"]
+    assert oracle.trainable_params(n, k, r) == fx["lora_params"]
+    assert (n * k) // oracle.trainable_params(n, k, r) == fx["reduction"]
+    # and it is the element count of the adapter tensors the layer holds
+    A = np.zeros((r, k)); B = np.zeros((n, r))
+    assert A.size + B.size == fx["lora_params"]
+
+
+def test_scaling_is_alpha_over_rank():
+    assert oracle.scaling(16.0, 8) == 2.0
+    assert oracle.scaling(16.0, 16) == 1.0
+    assert oracle.scaling(16.0, 64) == 0.25
+
+
+# -------------------------------------------------------------- invariants
+def test_B_zero_gives_base_layer_exactly():
+    X, W, A, B, dY = _lin()
+    B0 = np.zeros_like(B)
+    s = 2.0
+    Y = oracle.linear_fwd(X, W, A, B0, s)
+    assert np.array_equal(Y, X @ W.T)
+    dX, dA, dB = oracle.linear_bwd(X, W, A, B0, s, dY)
+    assert np.array_equal(dA, np.zeros_like(A))
+    assert np.array_equal(dX, dY @ W)
+    assert np.abs(dB).max() > 0     # dB is nonzero even at B = 0
+
+
+def test_merged_weight_equals_unmerged():
+    for (T, k, n, r) in [(5, 7, 6, 3), (9, 16, 24, 4), (4, 8, 8, 8)]:
+        X, W, A, B, _ = _lin(T, k, n, r, seed=T + k)
+        s = 0.75
+        Y = oracle.linear_fwd(X, W, A, B, s)
+        Wm = W + s * np.einsum("nq,qk->nk", B, A)
+        Ym = X @ Wm.T
+        assert oracle.rel_fro(Y, Ym) < 1e-13
+        assert oracle.rel_fro(oracle.merged_weight(W, A, B, s), Wm) < 1e-15
+
+
+def test_forward_brute_force_loops():
+    X, W, A, B, _ = _lin(T=3, k=4, n=5, r=2, seed=7)
+    s = 1.5
+    Y = oracle.linear_fwd(X, W, A, B, s)
+    for t in range(3):
+        for j in range(5):
+            base = sum(X[t, i] * W[j, i] for i in range(4))
+            lora = 0.0
+            for q in range(2):
+                lora += B[j, q] * sum(A[q, i] * X[t, i] for i in range(4))
+            assert abs(Y[t, j] - (base + s * lora)) < 1e-12
+
+
+def test_identity_adapter_reduces_to_plain_gemm():
+    # r = k and A = I: X A^T B^T = X B^T, so Y = X (W + s B)^T, a plain GEMM
+    g = np.random.default_rng(3)
+    T, k, n = 6, 5, 4
+    X = g.standard_normal((T, k)); W = g.standard_normal((n, k))
+    B = g.standard_normal((n, k))
+    Y = oracle.linear_fwd(X, W, np.eye(k), B, 0.5)
+    ref = np.array([[sum(X[t, i] * (W[j, i] + 0.5 * B[j, i]) for i in range(k))
+                     for j in range(n)] for t in range(T)])
+    assert np.abs(Y - ref).max() < 1e-12
+
+
+def test_linearity_in_x_and_in_s():
+    X, W, A, B, _ = _lin()
+    Y = oracle.linear_fwd(X, W, A, B, 1.0)
+    assert np.array_equal(oracle.linear_fwd(2 * X, W, A, B, 1.0), 2 * Y)
+    Y0 = oracle.linear_fwd(X, W, A, B, 0.0)
+    Y1 = oracle.linear_fwd(X, W, A, B, 1.0)
+    Y3 = oracle.linear_fwd(X, W, A, B, 3.0)
+    assert np.abs((Y3 - Y0) - 3 * (Y1 - Y0)).max() < 1e-12
+
+
+# ------------------------------------------------------ finite differences
+def _fd(fun, arr, h=1e-6):
+    grad = np.zeros_like(arr)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        old = arr[idx]
+        arr[idx] = old + h; fp = fun()
+        arr[idx] = old - h; fm = fun()
+        arr[idx] = old
+        grad[idx] = (fp - fm) / (2 * h)
+    return grad
+
+
+def test_linear_gradients_finite_differences():
+    X, W, A, B, dY = _lin(T=4, k=6, n=5, r=2, seed=11)
+    s = 2.0
+    loss = lambda: float(np.sum(dY * oracle.linear_fwd(X, W, A, B, s)))
+    dX, dA, dB = oracle.linear_bwd(X, W, A, B, s, dY)
+    for name, arr, got in (("X", X, dX), ("A", A, dA), ("B", B, dB)):
+        fd = _fd(loss, arr)
+        assert oracle.rel_fro(got, fd) < 1e-7, name
+
+
+def test_mlp_gradients_finite_differences():
+    X, W, A, B, dY = _mlp(T=3, d=4, f=6, r=2, seed=5)
+    s = 0.5
+    loss = lambda: float(np.sum(dY * oracle.mlp_fwd(X, W, A, B, s)[0]))
+    got = oracle.mlp_bwd(X, W, A, B, s, dY)
+    assert oracle.rel_fro(got["dX"], _fd(loss, X)) < 1e-7
+    for p in ("gate", "up", "down"):
+        assert oracle.rel_fro(got["dA_" + p], _fd(loss, A[p])) < 1e-7, p
+        assert oracle.rel_fro(got["dB_" + p], _fd(loss, B[p])) < 1e-7, p
+
+
+def test_mlp_against_torch_autograd_float64():
+    torch = pytest.importorskip("torch")
+    X, W, A, B, dY = _mlp(T=17, d=24, f=40, r=3, seed=9)
+    s = 0.25
+    tX = torch.tensor(X, requires_grad=True)
+    tA = {k: torch.tensor(v, requires_grad=True) for k, v in A.items()}
+    tB = {k: torch.tensor(v, requires_grad=True) for k, v in B.items()}
+    tW = {k: torch.tensor(v) for k, v in W.items()}
+
+    def lin(x, p):
+        return torch.nn.functional.linear(x, tW[p]) + s * torch.nn.functional.linear(
+            torch.nn.functional.linear(x, tA[p]), tB[p])
+    e, g = lin(tX, "gate"), lin(tX, "up")
+    Y = lin(torch.nn.functional.silu(e) * g, "down")
+    Y.backward(torch.tensor(dY))
+    ref_Y, ref_e, ref_g = oracle.mlp_fwd(X, W, A, B, s)
+    assert oracle.rel_fro(ref_Y, Y.detach().numpy()) < 1e-13
+    assert oracle.rel_fro(ref_e, e.detach().numpy()) < 1e-13
+    got = oracle.mlp_bwd(X, W, A, B, s, dY)
+    assert oracle.rel_fro(got["dX"], tX.grad.numpy()) < 1e-12
+    for p in ("gate", "up", "down"):
+        assert oracle.rel_fro(got["dA_" + p], tA[p].grad.numpy()) < 1e-12
+        assert oracle.rel_fro(got["dB_" + p], tB[p].grad.numpy()) < 1e-12
+
+
+def test_linear_against_torch_autograd_float64():
+    torch = pytest.importorskip("torch")
+    X, W, A, B, dY = _lin(T=33, k=20, n=12, r=5, seed=4)
+    s = 2.0
+    tX, tA, tB = (torch.tensor(v, requires_grad=True) for v in (X, A, B))
+    Y = tX @ torch.tensor(W).T + s * (tX @ tA.T) @ tB.T
+    Y.backward(torch.tensor(dY))
+    dX, dA, dB = oracle.linear_bwd(X, W, A, B, s, dY)
+    assert oracle.rel_fro(dX, tX.grad.numpy()) < 1e-13
+    assert oracle.rel_fro(dA, tA.grad.numpy()) < 1e-13
+    assert oracle.rel_fro(dB, tB.grad.numpy()) < 1e-13
+
+
+# ------------------------------------------------------------- silu / swiglu
+def test_silu_closed_forms():
+    from scipy.special import expit
+    z = np.linspace(-30, 30, 2001)
+    assert np.abs(oracle.sigmoid(z) - expit(z)).max() < 1e-15
+    assert oracle.swiglu(np.array([0.0]), np.array([3.0]))[0] == 0.0
+    assert oracle.sigmoid(np.array([0.0]))[0] == 0.5
+    # silu'(0) = 1/2: with g = 1 and dh = 1, de = silu'(e)
+    de, dg = oracle.swiglu_bwd(np.array([0.0]), np.array([1.0]), np.array([1.0]))
+    assert de[0] == 0.5 and dg[0] == 0.0
+    big = np.array([50.0])
+    assert abs(oracle.swiglu(big, np.array([1.0]))[0] - 50.0) < 1e-12
+    assert abs(oracle.swiglu(-big, np.array([1.0]))[0]) < 1e-18
+    # huge negative gate: no inf * 0
+    de, dg = oracle.swiglu_bwd(np.array([-1e4]), np.array([2.0]), np.array([1.0]))
+    assert de[0] == 0.0 and np.isfinite(dg[0])
+
+
+def test_swiglu_derivative_finite_differences():
+    e = np.linspace(-6, 6, 61); g = np.cos(e) + 1.5; h = 1e-6
+    de, dg = oracle.swiglu_bwd(e, g, np.ones_like(e))
+    fd_e = (oracle.swiglu(e + h, g) - oracle.swiglu(e - h, g)) / (2 * h)
+    fd_g = (oracle.swiglu(e, g + h) - oracle.swiglu(e, g - h)) / (2 * h)
+    assert np.abs(de - fd_e).max() < 1e-8
+    assert np.abs(dg - fd_g).max() < 1e-8
+
+
+# -------------------------------------------------------------- bf16 / 4-bit
+def test_bf16_rne_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = (rng.standard_normal(1_000_000) * np.exp(rng.uniform(-20, 20, 1_000_000))).astype(np.float32)
+    # exact ties: low 16 bits == 0x8000, with both parities of bit 16
+    ties = (rng.integers(0, 2**31, 20000, dtype=np.uint32) & 0xFFFF0000) | 0x8000
+    extra = np.array([0.0, -0.0, np.inf, -np.inf, np.finfo(np.float32).max,
+                      -np.finfo(np.float32).max, 1e-40, -1e-40], dtype=np.float32)
+    x = np.concatenate([x, ties.view(np.float32), extra])
+    x = x[~np.isnan(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_rne_bits(x), ref)
+
+
+def test_bf16_rne_hand_cases():
+    f = lambda v: int(oracle.bf16_rne_bits(np.array([v], dtype=np.float32))[0])
+    assert f(1.0) == 0x3F80
+    assert f(1.0 + 2**-8) == 0x3F80            # tie, 1.0 is even
+    assert f(1.0 + 3 * 2**-8) == 0x3F82        # tie between 0x3F81 and 0x3F82
+    assert f(1.0 + 2**-8 + 2**-20) == 0x3F81   # above the tie
+    assert f(-2.0) == 0xC000
+
+
+def test_q4_decode_hand_fixture():
+    # codebook entries chosen so that every product below is worked out by hand
+    cb = np.array([-1.0, -0.5, -0.25, 0.0, 0.25, 0.5, 1.0, 1 + 2**-8, 1 + 3 * 2**-8,
+                   0.75, -0.75, 0.125, -0.125, 0.375, -0.375,
+                   float.fromhex("0x1.00fffep+0")], dtype=np.float32)
+    n, k = 2, 128
+    codes = np.full((n, k), 3, dtype=np.uint8)       # level 0.0 everywhere
+    absmax = np.array([2.0, 1.0, 0.5, float.fromhex("0x1.000002p+0")], dtype=np.float32)
+    codes[0, 0:4] = [6, 0, 3, 4]       # 1*2, -1*2, 0*2, 0.25*2
+    codes[0, 64:70] = [7, 8, 9, 10, 11, 1]
+    codes[1, 0:2] = [12, 13]           # row 1 block 0 uses absmax 0.5
+    codes[1, 64] = 15                  # double-rounding case
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    # nibble order: element 2j is the low nibble of byte j
+    assert packed[0, 0] == 0x06 and packed[0, 1] == 0x43 and packed[0, 32] == 0x87
+    bits = oracle.decode_q4_bits(packed, absmax, cb, n, k)
+    assert bits.dtype == np.uint16
+    assert list(bits[0, 0:4]) == [0x4000, 0xC000, 0x0000, 0x3F00]
+    # 1+2^-8 (tie -> even 0x3F80); 1+3*2^-8 (tie -> even 0x3F82); 0.75; -0.75; 0.125; -0.5
+    assert list(bits[0, 64:70]) == [0x3F80, 0x3F82, 0x3F40, 0xBF40, 0x3E00, 0xBF00]
+    assert list(bits[1, 0:2]) == [0xBD80, 0x3E40]    # -0.0625, 0.1875
+    # (1+2^-8-2^-23)*(1+2^-23) = 1+2^-8+2^-31-2^-46: the float32 product rounds
+    # onto the bf16 tie 1+2^-8, which then rounds to even 0x3F80 (a single
+    # rounding of the exact product would give 0x3F81)
+    assert bits[1, 64] == 0x3F80
+    # zero level decodes to +0, never -0
+    assert bits[0, 2] == 0 and bits[0, 100] == 0
+    vals = oracle.decode_q4(packed, absmax, cb, n, k)
+    assert vals[0, 0] == 2.0 and vals[1, 1] == 0.1875
+
+
+def test_q4_extremes_decode_to_absmax():
+    cb = np.linspace(-1, 1, 16).astype(np.float32)
+    g = np.random.default_rng(8)
+    am = np.abs(g.standard_normal(4).astype(np.float32))
+    codes = np.zeros((1, 256), np.uint8); codes[0, 1::2] = 15
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    bits = oracle.decode_q4_bits(packed, am, cb, 1, 256)
+    exp_neg = bf16_bits_of(to_bf16_values(-np.repeat(am, 64)))
+    exp_pos = bf16_bits_of(to_bf16_values(np.repeat(am, 64)))
+    assert np.array_equal(bits[0, 0::2], exp_neg[0::2])
+    assert np.array_equal(bits[0, 1::2], exp_pos[1::2])
+
+
+def test_config_inputs_roundtrip_through_oracle_shapes():
+    li = gen_linear(16, 64, 32, 4, 16.0, "bf16")
+    Y = oracle.linear_fwd(li.X, li.W, li.A, li.B, oracle.scaling(li.alpha, li.r))
+    assert Y.shape == (16, 32) and np.isfinite(Y).all()
+    mi = gen_mlp(8, 64, 128, 4, 16.0, "bf16")
+    Y, e, g = oracle.mlp_fwd(mi.X, mi.W, mi.A, mi.B, 4.0)
+    assert Y.shape == (8, 64) and e.shape == (8, 128)
