@@ -1,0 +1,200 @@
+"""Throughput of the LoRA-SwiGLU MLP forward + hand-derived backward on one GPU.
+
+One step = lora_swiglu_mlp_fwd + lora_swiglu_mlp_bwd (with dX) over one batch
+of synthetic, seeded inputs already resident in HBM; default workload is the
+Llama-3-8B MLP shape (T = 4 x 2048 tokens, d = 4096, f = 14336, LoRA r = 16,
+alpha = 16 on gate, up and down; bf16 storage, fp32 accumulation).
+
+Prints ONE JSON line.  `value` is algorithmic TFLOP/s
+(12 T d f + 18 T r (d + f) FLOP per step); tokens/s and percent of the
+MI355X bf16 dense MFMA peak ride along.  The roofline object describes the
+slowest GEMM of the step, timed with HIP events recorded by the library on
+its own launch stream around every launch of that kernel in the timed
+region.  cpu_baseline runs the float64 CPU oracle on a bounded sample of the
+same workload (fewer tokens).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=(2, 3, 5))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    return ap.parse_args()
+
+
+def mlp_flops(T, d, f, r):
+    # fwd: 3 x (2 T k n + 2 T r (k + n)); bwd: 3 x (2 T n k + 4 T r (n + k))
+    return 12 * T * d * f + 18 * T * r * (d + f)
+
+
+def gemm_flops(kc, T, d, f, r):
+    """Algorithmic FLOPs of one launch of each timed GEMM class."""
+    import lora_linear_fwd_amd as L
+    if kc == L.KC_GATEUP_FWD:     # two LoRA linears d -> f
+        return 2 * (2 * T * d * f + 2 * T * r * (d + f))
+    if kc == L.KC_DOWN_FWD:       # one LoRA linear f -> d
+        return 2 * T * f * d + 2 * T * r * (d + f)
+    if kc == L.KC_DOWN_BWD:       # dh = dY Wd + s (dY Bd) Ad
+        return 2 * T * d * f + 2 * T * r * (d + f)
+    if kc == L.KC_GATEUP_BWD:     # dX = de Wg + dg Wu + LoRA terms
+        return 2 * (2 * T * f * d + 2 * T * r * (d + f))
+    raise ValueError(kc)
+
+
+def cpu_baseline(cfg, tokens, mi):
+    """The float64 CPU oracle on the first `tokens` tokens of the same
+    workload (same weights)."""
+    import numpy as np
+    import oracle
+    from lora_inputs import CONFIGS
+    c = CONFIGS[cfg]
+    W = dict(mi.W)
+    if mi.q4:
+        W = {p: oracle.decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k) for p, q in mi.q4.items()}
+    s = oracle.scaling(mi.alpha, mi.r)
+    X, dY = mi.X[:tokens].astype(np.float64), mi.dY[:tokens].astype(np.float64)
+    Wf = {p: np.asarray(v, np.float64) for p, v in W.items()}
+    Af = {p: np.asarray(v, np.float64) for p, v in mi.A.items()}
+    Bf = {p: np.asarray(v, np.float64) for p, v in mi.B.items()}
+    oracle.mlp_fwd(X, Wf, Af, Bf, s)                      # warm-up
+    t0 = time.perf_counter()
+    oracle.mlp_fwd(X, Wf, Af, Bf, s)
+    oracle.mlp_bwd(X, Wf, Af, Bf, s, dY)
+    dt = time.perf_counter() - t0
+    fl = mlp_flops(tokens, c["d"], c["f"], c["r"])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 NumPy oracle, MLP fwd+bwd on {tokens} of {c['T']} tokens "
+                      f"(d={c['d']}, f={c['f']}, r={c['r']}), 1 timed rep after 1 warm-up, "
+                      f"{dt:.2f} s", "tokens_per_s": tokens / dt, "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import lora_linear_fwd_amd as L
+    from lora_inputs import CONFIGS, gen_config
+
+    c = CONFIGS[args.config]
+    T, d, f, r, alpha = c["T"], c["d"], c["f"], c["r"], c["alpha"]
+    q4 = c.get("q4", False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mi = gen_config(args.config)
+    up = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    if q4:
+        W = {p: L.to_device_q4(mi.q4[p]) for p in mi.q4}
+    else:
+        W = {p: up(mi.W[p]) for p in mi.W}
+    A = {p: up(mi.A[p]) for p in mi.A}
+    B = {p: up(mi.B[p]) for p in mi.B}
+    X, dY = up(mi.X), up(mi.dY)
+    Y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    e = torch.empty((T, f), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((T, f), dtype=torch.bfloat16, device=dev)
+    out = {"dX": torch.empty((T, d), dtype=torch.bfloat16, device=dev)}
+    for p in ("gate", "up", "down"):
+        out["dA_" + p] = torch.empty_like(A[p])
+        out["dB_" + p] = torch.empty_like(B[p])
+    ws_bytes = max(L.workspace_bytes(L.OP_MLP_FWD, L.LORA_BF16, int(q4), T, d, f, r),
+                   L.workspace_bytes(L.OP_MLP_BWD, L.LORA_BF16, int(q4), T, d, f, r))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.lora_swiglu_mlp_fwd(X, W, A, B, alpha, Y=Y, e=e, g=g, workspace=ws, stream=stream)
+        L.lora_swiglu_mlp_bwd(X, W, A, B, alpha, e, g, dY, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    kcs = [L.KC_GATEUP_FWD, L.KC_DOWN_FWD, L.KC_DOWN_BWD, L.KC_GATEUP_BWD]
+    ev = {kc: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for kc in kcs}
+    for kc in kcs:
+        for a_, b_ in ev[kc]:
+            a_.record(stream); b_.record(stream)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        for kc in kcs:
+            L.time_next(kc, *ev[kc][i])
+        step()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_stop) / args.steps
+
+    kms = {kc: float(np.mean([a_.elapsed_time(b_) for a_, b_ in ev[kc]])) for kc in kcs}
+    dom = max(kcs, key=lambda kc: kms[kc])
+    names = {L.KC_GATEUP_FWD: "gate/up fwd GEMM + SwiGLU epilogue",
+             L.KC_DOWN_FWD: "down fwd GEMM", L.KC_DOWN_BWD: "down bwd GEMM + SwiGLU' epilogue",
+             L.KC_GATEUP_BWD: "gate/up bwd dX GEMM"}
+    dom_tflops = gemm_flops(dom, T, d, f, r) / (kms[dom] * 1e-3) / 1e12
+    flops = mlp_flops(T, d, f, r)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    line = {
+        "metric": "LoRA-SwiGLU-MLP fwd+bwd TFLOP/s & tokens/s; % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"LoRA-SwiGLU MLP fwd+bwd, T={T} (4x2048), d={d}, f={f}, "
+                               f"r={r}, alpha={alpha:g}, {'4-bit' if q4 else 'bf16'} base "
+                               f"weights, bf16 adapters",
+                   "config_id": args.config, "T": T, "d": d, "f": f, "r": r},
+        "wall_s_timed": round(wall, 3),
+        "kernels_ms": {names[kc]: round(kms[kc], 4) for kc in kcs},
+        "roofline": {"bound": "mfma", "kernel": names[dom], "achieved": round(dom_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": gemm_flops(dom, T, d, f, r),
+                     "avg_launch_ms": round(kms[dom], 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens, mi)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

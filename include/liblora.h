@@ -1,0 +1,204 @@
+/*
+ * liblora -- LoRA-adapted linear layer and LoRA-SwiGLU MLP, forward and
+ * hand-derived backward, for AMD Instinct MI355X (gfx950).
+ *
+ * Definitions the entry points implement (sources are web pages; sections
+ * as printed on them):
+ *   [DD]  "Unsloth deep-dive: Triton kernels + hand-written backprop"
+ *         (chenxutan.com/d/6058) -- 1.2 low-rank update dW = B.A,
+ *         1.3 LoRALayer/LinearWithLoRA: y = x W^T + (x A^T B^T) * alpha/r,
+ *         W frozen; 1.4 QLoRA 4-bit NormalFloat codes; 2.4 hand-written
+ *         backward without an autograd graph.
+ *   [WHY] "Why Unsloth trains 5-8x faster" (mokono.cn/news/868259) --
+ *         3.1/3.2 the rank-r product x A^T stays on chip inside one fused
+ *         kernel; 5.2 4-bit dequantisation fused into the matmul.
+ *   [CR]  "Unsloth code-reading guide" (ai-reference-codex.pages.dev/
+ *         frontier/unsloth) -- 2.1 4-bit weights decoded to bf16 every
+ *         step; 2.3 mlp.forward := LoRA SwiGLU MLP with a manual backward;
+ *         4 the MLP saves only X, e (gate output) and g (up output);
+ *         5 the fast path exists only for dropout 0, no bias, no DoRA.
+ *
+ * Notation: T tokens, k in_features, n out_features, r rank, s = alpha/r
+ * computed in fp32.  Row-major, contiguous tensors:
+ *   X [T x k], W [n x k] (frozen), A [r x k], B [n x r], Y/dY [T x n].
+ *   MLP: d hidden, f ffn; gate/up W [f x d], A [r x d], B [f x r];
+ *        down W [d x f], A [r x f], B [d x r]; e, g [T x f].
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or retains them.  Pointers must be
+ *     16-byte aligned (LORA_ERR_MISALIGNED otherwise).
+ *   - bf16 (LORA_BF16): tensors hold bfloat16; products accumulate in fp32
+ *     and results are rounded once to bf16 (round to nearest even).  Rows
+ *     must be 16-byte multiples: k % 8 == 0 and n % 8 == 0 (d, f for the
+ *     MLP); r may be anything in 1..LORA_MAX_RANK.
+ *   - fp32 (LORA_F32): every tensor fp32, fp32 arithmetic throughout, any
+ *     shape.  4-bit weights are bf16-only.
+ *   - Outputs are overwritten (except where a flag says accumulate).
+ *     dA and dB are reduced over all T tokens in a fixed order, so results
+ *     are bitwise reproducible run to run.
+ *   - T == 0 is valid: forwards write nothing, backwards write dA = dB = 0;
+ *     the token-sized pointers (X, Y, dY, dX, e, g) may then be NULL.
+ *   - `ws`/`ws_bytes`: caller-provided device workspace of at least
+ *     lora_workspace_bytes(...) bytes (may be NULL when that is 0).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous on it and reentrant; kernel faults surface at the
+ *     caller's next synchronisation.
+ *   - Every argument is validated BEFORE any HIP call; on error nothing is
+ *     launched and a status code below is returned.  No exception crosses
+ *     the ABI and nothing aborts.
+ *   - Dropout, bias and DoRA are not representable ([CR] 5).
+ */
+#ifndef LIBLORA_H
+#define LIBLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+#define LORA_MAX_RANK 128
+
+/* status codes */
+#define LORA_OK               0
+#define LORA_ERR_NULL_POINTER 1
+#define LORA_ERR_BAD_SHAPE    2
+#define LORA_ERR_UNSUPPORTED  3
+#define LORA_ERR_WORKSPACE    4
+#define LORA_ERR_MISALIGNED   5
+#define LORA_ERR_HIP          6
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+typedef enum { LORA_W_DENSE = 0, LORA_W_Q4 = 1 } lora_wfmt;
+
+/* flags */
+#define LORA_FLAG_ACCUMULATE_DX 1u   /* lora_linear_bwd: dX += result */
+
+/*
+ * Frozen base weight, logical shape [n x k] (out x in).
+ *   DENSE: `w` holds n*k elements of the call's dtype.
+ *   Q4 ([DD] 1.4, [CR] 2.1): 4-bit codes of a 16-level codebook with one
+ *     fp32 scale per block of `blocksize` (= 64) consecutive k of one row.
+ *     codes:    n*k/2 bytes; flat row-major element 2j is the LOW nibble of
+ *               byte j, element 2j+1 the high nibble.
+ *     absmax:   n*k/64 fp32, block b covers flat elements [64b, 64b+64).
+ *     codebook: 16 fp32 levels (device memory).
+ *   Decoded value of element i: bf16_rne(codebook[c_i] * absmax[i/64]) with
+ *   the product taken as one fp32 multiply (round to nearest even).
+ *   Requires k % 64 == 0 and the bf16 dtype.
+ */
+typedef struct {
+  int32_t fmt;              /* lora_wfmt */
+  int32_t blocksize;        /* Q4 only; must be 64 */
+  const void *w;            /* DENSE */
+  const uint8_t *codes;     /* Q4 */
+  const float *absmax;      /* Q4 */
+  const float *codebook;    /* Q4 */
+} lora_weight;
+
+/* ops for lora_workspace_bytes */
+#define LORA_OP_LINEAR_FWD 0
+#define LORA_OP_LINEAR_BWD 1
+#define LORA_OP_MLP_FWD    2
+#define LORA_OP_MLP_BWD    3
+
+/*
+ * Y = X W^T + s (X A^T) B^T                                  ([DD] 1.3)
+ * The rank-r product X A^T is formed on chip inside the GEMM and applied
+ * in its epilogue; it is never written to memory ([WHY] 3.2).
+ * In: X [T x k], W (lora_weight [n x k]), A [r x k], B [n x r].
+ * Out: Y [T x n].
+ */
+int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r,
+                    float alpha, const void *X, const lora_weight *W,
+                    const void *A, const void *B, void *Y,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Hand-derived backward of lora_linear_fwd for upstream gradient dY
+ * ([DD] 2.4; W frozen, so there is no dW):
+ *   G = dY B,  dX = dY W + s G A,  dA = s G^T X,  dB = s dY^T (X A^T).
+ * In: X, W, A, B as in the forward, dY [T x n].
+ * Out: dX [T x k] (NULL skips it; with LORA_FLAG_ACCUMULATE_DX the result
+ *      is added to dX, which lets projections that share one input, such as
+ *      q/k/v, sum their input gradients), dA [r x k], dB [n x r].
+ */
+int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r,
+                    float alpha, const void *X, const lora_weight *W,
+                    const void *A, const void *B, const void *dY, void *dX,
+                    void *dA, void *dB, uint32_t flags,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * LoRA-SwiGLU MLP forward ([CR] 2.3, 4; SwiGLU per [HF]-blog section 1):
+ *   e = lin(X; gate), g = lin(X; up), h = silu(e) * g, Y = lin(h; down),
+ * each lin a LoRA linear with the same r and alpha.  silu(z) = z/(1+e^-z).
+ * Out: Y [T x d]; e_saved, g_saved [T x f] (the activations the backward
+ * needs; X is the caller's).  h lives in the workspace.
+ */
+int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r,
+                        float alpha, const void *X,
+                        const lora_weight *Wg, const void *Ag, const void *Bg,
+                        const lora_weight *Wu, const void *Au, const void *Bu,
+                        const lora_weight *Wd, const void *Ad, const void *Bd,
+                        void *Y, void *e_saved, void *g_saved,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * LoRA-SwiGLU MLP backward from the saved X, e, g and upstream dY:
+ *   h = silu(e) g;  (dh, dAd, dBd) = linear_bwd(h, dY; down)
+ *   de = dh g sig(e) (1 + e (1 - sig(e))),  dg = dh silu(e)
+ *   (dXg, dAg, dBg) = linear_bwd(X, de; gate), same for up; dX = dXg + dXu.
+ * Out: dX [T x d] (NULL skips it), dAg, dAu [r x d], dBg, dBu [f x r],
+ *      dAd [r x f], dBd [d x r].
+ */
+int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r,
+                        float alpha, const void *X,
+                        const lora_weight *Wg, const void *Ag, const void *Bg,
+                        const lora_weight *Wu, const void *Au, const void *Bu,
+                        const lora_weight *Wd, const void *Ad, const void *Bd,
+                        const void *e_saved, const void *g_saved, const void *dY,
+                        void *dX, void *dAg, void *dBg, void *dAu, void *dBu,
+                        void *dAd, void *dBd,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Standalone 4-bit decode ([CR] 2.1 fast_dequantize; [DD] 1.4):
+ * out[i] = bf16_rne(codebook[c_i] * absmax[i/64]) for i in [0, n*k),
+ * same layout rules as lora_weight Q4.  out_dtype must be LORA_BF16.
+ * out: n*k bf16, device.
+ */
+int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absmax,
+                  const float *codebook, int blocksize, int out_dtype, void *out,
+                  void *stream);
+
+/* Workspace bytes an op needs (k_or_d / n_or_f as in the op's signature;
+ * `wfmt` is the base-weight format).  Returns 0 for invalid arguments. */
+size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T,
+                            int64_t k_or_d, int64_t n_or_f, int64_t r);
+
+/*
+ * Benchmark instrumentation (not part of the method): record the hipEvents
+ * `start` and `stop` (hipEvent_t handles) on the launch stream immediately
+ * before and after the next launch of GEMM class `which`.  One-shot per
+ * class; process-global, not thread-safe; NULL events clear the slot.
+ */
+#define LORA_KC_GATEUP_FWD  0   /* gate/up GEMM with the SwiGLU epilogue   */
+#define LORA_KC_DOWN_FWD    1   /* down-projection forward GEMM            */
+#define LORA_KC_DOWN_BWD    2   /* dY Wd GEMM with the SwiGLU' epilogue    */
+#define LORA_KC_GATEUP_BWD  3   /* [de|dg] [Wg;Wu] GEMM (MLP dX)           */
+#define LORA_KC_LINEAR_FWD  4   /* lora_linear_fwd GEMM                    */
+#define LORA_KC_LINEAR_DX   5   /* lora_linear_bwd dX GEMM                 */
+#define LORA_KC_COUNT       6
+int lora_debug_time_next(int which, void *start, void *stop);
+
+const char *lora_strerror(int status);
+int lora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBLORA_H */

@@ -1,0 +1,310 @@
+"""Python binding of liblora (ctypes; argument marshalling only).
+
+Every step of the LoRA path runs in liblora's HIP kernels.  PyTorch provides
+device memory and the current stream.  Importing this module does not touch
+the GPU; loading the library fails loudly when it has not been built.
+
+Entry points mirror the C ABI in include/liblora.h:
+  lora_linear_fwd, lora_linear_bwd, lora_swiglu_mlp_fwd, lora_swiglu_mlp_bwd,
+  lora_dequant4, lora_workspace_bytes, lora_strerror, lora_abi_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional, Union
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora.so")
+
+LORA_F32, LORA_BF16 = 0, 1
+LORA_W_DENSE, LORA_W_Q4 = 0, 1
+LORA_FLAG_ACCUMULATE_DX = 1
+OP_LINEAR_FWD, OP_LINEAR_BWD, OP_MLP_FWD, OP_MLP_BWD = 0, 1, 2, 3
+STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
+          3: "LORA_ERR_UNSUPPORTED", 4: "LORA_ERR_WORKSPACE", 5: "LORA_ERR_MISALIGNED",
+          6: "LORA_ERR_HIP"}
+
+EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_swiglu_mlp_bwd",
+           "lora_dequant4", "lora_workspace_bytes", "lora_strerror", "lora_abi_version",
+           "lora_debug_time_next"]
+KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX = range(6)
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({strerror(status)})")
+
+
+class LoraWeightC(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("blocksize", ctypes.c_int32),
+                ("w", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("absmax", ctypes.c_void_p), ("codebook", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load liblora.so (built by __graft_entry__.build() or build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"liblora is not built ({LIB_PATH} missing); "
+                           "run python lora_linear_fwd_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32, i32, u32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                  ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t)
+    W = ctypes.POINTER(LoraWeightC)
+    L.lora_linear_fwd.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, vp, vp, sz, vp]
+    L.lora_linear_bwd.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, vp, vp, vp, vp,
+                                  u32, vp, sz, vp]
+    L.lora_swiglu_mlp_fwd.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W,
+                                      vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lora_swiglu_mlp_bwd.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W,
+                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lora_dequant4.argtypes = [i64, i64, vp, vp, vp, i32, i32, vp, vp]
+    L.lora_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i64, i64]
+    L.lora_workspace_bytes.restype = sz
+    L.lora_strerror.argtypes = [i32]
+    L.lora_strerror.restype = ctypes.c_char_p
+    L.lora_abi_version.argtypes = []
+    L.lora_debug_time_next.argtypes = [i32, vp, vp]
+    L.lora_debug_time_next.restype = ctypes.c_int
+    for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
+                 "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().lora_strerror(status).decode()
+
+
+def abi_version() -> int:
+    return lib().lora_abi_version()
+
+
+def time_next(kernel_class: int, start_event, stop_event):
+    """Have the next launch of GEMM `kernel_class` record the two
+    torch.cuda.Event objects around it on the library's launch stream."""
+    for ev in (start_event, stop_event):
+        if ev.cuda_event == 0:
+            ev.record()          # creates the underlying hipEvent
+    _check(lib().lora_debug_time_next(kernel_class, ctypes.c_void_p(start_event.cuda_event),
+                                      ctypes.c_void_p(stop_event.cuda_event)),
+           "lora_debug_time_next")
+
+
+def workspace_bytes(op, dtype, wfmt, T, k_or_d, n_or_f, r) -> int:
+    return int(lib().lora_workspace_bytes(op, dtype, wfmt, T, k_or_d, n_or_f, r))
+
+
+# --------------------------------------------------------------- tensors
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, where):
+    if status != 0:
+        raise LoraError(status, where)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LORA_BF16
+    if t.dtype == torch.float32:
+        return LORA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass
+class Q4Weight:
+    """4-bit base weight on the device: codes [n, k/2] uint8, absmax
+    [n*k/64] fp32, codebook [16] fp32 (layout of include/liblora.h)."""
+    n: int
+    k: int
+    codes: object
+    absmax: object
+    codebook: object
+    blocksize: int = 64
+
+    @property
+    def shape(self):
+        return (self.n, self.k)
+
+
+Weight = Union["torch.Tensor", Q4Weight]
+
+
+def _wstruct(W) -> LoraWeightC:
+    if isinstance(W, Q4Weight):
+        return LoraWeightC(LORA_W_Q4, W.blocksize, None, W.codes.data_ptr(),
+                           W.absmax.data_ptr(), W.codebook.data_ptr())
+    return LoraWeightC(LORA_W_DENSE, 0, W.data_ptr(), None, None, None)
+
+
+def _wfmt(W):
+    return LORA_W_Q4 if isinstance(W, Q4Weight) else LORA_W_DENSE
+
+
+_ws_cache: Dict[tuple, object] = {}
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def clear_workspace_cache():
+    _ws_cache.clear()
+
+
+# ------------------------------------------------------------ entry points
+def lora_linear_fwd(X, W: Weight, A, B, alpha: float, Y=None, workspace=None, stream=None):
+    """Y = X W^T + (alpha/r) (X A^T) B^T."""
+    torch = _torch()
+    T, k = X.shape
+    r = A.shape[0]
+    n = W.shape[0]
+    dt = _dtype_code(X)
+    if Y is None:
+        Y = torch.empty((T, n), dtype=X.dtype, device=X.device)
+    ws = _workspace(workspace_bytes(OP_LINEAR_FWD, dt, _wfmt(W), T, k, n, r), X.device, workspace)
+    wst = _wstruct(W)
+    _check(lib().lora_linear_fwd(dt, T, k, n, r, float(alpha), _ptr(X), ctypes.byref(wst),
+                                 _ptr(A), _ptr(B), _ptr(Y), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)),
+           "lora_linear_fwd")
+    return Y
+
+
+def lora_linear_bwd(X, W: Weight, A, B, alpha: float, dY, need_dx=True, dX=None,
+                    accumulate_dx=False, dA=None, dB=None, workspace=None, stream=None):
+    """Returns (dX or None, dA, dB)."""
+    torch = _torch()
+    T, k = X.shape
+    r = A.shape[0]
+    n = W.shape[0]
+    dt = _dtype_code(X)
+    if need_dx and dX is None:
+        dX = torch.empty((T, k), dtype=X.dtype, device=X.device)
+    if not need_dx:
+        dX = None
+    dA = torch.empty_like(A) if dA is None else dA
+    dB = torch.empty_like(B) if dB is None else dB
+    ws = _workspace(workspace_bytes(OP_LINEAR_BWD, dt, _wfmt(W), T, k, n, r), X.device, workspace)
+    wst = _wstruct(W)
+    flags = LORA_FLAG_ACCUMULATE_DX if accumulate_dx else 0
+    _check(lib().lora_linear_bwd(dt, T, k, n, r, float(alpha), _ptr(X), ctypes.byref(wst),
+                                 _ptr(A), _ptr(B), _ptr(dY), _ptr(dX), _ptr(dA), _ptr(dB),
+                                 flags, _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(stream)),
+           "lora_linear_bwd")
+    return dX, dA, dB
+
+
+def _mlp_dims(X, W, A):
+    T, d = X.shape
+    f = W["gate"].shape[0]
+    r = A["gate"].shape[0]
+    return T, d, f, r
+
+
+def lora_swiglu_mlp_fwd(X, W: Dict[str, Weight], A, B, alpha: float, Y=None, e=None, g=None,
+                        workspace=None, stream=None):
+    """Returns (Y, e, g); W/A/B are dicts keyed 'gate', 'up', 'down'."""
+    torch = _torch()
+    T, d, f, r = _mlp_dims(X, W, A)
+    dt = _dtype_code(X)
+    Y = torch.empty((T, d), dtype=X.dtype, device=X.device) if Y is None else Y
+    e = torch.empty((T, f), dtype=X.dtype, device=X.device) if e is None else e
+    g = torch.empty((T, f), dtype=X.dtype, device=X.device) if g is None else g
+    ws = _workspace(workspace_bytes(OP_MLP_FWD, dt, _wfmt(W["gate"]), T, d, f, r), X.device,
+                    workspace)
+    ws_ = [_wstruct(W[p]) for p in ("gate", "up", "down")]
+    _check(lib().lora_swiglu_mlp_fwd(
+        dt, T, d, f, r, float(alpha), _ptr(X),
+        ctypes.byref(ws_[0]), _ptr(A["gate"]), _ptr(B["gate"]),
+        ctypes.byref(ws_[1]), _ptr(A["up"]), _ptr(B["up"]),
+        ctypes.byref(ws_[2]), _ptr(A["down"]), _ptr(B["down"]),
+        _ptr(Y), _ptr(e), _ptr(g), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+        "lora_swiglu_mlp_fwd")
+    return Y, e, g
+
+
+def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, need_dx=True,
+                        out: Optional[dict] = None, workspace=None, stream=None):
+    """Returns dict with dX (or None) and dA_*/dB_* per projection."""
+    torch = _torch()
+    T, d, f, r = _mlp_dims(X, W, A)
+    dt = _dtype_code(X)
+    o = dict(out or {})
+    if need_dx and o.get("dX") is None:
+        o["dX"] = torch.empty((T, d), dtype=X.dtype, device=X.device)
+    if not need_dx:
+        o["dX"] = None
+    for p in ("gate", "up", "down"):
+        o.setdefault("dA_" + p, torch.empty_like(A[p]))
+        o.setdefault("dB_" + p, torch.empty_like(B[p]))
+    ws = _workspace(workspace_bytes(OP_MLP_BWD, dt, _wfmt(W["gate"]), T, d, f, r), X.device,
+                    workspace)
+    ws_ = [_wstruct(W[p]) for p in ("gate", "up", "down")]
+    _check(lib().lora_swiglu_mlp_bwd(
+        dt, T, d, f, r, float(alpha), _ptr(X),
+        ctypes.byref(ws_[0]), _ptr(A["gate"]), _ptr(B["gate"]),
+        ctypes.byref(ws_[1]), _ptr(A["up"]), _ptr(B["up"]),
+        ctypes.byref(ws_[2]), _ptr(A["down"]), _ptr(B["down"]),
+        _ptr(e), _ptr(g), _ptr(dY), _ptr(o["dX"]),
+        _ptr(o["dA_gate"]), _ptr(o["dB_gate"]), _ptr(o["dA_up"]), _ptr(o["dB_up"]),
+        _ptr(o["dA_down"]), _ptr(o["dB_down"]),
+        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+        "lora_swiglu_mlp_bwd")
+    return o
+
+
+def lora_dequant4(q: Q4Weight, out=None, stream=None):
+    """Decode a 4-bit weight to a bf16 [n, k] tensor."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((q.n, q.k), dtype=torch.bfloat16, device=q.codes.device)
+    _check(lib().lora_dequant4(q.n, q.k, _ptr(q.codes), _ptr(q.absmax), _ptr(q.codebook),
+                               q.blocksize, LORA_BF16, _ptr(out), _stream(stream)),
+           "lora_dequant4")
+    return out
+
+
+# ------------------------------------------------------ host -> device helpers
+def to_device_q4(qw, device="cuda"):
+    """Upload a host-side lora_inputs.Q4Weight."""
+    torch = _torch()
+    return Q4Weight(qw.n, qw.k, torch.from_numpy(qw.codes).to(device),
+                    torch.from_numpy(qw.absmax).to(device),
+                    torch.from_numpy(qw.codebook).to(device), qw.blocksize)

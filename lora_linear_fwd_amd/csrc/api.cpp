@@ -1,0 +1,717 @@
+// liblora C ABI: argument validation, workspace planning and kernel dispatch.
+// Every check runs before the first HIP call; no exception leaves this file.
+#include "liblora.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "aux_kernels.hpp"
+#include "gemm_launch.hpp"
+
+using namespace lora;
+
+namespace {
+
+constexpr int kInloopMaxRS = 32;   // wider side products are precomputed
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int rs_of(int64_t width) { return (int)(cdiv(width, 16) * 16); }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------- workspace
+struct Bump {
+  size_t cur = 0;
+  size_t take(size_t bytes) {
+    const size_t o = cur;
+    cur += (bytes + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+// split choices shared by the planner and the launchers
+struct NTSplit { int ks; int kchunk; };
+inline NTSplit nt_split(int64_t T, int64_t K) {
+  const int64_t gx = std::max<int64_t>(1, cdiv(T, 64));
+  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, gx), cdiv(K, 512)));
+  int64_t kchunk = cdiv(cdiv(K, ks), 128) * 128;
+  ks = std::max<int64_t>(1, cdiv(K, kchunk));
+  return {(int)ks, (int)kchunk};
+}
+struct TNSplit { int ts; int tchunk; };
+inline TNSplit tn_split(int64_t T, int64_t N) {
+  const int64_t gx = cdiv(N, 256);
+  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, gx), cdiv(T, 64)));
+  int64_t tchunk = std::max<int64_t>(64, cdiv(cdiv(T, ts), 64) * 64);
+  ts = std::max<int64_t>(1, cdiv(T, tchunk));
+  return {(int)ts, (int)tchunk};
+}
+inline size_t nt_part_bytes(int64_t T, int64_t K, int RS) {
+  return (size_t)nt_split(T, K).ks * T * RS * 4;
+}
+inline size_t tn_part_bytes(int64_t T, int64_t N, int RS) {
+  return (size_t)tn_split(T, N).ts * RS * N * 4;
+}
+
+struct LinFwdPlan { size_t side, epi, hpart, hbf, total; };
+LinFwdPlan plan_lin_fwd(int64_t T, int64_t k, int64_t n, int64_t r) {
+  Bump b; LinFwdPlan p{};
+  const int RS = rs_of(r);
+  p.side = b.take((size_t)RS * k * 2);
+  p.epi = b.take((size_t)n * RS * 2);
+  if (RS > kInloopMaxRS) {
+    p.hpart = b.take(nt_part_bytes(T, k, RS));
+    p.hbf = b.take((size_t)T * RS * 2);
+  }
+  p.total = b.cur;
+  return p;
+}
+
+struct LinBwdPlan { size_t side_nn, epi_nn, side_nt, g32, gbf, h32, ntpart, tnpart, total; };
+LinBwdPlan plan_lin_bwd(int64_t T, int64_t k, int64_t n, int64_t r) {
+  Bump b; LinBwdPlan p{};
+  const int RS = rs_of(r);
+  p.side_nn = b.take((size_t)RS * n * 2);
+  p.epi_nn = b.take((size_t)k * RS * 2);
+  p.side_nt = b.take((size_t)RS * k * 2);
+  p.g32 = b.take((size_t)T * RS * 4);
+  p.gbf = b.take((size_t)T * RS * 2);
+  p.h32 = b.take((size_t)T * RS * 4);
+  p.ntpart = b.take(std::max(nt_part_bytes(T, n, RS), nt_part_bytes(T, k, RS)));
+  p.tnpart = b.take(std::max(tn_part_bytes(T, k, RS), tn_part_bytes(T, n, RS)));
+  p.total = b.cur;
+  return p;
+}
+
+struct MlpFwdPlan { size_t h, side_gu, epi_gu, side_d, epi_d, hpart, hbf, total; };
+MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r) {
+  Bump b; MlpFwdPlan p{};
+  const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
+  p.h = b.take((size_t)T * f * 2);
+  p.side_gu = b.take((size_t)RS1 * d * 2);
+  p.epi_gu = b.take((size_t)2 * f * RS1 * 2);
+  p.side_d = b.take((size_t)RS2 * f * 2);
+  p.epi_d = b.take((size_t)d * RS2 * 2);
+  p.hpart = b.take(std::max(nt_part_bytes(T, d, RS1), nt_part_bytes(T, f, RS2)));
+  p.hbf = b.take((size_t)T * std::max(RS1, RS2) * 2);
+  p.total = b.cur;
+  return p;
+}
+
+struct MlpBwdPlan {
+  size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, side_gu_nn, epi_gu_nn, side_gu_nt;
+  size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, total;
+};
+MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r) {
+  Bump b; MlpBwdPlan p{};
+  const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
+  p.de = b.take((size_t)T * f * 2);
+  p.dg = b.take((size_t)T * f * 2);
+  p.side_d_nn = b.take((size_t)RS2 * d * 2);
+  p.epi_d_nn = b.take((size_t)f * RS2 * 2);
+  p.side_d_nt = b.take((size_t)RS2 * f * 2);
+  p.side_gu_nn = b.take((size_t)RS1 * 2 * f * 2);
+  p.epi_gu_nn = b.take((size_t)d * RS1 * 2);
+  p.side_gu_nt = b.take((size_t)RS1 * d * 2);
+  p.gd32 = b.take((size_t)T * RS2 * 4);
+  p.gdbf = b.take((size_t)T * RS2 * 2);
+  p.hd32 = b.take((size_t)T * RS2 * 4);
+  p.ggu32 = b.take((size_t)T * RS1 * 4);
+  p.ggubf = b.take((size_t)T * RS1 * 2);
+  p.hgu32 = b.take((size_t)T * RS1 * 4);
+  p.ntpart = b.take(std::max({nt_part_bytes(T, d, RS2), nt_part_bytes(T, f, RS2),
+                              nt_part_bytes(T, 2 * f, RS1), nt_part_bytes(T, d, RS1)}));
+  p.tnpart = b.take(std::max({tn_part_bytes(T, f, RS2), tn_part_bytes(T, d, RS2),
+                              tn_part_bytes(T, d, RS1), tn_part_bytes(T, 2 * f, RS1)}));
+  p.total = b.cur;
+  return p;
+}
+
+// fp32 path workspaces
+size_t plan_f32(int op, int64_t T, int64_t kd, int64_t nf, int64_t r) {
+  switch (op) {
+    case LORA_OP_LINEAR_FWD: return (size_t)T * r * 4;
+    case LORA_OP_LINEAR_BWD: return 2 * (size_t)T * r * 4;
+    case LORA_OP_MLP_FWD: return (size_t)T * nf * 4 + (size_t)T * r * 4 + 256;
+    case LORA_OP_MLP_BWD: return 4 * (size_t)T * nf * 4 + 2 * (size_t)T * r * 4 + 1024;
+  }
+  return 0;
+}
+
+// ------------------------------------------------------------- validation
+struct WeightView {
+  bool q4;
+  const bf16_t *w;
+  const uint8_t *codes;
+  const float *absmax;
+  const float *codebook;
+};
+
+int check_weight(const lora_weight *W, int dtype, int64_t k_in, WeightView &out) {
+  if (!W) return LORA_ERR_NULL_POINTER;
+  if (W->fmt == LORA_W_DENSE) {
+    if (!W->w) return LORA_ERR_NULL_POINTER;
+    if (!aligned16(W->w)) return LORA_ERR_MISALIGNED;
+    out = {false, (const bf16_t *)W->w, nullptr, nullptr, nullptr};
+    return LORA_OK;
+  }
+  if (W->fmt != LORA_W_Q4) return LORA_ERR_UNSUPPORTED;
+  if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (W->blocksize != 64) return LORA_ERR_UNSUPPORTED;
+  if (!W->codes || !W->absmax || !W->codebook) return LORA_ERR_NULL_POINTER;
+  if (k_in % 64) return LORA_ERR_BAD_SHAPE;
+  if (!aligned16(W->codes) || !aligned16(W->absmax) || !aligned16(W->codebook))
+    return LORA_ERR_MISALIGNED;
+  out = {true, nullptr, W->codes, W->absmax, W->codebook};
+  return LORA_OK;
+}
+
+int check_dims(int dtype, int64_t T, int64_t k, int64_t n, int64_t r) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (T < 0 || k <= 0 || n <= 0 || r <= 0) return LORA_ERR_BAD_SHAPE;
+  if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  if (T > (int64_t)1 << 30 || k > (int64_t)1 << 24 || n > (int64_t)1 << 24) return LORA_ERR_BAD_SHAPE;
+  if (dtype == LORA_BF16 && ((k % 8) || (n % 8))) return LORA_ERR_BAD_SHAPE;
+  return LORA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (!p) return LORA_ERR_NULL_POINTER;
+  for (const void *p : ps)
+    if (!aligned16(p)) return LORA_ERR_MISALIGNED;
+  return LORA_OK;
+}
+
+// token-sized tensors ([T x ...]) hold no elements when T == 0 and may then
+// be NULL
+int check_tok_ptrs(int64_t T, std::initializer_list<const void *> ps) {
+  if (T == 0) {
+    for (const void *p : ps)
+      if (p && !aligned16(p)) return LORA_ERR_MISALIGNED;
+    return LORA_OK;
+  }
+  for (const void *p : ps)
+    if (!p) return LORA_ERR_NULL_POINTER;
+  for (const void *p : ps)
+    if (!aligned16(p)) return LORA_ERR_MISALIGNED;
+  return LORA_OK;
+}
+
+#define LORA_TRY(expr)                         \
+  do {                                         \
+    int _st = (expr);                          \
+    if (_st != LORA_OK) return _st;            \
+  } while (0)
+#define HIP_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return LORA_ERR_HIP; \
+  } while (0)
+
+inline unsigned blocks_for(int64_t count, int per = 256) { return (unsigned)cdiv(count, per); }
+
+// ------------------------------------------------------------ bf16 helpers
+int build_side(bf16_t *dst, int RS, int64_t K, const void *src0, const void *src1, int64_t r,
+               int64_t ksplit, int tr, hipStream_t st) {
+  const int64_t cnt = (int64_t)RS * K;
+  if (cnt == 0) return LORA_OK;
+  hipLaunchKernelGGL(k_build_side, dim3(blocks_for(cnt)), dim3(256), 0, st, dst, RS, (int)K,
+                     (const bf16_t *)src0, (const bf16_t *)src1, (int)r, (int)ksplit, tr);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+int build_epi(bf16_t *dst, int64_t rows, int RS, const void *src0, const void *src1, int64_t r,
+              int64_t rsplit, int tr, hipStream_t st) {
+  const int64_t cnt = rows * RS;
+  if (cnt == 0) return LORA_OK;
+  hipLaunchKernelGGL(k_build_epi, dim3(blocks_for(cnt)), dim3(256), 0, st, dst, (int)rows, RS,
+                     (const bf16_t *)src0, (const bf16_t *)src1, (int)r, (int)rsplit, tr);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+// out = Z . SIDE^T over all K (deterministic split-K); fp32 and/or scaled bf16
+int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, const bf16_t *Z1,
+              int64_t ksplit, int64_t ldz, const bf16_t *E, const bf16_t *G, const bf16_t *side,
+              float *part, float *out32, bf16_t *outbf, float scale, hipStream_t st) {
+  if (T == 0) return LORA_OK;
+  const NTSplit sp = nt_split(T, K);
+  SkinnyNTArgs a{(int)T, (int)K, (int)ksplit, sp.kchunk, Z0, Z1, ldz, E, G, side, part};
+  dim3 grid((unsigned)cdiv(T, 64), (unsigned)sp.ks);
+#define SNT(R)                                                                          \
+  case R:                                                                               \
+    if (zswiglu) hipLaunchKernelGGL((k_skinny_nt<R, true>), grid, dim3(256), 0, st, a);  \
+    else hipLaunchKernelGGL((k_skinny_nt<R, false>), grid, dim3(256), 0, st, a);         \
+    break;
+  switch (RS) {
+    SNT(16) SNT(32) SNT(48) SNT(64) SNT(80) SNT(96) SNT(112) SNT(128)
+    SNT(144) SNT(160) SNT(176) SNT(192) SNT(208) SNT(224) SNT(240) SNT(256)
+    default: return LORA_ERR_UNSUPPORTED;
+  }
+#undef SNT
+  HIP_TRY(hipGetLastError());
+  const int64_t cnt = T * RS;
+  hipLaunchKernelGGL(k_reduce_side, dim3(blocks_for(cnt)), dim3(256), 0, st, part, sp.ks, cnt,
+                     scale, out32, outbf);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+// adapter gradient: s * P^T Z reduced over T, scattered per ReduceTNArgs
+int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const bf16_t *Z0,
+              const bf16_t *Z1, int64_t nsplit, int64_t ldz, const bf16_t *E, const bf16_t *G,
+              float *part, int64_t r, float scale, int transposed, bf16_t *out0, bf16_t *out1,
+              int64_t out_nsplit, hipStream_t st) {
+  const TNSplit sp = tn_split(T, N);
+  SkinnyTNArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, P, Z0, Z1, ldz, E, G, part};
+  dim3 grid((unsigned)cdiv(N, 256), (unsigned)sp.ts);
+#define STN(R)                                                                          \
+  case R:                                                                               \
+    if (zswiglu) hipLaunchKernelGGL((k_skinny_tn<R, true>), grid, dim3(256), 0, st, a);  \
+    else hipLaunchKernelGGL((k_skinny_tn<R, false>), grid, dim3(256), 0, st, a);         \
+    break;
+  switch (RS) {
+    STN(16) STN(32) STN(48) STN(64) STN(80) STN(96) STN(112) STN(128)
+    STN(144) STN(160) STN(176) STN(192) STN(208) STN(224) STN(240) STN(256)
+    default: return LORA_ERR_UNSUPPORTED;
+  }
+#undef STN
+  HIP_TRY(hipGetLastError());
+  ReduceTNArgs ra{part, sp.ts, RS, (int)N, (int)r, (int)out_nsplit, scale, transposed, out0, out1};
+  hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)RS * N)), dim3(256), 0, st, ra);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+GemmArgs gemm_base() {
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  return a;
+}
+
+void set_b(GemmArgs &a, const WeightView &w0, const WeightView &w1) {
+  a.B0 = w0.w; a.B1 = w1.w;
+  a.Q0 = w0.codes; a.Q1 = w1.codes;
+  a.S0 = w0.absmax; a.S1 = w1.absmax;
+  a.codebook = w0.codebook;
+}
+
+struct TimerSlot { hipEvent_t start = nullptr, stop = nullptr; };
+TimerSlot g_timer[LORA_KC_COUNT];
+
+int run_gemm(int kc, bool nn, bool q4, int rs_inloop, int epi, const GemmArgs &a, hipStream_t st) {
+  TimerSlot ts = g_timer[kc];
+  g_timer[kc] = TimerSlot{};
+  if (ts.start) HIP_TRY(hipEventRecord(ts.start, st));
+  hipError_t e;
+  if (!nn) e = q4 ? launch_gemm_nt_q4(rs_inloop, epi, a, st) : launch_gemm_nt(rs_inloop, epi, a, st);
+  else e = q4 ? launch_gemm_nn_q4(rs_inloop, epi, a, st) : launch_gemm_nn(rs_inloop, epi, a, st);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  if (ts.stop) HIP_TRY(hipEventRecord(ts.stop, st));
+  return LORA_OK;
+}
+
+// --------------------------------------------------------------- fp32 path
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t sam, int64_t sak,
+             const float *B, int64_t sbk, int64_t sbn, float *C, int64_t ldc, float alpha,
+             float beta, hipStream_t st) {
+  if (M == 0 || N == 0) return LORA_OK;
+  F32GemmArgs a{(int)M, (int)N, (int)K, A, sam, sak, B, sbk, sbn, C, ldc, alpha, beta};
+  hipLaunchKernelGGL(k_gemm_f32, dim3((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 64)), dim3(256), 0,
+                     st, a);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+// Y = X W^T + s (X A^T) B^T   (fp32); H: [T x r] scratch
+int lin_fwd_f32(int64_t T, int64_t k, int64_t n, int64_t r, float s, const float *X,
+                const float *W, const float *A, const float *B, float *Y, float *H,
+                hipStream_t st) {
+  LORA_TRY(gemm_f32(T, r, k, X, k, 1, A, 1, k, H, r, 1.f, 0.f, st));
+  LORA_TRY(gemm_f32(T, n, k, X, k, 1, W, 1, k, Y, n, 1.f, 0.f, st));
+  LORA_TRY(gemm_f32(T, n, r, H, r, 1, B, 1, r, Y, n, s, 1.f, st));
+  return LORA_OK;
+}
+
+// dX (+)= dY W + s G A;  dA = s G^T X;  dB = s dY^T H   (fp32)
+int lin_bwd_f32(int64_t T, int64_t k, int64_t n, int64_t r, float s, const float *X,
+                const float *W, const float *A, const float *B, const float *dY, float *dX,
+                bool acc, float *dA, float *dB, float *G, float *H, hipStream_t st) {
+  LORA_TRY(gemm_f32(T, r, n, dY, n, 1, B, r, 1, G, r, 1.f, 0.f, st));
+  LORA_TRY(gemm_f32(T, r, k, X, k, 1, A, 1, k, H, r, 1.f, 0.f, st));
+  if (dX) {
+    LORA_TRY(gemm_f32(T, k, n, dY, n, 1, W, k, 1, dX, k, 1.f, acc ? 1.f : 0.f, st));
+    LORA_TRY(gemm_f32(T, k, r, G, r, 1, A, k, 1, dX, k, s, 1.f, st));
+  }
+  LORA_TRY(gemm_f32(r, k, T, G, 1, r, X, k, 1, dA, k, s, 0.f, st));
+  LORA_TRY(gemm_f32(n, r, T, dY, 1, n, H, r, 1, dB, r, s, 0.f, st));
+  return LORA_OK;
+}
+
+}  // namespace
+
+// ============================================================== public ABI
+extern "C" {
+
+int lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+int lora_debug_time_next(int which, void *start, void *stop) {
+  if (which < 0 || which >= LORA_KC_COUNT) return LORA_ERR_BAD_SHAPE;
+  g_timer[which] = TimerSlot{(hipEvent_t)start, (hipEvent_t)stop};
+  return LORA_OK;
+}
+
+const char *lora_strerror(int status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_NULL_POINTER: return "null pointer argument";
+    case LORA_ERR_BAD_SHAPE: return "invalid shape";
+    case LORA_ERR_UNSUPPORTED: return "unsupported dtype, format or rank";
+    case LORA_ERR_WORKSPACE: return "workspace too small";
+    case LORA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case LORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, int64_t nf,
+                            int64_t r) {
+  (void)wfmt;
+  if (T < 0 || kd <= 0 || nf <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
+  if (dtype == LORA_F32) return plan_f32(op, T, kd, nf, r);
+  if (dtype != LORA_BF16) return 0;
+  switch (op) {
+    case LORA_OP_LINEAR_FWD: return plan_lin_fwd(T, kd, nf, r).total;
+    case LORA_OP_LINEAR_BWD: return plan_lin_bwd(T, kd, nf, r).total;
+    case LORA_OP_MLP_FWD: return plan_mlp_fwd(T, kd, nf, r).total;
+    case LORA_OP_MLP_BWD: return plan_mlp_bwd(T, kd, nf, r).total;
+  }
+  return 0;
+}
+
+int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float alpha,
+                    const void *X, const lora_weight *W, const void *A, const void *B, void *Y,
+                    void *ws, size_t ws_bytes, void *stream) {
+  LORA_TRY(check_dims(dtype, T, k, n, r));
+  WeightView wv;
+  LORA_TRY(check_weight(W, dtype, k, wv));
+  LORA_TRY(check_ptrs({A, B}));
+  LORA_TRY(check_tok_ptrs(T, {X, Y}));
+  const size_t need = lora_workspace_bytes(LORA_OP_LINEAR_FWD, dtype, W->fmt, T, k, n, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  hipStream_t st = (hipStream_t)stream;
+  const float s = alpha / (float)r;
+  if (T == 0) return LORA_OK;
+  char *w = (char *)ws;
+  if (dtype == LORA_F32)
+    return lin_fwd_f32(T, k, n, r, s, (const float *)X, (const float *)wv.w, (const float *)A,
+                       (const float *)B, (float *)Y, (float *)w, st);
+
+  const LinFwdPlan pl = plan_lin_fwd(T, k, n, r);
+  const int RS = rs_of(r);
+  bf16_t *side = (bf16_t *)(w + pl.side), *epi = (bf16_t *)(w + pl.epi);
+  LORA_TRY(build_side(side, RS, k, A, nullptr, r, k, 0, st));
+  LORA_TRY(build_epi(epi, n, RS, B, nullptr, r, n, 0, st));
+  GemmArgs a = gemm_base();
+  a.M = (int)T; a.N = (int)n; a.K = (int)k; a.ksplit = (int)k;
+  a.A0 = a.A1 = (const bf16_t *)X; a.lda = k;
+  set_b(a, wv, wv); a.ldb = k;
+  a.side = side; a.ld_side = k; a.rs = RS; a.epi = epi; a.s = s;
+  a.C = (bf16_t *)Y; a.ldc = n;
+  a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(n, BN);
+  int rs_inloop = RS;
+  if (RS > kInloopMaxRS) {
+    bf16_t *hbf = (bf16_t *)(w + pl.hbf);
+    LORA_TRY(skinny_nt(RS, false, T, k, (const bf16_t *)X, (const bf16_t *)X, k, k, nullptr,
+                       nullptr, side, (float *)(w + pl.hpart), nullptr, hbf, s, st));
+    a.hglob = hbf;
+    rs_inloop = 0;
+  }
+  return run_gemm(LORA_KC_LINEAR_FWD, false, wv.q4, rs_inloop, EPI_STORE, a, st);
+}
+
+int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float alpha,
+                    const void *X, const lora_weight *W, const void *A, const void *B,
+                    const void *dY, void *dX, void *dA, void *dB, uint32_t flags, void *ws,
+                    size_t ws_bytes, void *stream) {
+  LORA_TRY(check_dims(dtype, T, k, n, r));
+  WeightView wv;
+  LORA_TRY(check_weight(W, dtype, k, wv));
+  LORA_TRY(check_ptrs({A, B, dA, dB}));
+  LORA_TRY(check_tok_ptrs(T, {X, dY}));
+  if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
+  if (flags & ~(uint32_t)LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
+  const size_t need = lora_workspace_bytes(LORA_OP_LINEAR_BWD, dtype, W->fmt, T, k, n, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  hipStream_t st = (hipStream_t)stream;
+  const float s = alpha / (float)r;
+  const bool acc = (flags & LORA_FLAG_ACCUMULATE_DX) != 0;
+  char *w = (char *)ws;
+  if (dtype == LORA_F32) {
+    float *G = (float *)w, *H = G + T * r;
+    return lin_bwd_f32(T, k, n, r, s, (const float *)X, (const float *)wv.w, (const float *)A,
+                       (const float *)B, (const float *)dY, (float *)dX, acc, (float *)dA,
+                       (float *)dB, G, H, st);
+  }
+  const LinBwdPlan pl = plan_lin_bwd(T, k, n, r);
+  const int RS = rs_of(r);
+  bf16_t *side_nn = (bf16_t *)(w + pl.side_nn), *epi_nn = (bf16_t *)(w + pl.epi_nn);
+  bf16_t *side_nt = (bf16_t *)(w + pl.side_nt);
+  float *g32 = (float *)(w + pl.g32), *h32 = (float *)(w + pl.h32);
+  bf16_t *gbf = (bf16_t *)(w + pl.gbf);
+  float *ntpart = (float *)(w + pl.ntpart), *tnpart = (float *)(w + pl.tnpart);
+  LORA_TRY(build_side(side_nn, RS, n, B, nullptr, r, n, 1, st));   // B^T padded [RS x n]
+  LORA_TRY(build_epi(epi_nn, k, RS, A, nullptr, r, k, 1, st));     // A^T padded [k x RS]
+  LORA_TRY(build_side(side_nt, RS, k, A, nullptr, r, k, 0, st));   // A padded [RS x k]
+  const bf16_t *Xb = (const bf16_t *)X, *dYb = (const bf16_t *)dY;
+  const bool inloop = RS <= kInloopMaxRS;
+  if (T > 0) {
+    if (!dX || !inloop)
+      LORA_TRY(skinny_nt(RS, false, T, n, dYb, dYb, n, n, nullptr, nullptr, side_nn, ntpart, g32,
+                         gbf, s, st));
+    if (dX) {
+      GemmArgs a = gemm_base();
+      a.M = (int)T; a.N = (int)k; a.K = (int)n; a.ksplit = (int)n;
+      a.A0 = a.A1 = dYb; a.lda = n;
+      set_b(a, wv, wv); a.ldb = k;
+      a.side = side_nn; a.ld_side = n; a.rs = RS; a.epi = epi_nn; a.s = s;
+      a.accumulate = acc; a.C = (bf16_t *)dX; a.ldc = k;
+      a.side_out = inloop ? g32 : nullptr;
+      a.hglob = gbf;
+      a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
+      LORA_TRY(run_gemm(LORA_KC_LINEAR_DX, true, wv.q4, inloop ? RS : 0, EPI_STORE, a, st));
+    }
+    LORA_TRY(skinny_nt(RS, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,
+                       nullptr, 1.f, st));
+  }
+  // dA = s G^T X  [r x k];  dB = s dY^T H  [n x r]
+  LORA_TRY(skinny_tn(RS, false, T, k, g32, Xb, Xb, k, k, nullptr, nullptr, tnpart, r, s, 0,
+                     (bf16_t *)dA, nullptr, k, st));
+  LORA_TRY(skinny_tn(RS, false, T, n, h32, dYb, dYb, n, n, nullptr, nullptr, tnpart, r, s, 1,
+                     (bf16_t *)dB, nullptr, n, st));
+  return LORA_OK;
+}
+
+int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+                        const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
+                        const lora_weight *Wu, const void *Au, const void *Bu,
+                        const lora_weight *Wd, const void *Ad, const void *Bd, void *Y,
+                        void *e_saved, void *g_saved, void *ws, size_t ws_bytes, void *stream) {
+  LORA_TRY(check_dims(dtype, T, d, f, r));
+  WeightView wg, wu, wd;
+  LORA_TRY(check_weight(Wg, dtype, d, wg));
+  LORA_TRY(check_weight(Wu, dtype, d, wu));
+  LORA_TRY(check_weight(Wd, dtype, f, wd));
+  if (wg.q4 != wu.q4) return LORA_ERR_UNSUPPORTED;
+  LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd}));
+  LORA_TRY(check_tok_ptrs(T, {X, Y, e_saved, g_saved}));
+  const size_t need = lora_workspace_bytes(LORA_OP_MLP_FWD, dtype, Wg->fmt, T, d, f, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  hipStream_t st = (hipStream_t)stream;
+  const float s = alpha / (float)r;
+  if (T == 0) return LORA_OK;
+  char *w = (char *)ws;
+  if (dtype == LORA_F32) {
+    float *h = (float *)w, *H = h + T * f;
+    float *e = (float *)e_saved, *g = (float *)g_saved;
+    LORA_TRY(lin_fwd_f32(T, d, f, r, s, (const float *)X, (const float *)wg.w, (const float *)Ag,
+                         (const float *)Bg, e, H, st));
+    LORA_TRY(lin_fwd_f32(T, d, f, r, s, (const float *)X, (const float *)wu.w, (const float *)Au,
+                         (const float *)Bu, g, H, st));
+    hipLaunchKernelGGL(k_swiglu_f32, dim3(blocks_for(T * f)), dim3(256), 0, st, e, g, h, T * f);
+    HIP_TRY(hipGetLastError());
+    return lin_fwd_f32(T, f, d, r, s, h, (const float *)wd.w, (const float *)Ad,
+                       (const float *)Bd, (float *)Y, H, st);
+  }
+  const MlpFwdPlan pl = plan_mlp_fwd(T, d, f, r);
+  const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
+  bf16_t *h = (bf16_t *)(w + pl.h);
+  bf16_t *side_gu = (bf16_t *)(w + pl.side_gu), *epi_gu = (bf16_t *)(w + pl.epi_gu);
+  bf16_t *side_d = (bf16_t *)(w + pl.side_d), *epi_d = (bf16_t *)(w + pl.epi_d);
+  bf16_t *hbf = (bf16_t *)(w + pl.hbf);
+  float *hpart = (float *)(w + pl.hpart);
+  LORA_TRY(build_side(side_gu, RS1, d, Ag, Au, r, d, 0, st));
+  LORA_TRY(build_epi(epi_gu, 2 * f, RS1, Bg, Bu, r, f, 0, st));
+  LORA_TRY(build_side(side_d, RS2, f, Ad, nullptr, r, f, 0, st));
+  LORA_TRY(build_epi(epi_d, d, RS2, Bd, nullptr, r, d, 0, st));
+  const bf16_t *Xb = (const bf16_t *)X;
+
+  // gate + up with the SwiGLU epilogue
+  GemmArgs a = gemm_base();
+  a.M = (int)T; a.N = (int)(2 * f); a.K = (int)d; a.ksplit = (int)d;
+  a.A0 = a.A1 = Xb; a.lda = d;
+  set_b(a, wg, wu); a.ldb = d;
+  a.gu_f = (int)f;
+  a.side = side_gu; a.ld_side = d; a.rs = RS1; a.epi = epi_gu; a.s = s;
+  a.E = (bf16_t *)e_saved; a.G = (bf16_t *)g_saved; a.H = h;
+  a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, 128);
+  int rs1 = RS1;
+  if (RS1 > kInloopMaxRS) {
+    LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
+                       hbf, s, st));
+    a.hglob = hbf;
+    rs1 = 0;
+  }
+  LORA_TRY(run_gemm(LORA_KC_GATEUP_FWD, false, wg.q4, rs1, EPI_SWIGLU_FWD, a, st));
+
+  // down
+  GemmArgs b = gemm_base();
+  b.M = (int)T; b.N = (int)d; b.K = (int)f; b.ksplit = (int)f;
+  b.A0 = b.A1 = h; b.lda = f;
+  set_b(b, wd, wd); b.ldb = f;
+  b.side = side_d; b.ld_side = f; b.rs = RS2; b.epi = epi_d; b.s = s;
+  b.C = (bf16_t *)Y; b.ldc = d;
+  b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
+  int rs2 = RS2;
+  if (RS2 > kInloopMaxRS) {
+    LORA_TRY(skinny_nt(RS2, false, T, f, h, h, f, f, nullptr, nullptr, side_d, hpart, nullptr, hbf,
+                       s, st));
+    b.hglob = hbf;
+    rs2 = 0;
+  }
+  return run_gemm(LORA_KC_DOWN_FWD, false, wd.q4, rs2, EPI_STORE, b, st);
+}
+
+int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+                        const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
+                        const lora_weight *Wu, const void *Au, const void *Bu,
+                        const lora_weight *Wd, const void *Ad, const void *Bd,
+                        const void *e_saved, const void *g_saved, const void *dY, void *dX,
+                        void *dAg, void *dBg, void *dAu, void *dBu, void *dAd, void *dBd,
+                        void *ws, size_t ws_bytes, void *stream) {
+  LORA_TRY(check_dims(dtype, T, d, f, r));
+  WeightView wg, wu, wd;
+  LORA_TRY(check_weight(Wg, dtype, d, wg));
+  LORA_TRY(check_weight(Wu, dtype, d, wu));
+  LORA_TRY(check_weight(Wd, dtype, f, wd));
+  if (wg.q4 != wu.q4) return LORA_ERR_UNSUPPORTED;
+  LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd, dAg, dBg, dAu, dBu, dAd, dBd}));
+  LORA_TRY(check_tok_ptrs(T, {X, e_saved, g_saved, dY}));
+  if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
+  const size_t need = lora_workspace_bytes(LORA_OP_MLP_BWD, dtype, Wg->fmt, T, d, f, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  hipStream_t st = (hipStream_t)stream;
+  const float s = alpha / (float)r;
+  char *w = (char *)ws;
+
+  if (dtype == LORA_F32) {
+    float *h = (float *)w, *dh = h + T * f, *de = dh + T * f, *dg = de + T * f;
+    float *G = dg + T * f, *H = G + T * r;
+    const float *e = (const float *)e_saved, *g = (const float *)g_saved;
+    if (T > 0) {
+      hipLaunchKernelGGL(k_swiglu_f32, dim3(blocks_for(T * f)), dim3(256), 0, st, e, g, h, T * f);
+      HIP_TRY(hipGetLastError());
+    }
+    LORA_TRY(lin_bwd_f32(T, f, d, r, s, h, (const float *)wd.w, (const float *)Ad,
+                         (const float *)Bd, (const float *)dY, dh, false, (float *)dAd,
+                         (float *)dBd, G, H, st));
+    if (T > 0) {
+      hipLaunchKernelGGL(k_swiglu_bwd_f32, dim3(blocks_for(T * f)), dim3(256), 0, st, e, g, dh, de,
+                         dg, T * f);
+      HIP_TRY(hipGetLastError());
+    }
+    LORA_TRY(lin_bwd_f32(T, d, f, r, s, (const float *)X, (const float *)wg.w, (const float *)Ag,
+                         (const float *)Bg, de, (float *)dX, false, (float *)dAg, (float *)dBg, G,
+                         H, st));
+    return lin_bwd_f32(T, d, f, r, s, (const float *)X, (const float *)wu.w, (const float *)Au,
+                       (const float *)Bu, dg, (float *)dX, true, (float *)dAu, (float *)dBu, G, H,
+                       st);
+  }
+
+  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r);
+  const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
+  bf16_t *de = (bf16_t *)(w + pl.de), *dg = (bf16_t *)(w + pl.dg);
+  bf16_t *side_d_nn = (bf16_t *)(w + pl.side_d_nn), *epi_d_nn = (bf16_t *)(w + pl.epi_d_nn);
+  bf16_t *side_d_nt = (bf16_t *)(w + pl.side_d_nt);
+  bf16_t *side_gu_nn = (bf16_t *)(w + pl.side_gu_nn), *epi_gu_nn = (bf16_t *)(w + pl.epi_gu_nn);
+  bf16_t *side_gu_nt = (bf16_t *)(w + pl.side_gu_nt);
+  float *gd32 = (float *)(w + pl.gd32), *hd32 = (float *)(w + pl.hd32);
+  float *ggu32 = (float *)(w + pl.ggu32), *hgu32 = (float *)(w + pl.hgu32);
+  bf16_t *gdbf = (bf16_t *)(w + pl.gdbf), *ggubf = (bf16_t *)(w + pl.ggubf);
+  float *ntpart = (float *)(w + pl.ntpart), *tnpart = (float *)(w + pl.tnpart);
+  const bf16_t *Xb = (const bf16_t *)X, *dYb = (const bf16_t *)dY;
+  const bf16_t *eb = (const bf16_t *)e_saved, *gb = (const bf16_t *)g_saved;
+
+  LORA_TRY(build_side(side_d_nn, RS2, d, Bd, nullptr, r, d, 1, st));       // Bd^T [RS2 x d]
+  LORA_TRY(build_epi(epi_d_nn, f, RS2, Ad, nullptr, r, f, 1, st));         // Ad^T [f x RS2]
+  LORA_TRY(build_side(side_d_nt, RS2, f, Ad, nullptr, r, f, 0, st));       // Ad   [RS2 x f]
+  LORA_TRY(build_side(side_gu_nn, RS1, 2 * f, Bg, Bu, r, f, 1, st));       // blockdiag(Bg,Bu)^T
+  LORA_TRY(build_epi(epi_gu_nn, d, RS1, Ag, Au, r, d, 1, st));             // [Ag;Au]^T [d x RS1]
+  LORA_TRY(build_side(side_gu_nt, RS1, d, Ag, Au, r, d, 0, st));           // [Ag;Au] [RS1 x d]
+
+  if (T > 0) {
+    // 1. dh = dY Wd + s (dY Bd) Ad with the SwiGLU-derivative epilogue -> de, dg
+    const bool in2 = RS2 <= kInloopMaxRS;
+    if (!in2)
+      LORA_TRY(skinny_nt(RS2, false, T, d, dYb, dYb, d, d, nullptr, nullptr, side_d_nn, ntpart,
+                         gd32, gdbf, s, st));
+    GemmArgs a = gemm_base();
+    a.M = (int)T; a.N = (int)f; a.K = (int)d; a.ksplit = (int)d;
+    a.A0 = a.A1 = dYb; a.lda = d;
+    set_b(a, wd, wd); a.ldb = f;
+    a.side = side_d_nn; a.ld_side = d; a.rs = RS2; a.epi = epi_d_nn; a.s = s;
+    a.Ein = eb; a.Gin = gb; a.DE = de; a.DG = dg;
+    a.side_out = in2 ? gd32 : nullptr;
+    a.hglob = gdbf;
+    a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
+    LORA_TRY(run_gemm(LORA_KC_DOWN_BWD, true, wd.q4, in2 ? RS2 : 0, EPI_SWIGLU_BWD, a, st));
+    // 2. H_d = h Ad^T with h recomputed from e, g
+    LORA_TRY(skinny_nt(RS2, true, T, f, nullptr, nullptr, f, f, eb, gb, side_d_nt, ntpart, hd32,
+                       nullptr, 1.f, st));
+  }
+  // 3. dAd = s G_d^T h ; dBd = s dY^T H_d
+  LORA_TRY(skinny_tn(RS2, true, T, f, gd32, nullptr, nullptr, f, f, eb, gb, tnpart, r, s, 0,
+                     (bf16_t *)dAd, nullptr, f, st));
+  LORA_TRY(skinny_tn(RS2, false, T, d, hd32, dYb, dYb, d, d, nullptr, nullptr, tnpart, r, s, 1,
+                     (bf16_t *)dBd, nullptr, d, st));
+  if (T > 0) {
+    // 4. dX = de Wg + dg Wu + s [de Bg | dg Bu] [Ag; Au]
+    const bool in1 = RS1 <= kInloopMaxRS;
+    if (!dX || !in1)
+      LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, f, nullptr, nullptr, side_gu_nn, ntpart,
+                         ggu32, ggubf, s, st));
+    if (dX) {
+      GemmArgs b = gemm_base();
+      b.M = (int)T; b.N = (int)d; b.K = (int)(2 * f); b.ksplit = (int)f;
+      b.A0 = de; b.A1 = dg; b.lda = f;
+      set_b(b, wg, wu); b.ldb = d;
+      b.side = side_gu_nn; b.ld_side = 2 * f; b.rs = RS1; b.epi = epi_gu_nn; b.s = s;
+      b.C = (bf16_t *)dX; b.ldc = d;
+      b.side_out = in1 ? ggu32 : nullptr;
+      b.hglob = ggubf;
+      b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
+      LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, true, wg.q4, in1 ? RS1 : 0, EPI_STORE, b, st));
+    }
+    // 5. H_gu = X [Ag; Au]^T
+    LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,
+                       nullptr, 1.f, st));
+  }
+  // 6. [dAg; dAu] = s G_gu^T X ;  dBg, dBu = s [de | dg]^T H_gu (diagonal blocks)
+  LORA_TRY(skinny_tn(RS1, false, T, d, ggu32, Xb, Xb, d, d, nullptr, nullptr, tnpart, r, s, 0,
+                     (bf16_t *)dAg, (bf16_t *)dAu, d, st));
+  LORA_TRY(skinny_tn(RS1, false, T, 2 * f, hgu32, de, dg, f, f, nullptr, nullptr, tnpart, r, s, 1,
+                     (bf16_t *)dBg, (bf16_t *)dBu, f, st));
+  return LORA_OK;
+}
+
+int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absmax,
+                  const float *codebook, int blocksize, int out_dtype, void *out, void *stream) {
+  if (!codes || !absmax || !codebook || !out) return LORA_ERR_NULL_POINTER;
+  if (out_dtype != LORA_BF16 || blocksize != 64) return LORA_ERR_UNSUPPORTED;
+  if (n <= 0 || k <= 0 || (k % 64) || n > ((int64_t)1 << 24) || k > ((int64_t)1 << 24))
+    return LORA_ERR_BAD_SHAPE;
+  if (!aligned16(codes) || !aligned16(absmax) || !aligned16(codebook) || !aligned16(out))
+    return LORA_ERR_MISALIGNED;
+  const int64_t total = n * k;
+  hipLaunchKernelGGL(k_dequant4, dim3(blocks_for(total / 32)), dim3(256), 0, (hipStream_t)stream,
+                     codes, absmax, codebook, total, (bf16_t *)out);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,401 @@
+// Kernels around the main GEMM: rank-r skinny products for the adapter
+// gradients, their deterministic reductions, operand preparation, the
+// standalone 4-bit decode and the fp32 path.
+#pragma once
+#include "common.hpp"
+
+namespace lora {
+
+// ---------------------------------------------------------------------------
+// skinny NT:  part[ks][t][q] = sum_{k in chunk ks} Z[t][k] * SIDE[q][k]
+// Z is bf16 [T x K] (two sources split at K index `ksplit`, for [de | dg]),
+// or silu(E) * G recomputed from the saved gate/up activations (ZSWIGLU).
+// SIDE is bf16 [RS x K] zero-padded.  Memory-bound: every Z element is read
+// once; MFMA 16x16x32 does the rank-RS contraction.
+// ---------------------------------------------------------------------------
+struct SkinnyNTArgs {
+  int T, K, ksplit, kchunk;
+  const bf16_t *Z0, *Z1;
+  int64_t ldz;
+  const bf16_t *E, *G;      // ZSWIGLU sources, ld = ldz
+  const bf16_t *side;       // [RS x K]
+  float *part;              // [KS x T x RS]
+};
+
+template <int RS, bool ZSWIGLU>
+__global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
+  constexpr int NSB = RS / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, hi16 = lane >> 4;
+  const int t = blockIdx.x * 64 + wave * 16 + l16;
+  const int kbeg = blockIdx.y * a.kchunk;
+  const int kend = min(a.K, kbeg + a.kchunk);
+  f32x4 acc[NSB];
+#pragma unroll
+  for (int i = 0; i < NSB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool trow = t < a.T;
+  for (int k0 = kbeg; k0 < kend; k0 += 128) {
+    u32x4 zf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + 32 * u + 8 * hi16;
+      u32x4 v = {0, 0, 0, 0};
+      if (trow && k < kend) {
+        if constexpr (ZSWIGLU) {
+          const u32x4 e = gload16(a.E + (int64_t)t * a.ldz + k);
+          const u32x4 g = gload16(a.G + (int64_t)t * a.ldz + k);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = bf16lo(e[w]), e1 = bf16hi(e[w]);
+            v[w] = pack_bf16x2(e0 * sigmoidf_fast(e0) * bf16lo(g[w]),
+                               e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
+          }
+        } else {
+          const bf16_t *src = k < a.ksplit ? a.Z0 + (int64_t)t * a.ldz + k
+                                           : a.Z1 + (int64_t)t * a.ldz + (k - a.ksplit);
+          v = gload16(src);
+        }
+      }
+      zf[u] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + 32 * u + 8 * hi16;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        u32x4 sv = {0, 0, 0, 0};
+        if (k < kend) sv = gload16(a.side + (int64_t)(sb * 16 + l16) * a.K + k);
+        acc[sb] = mfma16(sv, zf[u], acc[sb]);
+      }
+    }
+  }
+  if (trow) {
+    float *dst = a.part + ((int64_t)blockIdx.y * a.T + t) * RS;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+      *reinterpret_cast<f32x4 *>(dst + sb * 16 + 4 * hi16) = acc[sb];
+  }
+}
+
+// out32[i] = sum_ks part[ks][i] (fixed order); outbf[i] = bf16(scale * out32[i])
+__global__ void k_reduce_side(const float *part, int ks, int64_t count, float scale,
+                              float *out32, bf16_t *outbf) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float s = 0.f;
+  for (int k = 0; k < ks; ++k) s += part[(int64_t)k * count + i];
+  if (out32) out32[i] = s;
+  if (outbf) {
+    const uint32_t w = pack_bf16x2(scale * s, 0.f);
+    outbf[i] = (bf16_t)(w & 0xFFFFu);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// skinny TN:  part[ts][q][n] = sum_{t in chunk ts} P[t][q] * Z[t][n]
+// P fp32 [T x RS]; Z bf16 [T x N] (two sources split at column `nsplit`,
+// for [de | dg]) or silu(E) * G (ZSWIGLU).  The Z tile is transposed 8x8 in
+// registers into a t-contiguous LDS layout so the contraction over tokens
+// runs on MFMA 16x16x32.
+// ---------------------------------------------------------------------------
+struct SkinnyTNArgs {
+  int T, N, nsplit, tchunk;
+  const float *P;
+  const bf16_t *Z0, *Z1;
+  int64_t ldz;
+  const bf16_t *E, *G;
+  float *part;              // [TS x RS x N]
+};
+
+template <int RS, bool ZSWIGLU>
+__global__ __launch_bounds__(256) void k_skinny_tn(const SkinnyTNArgs a) {
+  constexpr int NQB = RS / 16;
+  __shared__ __attribute__((aligned(16))) char zs[256 * 128];
+  __shared__ __attribute__((aligned(16))) char ps[RS * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, hi16 = lane >> 4;
+  const int n0 = blockIdx.x * 256;
+  const int tbeg = blockIdx.y * a.tchunk;
+  const int tend = min(a.T, tbeg + a.tchunk);
+  f32x4 acc[4][NQB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int kb = tid >> 5, nb = tid & 31;
+  for (int t0 = tbeg; t0 < tend; t0 += 64) {
+    u32x4 rows[8], cols[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + kb * 8 + i, n = n0 + nb * 8;
+      u32x4 v = {0, 0, 0, 0};
+      if (t < tend && n < a.N) {
+        if constexpr (ZSWIGLU) {
+          const u32x4 e = gload16(a.E + (int64_t)t * a.ldz + n);
+          const u32x4 g = gload16(a.G + (int64_t)t * a.ldz + n);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = bf16lo(e[w]), e1 = bf16hi(e[w]);
+            v[w] = pack_bf16x2(e0 * sigmoidf_fast(e0) * bf16lo(g[w]),
+                               e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
+          }
+        } else {
+          const bf16_t *src = n < a.nsplit ? a.Z0 + (int64_t)t * a.ldz + n
+                                           : a.Z1 + (int64_t)t * a.ldz + (n - a.nsplit);
+          v = gload16(src);
+        }
+      }
+      rows[i] = v;
+    }
+    transpose8x8(rows, cols);
+    u32x4 pv[(RS * 8 + 255) / 256];
+#pragma unroll
+    for (int u = 0; u < (RS * 8 + 255) / 256; ++u) {
+      const int idx = tid + 256 * u;
+      const int q = idx >> 3, tc = idx & 7;
+      u32x4 w = {0, 0, 0, 0};
+      if (q < RS) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int t = t0 + tc * 8 + 2 * h;
+          const float lo = t < tend ? a.P[(int64_t)t * RS + q] : 0.f;
+          const float hi = t + 1 < tend ? a.P[(int64_t)(t + 1) * RS + q] : 0.f;
+          w[h] = pack_bf16x2(lo, hi);
+        }
+      }
+      pv[u] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lds_write16(zs, swz_off(nb * 8 + j, kb), cols[j]);
+#pragma unroll
+    for (int u = 0; u < (RS * 8 + 255) / 256; ++u) {
+      const int idx = tid + 256 * u;
+      if ((idx >> 3) < RS) lds_write16(ps, swz_off(idx >> 3, idx & 7), pv[u]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      u32x4 za[4], pb[NQB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) za[i] = lds_read16(zs, swz_off(wave * 64 + i * 16 + l16, 4 * kq + hi16));
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) pb[j] = lds_read16(ps, swz_off(j * 16 + l16, 4 * kq + hi16));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) acc[i][j] = mfma16(za[i], pb[j], acc[i][j]);
+    }
+  }
+  // D[n][q]: lane holds 4 consecutive n (rows) of column q
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + wave * 64 + i * 16 + 4 * hi16;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) {
+      const int q = j * 16 + l16;
+      *reinterpret_cast<f32x4 *>(a.part + ((int64_t)blockIdx.y * RS + q) * a.N + n) = acc[i][j];
+    }
+  }
+}
+
+// Sum the TS partials of a TN product, scale, round once to bf16 and scatter
+// into the adapter-gradient layout.
+//   rowmajor (dA-type): rows q in [0, r) -> out0[q][n], q in [r, 2r) -> out1[q-r][n]
+//   transposed (dB-type): out0[n][q] for n < nsplit, q < r;
+//                         out1[n-nsplit][q-r] for n >= nsplit, r <= q < 2r
+struct ReduceTNArgs {
+  const float *part;
+  int ts, RS, N, r, nsplit;
+  float scale;
+  int transposed;
+  bf16_t *out0, *out1;
+};
+__global__ void k_reduce_tn(const ReduceTNArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t count = (int64_t)a.RS * a.N;
+  if (i >= count) return;
+  const int q = (int)(i / a.N), n = (int)(i % a.N);
+  bf16_t *dst = nullptr;
+  if (!a.transposed) {
+    if (q < a.r) dst = a.out0 + (int64_t)q * a.N + n;
+    else if (q < 2 * a.r && a.out1) dst = a.out1 + (int64_t)(q - a.r) * a.N + n;
+  } else {
+    if (n < a.nsplit) {
+      if (q < a.r) dst = a.out0 + (int64_t)n * a.r + q;
+    } else if (a.out1 && q >= a.r && q < 2 * a.r) {
+      dst = a.out1 + (int64_t)(n - a.nsplit) * a.r + (q - a.r);
+    }
+  }
+  if (!dst) return;
+  float s = 0.f;
+  for (int k = 0; k < a.ts; ++k) s += a.part[(int64_t)k * count + i];
+  const uint32_t w = pack_bf16x2(a.scale * s, 0.f);
+  *dst = (bf16_t)(w & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// operand preparation (tiny, bf16 copies with zero padding)
+// side[q][k], q < RS, k < K:
+//   !tr: q < r -> src0[q][k] (ld K); r <= q < 2r -> src1[q-r][k]
+//    tr: k < ksplit: q < r -> src0[k][q] (ld r);  k >= ksplit: r <= q < 2r ->
+//        src1[k-ksplit][q-r]
+// ---------------------------------------------------------------------------
+__global__ void k_build_side(bf16_t *dst, int RS, int K, const bf16_t *src0, const bf16_t *src1,
+                             int r, int ksplit, int tr) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)RS * K) return;
+  const int q = (int)(i / K), k = (int)(i % K);
+  bf16_t v = 0;
+  if (!tr) {
+    if (q < r) v = src0[(int64_t)q * K + k];
+    else if (src1 && q < 2 * r) v = src1[(int64_t)(q - r) * K + k];
+  } else {
+    if (k < ksplit) {
+      if (q < r) v = src0[(int64_t)k * r + q];
+    } else if (src1 && q >= r && q < 2 * r) {
+      v = src1[(int64_t)(k - ksplit) * r + (q - r)];
+    }
+  }
+  dst[i] = v;
+}
+
+// epi[row][q], row < rows, q < RS:
+//   !tr (from B [rows x r]): row < rsplit: q < r -> src0[row][q];
+//                            row >= rsplit: r <= q < 2r -> src1[row-rsplit][q-r]
+//    tr (from A [r x rows]): q < r -> src0[q][row]; r <= q < 2r -> src1[q-r][row]
+__global__ void k_build_epi(bf16_t *dst, int rows, int RS, const bf16_t *src0, const bf16_t *src1,
+                            int r, int rsplit, int tr) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows * RS) return;
+  const int row = (int)(i / RS), q = (int)(i % RS);
+  bf16_t v = 0;
+  if (!tr) {
+    if (row < rsplit) {
+      if (q < r) v = src0[(int64_t)row * r + q];
+    } else if (src1 && q >= r && q < 2 * r) {
+      v = src1[(int64_t)(row - rsplit) * r + (q - r)];
+    }
+  } else {
+    if (q < r) v = src0[(int64_t)q * rows + row];
+    else if (src1 && q < 2 * r) v = src1[(int64_t)(q - r) * rows + row];
+  }
+  dst[i] = v;
+}
+
+__global__ void k_fill_u16(bf16_t *dst, int64_t count, bf16_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) dst[i] = v;
+}
+__global__ void k_fill_f32(float *dst, int64_t count, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) dst[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// standalone 4-bit decode: each thread decodes 32 consecutive elements
+// (16 code bytes) and writes 64 bytes of bf16.  HBM-bound.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dequant4(const uint8_t *codes, const float *absmax,
+                                                  const float *codebook, int64_t total,
+                                                  bf16_t *out) {
+  __shared__ float2 cbt[256];
+  cbt[threadIdx.x] = make_float2(codebook[threadIdx.x & 15], codebook[threadIdx.x >> 4]);
+  __syncthreads();
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 32-element group
+  if (g * 32 >= total) return;
+  const u32x4 c = gload16(codes + g * 16);
+  const float am = absmax[(g * 32) >> 6];
+  u32x4 o[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float2 cv = cbt[(c[w] >> (8 * b)) & 0xFFu];
+      o[w][b] = pack_bf16x2(cv.x * am, cv.y * am);
+    }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) gstore16(out + g * 32 + 8 * w, o[w]);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: generic strided GEMM with fp32 FMA (no matrix cores, so the
+// arithmetic stays IEEE fp32):
+//   C[m][n] = alpha * sum_k A(m,k) B(k,n) + beta * C[m][n]
+//   A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn], C ld = ldc
+// 64 x 64 tiles, 256 threads with 4 x 4 outputs each, K step 16 via LDS.
+// ---------------------------------------------------------------------------
+struct F32GemmArgs {
+  int M, N, K;
+  const float *A;
+  int64_t sam, sak;
+  const float *B;
+  int64_t sbk, sbn;
+  float *C;
+  int64_t ldc;
+  float alpha, beta;
+};
+__global__ __launch_bounds__(256) void k_gemm_f32(const F32GemmArgs a) {
+  __shared__ float As[16][64 + 1];
+  __shared__ float Bs[16][64 + 1];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tr = tid / 16, tc = tid % 16;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < a.K; k0 += 16) {
+    for (int e = tid; e < 16 * 64; e += 256) {
+      const int kk = e / 64, mm = e % 64;
+      const int m = m0 + mm, k = k0 + kk;
+      As[kk][mm] = (m < a.M && k < a.K) ? a.A[(int64_t)m * a.sam + (int64_t)k * a.sak] : 0.f;
+      const int n = n0 + mm;
+      Bs[kk][mm] = (n < a.N && k < a.K) ? a.B[(int64_t)k * a.sbk + (int64_t)n * a.sbn] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][tr * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tc * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + tr * 4 + i;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tc * 4 + j;
+      if (n >= a.N) continue;
+      float *c = a.C + (int64_t)m * a.ldc + n;
+      const float v = a.alpha * acc[i][j];
+      *c = (a.beta == 0.f) ? v : v + a.beta * *c;
+    }
+  }
+}
+
+// h = silu(e) * g (fp32, accurate exp)
+__global__ void k_swiglu_f32(const float *e, const float *g, float *h, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const float z = e[i];
+  h[i] = z / (1.0f + expf(-z)) * g[i];
+}
+// de = dh g sig (1 + e (1 - sig)), dg = dh e sig (fp32)
+__global__ void k_swiglu_bwd_f32(const float *e, const float *g, const float *dh, float *de,
+                                 float *dg, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const float z = e[i], sg = 1.0f / (1.0f + expf(-z));
+  de[i] = dh[i] * g[i] * sg * (1.0f + z * (1.0f - sg));
+  dg[i] = dh[i] * z * sg;
+}
+
+}  // namespace lora

@@ -1,0 +1,92 @@
+// Device building blocks shared by the liblora kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t bf16_t;  // bf16 storage (bit pattern)
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16x2 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  f32x2_t v = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// --------------------------------------------------------------- MFMA -----
+__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------ LDS tile layout ----
+// A tile row holds 64 bf16 (128 B) = 8 chunks of 16 B.  The chunk index is
+// XOR-swizzled with (row ^ row>>3) & 7 so that both the MFMA fragment reads
+// (consecutive rows, same chunk) and the transposing writes of the NN loader
+// (rows 8 apart, same chunk) spread over distinct banks.
+__device__ __forceinline__ uint32_t swz_off(uint32_t row, uint32_t chunk) {
+  return row * 128u + ((chunk ^ ((row ^ (row >> 3)) & 7u)) << 4);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char *base, uint32_t off) {
+  return *reinterpret_cast<const u32x4 *>(base + off);
+}
+__device__ __forceinline__ void lds_write16(char *base, uint32_t off, const u32x4 &v) {
+  *reinterpret_cast<u32x4 *>(base + off) = v;
+}
+
+// -------------------------------------------------------- global access ----
+__device__ __forceinline__ u32x4 gload16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x2 gload8(const void *p) {
+  return *reinterpret_cast<const u32x2 *>(p);
+}
+__device__ __forceinline__ void gstore8(void *p, const u32x2 &v) {
+  *reinterpret_cast<u32x2 *>(p) = v;
+}
+__device__ __forceinline__ void gstore16(void *p, const u32x4 &v) {
+  *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// 8x8 transpose of bf16: in[i] holds row i (8 values, element j in 16-bit
+// lane j), out[j] holds column j (element i = in[i][j]).
+__device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int dw = j >> 1;
+    // selector picks the low (j even) or high (j odd) halves of two words
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // out[j] dword p = (in[2p][j], in[2p+1][j])
+      out[j][p] = __builtin_amdgcn_perm(in[2 * p + 1][dw], in[2 * p][dw], sel);
+    }
+  }
+}
+
+// fast logistic with the hardware exp2 / reciprocal
+__device__ __forceinline__ float sigmoidf_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+}  // namespace lora

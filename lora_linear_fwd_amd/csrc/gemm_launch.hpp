@@ -1,0 +1,54 @@
+// Instantiation + launch of the LoRA GEMM for one B-operand form.
+#pragma once
+#include <atomic>
+#include "gemm_lora.hpp"
+
+namespace lora {
+
+// Raise the dynamic-LDS limit of a kernel once per device (the kernels need
+// more than the 64 KB default).
+template <typename Kern>
+inline hipError_t ensure_lds(Kern kern, size_t bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
+template <int BMODE, int RS, int EPI, int SMODE>
+inline hipError_t launch_one(const GemmArgs &a, hipStream_t st) {
+  static std::atomic<uint64_t> done{0};
+  constexpr size_t lds = gemm_lds_bytes<BMODE, RS, EPI, SMODE>();
+  auto kern = k_lora_gemm<BMODE, RS, EPI, SMODE>;
+  hipError_t e = ensure_lds(kern, lds, done);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), lds, st, a);
+  return hipGetLastError();
+}
+
+// rs_inloop: 16/32/64 = side product accumulated in the K loop; 0 = the
+// scaled side product is read from a.hglob (width a.rs).
+template <int BMODE, int EPI>
+inline hipError_t launch_gemm_t(int rs_inloop, const GemmArgs &a, hipStream_t st) {
+  switch (rs_inloop) {
+    case 16: return launch_one<BMODE, 16, EPI, SIDE_INLOOP>(a, st);
+    case 32: return launch_one<BMODE, 32, EPI, SIDE_INLOOP>(a, st);
+    case 64: return launch_one<BMODE, 64, EPI, SIDE_INLOOP>(a, st);
+    case 0: return launch_one<BMODE, 16, EPI, SIDE_GLOBAL>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_nt(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nt_q4(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nn(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nn_q4(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
+
+}  // namespace lora

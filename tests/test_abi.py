@@ -1,0 +1,139 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/liblora.h declares, and rejects bad arguments before any HIP
+call (so these calls are safe on a machine without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import lora_linear_fwd_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "liblora.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="liblora not built")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    fns = header_functions()
+    for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
+                 "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_workspace_bytes",
+                 "lora_strerror", "lora_abi_version"):
+        assert name in fns
+    assert set(fns) == set(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(lora_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(header_functions()) <= exported
+    lib = L.lib()
+    for name in header_functions():
+        assert hasattr(lib, name)
+
+
+def test_version_and_strerror():
+    assert L.abi_version() == 1
+    assert L.strerror(0) == "ok"
+    for s in range(1, 7):
+        assert L.strerror(s) and L.strerror(s) != "unknown status"
+    assert L.strerror(99) == "unknown status"
+
+
+def test_workspace_bytes_rules():
+    wb = L.workspace_bytes
+    assert wb(L.OP_LINEAR_FWD, L.LORA_BF16, 0, 8192, 4096, 4096, 16) > 0
+    assert wb(L.OP_LINEAR_FWD, L.LORA_BF16, 0, 8192, 4096, 4096, 0) == 0
+    assert wb(L.OP_LINEAR_FWD, L.LORA_BF16, 0, 8192, 4096, 4096, 129) == 0
+    assert wb(L.OP_LINEAR_FWD, 7, 0, 8192, 4096, 4096, 16) == 0
+    # MLP forward holds h [T x f] bf16 in the workspace
+    assert wb(L.OP_MLP_FWD, L.LORA_BF16, 0, 8192, 4096, 14336, 16) >= 8192 * 14336 * 2
+    # MLP backward holds de, dg
+    assert wb(L.OP_MLP_BWD, L.LORA_BF16, 0, 8192, 4096, 14336, 16) >= 2 * 8192 * 14336 * 2
+    assert wb(L.OP_LINEAR_BWD, L.LORA_F32, 0, 256, 512, 512, 8) == 2 * 256 * 8 * 4
+
+
+# fake, aligned, non-null host addresses: every call below fails validation
+# before touching them
+_buf = (ctypes.c_uint8 * 4096)()
+_base = (ctypes.addressof(_buf) + 255) & ~255
+P = ctypes.c_void_p(_base)
+P_MIS = ctypes.c_void_p(_base + 2)
+
+
+def _w(fmt=0, blocksize=0, w=P, codes=None, absmax=None, codebook=None):
+    return L.LoraWeightC(fmt, blocksize, w, codes, absmax, codebook)
+
+
+def fwd(dtype=1, T=16, k=64, n=64, r=8, X=P, W=None, A=P, B=P, Y=P, ws=P, wsb=1 << 30):
+    W = W or _w()
+    return L.lib().lora_linear_fwd(dtype, T, k, n, r, 16.0, X, ctypes.byref(W), A, B, Y, ws,
+                                   wsb, None)
+
+
+def test_linear_fwd_validation_codes():
+    assert fwd(X=None) == 1
+    assert fwd(Y=None) == 1
+    assert fwd(W=_w(w=None)) == 1
+    assert fwd(k=60) == 2           # bf16 rows must be 16-byte multiples
+    assert fwd(n=12) == 2
+    assert fwd(T=-1) == 2
+    assert fwd(k=0) == 2
+    assert fwd(r=0) == 2
+    assert fwd(r=129) == 3
+    assert fwd(dtype=5) == 3
+    assert fwd(X=P_MIS) == 5
+    assert fwd(wsb=0) == 4
+    assert fwd(ws=None) == 1
+    # 4-bit weights: bf16 only, blocksize 64, k % 64 == 0, all three pointers
+    q4 = _w(1, 64, None, P, P, P)
+    assert fwd(dtype=0, W=q4) == 3
+    assert fwd(W=_w(1, 32, None, P, P, P)) == 3
+    assert fwd(k=72, W=q4) == 2
+    assert fwd(W=_w(1, 64, None, P, None, P)) == 1
+    assert fwd(W=_w(7)) == 3
+
+
+def test_linear_bwd_validation_codes():
+    W = _w()
+    call = lambda **kw: L.lib().lora_linear_bwd(
+        kw.get("dtype", 1), 16, 64, 64, 8, 16.0, P, ctypes.byref(W), P, P, kw.get("dY", P),
+        kw.get("dX", P), kw.get("dA", P), kw.get("dB", P), kw.get("flags", 0), P, 1 << 30, None)
+    assert call(dY=None) == 1
+    assert call(dA=None) == 1
+    assert call(dX=P_MIS) == 5
+    assert call(flags=2) == 3
+
+
+def test_mlp_validation_codes():
+    W = _w()
+    args = lambda **kw: [1, kw.get("T", 16), kw.get("d", 64), kw.get("f", 128), 8, 16.0, P,
+                         ctypes.byref(W), P, P, ctypes.byref(W), P, P, ctypes.byref(W), P, P]
+    lib = L.lib()
+    assert lib.lora_swiglu_mlp_fwd(*args(d=60), P, P, P, P, 1 << 30, None) == 2
+    assert lib.lora_swiglu_mlp_fwd(*args(), None, P, P, P, 1 << 30, None) == 1
+    assert lib.lora_swiglu_mlp_fwd(*args(), P, P, P, P, 10, None) == 4
+    assert lib.lora_swiglu_mlp_bwd(*args(), P, P, P, P, P, P, P, P, None, P, P, 1 << 30,
+                                   None) == 1
+    q4 = _w(1, 64, None, P, P, P)
+    mixed = [1, 16, 64, 128, 8, 16.0, P, ctypes.byref(q4), P, P, ctypes.byref(W), P, P,
+             ctypes.byref(W), P, P]
+    assert lib.lora_swiglu_mlp_fwd(*mixed, P, P, P, P, 1 << 30, None) == 3
+
+
+def test_dequant4_validation_codes():
+    lib = L.lib()
+    assert lib.lora_dequant4(16, 128, None, P, P, 64, 1, P, None) == 1
+    assert lib.lora_dequant4(16, 100, P, P, P, 64, 1, P, None) == 2
+    assert lib.lora_dequant4(16, 128, P, P, P, 32, 1, P, None) == 3
+    assert lib.lora_dequant4(16, 128, P, P, P, 64, 0, P, None) == 3
+    assert lib.lora_dequant4(16, 128, P_MIS, P, P, 64, 1, P, None) == 5
