@@ -68,6 +68,42 @@ __device__ __forceinline__ void gstore16(void *p, const u32x4 &v) {
   *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// ----------------------------------------------------- buffer resources ----
+// Raw buffer descriptor (gfx9 layout) over `base`, `bytes` long.  Loads at
+// offsets >= bytes return zeros, which the kernels use for every tail: an
+// invalid lane gets the offset kOOB.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr uint32_t kMaxRecords = 0x7FFFFF00u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane straight into LDS: lane l writes lds_wave_base + 16 l
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char *lds_wave_base, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+}
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, source lane s supplies the 8-byte row at its address; lane i
+// receives element i%4 of the rows of lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.
+// With source lane s pointing at W[k0 + s/4][n0 + 4 (s%4) .. +3] of a
+// row-major [K x N] tile, lane i gets W[k0 .. k0+3][n0 + i].
+__device__ __forceinline__ u32x2 lds_read_tr8(const char *base, uint32_t off) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)((__attribute__((address_space(3))) char *)base + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // 8x8 transpose of bf16: in[i] holds row i (8 values, element j in 16-bit
 // lane j), out[j] holds column j (element i = in[i][j]).
 __device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {

@@ -86,14 +86,35 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int 
   tn = in_group / gsz;
 }
 
-template <int BMODE, int RS, int SMODE>
+// Instruction-scheduling groups (masks: 0x008 MFMA, 0x100 LDS read).
+template <int MASK, int COUNT>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (COUNT > 0) __builtin_amdgcn_sched_group_barrier(MASK, COUNT, 0);
+}
+// COUNT pairs of (one MFMA, one LDS read)
+template <int COUNT>
+__device__ __forceinline__ void sched_pairs() {
+#pragma unroll
+  for (int i = 0; i < COUNT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// NN weight tiles are kept in their natural [64 K-rows x 256 N-cols] layout
+// (512-byte rows); the 16-byte chunk index is XORed with 4 (row % 4) so the
+// four rows one 16-lane group reads with ds_read_b64_tr_b16 fall in
+// different banks.
+__device__ __forceinline__ uint32_t nn_off(uint32_t row, uint32_t chunk) {
+  return row * 512u + ((chunk ^ ((row & 3u) << 2)) << 4);
+}
+
+template <int BMODE>
 struct Stage {
-  u32x4 xa[8];
-  u32x4 wb[(BMODE == B_NT || BMODE == B_NN) ? 8 : 1];
+  // register-staged B operand (the DMA-loaded forms keep nothing here)
   u32x4 qc[(BMODE == B_NT_Q4) ? 2 : 1];
   uint32_t qn[(BMODE == B_NN_Q4) ? 8 : 1];
   float qs[(BMODE == B_NN_Q4) ? 8 : 1];
-  u32x4 sd[(SMODE == SIDE_INLOOP && RS * 8 > NTHREADS) ? (RS * 8 / NTHREADS) : 1];
 };
 
 template <int BMODE, int RS, int EPI, int SMODE>
@@ -101,14 +122,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
   constexpr bool Q4 = (BMODE == B_NT_Q4 || BMODE == B_NN_Q4);
-  constexpr bool NN = (BMODE == B_NN || BMODE == B_NN_Q4);
   constexpr bool INLOOP = (SMODE == SIDE_INLOOP);
+  constexpr bool NN = (BMODE == B_NN || BMODE == B_NN_Q4);
   constexpr int XS = BM * BK * 2, WS = BN * BK * 2;
   constexpr int SS = INLOOP ? RS * BK * 2 : 0;
   constexpr int STAGE = XS + WS + SS;
   constexpr int NSB = INLOOP ? RS / 16 : 1;   // side row blocks of 16
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hi32 = lane >> 5;
   const int l16 = lane & 15, hi16 = lane >> 4;
@@ -116,7 +138,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   int tm, tn;
   map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int M = p.M, N = p.N, K = p.K;
+  const int M = p.M, N = p.N, K = p.K, ksplit = p.ksplit;
 
   float2 *cbt = reinterpret_cast<float2 *>(smem + 2 * STAGE);   // 4-bit pair table
   if constexpr (Q4) {
@@ -125,105 +147,175 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     cbt[tid] = make_float2(p.codebook[tid & 15], p.codebook[tid >> 4]);
   }
 
-  // ------------------------------------------------ global -> registers
-  auto load_stage = [&](Stage<BMODE, RS, SMODE> &st, int kt) {
-    const int k0 = kt * BK;
-    // A_op tile: 256 rows x 8 chunks, thread takes chunk (tid&7) of 8 rows
+  // ---------------------------------------------------- DMA lane geometry
+  // DMA instruction u of wave w fills tile rows 8b..8b+7 (b = 4u + w); lane
+  // l lands in row 8b + l/8 at LDS chunk l%8, which holds logical K chunk
+  // c = (l%8) ^ swz(row) = (l%8) ^ (l/8) ^ (b%8).
+  const int lr = lane >> 3;
+  const int c0 = (lane & 7) ^ lr;
+  // A_op: byte offsets relative to row m0 (kOOB for rows past M)
+  const bf16_t *Abase = p.A0 + (int64_t)m0 * p.lda;
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Abase, kMaxRecords);
+  // A1 - A0 - 2 ksplit: added to offsets of columns >= ksplit
+  const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
+  uint32_t aoff[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 3) + 32 * i, c = tid & 7;
-      const int gm = m0 + row, gk = k0 + c * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (gm < M && gk < K) {
-        const bf16_t *src = gk < p.ksplit ? p.A0 + (int64_t)gm * p.lda + gk
-                                          : p.A1 + (int64_t)gm * p.lda + (gk - p.ksplit);
-        v = gload16(src);
-      }
-      st.xa[i] = v;
+  for (int u = 0; u < 8; ++u) {
+    const int b = 4 * u + wave, row = 8 * b + lr, c = c0 ^ (b & 7);
+    aoff[u] = (m0 + row < M) ? (uint32_t)(row * p.lda * 2 + c * 16) : kOOB;
+  }
+  uint32_t boff[8];
+  __amdgpu_buffer_rsrc_t rsB0, rsB1;
+  if constexpr (BMODE == B_NT) {
+    if constexpr (GU) {
+      rsB0 = make_rsrc(p.B0 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
+      rsB1 = make_rsrc(p.B1 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
+    } else {
+      rsB0 = rsB1 = make_rsrc(p.B0 + (int64_t)n0 * p.ldb, kMaxRecords);
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = 4 * u + wave, row = 8 * b + lr, c = c0 ^ (b & 7);
+      if constexpr (GU) {
+        const int jl = (row >> 7) * 64 + (row & 63);
+        boff[u] = (tn * 128 + jl < p.gu_f) ? (uint32_t)(jl * p.ldb * 2 + c * 16) : kOOB;
+      } else {
+        boff[u] = (n0 + row < N) ? (uint32_t)(row * p.ldb * 2 + c * 16) : kOOB;
+      }
+    }
+  } else if constexpr (BMODE == B_NN) {
+    // DMA instruction u of wave w fills K-rows 2b, 2b+1 (b = 4u + w); lane l
+    // lands in row 2b + l/32 at 16-byte chunk l%32, holding logical chunk
+    // (l%32) ^ 4 (row%4).  Rows >= ksplit come from B1.
+    rsB0 = make_rsrc(p.B0 + n0, kMaxRecords);
+    rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = 4 * u + wave, row = 2 * b + (lane >> 5);
+      const int c = (lane & 31) ^ ((row & 3) << 2);
+      boff[u] = (n0 + 8 * c < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + c * 16) : kOOB;
+    }
+  } else if constexpr (BMODE == B_NT_Q4) {
+    // one weight row per thread; gate rows for waves 0, 2 and up rows for
+    // waves 1, 3 when the tile interleaves gate/up
+    const int row = tid;
+    int jl = row, jg = n0 + row;
+    bool up = false;
+    if constexpr (GU) {
+      jl = (row >> 7) * 64 + (row & 63);
+      jg = tn * 128 + jl;
+      up = (row >> 6) & 1;
+    }
+    const int64_t grow0 = GU ? (int64_t)tn * 128 : (int64_t)n0;
+    const uint8_t *q = up ? p.Q1 : p.Q0;
+    const float *sc = up ? p.S1 : p.S0;
+    rsB0 = make_rsrc(q + grow0 * (K / 2), kMaxRecords);
+    rsB1 = make_rsrc(sc + grow0 * (K / 64), kMaxRecords);
+    const bool ok = GU ? (jg < p.gu_f) : (jg < N);
+    boff[0] = ok ? (uint32_t)(jl * (K / 2)) : kOOB;       // codes
+    boff[1] = ok ? (uint32_t)(jl * (K / 64) * 4) : kOOB;  // absmax
+  }
+  // NN: byte offset of this lane's transpose-read row for n-block i at
+  // K sub-step 0 (rows kk*16 + 4t are reached with immediate offsets)
+  uint32_t trb[4];
+  if constexpr (NN) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int krow0 = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nl = wn * 128 + i * 32 + 16 * (g & 1) + 4 * (sl & 3);
+      trb[i] = nn_off(krow0, nl >> 3) + ((nl >> 2) & 1) * 8;
+    }
+  }
+  uint32_t soff_side[(RS / 8 + 3) / 4];
+  __amdgpu_buffer_rsrc_t rsS;
+  if constexpr (INLOOP) {
+    rsS = make_rsrc(p.side, kMaxRecords);
+#pragma unroll
+    for (int u = 0; u < (RS / 8 + 3) / 4; ++u) {
+      const int b = 4 * u + wave, row = 8 * b + lr, c = c0 ^ (b & 7);
+      soff_side[u] = (uint32_t)(row * p.ld_side * 2 + c * 16);
+    }
+  }
+
+  // ------------------------------------------------ K tile kt -> stage
+  // Issues the DMA loads of tile kt into `stage` and fills the register
+  // staging of the non-DMA operand forms.
+  auto issue_tile = [&](Stage<BMODE> &st, int kt, char *stage) {
+    const int k0 = kt * BK;
+    char *Xs = stage, *Ws = stage + XS, *Ss = stage + XS + WS;
+    const bool full = (k0 + BK <= K) && (k0 + BK <= ksplit || k0 >= ksplit);
+    if (full) {
+      const uint32_t sa = 2u * (uint32_t)k0 + (k0 >= ksplit ? dA1 : 0u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dma16(rsA, Xs + (4 * u + wave) * 1024, aoff[u], sa);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int b = 4 * u + wave, col = k0 + 8 * (c0 ^ (b & 7));
+        const uint32_t v = (aoff[u] != kOOB && col < K)
+                               ? aoff[u] + 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u)
+                               : kOOB;
+        dma16(rsA, Xs + b * 1024, v, 0);
+      }
+    }
+    const bool kfull = k0 + BK <= K;
     if constexpr (BMODE == B_NT) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = (tid >> 3) + 32 * i, c = tid & 7;
-        const int gk = k0 + c * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if constexpr (GU) {
-          const int half = row >> 7, sub = row & 127;
-          const int j = tn * 128 + half * 64 + (sub & 63);
-          if (j < p.gu_f && gk < K)
-            v = gload16(((sub >> 6) ? p.B1 : p.B0) + (int64_t)j * p.ldb + gk);
-        } else {
-          const int gn = n0 + row;
-          if (gn < N && gk < K) v = gload16(p.B0 + (int64_t)gn * p.ldb + gk);
+      for (int u = 0; u < 8; ++u) {
+        const int b = 4 * u + wave;
+        const __amdgpu_buffer_rsrc_t r = (GU && ((b >> 3) & 1)) ? rsB1 : rsB0;
+        uint32_t v = boff[u];
+        if (!kfull) {
+          const int col = k0 + 8 * (c0 ^ (b & 7));
+          if (col >= K) v = kOOB;
         }
-        st.wb[i] = v;
+        dma16(r, Ws + b * 1024, v, 2u * (uint32_t)k0);
       }
     } else if constexpr (BMODE == B_NT_Q4) {
-      // one weight row per thread: 64 codes (32 bytes) + one absmax (K % 64 == 0)
-      const int row = tid;
-      int64_t grow = -1;
-      const uint8_t *q = p.Q0;
-      const float *sc = p.S0;
-      if constexpr (GU) {
-        const int half = row >> 7, sub = row & 127;
-        const int j = tn * 128 + half * 64 + (sub & 63);
-        if (j < p.gu_f) grow = j;
-        if (sub >> 6) { q = p.Q1; sc = p.S1; }
-      } else {
-        if (n0 + row < N) grow = n0 + row;
-      }
-      u32x4 c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
-      float am = 0.f;
-      if (grow >= 0) {
-        const uint8_t *src = q + grow * (int64_t)(K / 2) + k0 / 2;
-        c0 = gload16(src);
-        c1 = gload16(src + 16);
-        am = sc[(grow * (int64_t)K + k0) >> 6];
-      }
-      st.qc[0] = c0;
-      st.qc[1] = c1;
-      st.qs[0] = am;
+      st.qc[0] = bload16(rsB0, boff[0], (uint32_t)k0 / 2);
+      st.qc[1] = bload16(rsB0, boff[0], (uint32_t)k0 / 2 + 16);
+      st.qs[0] = __uint_as_float(bload4(rsB1, boff[1], (uint32_t)k0 / 16));
     } else if constexpr (BMODE == B_NN) {
-      const int kb = tid >> 5, nb = tid & 31;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int gk = k0 + kb * 8 + i, gn = n0 + nb * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (gk < K && gn < N) {
-          const bf16_t *src = gk < p.ksplit ? p.B0 + (int64_t)gk * p.ldb + gn
-                                            : p.B1 + (int64_t)(gk - p.ksplit) * p.ldb + gn;
-          v = gload16(src);
-        }
-        st.wb[i] = v;
+      for (int u = 0; u < 8; ++u) {
+        const int b = 4 * u + wave;
+        const int kr = k0 + 2 * b;            // first of the two rows (even)
+        const bool second = kr >= ksplit;     // ksplit is even: no straddle
+        uint32_t v = boff[u];
+        if (!kfull && kr + (lane >> 5) >= K) v = kOOB;
+        dma16(second ? rsB1 : rsB0, Ws + b * 1024, v,
+              (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2));
       }
     } else {  // B_NN_Q4: weight rows gk, 8 columns gn.. (4 bytes of codes)
       const int kb = tid >> 5, nb = tid & 31;
+      const int gn = n0 + nb * 8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int gk = k0 + kb * 8 + i, gn = n0 + nb * 8;
-        uint32_t cw = 0;
-        float am = 0.f;
-        if (gk < K && gn < N) {
-          const bool first = gk < p.ksplit;
-          const int64_t wr = first ? gk : gk - p.ksplit;
-          const uint8_t *q = first ? p.Q0 : p.Q1;
-          const float *sc = first ? p.S0 : p.S1;
-          cw = *reinterpret_cast<const uint32_t *>(q + wr * (int64_t)(N / 2) + gn / 2);
-          am = sc[(wr * (int64_t)N + gn) >> 6];
-        }
-        st.qn[i] = cw;
-        st.qs[i] = am;
+        const int gk = k0 + kb * 8 + i;
+        const bool ok = gk < K && gn < N;
+        const bool first = gk < ksplit;
+        const int64_t wr = first ? gk : gk - ksplit;
+        const uint8_t *q = (first ? p.Q0 : p.Q1) + wr * (int64_t)(N / 2) + gn / 2;
+        const float *sc = (first ? p.S0 : p.S1) + ((wr * (int64_t)N + gn) >> 6);
+        const uint32_t cw = *reinterpret_cast<const uint32_t *>(ok ? q : p.Q0);
+        const float am = *(ok ? sc : p.S0);
+        st.qn[i] = ok ? cw : 0u;
+        st.qs[i] = ok ? am : 0.f;
       }
     }
     if constexpr (INLOOP) {
 #pragma unroll
-      for (int u = 0; u < (RS * 8 + NTHREADS - 1) / NTHREADS; ++u) {
-        const int q = tid + NTHREADS * u;
-        const int row = q >> 3, c = q & 7;
-        const int gk = k0 + c * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (row < RS && gk < K) v = gload16(p.side + (int64_t)row * p.ld_side + gk);
-        st.sd[u] = v;
+      for (int u = 0; u < (RS / 8 + 3) / 4; ++u) {
+        const int b = 4 * u + wave;
+        if (b < RS / 8) {
+          uint32_t v = soff_side[u];
+          if (!kfull) {
+            const int col = k0 + 8 * (c0 ^ (b & 7));
+            if (col >= K) v = kOOB;
+          }
+          dma16(rsS, Ss + b * 1024, v, 2u * (uint32_t)k0);
+        }
       }
     }
   };
@@ -239,40 +331,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     return o;
   };
 
-  // ------------------------------------------------ registers -> LDS
-  auto store_stage = [&](Stage<BMODE, RS, SMODE> &st, char *stage) {
-    char *Xs = stage, *Ws = stage + XS, *Ss = stage + XS + WS;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      lds_write16(Xs, swz_off((tid >> 3) + 32 * i, tid & 7), st.xa[i]);
-    if constexpr (BMODE == B_NT) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        lds_write16(Ws, swz_off((tid >> 3) + 32 * i, tid & 7), st.wb[i]);
-    } else if constexpr (BMODE == B_NT_Q4) {
+  // ------------------------------------ register staging -> LDS (non-DMA)
+  auto commit_tile = [&](Stage<BMODE> &st, char *stage) {
+    char *Ws = stage + XS;
+    if constexpr (BMODE == B_NT_Q4) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const u32x4 &src = st.qc[c >> 2];
         lds_write16(Ws, swz_off(tid, c), decode4(src[c & 3], st.qs[0]));
       }
-    } else {
-      u32x4 rows[8], cols[8];
+    } else if constexpr (BMODE == B_NN_Q4) {
       const int kb = tid >> 5, nb = tid & 31;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (BMODE == B_NN) rows[i] = st.wb[i];
-        else rows[i] = decode4(st.qn[i], st.qs[i]);
-      }
-      transpose8x8(rows, cols);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lds_write16(Ws, swz_off(nb * 8 + j, kb), cols[j]);
-    }
-    if constexpr (INLOOP) {
-#pragma unroll
-      for (int u = 0; u < (RS * 8 + NTHREADS - 1) / NTHREADS; ++u) {
-        const int q = tid + NTHREADS * u;
-        if (q < RS * 8) lds_write16(Ss, swz_off(q >> 3, q & 7), st.sd[u]);
-      }
+      for (int i = 0; i < 8; ++i)
+        lds_write16(Ws, nn_off(kb * 8 + i, nb), decode4(st.qn[i], st.qs[i]));
     }
   };
 
@@ -290,31 +362,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     for (int b = 0; b < 4; ++b) sacc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nkt = (K + BK - 1) / BK;
-  Stage<BMODE, RS, SMODE> st;
+  Stage<BMODE> st;
   if (Q4) __syncthreads();  // pair table visible before the first decode
-  load_stage(st, 0);
-  store_stage(st, smem);
+  issue_tile(st, 0, smem);
+  commit_tile(st, smem);
+  wait_vmem();
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const char *cur = smem + (kt & 1) * STAGE;
-    if (kt + 1 < nkt) load_stage(st, kt + 1);
+    if (kt + 1 < nkt) issue_tile(st, kt + 1, smem + ((kt + 1) & 1) * STAGE);
     {
+      // Fragment reads of sub-step kk+1 (and of the side pass during the
+      // last sub-step) are in flight while the 16 MFMAs of sub-step kk run;
+      // the sched_group_barrier pattern below pins that interleave.
       const char *Xs = cur, *Ws = cur + XS;
       u32x4 fa[2][4], fb[2][4];
+      u32x4 sa[2][NSB], xb[2][4];
+      auto read_frags = [&](int kk, int bsel) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[0][i] = lds_read16(Ws, swz_off(wn * 128 + i * 32 + l32, hi32));
-        fb[0][i] = lds_read16(Xs, swz_off(wm * 128 + i * 32 + l32, hi32));
-      }
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (NN) {
+            const u32x2 lo = lds_read_tr8(Ws, trb[i] + kk * 16 * 512);
+            const u32x2 hi = lds_read_tr8(Ws, trb[i] + (kk * 16 + 4) * 512);
+            fa[bsel][i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          } else {
+            fa[bsel][i] = lds_read16(Ws, swz_off(wn * 128 + i * 32 + l32, 2 * kk + hi32));
+          }
+          fb[bsel][i] = lds_read16(Xs, swz_off(wm * 128 + i * 32 + l32, 2 * kk + hi32));
+        }
+      };
+      read_frags(0, 0);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int cb = kk & 1, nb = cb ^ 1;
         if (kk < 3) {
+          read_frags(kk + 1, nb);
+        } else if constexpr (INLOOP) {
+          const char *Ss = cur + XS + WS;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            fa[nb][i] = lds_read16(Ws, swz_off(wn * 128 + i * 32 + l32, 2 * (kk + 1) + hi32));
-            fb[nb][i] = lds_read16(Xs, swz_off(wm * 128 + i * 32 + l32, 2 * (kk + 1) + hi32));
+          for (int kq = 0; kq < 2; ++kq) {
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+              sa[kq][sb] = lds_read16(Ss, swz_off(sb * 16 + l16, 4 * kq + hi16));
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              xb[kq][mb] = lds_read16(Xs, swz_off(wm * 128 + wn * 64 + mb * 16 + l16, 4 * kq + hi16));
           }
         }
 #pragma unroll
@@ -323,24 +416,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[cb][i], fb[cb][j], acc[i][j]);
       }
       if constexpr (INLOOP) {
-        const char *Ss = cur + XS + WS;
 #pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          u32x4 sa[NSB], xb[4];
-#pragma unroll
-          for (int sb = 0; sb < NSB; ++sb)
-            sa[sb] = lds_read16(Ss, swz_off(sb * 16 + l16, 4 * kq + hi16));
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-            xb[mb] = lds_read16(Xs, swz_off(wm * 128 + wn * 64 + mb * 16 + l16, 4 * kq + hi16));
+        for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
           for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) sacc[sb][mb] = mfma16(sa[sb], xb[mb], sacc[sb][mb]);
-        }
+            for (int mb = 0; mb < 4; ++mb) sacc[sb][mb] = mfma16(sa[kq][sb], xb[kq][mb], sacc[sb][mb]);
       }
+      // schedule: the first sub-step's reads, then per sub-step 16 MFMAs
+      // with the next sub-step's reads interleaved one per MFMA
+      constexpr int kReads = NN ? 12 : 8;
+      constexpr int kSideReads = INLOOP ? 2 * (NSB + 4) : 0;
+      sched_group<0x100, kReads>();
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+        sched_pairs<kReads>();
+        sched_group<0x008, 16 - kReads>();
+      }
+      sched_pairs<kSideReads>();
+      sched_group<0x008, 16 - kSideReads + (INLOOP ? 8 * NSB : 0)>();
     }
-    if (kt + 1 < nkt) store_stage(st, smem + ((kt + 1) & 1) * STAGE);
+    if (kt + 1 < nkt) commit_tile(st, smem + ((kt + 1) & 1) * STAGE);
+    wait_vmem();
     __syncthreads();
   }
 
