@@ -147,9 +147,10 @@ def _q4(rng, n, k, codebook) -> Q4Weight:
 
 
 def gen_linear(T, k, n, r, alpha, dtype="bf16", seed=BASE_SEED, b_std=0.02,
-               w_std=0.02, q4=False) -> LinearInputs:
+               w_std=0.02, q4=False, X=None) -> LinearInputs:
+    """One LoRA linear layer's tensors; pass X to share an input tensor."""
     rx, rw, ra, rb, rdy = _rngs(seed, 5)
-    X = _normal(rx, (T, k), 1.0, dtype)
+    X = _normal(rx, (T, k), 1.0, dtype) if X is None else X
     qw = None
     W = None
     if q4:
@@ -196,9 +197,10 @@ CONFIGS = {
 }
 
 
-def gen_config(cfg: int, seed: Optional[int] = None, b_std=0.02, scale_T=None):
+def gen_config(cfg: int, seed: Optional[int] = None, b_std=0.02, scale_T=None, part=None):
     """Inputs of one benchmark workload.  `scale_T` optionally replaces T
-    (same distributions, fewer tokens) for bounded samples."""
+    (same distributions, fewer tokens) for bounded samples.  For workload 4,
+    `part` = "attn" or "mlp" generates only that half."""
     c = dict(CONFIGS[cfg])
     seed = BASE_SEED + cfg if seed is None else seed
     T = c["T"] if scale_T is None else scale_T
@@ -210,13 +212,15 @@ def gen_config(cfg: int, seed: Optional[int] = None, b_std=0.02, scale_T=None):
                        b_std=b_std, q4=c.get("q4", False))
     # attention projections + MLP: q/k/v share X_attn, o has its own input
     d, dkv = c["d"], c["d_kv"]
-    layers = {}
-    layers["q"] = gen_linear(T, d, d, c["r"], c["alpha"], "bf16", seed * 10 + 1, b_std)
-    kk = gen_linear(T, d, dkv, c["r"], c["alpha"], "bf16", seed * 10 + 2, b_std)
-    vv = gen_linear(T, d, dkv, c["r"], c["alpha"], "bf16", seed * 10 + 3, b_std)
-    kk.X = layers["q"].X
-    vv.X = layers["q"].X
-    layers["k"], layers["v"] = kk, vv
-    layers["o"] = gen_linear(T, d, d, c["r"], c["alpha"], "bf16", seed * 10 + 4, b_std)
-    mlp = gen_mlp(T, d, c["f"], c["r"], c["alpha"], "bf16", seed * 10 + 5, b_std)
-    return {"attn": layers, "mlp": mlp}
+    out = {}
+    if part in (None, "attn"):
+        layers = {}
+        layers["q"] = gen_linear(T, d, d, c["r"], c["alpha"], "bf16", seed * 10 + 1, b_std)
+        Xq = layers["q"].X
+        layers["k"] = gen_linear(T, d, dkv, c["r"], c["alpha"], "bf16", seed * 10 + 2, b_std, X=Xq)
+        layers["v"] = gen_linear(T, d, dkv, c["r"], c["alpha"], "bf16", seed * 10 + 3, b_std, X=Xq)
+        layers["o"] = gen_linear(T, d, d, c["r"], c["alpha"], "bf16", seed * 10 + 4, b_std)
+        out["attn"] = layers
+    if part in (None, "mlp"):
+        out["mlp"] = gen_mlp(T, d, c["f"], c["r"], c["alpha"], "bf16", seed * 10 + 5, b_std)
+    return out

@@ -14,7 +14,7 @@ using namespace lora;
 
 namespace {
 
-constexpr int kInloopMaxRS = 32;   // wider side products are precomputed
+constexpr int kInloopMaxRS = 0;    // side products up to this width run in the K loop
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int rs_of(int64_t width) { return (int)(cdiv(width, 16) * 16); }
