@@ -14,7 +14,6 @@ using namespace lora;
 
 namespace {
 
-constexpr int kInloopMaxRS = 0;    // side products up to this width run in the K loop
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int rs_of(int64_t width) { return (int)(cdiv(width, 16) * 16); }
@@ -60,10 +59,8 @@ LinFwdPlan plan_lin_fwd(int64_t T, int64_t k, int64_t n, int64_t r) {
   const int RS = rs_of(r);
   p.side = b.take((size_t)RS * k * 2);
   p.epi = b.take((size_t)n * RS * 2);
-  if (RS > kInloopMaxRS) {
-    p.hpart = b.take(nt_part_bytes(T, k, RS));
-    p.hbf = b.take((size_t)T * RS * 2);
-  }
+  p.hpart = b.take(nt_part_bytes(T, k, RS));
+  p.hbf = b.take((size_t)T * RS * 2);
   p.total = b.cur;
   return p;
 }
@@ -300,13 +297,13 @@ void set_b(GemmArgs &a, const WeightView &w0, const WeightView &w1) {
 struct TimerSlot { hipEvent_t start = nullptr, stop = nullptr; };
 TimerSlot g_timer[LORA_KC_COUNT];
 
-int run_gemm(int kc, bool nn, bool q4, int rs_inloop, int epi, const GemmArgs &a, hipStream_t st) {
+int run_gemm(int kc, bool nn, bool q4, int epi, const GemmArgs &a, hipStream_t st) {
   TimerSlot ts = g_timer[kc];
   g_timer[kc] = TimerSlot{};
   if (ts.start) HIP_TRY(hipEventRecord(ts.start, st));
   hipError_t e;
-  if (!nn) e = q4 ? launch_gemm_nt_q4(rs_inloop, epi, a, st) : launch_gemm_nt(rs_inloop, epi, a, st);
-  else e = q4 ? launch_gemm_nn_q4(rs_inloop, epi, a, st) : launch_gemm_nn(rs_inloop, epi, a, st);
+  if (!nn) e = q4 ? launch_gemm_nt_q4(epi, a, st) : launch_gemm_nt(epi, a, st);
+  else e = q4 ? launch_gemm_nn_q4(epi, a, st) : launch_gemm_nn(epi, a, st);
   if (e != hipSuccess) return LORA_ERR_HIP;
   if (ts.stop) HIP_TRY(hipEventRecord(ts.stop, st));
   return LORA_OK;
@@ -418,18 +415,15 @@ int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
   a.M = (int)T; a.N = (int)n; a.K = (int)k; a.ksplit = (int)k;
   a.A0 = a.A1 = (const bf16_t *)X; a.lda = k;
   set_b(a, wv, wv); a.ldb = k;
-  a.side = side; a.ld_side = k; a.rs = RS; a.epi = epi; a.s = s;
+  a.rs = RS; a.epi = epi;
   a.C = (bf16_t *)Y; a.ldc = n;
   a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(n, BN);
-  int rs_inloop = RS;
-  if (RS > kInloopMaxRS) {
-    bf16_t *hbf = (bf16_t *)(w + pl.hbf);
-    LORA_TRY(skinny_nt(RS, false, T, k, (const bf16_t *)X, (const bf16_t *)X, k, k, nullptr,
-                       nullptr, side, (float *)(w + pl.hpart), nullptr, hbf, s, st));
-    a.hglob = hbf;
-    rs_inloop = 0;
-  }
-  return run_gemm(LORA_KC_LINEAR_FWD, false, wv.q4, rs_inloop, EPI_STORE, a, st);
+  // rank-r product s (X A^T), once per call, applied in the GEMM epilogue
+  bf16_t *hbf = (bf16_t *)(w + pl.hbf);
+  LORA_TRY(skinny_nt(RS, false, T, k, (const bf16_t *)X, (const bf16_t *)X, k, k, nullptr,
+                     nullptr, side, (float *)(w + pl.hpart), nullptr, hbf, s, st));
+  a.hglob = hbf;
+  return run_gemm(LORA_KC_LINEAR_FWD, false, wv.q4, EPI_STORE, a, st);
 }
 
 int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float alpha,
@@ -467,22 +461,20 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
   LORA_TRY(build_epi(epi_nn, k, RS, A, nullptr, r, k, 1, st));     // A^T padded [k x RS]
   LORA_TRY(build_side(side_nt, RS, k, A, nullptr, r, k, 0, st));   // A padded [RS x k]
   const bf16_t *Xb = (const bf16_t *)X, *dYb = (const bf16_t *)dY;
-  const bool inloop = RS <= kInloopMaxRS;
   if (T > 0) {
-    if (!dX || !inloop)
-      LORA_TRY(skinny_nt(RS, false, T, n, dYb, dYb, n, n, nullptr, nullptr, side_nn, ntpart, g32,
-                         gbf, s, st));
+    // G = dY B (fp32 for dA, s G in bf16 for the dX epilogue)
+    LORA_TRY(skinny_nt(RS, false, T, n, dYb, dYb, n, n, nullptr, nullptr, side_nn, ntpart, g32,
+                       gbf, s, st));
     if (dX) {
       GemmArgs a = gemm_base();
       a.M = (int)T; a.N = (int)k; a.K = (int)n; a.ksplit = (int)n;
       a.A0 = a.A1 = dYb; a.lda = n;
       set_b(a, wv, wv); a.ldb = k;
-      a.side = side_nn; a.ld_side = n; a.rs = RS; a.epi = epi_nn; a.s = s;
+      a.rs = RS; a.epi = epi_nn;
       a.accumulate = acc; a.C = (bf16_t *)dX; a.ldc = k;
-      a.side_out = inloop ? g32 : nullptr;
       a.hglob = gbf;
       a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
-      LORA_TRY(run_gemm(LORA_KC_LINEAR_DX, true, wv.q4, inloop ? RS : 0, EPI_STORE, a, st));
+      LORA_TRY(run_gemm(LORA_KC_LINEAR_DX, true, wv.q4, EPI_STORE, a, st));
     }
     LORA_TRY(skinny_nt(RS, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,
                        nullptr, 1.f, st));
@@ -546,34 +538,28 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   a.A0 = a.A1 = Xb; a.lda = d;
   set_b(a, wg, wu); a.ldb = d;
   a.gu_f = (int)f;
-  a.side = side_gu; a.ld_side = d; a.rs = RS1; a.epi = epi_gu; a.s = s;
+  a.rs = RS1; a.epi = epi_gu;
   a.E = (bf16_t *)e_saved; a.G = (bf16_t *)g_saved; a.H = h;
   a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, 128);
-  int rs1 = RS1;
-  if (RS1 > kInloopMaxRS) {
-    LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
-                       hbf, s, st));
-    a.hglob = hbf;
-    rs1 = 0;
-  }
-  LORA_TRY(run_gemm(LORA_KC_GATEUP_FWD, false, wg.q4, rs1, EPI_SWIGLU_FWD, a, st));
+  // [s X Ag^T | s X Au^T], once per call
+  LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
+                     hbf, s, st));
+  a.hglob = hbf;
+  LORA_TRY(run_gemm(LORA_KC_GATEUP_FWD, false, wg.q4, EPI_SWIGLU_FWD, a, st));
 
   // down
   GemmArgs b = gemm_base();
   b.M = (int)T; b.N = (int)d; b.K = (int)f; b.ksplit = (int)f;
   b.A0 = b.A1 = h; b.lda = f;
   set_b(b, wd, wd); b.ldb = f;
-  b.side = side_d; b.ld_side = f; b.rs = RS2; b.epi = epi_d; b.s = s;
+  b.rs = RS2; b.epi = epi_d;
   b.C = (bf16_t *)Y; b.ldc = d;
   b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
-  int rs2 = RS2;
-  if (RS2 > kInloopMaxRS) {
-    LORA_TRY(skinny_nt(RS2, false, T, f, h, h, f, f, nullptr, nullptr, side_d, hpart, nullptr, hbf,
-                       s, st));
-    b.hglob = hbf;
-    rs2 = 0;
-  }
-  return run_gemm(LORA_KC_DOWN_FWD, false, wd.q4, rs2, EPI_STORE, b, st);
+  // s h Ad^T, once per call
+  LORA_TRY(skinny_nt(RS2, false, T, f, h, h, f, f, nullptr, nullptr, side_d, hpart, nullptr, hbf,
+                     s, st));
+  b.hglob = hbf;
+  return run_gemm(LORA_KC_DOWN_FWD, false, wd.q4, EPI_STORE, b, st);
 }
 
 int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
@@ -646,20 +632,18 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
 
   if (T > 0) {
     // 1. dh = dY Wd + s (dY Bd) Ad with the SwiGLU-derivative epilogue -> de, dg
-    const bool in2 = RS2 <= kInloopMaxRS;
-    if (!in2)
-      LORA_TRY(skinny_nt(RS2, false, T, d, dYb, dYb, d, d, nullptr, nullptr, side_d_nn, ntpart,
-                         gd32, gdbf, s, st));
+    // G_d = dY Bd (fp32 for dAd, s G_d in bf16 for the epilogue)
+    LORA_TRY(skinny_nt(RS2, false, T, d, dYb, dYb, d, d, nullptr, nullptr, side_d_nn, ntpart,
+                       gd32, gdbf, s, st));
     GemmArgs a = gemm_base();
     a.M = (int)T; a.N = (int)f; a.K = (int)d; a.ksplit = (int)d;
     a.A0 = a.A1 = dYb; a.lda = d;
     set_b(a, wd, wd); a.ldb = f;
-    a.side = side_d_nn; a.ld_side = d; a.rs = RS2; a.epi = epi_d_nn; a.s = s;
+    a.rs = RS2; a.epi = epi_d_nn;
     a.Ein = eb; a.Gin = gb; a.DE = de; a.DG = dg;
-    a.side_out = in2 ? gd32 : nullptr;
     a.hglob = gdbf;
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
-    LORA_TRY(run_gemm(LORA_KC_DOWN_BWD, true, wd.q4, in2 ? RS2 : 0, EPI_SWIGLU_BWD, a, st));
+    LORA_TRY(run_gemm(LORA_KC_DOWN_BWD, true, wd.q4, EPI_SWIGLU_BWD, a, st));
     // 2. H_d = h Ad^T with h recomputed from e, g
     LORA_TRY(skinny_nt(RS2, true, T, f, nullptr, nullptr, f, f, eb, gb, side_d_nt, ntpart, hd32,
                        nullptr, 1.f, st));
@@ -671,21 +655,19 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
                      (bf16_t *)dBd, nullptr, d, st));
   if (T > 0) {
     // 4. dX = de Wg + dg Wu + s [de Bg | dg Bu] [Ag; Au]
-    const bool in1 = RS1 <= kInloopMaxRS;
-    if (!dX || !in1)
-      LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, f, nullptr, nullptr, side_gu_nn, ntpart,
-                         ggu32, ggubf, s, st));
+    // G_gu = [de Bg | dg Bu] (fp32 for dA_gu, scaled bf16 for the epilogue)
+    LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, f, nullptr, nullptr, side_gu_nn, ntpart,
+                       ggu32, ggubf, s, st));
     if (dX) {
       GemmArgs b = gemm_base();
       b.M = (int)T; b.N = (int)d; b.K = (int)(2 * f); b.ksplit = (int)f;
       b.A0 = de; b.A1 = dg; b.lda = f;
       set_b(b, wg, wu); b.ldb = d;
-      b.side = side_gu_nn; b.ld_side = 2 * f; b.rs = RS1; b.epi = epi_gu_nn; b.s = s;
+      b.rs = RS1; b.epi = epi_gu_nn;
       b.C = (bf16_t *)dX; b.ldc = d;
-      b.side_out = in1 ? ggu32 : nullptr;
       b.hglob = ggubf;
       b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
-      LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, true, wg.q4, in1 ? RS1 : 0, EPI_STORE, b, st));
+      LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, true, wg.q4, EPI_STORE, b, st));
     }
     // 5. H_gu = X [Ag; Au]^T
     LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,

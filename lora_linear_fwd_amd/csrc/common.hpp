@@ -102,7 +102,18 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const char *base, uint32_t off) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// s_waitcnt vmcnt(N) with a compile-time N
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier without the memory fence of __syncthreads(): the caller
+// waits for exactly the loads it needs first (vmcnt / lgkmcnt), so loads of
+// later pipeline stages stay in flight across the barrier.  The "memory"
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 // 8x8 transpose of bf16: in[i] holds row i (8 values, element j in 16-bit
 // lane j), out[j] holds column j (element i = in[i][j]).

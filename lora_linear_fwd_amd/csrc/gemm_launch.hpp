@@ -20,11 +20,11 @@ inline hipError_t ensure_lds(Kern kern, size_t bytes, std::atomic<uint64_t> &don
   return e;
 }
 
-template <int BMODE, int RS, int EPI, int SMODE>
-inline hipError_t launch_one(const GemmArgs &a, hipStream_t st) {
+template <int BMODE, int EPI>
+inline hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t st) {
   static std::atomic<uint64_t> done{0};
-  constexpr size_t lds = gemm_lds_bytes<BMODE, RS, EPI, SMODE>();
-  auto kern = k_lora_gemm<BMODE, RS, EPI, SMODE>;
+  constexpr size_t lds = gemm_lds_bytes<BMODE>();
+  auto kern = k_lora_gemm<BMODE, EPI>;
   hipError_t e = ensure_lds(kern, lds, done);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
@@ -33,22 +33,9 @@ inline hipError_t launch_one(const GemmArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// rs_inloop: 16/32/64 = side product accumulated in the K loop; 0 = the
-// scaled side product is read from a.hglob (width a.rs).
-template <int BMODE, int EPI>
-inline hipError_t launch_gemm_t(int rs_inloop, const GemmArgs &a, hipStream_t st) {
-  switch (rs_inloop) {
-    case 16: return launch_one<BMODE, 16, EPI, SIDE_INLOOP>(a, st);
-    case 32: return launch_one<BMODE, 32, EPI, SIDE_INLOOP>(a, st);
-    case 64: return launch_one<BMODE, 64, EPI, SIDE_INLOOP>(a, st);
-    case 0: return launch_one<BMODE, 16, EPI, SIDE_GLOBAL>(a, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_gemm_nt(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
-hipError_t launch_gemm_nt_q4(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
-hipError_t launch_gemm_nn(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
-hipError_t launch_gemm_nn_q4(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nt_q4(int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nn(int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nn_q4(int epi, const GemmArgs &a, hipStream_t st);
 
 }  // namespace lora

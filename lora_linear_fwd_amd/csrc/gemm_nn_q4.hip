@@ -2,9 +2,9 @@
 #include "gemm_launch.hpp"
 
 namespace lora {
-hipError_t launch_gemm_nn_q4(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st) {
-  if (epi == EPI_STORE) return launch_gemm_t<B_NN_Q4, EPI_STORE>(rs_inloop, a, st);
-  if (epi == EPI_SWIGLU_BWD) return launch_gemm_t<B_NN_Q4, EPI_SWIGLU_BWD>(rs_inloop, a, st);
+hipError_t launch_gemm_nn_q4(int epi, const GemmArgs &a, hipStream_t st) {
+  if (epi == EPI_STORE) return launch_gemm_t<B_NN_Q4, EPI_STORE>(a, st);
+  if (epi == EPI_SWIGLU_BWD) return launch_gemm_t<B_NN_Q4, EPI_SWIGLU_BWD>(a, st);
   return hipErrorInvalidValue;
 }
 }  // namespace lora

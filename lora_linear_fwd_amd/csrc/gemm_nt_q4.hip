@@ -2,9 +2,9 @@
 #include "gemm_launch.hpp"
 
 namespace lora {
-hipError_t launch_gemm_nt_q4(int rs_inloop, int epi, const GemmArgs &a, hipStream_t st) {
-  if (epi == EPI_STORE) return launch_gemm_t<B_NT_Q4, EPI_STORE>(rs_inloop, a, st);
-  if (epi == EPI_SWIGLU_FWD) return launch_gemm_t<B_NT_Q4, EPI_SWIGLU_FWD>(rs_inloop, a, st);
+hipError_t launch_gemm_nt_q4(int epi, const GemmArgs &a, hipStream_t st) {
+  if (epi == EPI_STORE) return launch_gemm_t<B_NT_Q4, EPI_STORE>(a, st);
+  if (epi == EPI_SWIGLU_FWD) return launch_gemm_t<B_NT_Q4, EPI_SWIGLU_FWD>(a, st);
   return hipErrorInvalidValue;
 }
 }  // namespace lora
