@@ -34,7 +34,21 @@ def parse():
     ap.add_argument("--config", type=int, default=3, choices=(2, 3, 5))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 256 MiB device-to-device copy (3 times): the "
+                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
 def mlp_flops(T, d, f, r):
@@ -93,6 +107,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import numpy as np
     import torch
 

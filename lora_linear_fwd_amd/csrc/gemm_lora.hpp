@@ -469,95 +469,130 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   }
 
   // ------------------------------------------------ output
-  if constexpr (EPI == EPI_STORE) {
+  // The accumulators hold 4 consecutive output columns of one token row per
+  // lane, 32 rows per instruction: stored directly that would scatter 8-byte
+  // pieces over 32 rows.  Each wave instead passes its 128 x 128 sub-tile
+  // through a private 32 KB LDS region, 64 token rows (fp32) at a time, and
+  // then reads and writes global memory in 16-byte pieces along rows (a
+  // wave instruction covers whole 128- or 256-byte row segments).
+  // Region layout: row r (0..63) of 512 bytes, 16-byte chunk c (4 columns)
+  // stored at chunk c ^ (r % 32), so the 16 rows one write instruction
+  // touches land in distinct banks.
+  __syncthreads();   // every wave is done with the pipeline stages
+  char *reg = smem + wave * 32768;
+  auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 512 + ((c ^ (r & 31)) << 4)); };
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 128 + j * 32 + l32;
-      if (m >= M) continue;
+  for (int half = 0; half < 2; ++half) {
+    // rows (j - 2 half) * 32 + l32 of the region hold acc[.][j]
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 128 + i * 32 + 8 * g + 4 * hi32;
-          if (n >= N) continue;
-          float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-          float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          bf16_t *dst = p.C + (int64_t)m * p.ldc + n;
-          if (p.accumulate) {
-            const u32x2 o = gload8(dst);
-            v0 += bf16lo(o[0]); v1 += bf16hi(o[0]);
-            v2 += bf16lo(o[1]); v3 += bf16hi(o[1]);
-          }
-          gstore8(dst, u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)});
+          const int j = 2 * half + jj;
+          const f32x16 &a = acc[i][j];
+          const u32x4 v = {__float_as_uint(a[4 * g]), __float_as_uint(a[4 * g + 1]),
+                           __float_as_uint(a[4 * g + 2]), __float_as_uint(a[4 * g + 3])};
+          lds_write16(reg, ep_off(jj * 32 + l32, 8 * i + 2 * g + hi32), v);
         }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-    const int f = p.gu_f;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    const int mrow0 = m0 + wm * 128 + half * 64;   // token of region row 0
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      // region columns 0..63: gate, 64..127: up (features tn*128 + wn*64 + c)
+      const int f = p.gu_f;
+      const int q = lane & 7;                       // 8-column group
+#pragma unroll 2
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int m = mrow0 + r;
+        const int jf = tn * 128 + wn * 64 + 8 * q;
+        const u32x4 e0 = lds_read16(reg, ep_off(r, 2 * q)), e1 = lds_read16(reg, ep_off(r, 2 * q + 1));
+        const u32x4 g0 = lds_read16(reg, ep_off(r, 16 + 2 * q)), g1 = lds_read16(reg, ep_off(r, 17 + 2 * q));
+        if (m < M && jf < f) {
+          const float ev[8] = {__uint_as_float(e0[0]), __uint_as_float(e0[1]), __uint_as_float(e0[2]),
+                               __uint_as_float(e0[3]), __uint_as_float(e1[0]), __uint_as_float(e1[1]),
+                               __uint_as_float(e1[2]), __uint_as_float(e1[3])};
+          const float gv[8] = {__uint_as_float(g0[0]), __uint_as_float(g0[1]), __uint_as_float(g0[2]),
+                               __uint_as_float(g0[3]), __uint_as_float(g1[0]), __uint_as_float(g1[1]),
+                               __uint_as_float(g1[2]), __uint_as_float(g1[3])};
+          u32x4 ew, gw, hw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 128 + j * 32 + l32;
-      if (m >= M) continue;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int jf = tn * 128 + wn * 64 + i * 32 + 8 * g + 4 * hi32;
-          if (jf >= f) continue;
-          uint32_t ew[2], gw[2], hw[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            ew[h2] = pack_bf16x2(acc[i][j][4 * g + 2 * h2], acc[i][j][4 * g + 2 * h2 + 1]);
-            gw[h2] = pack_bf16x2(acc[i + 2][j][4 * g + 2 * h2], acc[i + 2][j][4 * g + 2 * h2 + 1]);
+          for (int t = 0; t < 4; ++t) {
+            ew[t] = pack_bf16x2(ev[2 * t], ev[2 * t + 1]);
+            gw[t] = pack_bf16x2(gv[2 * t], gv[2 * t + 1]);
             // h from the rounded e, g: the same values the backward reloads
-            const float e0 = bf16lo(ew[h2]), e1 = bf16hi(ew[h2]);
-            const float g0 = bf16lo(gw[h2]), g1 = bf16hi(gw[h2]);
-            hw[h2] = pack_bf16x2(e0 * sigmoidf_fast(e0) * g0, e1 * sigmoidf_fast(e1) * g1);
+            const float ea = bf16lo(ew[t]), eb = bf16hi(ew[t]);
+            const float ga = bf16lo(gw[t]), gb = bf16hi(gw[t]);
+            hw[t] = pack_bf16x2(ea * sigmoidf_fast(ea) * ga, eb * sigmoidf_fast(eb) * gb);
           }
           const int64_t off = (int64_t)m * f + jf;
-          gstore8(p.E + off, u32x2{ew[0], ew[1]});
-          gstore8(p.G + off, u32x2{gw[0], gw[1]});
-          gstore8(p.H + off, u32x2{hw[0], hw[1]});
+          gstore16(p.E + off, ew);
+          gstore16(p.G + off, gw);
+          gstore16(p.H + off, hw);
         }
-    }
-  } else {  // EPI_SWIGLU_BWD
+      }
+    } else {
+      const int q = lane & 15;                      // 8-column group
+      const int n = n0 + wn * 128 + 8 * q;
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int m = mrow0 + r;
+        const u32x4 a0 = lds_read16(reg, ep_off(r, 2 * q)), a1 = lds_read16(reg, ep_off(r, 2 * q + 1));
+        if (m >= M || n >= N) continue;
+        float v[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
+                      __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
+                      __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+        if constexpr (EPI == EPI_STORE) {
+          bf16_t *dst = p.C + (int64_t)m * p.ldc + n;
+          if (p.accumulate) {
+            const u32x4 o = gload16(dst);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 128 + j * 32 + l32;
-      if (m >= M) continue;
+            for (int t = 0; t < 4; ++t) {
+              v[2 * t] += bf16lo(o[t]);
+              v[2 * t + 1] += bf16hi(o[t]);
+            }
+          }
+          u32x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 128 + i * 32 + 8 * g + 4 * hi32;
-          if (n >= N) continue;
+          for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
+          gstore16(dst, w);
+        } else {  // EPI_SWIGLU_BWD: v = dh
           const int64_t off = (int64_t)m * N + n;
-          const u32x2 ev = gload8(p.Ein + off), gv = gload8(p.Gin + off);
-          uint32_t dew[2], dgw[2];
+          const u32x4 ev = gload16(p.Ein + off), gv = gload16(p.Gin + off);
+          u32x4 dew, dgw;
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
+          for (int t = 0; t < 4; ++t) {
             float de[2], dg[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const float e = t ? bf16hi(ev[h2]) : bf16lo(ev[h2]);
-              const float gg = t ? bf16hi(gv[h2]) : bf16lo(gv[h2]);
-              const float dh = acc[i][j][4 * g + 2 * h2 + t];
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
+              const float gg = h2 ? bf16hi(gv[t]) : bf16lo(gv[t]);
+              const float dh = v[2 * t + h2];
               const float sg = sigmoidf_fast(e);
-              dg[t] = dh * e * sg;
-              de[t] = dh * gg * sg * (1.0f + e * (1.0f - sg));
+              dg[h2] = dh * e * sg;
+              de[h2] = dh * gg * sg * (1.0f + e * (1.0f - sg));
             }
-            dew[h2] = pack_bf16x2(de[0], de[1]);
-            dgw[h2] = pack_bf16x2(dg[0], dg[1]);
+            dew[t] = pack_bf16x2(de[0], de[1]);
+            dgw[t] = pack_bf16x2(dg[0], dg[1]);
           }
-          gstore8(p.DE + off, u32x2{dew[0], dew[1]});
-          gstore8(p.DG + off, u32x2{dgw[0], dgw[1]});
+          gstore16(p.DE + off, dew);
+          gstore16(p.DG + off, dgw);
         }
+      }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
 template <int BMODE, int BK = kBK, int NSTAGE = kNSTAGE>
 constexpr size_t gemm_lds_bytes() {
-  return (size_t)NSTAGE * (BM * BK * 2 + BN * BK * 2) +
+  // pipeline stages, at least the 4 x 32 KB the output staging uses
+  return (NSTAGE * (BM * BK * 2 + BN * BK * 2) > 4 * 32768 ? (size_t)NSTAGE * (BM * BK * 2 + BN * BK * 2)
+                                                           : (size_t)4 * 32768) +
          ((BMODE == B_NT_Q4 || BMODE == B_NN_Q4) ? 256 * sizeof(float2) : 0);
 }
 
