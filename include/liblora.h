@@ -40,7 +40,17 @@
  *   - T == 0 is valid: forwards write nothing, backwards write dA = dB = 0;
  *     the token-sized pointers (X, Y, dY, dX, e, g) may then be NULL.
  *   - `ws`/`ws_bytes`: caller-provided device workspace of at least
- *     lora_workspace_bytes(...) bytes (may be NULL when that is 0).
+ *     lora_workspace_bytes(op | LORA_WS_MINIMAL, ...) bytes (may be NULL
+ *     when that is 0).  The size picks the strategy (bf16 path):
+ *       >= lora_workspace_bytes(op, ...): the frozen base weight is first
+ *         copied into the workspace in the form the GEMM reads fastest
+ *         (transposed for the backward dX products, decoded to bf16 for
+ *         4-bit weights) and every GEMM reads it K-contiguous;
+ *       otherwise (minimal): no weight copy; the backward GEMMs read W in
+ *         place (row-major [n x k] as the B operand of dY W) and 4-bit
+ *         codes are decoded inside the GEMM while its LDS tiles fill.
+ *     Both give results within the same tolerance of the exact product
+ *     (fp32 accumulation in a different summation order).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous on it and reentrant; kernel faults surface at the
  *     caller's next synchronisation.
@@ -104,6 +114,8 @@ typedef struct {
 #define LORA_OP_LINEAR_BWD 1
 #define LORA_OP_MLP_FWD    2
 #define LORA_OP_MLP_BWD    3
+/* or-ed into `op`: size of the minimal-memory strategy */
+#define LORA_WS_MINIMAL    0x100
 
 /*
  * Y = X W^T + s (X A^T) B^T                                  ([DD] 1.3)
@@ -175,8 +187,10 @@ int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absma
                   const float *codebook, int blocksize, int out_dtype, void *out,
                   void *stream);
 
-/* Workspace bytes an op needs (k_or_d / n_or_f as in the op's signature;
- * `wfmt` is the base-weight format).  Returns 0 for invalid arguments. */
+/* Workspace bytes of an op (k_or_d / n_or_f as in the op's signature;
+ * `wfmt` is the base-weight format): the fast strategy's size, or with
+ * LORA_WS_MINIMAL or-ed into `op` the smallest size the op accepts.
+ * Returns 0 for invalid arguments. */
 size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T,
                             int64_t k_or_d, int64_t n_or_f, int64_t r);
 

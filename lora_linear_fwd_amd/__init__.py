@@ -22,6 +22,7 @@ LORA_F32, LORA_BF16 = 0, 1
 LORA_W_DENSE, LORA_W_Q4 = 0, 1
 LORA_FLAG_ACCUMULATE_DX = 1
 OP_LINEAR_FWD, OP_LINEAR_BWD, OP_MLP_FWD, OP_MLP_BWD = 0, 1, 2, 3
+LORA_WS_MINIMAL = 0x100
 STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
           3: "LORA_ERR_UNSUPPORTED", 4: "LORA_ERR_WORKSPACE", 5: "LORA_ERR_MISALIGNED",
           6: "LORA_ERR_HIP"}
@@ -167,20 +168,22 @@ def _wfmt(W):
 _ws_cache: Dict[tuple, object] = {}
 
 
-def _workspace(nbytes: int, device, workspace=None):
+def _workspace(op, dt, wfmt, dims, device, workspace=None, minimal=False):
+    """(pointer, byte count) of the workspace handed to the library: the
+    caller's tensor at its full size, else a cached buffer passed at exactly
+    the size of the requested strategy (fast, or minimal-memory)."""
     torch = _torch()
-    if nbytes == 0:
-        return None
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError("workspace too small")
-        return workspace
+        return _ptr(workspace), workspace.numel() * workspace.element_size()
+    nbytes = workspace_bytes(op | (LORA_WS_MINIMAL if minimal else 0), dt, wfmt, *dims)
+    if nbytes == 0:
+        return None, 0
     key = (str(device), torch.cuda.current_stream(device).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
-    return buf
+    return _ptr(buf), nbytes
 
 
 def clear_workspace_cache():
@@ -188,7 +191,8 @@ def clear_workspace_cache():
 
 
 # ------------------------------------------------------------ entry points
-def lora_linear_fwd(X, W: Weight, A, B, alpha: float, Y=None, workspace=None, stream=None):
+def lora_linear_fwd(X, W: Weight, A, B, alpha: float, Y=None, workspace=None, stream=None,
+                    minimal_workspace=False):
     """Y = X W^T + (alpha/r) (X A^T) B^T."""
     torch = _torch()
     T, k = X.shape
@@ -197,17 +201,18 @@ def lora_linear_fwd(X, W: Weight, A, B, alpha: float, Y=None, workspace=None, st
     dt = _dtype_code(X)
     if Y is None:
         Y = torch.empty((T, n), dtype=X.dtype, device=X.device)
-    ws = _workspace(workspace_bytes(OP_LINEAR_FWD, dt, _wfmt(W), T, k, n, r), X.device, workspace)
+    wsp, wsn = _workspace(OP_LINEAR_FWD, dt, _wfmt(W), (T, k, n, r), X.device, workspace,
+                          minimal_workspace)
     wst = _wstruct(W)
     _check(lib().lora_linear_fwd(dt, T, k, n, r, float(alpha), _ptr(X), ctypes.byref(wst),
-                                 _ptr(A), _ptr(B), _ptr(Y), _ptr(ws),
-                                 0 if ws is None else ws.numel(), _stream(stream)),
+                                 _ptr(A), _ptr(B), _ptr(Y), wsp, wsn, _stream(stream)),
            "lora_linear_fwd")
     return Y
 
 
 def lora_linear_bwd(X, W: Weight, A, B, alpha: float, dY, need_dx=True, dX=None,
-                    accumulate_dx=False, dA=None, dB=None, workspace=None, stream=None):
+                    accumulate_dx=False, dA=None, dB=None, workspace=None, stream=None,
+                    minimal_workspace=False):
     """Returns (dX or None, dA, dB)."""
     torch = _torch()
     T, k = X.shape
@@ -220,13 +225,13 @@ def lora_linear_bwd(X, W: Weight, A, B, alpha: float, dY, need_dx=True, dX=None,
         dX = None
     dA = torch.empty_like(A) if dA is None else dA
     dB = torch.empty_like(B) if dB is None else dB
-    ws = _workspace(workspace_bytes(OP_LINEAR_BWD, dt, _wfmt(W), T, k, n, r), X.device, workspace)
+    wsp, wsn = _workspace(OP_LINEAR_BWD, dt, _wfmt(W), (T, k, n, r), X.device, workspace,
+                          minimal_workspace)
     wst = _wstruct(W)
     flags = LORA_FLAG_ACCUMULATE_DX if accumulate_dx else 0
     _check(lib().lora_linear_bwd(dt, T, k, n, r, float(alpha), _ptr(X), ctypes.byref(wst),
                                  _ptr(A), _ptr(B), _ptr(dY), _ptr(dX), _ptr(dA), _ptr(dB),
-                                 flags, _ptr(ws), 0 if ws is None else ws.numel(),
-                                 _stream(stream)),
+                                 flags, wsp, wsn, _stream(stream)),
            "lora_linear_bwd")
     return dX, dA, dB
 
@@ -239,7 +244,7 @@ def _mlp_dims(X, W, A):
 
 
 def lora_swiglu_mlp_fwd(X, W: Dict[str, Weight], A, B, alpha: float, Y=None, e=None, g=None,
-                        workspace=None, stream=None):
+                        workspace=None, stream=None, minimal_workspace=False):
     """Returns (Y, e, g); W/A/B are dicts keyed 'gate', 'up', 'down'."""
     torch = _torch()
     T, d, f, r = _mlp_dims(X, W, A)
@@ -247,21 +252,22 @@ def lora_swiglu_mlp_fwd(X, W: Dict[str, Weight], A, B, alpha: float, Y=None, e=N
     Y = torch.empty((T, d), dtype=X.dtype, device=X.device) if Y is None else Y
     e = torch.empty((T, f), dtype=X.dtype, device=X.device) if e is None else e
     g = torch.empty((T, f), dtype=X.dtype, device=X.device) if g is None else g
-    ws = _workspace(workspace_bytes(OP_MLP_FWD, dt, _wfmt(W["gate"]), T, d, f, r), X.device,
-                    workspace)
+    wsp, wsn = _workspace(OP_MLP_FWD, dt, _wfmt(W["gate"]), (T, d, f, r), X.device, workspace,
+                          minimal_workspace)
     ws_ = [_wstruct(W[p]) for p in ("gate", "up", "down")]
     _check(lib().lora_swiglu_mlp_fwd(
         dt, T, d, f, r, float(alpha), _ptr(X),
         ctypes.byref(ws_[0]), _ptr(A["gate"]), _ptr(B["gate"]),
         ctypes.byref(ws_[1]), _ptr(A["up"]), _ptr(B["up"]),
         ctypes.byref(ws_[2]), _ptr(A["down"]), _ptr(B["down"]),
-        _ptr(Y), _ptr(e), _ptr(g), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+        _ptr(Y), _ptr(e), _ptr(g), wsp, wsn, _stream(stream)),
         "lora_swiglu_mlp_fwd")
     return Y, e, g
 
 
 def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, need_dx=True,
-                        out: Optional[dict] = None, workspace=None, stream=None):
+                        out: Optional[dict] = None, workspace=None, stream=None,
+                        minimal_workspace=False):
     """Returns dict with dX (or None) and dA_*/dB_* per projection."""
     torch = _torch()
     T, d, f, r = _mlp_dims(X, W, A)
@@ -274,8 +280,8 @@ def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, n
     for p in ("gate", "up", "down"):
         o.setdefault("dA_" + p, torch.empty_like(A[p]))
         o.setdefault("dB_" + p, torch.empty_like(B[p]))
-    ws = _workspace(workspace_bytes(OP_MLP_BWD, dt, _wfmt(W["gate"]), T, d, f, r), X.device,
-                    workspace)
+    wsp, wsn = _workspace(OP_MLP_BWD, dt, _wfmt(W["gate"]), (T, d, f, r), X.device, workspace,
+                          minimal_workspace)
     ws_ = [_wstruct(W[p]) for p in ("gate", "up", "down")]
     _check(lib().lora_swiglu_mlp_bwd(
         dt, T, d, f, r, float(alpha), _ptr(X),
@@ -285,7 +291,7 @@ def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, n
         _ptr(e), _ptr(g), _ptr(dY), _ptr(o["dX"]),
         _ptr(o["dA_gate"]), _ptr(o["dB_gate"]), _ptr(o["dA_up"]), _ptr(o["dB_up"]),
         _ptr(o["dA_down"]), _ptr(o["dB_down"]),
-        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+        wsp, wsn, _stream(stream)),
         "lora_swiglu_mlp_bwd")
     return o
 

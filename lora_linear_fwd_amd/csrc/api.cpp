@@ -53,10 +53,12 @@ inline size_t tn_part_bytes(int64_t T, int64_t N, int RS) {
   return (size_t)tn_split(T, N).ts * RS * N * 4;
 }
 
-struct LinFwdPlan { size_t side, epi, hpart, hbf, total; };
-LinFwdPlan plan_lin_fwd(int64_t T, int64_t k, int64_t n, int64_t r) {
+// `wcopy`: room for a bf16 copy of the base weight (decoded or transposed)
+struct LinFwdPlan { size_t side, epi, hpart, hbf, wbuf, total; };
+LinFwdPlan plan_lin_fwd(int64_t T, int64_t k, int64_t n, int64_t r, bool wcopy) {
   Bump b; LinFwdPlan p{};
   const int RS = rs_of(r);
+  if (wcopy) p.wbuf = b.take((size_t)n * k * 2);
   p.side = b.take((size_t)RS * k * 2);
   p.epi = b.take((size_t)n * RS * 2);
   p.hpart = b.take(nt_part_bytes(T, k, RS));
@@ -65,10 +67,11 @@ LinFwdPlan plan_lin_fwd(int64_t T, int64_t k, int64_t n, int64_t r) {
   return p;
 }
 
-struct LinBwdPlan { size_t side_nn, epi_nn, side_nt, g32, gbf, h32, ntpart, tnpart, total; };
-LinBwdPlan plan_lin_bwd(int64_t T, int64_t k, int64_t n, int64_t r) {
+struct LinBwdPlan { size_t side_nn, epi_nn, side_nt, g32, gbf, h32, ntpart, tnpart, wbuf, total; };
+LinBwdPlan plan_lin_bwd(int64_t T, int64_t k, int64_t n, int64_t r, bool wcopy) {
   Bump b; LinBwdPlan p{};
   const int RS = rs_of(r);
+  if (wcopy) p.wbuf = b.take((size_t)k * n * 2);
   p.side_nn = b.take((size_t)RS * n * 2);
   p.epi_nn = b.take((size_t)k * RS * 2);
   p.side_nt = b.take((size_t)RS * k * 2);
@@ -81,10 +84,11 @@ LinBwdPlan plan_lin_bwd(int64_t T, int64_t k, int64_t n, int64_t r) {
   return p;
 }
 
-struct MlpFwdPlan { size_t h, side_gu, epi_gu, side_d, epi_d, hpart, hbf, total; };
-MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r) {
+struct MlpFwdPlan { size_t h, side_gu, epi_gu, side_d, epi_d, hpart, hbf, wbuf, total; };
+MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) {
   Bump b; MlpFwdPlan p{};
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
+  if (wcopy) p.wbuf = b.take((size_t)2 * f * d * 2);   // Wg | Wu, later Wd
   p.h = b.take((size_t)T * f * 2);
   p.side_gu = b.take((size_t)RS1 * d * 2);
   p.epi_gu = b.take((size_t)2 * f * RS1 * 2);
@@ -98,11 +102,12 @@ MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r) {
 
 struct MlpBwdPlan {
   size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, side_gu_nn, epi_gu_nn, side_gu_nt;
-  size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, total;
+  size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, total;
 };
-MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r) {
+MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) {
   Bump b; MlpBwdPlan p{};
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
+  if (wcopy) p.wbuf = b.take((size_t)2 * d * f * 2);   // Wd^T, later [Wg^T | Wu^T]
   p.de = b.take((size_t)T * f * 2);
   p.dg = b.take((size_t)T * f * 2);
   p.side_d_nn = b.take((size_t)RS2 * d * 2);
@@ -281,6 +286,42 @@ int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const 
   return LORA_OK;
 }
 
+// bf16 copies of a base weight W [rows x cols] in the workspace
+//   decode_w:    out = W (4-bit codes decoded), same layout
+//   transpose_w: out[c * ld_out + r] = W[r][c] (decoded if 4-bit)
+int decode_w(bf16_t *out, const WeightView &w, int64_t rows, int64_t cols, hipStream_t st) {
+  const int64_t total = rows * cols;
+  hipLaunchKernelGGL(k_dequant4, dim3(blocks_for(total / 32)), dim3(256), 0, st, w.codes,
+                     w.absmax, w.codebook, total, out);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+int transpose_w(bf16_t *out, int64_t ld_out, const WeightView &w, int64_t rows, int64_t cols,
+                hipStream_t st) {
+  const int64_t rb = cdiv(rows, 256), cb = cdiv(cols, w.q4 ? 256 : 64);
+  if (rb * cb >= ((int64_t)1 << 31)) return LORA_ERR_BAD_SHAPE;
+  if (w.q4)
+    hipLaunchKernelGGL(k_dequant4_t, dim3((unsigned)(rb * cb)), dim3(256), 0, st, w.codes, w.absmax,
+                       w.codebook, (int)rows, (int)cols, out, ld_out, (int)cb);
+  else
+    hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)(rb * cb)), dim3(256), 0, st, w.w,
+                       (int)rows, (int)cols, (int64_t)cols, out, ld_out, (int)cb);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+inline WeightView dense_view(const bf16_t *p) { return {false, p, nullptr, nullptr, nullptr}; }
+
+// workspace check shared by the entry points; `fast` = room for the
+// weight copies
+int check_ws(int op, int dtype, int wfmt, int64_t T, int64_t kd, int64_t nf, int64_t r,
+             const void *ws, size_t ws_bytes, bool &fast) {
+  const size_t need = lora_workspace_bytes(op | LORA_WS_MINIMAL, dtype, wfmt, T, kd, nf, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  fast = ws_bytes >= lora_workspace_bytes(op, dtype, wfmt, T, kd, nf, r);
+  return LORA_OK;
+}
+
 GemmArgs gemm_base() {
   GemmArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -374,15 +415,21 @@ const char *lora_strerror(int status) {
 
 size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, int64_t nf,
                             int64_t r) {
-  (void)wfmt;
+  if (op & ~(0xFF | LORA_WS_MINIMAL)) return 0;
+  const bool minimal = (op & LORA_WS_MINIMAL) != 0;
+  op &= 0xFF;
+  if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4) return 0;
   if (T < 0 || kd <= 0 || nf <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
   if (dtype == LORA_F32) return plan_f32(op, T, kd, nf, r);
   if (dtype != LORA_BF16) return 0;
+  // forwards copy only 4-bit weights (decoded); backwards copy every weight
+  // (transposed, decoded if 4-bit)
+  const bool fwd_copy = !minimal && wfmt == LORA_W_Q4, bwd_copy = !minimal;
   switch (op) {
-    case LORA_OP_LINEAR_FWD: return plan_lin_fwd(T, kd, nf, r).total;
-    case LORA_OP_LINEAR_BWD: return plan_lin_bwd(T, kd, nf, r).total;
-    case LORA_OP_MLP_FWD: return plan_mlp_fwd(T, kd, nf, r).total;
-    case LORA_OP_MLP_BWD: return plan_mlp_bwd(T, kd, nf, r).total;
+    case LORA_OP_LINEAR_FWD: return plan_lin_fwd(T, kd, nf, r, fwd_copy).total;
+    case LORA_OP_LINEAR_BWD: return plan_lin_bwd(T, kd, nf, r, bwd_copy).total;
+    case LORA_OP_MLP_FWD: return plan_mlp_fwd(T, kd, nf, r, fwd_copy).total;
+    case LORA_OP_MLP_BWD: return plan_mlp_bwd(T, kd, nf, r, bwd_copy).total;
   }
   return 0;
 }
@@ -395,9 +442,8 @@ int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
   LORA_TRY(check_weight(W, dtype, k, wv));
   LORA_TRY(check_ptrs({A, B}));
   LORA_TRY(check_tok_ptrs(T, {X, Y}));
-  const size_t need = lora_workspace_bytes(LORA_OP_LINEAR_FWD, dtype, W->fmt, T, k, n, r);
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
-  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  bool fast;
+  LORA_TRY(check_ws(LORA_OP_LINEAR_FWD, dtype, W->fmt, T, k, n, r, ws, ws_bytes, fast));
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
   if (T == 0) return LORA_OK;
@@ -406,9 +452,14 @@ int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
     return lin_fwd_f32(T, k, n, r, s, (const float *)X, (const float *)wv.w, (const float *)A,
                        (const float *)B, (float *)Y, (float *)w, st);
 
-  const LinFwdPlan pl = plan_lin_fwd(T, k, n, r);
+  const LinFwdPlan pl = plan_lin_fwd(T, k, n, r, fast && wv.q4);
   const int RS = rs_of(r);
   bf16_t *side = (bf16_t *)(w + pl.side), *epi = (bf16_t *)(w + pl.epi);
+  if (fast && wv.q4) {   // decode once, then the dense GEMM
+    bf16_t *wb = (bf16_t *)(w + pl.wbuf);
+    LORA_TRY(decode_w(wb, wv, n, k, st));
+    wv = dense_view(wb);
+  }
   LORA_TRY(build_side(side, RS, k, A, nullptr, r, k, 0, st));
   LORA_TRY(build_epi(epi, n, RS, B, nullptr, r, n, 0, st));
   GemmArgs a = gemm_base();
@@ -437,9 +488,8 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
   LORA_TRY(check_tok_ptrs(T, {X, dY}));
   if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
   if (flags & ~(uint32_t)LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
-  const size_t need = lora_workspace_bytes(LORA_OP_LINEAR_BWD, dtype, W->fmt, T, k, n, r);
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
-  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  bool fast;
+  LORA_TRY(check_ws(LORA_OP_LINEAR_BWD, dtype, W->fmt, T, k, n, r, ws, ws_bytes, fast));
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
   const bool acc = (flags & LORA_FLAG_ACCUMULATE_DX) != 0;
@@ -450,7 +500,7 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
                        (const float *)B, (const float *)dY, (float *)dX, acc, (float *)dA,
                        (float *)dB, G, H, st);
   }
-  const LinBwdPlan pl = plan_lin_bwd(T, k, n, r);
+  const LinBwdPlan pl = plan_lin_bwd(T, k, n, r, fast);
   const int RS = rs_of(r);
   bf16_t *side_nn = (bf16_t *)(w + pl.side_nn), *epi_nn = (bf16_t *)(w + pl.epi_nn);
   bf16_t *side_nt = (bf16_t *)(w + pl.side_nt);
@@ -469,12 +519,21 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
       GemmArgs a = gemm_base();
       a.M = (int)T; a.N = (int)k; a.K = (int)n; a.ksplit = (int)n;
       a.A0 = a.A1 = dYb; a.lda = n;
-      set_b(a, wv, wv); a.ldb = k;
+      bool nn = true, q4 = wv.q4;
+      if (fast) {   // W^T [k x n]: the NT GEMM reads it K-contiguous
+        bf16_t *wt = (bf16_t *)(w + pl.wbuf);
+        LORA_TRY(transpose_w(wt, n, wv, n, k, st));
+        const WeightView tv = dense_view(wt);
+        set_b(a, tv, tv); a.ldb = n;
+        nn = false; q4 = false;
+      } else {
+        set_b(a, wv, wv); a.ldb = k;
+      }
       a.rs = RS; a.epi = epi_nn;
       a.accumulate = acc; a.C = (bf16_t *)dX; a.ldc = k;
       a.hglob = gbf;
       a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
-      LORA_TRY(run_gemm(LORA_KC_LINEAR_DX, true, wv.q4, EPI_STORE, a, st));
+      LORA_TRY(run_gemm(LORA_KC_LINEAR_DX, nn, q4, EPI_STORE, a, st));
     }
     LORA_TRY(skinny_nt(RS, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,
                        nullptr, 1.f, st));
@@ -500,9 +559,8 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   if (wg.q4 != wu.q4) return LORA_ERR_UNSUPPORTED;
   LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd}));
   LORA_TRY(check_tok_ptrs(T, {X, Y, e_saved, g_saved}));
-  const size_t need = lora_workspace_bytes(LORA_OP_MLP_FWD, dtype, Wg->fmt, T, d, f, r);
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
-  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  bool fast;
+  LORA_TRY(check_ws(LORA_OP_MLP_FWD, dtype, Wg->fmt, T, d, f, r, ws, ws_bytes, fast));
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
   if (T == 0) return LORA_OK;
@@ -519,7 +577,15 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     return lin_fwd_f32(T, f, d, r, s, h, (const float *)wd.w, (const float *)Ad,
                        (const float *)Bd, (float *)Y, H, st);
   }
-  const MlpFwdPlan pl = plan_mlp_fwd(T, d, f, r);
+  const bool wcopy = fast && wg.q4;   // the plan holds a weight buffer
+  const MlpFwdPlan pl = plan_mlp_fwd(T, d, f, r, wcopy);
+  bf16_t *wb = (bf16_t *)(w + pl.wbuf);
+  if (wcopy) {   // decode Wg, Wu once, then the dense GEMM
+    LORA_TRY(decode_w(wb, wg, f, d, st));
+    LORA_TRY(decode_w(wb + f * d, wu, f, d, st));
+    wg = dense_view(wb);
+    wu = dense_view(wb + f * d);
+  }
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   bf16_t *h = (bf16_t *)(w + pl.h);
   bf16_t *side_gu = (bf16_t *)(w + pl.side_gu), *epi_gu = (bf16_t *)(w + pl.epi_gu);
@@ -548,6 +614,10 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(run_gemm(LORA_KC_GATEUP_FWD, false, wg.q4, EPI_SWIGLU_FWD, a, st));
 
   // down
+  if (wcopy && wd.q4) {   // reuses the buffer once the gate/up GEMM is done
+    LORA_TRY(decode_w(wb, wd, d, f, st));
+    wd = dense_view(wb);
+  }
   GemmArgs b = gemm_base();
   b.M = (int)T; b.N = (int)d; b.K = (int)f; b.ksplit = (int)f;
   b.A0 = b.A1 = h; b.lda = f;
@@ -578,9 +648,8 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd, dAg, dBg, dAu, dBu, dAd, dBd}));
   LORA_TRY(check_tok_ptrs(T, {X, e_saved, g_saved, dY}));
   if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
-  const size_t need = lora_workspace_bytes(LORA_OP_MLP_BWD, dtype, Wg->fmt, T, d, f, r);
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
-  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  bool fast;
+  LORA_TRY(check_ws(LORA_OP_MLP_BWD, dtype, Wg->fmt, T, d, f, r, ws, ws_bytes, fast));
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
   char *w = (char *)ws;
@@ -609,7 +678,8 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
                        st);
   }
 
-  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r);
+  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r, fast);
+  bf16_t *wt = (bf16_t *)(w + pl.wbuf);
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   bf16_t *de = (bf16_t *)(w + pl.de), *dg = (bf16_t *)(w + pl.dg);
   bf16_t *side_d_nn = (bf16_t *)(w + pl.side_d_nn), *epi_d_nn = (bf16_t *)(w + pl.epi_d_nn);
@@ -638,12 +708,20 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     GemmArgs a = gemm_base();
     a.M = (int)T; a.N = (int)f; a.K = (int)d; a.ksplit = (int)d;
     a.A0 = a.A1 = dYb; a.lda = d;
-    set_b(a, wd, wd); a.ldb = f;
+    bool nn = true, q4 = wd.q4;
+    if (fast) {   // Wd^T [f x d]
+      LORA_TRY(transpose_w(wt, d, wd, d, f, st));
+      const WeightView tv = dense_view(wt);
+      set_b(a, tv, tv); a.ldb = d;
+      nn = false; q4 = false;
+    } else {
+      set_b(a, wd, wd); a.ldb = f;
+    }
     a.rs = RS2; a.epi = epi_d_nn;
     a.Ein = eb; a.Gin = gb; a.DE = de; a.DG = dg;
     a.hglob = gdbf;
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
-    LORA_TRY(run_gemm(LORA_KC_DOWN_BWD, true, wd.q4, EPI_SWIGLU_BWD, a, st));
+    LORA_TRY(run_gemm(LORA_KC_DOWN_BWD, nn, q4, EPI_SWIGLU_BWD, a, st));
     // 2. H_d = h Ad^T with h recomputed from e, g
     LORA_TRY(skinny_nt(RS2, true, T, f, nullptr, nullptr, f, f, eb, gb, side_d_nt, ntpart, hd32,
                        nullptr, 1.f, st));
@@ -662,12 +740,21 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
       GemmArgs b = gemm_base();
       b.M = (int)T; b.N = (int)d; b.K = (int)(2 * f); b.ksplit = (int)f;
       b.A0 = de; b.A1 = dg; b.lda = f;
-      set_b(b, wg, wu); b.ldb = d;
+      bool nn = true, q4 = wg.q4;
+      if (fast) {   // [Wg^T | Wu^T] [d x 2f], over Wd^T (its GEMM is done)
+        LORA_TRY(transpose_w(wt, 2 * f, wg, f, d, st));
+        LORA_TRY(transpose_w(wt + f, 2 * f, wu, f, d, st));
+        const WeightView tv = dense_view(wt);
+        set_b(b, tv, tv); b.ldb = 2 * f;
+        nn = false; q4 = false;
+      } else {
+        set_b(b, wg, wu); b.ldb = d;
+      }
       b.rs = RS1; b.epi = epi_gu_nn;
       b.C = (bf16_t *)dX; b.ldc = d;
       b.hglob = ggubf;
       b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
-      LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, true, wg.q4, EPI_STORE, b, st));
+      LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, nn, q4, EPI_STORE, b, st));
     }
     // 5. H_gu = X [Ag; Au]^T
     LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,

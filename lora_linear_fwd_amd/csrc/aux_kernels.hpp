@@ -320,6 +320,65 @@ __global__ __launch_bounds__(256) void k_dequant4(const uint8_t *codes, const fl
 }
 
 // ---------------------------------------------------------------------------
+// Transposed copies of a frozen base weight for the backward dX GEMMs, so
+// they read the weight K-contiguous like the forward GEMMs.  HBM-bound.
+//   k_transpose_bf16: out[c * ld_out + r] = in[r * ld_in + c]
+//   k_dequant4_t:     out[c * ld_out + r] = decode(W)[r][c]  (4-bit W [rows x cols])
+// rows and cols are multiples of 8 (cols of 64 for the 4-bit form).  A thread
+// moves 8 rows x 8 columns (transpose) or 8 rows x 32 columns (decode)
+// through registers with 8 x 8 register transposes; a wave's loads and
+// stores cover 128-byte row segments.  Block b covers column block b % ncb
+// and row block b / ncb (a 1-D grid, so neither extent is capped at 65535).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_transpose_bf16(const bf16_t *in, int rows, int cols,
+                                                        int64_t ld_in, bf16_t *out,
+                                                        int64_t ld_out, int ncb) {
+  const int cc = threadIdx.x & 7, rb = threadIdx.x >> 3;
+  const int c0 = (int)(blockIdx.x % (unsigned)ncb) * 64 + cc * 8;
+  const int r0 = (int)(blockIdx.x / (unsigned)ncb) * 256 + rb * 8;
+  if (c0 >= cols || r0 >= rows) return;
+  u32x4 v[8], t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = gload16(in + (int64_t)(r0 + i) * ld_in + c0);
+  transpose8x8(v, t);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gstore16(out + (int64_t)(c0 + j) * ld_out + r0, t[j]);
+}
+
+__global__ __launch_bounds__(256) void k_dequant4_t(const uint8_t *codes, const float *absmax,
+                                                    const float *codebook, int rows, int cols,
+                                                    bf16_t *out, int64_t ld_out, int ncb) {
+  __shared__ float2 cbt[256];
+  cbt[threadIdx.x] = make_float2(codebook[threadIdx.x & 15], codebook[threadIdx.x >> 4]);
+  __syncthreads();
+  const int cc = threadIdx.x & 7, rb = threadIdx.x >> 3;
+  const int c0 = (int)(blockIdx.x % (unsigned)ncb) * 256 + cc * 32;   // 16 code bytes
+  const int r0 = (int)(blockIdx.x / (unsigned)ncb) * 256 + rb * 8;
+  if (c0 >= cols || r0 >= rows) return;
+  u32x4 v[4][8];   // [8-column group][row]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t e0 = (int64_t)(r0 + i) * cols + c0;   // flat element index
+    const u32x4 c = gload16(codes + e0 / 2);
+    const float am = absmax[e0 >> 6];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float2 cv = cbt[(c[w] >> (8 * b)) & 0xFFu];
+        v[w][i][b] = pack_bf16x2(cv.x * am, cv.y * am);
+      }
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    u32x4 t[8];
+    transpose8x8(v[w], t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gstore16(out + (int64_t)(c0 + 8 * w + j) * ld_out + r0, t[j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: generic strided GEMM with fp32 FMA (no matrix cores, so the
 // arithmetic stays IEEE fp32):
 //   C[m][n] = alpha * sum_k A(m,k) B(k,n) + beta * C[m][n]

@@ -5,6 +5,7 @@ namespace lora {
 hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st) {
   if (epi == EPI_STORE) return launch_gemm_t<B_NT, EPI_STORE>(a, st);
   if (epi == EPI_SWIGLU_FWD) return launch_gemm_t<B_NT, EPI_SWIGLU_FWD>(a, st);
+  if (epi == EPI_SWIGLU_BWD) return launch_gemm_t<B_NT, EPI_SWIGLU_BWD>(a, st);
   return hipErrorInvalidValue;
 }
 }  // namespace lora

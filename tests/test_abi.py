@@ -60,6 +60,30 @@ def test_workspace_bytes_rules():
     # MLP backward holds de, dg
     assert wb(L.OP_MLP_BWD, L.LORA_BF16, 0, 8192, 4096, 14336, 16) >= 2 * 8192 * 14336 * 2
     assert wb(L.OP_LINEAR_BWD, L.LORA_F32, 0, 256, 512, 512, 8) == 2 * 256 * 8 * 4
+    assert wb(L.OP_MLP_FWD | 0x200, L.LORA_BF16, 0, 8192, 4096, 14336, 16) == 0
+    assert wb(L.OP_MLP_FWD, L.LORA_BF16, 5, 8192, 4096, 14336, 16) == 0
+
+
+def test_workspace_strategies():
+    """The fast size adds exactly the weight copies to the minimal size."""
+    wb, M = L.workspace_bytes, L.LORA_WS_MINIMAL
+    T, d, f, r = 8192, 4096, 14336, 16
+    # dense forwards copy nothing
+    for op, kd, nf in ((L.OP_LINEAR_FWD, d, f), (L.OP_MLP_FWD, d, f)):
+        assert wb(op, L.LORA_BF16, 0, T, kd, nf, r) == wb(op | M, L.LORA_BF16, 0, T, kd, nf, r)
+    # 4-bit forwards hold decoded weights: W [n x k]; MLP Wg | Wu (Wd reuses it)
+    assert (wb(L.OP_LINEAR_FWD, L.LORA_BF16, 1, T, d, f, r)
+            - wb(L.OP_LINEAR_FWD | M, L.LORA_BF16, 1, T, d, f, r)) == f * d * 2
+    assert (wb(L.OP_MLP_FWD, L.LORA_BF16, 1, T, d, f, r)
+            - wb(L.OP_MLP_FWD | M, L.LORA_BF16, 1, T, d, f, r)) == 2 * f * d * 2
+    # backwards hold transposed weights: W^T; MLP [Wg^T | Wu^T] (Wd^T reuses it)
+    for fmt in (0, 1):
+        assert (wb(L.OP_LINEAR_BWD, L.LORA_BF16, fmt, T, d, f, r)
+                - wb(L.OP_LINEAR_BWD | M, L.LORA_BF16, fmt, T, d, f, r)) == f * d * 2
+        assert (wb(L.OP_MLP_BWD, L.LORA_BF16, fmt, T, d, f, r)
+                - wb(L.OP_MLP_BWD | M, L.LORA_BF16, fmt, T, d, f, r)) == 2 * f * d * 2
+    # fp32 has one strategy
+    assert wb(L.OP_MLP_BWD, L.LORA_F32, 0, 67, 48, 80, 5) == wb(L.OP_MLP_BWD | M, L.LORA_F32, 0, 67, 48, 80, 5)
 
 
 # fake, aligned, non-null host addresses: every call below fails validation

@@ -20,18 +20,26 @@ def _sync():
     torch.cuda.synchronize()
 
 
-def run_linear(li, need_dx=True):
+# the two workspace strategies: "fast" (weight copied transposed / decoded
+# into the workspace, NT GEMMs) and "minimal" (weight read in place: NN
+# GEMMs for dX, 4-bit codes decoded inside the GEMM)
+WS_MODES = ["fast", "minimal"]
+
+
+def run_linear(li, need_dx=True, ws="fast"):
     Wd, Wref = linear_weight(li)
     X, A, B, dY = (dev(v, li.dtype) for v in (li.X, li.A, li.B, li.dY))
-    Y = L.lora_linear_fwd(X, Wd, A, B, li.alpha)
-    dX, dA, dB = L.lora_linear_bwd(X, Wd, A, B, li.alpha, dY, need_dx=need_dx)
+    mw = ws == "minimal"
+    Y = L.lora_linear_fwd(X, Wd, A, B, li.alpha, minimal_workspace=mw)
+    dX, dA, dB = L.lora_linear_bwd(X, Wd, A, B, li.alpha, dY, need_dx=need_dx,
+                                   minimal_workspace=mw)
     _sync()
     return Wref, (Y, dX, dA, dB)
 
 
-def check_linear(li, need_dx=True):
+def check_linear(li, need_dx=True, ws="fast"):
     s = oracle.scaling(li.alpha, li.r)
-    Wref, (Y, dX, dA, dB) = run_linear(li, need_dx)
+    Wref, (Y, dX, dA, dB) = run_linear(li, need_dx, ws)
     Yr = oracle.linear_fwd(li.X, Wref, li.A, li.B, s)
     dXr, dAr, dBr = oracle.linear_bwd(li.X, Wref, li.A, li.B, s, li.dY)
     check("Y", host(Y), Yr, li.dtype)
@@ -52,11 +60,12 @@ LINEAR_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("ws", WS_MODES)
 @pytest.mark.parametrize("shape", LINEAR_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_linear_bf16(shape):
+def test_linear_bf16(shape, ws):
     T, k, n, r = shape
-    log(f"linear bf16 T={T} k={k} n={n} r={r}")
-    check_linear(gen_linear(T, k, n, r, 16.0, "bf16", seed=T + k + n + r))
+    log(f"linear bf16 T={T} k={k} n={n} r={r} ws={ws}")
+    check_linear(gen_linear(T, k, n, r, 16.0, "bf16", seed=T + k + n + r), ws=ws)
 
 
 @pytest.mark.parametrize("shape", [(300, 320, 520, 16), (260, 256, 136, 64)],
@@ -82,10 +91,11 @@ def test_linear_fp32(shape):
     check_linear(gen_linear(T, k, n, r, 16.0, "f32", seed=T * 3 + 1))
 
 
-def test_linear_q4():
-    log("linear q4 T=300 k=320 n=264 r=16")
-    check_linear(gen_linear(300, 320, 264, 16, 16.0, "bf16", seed=11, q4=True))
-    check_linear(gen_linear(77, 128, 136, 16, 16.0, "bf16", seed=12, q4=True, b_std=1.0))
+@pytest.mark.parametrize("ws", WS_MODES)
+def test_linear_q4(ws):
+    log(f"linear q4 T=300 k=320 n=264 r=16 ws={ws}")
+    check_linear(gen_linear(300, 320, 264, 16, 16.0, "bf16", seed=11, q4=True), ws=ws)
+    check_linear(gen_linear(77, 128, 136, 16, 16.0, "bf16", seed=12, q4=True, b_std=1.0), ws=ws)
 
 
 def test_linear_B_zero_is_base_layer():
@@ -137,20 +147,22 @@ def test_linear_deterministic():
 
 
 # ------------------------------------------------------------------ MLP
-def run_mlp(mi, need_dx=True):
+def run_mlp(mi, need_dx=True, ws="fast"):
     Wd, Wref = mlp_weights(mi)
     X, dY = dev(mi.X, mi.dtype), dev(mi.dY, mi.dtype)
     A = {p: dev(mi.A[p], mi.dtype) for p in mi.A}
     B = {p: dev(mi.B[p], mi.dtype) for p in mi.B}
-    Y, e, g = L.lora_swiglu_mlp_fwd(X, Wd, A, B, mi.alpha)
-    grads = L.lora_swiglu_mlp_bwd(X, Wd, A, B, mi.alpha, e, g, dY, need_dx=need_dx)
+    mw = ws == "minimal"
+    Y, e, g = L.lora_swiglu_mlp_fwd(X, Wd, A, B, mi.alpha, minimal_workspace=mw)
+    grads = L.lora_swiglu_mlp_bwd(X, Wd, A, B, mi.alpha, e, g, dY, need_dx=need_dx,
+                                  minimal_workspace=mw)
     _sync()
     return Wref, Y, e, g, grads
 
 
-def check_mlp(mi, need_dx=True):
+def check_mlp(mi, need_dx=True, ws="fast"):
     s = oracle.scaling(mi.alpha, mi.r)
-    Wref, Y, e, g, grads = run_mlp(mi, need_dx)
+    Wref, Y, e, g, grads = run_mlp(mi, need_dx, ws)
     Yr, er, gr = oracle.mlp_fwd(mi.X, Wref, mi.A, mi.B, s)
     check("Y", host(Y), Yr, mi.dtype)
     check("e", host(e), er, mi.dtype)
@@ -171,11 +183,12 @@ MLP_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("ws", WS_MODES)
 @pytest.mark.parametrize("shape", MLP_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_mlp_bf16(shape):
+def test_mlp_bf16(shape, ws):
     T, d, f, r = shape
-    log(f"mlp bf16 T={T} d={d} f={f} r={r}")
-    check_mlp(gen_mlp(T, d, f, r, 16.0, "bf16", seed=T + d + f + r))
+    log(f"mlp bf16 T={T} d={d} f={f} r={r} ws={ws}")
+    check_mlp(gen_mlp(T, d, f, r, 16.0, "bf16", seed=T + d + f + r), ws=ws)
 
 
 def test_mlp_bf16_lora_dominant():
@@ -192,10 +205,11 @@ def test_mlp_fp32():
     check_mlp(gen_mlp(67, 48, 80, 5, 16.0, "f32", seed=23))
 
 
-def test_mlp_q4():
-    log("mlp q4 T=300 d=256 f=576 r=16")
-    check_mlp(gen_mlp(300, 256, 576, 16, 16.0, "bf16", seed=24, q4=True))
-    check_mlp(gen_mlp(70, 128, 192, 16, 16.0, "bf16", seed=25, q4=True, b_std=1.0))
+@pytest.mark.parametrize("ws", WS_MODES)
+def test_mlp_q4(ws):
+    log(f"mlp q4 T=300 d=256 f=576 r=16 ws={ws}")
+    check_mlp(gen_mlp(300, 256, 576, 16, 16.0, "bf16", seed=24, q4=True), ws=ws)
+    check_mlp(gen_mlp(70, 128, 192, 16, 16.0, "bf16", seed=25, q4=True, b_std=1.0), ws=ws)
 
 
 def test_mlp_T_zero():
