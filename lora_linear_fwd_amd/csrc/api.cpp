@@ -214,24 +214,36 @@ int check_tok_ptrs(int64_t T, std::initializer_list<const void *> ps) {
 inline unsigned blocks_for(int64_t count, int per = 256) { return (unsigned)cdiv(count, per); }
 
 // ------------------------------------------------------------ bf16 helpers
-int build_side(bf16_t *dst, int RS, int64_t K, const void *src0, const void *src1, int64_t r,
-               int64_t ksplit, int tr, hipStream_t st) {
-  const int64_t cnt = (int64_t)RS * K;
-  if (cnt == 0) return LORA_OK;
-  hipLaunchKernelGGL(k_build_side, dim3(blocks_for(cnt)), dim3(256), 0, st, dst, RS, (int)K,
-                     (const bf16_t *)src0, (const bf16_t *)src1, (int)r, (int)ksplit, tr);
-  HIP_TRY(hipGetLastError());
-  return LORA_OK;
-}
-int build_epi(bf16_t *dst, int64_t rows, int RS, const void *src0, const void *src1, int64_t r,
-              int64_t rsplit, int tr, hipStream_t st) {
-  const int64_t cnt = rows * RS;
-  if (cnt == 0) return LORA_OK;
-  hipLaunchKernelGGL(k_build_epi, dim3(blocks_for(cnt)), dim3(256), 0, st, dst, (int)rows, RS,
-                     (const bf16_t *)src0, (const bf16_t *)src1, (int)r, (int)rsplit, tr);
-  HIP_TRY(hipGetLastError());
-  return LORA_OK;
-}
+// Collects the call's small operand copies (zero-padded side / epilogue
+// operands, layouts as documented at k_prep) and launches them at once.
+struct Prep {
+  PrepBatch b{};
+  unsigned blocks = 0;
+  void add(int kind, bf16_t *dst, int64_t a, int64_t bb, const void *src0, const void *src1,
+           int64_t r, int64_t split, int tr) {
+    const int64_t cnt = a * bb;
+    if (cnt == 0) return;
+    PrepJob &j = b.job[b.njobs];
+    j = PrepJob{dst, (const bf16_t *)src0, (const bf16_t *)src1, kind, (int)a, (int)bb, (int)r,
+                (int)split, tr};
+    b.start[b.njobs] = blocks;
+    blocks += (unsigned)cdiv(cnt, 256);
+    ++b.njobs;
+  }
+  // side[q][k], q < RS, k < K
+  void side(bf16_t *dst, int RS, int64_t K, const void *s0, const void *s1, int64_t r,
+            int64_t ksplit, int tr) { add(0, dst, RS, K, s0, s1, r, ksplit, tr); }
+  // epi[row][q], row < rows, q < RS
+  void epi(bf16_t *dst, int64_t rows, int RS, const void *s0, const void *s1, int64_t r,
+           int64_t rsplit, int tr) { add(1, dst, rows, RS, s0, s1, r, rsplit, tr); }
+  int launch(hipStream_t st) {
+    if (!b.njobs) return LORA_OK;
+    b.start[b.njobs] = blocks;
+    hipLaunchKernelGGL(k_prep, dim3(blocks), dim3(256), 0, st, b);
+    HIP_TRY(hipGetLastError());
+    return LORA_OK;
+  }
+};
 
 // out = Z . SIDE^T over all K (deterministic split-K); fp32 and/or scaled bf16
 int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, const bf16_t *Z1,
@@ -460,8 +472,10 @@ int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
     LORA_TRY(decode_w(wb, wv, n, k, st));
     wv = dense_view(wb);
   }
-  LORA_TRY(build_side(side, RS, k, A, nullptr, r, k, 0, st));
-  LORA_TRY(build_epi(epi, n, RS, B, nullptr, r, n, 0, st));
+  Prep prep;
+  prep.side(side, RS, k, A, nullptr, r, k, 0);
+  prep.epi(epi, n, RS, B, nullptr, r, n, 0);
+  LORA_TRY(prep.launch(st));
   GemmArgs a = gemm_base();
   a.M = (int)T; a.N = (int)n; a.K = (int)k; a.ksplit = (int)k;
   a.A0 = a.A1 = (const bf16_t *)X; a.lda = k;
@@ -507,9 +521,11 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
   float *g32 = (float *)(w + pl.g32), *h32 = (float *)(w + pl.h32);
   bf16_t *gbf = (bf16_t *)(w + pl.gbf);
   float *ntpart = (float *)(w + pl.ntpart), *tnpart = (float *)(w + pl.tnpart);
-  LORA_TRY(build_side(side_nn, RS, n, B, nullptr, r, n, 1, st));   // B^T padded [RS x n]
-  LORA_TRY(build_epi(epi_nn, k, RS, A, nullptr, r, k, 1, st));     // A^T padded [k x RS]
-  LORA_TRY(build_side(side_nt, RS, k, A, nullptr, r, k, 0, st));   // A padded [RS x k]
+  Prep prep;
+  prep.side(side_nn, RS, n, B, nullptr, r, n, 1);   // B^T padded [RS x n]
+  prep.epi(epi_nn, k, RS, A, nullptr, r, k, 1);     // A^T padded [k x RS]
+  prep.side(side_nt, RS, k, A, nullptr, r, k, 0);   // A padded [RS x k]
+  LORA_TRY(prep.launch(st));
   const bf16_t *Xb = (const bf16_t *)X, *dYb = (const bf16_t *)dY;
   if (T > 0) {
     // G = dY B (fp32 for dA, s G in bf16 for the dX epilogue)
@@ -592,10 +608,12 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   bf16_t *side_d = (bf16_t *)(w + pl.side_d), *epi_d = (bf16_t *)(w + pl.epi_d);
   bf16_t *hbf = (bf16_t *)(w + pl.hbf);
   float *hpart = (float *)(w + pl.hpart);
-  LORA_TRY(build_side(side_gu, RS1, d, Ag, Au, r, d, 0, st));
-  LORA_TRY(build_epi(epi_gu, 2 * f, RS1, Bg, Bu, r, f, 0, st));
-  LORA_TRY(build_side(side_d, RS2, f, Ad, nullptr, r, f, 0, st));
-  LORA_TRY(build_epi(epi_d, d, RS2, Bd, nullptr, r, d, 0, st));
+  Prep prep;
+  prep.side(side_gu, RS1, d, Ag, Au, r, d, 0);
+  prep.epi(epi_gu, 2 * f, RS1, Bg, Bu, r, f, 0);
+  prep.side(side_d, RS2, f, Ad, nullptr, r, f, 0);
+  prep.epi(epi_d, d, RS2, Bd, nullptr, r, d, 0);
+  LORA_TRY(prep.launch(st));
   const bf16_t *Xb = (const bf16_t *)X;
 
   // gate + up with the SwiGLU epilogue
@@ -693,12 +711,14 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   const bf16_t *Xb = (const bf16_t *)X, *dYb = (const bf16_t *)dY;
   const bf16_t *eb = (const bf16_t *)e_saved, *gb = (const bf16_t *)g_saved;
 
-  LORA_TRY(build_side(side_d_nn, RS2, d, Bd, nullptr, r, d, 1, st));       // Bd^T [RS2 x d]
-  LORA_TRY(build_epi(epi_d_nn, f, RS2, Ad, nullptr, r, f, 1, st));         // Ad^T [f x RS2]
-  LORA_TRY(build_side(side_d_nt, RS2, f, Ad, nullptr, r, f, 0, st));       // Ad   [RS2 x f]
-  LORA_TRY(build_side(side_gu_nn, RS1, 2 * f, Bg, Bu, r, f, 1, st));       // blockdiag(Bg,Bu)^T
-  LORA_TRY(build_epi(epi_gu_nn, d, RS1, Ag, Au, r, d, 1, st));             // [Ag;Au]^T [d x RS1]
-  LORA_TRY(build_side(side_gu_nt, RS1, d, Ag, Au, r, d, 0, st));           // [Ag;Au] [RS1 x d]
+  Prep prep;
+  prep.side(side_d_nn, RS2, d, Bd, nullptr, r, d, 1);       // Bd^T [RS2 x d]
+  prep.epi(epi_d_nn, f, RS2, Ad, nullptr, r, f, 1);         // Ad^T [f x RS2]
+  prep.side(side_d_nt, RS2, f, Ad, nullptr, r, f, 0);       // Ad   [RS2 x f]
+  prep.side(side_gu_nn, RS1, 2 * f, Bg, Bu, r, f, 1);       // blockdiag(Bg,Bu)^T
+  prep.epi(epi_gu_nn, d, RS1, Ag, Au, r, d, 1);             // [Ag;Au]^T [d x RS1]
+  prep.side(side_gu_nt, RS1, d, Ag, Au, r, d, 0);           // [Ag;Au] [RS1 x d]
+  LORA_TRY(prep.launch(st));
 
   if (T > 0) {
     // 1. dh = dY Wd + s (dY Bd) Ad with the SwiGLU-derivative epilogue -> de, dg

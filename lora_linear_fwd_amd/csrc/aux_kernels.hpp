@@ -241,56 +241,60 @@ __global__ void k_reduce_tn(const ReduceTNArgs a) {
 //   !tr: q < r -> src0[q][k] (ld K); r <= q < 2r -> src1[q-r][k]
 //    tr: k < ksplit: q < r -> src0[k][q] (ld r);  k >= ksplit: r <= q < 2r ->
 //        src1[k-ksplit][q-r]
-// ---------------------------------------------------------------------------
-__global__ void k_build_side(bf16_t *dst, int RS, int K, const bf16_t *src0, const bf16_t *src1,
-                             int r, int ksplit, int tr) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)RS * K) return;
-  const int q = (int)(i / K), k = (int)(i % K);
-  bf16_t v = 0;
-  if (!tr) {
-    if (q < r) v = src0[(int64_t)q * K + k];
-    else if (src1 && q < 2 * r) v = src1[(int64_t)(q - r) * K + k];
-  } else {
-    if (k < ksplit) {
-      if (q < r) v = src0[(int64_t)k * r + q];
-    } else if (src1 && q >= r && q < 2 * r) {
-      v = src1[(int64_t)(k - ksplit) * r + (q - r)];
-    }
-  }
-  dst[i] = v;
-}
-
 // epi[row][q], row < rows, q < RS:
 //   !tr (from B [rows x r]): row < rsplit: q < r -> src0[row][q];
 //                            row >= rsplit: r <= q < 2r -> src1[row-rsplit][q-r]
 //    tr (from A [r x rows]): q < r -> src0[q][row]; r <= q < 2r -> src1[q-r][row]
-__global__ void k_build_epi(bf16_t *dst, int rows, int RS, const bf16_t *src0, const bf16_t *src1,
-                            int r, int rsplit, int tr) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)rows * RS) return;
-  const int row = (int)(i / RS), q = (int)(i % RS);
+// Every other element is zero.
+// ---------------------------------------------------------------------------
+// All the small operand copies of one call in a single launch: block b
+// works on the job whose block range [start[j], start[j+1]) holds b.
+struct PrepJob {
+  bf16_t *dst;
+  const bf16_t *src0, *src1;
+  int kind;            // 0: side [a = RS x b = K], 1: epi [a = rows x b = RS]
+  int a, b, r, split, tr;
+};
+constexpr int kMaxPrepJobs = 8;
+struct PrepBatch {
+  PrepJob job[kMaxPrepJobs];
+  unsigned start[kMaxPrepJobs + 1];
+  int njobs;
+};
+__global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
+  int j = 0;
+  while (j + 1 < pb.njobs && blockIdx.x >= pb.start[j + 1]) ++j;
+  const PrepJob &jb = pb.job[j];
+  const int64_t i = (int64_t)(blockIdx.x - pb.start[j]) * 256 + threadIdx.x;
+  if (i >= (int64_t)jb.a * jb.b) return;
+  const int r = jb.r;
   bf16_t v = 0;
-  if (!tr) {
-    if (row < rsplit) {
-      if (q < r) v = src0[(int64_t)row * r + q];
-    } else if (src1 && q >= r && q < 2 * r) {
-      v = src1[(int64_t)(row - rsplit) * r + (q - r)];
+  if (jb.kind == 0) {   // side[q][k]
+    const int K = jb.b, q = (int)(i / K), k = (int)(i % K);
+    if (!jb.tr) {
+      if (q < r) v = jb.src0[(int64_t)q * K + k];
+      else if (jb.src1 && q < 2 * r) v = jb.src1[(int64_t)(q - r) * K + k];
+    } else {
+      if (k < jb.split) {
+        if (q < r) v = jb.src0[(int64_t)k * r + q];
+      } else if (jb.src1 && q >= r && q < 2 * r) {
+        v = jb.src1[(int64_t)(k - jb.split) * r + (q - r)];
+      }
     }
-  } else {
-    if (q < r) v = src0[(int64_t)q * rows + row];
-    else if (src1 && q < 2 * r) v = src1[(int64_t)(q - r) * rows + row];
+  } else {              // epi[row][q]
+    const int rows = jb.a, RS = jb.b, row = (int)(i / RS), q = (int)(i % RS);
+    if (!jb.tr) {
+      if (row < jb.split) {
+        if (q < r) v = jb.src0[(int64_t)row * r + q];
+      } else if (jb.src1 && q >= r && q < 2 * r) {
+        v = jb.src1[(int64_t)(row - jb.split) * r + (q - r)];
+      }
+    } else {
+      if (q < r) v = jb.src0[(int64_t)q * rows + row];
+      else if (jb.src1 && q < 2 * r) v = jb.src1[(int64_t)(q - r) * rows + row];
+    }
   }
-  dst[i] = v;
-}
-
-__global__ void k_fill_u16(bf16_t *dst, int64_t count, bf16_t v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) dst[i] = v;
-}
-__global__ void k_fill_f32(float *dst, int64_t count, float v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) dst[i] = v;
+  jb.dst[i] = v;
 }
 
 // ---------------------------------------------------------------------------

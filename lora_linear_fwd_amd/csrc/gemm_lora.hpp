@@ -137,7 +137,9 @@ struct Stage {  // sized for BK <= 64
   float qs[(BMODE == B_NN_Q4) ? 8 : 1];
 };
 
-template <int BMODE, int EPI, int BK = kBK, int NSTAGE = kNSTAGE>
+// PF (dense NT form only): each K step also warms L2 for the step PF steps
+// after the one it loads (0 = off)
+template <int BMODE, int EPI, int PF = 0, int BK = kBK, int NSTAGE = kNSTAGE>
 __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
@@ -247,11 +249,46 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     }
   }
 
+  const int nkt = (K + BK - 1) / BK;
+  // ------------------------------------------------ L2 prefetch (dense NT)
+  // Every operand row of a K step is one 128-byte line per operand.  Lane
+  // (wave, l) touches the line of tile row 64 wave + l of A_op and of B_op
+  // with a 4-byte LDS-DMA load into a scratch slot nobody reads, PF steps
+  // before the step's real DMA; the loads ride in the same in-order vmcnt
+  // queue as the stage loads.
+  constexpr bool DOPF = (BMODE == B_NT) && (BK == 64) && (PF > 0);
+  char *pf_lds = smem + NSTAGE * STAGE + wave * 512;
+  uint32_t pfa = kOOB, pfb = kOOB;
+  __amdgpu_buffer_rsrc_t rsPB;
+  if constexpr (DOPF) {
+    const int pr = wave * 64 + lane;
+    if (m0 + pr < M) pfa = (uint32_t)(pr * p.lda * 2);
+    if constexpr (GU) {
+      const int jl = (pr >> 7) * 64 + (pr & 63);
+      if (tn * 128 + jl < p.gu_f) pfb = (uint32_t)(jl * p.ldb * 2);
+      rsPB = (wave & 1) ? rsB1 : rsB0;
+    } else {
+      if (n0 + pr < N) pfb = (uint32_t)(pr * p.ldb * 2);
+      rsPB = rsB0;
+    }
+  }
+  auto issue_pf = [&](int kt) {
+    if constexpr (DOPF) {
+      const int k0 = kt * BK;
+      const bool live = kt < nkt;
+      const uint32_t sa = live ? 2u * (uint32_t)k0 + (k0 >= ksplit ? dA1 : 0u) : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (__attribute__((address_space(3))) void *)pf_lds, 4, live ? pfa : kOOB, sa, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsPB, (__attribute__((address_space(3))) void *)(pf_lds + 256), 4, live ? pfb : kOOB,
+          live ? 2u * (uint32_t)k0 : 0u, 0, 0);
+    }
+  };
+
   // ---------------------------------------- DMA of K step kt into a stage
   // Steps past the end issue loads whose lanes are all out of range (they
   // write zeros into a stage nobody reads), which keeps the per-wave count
   // of outstanding loads uniform for the vmcnt waits.
-  const int nkt = (K + BK - 1) / BK;
   auto issue_dma = [&](int kt, char *stage) {
     const int k0 = kt * BK;
     char *Xs = stage, *Ws = stage + XS;
@@ -386,6 +423,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   if constexpr (Q4) load_q4(st, 0);
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i) issue_dma(i, smem + i * STAGE);
+  if constexpr (DOPF) {
+#pragma unroll
+    for (int i = NSTAGE; i < NSTAGE - 1 + PF; ++i) issue_pf(i);
+  }
   wait_vmem();
   if constexpr (Q4) commit_q4(st, smem);
   __syncthreads();
@@ -401,13 +442,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   // step's last 16-K sub-step, whose MFMAs overlap the next stage's first
   // fragment reads.
   constexpr int kDmaPerStep = NDMA + ((BMODE == B_NT || BMODE == B_NN) ? NDMA : 0);
-  constexpr int kWaitDense = (NSTAGE - 2) * kDmaPerStep;
+  constexpr int kWaitDense = (NSTAGE - 2) * kDmaPerStep + (DOPF ? 2 : 0);
   constexpr int kWaitQ4 = NSTAGE == 2 ? 0 : kDmaPerStep;
   for (int kt = 0; kt < nkt; ++kt) {
     const char *cur = smem + (kt % NSTAGE) * STAGE;
     char *nxt = smem + ((kt + 1) % NSTAGE) * STAGE;
     if constexpr (Q4) load_q4(st, kt + 1);
     issue_dma(kt + NSTAGE - 1, smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE);
+    issue_pf(kt + NSTAGE - 1 + PF);
 #pragma unroll
     for (int kk = 0; kk + 1 < KSUB; ++kk) {
       // sub-step kk: MFMAs on fragment set kk&1, reads of kk+1 interleaved
@@ -588,8 +630,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   }
 }
 
-template <int BMODE, int BK = kBK, int NSTAGE = kNSTAGE>
+template <int BMODE, int PF = 0, int BK = kBK, int NSTAGE = kNSTAGE>
 constexpr size_t gemm_lds_bytes() {
+  if constexpr (BMODE == B_NT && BK == 64 && PF > 0)   // + prefetch scratch
+    return (NSTAGE * (BM * BK * 2 + BN * BK * 2) > 4 * 32768 ? (size_t)NSTAGE * (BM * BK * 2 + BN * BK * 2)
+                                                             : (size_t)4 * 32768) + 2048;
   // pipeline stages, at least the 4 x 32 KB the output staging uses
   return (NSTAGE * (BM * BK * 2 + BN * BK * 2) > 4 * 32768 ? (size_t)NSTAGE * (BM * BK * 2 + BN * BK * 2)
                                                            : (size_t)4 * 32768) +
