@@ -22,25 +22,36 @@ struct SkinnyNTArgs {
   float *part;              // [KS x T x RS]
 };
 
+// Block: 64 tokens x one K chunk, stepping 128 columns at a time.  Each
+// step's Z tile (64 x 128) and SIDE tile (RS x 128) are loaded with
+// row-contiguous 16-byte lanes (a wave instruction covers 4 rows x 256 B),
+// kept in registers while the previous step's tiles are contracted from LDS,
+// then written to LDS.  Wave w contracts tokens 16 w .. 16 w + 15.
+// LDS rows are 256 B (16 chunks of 16 B), chunk index XOR (row % 16).
 template <int RS, bool ZSWIGLU>
 __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
-  constexpr int NSB = RS / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NQ = RS / 16;
+  constexpr int SL = (RS * 16 + 255) / 256;   // side chunks per thread
+  __shared__ __attribute__((aligned(16))) char zs[64 * 256];
+  __shared__ __attribute__((aligned(16))) char ss[RS * 256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, hi16 = lane >> 4;
-  const int t = blockIdx.x * 64 + wave * 16 + l16;
+  const int t0 = blockIdx.x * 64;
   const int kbeg = blockIdx.y * a.kchunk;
   const int kend = min(a.K, kbeg + a.kchunk);
-  f32x4 acc[NSB];
+  const int c = tid & 15, rb = tid >> 4;      // load chunk column, first row
+  auto off = [](int row, int chunk) -> uint32_t {
+    return (uint32_t)(row * 256 + ((chunk ^ (row & 15)) << 4));
+  };
+  u32x4 zr[4], sr[SL];
+  auto load = [&](int k0) {
+    const int k = k0 + 8 * c;
+    const bool kin = k < kend;
 #pragma unroll
-  for (int i = 0; i < NSB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool trow = t < a.T;
-  for (int k0 = kbeg; k0 < kend; k0 += 128) {
-    u32x4 zf[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = k0 + 32 * u + 8 * hi16;
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + rb + 16 * i;
       u32x4 v = {0, 0, 0, 0};
-      if (trow && k < kend) {
+      if (kin && t < a.T) {
         if constexpr (ZSWIGLU) {
           const u32x4 e = gload16(a.E + (int64_t)t * a.ldz + k);
           const u32x4 g = gload16(a.G + (int64_t)t * a.ldz + k);
@@ -51,29 +62,56 @@ __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
                                e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
           }
         } else {
-          const bf16_t *src = k < a.ksplit ? a.Z0 + (int64_t)t * a.ldz + k
-                                           : a.Z1 + (int64_t)t * a.ldz + (k - a.ksplit);
-          v = gload16(src);
+          v = gload16(k < a.ksplit ? a.Z0 + (int64_t)t * a.ldz + k
+                                   : a.Z1 + (int64_t)t * a.ldz + (k - a.ksplit));
         }
       }
-      zf[u] = v;
+      zr[i] = v;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = k0 + 32 * u + 8 * hi16;
+    for (int i = 0; i < SL; ++i) {
+      const int q = rb + 16 * i;
+      u32x4 v = {0, 0, 0, 0};
+      if (kin && q < RS) v = gload16(a.side + (int64_t)q * a.K + k);
+      sr[i] = v;
+    }
+  };
+  auto store = [&]() {
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        u32x4 sv = {0, 0, 0, 0};
-        if (k < kend) sv = gload16(a.side + (int64_t)(sb * 16 + l16) * a.K + k);
-        acc[sb] = mfma16(sv, zf[u], acc[sb]);
-      }
+    for (int i = 0; i < 4; ++i) lds_write16(zs, off(rb + 16 * i, c), zr[i]);
+#pragma unroll
+    for (int i = 0; i < SL; ++i)
+      if (rb + 16 * i < RS) lds_write16(ss, off(rb + 16 * i, c), sr[i]);
+  };
+  f32x4 acc[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(kbeg);
+  store();
+  __syncthreads();
+  for (int k0 = kbeg; k0 < kend; k0 += 128) {
+    const bool more = k0 + 128 < kend;
+    if (more) load(k0 + 128);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 zf = lds_read16(zs, off(wave * 16 + l16, 4 * kb + hi16));
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb)
+        acc[qb] = mfma16(lds_read16(ss, off(qb * 16 + l16, 4 * kb + hi16)), zf, acc[qb]);
+    }
+    __syncthreads();
+    if (more) {
+      store();
+      __syncthreads();
     }
   }
-  if (trow) {
+  // D[q][t]: lane holds q = 16 qb + 4 hi16 .. +3 of token t = t0 + 16 wave + l16
+  const int t = t0 + wave * 16 + l16;
+  if (t < a.T) {
     float *dst = a.part + ((int64_t)blockIdx.y * a.T + t) * RS;
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-      *reinterpret_cast<f32x4 *>(dst + sb * 16 + 4 * hi16) = acc[sb];
+    for (int qb = 0; qb < NQ; ++qb)
+      *reinterpret_cast<f32x4 *>(dst + qb * 16 + 4 * hi16) = acc[qb];
   }
 }
 

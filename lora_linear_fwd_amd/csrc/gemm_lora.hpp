@@ -35,6 +35,8 @@
 // between its two 16-K sub-steps, so the next stage's first fragment reads
 // overlap the current stage's last 16 MFMAs.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace lora {
@@ -124,6 +126,24 @@ template <int COUNT>
 __device__ __forceinline__ void sched_pairs() {
 #pragma unroll
   for (int i = 0; i < COUNT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// 16 - READS MFMAs each followed by an equal share of the DMAS VMEM loads
+// (the next stage's DMA), then READS pairs of (MFMA, LDS read).  The LDS
+// reads stay after the DMA: the compiler cannot tell the DMA's LDS writes
+// from the reads' addresses.
+template <int READS, int DMAS>
+__device__ __forceinline__ void sched_mfma_read_dma() {
+#pragma unroll
+  for (int i = 0; i < 16 - READS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, DMAS / (16 - READS), 0);
+  }
+#pragma unroll
+  for (int i = 0; i < READS; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
@@ -333,6 +353,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     }
   };
 
+  // DMA of a step that lies inside K and inside one of the two K sources:
+  // no per-lane or per-step conditions (rows past the end carry kOOB)
+  auto issue_dma_fast = [&](int kt, char *stage) {
+    const int k0 = kt * BK;
+    char *Xs = stage, *Ws = stage + XS;
+    const uint32_t sa = 2u * (uint32_t)k0 + (k0 >= ksplit ? dA1 : 0u);
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) dma16(rsA, Xs + (4 * u + wave) * 1024, aoff[u], sa);
+    if constexpr (BMODE == B_NT) {
+#pragma unroll
+      for (int u = 0; u < NDMA; ++u) {
+        const int b = 4 * u + wave;
+        const __amdgpu_buffer_rsrc_t r = (GU && (((RPI * b) >> 6) & 1)) ? rsB1 : rsB0;
+        dma16(r, Ws + b * 1024, boff[u], 2u * (uint32_t)k0);
+      }
+    } else if constexpr (BMODE == B_NN) {
+      const bool second = k0 >= ksplit;
+      const __amdgpu_buffer_rsrc_t r = second ? rsB1 : rsB0;
+#pragma unroll
+      for (int u = 0; u < BK / 8; ++u) {
+        const int b = 4 * u + wave;
+        const int kr = k0 + 2 * b - (second ? ksplit : 0);
+        dma16(r, Ws + b * 1024, boff[u], (uint32_t)(kr * p.ldb * 2));
+      }
+    }
+  };
+
   // ----------------------------- 4-bit weights: global -> registers -> LDS
   auto load_q4 = [&](Stage<BMODE> &st, int kt) {
     const int k0 = kt * BK;
@@ -444,20 +491,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   constexpr int kDmaPerStep = NDMA + ((BMODE == B_NT || BMODE == B_NN) ? NDMA : 0);
   constexpr int kWaitDense = (NSTAGE - 2) * kDmaPerStep + (DOPF ? 2 : 0);
   constexpr int kWaitQ4 = NSTAGE == 2 ? 0 : kDmaPerStep;
-  for (int kt = 0; kt < nkt; ++kt) {
+  // Steps whose DMA target lies inside K and inside one K source run a
+  // branch-free body with the DMA interleaved into the first sub-step's
+  // MFMAs; the rest (tails, a source boundary inside a step, 4-bit forms)
+  // take the general loads.
+  int nfast = 0;
+  if constexpr (!Q4) {
+    int s_end = K / BK;                       // first step reaching past K
+    if ((ksplit % BK) != 0 && ksplit < K) s_end = min(s_end, ksplit / BK);
+    nfast = max(0, min(nkt, s_end - (NSTAGE - 1)));
+  }
+  auto step = [&](int kt, auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
     const char *cur = smem + (kt % NSTAGE) * STAGE;
     char *nxt = smem + ((kt + 1) % NSTAGE) * STAGE;
+    char *tgt = smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE;
     if constexpr (Q4) load_q4(st, kt + 1);
-    issue_dma(kt + NSTAGE - 1, smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE);
+    if constexpr (FAST) issue_dma_fast(kt + NSTAGE - 1, tgt);
+    else issue_dma(kt + NSTAGE - 1, tgt);
     issue_pf(kt + NSTAGE - 1 + PF);
 #pragma unroll
     for (int kk = 0; kk + 1 < KSUB; ++kk) {
       // sub-step kk: MFMAs on fragment set kk&1, reads of kk+1 interleaved
       read_frags(cur, kk + 1, (kk + 1) & 1);
       mfmas(kk & 1);
-      sched_pairs<kReads>();
-      sched_group<0x008, 16 - kReads>();
+      if (FAST && kk == 0 && kDmaPerStep % (16 - kReads) == 0) {
+        sched_mfma_read_dma<kReads, kDmaPerStep>();
+      } else {
+        sched_pairs<kReads>();
+        sched_group<0x008, 16 - kReads>();
+      }
     }
+    // keep every MFMA of the earlier sub-steps ahead of the wait: the
+    // longer the DMA has, the less the wait stalls
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (Q4) {
       vm_wait<kWaitQ4>();
       commit_q4(st, nxt);
@@ -466,13 +533,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
       vm_wait<kWaitDense>();
     }
     barrier_only();
+    __builtin_amdgcn_sched_barrier(0);
     // last sub-step: MFMAs on its fragment set, the next stage's first
     // reads interleaved (on the last step they read a stage nobody uses)
     read_frags(nxt, 0, 0);
     mfmas((KSUB - 1) & 1);
     sched_pairs<kReads>();
     sched_group<0x008, 16 - kReads>();
-  }
+  };
+  int kt = 0;
+  for (; kt < nfast; ++kt) step(kt, std::true_type{});
+  for (; kt < nkt; ++kt) step(kt, std::false_type{});
   wait_vmem();
 
   // ------------------------------------------------ LoRA epilogue pass

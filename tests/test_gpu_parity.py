@@ -180,6 +180,7 @@ MLP_SHAPES = [
     (37, 64, 72, 3),
     (260, 128, 264, 64),
     (513, 136, 256, 8),
+    (70, 64, 136, 128),     # widest side operands (2 r = 256)
 ]
 
 
