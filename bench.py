@@ -24,6 +24,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "lora_linear_fwd_amd", "csrc")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_cfg{cfg}_hbm_traffic.md")
+KC_NAMES = ["gate/up fwd GEMM + SwiGLU epilogue", "down fwd GEMM",
+            "down bwd GEMM + SwiGLU' epilogue", "gate/up bwd dX GEMM"]
 
 
 def parse():
@@ -33,11 +37,87 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=(2, 3, 5))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device-to-device copy (3 times): the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                              "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the HBM-traffic summary (markdown) of the GEMM classes from "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection CSVs of "
+                         "bench.py and of --calibrate-copy")
     return ap.parse_args()
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources (any change invalidates stored counters)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def _counter_rows(path):
+    import csv
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def _gemm_class_values(rows):
+    """Counter value (KiB) per dispatch of each GEMM class: a step launches
+    the GEMMs in the order gate/up fwd, down fwd, down bwd, gate/up bwd."""
+    gem = [v for _, name, v in rows if "k_lora_gemm" in name]
+    out = {i: [] for i in range(4)}
+    for j, v in enumerate(gem):
+        out[j % 4].append(v)
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, cf_csv, cw_csv, cfg):
+    """Markdown summary with a machine-readable line read back by bench.py."""
+    copy_bytes = 256 << 20
+    cf = [v for _, n, v in _counter_rows(cf_csv) if "copyBuffer" in n]
+    cw = [v for _, n, v in _counter_rows(cw_csv) if "copyBuffer" in n]
+    f_fac = copy_bytes / (sum(cf) / len(cf) * 1024)
+    w_fac = copy_bytes / (sum(cw) / len(cw) * 1024)
+    fv, wv = _gemm_class_values(_counter_rows(fetch_csv)), _gemm_class_values(_counter_rows(write_csv))
+    per = {}
+    for i in range(4):
+        fb = sum(fv[i]) / len(fv[i]) * 1024 * f_fac
+        wb = sum(wv[i]) / len(wv[i]) * 1024 * w_fac
+        per[KC_NAMES[i]] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                            "traffic_bytes": round(fb + wb)}
+    rec = {"config_id": cfg, "source_sha256": kernel_source_digest(),
+           "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4), "per_launch": per}
+    lines = ["| GEMM | FETCH (scaled) MB | WRITE (scaled) MB | total MB |", "|---|---|---|---|"]
+    for k, v in per.items():
+        lines.append(f"| {k} | {v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.1f} | "
+                     f"{v['traffic_bytes'] / 1e6:.1f} |")
+    return "\n".join(lines) + "\n\ntraffic-record: " + json.dumps(rec) + "\n"
+
+
+def stored_traffic(cfg, kernel_name):
+    """HBM bytes per launch of `kernel_name` from the committed counter
+    summary, or None when there is none or the HIP sources changed since."""
+    path = TRAFFIC_SUMMARY.format(cfg=cfg)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec.get("source_sha256") != kernel_source_digest():
+                    return None
+                v = rec["per_launch"].get(kernel_name)
+                return None if v is None else v["traffic_bytes"]
+    return None
 
 
 def calibrate_copy():
@@ -70,13 +150,15 @@ def gemm_flops(kc, T, d, f, r):
     raise ValueError(kc)
 
 
-def cpu_baseline(cfg, tokens, mi):
+def cpu_baseline(cfg, tokens, mi, reps=2):
     """The float64 CPU oracle on the first `tokens` tokens of the same
-    workload (same weights)."""
+    workload (same weights): one warm-up on 512 tokens, then `reps` timed
+    forward+backward passes."""
     import numpy as np
     import oracle
     from lora_inputs import CONFIGS
     c = CONFIGS[cfg]
+    tokens = min(tokens, c["T"])
     W = dict(mi.W)
     if mi.q4:
         W = {p: oracle.decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k) for p, q in mi.q4.items()}
@@ -85,11 +167,12 @@ def cpu_baseline(cfg, tokens, mi):
     Wf = {p: np.asarray(v, np.float64) for p, v in W.items()}
     Af = {p: np.asarray(v, np.float64) for p, v in mi.A.items()}
     Bf = {p: np.asarray(v, np.float64) for p, v in mi.B.items()}
-    oracle.mlp_fwd(X, Wf, Af, Bf, s)                      # warm-up
+    oracle.mlp_bwd(X[:512], Wf, Af, Bf, s, dY[:512])       # warm-up
     t0 = time.perf_counter()
-    oracle.mlp_fwd(X, Wf, Af, Bf, s)
-    oracle.mlp_bwd(X, Wf, Af, Bf, s, dY)
-    dt = time.perf_counter() - t0
+    for _ in range(reps):
+        oracle.mlp_fwd(X, Wf, Af, Bf, s)
+        oracle.mlp_bwd(X, Wf, Af, Bf, s, dY)
+    dt = (time.perf_counter() - t0) / reps
     fl = mlp_flops(tokens, c["d"], c["f"], c["r"])
     try:
         cores = len(os.sched_getaffinity(0))
@@ -97,8 +180,9 @@ def cpu_baseline(cfg, tokens, mi):
         cores = os.cpu_count()
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 NumPy oracle, MLP fwd+bwd on {tokens} of {c['T']} tokens "
-                      f"(d={c['d']}, f={c['f']}, r={c['r']}), 1 timed rep after 1 warm-up, "
-                      f"{dt:.2f} s", "tokens_per_s": tokens / dt, "seconds": dt}
+                      f"(d={c['d']}, f={c['f']}, r={c['r']}), mean of {reps} timed reps after "
+                      f"a 512-token warm-up, {dt:.2f} s per rep",
+            "tokens_per_s": tokens / dt, "seconds_per_rep": dt}
 
 
 def main():
@@ -109,6 +193,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.config), end="")
         return
     import numpy as np
     import torch
@@ -173,9 +260,7 @@ def main():
 
     kms = {kc: float(np.mean([a_.elapsed_time(b_) for a_, b_ in ev[kc]])) for kc in kcs}
     dom = max(kcs, key=lambda kc: kms[kc])
-    names = {L.KC_GATEUP_FWD: "gate/up fwd GEMM + SwiGLU epilogue",
-             L.KC_DOWN_FWD: "down fwd GEMM", L.KC_DOWN_BWD: "down bwd GEMM + SwiGLU' epilogue",
-             L.KC_GATEUP_BWD: "gate/up bwd dX GEMM"}
+    names = dict(zip([L.KC_GATEUP_FWD, L.KC_DOWN_FWD, L.KC_DOWN_BWD, L.KC_GATEUP_BWD], KC_NAMES))
     dom_tflops = gemm_flops(dom, T, d, f, r) / (kms[dom] * 1e-3) / 1e12
     flops = mlp_flops(T, d, f, r)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -203,7 +288,8 @@ def main():
         "kernels_ms": {names[kc]: round(kms[kc], 4) for kc in kcs},
         "roofline": {"bound": "mfma", "kernel": names[dom], "achieved": round(dom_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic(args.config, names[dom]),
                      "flops_per_launch": gemm_flops(dom, T, d, f, r),
                      "avg_launch_ms": round(kms[dom], 4)},
         "cpu_baseline": None,
