@@ -594,8 +594,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   __syncthreads();   // every wave is done with the pipeline stages
   char *reg = smem + wave * 32768;
   auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 512 + ((c ^ (r & 31)) << 4)); };
+  // SwiGLU backward: a half's saved e, g (16 row groups x 16 bytes each per
+  // lane) are all requested before the half is staged, so their latency is
+  // paid once per half
+  u32x4 ein[16], gin[16];
+  auto load_eg = [&](int half) {
+    if constexpr (EPI == EPI_SWIGLU_BWD) {
+      const int q = lane & 15, n = n0 + wn * 128 + 8 * q;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int m = m0 + wm * 128 + half * 64 + it * 4 + (lane >> 4);
+        u32x4 e = {0, 0, 0, 0}, g = {0, 0, 0, 0};
+        if (m < M && n < N) {
+          const int64_t off = (int64_t)m * N + n;
+          e = gload16(p.Ein + off);
+          g = gload16(p.Gin + off);
+        }
+        ein[it] = e;
+        gin[it] = g;
+      }
+    }
+  };
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    load_eg(half);
     // rows (j - 2 half) * 32 + l32 of the region hold acc[.][j]
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
@@ -649,7 +671,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     } else {
       const int q = lane & 15;                      // 8-column group
       const int n = n0 + wn * 128 + 8 * q;
-#pragma unroll 4
+#pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int r = it * 4 + (lane >> 4);
         const int m = mrow0 + r;
@@ -674,7 +696,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
           gstore16(dst, w);
         } else {  // EPI_SWIGLU_BWD: v = dh
           const int64_t off = (int64_t)m * N + n;
-          const u32x4 ev = gload16(p.Ein + off), gv = gload16(p.Gin + off);
+          const u32x4 ev = ein[it], gv = gin[it];
           u32x4 dew, dgw;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
