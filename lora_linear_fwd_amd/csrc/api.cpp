@@ -52,6 +52,27 @@ inline size_t nt_part_bytes(int64_t T, int64_t K, int RS) {
 inline size_t tn_part_bytes(int64_t T, int64_t N, int RS) {
   return (size_t)tn_split(T, N).ts * RS * N * 4;
 }
+// dual pass: 256-column blocks per segment x token chunks (multiples of 64)
+struct DualSplit { int nb0, nb1, ts, tchunk; };
+inline DualSplit dual_split(int64_t T, int64_t N, int64_t nsplit) {
+  DualSplit d;
+  d.nb0 = (int)cdiv(nsplit, 256);
+  d.nb1 = (int)cdiv(N - nsplit, 256);
+  const int64_t nbc = std::max<int64_t>(1, d.nb0 + d.nb1);
+  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(T, 64), cdiv(1024, nbc)));
+  const int64_t tchunk = std::max<int64_t>(64, cdiv(cdiv(T, ts), 64) * 64);
+  d.tchunk = (int)tchunk;
+  d.ts = (int)std::max<int64_t>(1, cdiv(T, tchunk));
+  return d;
+}
+inline size_t dual_u_bytes(int64_t T, int64_t N, int64_t nsplit, int RS) {
+  const DualSplit d = dual_split(T, N, nsplit);
+  return (size_t)(d.nb0 + d.nb1) * T * RS * 4;
+}
+inline size_t dual_v_bytes(int64_t T, int64_t N, int64_t nsplit, int RS) {
+  return (size_t)dual_split(T, N, nsplit).ts * RS * N * 4;
+}
+inline int64_t ldp_of(int64_t T) { return std::max<int64_t>(64, cdiv(T, 64) * 64); }
 
 // `wcopy`: room for a bf16 copy of the base weight (decoded or transposed)
 struct LinFwdPlan { size_t side, epi, hpart, hbf, wbuf, total; };
@@ -101,7 +122,8 @@ MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) 
 }
 
 struct MlpBwdPlan {
-  size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, side_gu_nn, epi_gu_nn, side_gu_nt;
+  size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, epi_gu_nn, side_gu_nt;
+  size_t side_g, side_u, pt_d, pt_g, pt_u, part_u, part_v;
   size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, total;
 };
 MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) {
@@ -113,7 +135,6 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) 
   p.side_d_nn = b.take((size_t)RS2 * d * 2);
   p.epi_d_nn = b.take((size_t)f * RS2 * 2);
   p.side_d_nt = b.take((size_t)RS2 * f * 2);
-  p.side_gu_nn = b.take((size_t)RS1 * 2 * f * 2);
   p.epi_gu_nn = b.take((size_t)d * RS1 * 2);
   p.side_gu_nt = b.take((size_t)RS1 * d * 2);
   p.gd32 = b.take((size_t)T * RS2 * 4);
@@ -122,10 +143,16 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) 
   p.ggu32 = b.take((size_t)T * RS1 * 4);
   p.ggubf = b.take((size_t)T * RS1 * 2);
   p.hgu32 = b.take((size_t)T * RS1 * 4);
-  p.ntpart = b.take(std::max({nt_part_bytes(T, d, RS2), nt_part_bytes(T, f, RS2),
-                              nt_part_bytes(T, 2 * f, RS1), nt_part_bytes(T, d, RS1)}));
-  p.tnpart = b.take(std::max({tn_part_bytes(T, f, RS2), tn_part_bytes(T, d, RS2),
-                              tn_part_bytes(T, d, RS1), tn_part_bytes(T, 2 * f, RS1)}));
+  p.ntpart = b.take(std::max(nt_part_bytes(T, d, RS2), nt_part_bytes(T, d, RS1)));
+  p.tnpart = b.take(std::max(tn_part_bytes(T, d, RS2), tn_part_bytes(T, d, RS1)));
+  p.side_g = b.take((size_t)RS2 * f * 2);
+  p.side_u = b.take((size_t)RS2 * f * 2);
+  const size_t ptb = (size_t)RS2 * ldp_of(T) * 2;
+  p.pt_d = b.take(ptb);
+  p.pt_g = b.take(ptb);
+  p.pt_u = b.take(ptb);
+  p.part_u = b.take(std::max(dual_u_bytes(T, f, f, RS2), dual_u_bytes(T, 2 * f, f, RS2)));
+  p.part_v = b.take(std::max(dual_v_bytes(T, f, f, RS2), dual_v_bytes(T, 2 * f, f, RS2)));
   p.total = b.cur;
   return p;
 }
@@ -292,7 +319,8 @@ int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const 
   }
 #undef STN
   HIP_TRY(hipGetLastError());
-  ReduceTNArgs ra{part, sp.ts, RS, (int)N, (int)r, (int)out_nsplit, scale, transposed, out0, out1};
+  ReduceTNArgs ra{part, sp.ts, RS, (int)N, (int)r, (int)out_nsplit, scale, transposed, out0, out1,
+                  (int)r};
   hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)RS * N)), dim3(256), 0, st, ra);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
@@ -331,6 +359,55 @@ int check_ws(int op, int dtype, int wfmt, int64_t T, int64_t kd, int64_t nf, int
   if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
   fast = ws_bytes >= lora_workspace_bytes(op, dtype, wfmt, T, kd, nf, r);
+  return LORA_OK;
+}
+
+// dual pass over Z (see k_skinny_dual), then its two reductions:
+//   U -> uout32 / uoutbf (k_reduce_dual_u, RSout columns, bf16 scaled by uscale)
+//   V -> vout0 / vout1 (k_reduce_tn; transposed = dB layout with segment-local
+//        rows, else dA layout), scaled by vscale
+int skinny_dual(int RS, bool zswiglu, int64_t T, int64_t N, int64_t nsplit, int64_t ldz,
+                const bf16_t *Z0, const bf16_t *Z1, const bf16_t *E, const bf16_t *G,
+                const bf16_t *S0, const bf16_t *S1, const bf16_t *P0, const bf16_t *P1,
+                float *part_u, float *part_v, int64_t r, int RSout, float uscale, float *uout32,
+                bf16_t *uoutbf, float vscale, int transposed, bf16_t *vout0, bf16_t *vout1,
+                hipStream_t st) {
+  const DualSplit sp = dual_split(T, N, nsplit);
+  DualArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, sp.nb0, ldz, Z0, Z1, E, G, S0, S1, P0, P1,
+             (int)ldp_of(T), part_u, part_v};
+  if (T > 0) {
+    dim3 grid((unsigned)(sp.nb0 + sp.nb1), (unsigned)sp.ts);
+#define SDU(R)                                                                              \
+  case R:                                                                                   \
+    if (zswiglu) hipLaunchKernelGGL((k_skinny_dual<R, R, true>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((k_skinny_dual<R, R, false>), grid, dim3(256), 0, st, a);         \
+    break;
+    switch (RS) {
+      SDU(16) SDU(32) SDU(48) SDU(64) SDU(80) SDU(96) SDU(112) SDU(128)
+      default: return LORA_ERR_UNSUPPORTED;
+    }
+#undef SDU
+    HIP_TRY(hipGetLastError());
+    ReduceUArgs ru{part_u, (int)T, RS, RSout, (int)r, sp.nb1 ? 2 : 1, sp.nb0, sp.nb1, uscale,
+                   uout32, uoutbf};
+    hipLaunchKernelGGL(k_reduce_dual_u, dim3(blocks_for(T * RSout)), dim3(256), 0, st, ru);
+    HIP_TRY(hipGetLastError());
+  }
+  ReduceTNArgs rv{part_v, T > 0 ? sp.ts : 0, RS, (int)N, (int)r, (int)nsplit, vscale, transposed,
+                  vout0, vout1, 0};
+  hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)RS * N)), dim3(256), 0, st, rv);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+// [RSout x ldp_of(T)] bf16 transposed copy of columns qoff .. qoff+nq-1 of a
+// [T x ldin] fp32 matrix, zero elsewhere
+int pack_pt(const float *in, int64_t T, int ldin, int qoff, int nq, int RSout, bf16_t *out,
+            hipStream_t st) {
+  const int64_t ldp = ldp_of(T);
+  hipLaunchKernelGGL(k_pack_pt, dim3(blocks_for(RSout * ldp)), dim3(256), 0, st, in, (int)T, ldin,
+                     qoff, nq, RSout, (int)ldp, out);
+  HIP_TRY(hipGetLastError());
   return LORA_OK;
 }
 
@@ -702,8 +779,12 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   bf16_t *de = (bf16_t *)(w + pl.de), *dg = (bf16_t *)(w + pl.dg);
   bf16_t *side_d_nn = (bf16_t *)(w + pl.side_d_nn), *epi_d_nn = (bf16_t *)(w + pl.epi_d_nn);
   bf16_t *side_d_nt = (bf16_t *)(w + pl.side_d_nt);
-  bf16_t *side_gu_nn = (bf16_t *)(w + pl.side_gu_nn), *epi_gu_nn = (bf16_t *)(w + pl.epi_gu_nn);
+  bf16_t *epi_gu_nn = (bf16_t *)(w + pl.epi_gu_nn);
   bf16_t *side_gu_nt = (bf16_t *)(w + pl.side_gu_nt);
+  bf16_t *side_g = (bf16_t *)(w + pl.side_g), *side_u = (bf16_t *)(w + pl.side_u);
+  bf16_t *pt_d = (bf16_t *)(w + pl.pt_d), *pt_g = (bf16_t *)(w + pl.pt_g);
+  bf16_t *pt_u = (bf16_t *)(w + pl.pt_u);
+  float *part_u = (float *)(w + pl.part_u), *part_v = (float *)(w + pl.part_v);
   float *gd32 = (float *)(w + pl.gd32), *hd32 = (float *)(w + pl.hd32);
   float *ggu32 = (float *)(w + pl.ggu32), *hgu32 = (float *)(w + pl.hgu32);
   bf16_t *gdbf = (bf16_t *)(w + pl.gdbf), *ggubf = (bf16_t *)(w + pl.ggubf);
@@ -715,7 +796,8 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   prep.side(side_d_nn, RS2, d, Bd, nullptr, r, d, 1);       // Bd^T [RS2 x d]
   prep.epi(epi_d_nn, f, RS2, Ad, nullptr, r, f, 1);         // Ad^T [f x RS2]
   prep.side(side_d_nt, RS2, f, Ad, nullptr, r, f, 0);       // Ad   [RS2 x f]
-  prep.side(side_gu_nn, RS1, 2 * f, Bg, Bu, r, f, 1);       // blockdiag(Bg,Bu)^T
+  prep.side(side_g, RS2, f, Bg, nullptr, r, f, 1);          // Bg^T [RS2 x f]
+  prep.side(side_u, RS2, f, Bu, nullptr, r, f, 1);          // Bu^T [RS2 x f]
   prep.epi(epi_gu_nn, d, RS1, Ag, Au, r, d, 1);             // [Ag;Au]^T [d x RS1]
   prep.side(side_gu_nt, RS1, d, Ag, Au, r, d, 0);           // [Ag;Au] [RS1 x d]
   LORA_TRY(prep.launch(st));
@@ -742,49 +824,52 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     a.hglob = gdbf;
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
     LORA_TRY(run_gemm(LORA_KC_DOWN_BWD, nn, q4, EPI_SWIGLU_BWD, a, st));
-    // 2. H_d = h Ad^T with h recomputed from e, g
-    LORA_TRY(skinny_nt(RS2, true, T, f, nullptr, nullptr, f, f, eb, gb, side_d_nt, ntpart, hd32,
-                       nullptr, 1.f, st));
   }
-  // 3. dAd = s G_d^T h ; dBd = s dY^T H_d
-  LORA_TRY(skinny_tn(RS2, true, T, f, gd32, nullptr, nullptr, f, f, eb, gb, tnpart, r, s, 0,
-                     (bf16_t *)dAd, nullptr, f, st));
+  // 2. one pass over h = silu(e) g (recomputed): H_d = h Ad^T (fp32, for dBd)
+  //    and dAd = s G_d^T h
+  if (T > 0) LORA_TRY(pack_pt(gd32, T, RS2, 0, (int)r, RS2, pt_d, st));   // G_d^T bf16
+  LORA_TRY(skinny_dual(RS2, true, T, f, f, f, nullptr, nullptr, eb, gb, side_d_nt, nullptr, pt_d,
+                       nullptr, part_u, part_v, r, RS2, 1.f, hd32, nullptr, s, 0, (bf16_t *)dAd,
+                       nullptr, st));
+  // 3. dBd = s dY^T H_d
   LORA_TRY(skinny_tn(RS2, false, T, d, hd32, dYb, dYb, d, d, nullptr, nullptr, tnpart, r, s, 1,
                      (bf16_t *)dBd, nullptr, d, st));
   if (T > 0) {
-    // 4. dX = de Wg + dg Wu + s [de Bg | dg Bu] [Ag; Au]
-    // G_gu = [de Bg | dg Bu] (fp32 for dA_gu, scaled bf16 for the epilogue)
-    LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, f, nullptr, nullptr, side_gu_nn, ntpart,
-                       ggu32, ggubf, s, st));
-    if (dX) {
-      GemmArgs b = gemm_base();
-      b.M = (int)T; b.N = (int)d; b.K = (int)(2 * f); b.ksplit = (int)f;
-      b.A0 = de; b.A1 = dg; b.lda = f;
-      bool nn = true, q4 = wg.q4;
-      if (fast) {   // [Wg^T | Wu^T] [d x 2f], over Wd^T (its GEMM is done)
-        LORA_TRY(transpose_w(wt, 2 * f, wg, f, d, st));
-        LORA_TRY(transpose_w(wt + f, 2 * f, wu, f, d, st));
-        const WeightView tv = dense_view(wt);
-        set_b(b, tv, tv); b.ldb = 2 * f;
-        nn = false; q4 = false;
-      } else {
-        set_b(b, wg, wu); b.ldb = d;
-      }
-      b.rs = RS1; b.epi = epi_gu_nn;
-      b.C = (bf16_t *)dX; b.ldc = d;
-      b.hglob = ggubf;
-      b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
-      LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, nn, q4, EPI_STORE, b, st));
-    }
-    // 5. H_gu = X [Ag; Au]^T
+    // 4. H_gu = X [Ag; Au]^T (fp32), its two halves transposed to bf16
     LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,
                        nullptr, 1.f, st));
+    LORA_TRY(pack_pt(hgu32, T, RS1, 0, (int)r, RS2, pt_g, st));
+    LORA_TRY(pack_pt(hgu32, T, RS1, (int)r, (int)r, RS2, pt_u, st));
   }
-  // 6. [dAg; dAu] = s G_gu^T X ;  dBg, dBu = s [de | dg]^T H_gu (diagonal blocks)
+  // 5. one pass over [de | dg]: G_gu = [de Bg | dg Bu] (fp32 for dA_gu, s G_gu in
+  //    bf16 for the dX epilogue) and dBg = s de^T H_g, dBu = s dg^T H_u
+  LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, f, de, dg, nullptr, nullptr, side_g, side_u, pt_g,
+                       pt_u, part_u, part_v, r, RS1, s, ggu32, ggubf, s, 1, (bf16_t *)dBg,
+                       (bf16_t *)dBu, st));
+  if (T > 0 && dX) {
+    // 6. dX = de Wg + dg Wu + s [de Bg | dg Bu] [Ag; Au]
+    GemmArgs b = gemm_base();
+    b.M = (int)T; b.N = (int)d; b.K = (int)(2 * f); b.ksplit = (int)f;
+    b.A0 = de; b.A1 = dg; b.lda = f;
+    bool nn = true, q4 = wg.q4;
+    if (fast) {   // [Wg^T | Wu^T] [d x 2f], over Wd^T (its GEMM is done)
+      LORA_TRY(transpose_w(wt, 2 * f, wg, f, d, st));
+      LORA_TRY(transpose_w(wt + f, 2 * f, wu, f, d, st));
+      const WeightView tv = dense_view(wt);
+      set_b(b, tv, tv); b.ldb = 2 * f;
+      nn = false; q4 = false;
+    } else {
+      set_b(b, wg, wu); b.ldb = d;
+    }
+    b.rs = RS1; b.epi = epi_gu_nn;
+    b.C = (bf16_t *)dX; b.ldc = d;
+    b.hglob = ggubf;
+    b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
+    LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, nn, q4, EPI_STORE, b, st));
+  }
+  // 7. [dAg; dAu] = s G_gu^T X
   LORA_TRY(skinny_tn(RS1, false, T, d, ggu32, Xb, Xb, d, d, nullptr, nullptr, tnpart, r, s, 0,
                      (bf16_t *)dAg, (bf16_t *)dAu, d, st));
-  LORA_TRY(skinny_tn(RS1, false, T, 2 * f, hgu32, de, dg, f, f, nullptr, nullptr, tnpart, r, s, 1,
-                     (bf16_t *)dBg, (bf16_t *)dBu, f, st));
   return LORA_OK;
 }
 

@@ -242,13 +242,16 @@ __global__ __launch_bounds__(256) void k_skinny_tn(const SkinnyTNArgs a) {
 // into the adapter-gradient layout.
 //   rowmajor (dA-type): rows q in [0, r) -> out0[q][n], q in [r, 2r) -> out1[q-r][n]
 //   transposed (dB-type): out0[n][q] for n < nsplit, q < r;
-//                         out1[n-nsplit][q-r] for n >= nsplit, r <= q < 2r
+//                         out1[n-nsplit][q-q1] for n >= nsplit, q1 <= q < q1 + r
+// (q1 = r when the second block's rows follow the first's, 0 when both
+// blocks start at row 0)
 struct ReduceTNArgs {
   const float *part;
   int ts, RS, N, r, nsplit;
   float scale;
   int transposed;
   bf16_t *out0, *out1;
+  int q1;
 };
 __global__ void k_reduce_tn(const ReduceTNArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -262,8 +265,8 @@ __global__ void k_reduce_tn(const ReduceTNArgs a) {
   } else {
     if (n < a.nsplit) {
       if (q < a.r) dst = a.out0 + (int64_t)n * a.r + q;
-    } else if (a.out1 && q >= a.r && q < 2 * a.r) {
-      dst = a.out1 + (int64_t)(n - a.nsplit) * a.r + (q - a.r);
+    } else if (a.out1 && q >= a.q1 && q < a.q1 + a.r) {
+      dst = a.out1 + (int64_t)(n - a.nsplit) * a.r + (q - a.q1);
     }
   }
   if (!dst) return;
@@ -271,6 +274,214 @@ __global__ void k_reduce_tn(const ReduceTNArgs a) {
   for (int k = 0; k < a.ts; ++k) s += a.part[(int64_t)k * count + i];
   const uint32_t w = pack_bf16x2(a.scale * s, 0.f);
   *dst = (bf16_t)(w & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// dual skinny pass: both rank-r products of one [T x N] operand Z from a
+// single read of Z
+//   U: part_u[j][t][q]  = sum_{n in column block j} Z[t][n] S[q][n]   (q < RSU)
+//   V: part_v[ts][q][n] = sum_{t in token chunk ts} P[q][t] Z[t][n]    (q < RSV)
+// Z = [Z0 | Z1]: two column segments (nsplit and N - nsplit columns), each
+// with its own S [RSU x segment columns] and P [RSV x ldp] (bf16, zero for
+// t >= T); or Z = silu(E) G recomputed from the saved activations (ZSWIGLU,
+// one segment).  Column blocks of 256 never straddle the segments; block
+// (j, ts) walks its token chunk 64 tokens at a time through LDS: the U part
+// reads the tile row-wise (wave w: tokens 16 w .. +15), the V part
+// column-wise with transpose reads (wave w: columns 64 w .. +63).
+// LDS tile rows are 512 B (32 chunks); chunk index XOR a 4-bit permutation of
+// (row % 16) that keeps both the 16-row reads and the 4-row transpose reads
+// free of bank conflicts.
+// ---------------------------------------------------------------------------
+struct DualArgs {
+  int T, N, nsplit, tchunk, nb0;   // nb0: column blocks of segment 0
+  int64_t ldz;
+  const bf16_t *Z0, *Z1, *E, *G;
+  const bf16_t *S0, *S1;           // row stride = the segment's column count
+  const bf16_t *P0, *P1;
+  int ldp;                         // P row stride, a multiple of 64 >= T
+  float *part_u;                   // [column blocks x T x RSU]
+  float *part_v;                   // [token chunks x RSV x N]
+};
+
+template <int RSU, int RSV, bool ZSWIGLU>
+__global__ __launch_bounds__(256) void k_skinny_dual(const DualArgs a) {
+  constexpr int NQU = RSU / 16, NQV = RSV / 16;
+  constexpr int SL = (RSU * 32 + 255) / 256;   // side chunks per thread
+  __shared__ __attribute__((aligned(16))) char zs[64 * 512];
+  __shared__ __attribute__((aligned(16))) char ss[RSU * 512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int j = blockIdx.x;
+  const bool seg1 = j >= a.nb0;
+  const int ncol = seg1 ? a.N - a.nsplit : a.nsplit;
+  const int c0 = (seg1 ? j - a.nb0 : j) * 256;
+  const bf16_t *S = seg1 ? a.S1 : a.S0;
+  const bf16_t *P = seg1 ? a.P1 : a.P0;
+  const int tbeg = blockIdx.y * a.tchunk, tend = min(a.T, tbeg + a.tchunk);
+  auto zoff = [](int r, int c) -> uint32_t {
+    const int sw = ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+    return (uint32_t)(r * 512 + ((c ^ sw) << 4));
+  };
+  auto soff = [](int q, int c) -> uint32_t { return (uint32_t)(q * 512 + ((c ^ (q & 15)) << 4)); };
+  const int lc = tid & 31, lr = tid >> 5;     // load chunk column, first row
+
+  // side tile of this column block, once
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    const int q = lr + 8 * i;
+    if (q < RSU) {
+      const int k = c0 + 8 * lc;
+      u32x4 v = {0, 0, 0, 0};
+      if (k < ncol) v = gload16(S + (int64_t)q * ncol + k);
+      lds_write16(ss, soff(q, lc), v);
+    }
+  }
+  u32x4 zr[8];
+  auto load = [&](int t0) {
+    const int k = c0 + 8 * lc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + lr + 8 * i;
+      u32x4 v = {0, 0, 0, 0};
+      if (t < tend && k < ncol) {
+        if constexpr (ZSWIGLU) {
+          const u32x4 e = gload16(a.E + (int64_t)t * a.ldz + k);
+          const u32x4 g = gload16(a.G + (int64_t)t * a.ldz + k);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = bf16lo(e[w]), e1 = bf16hi(e[w]);
+            v[w] = pack_bf16x2(e0 * sigmoidf_fast(e0) * bf16lo(g[w]),
+                               e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
+          }
+        } else {
+          v = gload16((seg1 ? a.Z1 : a.Z0) + (int64_t)t * a.ldz + k);
+        }
+      }
+      zr[i] = v;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lds_write16(zs, zoff(lr + 8 * i, lc), zr[i]);
+  };
+
+  f32x4 vacc[4][NQV];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int qb = 0; qb < NQV; ++qb) vacc[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load(tbeg);
+  store();
+  __syncthreads();
+  for (int t0 = tbeg; t0 < tend; t0 += 64) {
+    const bool more = t0 + 64 < tend;
+    if (more) load(t0 + 64);
+    // U: tokens t0 + 16 wave + l16, all 256 columns of the block
+    f32x4 uacc[NQU];
+#pragma unroll
+    for (int qb = 0; qb < NQU; ++qb) uacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const u32x4 zf = lds_read16(zs, zoff(wave * 16 + l16, 4 * kb + g4));
+#pragma unroll
+      for (int qb = 0; qb < NQU; ++qb)
+        uacc[qb] = mfma16(lds_read16(ss, soff(qb * 16 + l16, 4 * kb + g4)), zf, uacc[qb]);
+    }
+    // V: columns 64 wave .. +63, the 64 tokens of the tile
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 pf[NQV];
+#pragma unroll
+      for (int qb = 0; qb < NQV; ++qb)
+        pf[qb] = gload16(P + (int64_t)(qb * 16 + l16) * a.ldp + t0 + 32 * kb + 8 * g4);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        // lane l16 of group g4: column 64 wave + 16 nb + l16, tokens
+        // 32 kb + 8 g4 .. +7 (two 4-token transpose reads)
+        const int n = wave * 64 + nb * 16 + 4 * (l16 & 3);
+        const int r0 = 32 * kb + 8 * g4 + (l16 >> 2);
+        const u32x2 lo = lds_read_tr8(zs, zoff(r0, n >> 3) + (n & 7) * 2);
+        const u32x2 hi = lds_read_tr8(zs, zoff(r0 + 4, n >> 3) + (n & 7) * 2);
+        const u32x4 za = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int qb = 0; qb < NQV; ++qb) vacc[nb][qb] = mfma16(za, pf[qb], vacc[nb][qb]);
+      }
+    }
+    // U partial: lane holds q = 16 qb + 4 g4 .. +3 of token t
+    const int t = t0 + wave * 16 + l16;
+    if (t < tend) {
+      float *dst = a.part_u + ((int64_t)j * a.T + t) * RSU;
+#pragma unroll
+      for (int qb = 0; qb < NQU; ++qb)
+        *reinterpret_cast<f32x4 *>(dst + qb * 16 + 4 * g4) = uacc[qb];
+    }
+    __syncthreads();
+    if (more) {
+      store();
+      __syncthreads();
+    }
+  }
+  // V partial: lane holds columns 16 nb + 4 g4 .. +3 (of the wave's 64) of row q
+  const int colbase = seg1 ? a.nsplit : 0;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int n = c0 + wave * 64 + nb * 16 + 4 * g4;
+    if (n >= ncol) continue;
+#pragma unroll
+    for (int qb = 0; qb < NQV; ++qb) {
+      const int q = qb * 16 + l16;
+      *reinterpret_cast<f32x4 *>(a.part_v + ((int64_t)blockIdx.y * RSV + q) * a.N + colbase + n) =
+          vacc[nb][qb];
+    }
+  }
+}
+
+// out32[t][qo], outbf[t][qo] = bf16(scale * out32), qo < RSout: with two
+// segments, qo < r sums segment 0's column blocks at q = qo, r <= qo < 2r
+// sums segment 1's at q = qo - r; with one, qo < RSU sums all blocks.
+// Everything else is 0.  Fixed summation order.
+struct ReduceUArgs {
+  const float *part;
+  int T, RSU, RSout, r, nseg, nb0, nb1;
+  float scale;
+  float *out32;
+  bf16_t *outbf;
+};
+__global__ void k_reduce_dual_u(const ReduceUArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)a.T * a.RSout) return;
+  const int t = (int)(i / a.RSout), qo = (int)(i % a.RSout);
+  int q = qo, jb = 0, je = a.nb0;
+  bool ok = qo < a.RSU;
+  if (a.nseg == 2) {
+    const bool s1 = qo >= a.r;
+    q = s1 ? qo - a.r : qo;
+    jb = s1 ? a.nb0 : 0;
+    je = s1 ? a.nb0 + a.nb1 : a.nb0;
+    ok = qo < 2 * a.r;
+  }
+  float s = 0.f;
+  if (ok)
+    for (int jj = jb; jj < je; ++jj) s += a.part[((int64_t)jj * a.T + t) * a.RSU + q];
+  if (a.out32) a.out32[i] = s;
+  if (a.outbf) {
+    const uint32_t w = pack_bf16x2(a.scale * s, 0.f);
+    a.outbf[i] = (bf16_t)(w & 0xFFFFu);
+  }
+}
+
+// out[q][t] = bf16(in[t][qoff + q]) for q < nq, t < T; 0 elsewhere in
+// [RSout x ldp]
+__global__ void k_pack_pt(const float *in, int T, int ldin, int qoff, int nq, int RSout, int ldp,
+                          bf16_t *out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)RSout * ldp) return;
+  const int q = (int)(i / ldp), t = (int)(i % ldp);
+  float v = 0.f;
+  if (q < nq && t < T) v = in[(int64_t)t * ldin + qoff + q];
+  const uint32_t w = pack_bf16x2(v, 0.f);
+  out[i] = (bf16_t)(w & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------------------
