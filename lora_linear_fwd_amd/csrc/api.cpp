@@ -58,8 +58,10 @@ inline DualSplit dual_split(int64_t T, int64_t N, int64_t nsplit) {
   DualSplit d;
   d.nb0 = (int)cdiv(nsplit, 256);
   d.nb1 = (int)cdiv(N - nsplit, 256);
+  // the narrow kernels run 4 workgroups on each of the 256 CUs: fill those
+  // 1024 slots once rather than spill a partial second round
   const int64_t nbc = std::max<int64_t>(1, d.nb0 + d.nb1);
-  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(T, 64), cdiv(1024, nbc)));
+  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(T, 64), 1024 / nbc));
   const int64_t tchunk = std::max<int64_t>(64, cdiv(cdiv(T, ts), 64) * 64);
   d.tchunk = (int)tchunk;
   d.ts = (int)std::max<int64_t>(1, cdiv(T, tchunk));

@@ -270,8 +270,15 @@ __global__ void k_reduce_tn(const ReduceTNArgs a) {
     }
   }
   if (!dst) return;
-  float s = 0.f;
-  for (int k = 0; k < a.ts; ++k) s += a.part[(int64_t)k * count + i];
+  // four interleaved partial sums (a fixed order) keep several loads in flight
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 4 <= a.ts; k += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s4[u] += a.part[(int64_t)(k + u) * count + i];
+  }
+  for (int u = 0; k < a.ts; ++k, ++u) s4[u] += a.part[(int64_t)k * count + i];
+  const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   const uint32_t w = pack_bf16x2(a.scale * s, 0.f);
   *dst = (bf16_t)(w & 0xFFFFu);
 }
@@ -303,8 +310,9 @@ struct DualArgs {
   float *part_v;                   // [token chunks x RSV x N]
 };
 
+// narrow forms are held to 128 VGPRs: 4 workgroups per CU (the LDS limit)
 template <int RSU, int RSV, bool ZSWIGLU>
-__global__ __launch_bounds__(256) void k_skinny_dual(const DualArgs a) {
+__global__ __launch_bounds__(256, (RSU <= 32 && RSV <= 32) ? 4 : 1) void k_skinny_dual(const DualArgs a) {
   constexpr int NQU = RSU / 16, NQV = RSV / 16;
   constexpr int SL = (RSU * 32 + 255) / 256;   // side chunks per thread
   __shared__ __attribute__((aligned(16))) char zs[64 * 512];
@@ -461,9 +469,19 @@ __global__ void k_reduce_dual_u(const ReduceUArgs a) {
     je = s1 ? a.nb0 + a.nb1 : a.nb0;
     ok = qo < 2 * a.r;
   }
-  float s = 0.f;
-  if (ok)
-    for (int jj = jb; jj < je; ++jj) s += a.part[((int64_t)jj * a.T + t) * a.RSU + q];
+  // four interleaved partial sums (a fixed order) keep several loads in flight
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    const float *src = a.part + (int64_t)t * a.RSU + q;
+    const int64_t stride = (int64_t)a.T * a.RSU;
+    int jj = jb;
+    for (; jj + 4 <= je; jj += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s4[u] += src[(int64_t)(jj + u) * stride];
+    }
+    for (int u = 0; jj < je; ++jj, ++u) s4[u] += src[(int64_t)jj * stride];
+  }
+  const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   if (a.out32) a.out32[i] = s;
   if (a.outbf) {
     const uint32_t w = pack_bf16x2(a.scale * s, 0.f);
