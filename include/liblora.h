@@ -187,6 +187,19 @@ int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absma
                   const float *codebook, int blocksize, int out_dtype, void *out,
                   void *stream);
 
+/*
+ * Merged weight out = W + sign * s * B A, s = alpha / r ([DD] 1.2: the
+ * low-rank update dW = B.A; added to the frozen weight it gives one plain
+ * linear layer with the same output, the merged export of [DD] 5.1).
+ * sign = +1 merges, -1 unmerges.  W: dense [n x k] in `dtype`, or 4-bit
+ * (dtype must be LORA_BF16; decoded to bf16 first).  A [r x k], B [n x r]
+ * in `dtype`.  out: [n x k] in `dtype`, device, may not alias W.  B A is
+ * accumulated in fp32; the sum is rounded once to `dtype`.  No workspace.
+ */
+int lora_merge(int dtype, int64_t n, int64_t k, int64_t r, float alpha, int sign,
+               const lora_weight *W, const void *A, const void *B, void *out,
+               void *stream);
+
 /* Workspace bytes of an op (k_or_d / n_or_f as in the op's signature;
  * `wfmt` is the base-weight format): the fast strategy's size, or with
  * LORA_WS_MINIMAL or-ed into `op` the smallest size the op accepts.

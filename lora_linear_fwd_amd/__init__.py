@@ -29,7 +29,7 @@ STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
 
 EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_swiglu_mlp_bwd",
            "lora_dequant4", "lora_workspace_bytes", "lora_strerror", "lora_abi_version",
-           "lora_debug_time_next"]
+           "lora_debug_time_next", "lora_merge"]
 KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX = range(6)
 
 
@@ -68,6 +68,7 @@ def lib():
     L.lora_swiglu_mlp_bwd.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W,
                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.lora_dequant4.argtypes = [i64, i64, vp, vp, vp, i32, i32, vp, vp]
+    L.lora_merge.argtypes = [i32, i64, i64, i64, f32, i32, W, vp, vp, vp, vp]
     L.lora_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i64, i64]
     L.lora_workspace_bytes.restype = sz
     L.lora_strerror.argtypes = [i32]
@@ -76,7 +77,7 @@ def lib():
     L.lora_debug_time_next.argtypes = [i32, vp, vp]
     L.lora_debug_time_next.restype = ctypes.c_int
     for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
-                 "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version"):
+                 "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version", "lora_merge"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -294,6 +295,21 @@ def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, n
         wsp, wsn, _stream(stream)),
         "lora_swiglu_mlp_bwd")
     return o
+
+
+def lora_merge(W: Weight, A, B, alpha: float, sign: int = 1, out=None, stream=None):
+    """W + sign * (alpha/r) B A as a new [n, k] tensor (bf16 for 4-bit W)."""
+    torch = _torch()
+    r = A.shape[0]
+    n, k = (W.n, W.k) if isinstance(W, Q4Weight) else W.shape
+    dt = _dtype_code(A)
+    if out is None:
+        out = torch.empty((n, k), dtype=A.dtype, device=A.device)
+    wst = _wstruct(W)
+    _check(lib().lora_merge(dt, n, k, r, float(alpha), int(sign), ctypes.byref(wst), _ptr(A),
+                            _ptr(B), _ptr(out), _stream(stream)),
+           "lora_merge")
+    return out
 
 
 def lora_dequant4(q: Q4Weight, out=None, stream=None):

@@ -875,6 +875,26 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   return LORA_OK;
 }
 
+int lora_merge(int dtype, int64_t n, int64_t k, int64_t r, float alpha, int sign,
+               const lora_weight *W, const void *A, const void *B, void *out, void *stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (sign != 1 && sign != -1) return LORA_ERR_UNSUPPORTED;
+  if (n <= 0 || k <= 0 || r <= 0 || n > ((int64_t)1 << 24) || k > ((int64_t)1 << 24))
+    return LORA_ERR_BAD_SHAPE;
+  if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  WeightView wv;
+  LORA_TRY(check_weight(W, dtype, k, wv));
+  LORA_TRY(check_ptrs({A, B, out}));
+  const int64_t ncb = cdiv(k, 64), blocks = cdiv(n, 64) * ncb;
+  if (blocks >= ((int64_t)1 << 31)) return LORA_ERR_BAD_SHAPE;
+  MergeArgs a{(int)n, (int)k, (int)r, (int)ncb, (float)sign * (alpha / (float)r),
+              dtype == LORA_F32, wv.q4 ? nullptr : (const void *)wv.w, wv.codes, wv.absmax,
+              wv.codebook, A, B, out};
+  hipLaunchKernelGGL(k_lora_merge, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
 int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absmax,
                   const float *codebook, int blocksize, int out_dtype, void *out, void *stream) {
   if (!codes || !absmax || !codebook || !out) return LORA_ERR_NULL_POINTER;

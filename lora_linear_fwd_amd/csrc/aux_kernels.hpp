@@ -650,6 +650,76 @@ __global__ __launch_bounds__(256) void k_dequant4_t(const uint8_t *codes, const 
 }
 
 // ---------------------------------------------------------------------------
+// Merged weight W' = W + ss * B A (ss = sign * alpha / r): one 64 x 64
+// output tile per workgroup; the tile's B rows and A columns are staged in
+// LDS as fp32, each thread forms 2 rows x 8 columns of B A (fp32 FMA, fixed
+// order over r) and adds them to W (dense bf16 / fp32, or 4-bit decoded to
+// bf16 first), rounding once to the output dtype.  HBM-bound.
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+  int n, k, r, ncb;            // ncb: 64-column blocks
+  float ss;                    // sign * alpha / r
+  int f32;                     // 1: W, A, B, out are fp32; 0: bf16
+  const void *W;               // dense weight (NULL for 4-bit)
+  const uint8_t *codes;        // 4-bit weight
+  const float *absmax, *codebook;
+  const void *A, *B;
+  void *out;
+};
+__global__ __launch_bounds__(256) void k_lora_merge(const MergeArgs a) {
+  __shared__ float bs[64][129];
+  __shared__ float as_[128][64];
+  const int tid = threadIdx.x;
+  const int i0 = (int)(blockIdx.x / (unsigned)a.ncb) * 64;
+  const int j0 = (int)(blockIdx.x % (unsigned)a.ncb) * 64;
+  auto ld = [&](const void *base, int64_t idx) -> float {
+    return a.f32 ? reinterpret_cast<const float *>(base)[idx]
+                 : __uint_as_float((uint32_t)reinterpret_cast<const bf16_t *>(base)[idx] << 16);
+  };
+  for (int e = tid; e < 64 * a.r; e += 256) {
+    const int ii = e / a.r, q = e % a.r, i = i0 + ii;
+    bs[ii][q] = i < a.n ? ld(a.B, (int64_t)i * a.r + q) : 0.f;
+  }
+  for (int e = tid; e < a.r * 64; e += 256) {
+    const int q = e >> 6, jj = e & 63, j = j0 + jj;
+    as_[q][jj] = j < a.k ? ld(a.A, (int64_t)q * a.k + j) : 0.f;
+  }
+  __syncthreads();
+  const int jj0 = (tid & 7) * 8, ii0 = (tid >> 3) * 2;
+  for (int rr = 0; rr < 2; ++rr) {
+    const int ii = ii0 + rr, i = i0 + ii;
+    if (i >= a.n) continue;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < a.r; ++q) {
+      const float b = bs[ii][q];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(b, as_[q][jj0 + c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int j = j0 + jj0 + c;
+      if (j >= a.k) break;
+      const int64_t idx = (int64_t)i * a.k + j;
+      float w;
+      if (a.codes) {   // 4-bit: decode to bf16 (fp32 product, rounded once)
+        const uint32_t byte = a.codes[idx >> 1];
+        const uint32_t code = (idx & 1) ? (byte >> 4) : (byte & 15u);
+        const uint32_t wb = pack_bf16x2(a.codebook[code] * a.absmax[idx >> 6], 0.f);
+        w = bf16lo(wb);
+      } else {
+        w = ld(a.W, idx);
+      }
+      const float v = w + a.ss * acc[c];
+      if (a.f32) {
+        reinterpret_cast<float *>(a.out)[idx] = v;
+      } else {
+        reinterpret_cast<bf16_t *>(a.out)[idx] = (bf16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: generic strided GEMM with fp32 FMA (no matrix cores, so the
 // arithmetic stays IEEE fp32):
 //   C[m][n] = alpha * sum_k A(m,k) B(k,n) + beta * C[m][n]

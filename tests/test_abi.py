@@ -161,3 +161,22 @@ def test_dequant4_validation_codes():
     assert lib.lora_dequant4(16, 128, P, P, P, 32, 1, P, None) == 3
     assert lib.lora_dequant4(16, 128, P, P, P, 64, 0, P, None) == 3
     assert lib.lora_dequant4(16, 128, P_MIS, P, P, 64, 1, P, None) == 5
+
+
+def test_merge_validation_codes():
+    W = _w()
+    call = lambda **kw: L.lib().lora_merge(kw.get("dtype", 1), kw.get("n", 64), kw.get("k", 64),
+                                          kw.get("r", 8), 16.0, kw.get("sign", 1),
+                                          ctypes.byref(kw.get("W", W)), kw.get("A", P),
+                                          kw.get("B", P), kw.get("out", P), None)
+    assert call(A=None) == 1
+    assert call(out=None) == 1
+    assert call(W=_w(w=None)) == 1
+    assert call(dtype=4) == 3
+    assert call(sign=0) == 3
+    assert call(n=0) == 2
+    assert call(k=-1) == 2
+    assert call(r=129) == 3
+    assert call(out=P_MIS) == 5
+    assert call(dtype=0, W=_w(1, 64, None, P, P, P)) == 3     # 4-bit is bf16-only
+    assert call(k=72, W=_w(1, 64, None, P, P, P)) == 2        # 4-bit needs k % 64 == 0
