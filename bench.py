@@ -35,7 +35,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=(2, 3, 5))
+    ap.add_argument("--config", type=int, default=3, choices=(2, 3, 4, 5),
+                    help="2, 3, 5: LoRA-SwiGLU MLP; 4: q/k/v/o LoRA projections + MLP")
+    ap.add_argument("--qkv-separate", action="store_true",
+                    help="config 4: run q, k, v as three LoRA linears instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle baseline runs on")
@@ -131,6 +134,11 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
+def linear_flops(T, k, n, r):
+    """fwd 2Tkn + 2Tr(k+n) plus bwd 2Tnk + 4Tr(n+k) of one LoRA linear (with dX)."""
+    return 4 * T * k * n + 6 * T * r * (k + n)
+
+
 def mlp_flops(T, d, f, r):
     # fwd: 3 x (2 T k n + 2 T r (k + n)); bwd: 3 x (2 T n k + 4 T r (n + k))
     return 12 * T * d * f + 18 * T * r * (d + f)
@@ -185,6 +193,86 @@ def cpu_baseline(cfg, tokens, mi, reps=2):
             "tokens_per_s": tokens / dt, "seconds_per_rep": dt}
 
 
+def bench_attn_mlp(args):
+    """Config 4: q, k, v (shared input, dX summed) and o LoRA projections plus
+    the LoRA-SwiGLU MLP, forward + backward, T = 16384, r = 64."""
+    import numpy as np
+    import torch
+
+    import lora_linear_fwd_amd as L
+    from lora_inputs import CONFIGS, gen_config
+
+    c = CONFIGS[4]
+    T, d, dkv, f, r, alpha = c["T"], c["d"], c["d_kv"], c["f"], c["r"], c["alpha"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = gen_config(4)
+    up = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    att, mi = inp["attn"], inp["mlp"]
+    Xa, Xo = up(att["q"].X), up(att["o"].X)
+    Wa = {p: up(att[p].W) for p in att}
+    Aa = {p: up(att[p].A) for p in att}
+    Ba = {p: up(att[p].B) for p in att}
+    dYa = {p: up(att[p].dY) for p in att}
+    Wm = {p: up(mi.W[p]) for p in mi.W}
+    Am = {p: up(mi.A[p]) for p in mi.A}
+    Bm = {p: up(mi.B[p]) for p in mi.B}
+    Xm, dYm = up(mi.X), up(mi.dY)
+    del inp, att, mi
+    stream = torch.cuda.current_stream()
+    qkv = ("q", "k", "v")
+
+    def step():
+        if args.qkv_separate:
+            for p in qkv:
+                L.lora_linear_fwd(Xa, Wa[p], Aa[p], Ba[p], alpha, stream=stream)
+        else:
+            L.lora_qkv_fwd(Xa, {p: Wa[p] for p in qkv}, Aa, Ba, alpha, stream=stream)
+        L.lora_linear_fwd(Xo, Wa["o"], Aa["o"], Ba["o"], alpha, stream=stream)
+        if args.qkv_separate:
+            dX = None
+            for i, p in enumerate(qkv):
+                dX, _, _ = L.lora_linear_bwd(Xa, Wa[p], Aa[p], Ba[p], alpha, dYa[p], dX=dX,
+                                             accumulate_dx=i > 0, stream=stream)
+        else:
+            L.lora_qkv_bwd(Xa, {p: Wa[p] for p in qkv}, Aa, Ba, alpha, dYa, stream=stream)
+        L.lora_linear_bwd(Xo, Wa["o"], Aa["o"], Ba["o"], alpha, dYa["o"], stream=stream)
+        Y, e, g = L.lora_swiglu_mlp_fwd(Xm, Wm, Am, Bm, alpha, stream=stream)
+        L.lora_swiglu_mlp_bwd(Xm, Wm, Am, Bm, alpha, e, g, dYm, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = (linear_flops(T, d, d, r) * 2 + linear_flops(T, d, dkv, r) * 2
+             + mlp_flops(T, d, f, r))
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "LoRA attention projections + SwiGLU MLP fwd+bwd TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"q/k/v/o LoRA projections (d={d}, d_kv={dkv}, q/k/v "
+                               f"{'separate' if args.qkv_separate else 'fused'}) + LoRA-SwiGLU "
+                               f"MLP (f={f}), T={T}, r={r}, alpha={alpha:g}, bf16",
+                   "config_id": 4, "T": T, "d": d, "d_kv": dkv, "f": f, "r": r},
+        "wall_s_timed": round(wall, 3), "flops_per_step": flops,
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -196,6 +284,9 @@ def main():
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.config), end="")
+        return
+    if args.config == 4:
+        bench_attn_mlp(args)
         return
     import numpy as np
     import torch

@@ -114,6 +114,8 @@ typedef struct {
 #define LORA_OP_LINEAR_BWD 1
 #define LORA_OP_MLP_FWD    2
 #define LORA_OP_MLP_BWD    3
+#define LORA_OP_QKV_FWD    4   /* lora_qkv_workspace_bytes only */
+#define LORA_OP_QKV_BWD    5
 /* or-ed into `op`: size of the minimal-memory strategy */
 #define LORA_WS_MINIMAL    0x100
 
@@ -188,6 +190,47 @@ int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absma
                   void *stream);
 
 /*
+ * Fused q/k/v LoRA projections of one input (the LoRA_QKV pattern of
+ * [CR] 4: three LoRA linears that share X, computed as one):
+ *   Q = lin(X; Wq, Aq, Bq) [T x nq], K = lin(X; Wk, Ak, Bk) [T x nkv],
+ *   V = lin(X; Wv, Av, Bv) [T x nkv], each exactly as lora_linear_fwd.
+ * bf16 with nq, nkv multiples of 256 and 3r <= 256: one GEMM over the
+ * stacked weights [Wq; Wk; Wv] with one rank-3r LoRA pass; other shapes,
+ * ranks and fp32 run the three projections one by one (same results within
+ * the same tolerance).  Weights share one format.  Workspace:
+ * lora_qkv_workspace_bytes(LORA_OP_QKV_FWD, ...).
+ */
+int lora_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                 float alpha, const void *X,
+                 const lora_weight *Wq, const void *Aq, const void *Bq,
+                 const lora_weight *Wk, const void *Ak, const void *Bk,
+                 const lora_weight *Wv, const void *Av, const void *Bv,
+                 void *Q, void *K, void *V, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of lora_qkv_fwd from dQ, dK, dV:
+ *   dX (+)= sum over p in {q, k, v} of dY_p W_p + s (dY_p B_p) A_p
+ *   dA_p = s (dY_p B_p)^T X,  dB_p = s dY_p^T (X A_p^T)
+ * dX NULL skips it; LORA_FLAG_ACCUMULATE_DX adds to dX.  bf16 with the
+ * fast workspace and 3r <= 256: [dQ | dK | dV] is packed into the workspace
+ * and dX is one GEMM with K = nq + 2 nkv against the transposed stacked
+ * weights; otherwise the three projections run one by one.
+ */
+int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                 float alpha, const void *X,
+                 const lora_weight *Wq, const void *Aq, const void *Bq,
+                 const lora_weight *Wk, const void *Ak, const void *Bk,
+                 const lora_weight *Wv, const void *Av, const void *Bv,
+                 const void *dQ, const void *dK, const void *dV, void *dX,
+                 void *dAq, void *dBq, void *dAk, void *dBk, void *dAv, void *dBv,
+                 uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of lora_qkv_fwd / lora_qkv_bwd (op LORA_OP_QKV_FWD or
+ * LORA_OP_QKV_BWD, optionally | LORA_WS_MINIMAL); 0 for invalid arguments. */
+size_t lora_qkv_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t k, int64_t nq,
+                                int64_t nkv, int64_t r);
+
+/*
  * Merged weight out = W + sign * s * B A, s = alpha / r ([DD] 1.2: the
  * low-rank update dW = B.A; added to the frozen weight it gives one plain
  * linear layer with the same output, the merged export of [DD] 5.1).
@@ -219,7 +262,9 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T,
 #define LORA_KC_GATEUP_BWD  3   /* [de|dg] [Wg;Wu] GEMM (MLP dX)           */
 #define LORA_KC_LINEAR_FWD  4   /* lora_linear_fwd GEMM                    */
 #define LORA_KC_LINEAR_DX   5   /* lora_linear_bwd dX GEMM                 */
-#define LORA_KC_COUNT       6
+#define LORA_KC_QKV_FWD     6   /* lora_qkv_fwd fused GEMM                 */
+#define LORA_KC_QKV_DX      7   /* lora_qkv_bwd fused dX GEMM              */
+#define LORA_KC_COUNT       8
 int lora_debug_time_next(int which, void *start, void *stop);
 
 const char *lora_strerror(int status);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "liblora.so")
 LORA_F32, LORA_BF16 = 0, 1
 LORA_W_DENSE, LORA_W_Q4 = 0, 1
 LORA_FLAG_ACCUMULATE_DX = 1
-OP_LINEAR_FWD, OP_LINEAR_BWD, OP_MLP_FWD, OP_MLP_BWD = 0, 1, 2, 3
+OP_LINEAR_FWD, OP_LINEAR_BWD, OP_MLP_FWD, OP_MLP_BWD, OP_QKV_FWD, OP_QKV_BWD = 0, 1, 2, 3, 4, 5
 LORA_WS_MINIMAL = 0x100
 STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
           3: "LORA_ERR_UNSUPPORTED", 4: "LORA_ERR_WORKSPACE", 5: "LORA_ERR_MISALIGNED",
@@ -29,8 +29,10 @@ STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
 
 EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_swiglu_mlp_bwd",
            "lora_dequant4", "lora_workspace_bytes", "lora_strerror", "lora_abi_version",
-           "lora_debug_time_next", "lora_merge"]
-KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX = range(6)
+           "lora_debug_time_next", "lora_merge", "lora_qkv_fwd", "lora_qkv_bwd",
+           "lora_qkv_workspace_bytes"]
+(KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX,
+ KC_QKV_FWD, KC_QKV_DX) = range(8)
 
 
 class LoraError(RuntimeError):
@@ -69,6 +71,12 @@ def lib():
                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.lora_dequant4.argtypes = [i64, i64, vp, vp, vp, i32, i32, vp, vp]
     L.lora_merge.argtypes = [i32, i64, i64, i64, f32, i32, W, vp, vp, vp, vp]
+    L.lora_qkv_fwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W, vp,
+                               vp, vp, vp, vp, vp, sz, vp]
+    L.lora_qkv_bwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W, vp,
+                               vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, sz, vp]
+    L.lora_qkv_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i64, i64, i64]
+    L.lora_qkv_workspace_bytes.restype = sz
     L.lora_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i64, i64]
     L.lora_workspace_bytes.restype = sz
     L.lora_strerror.argtypes = [i32]
@@ -77,7 +85,8 @@ def lib():
     L.lora_debug_time_next.argtypes = [i32, vp, vp]
     L.lora_debug_time_next.restype = ctypes.c_int
     for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
-                 "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version", "lora_merge"):
+                 "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version", "lora_merge",
+                 "lora_qkv_fwd", "lora_qkv_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -176,7 +185,11 @@ def _workspace(op, dt, wfmt, dims, device, workspace=None, minimal=False):
     torch = _torch()
     if workspace is not None:
         return _ptr(workspace), workspace.numel() * workspace.element_size()
-    nbytes = workspace_bytes(op | (LORA_WS_MINIMAL if minimal else 0), dt, wfmt, *dims)
+    flag = LORA_WS_MINIMAL if minimal else 0
+    if op in (OP_QKV_FWD, OP_QKV_BWD):
+        nbytes = int(lib().lora_qkv_workspace_bytes(op | flag, dt, wfmt, *dims))
+    else:
+        nbytes = workspace_bytes(op | flag, dt, wfmt, *dims)
     if nbytes == 0:
         return None, 0
     key = (str(device), torch.cuda.current_stream(device).cuda_stream)
@@ -294,6 +307,63 @@ def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, n
         _ptr(o["dA_down"]), _ptr(o["dB_down"]),
         wsp, wsn, _stream(stream)),
         "lora_swiglu_mlp_bwd")
+    return o
+
+
+def lora_qkv_fwd(X, W: Dict[str, Weight], A, B, alpha: float, out: Optional[dict] = None,
+                 workspace=None, stream=None, minimal_workspace=False):
+    """Returns dict q, k, v of the three LoRA projections of X; W/A/B are
+    dicts keyed 'q', 'k', 'v'."""
+    torch = _torch()
+    T, k = X.shape
+    nq, nkv = W["q"].shape[0], W["k"].shape[0]
+    r = A["q"].shape[0]
+    dt = _dtype_code(X)
+    o = dict(out or {})
+    for p, n in (("q", nq), ("k", nkv), ("v", nkv)):
+        if o.get(p) is None:
+            o[p] = torch.empty((T, n), dtype=X.dtype, device=X.device)
+    wsp, wsn = _workspace(OP_QKV_FWD, dt, _wfmt(W["q"]), (T, k, nq, nkv, r), X.device, workspace,
+                          minimal_workspace)
+    ws_ = [_wstruct(W[p]) for p in ("q", "k", "v")]
+    _check(lib().lora_qkv_fwd(
+        dt, T, k, nq, nkv, r, float(alpha), _ptr(X),
+        ctypes.byref(ws_[0]), _ptr(A["q"]), _ptr(B["q"]),
+        ctypes.byref(ws_[1]), _ptr(A["k"]), _ptr(B["k"]),
+        ctypes.byref(ws_[2]), _ptr(A["v"]), _ptr(B["v"]),
+        _ptr(o["q"]), _ptr(o["k"]), _ptr(o["v"]), wsp, wsn, _stream(stream)), "lora_qkv_fwd")
+    return o
+
+
+def lora_qkv_bwd(X, W: Dict[str, Weight], A, B, alpha: float, dY: Dict[str, object],
+                 need_dx=True, dX=None, accumulate_dx=False, out: Optional[dict] = None,
+                 workspace=None, stream=None, minimal_workspace=False):
+    """Returns dict dX (or None) and dA_p / dB_p for p in q, k, v."""
+    torch = _torch()
+    T, k = X.shape
+    nq, nkv = W["q"].shape[0], W["k"].shape[0]
+    r = A["q"].shape[0]
+    dt = _dtype_code(X)
+    o = dict(out or {})
+    if need_dx:
+        o["dX"] = torch.empty((T, k), dtype=X.dtype, device=X.device) if dX is None else dX
+    else:
+        o["dX"] = None
+    for p in ("q", "k", "v"):
+        o.setdefault("dA_" + p, torch.empty_like(A[p]))
+        o.setdefault("dB_" + p, torch.empty_like(B[p]))
+    wsp, wsn = _workspace(OP_QKV_BWD, dt, _wfmt(W["q"]), (T, k, nq, nkv, r), X.device, workspace,
+                          minimal_workspace)
+    ws_ = [_wstruct(W[p]) for p in ("q", "k", "v")]
+    flags = LORA_FLAG_ACCUMULATE_DX if accumulate_dx else 0
+    _check(lib().lora_qkv_bwd(
+        dt, T, k, nq, nkv, r, float(alpha), _ptr(X),
+        ctypes.byref(ws_[0]), _ptr(A["q"]), _ptr(B["q"]),
+        ctypes.byref(ws_[1]), _ptr(A["k"]), _ptr(B["k"]),
+        ctypes.byref(ws_[2]), _ptr(A["v"]), _ptr(B["v"]),
+        _ptr(dY["q"]), _ptr(dY["k"]), _ptr(dY["v"]), _ptr(o["dX"]),
+        _ptr(o["dA_q"]), _ptr(o["dB_q"]), _ptr(o["dA_k"]), _ptr(o["dB_k"]),
+        _ptr(o["dA_v"]), _ptr(o["dB_v"]), flags, wsp, wsn, _stream(stream)), "lora_qkv_bwd")
     return o
 
 

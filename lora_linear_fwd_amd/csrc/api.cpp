@@ -123,8 +123,12 @@ MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) 
   return p;
 }
 
+// The dual rank-r pass is used up to RS = 32 (2r rounded): its per-column-
+// block partials grow with RS, and at r = 64 they outweigh the second read it
+// saves (measured: 0.97 ms vs 0.5 ms per step at T = 16384).
+inline bool mlp_bwd_dual(int64_t r) { return rs_of(r) <= 32; }
 struct MlpBwdPlan {
-  size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, epi_gu_nn, side_gu_nt;
+  size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, epi_gu_nn, side_gu_nt, side_gu_nn;
   size_t side_g, side_u, pt_d, pt_g, pt_u, part_u, part_v;
   size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, total;
 };
@@ -145,16 +149,59 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) 
   p.ggu32 = b.take((size_t)T * RS1 * 4);
   p.ggubf = b.take((size_t)T * RS1 * 2);
   p.hgu32 = b.take((size_t)T * RS1 * 4);
-  p.ntpart = b.take(std::max(nt_part_bytes(T, d, RS2), nt_part_bytes(T, d, RS1)));
-  p.tnpart = b.take(std::max(tn_part_bytes(T, d, RS2), tn_part_bytes(T, d, RS1)));
-  p.side_g = b.take((size_t)RS2 * f * 2);
-  p.side_u = b.take((size_t)RS2 * f * 2);
-  const size_t ptb = (size_t)RS2 * ldp_of(T) * 2;
-  p.pt_d = b.take(ptb);
-  p.pt_g = b.take(ptb);
-  p.pt_u = b.take(ptb);
-  p.part_u = b.take(std::max(dual_u_bytes(T, f, f, RS2), dual_u_bytes(T, 2 * f, f, RS2)));
-  p.part_v = b.take(std::max(dual_v_bytes(T, f, f, RS2), dual_v_bytes(T, 2 * f, f, RS2)));
+  if (mlp_bwd_dual(r)) {
+    p.ntpart = b.take(std::max(nt_part_bytes(T, d, RS2), nt_part_bytes(T, d, RS1)));
+    p.tnpart = b.take(std::max(tn_part_bytes(T, d, RS2), tn_part_bytes(T, d, RS1)));
+    p.side_g = b.take((size_t)RS2 * f * 2);
+    p.side_u = b.take((size_t)RS2 * f * 2);
+    const size_t ptb = (size_t)RS2 * ldp_of(T) * 2;
+    p.pt_d = b.take(ptb);
+    p.pt_g = b.take(ptb);
+    p.pt_u = b.take(ptb);
+    p.part_u = b.take(std::max(dual_u_bytes(T, f, f, RS2), dual_u_bytes(T, 2 * f, f, RS2)));
+    p.part_v = b.take(std::max(dual_v_bytes(T, f, f, RS2), dual_v_bytes(T, 2 * f, f, RS2)));
+  } else {
+    p.side_gu_nn = b.take((size_t)RS1 * 2 * f * 2);
+    p.ntpart = b.take(std::max({nt_part_bytes(T, d, RS2), nt_part_bytes(T, d, RS1),
+                                nt_part_bytes(T, f, RS2), nt_part_bytes(T, 2 * f, RS1)}));
+    p.tnpart = b.take(std::max({tn_part_bytes(T, d, RS2), tn_part_bytes(T, d, RS1),
+                                tn_part_bytes(T, f, RS2), tn_part_bytes(T, 2 * f, RS1)}));
+  }
+  p.total = b.cur;
+  return p;
+}
+
+// fused q/k/v projections: N = nq + 2 nkv output columns, rank products of
+// width RS3 = 3r rounded up to 16 (q, k, v blocks stacked)
+inline bool qkv_rank_ok(int64_t r) { return rs_of(3 * r) <= 256; }
+struct QkvFwdPlan { size_t side, epi, hpart, hbf, wbuf, total; };
+QkvFwdPlan plan_qkv_fwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r, bool wcopy) {
+  Bump b; QkvFwdPlan p{};
+  const int64_t N = nq + 2 * nkv;
+  const int RS3 = rs_of(3 * r);
+  if (wcopy) p.wbuf = b.take((size_t)N * k * 2);
+  p.side = b.take((size_t)RS3 * k * 2);
+  p.epi = b.take((size_t)N * RS3 * 2);
+  p.hpart = b.take(nt_part_bytes(T, k, RS3));
+  p.hbf = b.take((size_t)T * RS3 * 2);
+  p.total = b.cur;
+  return p;
+}
+struct QkvBwdPlan { size_t dyc, side_nn, epi_nn, side_nt, g32, gbf, h32, ntpart, tnpart, wbuf, total; };
+QkvBwdPlan plan_qkv_bwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r) {
+  Bump b; QkvBwdPlan p{};
+  const int64_t N = nq + 2 * nkv;
+  const int RS3 = rs_of(3 * r);
+  p.wbuf = b.take((size_t)k * N * 2);
+  p.dyc = b.take((size_t)T * N * 2);
+  p.side_nn = b.take((size_t)RS3 * N * 2);
+  p.epi_nn = b.take((size_t)k * RS3 * 2);
+  p.side_nt = b.take((size_t)RS3 * k * 2);
+  p.g32 = b.take((size_t)T * RS3 * 4);
+  p.gbf = b.take((size_t)T * RS3 * 2);
+  p.h32 = b.take((size_t)T * RS3 * 4);
+  p.ntpart = b.take(std::max(nt_part_bytes(T, N, RS3), nt_part_bytes(T, k, RS3)));
+  p.tnpart = b.take(std::max(tn_part_bytes(T, k, RS3), tn_part_bytes(T, N, RS3)));
   p.total = b.cur;
   return p;
 }
@@ -249,22 +296,26 @@ struct Prep {
   PrepBatch b{};
   unsigned blocks = 0;
   void add(int kind, bf16_t *dst, int64_t a, int64_t bb, const void *src0, const void *src1,
-           int64_t r, int64_t split, int tr) {
+           int64_t r, int64_t split, int tr, const void *src2 = nullptr, int64_t split2 = 0) {
     const int64_t cnt = a * bb;
     if (cnt == 0) return;
     PrepJob &j = b.job[b.njobs];
-    j = PrepJob{dst, (const bf16_t *)src0, (const bf16_t *)src1, kind, (int)a, (int)bb, (int)r,
-                (int)split, tr};
+    j = PrepJob{dst, (const bf16_t *)src0, (const bf16_t *)src1, (const bf16_t *)src2, kind,
+                (int)a, (int)bb, (int)r, (int)split, (int)split2, tr};
     b.start[b.njobs] = blocks;
     blocks += (unsigned)cdiv(cnt, 256);
     ++b.njobs;
   }
   // side[q][k], q < RS, k < K
   void side(bf16_t *dst, int RS, int64_t K, const void *s0, const void *s1, int64_t r,
-            int64_t ksplit, int tr) { add(0, dst, RS, K, s0, s1, r, ksplit, tr); }
+            int64_t ksplit, int tr, const void *s2 = nullptr, int64_t ksplit2 = 0) {
+    add(0, dst, RS, K, s0, s1, r, ksplit, tr, s2, ksplit2);
+  }
   // epi[row][q], row < rows, q < RS
   void epi(bf16_t *dst, int64_t rows, int RS, const void *s0, const void *s1, int64_t r,
-           int64_t rsplit, int tr) { add(1, dst, rows, RS, s0, s1, r, rsplit, tr); }
+           int64_t rsplit, int tr, const void *s2 = nullptr, int64_t rsplit2 = 0) {
+    add(1, dst, rows, RS, s0, s1, r, rsplit, tr, s2, rsplit2);
+  }
   int launch(hipStream_t st) {
     if (!b.njobs) return LORA_OK;
     b.start[b.njobs] = blocks;
@@ -305,7 +356,8 @@ int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, cons
 int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const bf16_t *Z0,
               const bf16_t *Z1, int64_t nsplit, int64_t ldz, const bf16_t *E, const bf16_t *G,
               float *part, int64_t r, float scale, int transposed, bf16_t *out0, bf16_t *out1,
-              int64_t out_nsplit, hipStream_t st) {
+              int64_t out_nsplit, hipStream_t st, bf16_t *out2 = nullptr,
+              int64_t out_nsplit2 = 0) {
   const TNSplit sp = tn_split(T, N);
   SkinnyTNArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, P, Z0, Z1, ldz, E, G, part};
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)sp.ts);
@@ -321,8 +373,8 @@ int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const 
   }
 #undef STN
   HIP_TRY(hipGetLastError());
-  ReduceTNArgs ra{part, sp.ts, RS, (int)N, (int)r, (int)out_nsplit, scale, transposed, out0, out1,
-                  (int)r};
+  ReduceTNArgs ra{part,       sp.ts, RS, (int)N, (int)r, (int)out_nsplit, scale, transposed, out0,
+                  out1,       (int)r, out2, (int)out_nsplit2, (int)(2 * r)};
   hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)RS * N)), dim3(256), 0, st, ra);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
@@ -396,7 +448,7 @@ int skinny_dual(int RS, bool zswiglu, int64_t T, int64_t N, int64_t nsplit, int6
     HIP_TRY(hipGetLastError());
   }
   ReduceTNArgs rv{part_v, T > 0 ? sp.ts : 0, RS, (int)N, (int)r, (int)nsplit, vscale, transposed,
-                  vout0, vout1, 0};
+                  vout0, vout1, 0, nullptr, 0, 0};
   hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)RS * N)), dim3(256), 0, st, rv);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
@@ -798,8 +850,14 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   prep.side(side_d_nn, RS2, d, Bd, nullptr, r, d, 1);       // Bd^T [RS2 x d]
   prep.epi(epi_d_nn, f, RS2, Ad, nullptr, r, f, 1);         // Ad^T [f x RS2]
   prep.side(side_d_nt, RS2, f, Ad, nullptr, r, f, 0);       // Ad   [RS2 x f]
-  prep.side(side_g, RS2, f, Bg, nullptr, r, f, 1);          // Bg^T [RS2 x f]
-  prep.side(side_u, RS2, f, Bu, nullptr, r, f, 1);          // Bu^T [RS2 x f]
+  const bool dual = mlp_bwd_dual(r);
+  bf16_t *side_gu_nn = (bf16_t *)(w + pl.side_gu_nn);
+  if (dual) {
+    prep.side(side_g, RS2, f, Bg, nullptr, r, f, 1);        // Bg^T [RS2 x f]
+    prep.side(side_u, RS2, f, Bu, nullptr, r, f, 1);        // Bu^T [RS2 x f]
+  } else {
+    prep.side(side_gu_nn, RS1, 2 * f, Bg, Bu, r, f, 1);     // blockdiag(Bg, Bu)^T
+  }
   prep.epi(epi_gu_nn, d, RS1, Ag, Au, r, d, 1);             // [Ag;Au]^T [d x RS1]
   prep.side(side_gu_nt, RS1, d, Ag, Au, r, d, 0);           // [Ag;Au] [RS1 x d]
   LORA_TRY(prep.launch(st));
@@ -829,10 +887,17 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   }
   // 2. one pass over h = silu(e) g (recomputed): H_d = h Ad^T (fp32, for dBd)
   //    and dAd = s G_d^T h
-  if (T > 0) LORA_TRY(pack_pt(gd32, T, RS2, 0, (int)r, RS2, pt_d, st));   // G_d^T bf16
-  LORA_TRY(skinny_dual(RS2, true, T, f, f, f, nullptr, nullptr, eb, gb, side_d_nt, nullptr, pt_d,
-                       nullptr, part_u, part_v, r, RS2, 1.f, hd32, nullptr, s, 0, (bf16_t *)dAd,
-                       nullptr, st));
+  if (dual) {
+    if (T > 0) LORA_TRY(pack_pt(gd32, T, RS2, 0, (int)r, RS2, pt_d, st));   // G_d^T bf16
+    LORA_TRY(skinny_dual(RS2, true, T, f, f, f, nullptr, nullptr, eb, gb, side_d_nt, nullptr,
+                         pt_d, nullptr, part_u, part_v, r, RS2, 1.f, hd32, nullptr, s, 0,
+                         (bf16_t *)dAd, nullptr, st));
+  } else {
+    LORA_TRY(skinny_nt(RS2, true, T, f, nullptr, nullptr, f, f, eb, gb, side_d_nt, ntpart, hd32,
+                       nullptr, 1.f, st));
+    LORA_TRY(skinny_tn(RS2, true, T, f, gd32, nullptr, nullptr, f, f, eb, gb, tnpart, r, s, 0,
+                       (bf16_t *)dAd, nullptr, f, st));
+  }
   // 3. dBd = s dY^T H_d
   LORA_TRY(skinny_tn(RS2, false, T, d, hd32, dYb, dYb, d, d, nullptr, nullptr, tnpart, r, s, 1,
                      (bf16_t *)dBd, nullptr, d, st));
@@ -840,14 +905,24 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     // 4. H_gu = X [Ag; Au]^T (fp32), its two halves transposed to bf16
     LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,
                        nullptr, 1.f, st));
-    LORA_TRY(pack_pt(hgu32, T, RS1, 0, (int)r, RS2, pt_g, st));
-    LORA_TRY(pack_pt(hgu32, T, RS1, (int)r, (int)r, RS2, pt_u, st));
+    if (dual) {
+      LORA_TRY(pack_pt(hgu32, T, RS1, 0, (int)r, RS2, pt_g, st));
+      LORA_TRY(pack_pt(hgu32, T, RS1, (int)r, (int)r, RS2, pt_u, st));
+    }
   }
-  // 5. one pass over [de | dg]: G_gu = [de Bg | dg Bu] (fp32 for dA_gu, s G_gu in
-  //    bf16 for the dX epilogue) and dBg = s de^T H_g, dBu = s dg^T H_u
-  LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, f, de, dg, nullptr, nullptr, side_g, side_u, pt_g,
-                       pt_u, part_u, part_v, r, RS1, s, ggu32, ggubf, s, 1, (bf16_t *)dBg,
-                       (bf16_t *)dBu, st));
+  // 5. G_gu = [de Bg | dg Bu] (fp32 for dA_gu, s G_gu in bf16 for the dX
+  //    epilogue) and dBg = s de^T H_g, dBu = s dg^T H_u: one pass over [de | dg]
+  if (dual) {
+    LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, f, de, dg, nullptr, nullptr, side_g, side_u,
+                         pt_g, pt_u, part_u, part_v, r, RS1, s, ggu32, ggubf, s, 1, (bf16_t *)dBg,
+                         (bf16_t *)dBu, st));
+  } else {
+    if (T > 0)
+      LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, f, nullptr, nullptr, side_gu_nn, ntpart,
+                         ggu32, ggubf, s, st));
+    LORA_TRY(skinny_tn(RS1, false, T, 2 * f, hgu32, de, dg, f, f, nullptr, nullptr, tnpart, r, s,
+                       1, (bf16_t *)dBg, (bf16_t *)dBu, f, st));
+  }
   if (T > 0 && dX) {
     // 6. dX = de Wg + dg Wu + s [de Bg | dg Bu] [Ag; Au]
     GemmArgs b = gemm_base();
@@ -872,6 +947,182 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   // 7. [dAg; dAu] = s G_gu^T X
   LORA_TRY(skinny_tn(RS1, false, T, d, ggu32, Xb, Xb, d, d, nullptr, nullptr, tnpart, r, s, 0,
                      (bf16_t *)dAg, (bf16_t *)dAu, d, st));
+  return LORA_OK;
+}
+
+size_t lora_qkv_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t k, int64_t nq,
+                                int64_t nkv, int64_t r) {
+  if (op & ~(0xFF | LORA_WS_MINIMAL)) return 0;
+  const bool minimal = (op & LORA_WS_MINIMAL) != 0;
+  const int base = op & 0xFF;
+  if (base != LORA_OP_QKV_FWD && base != LORA_OP_QKV_BWD) return 0;
+  if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4) return 0;
+  if (T < 0 || k <= 0 || nq <= 0 || nkv <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
+  const int lop = base == LORA_OP_QKV_FWD ? LORA_OP_LINEAR_FWD : LORA_OP_LINEAR_BWD;
+  const int mflag = minimal ? LORA_WS_MINIMAL : 0;
+  // the per-projection calls (used for shapes and strategies the fused
+  // kernels do not take) share the workspace
+  size_t need = std::max(lora_workspace_bytes(lop | mflag, dtype, wfmt, T, k, nq, r),
+                         lora_workspace_bytes(lop | mflag, dtype, wfmt, T, k, nkv, r));
+  if (need == 0 && dtype == LORA_BF16) return 0;
+  if (dtype == LORA_BF16 && qkv_rank_ok(r)) {
+    if (base == LORA_OP_QKV_FWD)
+      need = std::max(need, plan_qkv_fwd(T, k, nq, nkv, r, !minimal && wfmt == LORA_W_Q4).total);
+    else if (!minimal)
+      need = std::max(need, plan_qkv_bwd(T, k, nq, nkv, r).total);
+  }
+  return need;
+}
+
+int lora_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                 float alpha, const void *X, const lora_weight *Wq, const void *Aq,
+                 const void *Bq, const lora_weight *Wk, const void *Ak, const void *Bk,
+                 const lora_weight *Wv, const void *Av, const void *Bv, void *Q, void *K,
+                 void *V, void *ws, size_t ws_bytes, void *stream) {
+  LORA_TRY(check_dims(dtype, T, k, nq, r));
+  LORA_TRY(check_dims(dtype, T, k, nkv, r));
+  WeightView wq, wk, wv;
+  LORA_TRY(check_weight(Wq, dtype, k, wq));
+  LORA_TRY(check_weight(Wk, dtype, k, wk));
+  LORA_TRY(check_weight(Wv, dtype, k, wv));
+  if (wq.q4 != wk.q4 || wq.q4 != wv.q4) return LORA_ERR_UNSUPPORTED;
+  LORA_TRY(check_ptrs({Aq, Bq, Ak, Bk, Av, Bv}));
+  LORA_TRY(check_tok_ptrs(T, {X, Q, K, V}));
+  const size_t need = lora_qkv_workspace_bytes(LORA_OP_QKV_FWD | LORA_WS_MINIMAL, dtype, Wq->fmt,
+                                               T, k, nq, nkv, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  const bool fast =
+      ws_bytes >= lora_qkv_workspace_bytes(LORA_OP_QKV_FWD, dtype, Wq->fmt, T, k, nq, nkv, r);
+  if (T == 0) return LORA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const bool fused = dtype == LORA_BF16 && qkv_rank_ok(r) && nq % BN == 0 && nkv % BN == 0 &&
+                     (!wq.q4 || fast);
+  if (!fused) {   // one LoRA linear per projection, same kernels
+    LORA_TRY(lora_linear_fwd(dtype, T, k, nq, r, alpha, X, Wq, Aq, Bq, Q, ws, ws_bytes, stream));
+    LORA_TRY(lora_linear_fwd(dtype, T, k, nkv, r, alpha, X, Wk, Ak, Bk, K, ws, ws_bytes, stream));
+    return lora_linear_fwd(dtype, T, k, nkv, r, alpha, X, Wv, Av, Bv, V, ws, ws_bytes, stream);
+  }
+  const int64_t N = nq + 2 * nkv;
+  const int RS3 = rs_of(3 * r);
+  const float s = alpha / (float)r;
+  char *w = (char *)ws;
+  const QkvFwdPlan pl = plan_qkv_fwd(T, k, nq, nkv, r, wq.q4);
+  bf16_t *side = (bf16_t *)(w + pl.side), *epi = (bf16_t *)(w + pl.epi);
+  bf16_t *hbf = (bf16_t *)(w + pl.hbf);
+  if (wq.q4) {   // decode the three weights once, stacked [Wq; Wk; Wv]
+    bf16_t *wb = (bf16_t *)(w + pl.wbuf);
+    LORA_TRY(decode_w(wb, wq, nq, k, st));
+    LORA_TRY(decode_w(wb + nq * k, wk, nkv, k, st));
+    LORA_TRY(decode_w(wb + (nq + nkv) * k, wv, nkv, k, st));
+    wq = dense_view(wb);
+    wk = dense_view(wb + nq * k);
+    wv = dense_view(wb + (nq + nkv) * k);
+  }
+  Prep prep;
+  prep.side(side, RS3, k, Aq, Ak, r, k, 0, Av, k);                  // [Aq; Ak; Av]
+  prep.epi(epi, N, RS3, Bq, Bk, r, nq, 0, Bv, nq + nkv);            // blockdiag(Bq, Bk, Bv)
+  LORA_TRY(prep.launch(st));
+  const bf16_t *Xb = (const bf16_t *)X;
+  LORA_TRY(skinny_nt(RS3, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side,
+                     (float *)(w + pl.hpart), nullptr, hbf, s, st));
+  GemmArgs a = gemm_base();
+  a.M = (int)T; a.N = (int)N; a.K = (int)k; a.ksplit = (int)k;
+  a.A0 = a.A1 = Xb; a.lda = k;
+  a.B0 = wq.w; a.B1 = wk.w; a.B2 = wv.w; a.ldb = k;
+  a.nseg1 = (int)nq; a.nseg2 = (int)(nq + nkv);
+  a.rs = RS3; a.epi = epi; a.hglob = hbf;
+  a.C = (bf16_t *)Q; a.ldc = nq;
+  a.C1 = (bf16_t *)K; a.ldc1 = nkv;
+  a.C2 = (bf16_t *)V; a.ldc2 = nkv;
+  a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)(N / BN);
+  return run_gemm(LORA_KC_QKV_FWD, false, false, EPI_STORE, a, st);
+}
+
+int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                 float alpha, const void *X, const lora_weight *Wq, const void *Aq,
+                 const void *Bq, const lora_weight *Wk, const void *Ak, const void *Bk,
+                 const lora_weight *Wv, const void *Av, const void *Bv, const void *dQ,
+                 const void *dK, const void *dV, void *dX, void *dAq, void *dBq, void *dAk,
+                 void *dBk, void *dAv, void *dBv, uint32_t flags, void *ws, size_t ws_bytes,
+                 void *stream) {
+  LORA_TRY(check_dims(dtype, T, k, nq, r));
+  LORA_TRY(check_dims(dtype, T, k, nkv, r));
+  WeightView wq, wk, wv;
+  LORA_TRY(check_weight(Wq, dtype, k, wq));
+  LORA_TRY(check_weight(Wk, dtype, k, wk));
+  LORA_TRY(check_weight(Wv, dtype, k, wv));
+  if (wq.q4 != wk.q4 || wq.q4 != wv.q4) return LORA_ERR_UNSUPPORTED;
+  LORA_TRY(check_ptrs({Aq, Bq, Ak, Bk, Av, Bv, dAq, dBq, dAk, dBk, dAv, dBv}));
+  LORA_TRY(check_tok_ptrs(T, {X, dQ, dK, dV}));
+  if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
+  if (flags & ~(uint32_t)LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
+  const size_t need = lora_qkv_workspace_bytes(LORA_OP_QKV_BWD | LORA_WS_MINIMAL, dtype, Wq->fmt,
+                                               T, k, nq, nkv, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  const bool fast =
+      ws_bytes >= lora_qkv_workspace_bytes(LORA_OP_QKV_BWD, dtype, Wq->fmt, T, k, nq, nkv, r);
+  hipStream_t st = (hipStream_t)stream;
+  const bool fused = dtype == LORA_BF16 && qkv_rank_ok(r) && fast;
+  if (!fused) {   // one LoRA linear per projection; their dX contributions accumulate
+    LORA_TRY(lora_linear_bwd(dtype, T, k, nq, r, alpha, X, Wq, Aq, Bq, dQ, dX, dAq, dBq, flags,
+                             ws, ws_bytes, stream));
+    LORA_TRY(lora_linear_bwd(dtype, T, k, nkv, r, alpha, X, Wk, Ak, Bk, dK, dX, dAk, dBk,
+                             LORA_FLAG_ACCUMULATE_DX, ws, ws_bytes, stream));
+    return lora_linear_bwd(dtype, T, k, nkv, r, alpha, X, Wv, Av, Bv, dV, dX, dAv, dBv,
+                           LORA_FLAG_ACCUMULATE_DX, ws, ws_bytes, stream);
+  }
+  const int64_t N = nq + 2 * nkv;
+  const int RS3 = rs_of(3 * r);
+  const float s = alpha / (float)r;
+  const bool acc = (flags & LORA_FLAG_ACCUMULATE_DX) != 0;
+  char *w = (char *)ws;
+  const QkvBwdPlan pl = plan_qkv_bwd(T, k, nq, nkv, r);
+  bf16_t *dyc = (bf16_t *)(w + pl.dyc), *wt = (bf16_t *)(w + pl.wbuf);
+  bf16_t *side_nn = (bf16_t *)(w + pl.side_nn), *epi_nn = (bf16_t *)(w + pl.epi_nn);
+  bf16_t *side_nt = (bf16_t *)(w + pl.side_nt), *gbf = (bf16_t *)(w + pl.gbf);
+  float *g32 = (float *)(w + pl.g32), *h32 = (float *)(w + pl.h32);
+  float *ntpart = (float *)(w + pl.ntpart), *tnpart = (float *)(w + pl.tnpart);
+  const bf16_t *Xb = (const bf16_t *)X;
+  Prep prep;
+  prep.side(side_nn, RS3, N, Bq, Bk, r, nq, 1, Bv, nq + nkv);       // blockdiag(Bq,Bk,Bv)^T
+  prep.epi(epi_nn, k, RS3, Aq, Ak, r, k, 1, Av, k);                 // [Aq; Ak; Av]^T
+  prep.side(side_nt, RS3, k, Aq, Ak, r, k, 0, Av, k);               // [Aq; Ak; Av]
+  LORA_TRY(prep.launch(st));
+  if (T > 0) {
+    // [dQ | dK | dV] as one [T x N] operand
+    hipLaunchKernelGGL(k_concat3, dim3(blocks_for(T * (N / 8))), dim3(256), 0, st,
+                       (const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV, (int)nq,
+                       (int)nkv, (int)nkv, T, dyc);
+    HIP_TRY(hipGetLastError());
+    // G = [dQ Bq | dK Bk | dV Bv] (fp32 for dA, s G in bf16 for the dX epilogue)
+    LORA_TRY(skinny_nt(RS3, false, T, N, dyc, dyc, N, N, nullptr, nullptr, side_nn, ntpart, g32,
+                       gbf, s, st));
+    if (dX) {
+      // dX (+)= [dQ | dK | dV] [Wq; Wk; Wv] + s G [Aq; Ak; Av]: one GEMM, K = N
+      LORA_TRY(transpose_w(wt, N, wq, nq, k, st));
+      LORA_TRY(transpose_w(wt + nq, N, wk, nkv, k, st));
+      LORA_TRY(transpose_w(wt + nq + nkv, N, wv, nkv, k, st));
+      GemmArgs a = gemm_base();
+      a.M = (int)T; a.N = (int)k; a.K = (int)N; a.ksplit = (int)N;
+      a.A0 = a.A1 = dyc; a.lda = N;
+      const WeightView tv = dense_view(wt);
+      set_b(a, tv, tv); a.ldb = N;
+      a.rs = RS3; a.epi = epi_nn; a.hglob = gbf;
+      a.accumulate = acc; a.C = (bf16_t *)dX; a.ldc = k;
+      a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
+      LORA_TRY(run_gemm(LORA_KC_QKV_DX, false, false, EPI_STORE, a, st));
+    }
+    // H = X [Aq; Ak; Av]^T
+    LORA_TRY(skinny_nt(RS3, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,
+                       nullptr, 1.f, st));
+  }
+  // [dAq; dAk; dAv] = s G^T X ;  dBq = s dQ^T H_q, dBk = s dK^T H_k, dBv = s dV^T H_v
+  LORA_TRY(skinny_tn(RS3, false, T, k, g32, Xb, Xb, k, k, nullptr, nullptr, tnpart, r, s, 0,
+                     (bf16_t *)dAq, (bf16_t *)dAk, k, st, (bf16_t *)dAv, 0));
+  LORA_TRY(skinny_tn(RS3, false, T, N, h32, dyc, dyc, N, N, nullptr, nullptr, tnpart, r, s, 1,
+                     (bf16_t *)dBq, (bf16_t *)dBk, nq, st, (bf16_t *)dBv, nq + nkv));
   return LORA_OK;
 }
 

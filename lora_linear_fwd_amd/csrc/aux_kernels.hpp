@@ -252,6 +252,10 @@ struct ReduceTNArgs {
   int transposed;
   bf16_t *out0, *out1;
   int q1;
+  // optional third block: rowmajor rows q in [2r, 3r); transposed columns
+  // n >= nsplit2 with q in [q2, q2 + r)
+  bf16_t *out2;
+  int nsplit2, q2;
 };
 __global__ void k_reduce_tn(const ReduceTNArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -262,9 +266,12 @@ __global__ void k_reduce_tn(const ReduceTNArgs a) {
   if (!a.transposed) {
     if (q < a.r) dst = a.out0 + (int64_t)q * a.N + n;
     else if (q < 2 * a.r && a.out1) dst = a.out1 + (int64_t)(q - a.r) * a.N + n;
+    else if (q >= 2 * a.r && q < 3 * a.r && a.out2) dst = a.out2 + (int64_t)(q - 2 * a.r) * a.N + n;
   } else {
     if (n < a.nsplit) {
       if (q < a.r) dst = a.out0 + (int64_t)n * a.r + q;
+    } else if (a.out2 && n >= a.nsplit2) {
+      if (q >= a.q2 && q < a.q2 + a.r) dst = a.out2 + (int64_t)(n - a.nsplit2) * a.r + (q - a.q2);
     } else if (a.out1 && q >= a.q1 && q < a.q1 + a.r) {
       dst = a.out1 + (int64_t)(n - a.nsplit) * a.r + (q - a.q1);
     }
@@ -504,23 +511,25 @@ __global__ void k_pack_pt(const float *in, int T, int ldin, int qoff, int nq, in
 
 // ---------------------------------------------------------------------------
 // operand preparation (tiny, bf16 copies with zero padding)
+// Up to three sources, stacked: source i fills rows (side) or columns (epi)
+// q in [i r, (i+1) r).
 // side[q][k], q < RS, k < K:
-//   !tr: q < r -> src0[q][k] (ld K); r <= q < 2r -> src1[q-r][k]
-//    tr: k < ksplit: q < r -> src0[k][q] (ld r);  k >= ksplit: r <= q < 2r ->
-//        src1[k-ksplit][q-r]
+//   !tr: q in block i -> src_i[q - i r][k] (ld K)
+//    tr: k in [split_i, split_{i+1}) (split_0 = 0, split_3 = K) and q in block
+//        i -> src_i[k - split_i][q - i r] (ld r)
 // epi[row][q], row < rows, q < RS:
-//   !tr (from B [rows x r]): row < rsplit: q < r -> src0[row][q];
-//                            row >= rsplit: r <= q < 2r -> src1[row-rsplit][q-r]
-//    tr (from A [r x rows]): q < r -> src0[q][row]; r <= q < 2r -> src1[q-r][row]
-// Every other element is zero.
+//   !tr (from B [rows x r]): row in [split_i, split_{i+1}) and q in block i ->
+//        src_i[row - split_i][q - i r]
+//    tr (from A [r x rows]): q in block i -> src_i[q - i r][row]
+// Every other element is zero.  With two sources split_2 = K (or rows).
 // ---------------------------------------------------------------------------
 // All the small operand copies of one call in a single launch: block b
 // works on the job whose block range [start[j], start[j+1]) holds b.
 struct PrepJob {
   bf16_t *dst;
-  const bf16_t *src0, *src1;
+  const bf16_t *src0, *src1, *src2;
   int kind;            // 0: side [a = RS x b = K], 1: epi [a = rows x b = RS]
-  int a, b, r, split, tr;
+  int a, b, r, split, split2, tr;
 };
 constexpr int kMaxPrepJobs = 8;
 struct PrepBatch {
@@ -535,30 +544,31 @@ __global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
   const int64_t i = (int64_t)(blockIdx.x - pb.start[j]) * 256 + threadIdx.x;
   if (i >= (int64_t)jb.a * jb.b) return;
   const int r = jb.r;
+  const bf16_t *src[3] = {jb.src0, jb.src1, jb.src2};
   bf16_t v = 0;
   if (jb.kind == 0) {   // side[q][k]
     const int K = jb.b, q = (int)(i / K), k = (int)(i % K);
-    if (!jb.tr) {
-      if (q < r) v = jb.src0[(int64_t)q * K + k];
-      else if (jb.src1 && q < 2 * r) v = jb.src1[(int64_t)(q - r) * K + k];
-    } else {
-      if (k < jb.split) {
-        if (q < r) v = jb.src0[(int64_t)k * r + q];
-      } else if (jb.src1 && q >= r && q < 2 * r) {
-        v = jb.src1[(int64_t)(k - jb.split) * r + (q - r)];
+    const int blk = q / r;
+    if (blk < 3 && src[blk]) {
+      if (!jb.tr) {
+        v = src[blk][(int64_t)(q - blk * r) * K + k];
+      } else {
+        const int lo = blk == 0 ? 0 : (blk == 1 ? jb.split : jb.split2);
+        const int hi = blk == 0 ? jb.split : (blk == 1 ? (jb.src2 ? jb.split2 : K) : K);
+        if (k >= lo && k < hi) v = src[blk][(int64_t)(k - lo) * r + (q - blk * r)];
       }
     }
   } else {              // epi[row][q]
     const int rows = jb.a, RS = jb.b, row = (int)(i / RS), q = (int)(i % RS);
-    if (!jb.tr) {
-      if (row < jb.split) {
-        if (q < r) v = jb.src0[(int64_t)row * r + q];
-      } else if (jb.src1 && q >= r && q < 2 * r) {
-        v = jb.src1[(int64_t)(row - jb.split) * r + (q - r)];
+    const int blk = q / r;
+    if (blk < 3 && src[blk]) {
+      if (!jb.tr) {
+        const int lo = blk == 0 ? 0 : (blk == 1 ? jb.split : jb.split2);
+        const int hi = blk == 0 ? jb.split : (blk == 1 ? (jb.src2 ? jb.split2 : rows) : rows);
+        if (row >= lo && row < hi) v = src[blk][(int64_t)(row - lo) * r + (q - blk * r)];
+      } else {
+        v = src[blk][(int64_t)(q - blk * r) * rows + row];
       }
-    } else {
-      if (q < r) v = jb.src0[(int64_t)q * rows + row];
-      else if (jb.src1 && q < 2 * r) v = jb.src1[(int64_t)(q - r) * rows + row];
     }
   }
   jb.dst[i] = v;
@@ -647,6 +657,23 @@ __global__ __launch_bounds__(256) void k_dequant4_t(const uint8_t *codes, const 
 #pragma unroll
     for (int j = 0; j < 8; ++j) gstore16(out + (int64_t)(c0 + 8 * w + j) * ld_out + r0, t[j]);
   }
+}
+
+// [T x (n0 + n1 + n2)] <- [src0 | src1 | src2] row by row (bf16, column
+// counts multiples of 8; 16 bytes per thread)
+__global__ __launch_bounds__(256) void k_concat3(const bf16_t *src0, const bf16_t *src1,
+                                                 const bf16_t *src2, int n0, int n1, int n2,
+                                                 int64_t T, bf16_t *dst) {
+  const int N8 = (n0 + n1 + n2) / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * N8) return;
+  const int64_t t = i / N8;
+  const int c = (int)(i % N8) * 8;
+  const bf16_t *src;
+  if (c < n0) src = src0 + t * n0 + c;
+  else if (c < n0 + n1) src = src1 + t * n1 + (c - n0);
+  else src = src2 + t * n2 + (c - n0 - n1);
+  gstore16(dst + t * (n0 + n1 + n2) + c, gload16(src));
 }
 
 // ---------------------------------------------------------------------------

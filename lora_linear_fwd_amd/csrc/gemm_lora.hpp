@@ -78,6 +78,14 @@ struct GemmArgs {
   const bf16_t *Ein, *Gin;      // SwiGLU backward saved activations [M x N]
   bf16_t *DE, *DG;              // SwiGLU backward outputs [M x N]
   int tiles_m, tiles_n;
+  // dense NT store form with N split into up to three segments (fused
+  // q/k/v projections): columns [0, nseg1) use B0 / C, [nseg1, nseg2) B1 / C1,
+  // [nseg2, N) B2 / C2; boundaries are multiples of the 256-column tile.
+  // nseg1 = 0: one segment.
+  int nseg1, nseg2;
+  const bf16_t *B2;
+  bf16_t *C1, *C2;
+  int64_t ldc1, ldc2;
 };
 
 // XCD-aware, grouped tile order.  Workgroups are dispatched round-robin over
@@ -213,7 +221,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
       rsB0 = make_rsrc(p.B0 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
       rsB1 = make_rsrc(p.B1 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
     } else {
-      rsB0 = rsB1 = make_rsrc(p.B0 + (int64_t)n0 * p.ldb, kMaxRecords);
+      const bf16_t *bseg = p.B0;
+      int nsb = 0;
+      if (p.nseg1 > 0 && n0 >= p.nseg1) {
+        const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
+        bseg = s2 ? p.B2 : p.B1;
+        nsb = s2 ? p.nseg2 : p.nseg1;
+      }
+      rsB0 = rsB1 = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
     }
 #pragma unroll
     for (int u = 0; u < NDMA; ++u) {
@@ -681,7 +696,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
                       __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
                       __uint_as_float(a1[2]), __uint_as_float(a1[3])};
         if constexpr (EPI == EPI_STORE) {
-          bf16_t *dst = p.C + (int64_t)m * p.ldc + n;
+          bf16_t *cb = p.C;
+          int64_t ldc = p.ldc;
+          int ncs = 0;
+          if (p.nseg1 > 0 && n0 >= p.nseg1) {
+            const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
+            cb = s2 ? p.C2 : p.C1;
+            ldc = s2 ? p.ldc2 : p.ldc1;
+            ncs = s2 ? p.nseg2 : p.nseg1;
+          }
+          bf16_t *dst = cb + (int64_t)m * ldc + (n - ncs);
           if (p.accumulate) {
             const u32x4 o = gload16(dst);
 #pragma unroll

@@ -131,3 +131,35 @@ def test_full_dequant4_8b_weight():
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
     ref = oracle.decode_q4_bits(q.codes, q.absmax, q.codebook, q.n, q.k)
     assert np.array_equal(got, ref)
+
+
+def test_full_config4_fused_qkv():
+    """The fused q/k/v path at the 8B attention shape (T = 16384, d = 4096,
+    d_kv = 1024, r = 64): sampled rows of q, k, v and dX, full adapter
+    gradients."""
+    import torch
+    log("config 4: generating attention inputs (fused q/k/v)")
+    layers = gen_config(4, part="attn")["attn"]
+    T = layers["q"].T
+    rows = sample_rows(T, seed=41)
+    rt = torch.from_numpy(rows).to("cuda")
+    X = dev(layers["q"].X, "bf16")
+    W = {p: dev(layers[p].W, "bf16") for p in ("q", "k", "v")}
+    A = {p: dev(layers[p].A, "bf16") for p in ("q", "k", "v")}
+    B = {p: dev(layers[p].B, "bf16") for p in ("q", "k", "v")}
+    dY = {p: dev(layers[p].dY, "bf16") for p in ("q", "k", "v")}
+    alpha = layers["q"].alpha
+    out = L.lora_qkv_fwd(X, W, A, B, alpha)
+    g = L.lora_qkv_bwd(X, W, A, B, alpha, dY)
+    torch.cuda.synchronize()
+    dX_ref = 0.0
+    for p in ("q", "k", "v"):
+        li = layers[p]
+        s = oracle.scaling(li.alpha, li.r)
+        check(f"{p}[rows]", host(out[p][rt]), oracle.linear_fwd(li.X[rows], li.W, li.A, li.B, s),
+              "bf16")
+        _, dAr, dBr = oracle.linear_bwd(li.X, li.W, li.A, li.B, s, li.dY, want_dx=False)
+        check(f"dA_{p}", host(g["dA_" + p]), dAr, "bf16")
+        check(f"dB_{p}", host(g["dB_" + p]), dBr, "bf16")
+        dX_ref = dX_ref + oracle.linear_bwd(li.X[rows], li.W, li.A, li.B, s, li.dY[rows])[0]
+    check("dX[rows]", host(g["dX"][rt]), dX_ref, "bf16")
