@@ -96,7 +96,10 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int 
   const int nwg = tiles_m * tiles_n;
   int logical = bid;
   if ((nwg & 7) == 0) logical = (bid & 7) * (nwg >> 3) + (bid >> 3);
-  constexpr int GM = 4;
+#ifndef LORA_GEMM_GM
+#define LORA_GEMM_GM 4
+#endif
+  constexpr int GM = LORA_GEMM_GM;
   const int group = logical / (GM * tiles_n);
   const int first_m = group * GM;
   const int gsz = min(tiles_m - first_m, GM);
