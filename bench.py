@@ -169,7 +169,7 @@ def cpu_baseline(cfg, tokens, mi, reps=2):
     tokens = min(tokens, c["T"])
     W = dict(mi.W)
     if mi.q4:
-        W = {p: oracle.decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k) for p, q in mi.q4.items()}
+        W = {p: oracle.decode_q4_weight(q) for p, q in mi.q4.items()}
     s = oracle.scaling(mi.alpha, mi.r)
     X, dY = mi.X[:tokens].astype(np.float64), mi.dY[:tokens].astype(np.float64)
     Wf = {p: np.asarray(v, np.float64) for p, v in W.items()}

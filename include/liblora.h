@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 #define LORA_MAX_RANK 128
 
 /* status codes */
@@ -82,7 +82,7 @@ extern "C" {
 #define LORA_ERR_HIP          6
 
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
-typedef enum { LORA_W_DENSE = 0, LORA_W_Q4 = 1 } lora_wfmt;
+typedef enum { LORA_W_DENSE = 0, LORA_W_Q4 = 1, LORA_W_Q4_DQ = 2 } lora_wfmt;
 
 /* flags */
 #define LORA_FLAG_ACCUMULATE_DX 1u   /* lora_linear_bwd: dX += result */
@@ -99,14 +99,32 @@ typedef enum { LORA_W_DENSE = 0, LORA_W_Q4 = 1 } lora_wfmt;
  *   Decoded value of element i: bf16_rne(codebook[c_i] * absmax[i/64]) with
  *   the product taken as one fp32 multiply (round to nearest even).
  *   Requires k % 64 == 0 and the bf16 dtype.
+ *   Q4_DQ ([DD] 1.4, double quantisation: the per-block constants are
+ *     themselves quantised): as Q4, but `absmax` is unused and the scale of
+ *     64-block b is decoded from 8 bits,
+ *       absmax[b] = absmax_codebook[absmax_codes[b]] * absmax_scale[b / 256]
+ *                   + absmax_offset,
+ *     the product and the sum each one fp32 operation rounded to nearest
+ *     even (no fused multiply-add).  The pages name the technique only;
+ *     the 8-bit codes through a 256-level table, one fp32 scale per 256
+ *     first-level blocks and one fp32 offset are this library's reading.
+ *     absmax_codes:    n*k/64 bytes;  absmax_codebook: 256 fp32 (device);
+ *     absmax_scale:    ceil(n*k/64 / 256) fp32;  absmax_blocksize: 256.
+ *   Fields after `codebook` are read only for Q4_DQ.  All device pointers
+ *   16-byte aligned.  The library never writes through any of them.
  */
 typedef struct {
   int32_t fmt;              /* lora_wfmt */
-  int32_t blocksize;        /* Q4 only; must be 64 */
+  int32_t blocksize;        /* Q4, Q4_DQ; must be 64 */
   const void *w;            /* DENSE */
-  const uint8_t *codes;     /* Q4 */
+  const uint8_t *codes;     /* Q4, Q4_DQ */
   const float *absmax;      /* Q4 */
-  const float *codebook;    /* Q4 */
+  const float *codebook;    /* Q4, Q4_DQ */
+  const uint8_t *absmax_codes;     /* Q4_DQ */
+  const float *absmax_codebook;    /* Q4_DQ */
+  const float *absmax_scale;       /* Q4_DQ */
+  float absmax_offset;             /* Q4_DQ */
+  int32_t absmax_blocksize;        /* Q4_DQ; must be 256 */
 } lora_weight;
 
 /* ops for lora_workspace_bytes */
@@ -188,6 +206,17 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r,
 int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absmax,
                   const float *codebook, int blocksize, int out_dtype, void *out,
                   void *stream);
+
+/*
+ * Decode a quantised base weight of either 4-bit format (Q4 or Q4_DQ,
+ * [DD] 1.4) to bf16 with exactly the values every other entry point uses:
+ * out[i] = bf16_rne(codebook[c_i] * absmax[i / 64]), absmax decoded from
+ * its 8-bit codes first for Q4_DQ (see lora_weight).  out: n*k bf16,
+ * device, 16-byte aligned; out_dtype must be LORA_BF16.  DENSE weights are
+ * rejected with LORA_ERR_UNSUPPORTED.  No workspace.
+ */
+int lora_decode_weight(int64_t n, int64_t k, const lora_weight *W, int out_dtype, void *out,
+                       void *stream);
 
 /*
  * Fused q/k/v LoRA projections of one input (the LoRA_QKV pattern of

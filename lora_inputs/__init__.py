@@ -14,7 +14,10 @@ bound of Kaiming-uniform with a=sqrt(5) that the LoRA reference layer of the
 B ~ N(0, b_std) with b_std = 0.02 (B != 0 on purpose, so the adapter term is
 exercised; B = 0 is the page's initialisation and is used by invariant tests).
 The 4-bit workload draws codes uniformly over 0..15 and one fp32 absmax
-~ |N(0,0.05)| per block of 64 consecutive in-features of a weight row.
+~ |N(0,0.05)| per block of 64 consecutive in-features of a weight row.  The
+double-quantised 4-bit form (q4="dq") draws the blocks' 8-bit constant codes
+uniformly over 0..255, one scale ~ U(0.01, 0.03) per 256 blocks and uses the
+offset 0.04 with a 256-level table evenly spaced over [-1, 1].
 """
 from __future__ import annotations
 
@@ -73,17 +76,38 @@ def make_codebook() -> np.ndarray:
 # --------------------------------------------------------------------------
 # tensor containers
 # --------------------------------------------------------------------------
+def make_absmax_codebook() -> np.ndarray:
+    """256 float32 levels evenly spaced over [-1, 1] (level c = (2c - 255) /
+    255): the table the 8-bit codes of double-quantised block constants
+    index in the synthetic weights."""
+    c = np.arange(256, dtype=np.float64)
+    return ((2.0 * c - 255.0) / 255.0).astype(np.float32)
+
+
 @dataclass
 class Q4Weight:
     """4-bit base weight [n x k]: codes[n, k/2] (flat element 2j in the low
     nibble of byte j), absmax[n*k/64] fp32 (block = 64 consecutive k of one
-    row), codebook[16] fp32."""
+    row), codebook[16] fp32.
+
+    Double-quantised form (absmax None): absmax_codes[n*k/64] uint8,
+    absmax_codebook[256] fp32, absmax_scale[ceil(n*k/64 / 256)] fp32 and
+    one float absmax_offset."""
     n: int
     k: int
     codes: np.ndarray
-    absmax: np.ndarray
+    absmax: Optional[np.ndarray]
     codebook: np.ndarray
     blocksize: int = Q4_BLOCK
+    absmax_codes: Optional[np.ndarray] = None
+    absmax_codebook: Optional[np.ndarray] = None
+    absmax_scale: Optional[np.ndarray] = None
+    absmax_offset: float = 0.0
+    absmax_blocksize: int = 256
+
+    @property
+    def double_quant(self) -> bool:
+        return self.absmax_codes is not None
 
 
 @dataclass
@@ -135,15 +159,23 @@ def _uniform(rng, shape, bound, dtype):
     return to_bf16_values(x) if dtype == "bf16" else x
 
 
-def _q4(rng, n, k, codebook) -> Q4Weight:
+def _q4(rng, n, k, codebook, dq=False) -> Q4Weight:
+    """Random 4-bit codes; block constants drawn directly (plain: |N(0,
+    0.05^2)|; double-quantised: uniform 8-bit codes, per-256-block scales
+    uniform in [0.01, 0.03], offset 0.04, so every constant lies in (0,
+    0.07]).  Nothing is quantised here: the codes are the data."""
     if k % Q4_BLOCK:
         raise ValueError("4-bit weights need k % 64 == 0")
     codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
-    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    absmax = np.abs(rng.standard_normal(size=(n * k) // Q4_BLOCK,
-                                        dtype=np.float32) * np.float32(0.05))
-    return Q4Weight(n, k, np.ascontiguousarray(packed), absmax.astype(np.float32),
-                    codebook.copy())
+    packed = np.ascontiguousarray((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8))
+    nblk = (n * k) // Q4_BLOCK
+    if dq:
+        acodes = rng.integers(0, 256, size=nblk, dtype=np.uint8)
+        scale = rng.uniform(0.01, 0.03, size=(nblk + 255) // 256).astype(np.float32)
+        return Q4Weight(n, k, packed, None, codebook.copy(), Q4_BLOCK, acodes,
+                        make_absmax_codebook(), scale, 0.04)
+    absmax = np.abs(rng.standard_normal(size=nblk, dtype=np.float32) * np.float32(0.05))
+    return Q4Weight(n, k, packed, absmax.astype(np.float32), codebook.copy())
 
 
 def gen_linear(T, k, n, r, alpha, dtype="bf16", seed=BASE_SEED, b_std=0.02,
@@ -154,7 +186,7 @@ def gen_linear(T, k, n, r, alpha, dtype="bf16", seed=BASE_SEED, b_std=0.02,
     qw = None
     W = None
     if q4:
-        qw = _q4(rw, n, k, make_codebook())
+        qw = _q4(rw, n, k, make_codebook(), dq=(q4 == "dq"))
     else:
         W = _normal(rw, (n, k), w_std, dtype)
     A = _uniform(ra, (r, k), 1.0 / math.sqrt(k), dtype)
@@ -173,7 +205,7 @@ def gen_mlp(T, d, f, r, alpha, dtype="bf16", seed=BASE_SEED, b_std=0.02,
     for i, name in enumerate(("gate", "up", "down")):
         n_out, k_in = shapes[name]
         if q4:
-            Q[name] = _q4(rng[1 + 3 * i], n_out, k_in, cb)
+            Q[name] = _q4(rng[1 + 3 * i], n_out, k_in, cb, dq=(q4 == "dq"))
             W[name] = None
         else:
             W[name] = _normal(rng[1 + 3 * i], (n_out, k_in), w_std, dtype)
@@ -197,11 +229,16 @@ CONFIGS = {
 }
 
 
-def gen_config(cfg: int, seed: Optional[int] = None, b_std=0.02, scale_T=None, part=None):
+def gen_config(cfg: int, seed: Optional[int] = None, b_std=0.02, scale_T=None, part=None,
+               q4=None):
     """Inputs of one benchmark workload.  `scale_T` optionally replaces T
     (same distributions, fewer tokens) for bounded samples.  For workload 4,
-    `part` = "attn" or "mlp" generates only that half."""
+    `part` = "attn" or "mlp" generates only that half.  `q4` (MLP workloads)
+    overrides the base-weight form: False, True (4-bit) or "dq" (4-bit with
+    double-quantised block constants)."""
     c = dict(CONFIGS[cfg])
+    if q4 is not None:
+        c["q4"] = q4
     seed = BASE_SEED + cfg if seed is None else seed
     T = c["T"] if scale_T is None else scale_T
     if c["kind"] == "linear":

@@ -6,7 +6,9 @@ the GPU; loading the library fails loudly when it has not been built.
 
 Entry points mirror the C ABI in include/liblora.h:
   lora_linear_fwd, lora_linear_bwd, lora_swiglu_mlp_fwd, lora_swiglu_mlp_bwd,
-  lora_dequant4, lora_workspace_bytes, lora_strerror, lora_abi_version.
+  lora_dequant4, lora_decode_weight, lora_merge, lora_qkv_fwd, lora_qkv_bwd,
+  lora_workspace_bytes, lora_qkv_workspace_bytes, lora_strerror,
+  lora_abi_version.
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblora.so")
 
 LORA_F32, LORA_BF16 = 0, 1
-LORA_W_DENSE, LORA_W_Q4 = 0, 1
+LORA_W_DENSE, LORA_W_Q4, LORA_W_Q4_DQ = 0, 1, 2
 LORA_FLAG_ACCUMULATE_DX = 1
 OP_LINEAR_FWD, OP_LINEAR_BWD, OP_MLP_FWD, OP_MLP_BWD, OP_QKV_FWD, OP_QKV_BWD = 0, 1, 2, 3, 4, 5
 LORA_WS_MINIMAL = 0x100
@@ -30,7 +32,7 @@ STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
 EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_swiglu_mlp_bwd",
            "lora_dequant4", "lora_workspace_bytes", "lora_strerror", "lora_abi_version",
            "lora_debug_time_next", "lora_merge", "lora_qkv_fwd", "lora_qkv_bwd",
-           "lora_qkv_workspace_bytes"]
+           "lora_qkv_workspace_bytes", "lora_decode_weight"]
 (KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX,
  KC_QKV_FWD, KC_QKV_DX) = range(8)
 
@@ -44,7 +46,10 @@ class LoraError(RuntimeError):
 class LoraWeightC(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("blocksize", ctypes.c_int32),
                 ("w", ctypes.c_void_p), ("codes", ctypes.c_void_p),
-                ("absmax", ctypes.c_void_p), ("codebook", ctypes.c_void_p)]
+                ("absmax", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
+                ("absmax_codes", ctypes.c_void_p), ("absmax_codebook", ctypes.c_void_p),
+                ("absmax_scale", ctypes.c_void_p), ("absmax_offset", ctypes.c_float),
+                ("absmax_blocksize", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,6 +76,7 @@ def lib():
                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.lora_dequant4.argtypes = [i64, i64, vp, vp, vp, i32, i32, vp, vp]
     L.lora_merge.argtypes = [i32, i64, i64, i64, f32, i32, W, vp, vp, vp, vp]
+    L.lora_decode_weight.argtypes = [i64, i64, W, i32, vp, vp]
     L.lora_qkv_fwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W, vp,
                                vp, vp, vp, vp, vp, sz, vp]
     L.lora_qkv_bwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W, vp,
@@ -86,7 +92,7 @@ def lib():
     L.lora_debug_time_next.restype = ctypes.c_int
     for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
                  "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version", "lora_merge",
-                 "lora_qkv_fwd", "lora_qkv_bwd"):
+                 "lora_qkv_fwd", "lora_qkv_bwd", "lora_decode_weight"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -148,13 +154,26 @@ def _dtype_code(t):
 @dataclass
 class Q4Weight:
     """4-bit base weight on the device: codes [n, k/2] uint8, absmax
-    [n*k/64] fp32, codebook [16] fp32 (layout of include/liblora.h)."""
+    [n*k/64] fp32, codebook [16] fp32 (layout of include/liblora.h).
+
+    Double-quantised form (absmax_codes set, absmax None): absmax_codes
+    [n*k/64] uint8, absmax_codebook [256] fp32, absmax_scale
+    [ceil(n*k/64/256)] fp32 and the float absmax_offset."""
     n: int
     k: int
     codes: object
     absmax: object
     codebook: object
     blocksize: int = 64
+    absmax_codes: object = None
+    absmax_codebook: object = None
+    absmax_scale: object = None
+    absmax_offset: float = 0.0
+    absmax_blocksize: int = 256
+
+    @property
+    def double_quant(self) -> bool:
+        return self.absmax_codes is not None
 
     @property
     def shape(self):
@@ -166,13 +185,20 @@ Weight = Union["torch.Tensor", Q4Weight]
 
 def _wstruct(W) -> LoraWeightC:
     if isinstance(W, Q4Weight):
+        if W.double_quant:
+            return LoraWeightC(LORA_W_Q4_DQ, W.blocksize, None, W.codes.data_ptr(), None,
+                               W.codebook.data_ptr(), W.absmax_codes.data_ptr(),
+                               W.absmax_codebook.data_ptr(), W.absmax_scale.data_ptr(),
+                               float(W.absmax_offset), W.absmax_blocksize)
         return LoraWeightC(LORA_W_Q4, W.blocksize, None, W.codes.data_ptr(),
                            W.absmax.data_ptr(), W.codebook.data_ptr())
     return LoraWeightC(LORA_W_DENSE, 0, W.data_ptr(), None, None, None)
 
 
 def _wfmt(W):
-    return LORA_W_Q4 if isinstance(W, Q4Weight) else LORA_W_DENSE
+    if isinstance(W, Q4Weight):
+        return LORA_W_Q4_DQ if W.double_quant else LORA_W_Q4
+    return LORA_W_DENSE
 
 
 _ws_cache: Dict[tuple, object] = {}
@@ -393,10 +419,25 @@ def lora_dequant4(q: Q4Weight, out=None, stream=None):
     return out
 
 
+def lora_decode_weight(q: Q4Weight, out=None, stream=None):
+    """Decode a 4-bit weight of either form (plain or double-quantised
+    block constants) to a bf16 [n, k] tensor."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((q.n, q.k), dtype=torch.bfloat16, device=q.codes.device)
+    wst = _wstruct(q)
+    _check(lib().lora_decode_weight(q.n, q.k, ctypes.byref(wst), LORA_BF16, _ptr(out),
+                                    _stream(stream)), "lora_decode_weight")
+    return out
+
+
 # ------------------------------------------------------ host -> device helpers
 def to_device_q4(qw, device="cuda"):
-    """Upload a host-side lora_inputs.Q4Weight."""
+    """Upload a host-side lora_inputs.Q4Weight (either form)."""
     torch = _torch()
-    return Q4Weight(qw.n, qw.k, torch.from_numpy(qw.codes).to(device),
-                    torch.from_numpy(qw.absmax).to(device),
-                    torch.from_numpy(qw.codebook).to(device), qw.blocksize)
+
+    def up(a):
+        return None if a is None else torch.from_numpy(a).to(device)
+    return Q4Weight(qw.n, qw.k, up(qw.codes), up(qw.absmax), up(qw.codebook), qw.blocksize,
+                    up(qw.absmax_codes), up(qw.absmax_codebook), up(qw.absmax_scale),
+                    float(qw.absmax_offset), qw.absmax_blocksize)

@@ -9,7 +9,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblora.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "gemm_nt.hip", "gemm_nt_q4.hip", "gemm_nn.hip", "gemm_nn_q4.hip"]
+SOURCES = ["api.cpp", "gemm_nt.hip", "gemm_nt_q4.hip", "gemm_nn.hip", "gemm_nn_q4.hip",
+           "gemm_nt_q4dq.hip", "gemm_nn_q4dq.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
          # packed-fp32 VALU forms are kept out of every kernel

@@ -219,10 +219,11 @@ size_t plan_f32(int op, int64_t T, int64_t kd, int64_t nf, int64_t r) {
 
 // ------------------------------------------------------------- validation
 struct WeightView {
-  bool q4;
+  bool q4;                // Q4 or Q4_DQ
+  int fmt;                // lora_wfmt
   const bf16_t *w;
   const uint8_t *codes;
-  const float *absmax;
+  AbsmaxSrc absmax;       // plain or double-quantised block constants
   const float *codebook;
 };
 
@@ -231,17 +232,32 @@ int check_weight(const lora_weight *W, int dtype, int64_t k_in, WeightView &out)
   if (W->fmt == LORA_W_DENSE) {
     if (!W->w) return LORA_ERR_NULL_POINTER;
     if (!aligned16(W->w)) return LORA_ERR_MISALIGNED;
-    out = {false, (const bf16_t *)W->w, nullptr, nullptr, nullptr};
+    out = {false, LORA_W_DENSE, (const bf16_t *)W->w, nullptr, AbsmaxSrc{}, nullptr};
     return LORA_OK;
   }
-  if (W->fmt != LORA_W_Q4) return LORA_ERR_UNSUPPORTED;
+  if (W->fmt != LORA_W_Q4 && W->fmt != LORA_W_Q4_DQ) return LORA_ERR_UNSUPPORTED;
   if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
   if (W->blocksize != 64) return LORA_ERR_UNSUPPORTED;
-  if (!W->codes || !W->absmax || !W->codebook) return LORA_ERR_NULL_POINTER;
+  if (!W->codes || !W->codebook) return LORA_ERR_NULL_POINTER;
   if (k_in % 64) return LORA_ERR_BAD_SHAPE;
-  if (!aligned16(W->codes) || !aligned16(W->absmax) || !aligned16(W->codebook))
-    return LORA_ERR_MISALIGNED;
-  out = {true, nullptr, W->codes, W->absmax, W->codebook};
+  if (!aligned16(W->codes) || !aligned16(W->codebook)) return LORA_ERR_MISALIGNED;
+  AbsmaxSrc am{};
+  if (W->fmt == LORA_W_Q4) {
+    if (!W->absmax) return LORA_ERR_NULL_POINTER;
+    if (!aligned16(W->absmax)) return LORA_ERR_MISALIGNED;
+    am.absmax = W->absmax;
+  } else {
+    if (W->absmax_blocksize != 256) return LORA_ERR_UNSUPPORTED;
+    if (!W->absmax_codes || !W->absmax_codebook || !W->absmax_scale) return LORA_ERR_NULL_POINTER;
+    if (!aligned16(W->absmax_codes) || !aligned16(W->absmax_codebook) ||
+        !aligned16(W->absmax_scale))
+      return LORA_ERR_MISALIGNED;
+    am.codes = W->absmax_codes;
+    am.table = W->absmax_codebook;
+    am.scale = W->absmax_scale;
+    am.offset = W->absmax_offset;
+  }
+  out = {true, W->fmt, nullptr, W->codes, am, W->codebook};
   return LORA_OK;
 }
 
@@ -403,7 +419,9 @@ int transpose_w(bf16_t *out, int64_t ld_out, const WeightView &w, int64_t rows, 
   HIP_TRY(hipGetLastError());
   return LORA_OK;
 }
-inline WeightView dense_view(const bf16_t *p) { return {false, p, nullptr, nullptr, nullptr}; }
+inline WeightView dense_view(const bf16_t *p) {
+  return {false, LORA_W_DENSE, p, nullptr, AbsmaxSrc{}, nullptr};
+}
 
 // workspace check shared by the entry points; `fast` = room for the
 // weight copies
@@ -474,8 +492,12 @@ GemmArgs gemm_base() {
 void set_b(GemmArgs &a, const WeightView &w0, const WeightView &w1) {
   a.B0 = w0.w; a.B1 = w1.w;
   a.Q0 = w0.codes; a.Q1 = w1.codes;
-  a.S0 = w0.absmax; a.S1 = w1.absmax;
-  a.codebook = w0.codebook;
+  a.S0 = w0.absmax.absmax; a.S1 = w1.absmax.absmax;
+  a.CB0 = w0.codebook; a.CB1 = w1.codebook;
+  a.D0 = w0.absmax.codes; a.D1 = w1.absmax.codes;
+  a.DT0 = w0.absmax.table; a.DT1 = w1.absmax.table;
+  a.DS0 = w0.absmax.scale; a.DS1 = w1.absmax.scale;
+  a.doff0 = w0.absmax.offset; a.doff1 = w1.absmax.offset;
 }
 
 struct TimerSlot { hipEvent_t start = nullptr, stop = nullptr; };
@@ -486,8 +508,14 @@ int run_gemm(int kc, bool nn, bool q4, int epi, const GemmArgs &a, hipStream_t s
   g_timer[kc] = TimerSlot{};
   if (ts.start) HIP_TRY(hipEventRecord(ts.start, st));
   hipError_t e;
-  if (!nn) e = q4 ? launch_gemm_nt_q4(epi, a, st) : launch_gemm_nt(epi, a, st);
-  else e = q4 ? launch_gemm_nn_q4(epi, a, st) : launch_gemm_nn(epi, a, st);
+  // 4-bit operands with double-quantised constants carry their 8-bit codes
+  const bool dq = q4 && a.D0 != nullptr;
+  if (!nn)
+    e = !q4 ? launch_gemm_nt(epi, a, st) : dq ? launch_gemm_nt_q4dq(epi, a, st)
+                                              : launch_gemm_nt_q4(epi, a, st);
+  else
+    e = !q4 ? launch_gemm_nn(epi, a, st) : dq ? launch_gemm_nn_q4dq(epi, a, st)
+                                              : launch_gemm_nn_q4(epi, a, st);
   if (e != hipSuccess) return LORA_ERR_HIP;
   if (ts.stop) HIP_TRY(hipEventRecord(ts.stop, st));
   return LORA_OK;
@@ -561,13 +589,13 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, 
   if (op & ~(0xFF | LORA_WS_MINIMAL)) return 0;
   const bool minimal = (op & LORA_WS_MINIMAL) != 0;
   op &= 0xFF;
-  if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4) return 0;
+  if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4 && wfmt != LORA_W_Q4_DQ) return 0;
   if (T < 0 || kd <= 0 || nf <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
   if (dtype == LORA_F32) return plan_f32(op, T, kd, nf, r);
   if (dtype != LORA_BF16) return 0;
   // forwards copy only 4-bit weights (decoded); backwards copy every weight
   // (transposed, decoded if 4-bit)
-  const bool fwd_copy = !minimal && wfmt == LORA_W_Q4, bwd_copy = !minimal;
+  const bool fwd_copy = !minimal && wfmt != LORA_W_DENSE, bwd_copy = !minimal;
   switch (op) {
     case LORA_OP_LINEAR_FWD: return plan_lin_fwd(T, kd, nf, r, fwd_copy).total;
     case LORA_OP_LINEAR_BWD: return plan_lin_bwd(T, kd, nf, r, bwd_copy).total;
@@ -703,7 +731,7 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(check_weight(Wg, dtype, d, wg));
   LORA_TRY(check_weight(Wu, dtype, d, wu));
   LORA_TRY(check_weight(Wd, dtype, f, wd));
-  if (wg.q4 != wu.q4) return LORA_ERR_UNSUPPORTED;
+  if (wg.fmt != wu.fmt) return LORA_ERR_UNSUPPORTED;
   LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd}));
   LORA_TRY(check_tok_ptrs(T, {X, Y, e_saved, g_saved}));
   bool fast;
@@ -793,7 +821,7 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(check_weight(Wg, dtype, d, wg));
   LORA_TRY(check_weight(Wu, dtype, d, wu));
   LORA_TRY(check_weight(Wd, dtype, f, wd));
-  if (wg.q4 != wu.q4) return LORA_ERR_UNSUPPORTED;
+  if (wg.fmt != wu.fmt) return LORA_ERR_UNSUPPORTED;
   LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd, dAg, dBg, dAu, dBu, dAd, dBd}));
   LORA_TRY(check_tok_ptrs(T, {X, e_saved, g_saved, dY}));
   if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
@@ -956,7 +984,7 @@ size_t lora_qkv_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t 
   const bool minimal = (op & LORA_WS_MINIMAL) != 0;
   const int base = op & 0xFF;
   if (base != LORA_OP_QKV_FWD && base != LORA_OP_QKV_BWD) return 0;
-  if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4) return 0;
+  if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4 && wfmt != LORA_W_Q4_DQ) return 0;
   if (T < 0 || k <= 0 || nq <= 0 || nkv <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
   const int lop = base == LORA_OP_QKV_FWD ? LORA_OP_LINEAR_FWD : LORA_OP_LINEAR_BWD;
   const int mflag = minimal ? LORA_WS_MINIMAL : 0;
@@ -967,7 +995,8 @@ size_t lora_qkv_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t 
   if (need == 0 && dtype == LORA_BF16) return 0;
   if (dtype == LORA_BF16 && qkv_rank_ok(r)) {
     if (base == LORA_OP_QKV_FWD)
-      need = std::max(need, plan_qkv_fwd(T, k, nq, nkv, r, !minimal && wfmt == LORA_W_Q4).total);
+      need = std::max(need,
+                      plan_qkv_fwd(T, k, nq, nkv, r, !minimal && wfmt != LORA_W_DENSE).total);
     else if (!minimal)
       need = std::max(need, plan_qkv_bwd(T, k, nq, nkv, r).total);
   }
@@ -985,7 +1014,7 @@ int lora_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64
   LORA_TRY(check_weight(Wq, dtype, k, wq));
   LORA_TRY(check_weight(Wk, dtype, k, wk));
   LORA_TRY(check_weight(Wv, dtype, k, wv));
-  if (wq.q4 != wk.q4 || wq.q4 != wv.q4) return LORA_ERR_UNSUPPORTED;
+  if (wq.fmt != wk.fmt || wq.fmt != wv.fmt) return LORA_ERR_UNSUPPORTED;
   LORA_TRY(check_ptrs({Aq, Bq, Ak, Bk, Av, Bv}));
   LORA_TRY(check_tok_ptrs(T, {X, Q, K, V}));
   const size_t need = lora_qkv_workspace_bytes(LORA_OP_QKV_FWD | LORA_WS_MINIMAL, dtype, Wq->fmt,
@@ -1052,7 +1081,7 @@ int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64
   LORA_TRY(check_weight(Wq, dtype, k, wq));
   LORA_TRY(check_weight(Wk, dtype, k, wk));
   LORA_TRY(check_weight(Wv, dtype, k, wv));
-  if (wq.q4 != wk.q4 || wq.q4 != wv.q4) return LORA_ERR_UNSUPPORTED;
+  if (wq.fmt != wk.fmt || wq.fmt != wv.fmt) return LORA_ERR_UNSUPPORTED;
   LORA_TRY(check_ptrs({Aq, Bq, Ak, Bk, Av, Bv, dAq, dBq, dAk, dBk, dAv, dBv}));
   LORA_TRY(check_tok_ptrs(T, {X, dQ, dK, dV}));
   if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
@@ -1155,10 +1184,24 @@ int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absma
   if (!aligned16(codes) || !aligned16(absmax) || !aligned16(codebook) || !aligned16(out))
     return LORA_ERR_MISALIGNED;
   const int64_t total = n * k;
+  const AbsmaxSrc am{absmax, nullptr, nullptr, nullptr, 0.f};
   hipLaunchKernelGGL(k_dequant4, dim3(blocks_for(total / 32)), dim3(256), 0, (hipStream_t)stream,
-                     codes, absmax, codebook, total, (bf16_t *)out);
+                     codes, am, codebook, total, (bf16_t *)out);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
+}
+
+int lora_decode_weight(int64_t n, int64_t k, const lora_weight *W, int out_dtype, void *out,
+                       void *stream) {
+  if (out_dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (n <= 0 || k <= 0 || n > ((int64_t)1 << 24) || k > ((int64_t)1 << 24))
+    return LORA_ERR_BAD_SHAPE;
+  if (!W) return LORA_ERR_NULL_POINTER;
+  if (W->fmt == LORA_W_DENSE) return LORA_ERR_UNSUPPORTED;
+  WeightView wv;
+  LORA_TRY(check_weight(W, LORA_BF16, k, wv));
+  LORA_TRY(check_ptrs({out}));
+  return decode_w((bf16_t *)out, wv, n, k, (hipStream_t)stream);
 }
 
 }  // extern "C"

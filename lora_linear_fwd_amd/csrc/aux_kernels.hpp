@@ -578,7 +578,7 @@ __global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
 // standalone 4-bit decode: each thread decodes 32 consecutive elements
 // (16 code bytes) and writes 64 bytes of bf16.  HBM-bound.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_dequant4(const uint8_t *codes, const float *absmax,
+__global__ __launch_bounds__(256) void k_dequant4(const uint8_t *codes, const AbsmaxSrc absmax,
                                                   const float *codebook, int64_t total,
                                                   bf16_t *out) {
   __shared__ float2 cbt[256];
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(256) void k_dequant4(const uint8_t *codes, const fl
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 32-element group
   if (g * 32 >= total) return;
   const u32x4 c = gload16(codes + g * 16);
-  const float am = absmax[(g * 32) >> 6];
+  const float am = absmax_at(absmax, (g * 32) >> 6);
   u32x4 o[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w)
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const bf16_t *in, int ro
   for (int j = 0; j < 8; ++j) gstore16(out + (int64_t)(c0 + j) * ld_out + r0, t[j]);
 }
 
-__global__ __launch_bounds__(256) void k_dequant4_t(const uint8_t *codes, const float *absmax,
+__global__ __launch_bounds__(256) void k_dequant4_t(const uint8_t *codes, const AbsmaxSrc absmax,
                                                     const float *codebook, int rows, int cols,
                                                     bf16_t *out, int64_t ld_out, int ncb) {
   __shared__ float2 cbt[256];
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(256) void k_dequant4_t(const uint8_t *codes, const 
   for (int i = 0; i < 8; ++i) {
     const int64_t e0 = (int64_t)(r0 + i) * cols + c0;   // flat element index
     const u32x4 c = gload16(codes + e0 / 2);
-    const float am = absmax[e0 >> 6];
+    const float am = absmax_at(absmax, e0 >> 6);
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
@@ -689,7 +689,8 @@ struct MergeArgs {
   int f32;                     // 1: W, A, B, out are fp32; 0: bf16
   const void *W;               // dense weight (NULL for 4-bit)
   const uint8_t *codes;        // 4-bit weight
-  const float *absmax, *codebook;
+  AbsmaxSrc absmax;
+  const float *codebook;
   const void *A, *B;
   void *out;
 };
@@ -731,7 +732,7 @@ __global__ __launch_bounds__(256) void k_lora_merge(const MergeArgs a) {
       if (a.codes) {   // 4-bit: decode to bf16 (fp32 product, rounded once)
         const uint32_t byte = a.codes[idx >> 1];
         const uint32_t code = (idx & 1) ? (byte >> 4) : (byte & 15u);
-        const uint32_t wb = pack_bf16x2(a.codebook[code] * a.absmax[idx >> 6], 0.f);
+        const uint32_t wb = pack_bf16x2(a.codebook[code] * absmax_at(a.absmax, idx >> 6), 0.f);
         w = bf16lo(wb);
       } else {
         w = ld(a.W, idx);

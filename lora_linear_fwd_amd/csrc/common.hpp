@@ -131,6 +131,29 @@ __device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
   }
 }
 
+// ------------------------------------------------- 4-bit block constants ----
+// Where the per-block absmax of a 4-bit weight comes from: plain fp32
+// (codes == nullptr) or double-quantised, absmax[b] = table[codes[b]] *
+// scale[b / 256] + offset with the product and the sum rounded to fp32
+// separately ("Unsloth deep-dive", 1.4: QLoRA also quantises the
+// quantisation constants).
+struct AbsmaxSrc {
+  const float *absmax;      // plain form
+  const uint8_t *codes;     // double-quantised form (nullptr: plain)
+  const float *table;       // 256 levels
+  const float *scale;       // one per 256 blocks
+  float offset;
+};
+__device__ __forceinline__ float absmax_dq(float level, float scale, float offset) {
+#pragma clang fp contract(off)
+  const float m = level * scale;
+  return m + offset;
+}
+__device__ __forceinline__ float absmax_at(const AbsmaxSrc &s, int64_t b) {
+  if (s.codes == nullptr) return s.absmax[b];
+  return absmax_dq(s.table[s.codes[b]], s.scale[b >> 8], s.offset);
+}
+
 // fast logistic with the hardware exp2 / reciprocal
 __device__ __forceinline__ float sigmoidf_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));

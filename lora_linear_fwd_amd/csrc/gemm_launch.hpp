@@ -40,5 +40,7 @@ hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nt_q4(int epi, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nn(int epi, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nn_q4(int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nt_q4dq(int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nn_q4dq(int epi, const GemmArgs &a, hipStream_t st);
 
 }  // namespace lora

@@ -14,6 +14,9 @@
 //            in natural layout in LDS; MFMA fragments are read with the LDS
 //            transpose read ds_read_b64_tr_b16
 //   B_NN_Q4  4-bit codes of the [K x N] weight, decoded into that layout
+//   B_NT_Q4DQ, B_NN_Q4DQ  the same with double-quantised block constants
+//            (8-bit absmax codes decoded through a 256-level table, a scale
+//            per 256 blocks and an offset: "Unsloth deep-dive", 1.4)
 // The 4-bit decode is bf16_rne(codebook[c] * absmax) with one fp32 multiply
 // ("Unsloth code-reading guide", 2.1: 4-bit weights are decoded to bf16
 // before every matmul; "Why Unsloth trains 5-8x faster", 5.2: decode fused
@@ -54,7 +57,11 @@ constexpr int kBK = LORA_GEMM_BK, kNSTAGE = LORA_GEMM_NSTAGE;
 static_assert(kBK == 32 || kBK == 64, "K step must be 32 or 64");
 static_assert(kNSTAGE >= 2 && kNSTAGE <= 4, "2 to 4 pipeline stages");
 
-enum BMode { B_NT = 0, B_NT_Q4 = 1, B_NN = 2, B_NN_Q4 = 3 };
+enum BMode { B_NT = 0, B_NT_Q4 = 1, B_NN = 2, B_NN_Q4 = 3, B_NT_Q4DQ = 4, B_NN_Q4DQ = 5 };
+constexpr bool bmode_nt_q4(int m) { return m == B_NT_Q4 || m == B_NT_Q4DQ; }
+constexpr bool bmode_nn_q4(int m) { return m == B_NN_Q4 || m == B_NN_Q4DQ; }
+constexpr bool bmode_q4(int m) { return bmode_nt_q4(m) || bmode_nn_q4(m); }
+constexpr bool bmode_dq(int m) { return m == B_NT_Q4DQ || m == B_NN_Q4DQ; }
 enum Epi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
 
 struct GemmArgs {
@@ -65,8 +72,13 @@ struct GemmArgs {
   const bf16_t *B0, *B1;        // dense B_op
   int64_t ldb;                  // NT: row stride (>= K); NN: row stride (>= N)
   const uint8_t *Q0, *Q1;       // 4-bit codes
-  const float *S0, *S1;         // 4-bit absmax
-  const float *codebook;        // 16 fp32 levels
+  const float *S0, *S1;         // 4-bit absmax (plain form)
+  const float *CB0, *CB1;       // 16 fp32 levels of the Q0 / Q1 weight
+  // double-quantised absmax of the Q0 / Q1 weight: 8-bit codes, 256-level
+  // tables, one scale per 256 blocks, offsets
+  const uint8_t *D0, *D1;
+  const float *DT0, *DT1, *DS0, *DS1;
+  float doff0, doff1;
   int gu_f;                     // SwiGLU forward: feature count f (N = 2 f)
   const bf16_t *hglob;          // s * (A_op SIDE^T), [M x rs] bf16
   int rs;                       // rank padded to a multiple of 16
@@ -164,8 +176,12 @@ template <int BMODE>
 struct Stage {  // sized for BK <= 64
   // register-staged 4-bit B operand (the dense forms go straight to LDS)
   u32x4 qc[2];
-  uint32_t qn[(BMODE == B_NN_Q4) ? 8 : 1];
-  float qs[(BMODE == B_NN_Q4) ? 8 : 1];
+  uint32_t qn[bmode_nn_q4(BMODE) ? 8 : 1];
+  float qs[bmode_nn_q4(BMODE) ? 8 : 1];   // absmax, or the 256-block scale (DQ)
+  // NN: bit i = row i comes from the second weight; DQ: bits 8 + i = row i
+  // valid, bytes of q8 = 8-bit absmax codes
+  uint32_t qf;
+  uint32_t q8[bmode_nn_q4(BMODE) ? 2 : 1];
 };
 
 // PF (dense NT form only): each K step also warms L2 for the step PF steps
@@ -174,8 +190,9 @@ template <int BMODE, int EPI, int PF = 0, int BK = kBK, int NSTAGE = kNSTAGE>
 __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
-  constexpr bool Q4 = (BMODE == B_NT_Q4 || BMODE == B_NN_Q4);
-  constexpr bool NN = (BMODE == B_NN || BMODE == B_NN_Q4);
+  constexpr bool Q4 = bmode_q4(BMODE);
+  constexpr bool DQ = bmode_dq(BMODE);
+  constexpr bool NN = (BMODE == B_NN || bmode_nn_q4(BMODE));
   constexpr int XS = BM * BK * 2, WS = BN * BK * 2;
   constexpr int STAGE = XS + WS;
   constexpr int kReads = NN ? 12 : 8;   // LDS reads per 16-K sub-step
@@ -195,11 +212,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K, ksplit = p.ksplit;
 
-  float2 *cbt = reinterpret_cast<float2 *>(smem + NSTAGE * STAGE);   // 4-bit pair table
+  // 4-bit pair tables of the Q0 and Q1 weights, then (DQ) their 256-level
+  // absmax tables
+  float2 *cbt = reinterpret_cast<float2 *>(smem + NSTAGE * STAGE);
+  float *dqt = reinterpret_cast<float *>(smem + NSTAGE * STAGE + 4096);
   if constexpr (Q4) {
     // entry b = (codebook[b & 15], codebook[b >> 4]): a code byte decodes
     // into its two elements with one LDS read
-    cbt[tid] = make_float2(p.codebook[tid & 15], p.codebook[tid >> 4]);
+    cbt[tid] = make_float2(p.CB0[tid & 15], p.CB0[tid >> 4]);
+    cbt[256 + tid] = make_float2(p.CB1[tid & 15], p.CB1[tid >> 4]);
+    if constexpr (DQ) {
+      dqt[tid] = p.DT0[tid];
+      dqt[256 + tid] = p.DT1[tid];
+    }
   }
 
   // ---------------------------------------------------- DMA lane geometry
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
       const int c = (lane & 31) ^ ((row & 3) << 2);
       boff[u] = (n0 + 8 * c < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + c * 16) : kOOB;
     }
-  } else if constexpr (BMODE == B_NT_Q4) {
+  } else if constexpr (bmode_nt_q4(BMODE)) {
     // one weight row per thread; gate rows for waves 0, 2 and up rows for
     // waves 1, 3 when the tile interleaves gate/up
     const int row = tid;
@@ -273,7 +298,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     const bool ok = GU ? (jg < p.gu_f) : (jg < N);
     boff[0] = ok ? (uint32_t)(jl * (K / 2)) : kOOB;       // codes
     boff[1] = ok ? (uint32_t)(jl * (K / 64) * 4) : kOOB;  // absmax
+    if constexpr (DQ) {
+      // flat index of the row's first 64-block in its own weight; -1: the
+      // row lies outside the weight
+      boff[1] = ok ? (uint32_t)((grow0 + jl) * (K / 64)) : 0xFFFFFFFFu;
+    }
   }
+  // NT 4-bit: this thread's tables (gate or up weight)
+  const int tsel = (bmode_nt_q4(BMODE) && GU && ((tid >> 6) & 1)) ? 256 : 0;
   // NN: byte offset of this lane's transpose-read row for n-block i at
   // K sub-step 0 (rows kk*16 + 4t are reached with immediate offsets)
   uint32_t trb[4];
@@ -402,16 +434,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   auto load_q4 = [&](Stage<BMODE> &st, int kt) {
     const int k0 = kt * BK;
     const bool live = kt < nkt;
-    if constexpr (BMODE == B_NT_Q4) {
+    if constexpr (bmode_nt_q4(BMODE)) {
       // BK codes (BK/2 bytes) and the row's absmax of this K step
 #pragma unroll
       for (int h = 0; h < BK / 32; ++h)
         st.qc[h] = bload16(rsB0, live ? boff[0] : kOOB, (uint32_t)k0 / 2 + 16 * h);
-      st.qs[0] = __uint_as_float(bload4(rsB1, live ? boff[1] : kOOB, (uint32_t)(k0 / 64) * 4));
-    } else if constexpr (BMODE == B_NN_Q4) {
+      if constexpr (DQ) {
+        // the block's 8-bit code and its 256-block scale (index 0 stands
+        // in for rows outside the weight; commit zeroes their absmax)
+        const bool ok = live && boff[1] != 0xFFFFFFFFu;
+        const uint32_t b = ok ? boff[1] + (uint32_t)(k0 / 64) : 0u;
+        const bool up = tsel != 0;
+        st.q8[0] = (up ? p.D1 : p.D0)[b];
+        st.qs[0] = (up ? p.DS1 : p.DS0)[b >> 8];
+        st.qf = ok ? 0x100u : 0u;
+      } else {
+        st.qs[0] = __uint_as_float(bload4(rsB1, live ? boff[1] : kOOB, (uint32_t)(k0 / 64) * 4));
+      }
+    } else if constexpr (bmode_nn_q4(BMODE)) {
       // weight rows k0 + (BK/8) kb .., 8 columns gn.. (4 code bytes each)
       const int kb = tid >> 5, nb = tid & 31;
       const int gn = n0 + nb * 8;
+      st.qf = 0u;
+      if constexpr (DQ) st.q8[0] = st.q8[1] = 0u;
 #pragma unroll
       for (int i = 0; i < BK / 8; ++i) {
         const int gk = k0 + kb * (BK / 8) + i;
@@ -419,35 +464,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
         const bool first = gk < ksplit;
         const int64_t wr = first ? gk : gk - ksplit;
         const uint8_t *q = (first ? p.Q0 : p.Q1) + wr * (int64_t)(N / 2) + gn / 2;
-        const float *sc = (first ? p.S0 : p.S1) + ((wr * (int64_t)N + gn) >> 6);
+        const int64_t blk = (wr * (int64_t)N + gn) >> 6;
         const uint32_t cw = *reinterpret_cast<const uint32_t *>(ok ? q : p.Q0);
-        const float am = *(ok ? sc : p.S0);
         st.qn[i] = ok ? cw : 0u;
-        st.qs[i] = ok ? am : 0.f;
+        st.qf |= (first ? 0u : 1u) << i;
+        if constexpr (DQ) {
+          const int64_t b = ok ? blk : 0;
+          const uint32_t c8 = (first ? p.D0 : p.D1)[b];
+          st.qs[i] = (first ? p.DS0 : p.DS1)[b >> 8];
+          st.q8[i >> 2] |= (ok ? c8 : 0u) << (8 * (i & 3));
+          st.qf |= (ok ? 1u : 0u) << (8 + i);
+        } else {
+          const float *sc = (first ? p.S0 : p.S1) + blk;
+          const float am = *(ok ? sc : p.S0);
+          st.qs[i] = ok ? am : 0.f;
+        }
       }
     }
   };
+  // DQ: absmax of a staged block from its 8-bit code and scale (second
+  // weight's tables when `second`); 0 for blocks outside the weight
+  auto dq_absmax = [&](uint32_t c8, float scale, bool second, bool valid) -> float {
+    const float am = absmax_dq(dqt[(second ? 256 : 0) + c8], scale, second ? p.doff1 : p.doff0);
+    return valid ? am : 0.f;
+  };
   // 4 code bytes (8 elements) -> 8 bf16 packed in 4 words
-  auto decode4 = [&](uint32_t cw, float am) -> u32x4 {
+  auto decode4 = [&](uint32_t cw, float am, int tb) -> u32x4 {
     u32x4 o;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float2 cv = cbt[(cw >> (8 * b)) & 0xFFu];
+      const float2 cv = cbt[tb + ((cw >> (8 * b)) & 0xFFu)];
       o[b] = pack_bf16x2(cv.x * am, cv.y * am);
     }
     return o;
   };
   auto commit_q4 = [&](Stage<BMODE> &st, char *stage) {
     char *Ws = stage + XS;
-    if constexpr (BMODE == B_NT_Q4) {
+    if constexpr (bmode_nt_q4(BMODE)) {
+      float am = st.qs[0];
+      if constexpr (DQ) am = dq_absmax(st.q8[0], st.qs[0], tsel != 0, st.qf != 0u);
 #pragma unroll
       for (int c = 0; c < CPR; ++c)
-        lds_write16(Ws, kc_off<BK>(tid, c), decode4(st.qc[c >> 2][c & 3], st.qs[0]));
-    } else if constexpr (BMODE == B_NN_Q4) {
+        lds_write16(Ws, kc_off<BK>(tid, c), decode4(st.qc[c >> 2][c & 3], am, tsel));
+    } else if constexpr (bmode_nn_q4(BMODE)) {
       const int kb = tid >> 5, nb = tid & 31;
 #pragma unroll
-      for (int i = 0; i < BK / 8; ++i)
-        lds_write16(Ws, nn_off(kb * (BK / 8) + i, nb), decode4(st.qn[i], st.qs[i]));
+      for (int i = 0; i < BK / 8; ++i) {
+        const bool second = (st.qf >> i) & 1u;
+        float am = st.qs[i];
+        if constexpr (DQ)
+          am = dq_absmax((st.q8[i >> 2] >> (8 * (i & 3))) & 0xFFu, st.qs[i], second,
+                         (st.qf >> (8 + i)) & 1u);
+        lds_write16(Ws, nn_off(kb * (BK / 8) + i, nb), decode4(st.qn[i], am, second ? 256 : 0));
+      }
     }
   };
 
@@ -758,7 +827,8 @@ constexpr size_t gemm_lds_bytes() {
   // pipeline stages, at least the 4 x 32 KB the output staging uses
   return (NSTAGE * (BM * BK * 2 + BN * BK * 2) > 4 * 32768 ? (size_t)NSTAGE * (BM * BK * 2 + BN * BK * 2)
                                                            : (size_t)4 * 32768) +
-         ((BMODE == B_NT_Q4 || BMODE == B_NN_Q4) ? 256 * sizeof(float2) : 0);
+         (bmode_q4(BMODE) ? 2 * 256 * sizeof(float2) + (bmode_dq(BMODE) ? 2 * 256 * sizeof(float) : 0)
+                          : 0);
 }
 
 }  // namespace lora

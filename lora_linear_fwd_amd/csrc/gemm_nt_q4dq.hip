@@ -1,0 +1,11 @@
+// LoRA GEMM instantiations for the B_NT_Q4DQ operand form (4-bit weight with
+// double-quantised block constants).
+#include "gemm_launch.hpp"
+
+namespace lora {
+hipError_t launch_gemm_nt_q4dq(int epi, const GemmArgs &a, hipStream_t st) {
+  if (epi == EPI_STORE) return launch_gemm_t<B_NT_Q4DQ, EPI_STORE>(a, st);
+  if (epi == EPI_SWIGLU_FWD) return launch_gemm_t<B_NT_Q4DQ, EPI_SWIGLU_FWD>(a, st);
+  return hipErrorInvalidValue;
+}
+}  // namespace lora

@@ -25,7 +25,9 @@ Sources (web pages; sections as printed on them):
 Pins (tests/test_oracle_pins.py): printed trainable-parameter count, B = 0
 invariant, merged-weight invariant, brute-force loops on tiny shapes, central
 finite differences of every gradient, torch.autograd in float64, silu closed
-forms, bf16 rounding against torch, and hand-computed 4-bit decodes.
+forms, bf16 rounding against torch, hand-computed 4-bit decodes, and
+hand-computed double-quantised block constants (including a case where a
+fused multiply-add would round differently) plus a per-element loop.
 """
 from __future__ import annotations
 
@@ -198,6 +200,57 @@ def decode_q4_bits(codes, absmax, codebook, n, k, blocksize=64) -> np.ndarray:
 def decode_q4(codes, absmax, codebook, n, k, blocksize=64) -> np.ndarray:
     """Decoded 4-bit weight as float64 values (exact images of the bf16s)."""
     return bf16_bits_to_f64(decode_q4_bits(codes, absmax, codebook, n, k, blocksize))
+
+
+def decode_absmax_dq(absmax_codes, absmax_codebook, absmax_scale, absmax_offset,
+                     nblocks, blocksize2=256) -> np.ndarray:
+    """First-level block constants of a double-quantised 4-bit weight.
+
+    For block b:  level = absmax_codebook[absmax_codes[b]];
+    m = level * absmax_scale[b // blocksize2] (one IEEE float32 multiply,
+    round to nearest even); absmax[b] = m + absmax_offset (one float32
+    add, round to nearest even).  Returns float32 [nblocks].
+    ([DD] 1.4 double quantisation: the quantisation constants are
+    themselves quantised.  The page gives no parameters; the 8-bit codes
+    through a 256-level table, one float32 scale per 256 blocks and one
+    float32 offset are this implementation's reading.)
+    """
+    if blocksize2 != 256:
+        raise ValueError("unsupported second-level block size")
+    c8 = np.asarray(absmax_codes, dtype=np.uint8).reshape(-1)[:nblocks]
+    if c8.size != nblocks:
+        raise ValueError("too few 8-bit codes")
+    table = np.asarray(absmax_codebook, dtype=np.float32).reshape(-1)
+    if table.size != 256:
+        raise ValueError("the 8-bit table has 256 levels")
+    sc = np.asarray(absmax_scale, dtype=np.float32).reshape(-1)
+    group = np.arange(nblocks) // blocksize2
+    if sc.size <= int(group.max(initial=-1)):
+        raise ValueError("too few second-level scales")
+    m = table[c8] * sc[group]                         # float32 * float32 -> float32
+    return (m + np.float32(absmax_offset)).astype(np.float32)   # float32 + float32
+
+
+def decode_q4dq_bits(codes, absmax_codes, absmax_codebook, absmax_scale, absmax_offset,
+                     codebook, n, k, blocksize=64, blocksize2=256) -> np.ndarray:
+    """Decode a 4-bit weight whose block constants are double-quantised:
+    the constants first (decode_absmax_dq), then the plain 4-bit decode."""
+    if blocksize != 64 or (n * k) % blocksize:
+        raise ValueError("unsupported 4-bit layout")
+    am = decode_absmax_dq(absmax_codes, absmax_codebook, absmax_scale, absmax_offset,
+                          (n * k) // blocksize, blocksize2)
+    return decode_q4_bits(codes, am, codebook, n, k, blocksize)
+
+
+def decode_q4_weight(q) -> np.ndarray:
+    """Float64 values of a 4-bit weight container with fields codes,
+    codebook, n, k and either absmax or the double-quantised constants."""
+    if getattr(q, "absmax_codes", None) is not None:
+        bits = decode_q4dq_bits(q.codes, q.absmax_codes, q.absmax_codebook, q.absmax_scale,
+                                q.absmax_offset, q.codebook, q.n, q.k, q.blocksize,
+                                q.absmax_blocksize)
+        return bf16_bits_to_f64(bits)
+    return decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k, q.blocksize)
 
 
 # ---------------------------------------------------------------------------

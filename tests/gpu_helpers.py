@@ -46,7 +46,7 @@ def linear_weight(li):
     if li.q4 is not None:
         q = li.q4
         Wd = L.to_device_q4(q)
-        Wref = oracle.decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k)
+        Wref = oracle.decode_q4_weight(q)
         return Wd, Wref
     return dev(li.W, li.dtype), li.W
 
@@ -57,7 +57,7 @@ def mlp_weights(mi):
         if mi.q4:
             q = mi.q4[p]
             Wd[p] = L.to_device_q4(q)
-            Wref[p] = oracle.decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k)
+            Wref[p] = oracle.decode_q4_weight(q)
         else:
             Wd[p] = dev(mi.W[p], mi.dtype)
             Wref[p] = mi.W[p]

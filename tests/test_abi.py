@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
                  "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_workspace_bytes",
-                 "lora_strerror", "lora_abi_version"):
+                 "lora_strerror", "lora_abi_version", "lora_decode_weight", "lora_merge"):
         assert name in fns
     assert set(fns) == set(L.EXPORTS)
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
     assert L.strerror(0) == "ok"
     for s in range(1, 7):
         assert L.strerror(s) and L.strerror(s) != "unknown status"
@@ -62,6 +62,29 @@ def test_workspace_bytes_rules():
     assert wb(L.OP_LINEAR_BWD, L.LORA_F32, 0, 256, 512, 512, 8) == 2 * 256 * 8 * 4
     assert wb(L.OP_MLP_FWD | 0x200, L.LORA_BF16, 0, 8192, 4096, 14336, 16) == 0
     assert wb(L.OP_MLP_FWD, L.LORA_BF16, 5, 8192, 4096, 14336, 16) == 0
+    # the double-quantised 4-bit form needs what the plain 4-bit form needs
+    for op in (L.OP_LINEAR_FWD, L.OP_LINEAR_BWD, L.OP_MLP_FWD, L.OP_MLP_BWD):
+        for m in (0, L.LORA_WS_MINIMAL):
+            assert (wb(op | m, L.LORA_BF16, 2, 8192, 4096, 14336, 16)
+                    == wb(op | m, L.LORA_BF16, 1, 8192, 4096, 14336, 16) > 0)
+
+
+def test_weight_struct_layout_matches_header():
+    """ctypes' lora_weight has the C struct's size and field offsets."""
+    import tempfile
+    fields = [f[0] for f in L.LoraWeightC._fields_]
+    src = "#include <stddef.h>\n#include <stdio.h>\n#include \"liblora.h\"\nint main(void){"
+    src += 'printf("%zu", sizeof(lora_weight));'
+    src += "".join(f'printf(" %zu", offsetof(lora_weight, {f}));' for f in fields)
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(L.LoraWeightC)
+    assert got[1:] == [getattr(L.LoraWeightC, f).offset for f in fields]
 
 
 def test_workspace_strategies():
@@ -98,6 +121,11 @@ def _w(fmt=0, blocksize=0, w=P, codes=None, absmax=None, codebook=None):
     return L.LoraWeightC(fmt, blocksize, w, codes, absmax, codebook)
 
 
+def _wdq(codes=P, codebook=P, acodes=P, atable=P, ascale=P, abs2=256, blocksize=64):
+    return L.LoraWeightC(2, blocksize, None, codes, None, codebook, acodes, atable, ascale, 0.04,
+                         abs2)
+
+
 def fwd(dtype=1, T=16, k=64, n=64, r=8, X=P, W=None, A=P, B=P, Y=P, ws=P, wsb=1 << 30):
     W = W or _w()
     return L.lib().lora_linear_fwd(dtype, T, k, n, r, 16.0, X, ctypes.byref(W), A, B, Y, ws,
@@ -125,6 +153,17 @@ def test_linear_fwd_validation_codes():
     assert fwd(k=72, W=q4) == 2
     assert fwd(W=_w(1, 64, None, P, None, P)) == 1
     assert fwd(W=_w(7)) == 3
+    # double-quantised constants: bf16, second-level block 256, every pointer
+    assert fwd(dtype=0, W=_wdq()) == 3
+    assert fwd(W=_wdq(abs2=128)) == 3
+    assert fwd(W=_wdq(blocksize=32)) == 3
+    assert fwd(W=_wdq(acodes=None)) == 1
+    assert fwd(W=_wdq(atable=None)) == 1
+    assert fwd(W=_wdq(ascale=None)) == 1
+    assert fwd(W=_wdq(codebook=None)) == 1
+    assert fwd(W=_wdq(ascale=P_MIS)) == 5
+    assert fwd(W=_wdq(acodes=P_MIS)) == 5
+    assert fwd(k=72, W=_wdq()) == 2
 
 
 def test_linear_bwd_validation_codes():
@@ -152,6 +191,26 @@ def test_mlp_validation_codes():
     mixed = [1, 16, 64, 128, 8, 16.0, P, ctypes.byref(q4), P, P, ctypes.byref(W), P, P,
              ctypes.byref(W), P, P]
     assert lib.lora_swiglu_mlp_fwd(*mixed, P, P, P, P, 1 << 30, None) == 3
+    # gate and up share one format (the fused gate/up GEMM reads both alike)
+    dq = _wdq()
+    mixed = [1, 16, 64, 128, 8, 16.0, P, ctypes.byref(q4), P, P, ctypes.byref(dq), P, P,
+             ctypes.byref(dq), P, P]
+    assert lib.lora_swiglu_mlp_fwd(*mixed, P, P, P, P, 1 << 30, None) == 3
+
+
+def test_decode_weight_validation_codes():
+    lib = L.lib()
+    dq, q4 = _wdq(), _w(1, 64, None, P, P, P)
+    call = lambda W, n=16, k=128, dt=1, out=P: lib.lora_decode_weight(n, k, ctypes.byref(W), dt,
+                                                                      out, None)
+    assert call(_w()) == 3                 # dense weights have nothing to decode
+    assert call(dq, out=None) == 1
+    assert call(q4, dt=0) == 3
+    assert call(dq, k=100) == 2
+    assert call(dq, n=0) == 2
+    assert call(_wdq(abs2=64)) == 3
+    assert call(q4, out=P_MIS) == 5
+    assert lib.lora_decode_weight(16, 128, None, 1, P, None) == 1
 
 
 def test_dequant4_validation_codes():

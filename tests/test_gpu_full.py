@@ -24,18 +24,18 @@ def sample_rows(T, n=40, seed=0):
     return rows
 
 
-def run_full_mlp(cfg):
+def run_full_mlp(cfg, q4=None, minimal=False):
     import torch
-    log(f"config {cfg}: generating inputs")
-    mi = gen_config(cfg)
+    log(f"config {cfg} (4-bit form {q4}, minimal workspace {minimal}): generating inputs")
+    mi = gen_config(cfg, q4=q4)
     s = oracle.scaling(mi.alpha, mi.r)
     Wd, Wref = mlp_weights(mi)
     X, dY = dev(mi.X, "bf16"), dev(mi.dY, "bf16")
     A = {p: dev(mi.A[p], "bf16") for p in mi.A}
     B = {p: dev(mi.B[p], "bf16") for p in mi.B}
     log(f"config {cfg}: GPU fwd+bwd T={mi.T} d={mi.d} f={mi.f} r={mi.r}")
-    Y, e, g = L.lora_swiglu_mlp_fwd(X, Wd, A, B, mi.alpha)
-    grads = L.lora_swiglu_mlp_bwd(X, Wd, A, B, mi.alpha, e, g, dY)
+    Y, e, g = L.lora_swiglu_mlp_fwd(X, Wd, A, B, mi.alpha, minimal_workspace=minimal)
+    grads = L.lora_swiglu_mlp_bwd(X, Wd, A, B, mi.alpha, e, g, dY, minimal_workspace=minimal)
     torch.cuda.synchronize()
     rows = sample_rows(mi.T, seed=cfg)
     rt = torch.from_numpy(rows).to("cuda")
@@ -56,6 +56,13 @@ def run_full_mlp(cfg):
 @pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_full_mlp(cfg):
     run_full_mlp(cfg)
+
+
+@pytest.mark.parametrize("minimal", [False, True], ids=["fast", "minimal"])
+def test_full_mlp_double_quantised(minimal):
+    """The 4-bit 8B MLP with double-quantised block constants (minimal
+    workspace: decoded inside the GEMMs)."""
+    run_full_mlp(5, q4="dq", minimal=minimal)
 
 
 def test_full_config4_attention_projections():
@@ -130,6 +137,20 @@ def test_full_dequant4_8b_weight():
     torch.cuda.synchronize()
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
     ref = oracle.decode_q4_bits(q.codes, q.absmax, q.codebook, q.n, q.k)
+    assert np.array_equal(got, ref)
+
+
+def test_full_decode_dq_8b_weight():
+    """Decode of one 8B-MLP weight [14336 x 4096] with double-quantised
+    block constants, bit-exact."""
+    import torch
+    mi = gen_config(5, q4="dq")
+    q = mi.q4["down"]
+    out = L.lora_decode_weight(L.to_device_q4(q))
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.decode_q4dq_bits(q.codes, q.absmax_codes, q.absmax_codebook, q.absmax_scale,
+                                  q.absmax_offset, q.codebook, q.n, q.k)
     assert np.array_equal(got, ref)
 
 

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 
 import oracle
-from lora_inputs import bf16_bits_of, gen_linear, gen_mlp, to_bf16_values
+from lora_inputs import (bf16_bits_of, gen_linear, gen_mlp, make_absmax_codebook, make_codebook,
+                         to_bf16_values)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 rng = np.random.default_rng(12345)
@@ -290,3 +291,98 @@ def test_config_inputs_roundtrip_through_oracle_shapes():
     mi = gen_mlp(8, 64, 128, 4, 16.0, "bf16")
     Y, e, g = oracle.mlp_fwd(mi.X, mi.W, mi.A, mi.B, 4.0)
     assert Y.shape == (8, 64) and e.shape == (8, 128)
+
+
+# ------------------------------------------- double-quantised block constants
+def _f32(v):
+    return np.float32(v)
+
+
+def test_absmax_dq_hand_fixture():
+    # levels, scales and offset chosen so that every value is worked out by hand
+    table = np.zeros(256, np.float32)
+    table[0], table[255], table[128], table[7] = -1.0, 1.0, 0.5, 0.125
+    scale = np.array([0.25, 2.0], np.float32)
+    codes8 = np.full(300, 7, np.uint8)            # 0.125 everywhere else
+    codes8[[0, 1, 255, 256, 299]] = [255, 0, 128, 128, 0]
+    am = oracle.decode_absmax_dq(codes8, table, scale, 0.5, 300)
+    assert am.dtype == np.float32 and am.shape == (300,)
+    assert am[0] == 0.75          # 1 * 0.25 + 0.5
+    assert am[1] == 0.25          # -1 * 0.25 + 0.5
+    assert am[2] == 0.53125       # 0.125 * 0.25 + 0.5
+    assert am[255] == 0.625       # last block of the first 256-group: scale[0]
+    assert am[256] == 1.5         # first block of the second group: scale[1]
+    assert am[257] == 0.75        # 0.125 * 2 + 0.5
+    assert am[299] == -1.5        # -1 * 2 + 0.5
+    with pytest.raises(ValueError):
+        oracle.decode_absmax_dq(codes8, table, scale[:1], 0.5, 300)   # group 1 has no scale
+
+
+def test_absmax_dq_rounds_product_then_sum():
+    # (1+2^-12)^2 = 1 + 2^-11 + 2^-24: the float32 product rounds the 2^-24
+    # tie to even (1 + 2^-11); adding -1 then gives exactly 2^-11.  A fused
+    # multiply-add would keep the 2^-24 and give 2^-11 + 2^-24.
+    t = np.zeros(256, np.float32)
+    t[9] = 1 + 2**-12
+    am = oracle.decode_absmax_dq(np.array([9], np.uint8), t, np.array([1 + 2**-12], np.float32),
+                                 -1.0, 1)
+    assert am[0] == _f32(2**-11)
+    assert am[0] != _f32(2**-11 + 2**-24)
+    # the sum rounds too: 1 + 2^-24 is a tie -> 1.0 (even); 1 + 3*2^-24 is a
+    # tie between 1 + 2^-23 (odd) and 1 + 2^-22 (even) -> 1 + 2^-22
+    t[9] = 1.0
+    one = np.array([1.0], np.float32)
+    assert oracle.decode_absmax_dq(np.array([9], np.uint8), t, one, 2**-24, 1)[0] == 1.0
+    assert oracle.decode_absmax_dq(np.array([9], np.uint8), t, one, 3 * 2**-24, 1)[0] == \
+        _f32(1 + 2**-22)
+
+
+def test_q4dq_decode_is_q4_decode_with_the_constants():
+    # the hand-fixture constants above, written out, drive the plain decode
+    table = np.zeros(256, np.float32)
+    table[0], table[255], table[128], table[7] = -1.0, 1.0, 0.5, 0.125
+    scale = np.array([0.25, 2.0], np.float32)
+    n, k = 4, 64 * 75                              # 300 blocks
+    codes8 = np.full(300, 7, np.uint8)
+    codes8[[0, 1, 255, 256, 299]] = [255, 0, 128, 128, 0]
+    am = np.full(300, 0.53125, np.float32)
+    am[256:] = 0.75
+    am[[0, 1, 255, 256, 299]] = [0.75, 0.25, 0.625, 1.5, -1.5]
+    g = np.random.default_rng(5)
+    codes = g.integers(0, 16, size=(n, k), dtype=np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    cb = make_codebook()
+    got = oracle.decode_q4dq_bits(packed, codes8, table, scale, 0.5, cb, n, k)
+    assert np.array_equal(got, oracle.decode_q4_bits(packed, am, cb, n, k))
+
+
+def test_absmax_dq_elementwise_loop():
+    # per-element loop: the product of two float32 is exact in a Python
+    # float; np.float32() rounds it to nearest even; with every term within
+    # 2^-16 .. 1 the float sum is exact again before its own rounding
+    g = np.random.default_rng(11)
+    nblk = 700
+    c8 = g.integers(0, 256, size=nblk, dtype=np.uint8)
+    table = make_absmax_codebook()
+    scale = g.uniform(0.01, 0.03, size=3).astype(np.float32)
+    off = np.float32(0.04)
+    want = np.empty(nblk, np.float32)
+    for b in range(nblk):
+        m = np.float32(float(table[int(c8[b])]) * float(scale[b // 256]))
+        want[b] = np.float32(float(m) + float(off))
+    got = oracle.decode_absmax_dq(c8, table, scale, off, nblk)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert (got > 0).all()
+
+
+def test_generated_dq_weight_layout():
+    li = gen_linear(4, 128, 72, 4, 16.0, "bf16", seed=3, q4="dq")
+    q = li.q4
+    assert q.absmax is None and q.double_quant
+    nblk = 72 * 128 // 64
+    assert q.absmax_codes.shape == (nblk,) and q.absmax_codes.dtype == np.uint8
+    assert q.absmax_scale.shape == ((nblk + 255) // 256,)
+    assert q.absmax_codebook.shape == (256,) and q.absmax_blocksize == 256
+    W = oracle.decode_q4_weight(q)
+    assert W.shape == (72, 128) and np.isfinite(W).all()
+    assert np.abs(W).max() <= 0.07
