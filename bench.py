@@ -39,6 +39,10 @@ def parse():
                     help="2, 3, 5: LoRA-SwiGLU MLP; 4: q/k/v/o LoRA projections + MLP")
     ap.add_argument("--qkv-separate", action="store_true",
                     help="config 4: run q, k, v as three LoRA linears instead of the fused call")
+    ap.add_argument("--dq", action="store_true",
+                    help="workload 5 with double-quantised 4-bit block constants")
+    ap.add_argument("--minimal-ws", action="store_true",
+                    help="minimal workspace (no weight copies; 4-bit decoded inside the GEMMs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle baseline runs on")
@@ -297,9 +301,13 @@ def main():
     c = CONFIGS[args.config]
     T, d, f, r, alpha = c["T"], c["d"], c["f"], c["r"], c["alpha"]
     q4 = c.get("q4", False)
+    if args.dq and not q4:
+        print("--dq needs a 4-bit workload (--config 5)", file=sys.stderr)
+        sys.exit(2)
+    wfmt = (2 if args.dq else 1) if q4 else 0
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    mi = gen_config(args.config)
+    mi = gen_config(args.config, q4=("dq" if args.dq else None))
     up = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
     if q4:
         W = {p: L.to_device_q4(mi.q4[p]) for p in mi.q4}
@@ -315,8 +323,9 @@ def main():
     for p in ("gate", "up", "down"):
         out["dA_" + p] = torch.empty_like(A[p])
         out["dB_" + p] = torch.empty_like(B[p])
-    ws_bytes = max(L.workspace_bytes(L.OP_MLP_FWD, L.LORA_BF16, int(q4), T, d, f, r),
-                   L.workspace_bytes(L.OP_MLP_BWD, L.LORA_BF16, int(q4), T, d, f, r))
+    mflag = L.LORA_WS_MINIMAL if args.minimal_ws else 0
+    ws_bytes = max(L.workspace_bytes(L.OP_MLP_FWD | mflag, L.LORA_BF16, wfmt, T, d, f, r),
+                   L.workspace_bytes(L.OP_MLP_BWD | mflag, L.LORA_BF16, wfmt, T, d, f, r))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -372,9 +381,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"LoRA-SwiGLU MLP fwd+bwd, T={T} (4x2048), d={d}, f={f}, "
-                               f"r={r}, alpha={alpha:g}, {'4-bit' if q4 else 'bf16'} base "
-                               f"weights, bf16 adapters",
-                   "config_id": args.config, "T": T, "d": d, "f": f, "r": r},
+                               f"r={r}, alpha={alpha:g}, "
+                               f"{('4-bit (double-quantised constants)' if args.dq else '4-bit') if q4 else 'bf16'} "
+                               f"base weights, bf16 adapters",
+                   "config_id": args.config, "T": T, "d": d, "f": f, "r": r,
+                   "workspace": "minimal" if args.minimal_ws else "fast"},
         "wall_s_timed": round(wall, 3),
         "kernels_ms": {names[kc]: round(kms[kc], 4) for kc in kcs},
         "roofline": {"bound": "mfma", "kernel": names[dom], "achieved": round(dom_tflops, 2),

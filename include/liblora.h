@@ -12,11 +12,15 @@
  *   [WHY] "Why Unsloth trains 5-8x faster" (mokono.cn/news/868259) --
  *         3.1/3.2 the rank-r product x A^T stays on chip inside one fused
  *         kernel; 5.2 4-bit dequantisation fused into the matmul.
+ *   [SPD] "Unsloth speed secret: Triton kernels accelerate backprop"
+ *         (mokono.cn/news/201055) -- 3.2 RMSNorm kernel: per-row mean of
+ *         squares, reciprocal root saved for the backward, times weight.
  *   [CR]  "Unsloth code-reading guide" (ai-reference-codex.pages.dev/
  *         frontier/unsloth) -- 2.1 4-bit weights decoded to bf16 every
  *         step; 2.3 mlp.forward := LoRA SwiGLU MLP with a manual backward;
  *         4 the MLP saves only X, e (gate output) and g (up output);
- *         5 the fast path exists only for dropout 0, no bias, no DoRA.
+ *         5 the fast path exists only for dropout 0, no bias, no DoRA;
+ *         highlights: RMSNorm statistics in fp32, cast back at the end.
  *
  * Notation: T tokens, k in_features, n out_features, r rank, s = alpha/r
  * computed in fp32.  Row-major, contiguous tensors:
@@ -217,6 +221,30 @@ int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absma
  */
 int lora_decode_weight(int64_t n, int64_t k, const lora_weight *W, int out_dtype, void *out,
                        void *stream);
+
+/*
+ * RMSNorm over the rows of X [T x d], the step in front of the gate/up and
+ * q/k/v projections ([SPD] 3.2; statistics in fp32 and one cast at the end
+ * per [CR] highlights):
+ *   rstd[t] = 1 / sqrt(sum_j X[t,j]^2 / d + eps)       (fp32, [T])
+ *   Y[t,j]  = X[t,j] * rstd[t] * w[j]                  (fp32, rounded once)
+ * X, Y [T x d] and w [d] in `dtype`; Y may not alias X.  rstd is saved for
+ * lora_rmsnorm_bwd.  eps must be finite and >= 0 (LORA_ERR_UNSUPPORTED).
+ * Sums run in a fixed order: bitwise reproducible.  No workspace.
+ */
+int lora_rmsnorm_fwd(int dtype, int64_t T, int64_t d, float eps, const void *X, const void *w,
+                     void *Y, float *rstd, void *stream);
+
+/*
+ * Input gradient of lora_rmsnorm_fwd for upstream dY [T x d] (w frozen, so
+ * there is no dw):  g = dY * w,
+ *   dX[t,i] = rstd g_i - rstd^3 X[t,i] (sum_j g_j X[t,j]) / d   (fp32).
+ * With LORA_FLAG_ACCUMULATE_DX the result is added to dX (the residual
+ * branch's gradient), rounded once.  X, w, rstd as in the forward.
+ */
+int lora_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void *X, const void *w,
+                     const float *rstd, const void *dY, void *dX, uint32_t flags,
+                     void *stream);
 
 /*
  * Fused q/k/v LoRA projections of one input (the LoRA_QKV pattern of

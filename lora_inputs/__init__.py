@@ -215,6 +215,28 @@ def gen_mlp(T, d, f, r, alpha, dtype="bf16", seed=BASE_SEED, b_std=0.02,
     return MLPInputs(dtype, T, d, f, r, float(alpha), X, W, A, B, dY, Q)
 
 
+@dataclass
+class RMSNormInputs:
+    dtype: str
+    T: int
+    d: int
+    eps: float
+    X: np.ndarray              # [T, d] the residual stream in front of the norm
+    w: np.ndarray              # [d] norm weight
+    dY: np.ndarray             # [T, d] upstream gradient of the normalised rows
+
+
+def gen_rmsnorm(T, d, dtype="bf16", seed=BASE_SEED, eps=1e-5, x_std=1.0) -> RMSNormInputs:
+    """X ~ N(0, x_std^2), w ~ 1 + N(0, 0.1^2) (a trained norm weight near its
+    initial value 1), dY ~ N(0, 1); eps 1e-5."""
+    rx, rw, rdy = _rngs(seed, 3)
+    X = _normal(rx, (T, d), x_std, dtype)
+    w = rw.standard_normal(size=d, dtype=np.float32) * np.float32(0.1) + np.float32(1.0)
+    w = to_bf16_values(w) if dtype == "bf16" else w.astype(np.float32)
+    dY = _normal(rdy, (T, d), 1.0, dtype)
+    return RMSNormInputs(dtype, T, d, float(eps), X, w, dY)
+
+
 # --------------------------------------------------------------------------
 # the five benchmark workloads
 # --------------------------------------------------------------------------

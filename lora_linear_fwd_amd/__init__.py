@@ -7,6 +7,7 @@ the GPU; loading the library fails loudly when it has not been built.
 Entry points mirror the C ABI in include/liblora.h:
   lora_linear_fwd, lora_linear_bwd, lora_swiglu_mlp_fwd, lora_swiglu_mlp_bwd,
   lora_dequant4, lora_decode_weight, lora_merge, lora_qkv_fwd, lora_qkv_bwd,
+  lora_rmsnorm_fwd, lora_rmsnorm_bwd,
   lora_workspace_bytes, lora_qkv_workspace_bytes, lora_strerror,
   lora_abi_version.
 """
@@ -32,7 +33,8 @@ STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
 EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_swiglu_mlp_bwd",
            "lora_dequant4", "lora_workspace_bytes", "lora_strerror", "lora_abi_version",
            "lora_debug_time_next", "lora_merge", "lora_qkv_fwd", "lora_qkv_bwd",
-           "lora_qkv_workspace_bytes", "lora_decode_weight"]
+           "lora_qkv_workspace_bytes", "lora_decode_weight", "lora_rmsnorm_fwd",
+           "lora_rmsnorm_bwd"]
 (KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX,
  KC_QKV_FWD, KC_QKV_DX) = range(8)
 
@@ -77,6 +79,8 @@ def lib():
     L.lora_dequant4.argtypes = [i64, i64, vp, vp, vp, i32, i32, vp, vp]
     L.lora_merge.argtypes = [i32, i64, i64, i64, f32, i32, W, vp, vp, vp, vp]
     L.lora_decode_weight.argtypes = [i64, i64, W, i32, vp, vp]
+    L.lora_rmsnorm_fwd.argtypes = [i32, i64, i64, f32, vp, vp, vp, vp, vp]
+    L.lora_rmsnorm_bwd.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, u32, vp]
     L.lora_qkv_fwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W, vp,
                                vp, vp, vp, vp, vp, sz, vp]
     L.lora_qkv_bwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W, vp,
@@ -92,7 +96,8 @@ def lib():
     L.lora_debug_time_next.restype = ctypes.c_int
     for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
                  "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version", "lora_merge",
-                 "lora_qkv_fwd", "lora_qkv_bwd", "lora_decode_weight"):
+                 "lora_qkv_fwd", "lora_qkv_bwd", "lora_decode_weight", "lora_rmsnorm_fwd",
+                 "lora_rmsnorm_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -417,6 +422,35 @@ def lora_dequant4(q: Q4Weight, out=None, stream=None):
                                q.blocksize, LORA_BF16, _ptr(out), _stream(stream)),
            "lora_dequant4")
     return out
+
+
+def lora_rmsnorm_fwd(X, w, eps: float, Y=None, rstd=None, stream=None):
+    """RMSNorm of the rows of X: returns (Y, rstd) with rstd [T] fp32."""
+    torch = _torch()
+    T, d = X.shape
+    dt = _dtype_code(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    if rstd is None:
+        rstd = torch.empty((T,), dtype=torch.float32, device=X.device)
+    _check(lib().lora_rmsnorm_fwd(dt, T, d, float(eps), _ptr(X), _ptr(w), _ptr(Y), _ptr(rstd),
+                                  _stream(stream)), "lora_rmsnorm_fwd")
+    return Y, rstd
+
+
+def lora_rmsnorm_bwd(X, w, rstd, dY, dX=None, accumulate=False, stream=None):
+    """Input gradient of lora_rmsnorm_fwd (added to dX when accumulate)."""
+    torch = _torch()
+    T, d = X.shape
+    dt = _dtype_code(X)
+    if dX is None:
+        if accumulate:
+            raise ValueError("accumulate needs dX")
+        dX = torch.empty_like(X)
+    flags = LORA_FLAG_ACCUMULATE_DX if accumulate else 0
+    _check(lib().lora_rmsnorm_bwd(dt, T, d, _ptr(X), _ptr(w), _ptr(rstd), _ptr(dY), _ptr(dX),
+                                  flags, _stream(stream)), "lora_rmsnorm_bwd")
+    return dX
 
 
 def lora_decode_weight(q: Q4Weight, out=None, stream=None):

@@ -5,10 +5,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 
 #include "aux_kernels.hpp"
 #include "gemm_launch.hpp"
+#include "norm_kernels.hpp"
 
 using namespace lora;
 
@@ -1187,6 +1189,47 @@ int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absma
   const AbsmaxSrc am{absmax, nullptr, nullptr, nullptr, 0.f};
   hipLaunchKernelGGL(k_dequant4, dim3(blocks_for(total / 32)), dim3(256), 0, (hipStream_t)stream,
                      codes, am, codebook, total, (bf16_t *)out);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+int lora_rmsnorm_fwd(int dtype, int64_t T, int64_t d, float eps, const void *X, const void *w,
+                     void *Y, float *rstd, void *stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return LORA_ERR_UNSUPPORTED;
+  if (T < 0 || d <= 0 || T > (int64_t)1 << 30 || d > (int64_t)1 << 24) return LORA_ERR_BAD_SHAPE;
+  if (dtype == LORA_BF16 && (d % 8)) return LORA_ERR_BAD_SHAPE;
+  LORA_TRY(check_ptrs({w}));
+  LORA_TRY(check_tok_ptrs(T, {X, Y, rstd}));
+  if (T == 0) return LORA_OK;
+  const unsigned grid = (unsigned)cdiv(T, 4);
+  if (dtype == LORA_F32)
+    hipLaunchKernelGGL(k_rmsnorm_fwd<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, X, w,
+                       eps, (int)T, (int)d, Y, rstd);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_fwd<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, X, w,
+                       eps, (int)T, (int)d, Y, rstd);
+  HIP_TRY(hipGetLastError());
+  return LORA_OK;
+}
+
+int lora_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void *X, const void *w,
+                     const float *rstd, const void *dY, void *dX, uint32_t flags, void *stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (flags & ~LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
+  if (T < 0 || d <= 0 || T > (int64_t)1 << 30 || d > (int64_t)1 << 24) return LORA_ERR_BAD_SHAPE;
+  if (dtype == LORA_BF16 && (d % 8)) return LORA_ERR_BAD_SHAPE;
+  LORA_TRY(check_ptrs({w}));
+  LORA_TRY(check_tok_ptrs(T, {X, rstd, dY, dX}));
+  if (T == 0) return LORA_OK;
+  const unsigned grid = (unsigned)cdiv(T, 4);
+  const int acc = (flags & LORA_FLAG_ACCUMULATE_DX) ? 1 : 0;
+  if (dtype == LORA_F32)
+    hipLaunchKernelGGL(k_rmsnorm_bwd<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, X, w,
+                       rstd, dY, (int)T, (int)d, dX, acc);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_bwd<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, X, w,
+                       rstd, dY, (int)T, (int)d, dX, acc);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
 }

@@ -1,0 +1,145 @@
+// RMSNorm forward / backward over the rows of a [T x d] activation, the step
+// in front of the gate/up and q/k/v projections ("Unsloth speed secret:
+// Triton kernels accelerate backprop", 3.2: per-row mean of squares, the
+// reciprocal root kept for the backward, normalised row times the weight;
+// "Unsloth code-reading guide", highlights: statistics in fp32, one cast
+// back to the storage dtype at the end).
+//
+//   rstd[t] = 1 / sqrt(sum_j X[t,j]^2 / d + eps)              (fp32, saved)
+//   Y[t,j]  = X[t,j] * rstd[t] * w[j]                         (fp32, rounded once)
+//   dX[t,i] = rstd g_i - rstd^3 x_i (sum_j g_j x_j) / d,  g_j = dY[t,j] w[j]
+//
+// The weight w is frozen (no dw), as the base weights are.  One wave per
+// row: a lane walks its 16-byte chunks in order and the wave adds the lane
+// sums with a fixed butterfly, so results are bitwise reproducible.  Both
+// kernels are HBM-bound (a row is read twice, the second time from L2).
+#pragma once
+#include "common.hpp"
+
+namespace lora {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 &v, float o[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = bf16lo(v[i]);
+    o[2 * i + 1] = bf16hi(v[i]);
+  }
+}
+
+// bf16 rows (d % 8 == 0) read as 16-byte chunks; fp32 rows element by element
+template <bool F32>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd(const void *Xv, const void *wv, float eps,
+                                                     int T, int d, void *Yv, float *rstd) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  float ss = 0.f;
+  if constexpr (F32) {
+    const float *x = reinterpret_cast<const float *>(Xv) + (int64_t)row * d;
+    for (int j = lane; j < d; j += 64) ss = fmaf(x[j], x[j], ss);
+  } else {
+    const bf16_t *x = reinterpret_cast<const bf16_t *>(Xv) + (int64_t)row * d;
+    for (int c = lane; c < d / 8; c += 64) {
+      float v[8];
+      unpack8(gload16(x + 8 * c), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  if (lane == 0) rstd[row] = r;
+  if constexpr (F32) {
+    const float *x = reinterpret_cast<const float *>(Xv) + (int64_t)row * d;
+    const float *w = reinterpret_cast<const float *>(wv);
+    float *y = reinterpret_cast<float *>(Yv) + (int64_t)row * d;
+    for (int j = lane; j < d; j += 64) y[j] = x[j] * r * w[j];
+  } else {
+    const bf16_t *x = reinterpret_cast<const bf16_t *>(Xv) + (int64_t)row * d;
+    const bf16_t *w = reinterpret_cast<const bf16_t *>(wv);
+    bf16_t *y = reinterpret_cast<bf16_t *>(Yv) + (int64_t)row * d;
+    for (int c = lane; c < d / 8; c += 64) {
+      float v[8], g[8];
+      unpack8(gload16(x + 8 * c), v);
+      unpack8(gload16(w + 8 * c), g);
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16x2(v[2 * i] * r * g[2 * i], v[2 * i + 1] * r * g[2 * i + 1]);
+      gstore16(y + 8 * c, o);
+    }
+  }
+}
+
+// dX = (or +=, accumulate != 0) the input gradient of k_rmsnorm_fwd
+template <bool F32>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const void *Xv, const void *wv,
+                                                     const float *rstd, const void *dYv, int T,
+                                                     int d, void *dXv, int accumulate) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const float r = rstd[row];
+  float dot = 0.f;
+  if constexpr (F32) {
+    const float *x = reinterpret_cast<const float *>(Xv) + (int64_t)row * d;
+    const float *w = reinterpret_cast<const float *>(wv);
+    const float *dy = reinterpret_cast<const float *>(dYv) + (int64_t)row * d;
+    for (int j = lane; j < d; j += 64) dot = fmaf(dy[j] * w[j], x[j], dot);
+  } else {
+    const bf16_t *x = reinterpret_cast<const bf16_t *>(Xv) + (int64_t)row * d;
+    const bf16_t *w = reinterpret_cast<const bf16_t *>(wv);
+    const bf16_t *dy = reinterpret_cast<const bf16_t *>(dYv) + (int64_t)row * d;
+    for (int c = lane; c < d / 8; c += 64) {
+      float xv[8], wv8[8], gv[8];
+      unpack8(gload16(x + 8 * c), xv);
+      unpack8(gload16(w + 8 * c), wv8);
+      unpack8(gload16(dy + 8 * c), gv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot = fmaf(gv[i] * wv8[i], xv[i], dot);
+    }
+  }
+  dot = wave_sum(dot);
+  const float cx = r * r * r * dot / (float)d;   // coefficient of x_i
+  if constexpr (F32) {
+    const float *x = reinterpret_cast<const float *>(Xv) + (int64_t)row * d;
+    const float *w = reinterpret_cast<const float *>(wv);
+    const float *dy = reinterpret_cast<const float *>(dYv) + (int64_t)row * d;
+    float *dx = reinterpret_cast<float *>(dXv) + (int64_t)row * d;
+    for (int j = lane; j < d; j += 64) {
+      const float v = r * (dy[j] * w[j]) - cx * x[j];
+      dx[j] = accumulate ? dx[j] + v : v;
+    }
+  } else {
+    const bf16_t *x = reinterpret_cast<const bf16_t *>(Xv) + (int64_t)row * d;
+    const bf16_t *w = reinterpret_cast<const bf16_t *>(wv);
+    const bf16_t *dy = reinterpret_cast<const bf16_t *>(dYv) + (int64_t)row * d;
+    bf16_t *dx = reinterpret_cast<bf16_t *>(dXv) + (int64_t)row * d;
+    for (int c = lane; c < d / 8; c += 64) {
+      float xv[8], wv8[8], gv[8], o8[8];
+      unpack8(gload16(x + 8 * c), xv);
+      unpack8(gload16(w + 8 * c), wv8);
+      unpack8(gload16(dy + 8 * c), gv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o8[i] = r * (gv[i] * wv8[i]) - cx * xv[i];
+      if (accumulate) {
+        float old[8];
+        unpack8(gload16(dx + 8 * c), old);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o8[i] += old[i];
+      }
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(o8[2 * i], o8[2 * i + 1]);
+      gstore16(dx + 8 * c, o);
+    }
+  }
+}
+
+}  // namespace lora

@@ -19,6 +19,8 @@ Sources (web pages; sections as printed on them):
   [CR]  "Unsloth code-reading guide" (ai-reference-codex.pages.dev/
         frontier/unsloth): 2.1 4-bit weights decoded to bf16 every step,
         2.3 manual LoRA path, 4 LoRA_MLP saves only X, e, g.
+  [SPD] "Unsloth speed secret: Triton kernels accelerate backprop"
+        (mokono.cn/news/201055): 3.2 RMSNorm kernel.
   [HF]  "Unsloth + TRL compiled blog" (bbs.huaweicloud.com/blogs/510494),
         section 1: SwiGLU named as a fused activation.
 
@@ -251,6 +253,33 @@ def decode_q4_weight(q) -> np.ndarray:
                                 q.absmax_blocksize)
         return bf16_bits_to_f64(bits)
     return decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k, q.blocksize)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm (the step in front of the gate/up and q/k/v projections)
+# ---------------------------------------------------------------------------
+def rmsnorm_fwd(X, w, eps):
+    """Y = X * rstd * w with rstd = 1 / sqrt(mean_j X[t,j]^2 + eps) per row.
+
+    Returns (Y, rstd).  ([SPD] 3.2, the RMSNorm kernel: mean of squares of
+    the row, reciprocal square root, kept for the backward, then the
+    normalised row times the weight; no bias in the Llama-style layer.)
+    """
+    X, w = _f64(X), _f64(w)
+    rstd = 1.0 / np.sqrt(np.mean(X * X, axis=1) + float(eps))
+    return X * rstd[:, None] * w[None, :], rstd
+
+
+def rmsnorm_bwd(X, w, eps, dY):
+    """dL/dX of rmsnorm_fwd for upstream dY, derived by hand ([DD] 2.4 style):
+    with g = dY * w and r = rstd,  dX_i = r g_i - r^3 X_i (sum_j g_j X_j) / d
+    (the weight is frozen, so there is no dw)."""
+    X, w, dY = _f64(X), _f64(w), _f64(dY)
+    d = X.shape[1]
+    r = 1.0 / np.sqrt(np.mean(X * X, axis=1) + float(eps))
+    g = dY * w[None, :]
+    dot = np.sum(g * X, axis=1)
+    return r[:, None] * g - (r ** 3 * dot / d)[:, None] * X
 
 
 # ---------------------------------------------------------------------------

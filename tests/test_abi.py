@@ -239,3 +239,27 @@ def test_merge_validation_codes():
     assert call(out=P_MIS) == 5
     assert call(dtype=0, W=_w(1, 64, None, P, P, P)) == 3     # 4-bit is bf16-only
     assert call(k=72, W=_w(1, 64, None, P, P, P)) == 2        # 4-bit needs k % 64 == 0
+
+
+def test_rmsnorm_validation_codes():
+    lib = L.lib()
+    fwd = lambda dt=1, T=16, d=64, eps=1e-5, X=P, w=P, Y=P, r=P: lib.lora_rmsnorm_fwd(
+        dt, T, d, eps, X, w, Y, r, None)
+    assert fwd(dt=3) == 3
+    assert fwd(eps=-1.0) == 3
+    assert fwd(eps=float("nan")) == 3
+    assert fwd(eps=float("inf")) == 3
+    assert fwd(d=60) == 2            # bf16 rows are 16-byte multiples
+    assert fwd(d=0) == 2
+    assert fwd(T=-1) == 2
+    assert fwd(w=None) == 1
+    assert fwd(X=None) == 1
+    assert fwd(r=None) == 1
+    assert fwd(Y=P_MIS) == 5
+    assert fwd(T=0, X=None, Y=None, r=None) == 0     # nothing to do, nothing launched
+    bwd = lambda dt=1, T=16, d=64, flags=0, dY=P, dX=P: lib.lora_rmsnorm_bwd(
+        dt, T, d, P, P, P, dY, dX, flags, None)
+    assert bwd(flags=2) == 3
+    assert bwd(dY=None) == 1
+    assert bwd(dX=P_MIS) == 5
+    assert bwd(dt=0, d=60, dX=None) == 1   # fp32 takes any width: the null dX is what fails

@@ -184,3 +184,19 @@ def test_full_config4_fused_qkv():
         check(f"dB_{p}", host(g["dB_" + p]), dBr, "bf16")
         dX_ref = dX_ref + oracle.linear_bwd(li.X[rows], li.W, li.A, li.B, s, li.dY[rows])[0]
     check("dX[rows]", host(g["dX"][rt]), dX_ref, "bf16")
+
+
+def test_full_rmsnorm_8b_rows():
+    """RMSNorm forward and backward over T=8192 rows of d=4096 (the 8B
+    model's hidden size), every element against the oracle."""
+    import torch
+    from lora_inputs import gen_rmsnorm
+    ri = gen_rmsnorm(8192, 4096, "bf16", seed=77)
+    X, w, dY = dev(ri.X, "bf16"), dev(ri.w, "bf16"), dev(ri.dY, "bf16")
+    Y, rstd = L.lora_rmsnorm_fwd(X, w, ri.eps)
+    dX = L.lora_rmsnorm_bwd(X, w, rstd, dY)
+    torch.cuda.synchronize()
+    Yr, rr = oracle.rmsnorm_fwd(ri.X, ri.w, ri.eps)
+    assert np.allclose(host(rstd), rr, rtol=1e-5, atol=0)
+    check("Y", host(Y), Yr, "bf16")
+    check("dX", host(dX), oracle.rmsnorm_bwd(ri.X, ri.w, ri.eps, ri.dY), "bf16")

@@ -386,3 +386,62 @@ def test_generated_dq_weight_layout():
     W = oracle.decode_q4_weight(q)
     assert W.shape == (72, 128) and np.isfinite(W).all()
     assert np.abs(W).max() <= 0.07
+
+
+# ------------------------------------------------------------------ RMSNorm
+def test_rmsnorm_constant_rows_closed_form():
+    # a row of equal values c: mean of squares c^2, so Y = c / sqrt(c^2 + eps) w
+    w = np.array([1.0, -2.0, 0.5, 3.0])
+    X = np.array([[2.0] * 4, [-0.5] * 4, [0.0] * 4])
+    Y, rstd = oracle.rmsnorm_fwd(X, w, 0.25)
+    assert np.allclose(rstd, [1 / math.sqrt(4.25), 1 / math.sqrt(0.5), 2.0], rtol=1e-15)
+    assert np.allclose(Y[0], 2.0 / math.sqrt(4.25) * w, rtol=1e-15)
+    assert np.allclose(Y[1], -0.5 / math.sqrt(0.5) * w, rtol=1e-15)
+    assert np.all(Y[2] == 0.0)
+    # eps = 0: a constant row normalises to sign(c) w
+    Y0, _ = oracle.rmsnorm_fwd(X[:2], w, 0.0)
+    assert np.allclose(Y0, [w, -w], rtol=1e-15)
+
+
+def test_rmsnorm_hand_row():
+    # X = [3, 4]: mean of squares 12.5, eps 0.0 -> rstd = 1/sqrt(12.5)
+    Y, rstd = oracle.rmsnorm_fwd(np.array([[3.0, 4.0]]), np.array([1.0, 10.0]), 0.0)
+    assert abs(rstd[0] - 1 / math.sqrt(12.5)) < 1e-16
+    assert np.allclose(Y[0], [3 / math.sqrt(12.5), 40 / math.sqrt(12.5)], rtol=1e-15)
+    # unit root-mean-square rows pass through unchanged (times w)
+    X = np.array([[1.0, -1.0, 1.0, -1.0]])
+    assert np.allclose(oracle.rmsnorm_fwd(X, np.ones(4), 0.0)[0], X, rtol=1e-15)
+
+
+def test_rmsnorm_scale_invariance_and_orthogonal_gradient():
+    g = np.random.default_rng(3)
+    X, w, dY = g.standard_normal((5, 12)), g.standard_normal(12), g.standard_normal((5, 12))
+    Y, _ = oracle.rmsnorm_fwd(X, w, 0.0)
+    Y3, _ = oracle.rmsnorm_fwd(3.5 * X, w, 0.0)
+    assert np.allclose(Y, Y3, rtol=1e-13)
+    # with eps = 0 the output does not change along x, so the gradient is
+    # orthogonal to x row by row
+    dX = oracle.rmsnorm_bwd(X, w, 0.0, dY)
+    assert np.allclose(np.sum(dX * X, axis=1), 0.0, atol=1e-12)
+
+
+def test_rmsnorm_gradient_finite_differences():
+    g = np.random.default_rng(4)
+    X, w, dY = g.standard_normal((3, 7)), g.standard_normal(7), g.standard_normal((3, 7))
+    eps = 1e-2
+    loss = lambda: float(np.sum(dY * oracle.rmsnorm_fwd(X, w, eps)[0]))
+    assert oracle.rel_fro(oracle.rmsnorm_bwd(X, w, eps, dY), _fd(loss, X)) < 1e-7
+
+
+def test_rmsnorm_against_torch_autograd_float64():
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(6)
+    X, w, dY = g.standard_normal((9, 16)), g.standard_normal(16), g.standard_normal((9, 16))
+    eps = 1e-5
+    tX = torch.tensor(X, requires_grad=True)
+    ty = tX * torch.rsqrt(tX.pow(2).mean(-1, keepdim=True) + eps) * torch.tensor(w)
+    ty.backward(torch.tensor(dY))
+    Y, _ = oracle.rmsnorm_fwd(X, w, eps)
+    assert np.allclose(Y, ty.detach().numpy(), rtol=1e-13, atol=1e-15)
+    assert np.allclose(oracle.rmsnorm_bwd(X, w, eps, dY), tX.grad.numpy(), rtol=1e-12,
+                       atol=1e-14)
