@@ -197,6 +197,43 @@ def cpu_baseline(cfg, tokens, mi, reps=2):
             "tokens_per_s": tokens / dt, "seconds_per_rep": dt}
 
 
+def time_rmsnorm(T, d, reps=20):
+    """RMSNorm in front of the MLP (outside the timed step): average kernel
+    time of the forward and the backward over `reps` launches each, and the
+    HBM rate of their algorithmic bytes (fwd: X, w read, Y, rstd written;
+    bwd: X, w, rstd, dY read, dX written)."""
+    import torch
+
+    import lora_linear_fwd_amd as L
+    from lora_inputs import gen_rmsnorm
+    ri = gen_rmsnorm(T, d, "bf16", seed=5)
+    up = lambda a: torch.from_numpy(a).to(torch.bfloat16).to("cuda:0")
+    X, w, dY = up(ri.X), up(ri.w), up(ri.dY)
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    rstd = torch.empty((T,), dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    out = {}
+    for name, fn, nbytes in (
+            ("fwd", lambda: L.lora_rmsnorm_fwd(X, w, ri.eps, Y=Y, rstd=rstd, stream=st),
+             4 * T * d + 2 * d + 4 * T),
+            ("bwd", lambda: L.lora_rmsnorm_bwd(X, w, rstd, dY, dX=dX, stream=st),
+             6 * T * d + 2 * d + 4 * T)):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[name + "_ms"] = round(ms, 4)
+        out[name + "_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    out["T"], out["d"] = T, d
+    return out
+
+
 def bench_attn_mlp(args):
     """Config 4: q, k, v (shared input, dX summed) and o LoRA projections plus
     the LoRA-SwiGLU MLP, forward + backward, T = 16384, r = 64."""
@@ -396,6 +433,8 @@ def main():
                      "avg_launch_ms": round(kms[dom], 4)},
         "cpu_baseline": None,
     }
+    # the RMSNorm in front of the MLP, timed on its own (not part of value)
+    line["rmsnorm_before_mlp"] = time_rmsnorm(T, d)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens, mi)
     print(json.dumps(line), flush=True)

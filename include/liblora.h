@@ -12,7 +12,7 @@
  *   [WHY] "Why Unsloth trains 5-8x faster" (mokono.cn/news/868259) --
  *         3.1/3.2 the rank-r product x A^T stays on chip inside one fused
  *         kernel; 5.2 4-bit dequantisation fused into the matmul.
- *   [SPD] "Unsloth speed secret: Triton kernels accelerate backprop"
+ *   [TB] "Unsloth speed secrets: Triton kernels accelerate backprop"
  *         (mokono.cn/news/201055) -- 3.2 RMSNorm kernel: per-row mean of
  *         squares, reciprocal root saved for the backward, times weight.
  *   [CR]  "Unsloth code-reading guide" (ai-reference-codex.pages.dev/
@@ -224,7 +224,7 @@ int lora_decode_weight(int64_t n, int64_t k, const lora_weight *W, int out_dtype
 
 /*
  * RMSNorm over the rows of X [T x d], the step in front of the gate/up and
- * q/k/v projections ([SPD] 3.2; statistics in fp32 and one cast at the end
+ * q/k/v projections ([TB] 3.2; statistics in fp32 and one cast at the end
  * per [CR] highlights):
  *   rstd[t] = 1 / sqrt(sum_j X[t,j]^2 / d + eps)       (fp32, [T])
  *   Y[t,j]  = X[t,j] * rstd[t] * w[j]                  (fp32, rounded once)

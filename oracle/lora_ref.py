@@ -19,7 +19,7 @@ Sources (web pages; sections as printed on them):
   [CR]  "Unsloth code-reading guide" (ai-reference-codex.pages.dev/
         frontier/unsloth): 2.1 4-bit weights decoded to bf16 every step,
         2.3 manual LoRA path, 4 LoRA_MLP saves only X, e, g.
-  [SPD] "Unsloth speed secret: Triton kernels accelerate backprop"
+  [TB] "Unsloth speed secrets: Triton kernels accelerate backprop"
         (mokono.cn/news/201055): 3.2 RMSNorm kernel.
   [HF]  "Unsloth + TRL compiled blog" (bbs.huaweicloud.com/blogs/510494),
         section 1: SwiGLU named as a fused activation.
@@ -261,7 +261,7 @@ def decode_q4_weight(q) -> np.ndarray:
 def rmsnorm_fwd(X, w, eps):
     """Y = X * rstd * w with rstd = 1 / sqrt(mean_j X[t,j]^2 + eps) per row.
 
-    Returns (Y, rstd).  ([SPD] 3.2, the RMSNorm kernel: mean of squares of
+    Returns (Y, rstd).  ([TB] 3.2, the RMSNorm kernel: mean of squares of
     the row, reciprocal square root, kept for the backward, then the
     normalised row times the weight; no bias in the Llama-style layer.)
     """
