@@ -27,16 +27,18 @@
 //   EPI_SWIGLU_FWD  gate/up interleaved tile: e, g, h = silu(e) g (bf16)
 //   EPI_SWIGLU_BWD  dh tile: loads saved e, g; writes de, dg (bf16)
 //
-// Tile 256 x 256, K step 32, 256 threads = 4 waves in a 2 x 2 grid, each wave
-// a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 blocks with its 256 fp32
+// Tile 256 x 256, 256 threads = 4 waves in a 2 x 2 grid, each wave a
+// 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 blocks with its 256 fp32
 // accumulators in AGPRs.  The MFMA "A" operand is the B_op fragment and the
 // "B" operand the A_op fragment, so each lane ends with 4 consecutive output
 // columns of one output row (8-byte stores).
 //
-// Pipeline: 4 LDS stages of 32 KB.  Global tiles go straight to LDS with
-// buffer_load ... lds three K steps ahead; the barrier of each step sits
-// between its two 16-K sub-steps, so the next stage's first fragment reads
-// overlap the current stage's last 16 MFMAs.
+// Pipeline: global tiles go straight to LDS with buffer_load ... lds.  Dense
+// NT: K step 32 over 4 LDS stages of 32 KB, loads three steps ahead, the A
+// tile's loads spread over the first 16-K sub-step and the B tile's over the
+// second; other forms: K step 64 over 2 stages of 64 KB, one step ahead.  The
+// barrier of each step sits before its last 16-K sub-step, so the next
+// stage's first fragment reads overlap the current stage's last 16 MFMAs.
 #pragma once
 #include <type_traits>
 
@@ -53,9 +55,23 @@ constexpr int BM = 256, BN = 256, NTHREADS = 256;
 #ifndef LORA_GEMM_NSTAGE
 #define LORA_GEMM_NSTAGE 2
 #endif
+// the dense NT form: K step 32 over four stages with its DMA split in two
+// (measured faster than K step 64 over two stages; the other forms are not)
+#ifndef LORA_GEMM_BK_NT
+#define LORA_GEMM_BK_NT 32
+#endif
+#ifndef LORA_GEMM_NSTAGE_NT
+#define LORA_GEMM_NSTAGE_NT 4
+#endif
+#ifndef LORA_DMA_SPLIT
+#define LORA_DMA_SPLIT 1
+#endif
 constexpr int kBK = LORA_GEMM_BK, kNSTAGE = LORA_GEMM_NSTAGE;
+constexpr int kBK_NT = LORA_GEMM_BK_NT, kNSTAGE_NT = LORA_GEMM_NSTAGE_NT;
 static_assert(kBK == 32 || kBK == 64, "K step must be 32 or 64");
 static_assert(kNSTAGE >= 2 && kNSTAGE <= 4, "2 to 4 pipeline stages");
+static_assert(kBK_NT == 32 || kBK_NT == 64, "K step must be 32 or 64");
+static_assert(kNSTAGE_NT >= 2 && kNSTAGE_NT <= 4, "2 to 4 pipeline stages");
 
 enum BMode { B_NT = 0, B_NT_Q4 = 1, B_NN = 2, B_NN_Q4 = 3, B_NT_Q4DQ = 4, B_NN_Q4DQ = 5 };
 constexpr bool bmode_nt_q4(int m) { return m == B_NT_Q4 || m == B_NT_Q4DQ; }
@@ -170,6 +186,27 @@ __device__ __forceinline__ void sched_mfma_read_dma() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+}
+
+// READS pairs of (MFMA, LDS read), then 16 - READS MFMAs with DMAS VMEM loads
+// spread evenly over them (I: compile-time position)
+template <int READS, int DMAS, int I = 0>
+__device__ __forceinline__ void sched_dma_tail() {
+  if constexpr (I < 16 - READS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int n = DMAS * (I + 1) / (16 - READS) - DMAS * I / (16 - READS);
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
+    sched_dma_tail<READS, DMAS, I + 1>();
+  }
+}
+template <int READS, int DMAS>
+__device__ __forceinline__ void sched_reads_then_dma() {
+#pragma unroll
+  for (int i = 0; i < READS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  sched_dma_tail<READS, DMAS>();
 }
 
 template <int BMODE>
@@ -430,6 +467,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     }
   };
 
+  // the same as issue_dma_fast in two parts: part 0 the A tile, part 1 the B tile
+  auto issue_dma_part = [&](int kt, char *stage, int part) {
+    const int k0 = kt * BK;
+    char *Xs = stage, *Ws = stage + XS;
+    if (part == 0) {
+      const uint32_t sa = 2u * (uint32_t)k0 + (k0 >= ksplit ? dA1 : 0u);
+#pragma unroll
+      for (int u = 0; u < NDMA; ++u) dma16(rsA, Xs + (4 * u + wave) * 1024, aoff[u], sa);
+    } else if constexpr (BMODE == B_NT) {
+#pragma unroll
+      for (int u = 0; u < NDMA; ++u) {
+        const int b = 4 * u + wave;
+        const __amdgpu_buffer_rsrc_t r = (GU && (((RPI * b) >> 6) & 1)) ? rsB1 : rsB0;
+        dma16(r, Ws + b * 1024, boff[u], 2u * (uint32_t)k0);
+      }
+    } else if constexpr (BMODE == B_NN) {
+      const bool second = k0 >= ksplit;
+      const __amdgpu_buffer_rsrc_t r = second ? rsB1 : rsB0;
+#pragma unroll
+      for (int u = 0; u < BK / 8; ++u) {
+        const int b = 4 * u + wave;
+        const int kr = k0 + 2 * b - (second ? ksplit : 0);
+        dma16(r, Ws + b * 1024, boff[u], (uint32_t)(kr * p.ldb * 2));
+      }
+    }
+  };
+
   // ----------------------------- 4-bit weights: global -> registers -> LDS
   auto load_q4 = [&](Stage<BMODE> &st, int kt) {
     const int k0 = kt * BK;
@@ -588,21 +652,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     if ((ksplit % BK) != 0 && ksplit < K) s_end = min(s_end, ksplit / BK);
     nfast = max(0, min(nkt, s_end - (NSTAGE - 1)));
   }
+  // Split DMA (three or more stages, dense forms): the A part of a step's
+  // DMA goes out in its first sub-step and the B part in its last, each
+  // spread over the MFMAs that follow the sub-step's fragment reads, so the
+  // loads never queue up in front of the MFMAs; the wait then lets the
+  // younger B part stay in flight.
+  constexpr bool kSplit = LORA_DMA_SPLIT && NSTAGE >= 3 && !Q4 && !DOPF;
+  constexpr int kDmaA = NDMA, kDmaB = kDmaPerStep - NDMA;
+  // at the wait of step kt the loads of stage kt+1 (step kt+2-NSTAGE, its B
+  // part last) are followed by NSTAGE-3 whole steps and this step's A part
+  constexpr int kWaitSplit = kSplit ? (NSTAGE - 3) * kDmaPerStep + kDmaA : 0;
   auto step = [&](int kt, auto fast_tag) {
     constexpr bool FAST = decltype(fast_tag)::value;
+    constexpr bool SPLIT = FAST && kSplit;
     const char *cur = smem + (kt % NSTAGE) * STAGE;
     char *nxt = smem + ((kt + 1) % NSTAGE) * STAGE;
     char *tgt = smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE;
     if constexpr (Q4) load_q4(st, kt + 1);
-    if constexpr (FAST) issue_dma_fast(kt + NSTAGE - 1, tgt);
-    else issue_dma(kt + NSTAGE - 1, tgt);
+    if constexpr (SPLIT) {
+      // issued inside the sub-steps below
+    } else if constexpr (FAST) {
+      issue_dma_fast(kt + NSTAGE - 1, tgt);
+    } else {
+      issue_dma(kt + NSTAGE - 1, tgt);
+    }
     issue_pf(kt + NSTAGE - 1 + PF);
 #pragma unroll
     for (int kk = 0; kk + 1 < KSUB; ++kk) {
       // sub-step kk: MFMAs on fragment set kk&1, reads of kk+1 interleaved
       read_frags(cur, kk + 1, (kk + 1) & 1);
+      if (SPLIT && kk == 0) issue_dma_part(kt + NSTAGE - 1, tgt, 0);
       mfmas(kk & 1);
-      if (FAST && kk == 0 && kDmaPerStep % (16 - kReads) == 0) {
+      if (SPLIT && kk == 0) {
+        sched_reads_then_dma<kReads, kDmaA>();
+      } else if (FAST && !SPLIT && kk == 0 && kDmaPerStep % (16 - kReads) == 0) {
         sched_mfma_read_dma<kReads, kDmaPerStep>();
       } else {
         sched_pairs<kReads>();
@@ -616,6 +699,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
       vm_wait<kWaitQ4>();
       commit_q4(st, nxt);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else if constexpr (SPLIT) {
+      vm_wait<kWaitSplit>();
     } else {
       vm_wait<kWaitDense>();
     }
@@ -624,9 +709,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     // last sub-step: MFMAs on its fragment set, the next stage's first
     // reads interleaved (on the last step they read a stage nobody uses)
     read_frags(nxt, 0, 0);
+    if constexpr (SPLIT) issue_dma_part(kt + NSTAGE - 1, tgt, 1);
     mfmas((KSUB - 1) & 1);
-    sched_pairs<kReads>();
-    sched_group<0x008, 16 - kReads>();
+    if constexpr (SPLIT) {
+      sched_reads_then_dma<kReads, kDmaB>();
+    } else {
+      sched_pairs<kReads>();
+      sched_group<0x008, 16 - kReads>();
+    }
   };
   int kt = 0;
   for (; kt < nfast; ++kt) step(kt, std::true_type{});
@@ -818,6 +908,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     __builtin_amdgcn_wave_barrier();
   }
 }
+
+// K step and pipeline depth of each B form
+template <int BMODE>
+constexpr int gemm_bk() { return BMODE == B_NT ? kBK_NT : kBK; }
+template <int BMODE>
+constexpr int gemm_nstage() { return BMODE == B_NT ? kNSTAGE_NT : kNSTAGE; }
 
 template <int BMODE, int PF = 0, int BK = kBK, int NSTAGE = kNSTAGE>
 constexpr size_t gemm_lds_bytes() {
