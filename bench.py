@@ -375,28 +375,40 @@ def main():
     torch.cuda.synchronize()
 
     kcs = [L.KC_GATEUP_FWD, L.KC_DOWN_FWD, L.KC_DOWN_BWD, L.KC_GATEUP_BWD]
-    ev = {kc: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)] for kc in kcs}
-    for kc in kcs:
-        for a_, b_ in ev[kc]:
-            a_.record(stream); b_.record(stream)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        for kc in kcs:
-            L.time_next(kc, *ev[kc][i])
-        step()
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_stop) / args.steps
 
-    kms = {kc: float(np.mean([a_.elapsed_time(b_) for a_, b_ in ev[kc]])) for kc in kcs}
-    dom = max(kcs, key=lambda kc: kms[kc])
+    def timed_steps(n, classes):
+        """n steps with HIP events around every launch of the given GEMM
+        classes (recorded by the library on its launch stream)."""
+        ev = {kc: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)] for kc in classes}
+        for kc in classes:
+            for a_, b_ in ev[kc]:
+                a_.record(stream); b_.record(stream)
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_stop = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        t_start.record(stream)
+        for i in range(n):
+            for kc in classes:
+                L.time_next(kc, *ev[kc][i])
+            step()
+        t_stop.record(stream)
+        torch.cuda.synchronize()
+        w = time.perf_counter() - w0
+        per = {kc: float(np.mean([a_.elapsed_time(b_) for a_, b_ in ev[kc]])) for kc in classes}
+        return t_start.elapsed_time(t_stop) / n, w, per
+
+    # the dominant GEMM class, from two untimed steps; the timed region then
+    # records events around that class only (each event pair adds a few
+    # microseconds of launch gap to the step)
+    _, _, probe = timed_steps(2, kcs)
+    dom = max(kcs, key=lambda kc: probe[kc])
+    ms, wall, live = timed_steps(args.steps, [dom])
+    # every GEMM class, in a separate pass after the timed region (reported
+    # as kernels_ms; not part of value)
+    _, _, kms = timed_steps(min(args.steps, 5), kcs)
+    kms[dom] = live[dom]
     names = dict(zip([L.KC_GATEUP_FWD, L.KC_DOWN_FWD, L.KC_DOWN_BWD, L.KC_GATEUP_BWD], KC_NAMES))
     dom_tflops = gemm_flops(dom, T, d, f, r) / (kms[dom] * 1e-3) / 1e12
     flops = mlp_flops(T, d, f, r)
@@ -425,6 +437,8 @@ def main():
                    "workspace": "minimal" if args.minimal_ws else "fast"},
         "wall_s_timed": round(wall, 3),
         "kernels_ms": {names[kc]: round(kms[kc], 4) for kc in kcs},
+        "kernels_ms_source": "roofline kernel: HIP events in the timed region; the others: "
+                             "a separate pass of up to 5 steps after it",
         "roofline": {"bound": "mfma", "kernel": names[dom], "achieved": round(dom_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),

@@ -71,7 +71,7 @@ constexpr int kBK_NT = LORA_GEMM_BK_NT, kNSTAGE_NT = LORA_GEMM_NSTAGE_NT;
 static_assert(kBK == 32 || kBK == 64, "K step must be 32 or 64");
 static_assert(kNSTAGE >= 2 && kNSTAGE <= 4, "2 to 4 pipeline stages");
 static_assert(kBK_NT == 32 || kBK_NT == 64, "K step must be 32 or 64");
-static_assert(kNSTAGE_NT >= 2 && kNSTAGE_NT <= 4, "2 to 4 pipeline stages");
+static_assert(kNSTAGE_NT >= 2 && kNSTAGE_NT <= 5, "2 to 5 pipeline stages");
 
 enum BMode { B_NT = 0, B_NT_Q4 = 1, B_NN = 2, B_NN_Q4 = 3, B_NT_Q4DQ = 4, B_NN_Q4DQ = 5 };
 constexpr bool bmode_nt_q4(int m) { return m == B_NT_Q4 || m == B_NT_Q4DQ; }
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   constexpr int RPI = 1024 / (2 * BK);   // tile rows per 1-KB DMA instruction
   constexpr int NDMA = BM / RPI / 4;     // DMA instructions per wave per operand tile
   constexpr int CPR = BK / 8;            // 16-byte chunks per row
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "pipeline depth");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5, "pipeline depth");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
