@@ -33,9 +33,12 @@ struct Bump {
 
 // split choices shared by the planner and the launchers
 struct NTSplit { int ks; int kchunk; };
+#ifndef LORA_NT_SLOTS
+#define LORA_NT_SLOTS 1024
+#endif
 inline NTSplit nt_split(int64_t T, int64_t K) {
   const int64_t gx = std::max<int64_t>(1, cdiv(T, 64));
-  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, gx), cdiv(K, 512)));
+  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(LORA_NT_SLOTS, gx), cdiv(K, 512)));
   int64_t kchunk = cdiv(cdiv(K, ks), 128) * 128;
   ks = std::max<int64_t>(1, cdiv(K, kchunk));
   return {(int)ks, (int)kchunk};
