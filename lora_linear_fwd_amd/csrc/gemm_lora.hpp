@@ -212,13 +212,12 @@ __device__ __forceinline__ void sched_reads_then_dma() {
 template <int BMODE>
 struct Stage {  // sized for BK <= 64
   // register-staged 4-bit B operand (the dense forms go straight to LDS)
-  u32x4 qc[2];
-  uint32_t qn[bmode_nn_q4(BMODE) ? 8 : 1];
-  float qs[bmode_nn_q4(BMODE) ? 8 : 1];   // absmax, or the 256-block scale (DQ)
+  u32x4 qc[2];                           // NT: BK/2 code bytes; NN: 16 per row
+  float qs[bmode_nn_q4(BMODE) ? 2 : 1];   // absmax, or the 256-block scale (DQ)
   // NN: bit i = row i comes from the second weight; DQ: bits 8 + i = row i
-  // valid, bytes of q8 = 8-bit absmax codes
+  // valid, byte i of q8 = row i's 8-bit absmax code
   uint32_t qf;
-  uint32_t q8[bmode_nn_q4(BMODE) ? 2 : 1];
+  uint32_t q8;
 };
 
 // PF (dense NT form only): each K step also warms L2 for the step PF steps
@@ -509,34 +508,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
         const bool ok = live && boff[1] != 0xFFFFFFFFu;
         const uint32_t b = ok ? boff[1] + (uint32_t)(k0 / 64) : 0u;
         const bool up = tsel != 0;
-        st.q8[0] = (up ? p.D1 : p.D0)[b];
+        st.q8 = (up ? p.D1 : p.D0)[b];
         st.qs[0] = (up ? p.DS1 : p.DS0)[b >> 8];
         st.qf = ok ? 0x100u : 0u;
       } else {
         st.qs[0] = __uint_as_float(bload4(rsB1, live ? boff[1] : kOOB, (uint32_t)(k0 / 64) * 4));
       }
     } else if constexpr (bmode_nn_q4(BMODE)) {
-      // weight rows k0 + (BK/8) kb .., 8 columns gn.. (4 code bytes each)
-      const int kb = tid >> 5, nb = tid & 31;
-      const int gn = n0 + nb * 8;
+      // weight rows k0 + kr + 32 i (i < BK/32), 32 columns gn .. gn+31 each:
+      // 16 code bytes (one 16-byte load) and one absmax, since N % 64 == 0
+      // puts the 32 columns inside one 64-block
+      const int kr = tid >> 3, gn = n0 + 32 * (tid & 7);
       st.qf = 0u;
-      if constexpr (DQ) st.q8[0] = st.q8[1] = 0u;
+      if constexpr (DQ) st.q8 = 0u;
 #pragma unroll
-      for (int i = 0; i < BK / 8; ++i) {
-        const int gk = k0 + kb * (BK / 8) + i;
+      for (int i = 0; i < BK / 32; ++i) {
+        const int gk = k0 + kr + 32 * i;
         const bool ok = live && gk < K && gn < N;
         const bool first = gk < ksplit;
         const int64_t wr = first ? gk : gk - ksplit;
-        const uint8_t *q = (first ? p.Q0 : p.Q1) + wr * (int64_t)(N / 2) + gn / 2;
-        const int64_t blk = (wr * (int64_t)N + gn) >> 6;
-        const uint32_t cw = *reinterpret_cast<const uint32_t *>(ok ? q : p.Q0);
-        st.qn[i] = ok ? cw : 0u;
+        const int64_t e0 = wr * (int64_t)N + gn;   // flat element index in its weight
+        const uint8_t *q = (first ? p.Q0 : p.Q1) + e0 / 2;
+        const int64_t blk = e0 >> 6;
+        const u32x4 cv = gload16(ok ? q : p.Q0);
+        st.qc[i] = cv;
+        if (!ok) st.qc[i] = u32x4{0u, 0u, 0u, 0u};
         st.qf |= (first ? 0u : 1u) << i;
         if constexpr (DQ) {
           const int64_t b = ok ? blk : 0;
           const uint32_t c8 = (first ? p.D0 : p.D1)[b];
           st.qs[i] = (first ? p.DS0 : p.DS1)[b >> 8];
-          st.q8[i >> 2] |= (ok ? c8 : 0u) << (8 * (i & 3));
+          st.q8 |= (ok ? c8 : 0u) << (8 * i);
           st.qf |= (ok ? 1u : 0u) << (8 + i);
         } else {
           const float *sc = (first ? p.S0 : p.S1) + blk;
@@ -566,20 +568,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     char *Ws = stage + XS;
     if constexpr (bmode_nt_q4(BMODE)) {
       float am = st.qs[0];
-      if constexpr (DQ) am = dq_absmax(st.q8[0], st.qs[0], tsel != 0, st.qf != 0u);
+      if constexpr (DQ) am = dq_absmax(st.q8, st.qs[0], tsel != 0, st.qf != 0u);
 #pragma unroll
       for (int c = 0; c < CPR; ++c)
         lds_write16(Ws, kc_off<BK>(tid, c), decode4(st.qc[c >> 2][c & 3], am, tsel));
     } else if constexpr (bmode_nn_q4(BMODE)) {
-      const int kb = tid >> 5, nb = tid & 31;
+      // row kr + 32 i, chunks 4 cg .. 4 cg + 3.  Lanes with cg >= 4 write
+      // their chunks rotated by one, so the 8 lanes of one row (64-byte
+      // slots, cg and cg + 4 a bank period apart) hit distinct banks.
+      const int kr = tid >> 3, cg = tid & 7, rot = cg >> 2;
 #pragma unroll
-      for (int i = 0; i < BK / 8; ++i) {
+      for (int i = 0; i < BK / 32; ++i) {
         const bool second = (st.qf >> i) & 1u;
         float am = st.qs[i];
         if constexpr (DQ)
-          am = dq_absmax((st.q8[i >> 2] >> (8 * (i & 3))) & 0xFFu, st.qs[i], second,
-                         (st.qf >> (8 + i)) & 1u);
-        lds_write16(Ws, nn_off(kb * (BK / 8) + i, nb), decode4(st.qn[i], am, second ? 256 : 0));
+          am = dq_absmax((st.q8 >> (8 * i)) & 0xFFu, st.qs[i], second, (st.qf >> (8 + i)) & 1u);
+        const u32x4 c = st.qc[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // word (j + rot) & 3 by selects (an indexed vector read would go
+          // through scratch memory)
+          const uint32_t w = rot ? c[(j + 1) & 3] : c[j];
+          lds_write16(Ws, nn_off(kr + 32 * i, 4 * cg + ((j + rot) & 3)),
+                      decode4(w, am, second ? 256 : 0));
+        }
       }
     }
   };
