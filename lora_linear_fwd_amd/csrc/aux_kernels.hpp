@@ -186,30 +186,38 @@ __global__ __launch_bounds__(256) void k_skinny_tn(const SkinnyTNArgs a) {
       rows[i] = v;
     }
     transpose8x8(rows, cols);
-    u32x4 pv[(RS * 8 + 255) / 256];
+    // P tile [64 tokens x RS] fp32 in units of 4 tokens x 4 ranks: four
+    // 16-byte row loads, transposed into four 8-byte runs of 4 tokens
+    constexpr int NPU = (RS * 4 + 255) / 256;   // units per thread
+    u32x2 pv[NPU][4];
 #pragma unroll
-    for (int u = 0; u < (RS * 8 + 255) / 256; ++u) {
+    for (int u = 0; u < NPU; ++u) {
       const int idx = tid + 256 * u;
-      const int q = idx >> 3, tc = idx & 7;
-      u32x4 w = {0, 0, 0, 0};
-      if (q < RS) {
+      const int qq = idx >> 4, tq = idx & 15;   // rank quad, token quad
+      f32x4 pr[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int t = t0 + tc * 8 + 2 * h;
-          const float lo = t < tend ? a.P[(int64_t)t * RS + q] : 0.f;
-          const float hi = t + 1 < tend ? a.P[(int64_t)(t + 1) * RS + q] : 0.f;
-          w[h] = pack_bf16x2(lo, hi);
-        }
+      for (int h = 0; h < 4; ++h) {
+        const int t = t0 + 4 * tq + h;
+        pr[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (qq < RS / 4 && t < tend)
+          pr[h] = *reinterpret_cast<const f32x4 *>(a.P + (int64_t)t * RS + 4 * qq);
       }
-      pv[u] = w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pv[u][i] = u32x2{pack_bf16x2(pr[0][i], pr[1][i]), pack_bf16x2(pr[2][i], pr[3][i])};
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j) lds_write16(zs, swz_off(nb * 8 + j, kb), cols[j]);
 #pragma unroll
-    for (int u = 0; u < (RS * 8 + 255) / 256; ++u) {
+    for (int u = 0; u < NPU; ++u) {
       const int idx = tid + 256 * u;
-      if ((idx >> 3) < RS) lds_write16(ps, swz_off(idx >> 3, idx & 7), pv[u]);
+      const int qq = idx >> 4, tq = idx & 15;
+      if (qq < RS / 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x2 *>(ps + swz_off(4 * qq + i, tq >> 1) + (tq & 1) * 8) = pv[u][i];
+      }
     }
     __syncthreads();
 #pragma unroll
