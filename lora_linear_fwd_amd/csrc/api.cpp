@@ -271,6 +271,8 @@ int check_dims(int dtype, int64_t T, int64_t k, int64_t n, int64_t r) {
   if (T < 0 || k <= 0 || n <= 0 || r <= 0) return LORA_ERR_BAD_SHAPE;
   if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
   if (T > (int64_t)1 << 30 || k > (int64_t)1 << 24 || n > (int64_t)1 << 24) return LORA_ERR_BAD_SHAPE;
+  // every GEMM grid (256-token by 128- or 256-column tiles) fits a 31-bit count
+  if (cdiv(T, 256) * cdiv(2 * std::max(k, n), 128) >= ((int64_t)1 << 31)) return LORA_ERR_BAD_SHAPE;
   if (dtype == LORA_BF16 && ((k % 8) || (n % 8))) return LORA_ERR_BAD_SHAPE;
   return LORA_OK;
 }
@@ -1184,7 +1186,8 @@ int lora_dequant4(int64_t n, int64_t k, const uint8_t *codes, const float *absma
                   const float *codebook, int blocksize, int out_dtype, void *out, void *stream) {
   if (!codes || !absmax || !codebook || !out) return LORA_ERR_NULL_POINTER;
   if (out_dtype != LORA_BF16 || blocksize != 64) return LORA_ERR_UNSUPPORTED;
-  if (n <= 0 || k <= 0 || (k % 64) || n > ((int64_t)1 << 24) || k > ((int64_t)1 << 24))
+  if (n <= 0 || k <= 0 || (k % 64) || n > ((int64_t)1 << 24) || k > ((int64_t)1 << 24) ||
+      n * k > ((int64_t)1 << 44))
     return LORA_ERR_BAD_SHAPE;
   if (!aligned16(codes) || !aligned16(absmax) || !aligned16(codebook) || !aligned16(out))
     return LORA_ERR_MISALIGNED;
@@ -1240,7 +1243,8 @@ int lora_rmsnorm_bwd(int dtype, int64_t T, int64_t d, const void *X, const void 
 int lora_decode_weight(int64_t n, int64_t k, const lora_weight *W, int out_dtype, void *out,
                        void *stream) {
   if (out_dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
-  if (n <= 0 || k <= 0 || n > ((int64_t)1 << 24) || k > ((int64_t)1 << 24))
+  if (n <= 0 || k <= 0 || n > ((int64_t)1 << 24) || k > ((int64_t)1 << 24) ||
+      n * k > ((int64_t)1 << 44))
     return LORA_ERR_BAD_SHAPE;
   if (!W) return LORA_ERR_NULL_POINTER;
   if (W->fmt == LORA_W_DENSE) return LORA_ERR_UNSUPPORTED;

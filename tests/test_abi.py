@@ -263,3 +263,12 @@ def test_rmsnorm_validation_codes():
     assert bwd(dY=None) == 1
     assert bwd(dX=P_MIS) == 5
     assert bwd(dt=0, d=60, dX=None) == 1   # fp32 takes any width: the null dX is what fails
+
+
+def test_grid_size_limits():
+    # 2^30 tokens by 2^24 features would need more than 2^31 GEMM tiles
+    assert fwd(T=1 << 30, k=64, n=1 << 24) == 2
+    lib = L.lib()
+    assert lib.lora_decode_weight(1 << 24, 1 << 24, ctypes.byref(_w(1, 64, None, P, P, P)), 1, P,
+                                  None) == 2
+    assert lib.lora_dequant4(1 << 24, 1 << 24, P, P, P, 64, 1, P, None) == 2
