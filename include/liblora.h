@@ -58,6 +58,11 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous on it and reentrant; kernel faults surface at the
  *     caller's next synchronisation.
+ *   - HIP graphs: a call launches kernels only (no allocation, memset,
+ *     copy or synchronisation), so it can be captured into a graph and
+ *     replayed; replays reproduce eager results bit for bit.  The first
+ *     call of an op on a device sets kernel attributes (dynamic LDS size):
+ *     make it once outside capture.
  *   - Every argument is validated BEFORE any HIP call; on error nothing is
  *     launched and a status code below is returned.  No exception crosses
  *     the ABI and nothing aborts.

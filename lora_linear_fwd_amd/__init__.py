@@ -323,8 +323,10 @@ def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, n
     if not need_dx:
         o["dX"] = None
     for p in ("gate", "up", "down"):
-        o.setdefault("dA_" + p, torch.empty_like(A[p]))
-        o.setdefault("dB_" + p, torch.empty_like(B[p]))
+        if o.get("dA_" + p) is None:
+            o["dA_" + p] = torch.empty_like(A[p])
+        if o.get("dB_" + p) is None:
+            o["dB_" + p] = torch.empty_like(B[p])
     wsp, wsn = _workspace(OP_MLP_BWD, dt, _wfmt(W["gate"]), (T, d, f, r), X.device, workspace,
                           minimal_workspace)
     ws_ = [_wstruct(W[p]) for p in ("gate", "up", "down")]
@@ -377,12 +379,17 @@ def lora_qkv_bwd(X, W: Dict[str, Weight], A, B, alpha: float, dY: Dict[str, obje
     dt = _dtype_code(X)
     o = dict(out or {})
     if need_dx:
-        o["dX"] = torch.empty((T, k), dtype=X.dtype, device=X.device) if dX is None else dX
+        if dX is not None:
+            o["dX"] = dX
+        elif o.get("dX") is None:
+            o["dX"] = torch.empty((T, k), dtype=X.dtype, device=X.device)
     else:
         o["dX"] = None
     for p in ("q", "k", "v"):
-        o.setdefault("dA_" + p, torch.empty_like(A[p]))
-        o.setdefault("dB_" + p, torch.empty_like(B[p]))
+        if o.get("dA_" + p) is None:
+            o["dA_" + p] = torch.empty_like(A[p])
+        if o.get("dB_" + p) is None:
+            o["dB_" + p] = torch.empty_like(B[p])
     wsp, wsn = _workspace(OP_QKV_BWD, dt, _wfmt(W["q"]), (T, k, nq, nkv, r), X.device, workspace,
                           minimal_workspace)
     ws_ = [_wstruct(W[p]) for p in ("q", "k", "v")]
