@@ -360,15 +360,19 @@ def main():
     for p in ("gate", "up", "down"):
         out["dA_" + p] = torch.empty_like(A[p])
         out["dB_" + p] = torch.empty_like(B[p])
+    # one buffer; each call gets a view of exactly its strategy's size (the
+    # library picks the strategy from the size it is handed)
     mflag = L.LORA_WS_MINIMAL if args.minimal_ws else 0
-    ws_bytes = max(L.workspace_bytes(L.OP_MLP_FWD | mflag, L.LORA_BF16, wfmt, T, d, f, r),
-                   L.workspace_bytes(L.OP_MLP_BWD | mflag, L.LORA_BF16, wfmt, T, d, f, r))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fwd_bytes = L.workspace_bytes(L.OP_MLP_FWD | mflag, L.LORA_BF16, wfmt, T, d, f, r)
+    bwd_bytes = L.workspace_bytes(L.OP_MLP_BWD | mflag, L.LORA_BF16, wfmt, T, d, f, r)
+    ws_all = torch.empty(max(fwd_bytes, bwd_bytes), dtype=torch.uint8, device=dev)
+    ws_fwd, ws_bwd = ws_all[:fwd_bytes], ws_all[:bwd_bytes]
     stream = torch.cuda.current_stream()
 
     def step():
-        L.lora_swiglu_mlp_fwd(X, W, A, B, alpha, Y=Y, e=e, g=g, workspace=ws, stream=stream)
-        L.lora_swiglu_mlp_bwd(X, W, A, B, alpha, e, g, dY, out=out, workspace=ws, stream=stream)
+        L.lora_swiglu_mlp_fwd(X, W, A, B, alpha, Y=Y, e=e, g=g, workspace=ws_fwd, stream=stream)
+        L.lora_swiglu_mlp_bwd(X, W, A, B, alpha, e, g, dY, out=out, workspace=ws_bwd,
+                              stream=stream)
 
     for _ in range(args.warmup):
         step()

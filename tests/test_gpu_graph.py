@@ -33,9 +33,12 @@ def test_mlp_step_graph_replays_match_eager(form, ws):
     X, dY = dev(mi.X, "bf16"), dev(mi.dY, "bf16")
     wfmt = L._wfmt(Wd["gate"])
     flag = L.LORA_WS_MINIMAL if ws == "minimal" else 0
-    nbytes = max(L.workspace_bytes(L.OP_MLP_FWD | flag, L.LORA_BF16, wfmt, T, d, f, r),
-                 L.workspace_bytes(L.OP_MLP_BWD | flag, L.LORA_BF16, wfmt, T, d, f, r))
-    wsb = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    # one buffer, a view of exactly each call's strategy size (the size
+    # handed to the library selects the strategy)
+    nf = L.workspace_bytes(L.OP_MLP_FWD | flag, L.LORA_BF16, wfmt, T, d, f, r)
+    nb = L.workspace_bytes(L.OP_MLP_BWD | flag, L.LORA_BF16, wfmt, T, d, f, r)
+    wsb = torch.empty(max(nf, nb), dtype=torch.uint8, device="cuda")
+    wsf, wsbw = wsb[:nf], wsb[:nb]
     Y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
     e = torch.empty((T, f), dtype=torch.bfloat16, device="cuda")
     g = torch.empty((T, f), dtype=torch.bfloat16, device="cuda")
@@ -45,8 +48,8 @@ def test_mlp_step_graph_replays_match_eager(form, ws):
         out["dB_" + p] = torch.empty_like(B[p])
 
     def step(stream):
-        L.lora_swiglu_mlp_fwd(X, Wd, A, B, mi.alpha, Y=Y, e=e, g=g, workspace=wsb, stream=stream)
-        L.lora_swiglu_mlp_bwd(X, Wd, A, B, mi.alpha, e, g, dY, out=out, workspace=wsb,
+        L.lora_swiglu_mlp_fwd(X, Wd, A, B, mi.alpha, Y=Y, e=e, g=g, workspace=wsf, stream=stream)
+        L.lora_swiglu_mlp_bwd(X, Wd, A, B, mi.alpha, e, g, dY, out=out, workspace=wsbw,
                               stream=stream)
 
     outs = lambda: [Y, e, g] + [out[k] for k in sorted(out)]
