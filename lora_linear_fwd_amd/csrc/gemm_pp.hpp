@@ -1,0 +1,368 @@
+// Eight-wave ("ping-pong") form of the dense NT LoRA GEMM, for gfx950.
+//
+// Same contract as k_lora_gemm<B_NT, EPI> (GemmArgs; 256 x 256 output tile;
+// K = rs LoRA epilogue pass adding S . E^T, "Unsloth deep-dive" 1.3; store,
+// SwiGLU and SwiGLU' epilogues), run by 512 threads: two waves per SIMD, in
+// two groups of four (waves 0-3 and 4-7, one of each on every SIMD).  The
+// groups alternate between
+//   a compute phase: 32 back-to-back MFMA 32x32x16 on one K step (64) of
+//     fragments already in registers, and
+//   a memory phase: the LDS-DMA of its share of a later K step and the LDS
+//     fragment reads of its next K step,
+// with a workgroup barrier between phases, so that while one wave of a SIMD
+// waits on its vector-memory issue the other keeps the matrix core busy.
+// With one wave per SIMD (the four-wave form) those stalls sit between the
+// wave's own MFMAs.  Each wave owns a 128 (tokens) x 64 (weight rows)
+// sub-tile: 128 fp32 accumulators per lane, 96 registers of fragments.
+//
+// Phase schedule (step s lives in LDS stage s % 2):
+//   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: DMA share of step s+1, read s
+//   G1:   --     | M0 | C0 | M1 | C1 ...   Ms: read s, then DMA share of s+2
+// A stage is refilled only after both groups have read it; each group waits
+// for its own share of a step before the barrier that precedes the first
+// read of that step.
+//
+// Gate/up tiles (SwiGLU forward) interleave weight rows in 32-row blocks,
+// [32 gate | 32 up] per 64 tile rows, so every wave's 64 columns hold the
+// gate and up values of the same 32 features.
+#pragma once
+#include "gemm_lora.hpp"
+
+namespace lora {
+
+constexpr int PP_THREADS = 512;
+// two K-step-64 stages of 64 KB; the epilogue reuses them (8 x 16 KB)
+constexpr size_t PP_LDS = 2 * 65536;
+
+__device__ __forceinline__ void pp_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
+  constexpr int BK = 64, XS = BM * BK * 2, STAGE = 2 * XS;
+  constexpr int NU = 4;        // 1-KB DMA instructions per wave, operand tile and K step
+  constexpr int ND = 2 * NU;   // per wave and K step
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wm = wave & 1, wn = wave >> 1;   // token half, 64-row weight quarter
+  const int l32 = lane & 31, hi32 = lane >> 5;
+
+  int tm, tn;
+  map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = p.M, N = p.N, K = p.K, ksplit = p.ksplit;
+
+  // ---------------------------------------------------- DMA lane geometry
+  // Instruction u of wave w fills rows 8b .. 8b+7 (b = w + 8u) of an operand
+  // tile; lane l lands in row 8b + l/8 at physical chunk l%8, which holds
+  // logical chunk c = (l%8) ^ swz(row), i.e. K columns 8c .. 8c+7.
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A0 + (int64_t)m0 * p.lda, kMaxRecords);
+  // A1 - A0 - 2 ksplit: added to offsets of columns >= ksplit
+  const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
+  __amdgpu_buffer_rsrc_t rsB;
+  if constexpr (GU) {
+    // tile rows 8b.. are up-projection rows when (8b / 32) is odd, which for
+    // b = w + 8u is the wave's group: group 0 loads gate rows, group 1 up rows
+    rsB = make_rsrc((grp ? p.B1 : p.B0) + (int64_t)tn * 128 * p.ldb, kMaxRecords);
+  } else {
+    const bf16_t *bseg = p.B0;
+    int nsb = 0;
+    if (p.nseg1 > 0 && n0 >= p.nseg1) {
+      const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
+      bseg = s2 ? p.B2 : p.B1;
+      nsb = s2 ? p.nseg2 : p.nseg1;
+    }
+    rsB = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
+  }
+  uint32_t aoff[NU], boff[NU];
+  int kcol[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int row = 8 * (wave + 8 * u) + (lane >> 3);
+    const int c = (lane & 7) ^ (int)kc_swz<BK>(row);
+    kcol[u] = 8 * c;
+    aoff[u] = (m0 + row < M) ? (uint32_t)(row * p.lda * 2 + c * 16) : kOOB;
+    if constexpr (GU) {
+      const int jl = (row >> 6) * 32 + (row & 31);   // feature within the tile
+      boff[u] = (tn * 128 + jl < p.gu_f) ? (uint32_t)(jl * p.ldb * 2 + c * 16) : kOOB;
+    } else {
+      boff[u] = (n0 + row < N) ? (uint32_t)(row * p.ldb * 2 + c * 16) : kOOB;
+    }
+  }
+  const int nk = (K + BK - 1) / BK;
+  // This wave's share of K step kt into a stage.  Every call issues ND
+  // loads (lanes past M, N or K, and steps past the end, read zeros), so the
+  // per-wave count of outstanding loads is the same at every wait.
+  auto dma = [&](int kt, int stg) {
+    char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
+    const int k0 = kt * BK;
+    const bool live = kt < nk;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int col = k0 + kcol[u];
+      const bool ok = live && col < K && aoff[u] != kOOB;
+      const uint32_t v = ok ? aoff[u] + 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u) : kOOB;
+      dma16(rsA, Xs + (wave + 8 * u) * 1024, v, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int col = k0 + kcol[u];
+      const bool ok = live && col < K && boff[u] != kOOB;
+      dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff[u] + 2u * (uint32_t)k0 : kOOB, 0);
+    }
+  };
+
+  // ---------------------------------------------------- fragments, MFMAs
+  u32x4 fw[4][2], ft[4][4];   // [16-K sub-step][32-row block]: weight rows, tokens
+  auto rd = [&](int stg) {
+    const char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));
+    }
+  };
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto comp = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fw[kk][i], ft[kk][j], acc[i][j]);
+    // the phase's MFMAs stay ahead of its closing wait and barrier
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto lgkm0 = []() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+
+  // ------------------------------------------------------------ K loop
+  // prologue: steps 0 and 1 in flight, this wave's share of step 0 landed
+  dma(0, 0);
+  dma(1, 1);
+  vm_wait<ND>();
+  pp_barrier();
+  if (grp == 0) {
+    rd(0);
+    lgkm0();
+    pp_barrier();
+    for (int s = 0; s < nk; ++s) {
+      comp();              // step s
+      wait_vmem();         // own share of step s+1 (issued one phase ago)
+      pp_barrier();
+      dma(s + 2, s & 1);   // step s's stage: both groups are done reading it
+      if (s + 1 < nk) rd((s + 1) & 1);
+      lgkm0();
+      pp_barrier();
+    }
+  } else {
+    pp_barrier();
+    for (int s = 0; s < nk; ++s) {
+      rd(s & 1);
+      lgkm0();             // reads of the stage done before it is refilled
+      dma(s + 2, s & 1);
+      vm_wait<ND>();       // own share of step s+1
+      pp_barrier();
+      comp();              // step s
+      pp_barrier();
+    }
+  }
+  wait_vmem();
+  __syncthreads();         // stages free for the epilogue
+
+  // ------------------------------------------------ LoRA epilogue pass
+  // acc += S . E^T with K = rs: S = s (A_op SIDE^T) [M x rs], E [N x rs]
+  const int rs = p.rs;
+  for (int kq = 0; kq < rs / 16; ++kq) {
+    u32x4 ea[2], hb[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int64_t erow;
+      bool ok;
+      if constexpr (GU) {
+        const int j = tn * 128 + wn * 32 + l32;
+        ok = j < p.gu_f;
+        erow = (i ? p.gu_f : 0) + j;
+      } else {
+        const int n = n0 + wn * 64 + i * 32 + l32;
+        ok = n < N;
+        erow = n;
+      }
+      u32x4 v = {0, 0, 0, 0};
+      if (ok) v = gload16(p.epi + erow * rs + kq * 16 + 8 * hi32);
+      ea[i] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 128 + j * 32 + l32;
+      u32x4 v = {0, 0, 0, 0};
+      if (m < M) v = gload16(p.hglob + (int64_t)m * rs + kq * 16 + 8 * hi32);
+      hb[j] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(ea[i], hb[j], acc[i][j]);
+  }
+
+  // ------------------------------------------------ output
+  // A lane holds 4 consecutive output columns of one token row per MFMA
+  // block.  Each wave passes its 128 x 64 sub-tile through a private 16 KB
+  // LDS region, 64 token rows (fp32) at a time, then reads and writes global
+  // memory in 16-byte pieces along rows.  Region row r (0..63) is 256 bytes;
+  // 16-byte chunk c (columns 4c .. 4c+3) sits at chunk c ^ (r % 16).
+  char *reg = smem + wave * 16384;
+  auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); };
+  // SwiGLU backward: a half's saved e, g are all requested before the half
+  // is staged
+  u32x4 ein[8], gin[8];
+  auto load_eg = [&](int half) {
+    if constexpr (EPI == EPI_SWIGLU_BWD) {
+      const int q = lane & 7, n = n0 + wn * 64 + 8 * q;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int m = m0 + wm * 128 + half * 64 + it * 8 + (lane >> 3);
+        u32x4 e = {0, 0, 0, 0}, g = {0, 0, 0, 0};
+        if (m < M && n < N) {
+          const int64_t off = (int64_t)m * N + n;
+          e = gload16(p.Ein + off);
+          g = gload16(p.Gin + off);
+        }
+        ein[it] = e;
+        gin[it] = g;
+      }
+    }
+  };
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    load_eg(half);
+    // region rows jj * 32 + l32 hold token block j = 2 half + jj
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16 &a = acc[i][2 * half + jj];
+          const u32x4 v = {__float_as_uint(a[4 * g]), __float_as_uint(a[4 * g + 1]),
+                           __float_as_uint(a[4 * g + 2]), __float_as_uint(a[4 * g + 3])};
+          lds_write16(reg, ep_off(jj * 32 + l32, 8 * i + 2 * g + hi32), v);
+        }
+    lgkm0();
+    __builtin_amdgcn_wave_barrier();
+    const int mrow0 = m0 + wm * 128 + half * 64;   // token of region row 0
+    if constexpr (GU) {
+      // region columns 0..31: gate, 32..63: up, features tn*128 + wn*32 + c
+      const int f = p.gu_f;
+      const int q = lane & 3;                       // 8-feature group
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 16 + (lane >> 2);
+        const int m = mrow0 + r;
+        const int jf = tn * 128 + wn * 32 + 8 * q;
+        const u32x4 e0 = lds_read16(reg, ep_off(r, 2 * q)), e1 = lds_read16(reg, ep_off(r, 2 * q + 1));
+        const u32x4 g0 = lds_read16(reg, ep_off(r, 8 + 2 * q)), g1 = lds_read16(reg, ep_off(r, 9 + 2 * q));
+        if (m < M && jf < f) {
+          const float ev[8] = {__uint_as_float(e0[0]), __uint_as_float(e0[1]), __uint_as_float(e0[2]),
+                               __uint_as_float(e0[3]), __uint_as_float(e1[0]), __uint_as_float(e1[1]),
+                               __uint_as_float(e1[2]), __uint_as_float(e1[3])};
+          const float gv[8] = {__uint_as_float(g0[0]), __uint_as_float(g0[1]), __uint_as_float(g0[2]),
+                               __uint_as_float(g0[3]), __uint_as_float(g1[0]), __uint_as_float(g1[1]),
+                               __uint_as_float(g1[2]), __uint_as_float(g1[3])};
+          u32x4 ew, gw, hw;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            ew[t] = pack_bf16x2(ev[2 * t], ev[2 * t + 1]);
+            gw[t] = pack_bf16x2(gv[2 * t], gv[2 * t + 1]);
+            // h from the rounded e, g: the same values the backward reloads
+            const float ea = bf16lo(ew[t]), eb = bf16hi(ew[t]);
+            const float ga = bf16lo(gw[t]), gb = bf16hi(gw[t]);
+            hw[t] = pack_bf16x2(ea * sigmoidf_fast(ea) * ga, eb * sigmoidf_fast(eb) * gb);
+          }
+          const int64_t off = (int64_t)m * f + jf;
+          gstore16(p.E + off, ew);
+          gstore16(p.G + off, gw);
+          gstore16(p.H + off, hw);
+        }
+      }
+    } else {
+      const int q = lane & 7;                       // 8-column group
+      const int n = n0 + wn * 64 + 8 * q;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int m = mrow0 + r;
+        const u32x4 a0 = lds_read16(reg, ep_off(r, 2 * q)), a1 = lds_read16(reg, ep_off(r, 2 * q + 1));
+        if (m >= M || n >= N) continue;
+        float v[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
+                      __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
+                      __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+        if constexpr (EPI == EPI_STORE) {
+          bf16_t *cb = p.C;
+          int64_t ldc = p.ldc;
+          int ncs = 0;
+          if (p.nseg1 > 0 && n0 >= p.nseg1) {
+            const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
+            cb = s2 ? p.C2 : p.C1;
+            ldc = s2 ? p.ldc2 : p.ldc1;
+            ncs = s2 ? p.nseg2 : p.nseg1;
+          }
+          bf16_t *dst = cb + (int64_t)m * ldc + (n - ncs);
+          if (p.accumulate) {
+            const u32x4 o = gload16(dst);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              v[2 * t] += bf16lo(o[t]);
+              v[2 * t + 1] += bf16hi(o[t]);
+            }
+          }
+          u32x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
+          gstore16(dst, w);
+        } else {  // EPI_SWIGLU_BWD: v = dh
+          const int64_t off = (int64_t)m * N + n;
+          const u32x4 ev = ein[it], gv = gin[it];
+          u32x4 dew, dgw;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float de[2], dg[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
+              const float gg = h2 ? bf16hi(gv[t]) : bf16lo(gv[t]);
+              const float dh = v[2 * t + h2];
+              const float sg = sigmoidf_fast(e);
+              dg[h2] = dh * e * sg;
+              de[h2] = dh * gg * sg * (1.0f + e * (1.0f - sg));
+            }
+            dew[t] = pack_bf16x2(de[0], de[1]);
+            dgw[t] = pack_bf16x2(dg[0], dg[1]);
+          }
+          gstore16(p.DE + off, dew);
+          gstore16(p.DG + off, dgw);
+        }
+      }
+    }
+    lgkm0();
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace lora
