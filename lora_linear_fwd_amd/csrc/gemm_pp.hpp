@@ -16,7 +16,7 @@
 // sub-tile: 128 fp32 accumulators per lane, 96 registers of fragments.
 //
 // Phase schedule (step s lives in LDS stage s % 2):
-//   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: DMA share of step s+1, read s
+//   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: read s, DMA share of step s+1
 //   G1:   --     | M0 | C0 | M1 | C1 ...   Ms: read s, then DMA share of s+2
 // A stage is refilled only after both groups have read it; each group waits
 // for its own share of a step before the barrier that precedes the first
@@ -166,8 +166,10 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       comp();              // step s
       wait_vmem();         // own share of step s+1 (issued one phase ago)
       pp_barrier();
-      dma(s + 2, s & 1);   // step s's stage: both groups are done reading it
+      // fragment reads first (measured ~1 % faster than DMA first), then
+      // step s's stage refilled: both groups are done reading it
       if (s + 1 < nk) rd((s + 1) & 1);
+      dma(s + 2, s & 1);
       lgkm0();
       pp_barrier();
     }
