@@ -25,6 +25,12 @@
 // Gate/up tiles (SwiGLU forward) interleave weight rows in 32-row blocks,
 // [32 gate | 32 up] per 64 tile rows, so every wave's 64 columns hold the
 // gate and up values of the same 32 features.
+//
+// NN = true: the weight operand is W as stored, [K x N] with N contiguous
+// (backward dX = dY W without a transposed copy).  Its LDS tile keeps that
+// layout, [64 K-rows x 256 columns], and the MFMA fragments are read with
+// the LDS transpose read ds_read_b64_tr_b16 (two per 32-column block and
+// 16-K sub-step).  K rows >= ksplit come from the second weight (B1).
 #pragma once
 #include "gemm_lora.hpp"
 
@@ -40,10 +46,11 @@ __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int EPI>
+template <int EPI, bool NN = false>
 __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
+  static_assert(!(NN && GU), "the gate/up forward reads its weights K-contiguous");
   constexpr int BK = 64, XS = BM * BK * 2, STAGE = 2 * XS;
   constexpr int NU = 4;        // 1-KB DMA instructions per wave, operand tile and K step
   constexpr int ND = 2 * NU;   // per wave and K step
@@ -66,8 +73,11 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A0 + (int64_t)m0 * p.lda, kMaxRecords);
   // A1 - A0 - 2 ksplit: added to offsets of columns >= ksplit
   const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
-  __amdgpu_buffer_rsrc_t rsB;
-  if constexpr (GU) {
+  __amdgpu_buffer_rsrc_t rsB, rsB1;
+  if constexpr (NN) {
+    rsB = make_rsrc(p.B0 + n0, kMaxRecords);
+    rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
+  } else if constexpr (GU) {
     // tile rows 8b.. are up-projection rows when (8b / 32) is odd, which for
     // b = w + 8u is the wave's group: group 0 loads gate rows, group 1 up rows
     rsB = make_rsrc((grp ? p.B1 : p.B0) + (int64_t)tn * 128 * p.ldb, kMaxRecords);
@@ -89,7 +99,14 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     const int c = (lane & 7) ^ (int)kc_swz<BK>(row);
     kcol[u] = 8 * c;
     aoff[u] = (m0 + row < M) ? (uint32_t)(row * p.lda * 2 + c * 16) : kOOB;
-    if constexpr (GU) {
+    if constexpr (NN) {
+      // K rows 2b, 2b+1 (b = w + 8u) of the [64 x 256] weight tile: lane l
+      // lands in row 2b + l/32 at physical chunk l%32, holding columns
+      // 8c .. 8c+7 with c = (l%32) ^ 4 (row%4)
+      const int krow = 2 * (wave + 8 * u) + (lane >> 5);
+      const int cn = (lane & 31) ^ ((krow & 3) << 2);
+      boff[u] = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + cn * 16) : kOOB;
+    } else if constexpr (GU) {
       const int jl = (row >> 6) * 32 + (row & 31);   // feature within the tile
       boff[u] = (tn * 128 + jl < p.gu_f) ? (uint32_t)(jl * p.ldb * 2 + c * 16) : kOOB;
     } else {
@@ -113,21 +130,49 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int col = k0 + kcol[u];
-      const bool ok = live && col < K && boff[u] != kOOB;
-      dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff[u] + 2u * (uint32_t)k0 : kOOB, 0);
+      if constexpr (NN) {
+        const int b = wave + 8 * u;
+        const int kr = k0 + 2 * b;          // first of the two K rows (even)
+        const bool second = kr >= ksplit;   // ksplit is even: no straddle
+        const bool ok = live && kr + (lane >> 5) < K && boff[u] != kOOB;
+        dma16(second ? rsB1 : rsB, Ws + b * 1024, ok ? boff[u] : kOOB,
+              live ? (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2) : 0u);
+      } else {
+        const int col = k0 + kcol[u];
+        const bool ok = live && col < K && boff[u] != kOOB;
+        dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff[u] + 2u * (uint32_t)k0 : kOOB, 0);
+      }
     }
   };
 
   // ---------------------------------------------------- fragments, MFMAs
+  // NN: byte offset of this lane's transpose-read row for column block i at
+  // K sub-step 0 (rows kk*16 and kk*16 + 4 are reached with immediates)
+  uint32_t trb[2];
+  if constexpr (NN) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int krow0 = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int nl = wn * 64 + i * 32 + 16 * (g & 1) + 4 * (sl & 3);
+      trb[i] = nn_off(krow0, nl >> 3) + ((nl >> 2) & 1) * 8;
+    }
+  }
   u32x4 fw[4][2], ft[4][4];   // [16-K sub-step][32-row block]: weight rows, tokens
   auto rd = [&](int stg) {
     const char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (NN) {
+          const u32x2 lo = lds_read_tr8(Ws, trb[i] + kk * 16 * 512);
+          const u32x2 hi = lds_read_tr8(Ws, trb[i] + (kk * 16 + 4) * 512);
+          fw[kk][i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));
