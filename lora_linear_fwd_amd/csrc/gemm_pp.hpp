@@ -233,49 +233,6 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   wait_vmem();
   __syncthreads();         // stages free for the epilogue
 
-  // ------------------------------------------------ LoRA epilogue pass
-  // acc += S . E^T with K = rs: S = s (A_op SIDE^T) [M x rs], E [N x rs]
-  const int rs = p.rs;
-  for (int kq = 0; kq < rs / 16; ++kq) {
-    u32x4 ea[2], hb[4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int64_t erow;
-      bool ok;
-      if constexpr (GU) {
-        const int j = tn * 128 + wn * 32 + l32;
-        ok = j < p.gu_f;
-        erow = (i ? p.gu_f : 0) + j;
-      } else {
-        const int n = n0 + wn * 64 + i * 32 + l32;
-        ok = n < N;
-        erow = n;
-      }
-      u32x4 v = {0, 0, 0, 0};
-      if (ok) v = gload16(p.epi + erow * rs + kq * 16 + 8 * hi32);
-      ea[i] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 128 + j * 32 + l32;
-      u32x4 v = {0, 0, 0, 0};
-      if (m < M) v = gload16(p.hglob + (int64_t)m * rs + kq * 16 + 8 * hi32);
-      hb[j] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(ea[i], hb[j], acc[i][j]);
-  }
-
-  // ------------------------------------------------ output
-  // A lane holds 4 consecutive output columns of one token row per MFMA
-  // block.  Each wave passes its 128 x 64 sub-tile through a private 16 KB
-  // LDS region, 64 token rows (fp32) at a time, then reads and writes global
-  // memory in 16-byte pieces along rows.  Region row r (0..63) is 256 bytes;
-  // 16-byte chunk c (columns 4c .. 4c+3) sits at chunk c ^ (r % 16).
-  char *reg = smem + wave * 16384;
-  auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); };
   // SwiGLU backward: a half's saved e, g are all requested before the half
   // is staged
   u32x4 ein[8], gin[8];
@@ -296,6 +253,61 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       }
     }
   };
+  // ------------------------------------------------ LoRA epilogue pass
+  // acc += S . E^T with K = rs: S = s (A_op SIDE^T) [M x rs], E [N x rs]
+  // Two 16-column slices per round trip: every load of the pair is issued
+  // before its MFMAs (the fragment registers are free by now).
+  const int rs = p.rs, nq = rs / 16;
+  for (int kq0 = 0; kq0 < nq; kq0 += 2) {
+    u32x4 ea[2][2], hb[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kq = kq0 + h;
+      const bool qok = kq < nq;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int64_t erow;
+        bool ok;
+        if constexpr (GU) {
+          const int j = tn * 128 + wn * 32 + l32;
+          ok = j < p.gu_f;
+          erow = (i ? p.gu_f : 0) + j;
+        } else {
+          const int n = n0 + wn * 64 + i * 32 + l32;
+          ok = n < N;
+          erow = n;
+        }
+        u32x4 v = {0, 0, 0, 0};
+        if (ok && qok) v = gload16(p.epi + erow * rs + kq * 16 + 8 * hi32);
+        ea[h][i] = v;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + wm * 128 + j * 32 + l32;
+        u32x4 v = {0, 0, 0, 0};
+        if (m < M && qok) v = gload16(p.hglob + (int64_t)m * rs + kq * 16 + 8 * hi32);
+        hb[h][j] = v;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (kq0 + h < nq) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(ea[h][i], hb[h][j], acc[i][j]);
+      }
+    }
+  }
+
+  // ------------------------------------------------ output
+  // A lane holds 4 consecutive output columns of one token row per MFMA
+  // block.  Each wave passes its 128 x 64 sub-tile through a private 16 KB
+  // LDS region, 64 token rows (fp32) at a time, then reads and writes global
+  // memory in 16-byte pieces along rows.  Region row r (0..63) is 256 bytes;
+  // 16-byte chunk c (columns 4c .. 4c+3) sits at chunk c ^ (r % 16).
+  char *reg = smem + wave * 16384;
+  auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); };
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     load_eg(half);
