@@ -7,8 +7,8 @@
 // groups alternate between
 //   a compute phase: 32 back-to-back MFMA 32x32x16 on one K step (64) of
 //     fragments already in registers, and
-//   a memory phase: the LDS-DMA of its share of a later K step and the LDS
-//     fragment reads of its next K step,
+//   a memory phase: the LDS fragment reads of its next K step (and group
+//     0's share of the LDS-DMA of a later K step),
 // with a workgroup barrier between phases, so that while one wave of a SIMD
 // waits on its vector-memory issue the other keeps the matrix core busy.
 // With one wave per SIMD (the four-wave form) those stalls sit between the
@@ -16,21 +16,22 @@
 // sub-tile: 128 fp32 accumulators per lane, 96 registers of fragments.
 //
 // Phase schedule (step s lives in LDS stage s % 2):
-//   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: read s, DMA share of step s+1
-//   G1:   --     | M0 | C0 | M1 | C1 ...   Ms: read s, then DMA share of s+2
-// A stage is refilled only after both groups have read it; each group waits
-// for its own share of a step before the barrier that precedes the first
-// read of that step.
+//   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: read s, then DMA share of s+1
+//   G1:   --     | M0 | C0 | M1 | C1 ...   Cs: MFMAs, DMA share of s+2 among them
+// A stage is refilled only in a phase opened by a barrier that every reader
+// of its previous step had passed with its reads complete: group 0 in its
+// memory phase (its own reads there target the other stage), group 1 in its
+// compute phase.  (A group-1 wave refilling the stage it had
+// just read, inside the same phase, raced with the other group-1 waves still
+// reading it: rare stale fragments, measured.)  Each group drains its loads
+// (vmcnt 0) before the barrier that precedes their first read: group 0 at
+// the end of its next compute phase, group 1 at the end of its next memory
+// phase.
 //
 // Gate/up tiles (SwiGLU forward) interleave weight rows in 32-row blocks,
 // [32 gate | 32 up] per 64 tile rows, so every wave's 64 columns hold the
 // gate and up values of the same 32 features.
-//
-// NN = true: the weight operand is W as stored, [K x N] with N contiguous
-// (backward dX = dY W without a transposed copy).  Its LDS tile keeps that
-// layout, [64 K-rows x 256 columns], and the MFMA fragments are read with
-// the LDS transpose read ds_read_b64_tr_b16 (two per 32-column block and
-// 16-K sub-step).  K rows >= ksplit come from the second weight (B1).
+
 #pragma once
 #include "gemm_lora.hpp"
 
@@ -46,14 +47,11 @@ __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int EPI, bool NN = false>
+template <int EPI>
 __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
-  static_assert(!(NN && GU), "the gate/up forward reads its weights K-contiguous");
   constexpr int BK = 64, XS = BM * BK * 2, STAGE = 2 * XS;
-  constexpr int NU = 4;        // 1-KB DMA instructions per wave, operand tile and K step
-  constexpr int ND = 2 * NU;   // per wave and K step
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -67,20 +65,33 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   const int M = p.M, N = p.N, K = p.K, ksplit = p.ksplit;
 
   // ---------------------------------------------------- DMA lane geometry
-  // Instruction u of wave w fills rows 8b .. 8b+7 (b = w + 8u) of an operand
-  // tile; lane l lands in row 8b + l/8 at physical chunk l%8, which holds
-  // logical chunk c = (l%8) ^ swz(row), i.e. K columns 8c .. 8c+7.
+  // Every wave loads its share of a K step: instruction u (0..3) of wave w
+  // fills tile rows 8b .. 8b+7 with b = w + 8u; lane l lands in row
+  // r0 + 64u (r0 = 8w + l/8) at physical chunk l%8, which holds logical chunk
+  // c = (l%8) ^ swz(row), i.e. K columns 8c .. 8c+7.  swz(row) = (row/2) % 8
+  // does not depend on u, so neither does c.
+  constexpr int NI = 4;
+  const int r0 = 8 * wave + (lane >> 3);
+  const int cA = (lane & 7) ^ (int)kc_swz<BK>(r0);
+  const int kcol = 8 * cA;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A0 + (int64_t)m0 * p.lda, kMaxRecords);
   // A1 - A0 - 2 ksplit: added to offsets of columns >= ksplit
   const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
-  __amdgpu_buffer_rsrc_t rsB, rsB1;
-  if constexpr (NN) {
-    rsB = make_rsrc(p.B0 + n0, kMaxRecords);
-    rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
-  } else if constexpr (GU) {
-    // tile rows 8b.. are up-projection rows when (8b / 32) is odd, which for
-    // b = w + 8u is the wave's group: group 0 loads gate rows, group 1 up rows
+  const uint32_t aoff0 = (uint32_t)(r0 * p.lda * 2 + cA * 16);
+  const uint32_t astep = (uint32_t)(64 * p.lda * 2);   // 64 tile rows
+  const int arem = M - m0 - r0;                         // instruction u valid if 64u < arem
+  __amdgpu_buffer_rsrc_t rsB;
+  uint32_t boff0, bstep;
+  int brem, bunit;
+  if constexpr (GU) {
+    // tile row r0 + 64u is feature 32u + (r0 % 32) of the tile, of the gate
+    // weight for r0 < 32 (group 0) and of the up weight otherwise (group 1)
+    const int jl = r0 & 31;
     rsB = make_rsrc((grp ? p.B1 : p.B0) + (int64_t)tn * 128 * p.ldb, kMaxRecords);
+    boff0 = (uint32_t)(jl * p.ldb * 2 + cA * 16);
+    bstep = (uint32_t)(32 * p.ldb * 2);
+    brem = p.gu_f - tn * 128 - jl;
+    bunit = 32;
   } else {
     const bf16_t *bseg = p.B0;
     int nsb = 0;
@@ -90,89 +101,41 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       nsb = s2 ? p.nseg2 : p.nseg1;
     }
     rsB = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
-  }
-  uint32_t aoff[NU], boff[NU];
-  int kcol[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int row = 8 * (wave + 8 * u) + (lane >> 3);
-    const int c = (lane & 7) ^ (int)kc_swz<BK>(row);
-    kcol[u] = 8 * c;
-    aoff[u] = (m0 + row < M) ? (uint32_t)(row * p.lda * 2 + c * 16) : kOOB;
-    if constexpr (NN) {
-      // K rows 2b, 2b+1 (b = w + 8u) of the [64 x 256] weight tile: lane l
-      // lands in row 2b + l/32 at physical chunk l%32, holding columns
-      // 8c .. 8c+7 with c = (l%32) ^ 4 (row%4)
-      const int krow = 2 * (wave + 8 * u) + (lane >> 5);
-      const int cn = (lane & 31) ^ ((krow & 3) << 2);
-      boff[u] = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + cn * 16) : kOOB;
-    } else if constexpr (GU) {
-      const int jl = (row >> 6) * 32 + (row & 31);   // feature within the tile
-      boff[u] = (tn * 128 + jl < p.gu_f) ? (uint32_t)(jl * p.ldb * 2 + c * 16) : kOOB;
-    } else {
-      boff[u] = (n0 + row < N) ? (uint32_t)(row * p.ldb * 2 + c * 16) : kOOB;
-    }
+    boff0 = (uint32_t)(r0 * p.ldb * 2 + cA * 16);
+    bstep = (uint32_t)(64 * p.ldb * 2);
+    brem = N - n0 - r0;
+    bunit = 64;
   }
   const int nk = (K + BK - 1) / BK;
-  // This wave's share of K step kt into a stage.  Every call issues ND
-  // loads (lanes past M, N or K, and steps past the end, read zeros), so the
-  // per-wave count of outstanding loads is the same at every wait.
+  // This wave's share of K step kt (< nk) into a stage: 8 loads; lanes past
+  // M, N or K read zeros.  No load is issued for steps past the end.
   auto dma = [&](int kt, int stg) {
     char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
     const int k0 = kt * BK;
-    const bool live = kt < nk;
+    const int col = k0 + kcol;
+    const bool kin = col < K;
+    const uint32_t ka = 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int col = k0 + kcol[u];
-      const bool ok = live && col < K && aoff[u] != kOOB;
-      const uint32_t v = ok ? aoff[u] + 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u) : kOOB;
-      dma16(rsA, Xs + (wave + 8 * u) * 1024, v, 0);
+    for (int u = 0; u < NI; ++u) {
+      const bool ok = kin && 64 * u < arem;
+      dma16(rsA, Xs + (wave + 8 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
     }
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if constexpr (NN) {
-        const int b = wave + 8 * u;
-        const int kr = k0 + 2 * b;          // first of the two K rows (even)
-        const bool second = kr >= ksplit;   // ksplit is even: no straddle
-        const bool ok = live && kr + (lane >> 5) < K && boff[u] != kOOB;
-        dma16(second ? rsB1 : rsB, Ws + b * 1024, ok ? boff[u] : kOOB,
-              live ? (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2) : 0u);
-      } else {
-        const int col = k0 + kcol[u];
-        const bool ok = live && col < K && boff[u] != kOOB;
-        dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff[u] + 2u * (uint32_t)k0 : kOOB, 0);
-      }
+    for (int u = 0; u < NI; ++u) {
+      const bool ok = kin && bunit * u < brem;
+      dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff0 + (uint32_t)u * bstep + 2u * (uint32_t)k0 : kOOB, 0);
     }
   };
 
   // ---------------------------------------------------- fragments, MFMAs
-  // NN: byte offset of this lane's transpose-read row for column block i at
-  // K sub-step 0 (rows kk*16 and kk*16 + 4 are reached with immediates)
-  uint32_t trb[2];
-  if constexpr (NN) {
-    const int g = lane >> 4, sl = lane & 15;
-    const int krow0 = 8 * (g >> 1) + (sl >> 2);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int nl = wn * 64 + i * 32 + 16 * (g & 1) + 4 * (sl & 3);
-      trb[i] = nn_off(krow0, nl >> 3) + ((nl >> 2) & 1) * 8;
-    }
-  }
   u32x4 fw[4][2], ft[4][4];   // [16-K sub-step][32-row block]: weight rows, tokens
   auto rd = [&](int stg) {
     const char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if constexpr (NN) {
-          const u32x2 lo = lds_read_tr8(Ws, trb[i] + kk * 16 * 512);
-          const u32x2 hi = lds_read_tr8(Ws, trb[i] + (kk * 16 + 4) * 512);
-          fw[kk][i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
-        }
-      }
+      for (int i = 0; i < 2; ++i)
+        fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));
@@ -185,23 +148,39 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  auto comp = [&]() {
+  auto mfma_step = [&]() {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fw[kk][i], ft[kk][j], acc[i][j]);
+  };
+  auto comp = [&]() {
+    mfma_step();
     // the phase's MFMAs stay ahead of its closing wait and barrier
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // group 1's compute phase with its DMA share of K step kt: one load after
+  // every two of the first 16 MFMAs
+  auto comp_dma = [&](int kt, int stg) {
+    dma(kt, stg);
+    mfma_step();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto lgkm0 = []() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
 
   // ------------------------------------------------------------ K loop
-  // prologue: steps 0 and 1 in flight, this wave's share of step 0 landed
+  // prologue: steps 0 and 1
   dma(0, 0);
-  dma(1, 1);
-  vm_wait<ND>();
+  if (nk > 1) dma(1, 1);
+  wait_vmem();
   pp_barrier();
   if (grp == 0) {
     rd(0);
@@ -211,22 +190,33 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       comp();              // step s
       wait_vmem();         // own share of step s+1 (issued one phase ago)
       pp_barrier();
-      // fragment reads first (measured ~1 % faster than DMA first), then
-      // step s's stage refilled: both groups are done reading it
+      // fragment reads first, then step s's stage refilled: every wave
+      // finished reading it before the last two barriers
       if (s + 1 < nk) rd((s + 1) & 1);
-      dma(s + 2, s & 1);
+      if (s + 2 < nk) dma(s + 2, s & 1);
       lgkm0();
       pp_barrier();
     }
   } else {
     pp_barrier();
-    for (int s = 0; s < nk; ++s) {
+    // step s's stage is refilled in the compute phase, once every group-1
+    // wave is done reading it; the loads are drained at the end of the next
+    // memory phase (own share of step s+1, issued one phase before)
+    int s = 0;
+    for (; s + 2 < nk; ++s) {
       rd(s & 1);
-      lgkm0();             // reads of the stage done before it is refilled
-      dma(s + 2, s & 1);
-      vm_wait<ND>();       // own share of step s+1
+      lgkm0();
+      wait_vmem();
       pp_barrier();
-      comp();              // step s
+      comp_dma(s + 2, s & 1);   // step s
+      pp_barrier();
+    }
+    for (; s < nk; ++s) {
+      rd(s & 1);
+      lgkm0();
+      wait_vmem();
+      pp_barrier();
+      comp();
       pp_barrier();
     }
   }
