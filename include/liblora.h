@@ -46,13 +46,15 @@
  *   - `ws`/`ws_bytes`: caller-provided device workspace of at least
  *     lora_workspace_bytes(op | LORA_WS_MINIMAL, ...) bytes (may be NULL
  *     when that is 0).  The size picks the strategy (bf16 path):
- *       >= lora_workspace_bytes(op, ...): the frozen base weight is first
- *         copied into the workspace in the form the GEMM reads fastest
- *         (transposed for the backward dX products, decoded to bf16 for
- *         4-bit weights) and every GEMM reads it K-contiguous;
- *       otherwise (minimal): no weight copy; the backward GEMMs read W in
- *         place (row-major [n x k] as the B operand of dY W) and 4-bit
- *         codes are decoded inside the GEMM while its LDS tiles fill.
+ *       >= lora_workspace_bytes(op, ...): a 4-bit base weight is first
+ *         decoded to bf16 into the workspace (transposed for the backward
+ *         dX products) and the GEMMs read the copy; the fused q/k/v
+ *         backward also copies dense weights (stacked, transposed);
+ *       otherwise (minimal): no weight copy; 4-bit codes are decoded
+ *         inside the GEMM while its LDS tiles fill.
+ *     Dense weights are read in place by both strategies (the backward
+ *     GEMMs take W row-major [n x k] as the B operand of dY W), so for
+ *     them the two sizes are equal except for the fused q/k/v backward.
  *     Both give results within the same tolerance of the exact product
  *     (fp32 accumulation in a different summation order).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are

@@ -600,9 +600,10 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, 
   if (T < 0 || kd <= 0 || nf <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
   if (dtype == LORA_F32) return plan_f32(op, T, kd, nf, r);
   if (dtype != LORA_BF16) return 0;
-  // forwards copy only 4-bit weights (decoded); backwards copy every weight
-  // (transposed, decoded if 4-bit)
-  const bool fwd_copy = !minimal && wfmt != LORA_W_DENSE, bwd_copy = !minimal;
+  // only 4-bit weights are copied: decoded for the forwards, decoded and
+  // transposed for the backwards (dense weights are read in place: the NN
+  // GEMM on W as stored is as fast as a transposed copy plus the NT GEMM)
+  const bool fwd_copy = !minimal && wfmt != LORA_W_DENSE, bwd_copy = fwd_copy;
   switch (op) {
     case LORA_OP_LINEAR_FWD: return plan_lin_fwd(T, kd, nf, r, fwd_copy).total;
     case LORA_OP_LINEAR_BWD: return plan_lin_bwd(T, kd, nf, r, bwd_copy).total;
@@ -680,7 +681,8 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
                        (const float *)B, (const float *)dY, (float *)dX, acc, (float *)dA,
                        (float *)dB, G, H, st);
   }
-  const LinBwdPlan pl = plan_lin_bwd(T, k, n, r, fast);
+  const bool wcopy = fast && wv.q4;   // the plan holds a decoded, transposed copy
+  const LinBwdPlan pl = plan_lin_bwd(T, k, n, r, wcopy);
   const int RS = rs_of(r);
   bf16_t *side_nn = (bf16_t *)(w + pl.side_nn), *epi_nn = (bf16_t *)(w + pl.epi_nn);
   bf16_t *side_nt = (bf16_t *)(w + pl.side_nt);
@@ -702,7 +704,7 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
       a.M = (int)T; a.N = (int)k; a.K = (int)n; a.ksplit = (int)n;
       a.A0 = a.A1 = dYb; a.lda = n;
       bool nn = true, q4 = wv.q4;
-      if (fast) {   // W^T [k x n]: the NT GEMM reads it K-contiguous
+      if (wcopy) {   // decoded W^T [k x n]: the NT GEMM reads it K-contiguous
         bf16_t *wt = (bf16_t *)(w + pl.wbuf);
         LORA_TRY(transpose_w(wt, n, wv, n, k, st));
         const WeightView tv = dense_view(wt);
@@ -862,7 +864,10 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
                        st);
   }
 
-  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r, fast);
+  // 4-bit gate/up weights (the format the workspace was sized for): a decoded,
+  // transposed copy per dX GEMM; dense weights are read in place (NN GEMM)
+  const bool wcopy = fast && wg.q4;
+  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r, wcopy);
   bf16_t *wt = (bf16_t *)(w + pl.wbuf);
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   bf16_t *de = (bf16_t *)(w + pl.de), *dg = (bf16_t *)(w + pl.dg);
@@ -906,7 +911,7 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     a.M = (int)T; a.N = (int)f; a.K = (int)d; a.ksplit = (int)d;
     a.A0 = a.A1 = dYb; a.lda = d;
     bool nn = true, q4 = wd.q4;
-    if (fast) {   // Wd^T [f x d]
+    if (wcopy && wd.q4) {   // decoded Wd^T [f x d]
       LORA_TRY(transpose_w(wt, d, wd, d, f, st));
       const WeightView tv = dense_view(wt);
       set_b(a, tv, tv); a.ldb = d;
@@ -964,7 +969,7 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     b.M = (int)T; b.N = (int)d; b.K = (int)(2 * f); b.ksplit = (int)f;
     b.A0 = de; b.A1 = dg; b.lda = f;
     bool nn = true, q4 = wg.q4;
-    if (fast) {   // [Wg^T | Wu^T] [d x 2f], over Wd^T (its GEMM is done)
+    if (wcopy) {   // decoded [Wg^T | Wu^T] [d x 2f], over Wd^T (its GEMM is done)
       LORA_TRY(transpose_w(wt, 2 * f, wg, f, d, st));
       LORA_TRY(transpose_w(wt + f, 2 * f, wu, f, d, st));
       const WeightView tv = dense_view(wt);

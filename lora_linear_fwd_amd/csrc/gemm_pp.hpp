@@ -31,6 +31,12 @@
 // Gate/up tiles (SwiGLU forward) interleave weight rows in 32-row blocks,
 // [32 gate | 32 up] per 64 tile rows, so every wave's 64 columns hold the
 // gate and up values of the same 32 features.
+//
+// NN = true: the weight operand is W as stored, [K x N] with N contiguous
+// (backward dX = dY W without a transposed copy).  Its LDS tile keeps that
+// layout, [64 K-rows x 256 columns], and the MFMA fragments are read with
+// the LDS transpose read ds_read_b64_tr_b16 (two per 32-column block and
+// 16-K sub-step).  K rows >= ksplit come from the second weight (B1).
 
 #pragma once
 #include "gemm_lora.hpp"
@@ -47,10 +53,11 @@ __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int EPI>
+template <int EPI, bool NN = false>
 __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
+  static_assert(!(NN && GU), "the gate/up forward reads its weights K-contiguous");
   constexpr int BK = 64, XS = BM * BK * 2, STAGE = 2 * XS;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -80,14 +87,26 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   const uint32_t aoff0 = (uint32_t)(r0 * p.lda * 2 + cA * 16);
   const uint32_t astep = (uint32_t)(64 * p.lda * 2);   // 64 tile rows
   const int arem = M - m0 - r0;                         // instruction u valid if 64u < arem
-  __amdgpu_buffer_rsrc_t rsB;
+  __amdgpu_buffer_rsrc_t rsB, rsB1;
   uint32_t boff0, bstep;
   int brem, bunit;
-  if constexpr (GU) {
+  if constexpr (NN) {
+    // K rows 2b, 2b+1 (b = w + 8u) of the [64 x 256] weight tile: lane l
+    // lands in row 2b + l/32 at physical chunk l%32, holding columns
+    // 8c .. 8c+7 with c = (l%32) ^ 4 (row%4); row%4 does not depend on u
+    const int krow = 2 * wave + (lane >> 5);
+    const int cn = (lane & 31) ^ ((krow & 3) << 2);
+    rsB = make_rsrc(p.B0 + n0, kMaxRecords);
+    rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
+    boff0 = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + cn * 16) : kOOB;
+    bstep = 0;
+    brem = 0;
+    bunit = 0;
+  } else if constexpr (GU) {
     // tile row r0 + 64u is feature 32u + (r0 % 32) of the tile, of the gate
     // weight for r0 < 32 (group 0) and of the up weight otherwise (group 1)
     const int jl = r0 & 31;
-    rsB = make_rsrc((grp ? p.B1 : p.B0) + (int64_t)tn * 128 * p.ldb, kMaxRecords);
+    rsB = rsB1 = make_rsrc((grp ? p.B1 : p.B0) + (int64_t)tn * 128 * p.ldb, kMaxRecords);
     boff0 = (uint32_t)(jl * p.ldb * 2 + cA * 16);
     bstep = (uint32_t)(32 * p.ldb * 2);
     brem = p.gu_f - tn * 128 - jl;
@@ -100,7 +119,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       bseg = s2 ? p.B2 : p.B1;
       nsb = s2 ? p.nseg2 : p.nseg1;
     }
-    rsB = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
+    rsB = rsB1 = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
     boff0 = (uint32_t)(r0 * p.ldb * 2 + cA * 16);
     bstep = (uint32_t)(64 * p.ldb * 2);
     brem = N - n0 - r0;
@@ -122,20 +141,48 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     }
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const bool ok = kin && bunit * u < brem;
-      dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff0 + (uint32_t)u * bstep + 2u * (uint32_t)k0 : kOOB, 0);
+      if constexpr (NN) {
+        const int b = wave + 8 * u;
+        const int kr = k0 + 2 * b;          // first of the two K rows (even)
+        const bool second = kr >= ksplit;   // ksplit is even: no straddle
+        const bool ok = kr + (lane >> 5) < K;
+        dma16(second ? rsB1 : rsB, Ws + b * 1024, ok ? boff0 : kOOB,
+              (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2));
+      } else {
+        const bool ok = kin && bunit * u < brem;
+        dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff0 + (uint32_t)u * bstep + 2u * (uint32_t)k0 : kOOB, 0);
+      }
     }
   };
 
   // ---------------------------------------------------- fragments, MFMAs
+  // NN: byte offset of this lane's transpose-read row for column block i at
+  // K sub-step 0 (rows kk*16 and kk*16 + 4 are reached with immediates)
+  uint32_t trb[2];
+  if constexpr (NN) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int krow0 = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int nl = wn * 64 + i * 32 + 16 * (g & 1) + 4 * (sl & 3);
+      trb[i] = nn_off(krow0, nl >> 3) + ((nl >> 2) & 1) * 8;
+    }
+  }
   u32x4 fw[4][2], ft[4][4];   // [16-K sub-step][32-row block]: weight rows, tokens
   auto rd = [&](int stg) {
     const char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (NN) {
+          const u32x2 lo = lds_read_tr8(Ws, trb[i] + kk * 16 * 512);
+          const u32x2 hi = lds_read_tr8(Ws, trb[i] + (kk * 16 + 4) * 512);
+          fw[kk][i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));

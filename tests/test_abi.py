@@ -99,12 +99,14 @@ def test_workspace_strategies():
             - wb(L.OP_LINEAR_FWD | M, L.LORA_BF16, 1, T, d, f, r)) == f * d * 2
     assert (wb(L.OP_MLP_FWD, L.LORA_BF16, 1, T, d, f, r)
             - wb(L.OP_MLP_FWD | M, L.LORA_BF16, 1, T, d, f, r)) == 2 * f * d * 2
-    # backwards hold transposed weights: W^T; MLP [Wg^T | Wu^T] (Wd^T reuses it)
-    for fmt in (0, 1):
-        assert (wb(L.OP_LINEAR_BWD, L.LORA_BF16, fmt, T, d, f, r)
-                - wb(L.OP_LINEAR_BWD | M, L.LORA_BF16, fmt, T, d, f, r)) == f * d * 2
-        assert (wb(L.OP_MLP_BWD, L.LORA_BF16, fmt, T, d, f, r)
-                - wb(L.OP_MLP_BWD | M, L.LORA_BF16, fmt, T, d, f, r)) == 2 * f * d * 2
+    # 4-bit backwards hold decoded, transposed weights: W^T; MLP [Wg^T | Wu^T]
+    # (Wd^T reuses it); dense backwards read W in place in both strategies
+    assert (wb(L.OP_LINEAR_BWD, L.LORA_BF16, 1, T, d, f, r)
+            - wb(L.OP_LINEAR_BWD | M, L.LORA_BF16, 1, T, d, f, r)) == f * d * 2
+    assert (wb(L.OP_MLP_BWD, L.LORA_BF16, 1, T, d, f, r)
+            - wb(L.OP_MLP_BWD | M, L.LORA_BF16, 1, T, d, f, r)) == 2 * f * d * 2
+    for op in (L.OP_LINEAR_BWD, L.OP_MLP_BWD):
+        assert wb(op, L.LORA_BF16, 0, T, d, f, r) == wb(op | M, L.LORA_BF16, 0, T, d, f, r)
     # fp32 has one strategy
     assert wb(L.OP_MLP_BWD, L.LORA_F32, 0, 67, 48, 80, 5) == wb(L.OP_MLP_BWD | M, L.LORA_F32, 0, 67, 48, 80, 5)
 
