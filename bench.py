@@ -148,6 +148,11 @@ def mlp_flops(T, d, f, r):
     return 12 * T * d * f + 18 * T * r * (d + f)
 
 
+def mlp_phase_flops(T, d, f, r):
+    """Algorithmic FLOPs of the MLP forward and of its backward."""
+    return 6 * T * d * f + 6 * T * r * (d + f), 6 * T * d * f + 12 * T * r * (d + f)
+
+
 def gemm_flops(kc, T, d, f, r):
     """Algorithmic FLOPs of one launch of each timed GEMM class."""
     import lora_linear_fwd_amd as L
@@ -413,6 +418,28 @@ def main():
     # as kernels_ms; not part of value)
     _, _, kms = timed_steps(min(args.steps, 5), kcs)
     kms[dom] = live[dom]
+
+    # forward and backward separately, in another pass after the timed region:
+    # HIP events around each call on the same stream
+    nph = max(3, min(args.steps, 10))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nph)]
+    for e0, e1, e2 in evs:
+        e0.record(stream)
+        L.lora_swiglu_mlp_fwd(X, W, A, B, alpha, Y=Y, e=e, g=g, workspace=ws_fwd, stream=stream)
+        e1.record(stream)
+        L.lora_swiglu_mlp_bwd(X, W, A, B, alpha, e, g, dY, out=out, workspace=ws_bwd,
+                              stream=stream)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    fwd_flops, bwd_flops = mlp_phase_flops(T, d, f, r)
+    phase = {}
+    for name, fl, pick in (("fwd", fwd_flops, lambda e0, e1, e2: e0.elapsed_time(e1)),
+                           ("bwd", bwd_flops, lambda e0, e1, e2: e1.elapsed_time(e2)),
+                           ("fwd+bwd", fwd_flops + bwd_flops, lambda e0, e1, e2: e0.elapsed_time(e2))):
+        ts = [pick(*x) for x in evs]
+        med = float(np.median(ts))
+        phase[name] = {"median_ms": round(med, 4), "min_ms": round(float(np.min(ts)), 4),
+                       "tflops_at_median": round(fl / (med * 1e-3) / 1e12, 2), "flops": fl}
     names = dict(zip([L.KC_GATEUP_FWD, L.KC_DOWN_FWD, L.KC_DOWN_BWD, L.KC_GATEUP_BWD], KC_NAMES))
     dom_tflops = gemm_flops(dom, T, d, f, r) / (kms[dom] * 1e-3) / 1e12
     flops = mlp_flops(T, d, f, r)
@@ -443,6 +470,8 @@ def main():
         "kernels_ms": {names[kc]: round(kms[kc], 4) for kc in kcs},
         "kernels_ms_source": "roofline kernel: HIP events in the timed region; the others: "
                              "a separate pass of up to 5 steps after it",
+        "phases_ms": phase,
+        "phases_ms_source": f"HIP events around each call, {nph} steps after the timed region",
         "roofline": {"bound": "mfma", "kernel": names[dom], "achieved": round(dom_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
