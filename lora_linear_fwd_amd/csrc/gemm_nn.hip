@@ -13,11 +13,11 @@ template <int EPI>
 static hipError_t launch_pp_nn(const GemmArgs &a, hipStream_t st) {
   static std::atomic<uint64_t> done{0};
   auto kern = k_lora_gemm_pp<EPI, true>;
-  hipError_t e = ensure_lds(kern, PP_LDS, done);
+  hipError_t e = ensure_lds(kern, pp_lds(true), done);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(PP_THREADS), PP_LDS, st, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(PP_THREADS), pp_lds(true), st, a);
   return hipGetLastError();
 }
 hipError_t launch_gemm_nn(int epi, const GemmArgs &a, hipStream_t st) {

@@ -7,26 +7,22 @@
 // groups alternate between
 //   a compute phase: 32 back-to-back MFMA 32x32x16 on one K step (64) of
 //     fragments already in registers, and
-//   a memory phase: the LDS fragment reads of its next K step (and group
-//     0's share of the LDS-DMA of a later K step),
+//   a memory phase: the LDS fragment reads of its next K step and the
+//     LDS-DMA of one operand tile of a later K step (group 0: tokens,
+//     group 1: weights),
 // with a workgroup barrier between phases, so that while one wave of a SIMD
 // waits on its vector-memory issue the other keeps the matrix core busy.
 // With one wave per SIMD (the four-wave form) those stalls sit between the
 // wave's own MFMAs.  Each wave owns a 128 (tokens) x 64 (weight rows)
 // sub-tile: 128 fp32 accumulators per lane, 96 registers of fragments.
 //
-// Phase schedule (step s lives in LDS stage s % 2):
-//   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: read s, then DMA share of s+1
-//   G1:   --     | M0 | C0 | M1 | C1 ...   Cs: MFMAs, DMA share of s+2 among them
-// A stage is refilled only in a phase opened by a barrier that every reader
-// of its previous step had passed with its reads complete: group 0 in its
-// memory phase (its own reads there target the other stage), group 1 in its
-// compute phase.  (A group-1 wave refilling the stage it had
-// just read, inside the same phase, raced with the other group-1 waves still
-// reading it: rare stale fragments, measured.)  Each group drains its loads
-// (vmcnt 0) before the barrier that precedes their first read: group 0 at
-// the end of its next compute phase, group 1 at the end of its next memory
-// phase.
+// Phase schedule (token tile of step s in LDS stage s % 2, weight tile in
+// stage s % 3):
+//   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: read s, load token tile s+1
+//   G1:   --     | M0 | C0 | M1 | C1 ...   Ms: load weight tile s+2, read s
+// Every load targets a stage whose last reads ended before an earlier
+// barrier, and each group drains all of its loads (vmcnt 0) before the
+// barrier that precedes their first read, with no younger load in flight.
 //
 // Gate/up tiles (SwiGLU forward) interleave weight rows in 32-row blocks,
 // [32 gate | 32 up] per 64 tile rows, so every wave's 64 columns hold the
@@ -36,7 +32,11 @@
 // (backward dX = dY W without a transposed copy).  Its LDS tile keeps that
 // layout, [64 K-rows x 256 columns], and the MFMA fragments are read with
 // the LDS transpose read ds_read_b64_tr_b16 (two per 32-column block and
-// 16-K sub-step).  K rows >= ksplit come from the second weight (B1).
+// 16-K sub-step).  K rows >= ksplit come from the second weight (B1).  The
+// NN form keeps two stages of both tiles, every wave loading a share of
+// each (group 1 inside its compute phase): with the weight tile loaded by
+// group 1 alone it ran 6-13 % slower than this, while the NT forms run up to
+// 5 % faster with the split loads.
 
 #pragma once
 #include "gemm_lora.hpp"
@@ -44,8 +44,10 @@
 namespace lora {
 
 constexpr int PP_THREADS = 512;
-// two K-step-64 stages of 64 KB; the epilogue reuses them (8 x 16 KB)
-constexpr size_t PP_LDS = 2 * 65536;
+// NT: two 32 KB stages of the token tile and three of the weight tile (K
+// step 64); NN: two stages of both.  The epilogue reuses the first 128 KB
+// (8 x 16 KB).
+constexpr size_t pp_lds(bool nn) { return (nn ? 4 : 5) * (size_t)32768; }
 
 __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
   static_assert(!(NN && GU), "the gate/up forward reads its weights K-contiguous");
-  constexpr int BK = 64, XS = BM * BK * 2, STAGE = 2 * XS;
+  constexpr int BK = 64, XS = BM * BK * 2, WS = BN * BK * 2;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,123 +73,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K, ksplit = p.ksplit;
 
-  // ---------------------------------------------------- DMA lane geometry
-  // Every wave loads its share of a K step: instruction u (0..3) of wave w
-  // fills tile rows 8b .. 8b+7 with b = w + 8u; lane l lands in row
-  // r0 + 64u (r0 = 8w + l/8) at physical chunk l%8, which holds logical chunk
-  // c = (l%8) ^ swz(row), i.e. K columns 8c .. 8c+7.  swz(row) = (row/2) % 8
-  // does not depend on u, so neither does c.
-  constexpr int NI = 4;
-  const int r0 = 8 * wave + (lane >> 3);
-  const int cA = (lane & 7) ^ (int)kc_swz<BK>(r0);
-  const int kcol = 8 * cA;
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A0 + (int64_t)m0 * p.lda, kMaxRecords);
-  // A1 - A0 - 2 ksplit: added to offsets of columns >= ksplit
-  const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
-  const uint32_t aoff0 = (uint32_t)(r0 * p.lda * 2 + cA * 16);
-  const uint32_t astep = (uint32_t)(64 * p.lda * 2);   // 64 tile rows
-  const int arem = M - m0 - r0;                         // instruction u valid if 64u < arem
-  __amdgpu_buffer_rsrc_t rsB, rsB1;
-  uint32_t boff0, bstep;
-  int brem, bunit;
-  if constexpr (NN) {
-    // K rows 2b, 2b+1 (b = w + 8u) of the [64 x 256] weight tile: lane l
-    // lands in row 2b + l/32 at physical chunk l%32, holding columns
-    // 8c .. 8c+7 with c = (l%32) ^ 4 (row%4); row%4 does not depend on u
-    const int krow = 2 * wave + (lane >> 5);
-    const int cn = (lane & 31) ^ ((krow & 3) << 2);
-    rsB = make_rsrc(p.B0 + n0, kMaxRecords);
-    rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
-    boff0 = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + cn * 16) : kOOB;
-    bstep = 0;
-    brem = 0;
-    bunit = 0;
-  } else if constexpr (GU) {
-    // tile row r0 + 64u is feature 32u + (r0 % 32) of the tile, of the gate
-    // weight for r0 < 32 (group 0) and of the up weight otherwise (group 1)
-    const int jl = r0 & 31;
-    rsB = rsB1 = make_rsrc((grp ? p.B1 : p.B0) + (int64_t)tn * 128 * p.ldb, kMaxRecords);
-    boff0 = (uint32_t)(jl * p.ldb * 2 + cA * 16);
-    bstep = (uint32_t)(32 * p.ldb * 2);
-    brem = p.gu_f - tn * 128 - jl;
-    bunit = 32;
-  } else {
-    const bf16_t *bseg = p.B0;
-    int nsb = 0;
-    if (p.nseg1 > 0 && n0 >= p.nseg1) {
-      const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
-      bseg = s2 ? p.B2 : p.B1;
-      nsb = s2 ? p.nseg2 : p.nseg1;
-    }
-    rsB = rsB1 = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
-    boff0 = (uint32_t)(r0 * p.ldb * 2 + cA * 16);
-    bstep = (uint32_t)(64 * p.ldb * 2);
-    brem = N - n0 - r0;
-    bunit = 64;
-  }
-  const int nk = (K + BK - 1) / BK;
-  // This wave's share of K step kt (< nk) into a stage: 8 loads; lanes past
-  // M, N or K read zeros.  No load is issued for steps past the end.
-  auto dma = [&](int kt, int stg) {
-    char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
-    const int k0 = kt * BK;
-    const int col = k0 + kcol;
-    const bool kin = col < K;
-    const uint32_t ka = 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u);
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const bool ok = kin && 64 * u < arem;
-      dma16(rsA, Xs + (wave + 8 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      if constexpr (NN) {
-        const int b = wave + 8 * u;
-        const int kr = k0 + 2 * b;          // first of the two K rows (even)
-        const bool second = kr >= ksplit;   // ksplit is even: no straddle
-        const bool ok = kr + (lane >> 5) < K;
-        dma16(second ? rsB1 : rsB, Ws + b * 1024, ok ? boff0 : kOOB,
-              (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2));
-      } else {
-        const bool ok = kin && bunit * u < brem;
-        dma16(rsB, Ws + (wave + 8 * u) * 1024, ok ? boff0 + (uint32_t)u * bstep + 2u * (uint32_t)k0 : kOOB, 0);
-      }
-    }
-  };
-
-  // ---------------------------------------------------- fragments, MFMAs
-  // NN: byte offset of this lane's transpose-read row for column block i at
-  // K sub-step 0 (rows kk*16 and kk*16 + 4 are reached with immediates)
-  uint32_t trb[2];
-  if constexpr (NN) {
-    const int g = lane >> 4, sl = lane & 15;
-    const int krow0 = 8 * (g >> 1) + (sl >> 2);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int nl = wn * 64 + i * 32 + 16 * (g & 1) + 4 * (sl & 3);
-      trb[i] = nn_off(krow0, nl >> 3) + ((nl >> 2) & 1) * 8;
-    }
-  }
   u32x4 fw[4][2], ft[4][4];   // [16-K sub-step][32-row block]: weight rows, tokens
-  auto rd = [&](int stg) {
-    const char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if constexpr (NN) {
-          const u32x2 lo = lds_read_tr8(Ws, trb[i] + kk * 16 * 512);
-          const u32x2 hi = lds_read_tr8(Ws, trb[i] + (kk * 16 + 4) * 512);
-          fw[kk][i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));
-    }
-  };
   f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -195,76 +81,294 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  auto mfma_step = [&]() {
+  auto comp = [&]() {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fw[kk][i], ft[kk][j], acc[i][j]);
-  };
-  auto comp = [&]() {
-    mfma_step();
     // the phase's MFMAs stay ahead of its closing wait and barrier
     __builtin_amdgcn_sched_barrier(0);
   };
-  // group 1's compute phase with its DMA share of K step kt: one load after
-  // every two of the first 16 MFMAs
-  auto comp_dma = [&](int kt, int stg) {
-    dma(kt, stg);
-    mfma_step();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
   auto lgkm0 = []() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
-
-  // ------------------------------------------------------------ K loop
-  // prologue: steps 0 and 1
-  dma(0, 0);
-  if (nk > 1) dma(1, 1);
-  wait_vmem();
-  pp_barrier();
-  if (grp == 0) {
-    rd(0);
-    lgkm0();
+  if constexpr (NN) {
+    // ------------------------------------------ NN form: shared loads
+    // Two stages of both tiles.  Every wave loads its share of a K step
+    // (4 A-tile blocks w + 8u, rows r0 + 64u with r0 = 8w + l/8, and 4
+    // weight blocks of two K rows each): group 0 in its memory phase, into
+    // the stage both groups finished reading before the barrier that opened
+    // it; group 1 inside its compute phase, one load after every two of the
+    // first 16 MFMAs, i.e. after the barrier that closed every read of that
+    // stage.  Group 0 drains its loads at the end of its next compute phase,
+    // group 1 at the end of its next memory phase.
+    constexpr int NI = 4;
+    const int r0 = 8 * wave + (lane >> 3);
+    const int cA = (lane & 7) ^ (int)kc_swz<BK>(r0);
+    const int kcol = 8 * cA;
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A0 + (int64_t)m0 * p.lda, kMaxRecords);
+    const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
+    const uint32_t aoff0 = (uint32_t)(r0 * p.lda * 2 + cA * 16);
+    const uint32_t astep = (uint32_t)(64 * p.lda * 2);   // 64 tile rows
+    const int arem = M - m0 - r0;
+    // weight K rows 2b, 2b+1 (b = w + 8u): lane l lands in row 2b + l/32 at
+    // physical chunk l%32, holding columns 8c .. 8c+7 with c = (l%32) ^
+    // 4 (row%4); row%4 does not depend on u
+    const int krow = 2 * wave + (lane >> 5);
+    const int cn = (lane & 31) ^ ((krow & 3) << 2);
+    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.B0 + n0, kMaxRecords);
+    const __amdgpu_buffer_rsrc_t rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
+    const uint32_t boff0 = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + cn * 16) : kOOB;
+    const int nk = (K + BK - 1) / BK;
+    constexpr int STAGE = XS + WS;
+    auto dma = [&](int kt, int stg) {
+      char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
+      const int k0 = kt * BK;
+      const int col = k0 + kcol;
+      const bool kin = col < K;
+      const uint32_t ka = 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u);
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        const bool ok = kin && 64 * u < arem;
+        dma16(rsA, Xs + (wave + 8 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        const int b = wave + 8 * u;
+        const int kr = k0 + 2 * b;          // first of the two K rows (even)
+        const bool second = kr >= ksplit;   // ksplit is even: no straddle
+        const bool ok = kr + (lane >> 5) < K;
+        dma16(second ? rsB1 : rsB, Ws + b * 1024, ok ? boff0 : kOOB,
+              (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2));
+      }
+    };
+    // byte offset of this lane's transpose-read row for column block i at K
+    // sub-step 0 (rows kk*16 and kk*16 + 4 are reached with immediates)
+    uint32_t trb[2];
+    {
+      const int g = lane >> 4, sl = lane & 15;
+      const int krow0 = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int nl = wn * 64 + i * 32 + 16 * (g & 1) + 4 * (sl & 3);
+        trb[i] = nn_off(krow0, nl >> 3) + ((nl >> 2) & 1) * 8;
+      }
+    }
+    auto rd = [&](int stg) {
+      const char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const u32x2 lo = lds_read_tr8(Ws, trb[i] + kk * 16 * 512);
+          const u32x2 hi = lds_read_tr8(Ws, trb[i] + (kk * 16 + 4) * 512);
+          fw[kk][i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));
+      }
+    };
+    auto comp_dma = [&](int kt, int stg) {
+      dma(kt, stg);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fw[kk][i], ft[kk][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    dma(0, 0);
+    if (nk > 1) dma(1, 1);
+    wait_vmem();
     pp_barrier();
-    for (int s = 0; s < nk; ++s) {
-      comp();              // step s
-      wait_vmem();         // own share of step s+1 (issued one phase ago)
-      pp_barrier();
-      // fragment reads first, then step s's stage refilled: every wave
-      // finished reading it before the last two barriers
-      if (s + 1 < nk) rd((s + 1) & 1);
-      if (s + 2 < nk) dma(s + 2, s & 1);
+    if (grp == 0) {
+      rd(0);
       lgkm0();
       pp_barrier();
+      for (int s = 0; s < nk; ++s) {
+        comp();              // step s
+        wait_vmem();         // own share of step s+1 (issued one phase ago)
+        pp_barrier();
+        if (s + 1 < nk) rd((s + 1) & 1);
+        if (s + 2 < nk) dma(s + 2, s & 1);
+        lgkm0();
+        pp_barrier();
+      }
+    } else {
+      pp_barrier();
+      int s = 0;
+      for (; s + 2 < nk; ++s) {
+        rd(s & 1);
+        lgkm0();
+        wait_vmem();         // own share of step s+1 (issued one phase ago)
+        pp_barrier();
+        comp_dma(s + 2, s & 1);   // step s
+        pp_barrier();
+      }
+      for (; s < nk; ++s) {
+        rd(s & 1);
+        lgkm0();
+        wait_vmem();
+        pp_barrier();
+        comp();
+        pp_barrier();
+      }
     }
   } else {
-    pp_barrier();
-    // step s's stage is refilled in the compute phase, once every group-1
-    // wave is done reading it; the loads are drained at the end of the next
-    // memory phase (own share of step s+1, issued one phase before)
-    int s = 0;
-    for (; s + 2 < nk; ++s) {
-      rd(s & 1);
-      lgkm0();
-      wait_vmem();
-      pp_barrier();
-      comp_dma(s + 2, s & 1);   // step s
-      pp_barrier();
+    // ---------------------------------------------------- DMA lane geometry
+    // LDS: two stages of the A_op tile (tokens, 32 KB each) and three of the
+    // B_op tile (weights, 32 KB each), 160 KB.  Group 0 loads every A tile,
+    // group 1 every B tile, each in its memory phase and each into a stage that
+    // every wave finished reading before an earlier barrier (see the K loop).
+    // A tile of 32 one-kilobyte blocks, block b = rows 8b .. 8b+7: wave w of a
+    // group issues blocks w + 4u (u < 8); lane l lands in row r0 + 32u
+    // (r0 = 8w + l/8) at physical chunk l%8, which holds logical chunk
+    // c = (l%8) ^ swz(row), i.e. K columns 8c .. 8c+7.  swz(row) = (row/2) % 8
+    // does not depend on u, so neither does c.  B tiles: the same geometry
+    // (dense NT), or two K rows per block (NN).
+    constexpr int NI = 8;
+    constexpr int ASTG = 2, BSTG = 3;
+    const int w4 = wave & 3;
+    const int r0 = 8 * w4 + (lane >> 3);
+    const int cA = (lane & 7) ^ (int)kc_swz<BK>(r0);
+    const int kcol = 8 * cA;
+    char *const a_lds = smem;                       // A stage i at a_lds + i * XS
+    char *const b_lds = smem + ASTG * XS;           // B stage i at b_lds + i * WS
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A0 + (int64_t)m0 * p.lda, kMaxRecords);
+    // A1 - A0 - 2 ksplit: added to offsets of columns >= ksplit
+    const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
+    const uint32_t aoff0 = (uint32_t)(r0 * p.lda * 2 + cA * 16);
+    const uint32_t astep = (uint32_t)(32 * p.lda * 2);   // 32 tile rows
+    const int arem = M - m0 - r0;                         // block u valid if 32u < arem
+    __amdgpu_buffer_rsrc_t rsB, rsB1;
+    uint32_t boff0;
+    int brem;
+    if constexpr (GU) {
+      // tile row r0 + 32u: feature 32 (u / 2) + r0 of the tile, of the gate
+      // weight for even u and of the up weight for odd u
+      rsB = make_rsrc(p.B0 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
+      rsB1 = make_rsrc(p.B1 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
+      boff0 = (uint32_t)(r0 * p.ldb * 2 + cA * 16);
+      brem = p.gu_f - tn * 128 - r0;
+    } else {
+      const bf16_t *bseg = p.B0;
+      int nsb = 0;
+      if (p.nseg1 > 0 && n0 >= p.nseg1) {
+        const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
+        bseg = s2 ? p.B2 : p.B1;
+        nsb = s2 ? p.nseg2 : p.nseg1;
+      }
+      rsB = rsB1 = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
+      boff0 = (uint32_t)(r0 * p.ldb * 2 + cA * 16);
+      brem = N - n0 - r0;
     }
-    for (; s < nk; ++s) {
-      rd(s & 1);
+    const uint32_t bstep32 = (uint32_t)(32 * p.ldb * 2);
+    const int nk = (K + BK - 1) / BK;
+    // A tile of K step kt (< nk) into A stage sa (group 0): 8 loads per wave;
+    // lanes past M or K read zeros.  No load is issued for steps past the end.
+    auto dma_a = [&](int kt, int sa) {
+      char *Xs = a_lds + sa * XS;
+      const int k0 = kt * BK;
+      const int col = k0 + kcol;
+      const bool kin = col < K;
+      const uint32_t ka = 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u);
+  #pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        const bool ok = kin && 32 * u < arem;
+        dma16(rsA, Xs + (w4 + 4 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
+      }
+    };
+    // B tile of K step kt (< nk) into B stage sb (group 1): 8 loads per wave
+    auto dma_b = [&](int kt, int sb) {
+      char *Ws = b_lds + sb * WS;
+      const int k0 = kt * BK;
+      const int col = k0 + kcol;
+      const bool kin = col < K;
+  #pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        const int b = w4 + 4 * u;
+        if constexpr (GU) {
+          const int v = u >> 1;
+          const bool ok = kin && 32 * v < brem;
+          dma16((u & 1) ? rsB1 : rsB, Ws + b * 1024,
+                ok ? boff0 + (uint32_t)v * bstep32 + 2u * (uint32_t)k0 : kOOB, 0);
+        } else {
+          const bool ok = kin && 32 * u < brem;
+          dma16(rsB, Ws + b * 1024, ok ? boff0 + (uint32_t)u * bstep32 + 2u * (uint32_t)k0 : kOOB, 0);
+        }
+      }
+    };
+
+    // ---------------------------------------------------- fragments, MFMAs
+    // fragments of K step s (A stage s % 2, B stage s % 3)
+    auto rd = [&](int s) {
+      const char *Xs = a_lds + (s & 1) * XS, *Ws = b_lds + (s % BSTG) * WS;
+  #pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+  #pragma unroll
+        for (int i = 0; i < 2; ++i)
+          fw[kk][i] = lds_read16(Ws, kc_off<BK>(wn * 64 + i * 32 + l32, 2 * kk + hi32));
+  #pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));
+      }
+    };
+
+    // ------------------------------------------------------------ K loop
+    // Phase t: group t % 2 computes, the other group reads its next fragments.
+    // Group 0 reads step s in phase 2s - 1, group 1 in phase 2s.
+    //   group 0, memory phase 2s+1: reads step s+1, then loads the A tile of
+    //     step s+2 into A stage s % 2 (step s: read in phases 2s-1 and 2s);
+    //     drained at the end of its compute phase 2s+2.
+    //   group 1, memory phase 2s: drains its B loads of step s+1 (issued two
+    //     phases before), loads the B tile of step s+2 into B stage
+    //     (s+2) % 3 (step s-1: read in phases 2s-3 and 2s-2), reads step s.
+    // Every load therefore targets a stage whose last reads ended before an
+    // earlier barrier, and each group's wait drains all of its loads (vmcnt 0)
+    // with nothing younger in flight.  (A group-1 wave refilling the stage it
+    // had just read, inside the same phase, raced with the other group-1
+    // waves still reading it: rare stale fragments, measured.)
+    if (grp == 0) {
+      dma_a(0, 0);
+      if (nk > 1) dma_a(1, 1);
+    } else {
+      dma_b(0, 0);
+      if (nk > 1) dma_b(1, 1);
+    }
+    wait_vmem();
+    pp_barrier();
+    if (grp == 0) {
+      rd(0);
       lgkm0();
-      wait_vmem();
       pp_barrier();
-      comp();
+      for (int s = 0; s < nk; ++s) {
+        comp();              // step s
+        wait_vmem();         // A tile of step s+1 (issued one phase ago)
+        pp_barrier();
+        if (s + 1 < nk) rd(s + 1);
+        if (s + 2 < nk) dma_a(s + 2, s & 1);
+        lgkm0();
+        pp_barrier();
+      }
+    } else {
       pp_barrier();
+      for (int s = 0; s < nk; ++s) {
+        wait_vmem();         // B tile of step s+1 (issued two phases ago)
+        if (s + 2 < nk) dma_b(s + 2, (s + 2) % BSTG);
+        rd(s);
+        lgkm0();
+        pp_barrier();
+        comp();              // step s
+        pp_barrier();
+      }
     }
   }
   wait_vmem();
