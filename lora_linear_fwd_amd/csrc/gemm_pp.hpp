@@ -34,7 +34,7 @@
 // the LDS transpose read ds_read_b64_tr_b16 (two per 32-column block and
 // 16-K sub-step).  K rows >= ksplit come from the second weight (B1).  The
 // NN form keeps two stages of both tiles, every wave loading a share of
-// each (group 1 inside its compute phase): with the weight tile loaded by
+// each (group 1 a quarter, inside its compute phase): with the weight tile loaded by
 // group 1 alone it ran 6-13 % slower than this, while the NT forms run up to
 // 5 % faster with the split loads.
 
@@ -94,34 +94,39 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   auto lgkm0 = []() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
   if constexpr (NN) {
     // ------------------------------------------ NN form: shared loads
-    // Two stages of both tiles.  Every wave loads its share of a K step
-    // (4 A-tile blocks w + 8u, rows r0 + 64u with r0 = 8w + l/8, and 4
-    // weight blocks of two K rows each): group 0 in its memory phase, into
-    // the stage both groups finished reading before the barrier that opened
-    // it; group 1 inside its compute phase, one load after every two of the
-    // first 16 MFMAs, i.e. after the barrier that closed every read of that
-    // stage.  Group 0 drains its loads at the end of its next compute phase,
-    // group 1 at the end of its next memory phase.
-    constexpr int NI = 4;
-    const int r0 = 8 * wave + (lane >> 3);
+    // Two stages of both tiles.  Each of a K step's 32 token blocks (rows
+    // 8b .. 8b+7) and 32 weight blocks (K rows 2b, 2b+1) is loaded by one
+    // wave: group-0 wave w blocks w + 4u (u < 6) of both tiles, in its
+    // memory phase, into the stage both groups finished reading before the
+    // barrier that opened it; group-1 wave w blocks 24 + w + 4u (u < 2),
+    // inside its compute phase, one load after every two of its first MFMAs,
+    // i.e. after the barrier that closed every read of that stage (measured
+    // 1-2 % faster than an even 8 / 8 share).  Group 0 drains its loads at
+    // the end of its next compute phase, group 1 at the end of its next
+    // memory phase.  Token block b = b0 + 4u holds rows r0 + 32u
+    // (r0 = 8 b0 + l/8); its swizzled chunk does not depend on u.
+    constexpr int NI0 = 6, NI1 = 2;
+    const int b0 = grp ? 24 + (wave & 3) : (wave & 3);
+    const int r0 = 8 * b0 + (lane >> 3);
     const int cA = (lane & 7) ^ (int)kc_swz<BK>(r0);
     const int kcol = 8 * cA;
     const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A0 + (int64_t)m0 * p.lda, kMaxRecords);
     const uint32_t dA1 = (uint32_t)((const char *)p.A1 - (const char *)p.A0) - 2u * (uint32_t)ksplit;
     const uint32_t aoff0 = (uint32_t)(r0 * p.lda * 2 + cA * 16);
-    const uint32_t astep = (uint32_t)(64 * p.lda * 2);   // 64 tile rows
+    const uint32_t astep = (uint32_t)(32 * p.lda * 2);   // 32 tile rows
     const int arem = M - m0 - r0;
-    // weight K rows 2b, 2b+1 (b = w + 8u): lane l lands in row 2b + l/32 at
-    // physical chunk l%32, holding columns 8c .. 8c+7 with c = (l%32) ^
-    // 4 (row%4); row%4 does not depend on u
-    const int krow = 2 * wave + (lane >> 5);
+    // weight K rows 2b, 2b+1: lane l lands in row 2b + l/32 at physical
+    // chunk l%32, holding columns 8c .. 8c+7 with c = (l%32) ^ 4 (row%4);
+    // row%4 does not depend on u
+    const int krow = 2 * b0 + (lane >> 5);
     const int cn = (lane & 31) ^ ((krow & 3) << 2);
     const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.B0 + n0, kMaxRecords);
     const __amdgpu_buffer_rsrc_t rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
     const uint32_t boff0 = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + cn * 16) : kOOB;
     const int nk = (K + BK - 1) / BK;
     constexpr int STAGE = XS + WS;
-    auto dma = [&](int kt, int stg) {
+    auto dma = [&](auto ni_tag, int kt, int stg) {
+      constexpr int NI = decltype(ni_tag)::value;
       char *Xs = smem + stg * STAGE, *Ws = Xs + XS;
       const int k0 = kt * BK;
       const int col = k0 + kcol;
@@ -129,12 +134,12 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       const uint32_t ka = 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u);
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
-        const bool ok = kin && 64 * u < arem;
-        dma16(rsA, Xs + (wave + 8 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
+        const bool ok = kin && 32 * u < arem;
+        dma16(rsA, Xs + (b0 + 4 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
       }
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
-        const int b = wave + 8 * u;
+        const int b = b0 + 4 * u;
         const int kr = k0 + 2 * b;          // first of the two K rows (even)
         const bool second = kr >= ksplit;   // ksplit is even: no straddle
         const bool ok = kr + (lane >> 5) < K;
@@ -169,8 +174,10 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           ft[kk][j] = lds_read16(Xs, kc_off<BK>(wm * 128 + j * 32 + l32, 2 * kk + hi32));
       }
     };
+    using G0N = std::integral_constant<int, NI0>;
+    using G1N = std::integral_constant<int, NI1>;
     auto comp_dma = [&](int kt, int stg) {
-      dma(kt, stg);
+      dma(G1N{}, kt, stg);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -178,15 +185,20 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fw[kk][i], ft[kk][j], acc[i][j]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 2 * NI1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 32 - 4 * NI1, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
-    dma(0, 0);
-    if (nk > 1) dma(1, 1);
+    if (grp == 0) {
+      dma(G0N{}, 0, 0);
+      if (nk > 1) dma(G0N{}, 1, 1);
+    } else {
+      dma(G1N{}, 0, 0);
+      if (nk > 1) dma(G1N{}, 1, 1);
+    }
     wait_vmem();
     pp_barrier();
     if (grp == 0) {
@@ -198,7 +210,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         wait_vmem();         // own share of step s+1 (issued one phase ago)
         pp_barrier();
         if (s + 1 < nk) rd((s + 1) & 1);
-        if (s + 2 < nk) dma(s + 2, s & 1);
+        if (s + 2 < nk) dma(G0N{}, s + 2, s & 1);
         lgkm0();
         pp_barrier();
       }
