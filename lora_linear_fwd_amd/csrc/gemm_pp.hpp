@@ -106,7 +106,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     // memory phase.  Token block b = b0 + 4u holds rows r0 + 32u
     // (r0 = 8 b0 + l/8); its swizzled chunk does not depend on u.
     constexpr int NI0 = 6, NI1 = 2;
-    const int b0 = grp ? 24 + (wave & 3) : (wave & 3);
+    const int b0 = grp ? 4 * NI0 + (wave & 3) : (wave & 3);
     const int r0 = 8 * b0 + (lane >> 3);
     const int cA = (lane & 7) ^ (int)kc_swz<BK>(r0);
     const int kcol = 8 * cA;
