@@ -19,6 +19,7 @@
 // Phase schedule (token tile of step s in LDS stage s % 2, weight tile in
 // stage s % 3):
 //   G0: read s=0 | C0 | M1 | C1 | M2 ...   Ms: read s, load token tile s+1
+//                                          (store form: load, then read)
 //   G1:   --     | M0 | C0 | M1 | C1 ...   Ms: load weight tile s+2, read s
 // Every load targets a stage whose last reads ended before an earlier
 // barrier, and each group drains all of its loads (vmcnt 0) before the
@@ -365,8 +366,16 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         comp();              // step s
         wait_vmem();         // A tile of step s+1 (issued one phase ago)
         pp_barrier();
-        if (s + 1 < nk) rd(s + 1);
-        if (s + 2 < nk) dma_a(s + 2, s & 1);
+        // token stage s & 1 was last read in the phase before, so its loads
+        // may go first: the store form issues them ahead of the fragment
+        // reads (3 % faster there), the SwiGLU forms after them (1 % faster)
+        if constexpr (EPI == EPI_STORE) {
+          if (s + 2 < nk) dma_a(s + 2, s & 1);
+          if (s + 1 < nk) rd(s + 1);
+        } else {
+          if (s + 1 < nk) rd(s + 1);
+          if (s + 2 < nk) dma_a(s + 2, s & 1);
+        }
         lgkm0();
         pp_barrier();
       }
