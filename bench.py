@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "lora_linear_fwd_amd", "csrc")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_cfg{cfg}_hbm_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_{shape}_hbm_traffic.md")
 KC_NAMES = ["gate/up fwd GEMM + SwiGLU epilogue", "down fwd GEMM",
             "down bwd GEMM + SwiGLU' epilogue", "gate/up bwd dX GEMM"]
 
@@ -113,7 +113,11 @@ def summarize_counters(fetch_csv, write_csv, cf_csv, cw_csv, cfg):
 def stored_traffic(cfg, kernel_name):
     """HBM bytes per launch of `kernel_name` from the committed counter
     summary, or None when there is none or the HIP sources changed since."""
-    path = TRAFFIC_SUMMARY.format(cfg=cfg)
+    from lora_inputs import CONFIGS
+    c = CONFIGS[cfg]
+    if c.get("kind") != "mlp":
+        return None
+    path = TRAFFIC_SUMMARY.format(shape="T%d_d%d_f%d_r%d" % (c["T"], c["d"], c["f"], c["r"]))
     if not os.path.exists(path):
         return None
     with open(path) as fh:
