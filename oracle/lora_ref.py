@@ -30,6 +30,10 @@ finite differences of every gradient, torch.autograd in float64, silu closed
 forms, bf16 rounding against torch, hand-computed 4-bit decodes, and
 hand-computed double-quantised block constants (including a case where a
 fused multiply-add would round differently) plus a per-element loop.
+tests/test_oracle_mutants.py plants 29 single-expression slips in a copy of
+this module (dropped terms and scales, wrong signs, a transposed operand,
+wrong indices, nibble order and rounding mode) and checks that each one
+fails at least one of those pins.
 """
 from __future__ import annotations
 
