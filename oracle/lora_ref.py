@@ -29,11 +29,15 @@ invariant, merged-weight invariant, brute-force loops on tiny shapes, central
 finite differences of every gradient, torch.autograd in float64, silu closed
 forms, bf16 rounding against torch, hand-computed 4-bit decodes, and
 hand-computed double-quantised block constants (including a case where a
-fused multiply-add would round differently) plus a per-element loop.
-tests/test_oracle_mutants.py plants 29 single-expression slips in a copy of
+fused multiply-add would round differently) plus a per-element loop, the
+comparator rel_fro on hand-worked vectors and matrices (zero reference, sign
+flip, one-component and all-component errors, asymmetry), and the 4-bit
+container dispatch on hand-worked containers of both forms.
+tests/test_oracle_mutants.py plants 39 single-expression slips in a copy of
 this module (dropped terms and scales, wrong signs, a transposed operand,
-wrong indices, nibble order and rounding mode) and checks that each one
-fails at least one of those pins.
+wrong indices, nibble order and rounding mode, a comparator that takes a
+difference of norms, a max-abs, a squared or an unnormalised error) and
+checks that each one fails at least one of those pins.
 """
 from __future__ import annotations
 

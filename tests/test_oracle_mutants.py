@@ -71,6 +71,25 @@ MUTANTS = [
     ("rmsnorm_bwd_missing_1_over_d", "    return r[:, None] * g - (r ** 3 * dot / d)[:, None] * X",
      "    return r[:, None] * g - (r ** 3 * dot)[:, None] * X"),
     ("rmsnorm_bwd_weight_dropped", "    g = dY * w[None, :]", "    g = dY"),
+    # comparator and the 4-bit container dispatch
+    ("rel_fro_norm_difference", "    num = np.linalg.norm((x - ref).ravel())",
+     "    num = abs(np.linalg.norm(x.ravel()) - np.linalg.norm(ref.ravel()))"),
+    ("rel_fro_max_abs", "    num = np.linalg.norm((x - ref).ravel())",
+     "    num = np.max(np.abs(x - ref))"),
+    ("rel_fro_no_ratio", "    return float(num / den)", "    return float(num)"),
+    ("rel_fro_squared", "    return float(num / den)", "    return float((num / den) ** 2)"),
+    ("rel_fro_denominator_x", "    den = np.linalg.norm(ref.ravel())",
+     "    den = np.linalg.norm(x.ravel())"),
+    ("rel_fro_zero_reference_passes", '        return 0.0 if num == 0.0 else float("inf")',
+     "        return 0.0"),
+    ("rel_fro_sum_not_difference", "    num = np.linalg.norm((x - ref).ravel())",
+     "    num = np.linalg.norm((x + ref).ravel())"),
+    ("dispatch_dims_swapped", "q.absmax_offset, q.codebook, q.n, q.k, q.blocksize,",
+     "q.absmax_offset, q.codebook, q.k, q.n, q.blocksize,"),
+    ("dispatch_plain_dims_swapped", "    return decode_q4(q.codes, q.absmax, q.codebook, q.n, q.k, q.blocksize)",
+     "    return decode_q4(q.codes, q.absmax, q.codebook, q.k, q.n, q.blocksize)"),
+    ("dispatch_dq_ignored", '    if getattr(q, "absmax_codes", None) is not None:',
+     '    if getattr(q, "absmax", None) is None and False:'),
 ]
 
 

@@ -445,3 +445,69 @@ def test_rmsnorm_against_torch_autograd_float64():
     assert np.allclose(Y, ty.detach().numpy(), rtol=1e-13, atol=1e-15)
     assert np.allclose(oracle.rmsnorm_bwd(X, w, eps, dY), tX.grad.numpy(), rtol=1e-12,
                        atol=1e-14)
+
+
+# ------------------------------------------------------- comparator, dispatch
+def test_rel_fro_hand_cases():
+    # ||x - ref||_F / ||ref||_F worked out by hand
+    x = np.array([3.0, 4.0])
+    assert oracle.rel_fro(x, x) == 0.0
+    assert oracle.rel_fro(np.zeros(2), np.zeros(2)) == 0.0              # both zero
+    assert oracle.rel_fro(x, np.zeros(2)) == math.inf                   # zero reference
+    assert oracle.rel_fro(np.zeros(2), x) == 1.0                        # zero result
+    assert oracle.rel_fro(-x, x) == 2.0                                 # sign flip: ||2x||/||x||
+    assert oracle.rel_fro(x + np.array([0.5, 0.0]), x) == 0.1           # |delta| / ||x|| = 0.5 / 5
+    # both components off by one: sqrt(2) / 5 (a max-abs or squared-norm
+    # comparator gives 0.2 or 0.08 here)
+    assert abs(oracle.rel_fro(np.array([4.0, 5.0]), x) - math.sqrt(2.0) / 5.0) < 1e-15
+    # matrices are compared element by element over the whole tensor:
+    # diff [[0, 2], [2, 0]] has norm sqrt(8), the identity sqrt(2)
+    got = oracle.rel_fro(np.array([[1.0, 2.0], [2.0, 1.0]]), np.eye(2))
+    assert abs(got - 2.0) < 1e-15
+    # a permutation with the same norm is far off, not equal
+    assert oracle.rel_fro(x[::-1].copy(), x) == math.sqrt(2.0) / 5.0
+    # not symmetric: the reference's norm is the denominator
+    assert abs(oracle.rel_fro(np.array([6.0, 8.0]), x) - 1.0) < 1e-15
+    assert abs(oracle.rel_fro(x, np.array([6.0, 8.0])) - 0.5) < 1e-15
+    # float32 inputs are compared in float64 (no float32 cancellation)
+    a = np.array([1.0 + 2**-20], dtype=np.float32)
+    assert abs(oracle.rel_fro(a, np.array([1.0], dtype=np.float32)) - 2**-20) < 1e-18
+
+
+def test_decode_q4_weight_dispatches_on_container_form():
+    # plain block constants, hand-worked: n = 2 rows of k = 64, codes 0x21
+    # (element 2j -> level 1, element 2j+1 -> level 2), row 0 scale 2, row 1 0.5
+    from types import SimpleNamespace
+    cb = np.array([0.0, 0.25, -0.5] + [0.0] * 13, dtype=np.float32)
+    codes = np.full((2, 32), 0x21, dtype=np.uint8)
+    q = SimpleNamespace(codes=codes, absmax=np.array([2.0, 0.5], np.float32), codebook=cb,
+                        n=2, k=64, blocksize=64, absmax_codes=None)
+    W = oracle.decode_q4_weight(q)
+    assert W.shape == (2, 64)
+    assert (W[0, 0::2] == 0.5).all() and (W[0, 1::2] == -1.0).all()
+    assert (W[1, 0::2] == 0.125).all() and (W[1, 1::2] == -0.25).all()
+    # double-quantised constants, hand-worked: table[c] * scale + offset
+    # block 0: 0.5 * 2 + 1 = 2;  block 1: 0.25 * 2 + 1 = 1.5
+    table = np.zeros(256, np.float32); table[7] = 0.5; table[9] = 0.25
+    qd = SimpleNamespace(codes=codes, absmax=None, codebook=cb, n=2, k=64, blocksize=64,
+                         absmax_codes=np.array([7, 9], np.uint8), absmax_codebook=table,
+                         absmax_scale=np.array([2.0], np.float32), absmax_offset=1.0,
+                         absmax_blocksize=256)
+    Wd = oracle.decode_q4_weight(qd)
+    assert Wd.shape == (2, 64)
+    assert (Wd[0, 0::2] == 0.5).all() and (Wd[0, 1::2] == -1.0).all()
+    assert (Wd[1, 0::2] == 0.375).all() and (Wd[1, 1::2] == -0.75).all()
+    # a generated container of each form decodes to the bits of its own
+    # branch: non-square (n != k) and several 64-blocks per row
+    for kind in ("plain", "dq"):
+        li = gen_linear(4, 128, 72, 4, 16.0, "bf16", seed=5, q4=kind if kind == "dq" else True)
+        qq = li.q4
+        if kind == "dq":
+            bits = oracle.decode_q4dq_bits(qq.codes, qq.absmax_codes, qq.absmax_codebook,
+                                           qq.absmax_scale, qq.absmax_offset, qq.codebook,
+                                           72, 128)
+        else:
+            bits = oracle.decode_q4_bits(qq.codes, qq.absmax, qq.codebook, 72, 128)
+        got = oracle.decode_q4_weight(qq)
+        assert got.shape == (72, 128)
+        assert np.array_equal(bf16_bits_of(got), bits)
