@@ -344,6 +344,9 @@ def main():
     import lora_linear_fwd_amd as L
     from lora_inputs import CONFIGS, gen_config
 
+    # the same kernels as liblora.so, plus the hook that records HIP events
+    # around one GEMM class's launches (include/liblora_timing.h)
+    L.use_timing_build()
     c = CONFIGS[args.config]
     T, d, f, r, alpha = c["T"], c["d"], c["f"], c["r"], c["alpha"]
     q4 = c.get("q4", False)

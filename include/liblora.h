@@ -58,8 +58,11 @@
  *     Both give results within the same tolerance of the exact product
  *     (fp32 accumulation in a different summation order).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
- *     asynchronous on it and reentrant; kernel faults surface at the
- *     caller's next synchronisation.
+ *     asynchronous on it; kernel faults surface at the caller's next
+ *     synchronisation.  The library keeps no mutable state between calls
+ *     (beyond a once-per-device kernel-attribute setup), so calls from
+ *     several host threads are safe; calls that run concurrently on the
+ *     device must not share a workspace or outputs.
  *   - HIP graphs: a call launches kernels only (no allocation, memset,
  *     copy or synchronisation), so it can be captured into a graph and
  *     replayed; replays reproduce eager results bit for bit.  The first
@@ -68,6 +71,9 @@
  *   - Every argument is validated BEFORE any HIP call; on error nothing is
  *     launched and a status code below is returned.  No exception crosses
  *     the ABI and nothing aborts.
+ *   - Sizes: T <= 2^30; feature sizes (k, n, d, f) <= 2^20 (so the 256 rows
+ *     of a GEMM tile of any operand span less than 2^31 bytes, one buffer
+ *     descriptor's range), LORA_ERR_BAD_SHAPE otherwise.
  *   - Dropout, bias and DoRA are not representable ([CR] 5).
  */
 #ifndef LIBLORA_H
@@ -150,8 +156,13 @@ typedef struct {
 
 /*
  * Y = X W^T + s (X A^T) B^T                                  ([DD] 1.3)
- * The rank-r product X A^T is formed on chip inside the GEMM and applied
- * in its epilogue; it is never written to memory ([WHY] 3.2).
+ * The rank-r product s (X A^T) is formed once per call by a skinny MFMA
+ * kernel and written to the workspace as bf16 [T x r] (rounded up to 16
+ * columns); the GEMM adds it in its epilogue as a second MFMA pass with
+ * K = r against B.  ([WHY] 3.2 keeps x A^T on chip inside the fused kernel;
+ * measured on MI355X, computing it inside the GEMM's K loop pushed the
+ * register file over its 512 entries and made the layer slower than this
+ * one extra [T x r] round trip, under 0.1 % of the GEMM's traffic.)
  * In: X [T x k], W (lora_weight [n x k]), A [r x k], B [n x r].
  * Out: Y [T x n].
  */
@@ -313,23 +324,6 @@ int lora_merge(int dtype, int64_t n, int64_t k, int64_t r, float alpha, int sign
  * Returns 0 for invalid arguments. */
 size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T,
                             int64_t k_or_d, int64_t n_or_f, int64_t r);
-
-/*
- * Benchmark instrumentation (not part of the method): record the hipEvents
- * `start` and `stop` (hipEvent_t handles) on the launch stream immediately
- * before and after the next launch of GEMM class `which`.  One-shot per
- * class; process-global, not thread-safe; NULL events clear the slot.
- */
-#define LORA_KC_GATEUP_FWD  0   /* gate/up GEMM with the SwiGLU epilogue   */
-#define LORA_KC_DOWN_FWD    1   /* down-projection forward GEMM            */
-#define LORA_KC_DOWN_BWD    2   /* dY Wd GEMM with the SwiGLU' epilogue    */
-#define LORA_KC_GATEUP_BWD  3   /* [de|dg] [Wg;Wu] GEMM (MLP dX)           */
-#define LORA_KC_LINEAR_FWD  4   /* lora_linear_fwd GEMM                    */
-#define LORA_KC_LINEAR_DX   5   /* lora_linear_bwd dX GEMM                 */
-#define LORA_KC_QKV_FWD     6   /* lora_qkv_fwd fused GEMM                 */
-#define LORA_KC_QKV_DX      7   /* lora_qkv_bwd fused dX GEMM              */
-#define LORA_KC_COUNT       8
-int lora_debug_time_next(int which, void *start, void *stop);
 
 const char *lora_strerror(int status);
 int lora_abi_version(void);

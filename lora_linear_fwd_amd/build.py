@@ -1,4 +1,8 @@
-"""Build liblora.so in-tree with hipcc for gfx950 (no GPU needed to build)."""
+"""Build liblora.so in-tree with hipcc for gfx950 (no GPU needed to build).
+
+Also links liblora_timed.so: the same kernel objects with the host dispatch
+file compiled with LORA_TIMING_HOOKS (include/liblora_timing.h), which the
+benchmark loads to time one GEMM class inside a whole step."""
 import os
 import subprocess
 import sys
@@ -8,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblora.so")
+OUT_TIMED = os.path.join(HERE, "liblora_timed.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "gemm_nt.hip", "gemm_nt_q4.hip", "gemm_nn.hip", "gemm_nn_q4.hip",
            "gemm_nt_q4dq.hip", "gemm_nn_q4dq.hip"]
@@ -24,28 +29,37 @@ def _hipcc():
     return "hipcc"
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job):
+    src, suffix, defs = job
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
+    cmd = [_hipcc(), *FLAGS, *defs, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-4000:]}")
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(out, objs):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    jobs_list = [(src, "", []) for src in SOURCES]
+    jobs_list.append(("api.cpp", "_timed", ["-DLORA_TIMING_HOOKS"]))
+    jobs = min(len(jobs_list), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, jobs_list))
+    kernels = objs[1:len(SOURCES)]          # every object but the host dispatch file
+    _link(OUT, [objs[0], *kernels])
+    _link(OUT_TIMED, [objs[-1], *kernels])
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", OUT_TIMED)
     return OUT
 
 

@@ -1,10 +1,14 @@
 // liblora C ABI: argument validation, workspace planning and kernel dispatch.
 // Every check runs before the first HIP call; no exception leaves this file.
 #include "liblora.h"
+#ifdef LORA_TIMING_HOOKS
+#include "liblora_timing.h"
+#endif
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -18,6 +22,8 @@ namespace {
 
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+constexpr int64_t kMaxFeatures = (int64_t)1 << 20;
+constexpr int kMaxDevices = 64;
 inline int rs_of(int64_t width) { return (int)(cdiv(width, 16) * 16); }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -141,8 +147,10 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) 
   Bump b; MlpBwdPlan p{};
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   if (wcopy) p.wbuf = b.take((size_t)2 * d * f * 2);   // Wd^T, later [Wg^T | Wu^T]
-  p.de = b.take((size_t)T * f * 2);
-  p.dg = b.take((size_t)T * f * 2);
+  // de and dg interleaved as one [T x 2f] matrix (dg = de + f): the dX
+  // GEMM then reads [de | dg] as one operand with tile-local offsets
+  p.de = b.take((size_t)T * 2 * f * 2);
+  p.dg = p.de + (size_t)f * 2;
   p.side_d_nn = b.take((size_t)RS2 * d * 2);
   p.epi_d_nn = b.take((size_t)f * RS2 * 2);
   p.side_d_nt = b.take((size_t)RS2 * f * 2);
@@ -270,7 +278,9 @@ int check_dims(int dtype, int64_t T, int64_t k, int64_t n, int64_t r) {
   if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
   if (T < 0 || k <= 0 || n <= 0 || r <= 0) return LORA_ERR_BAD_SHAPE;
   if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
-  if (T > (int64_t)1 << 30 || k > (int64_t)1 << 24 || n > (int64_t)1 << 24) return LORA_ERR_BAD_SHAPE;
+  // feature sizes up to 2^20: a GEMM tile's 256 rows of any operand then
+  // span less than 2^31 bytes, the range of one buffer descriptor
+  if (T > (int64_t)1 << 30 || k > kMaxFeatures || n > kMaxFeatures) return LORA_ERR_BAD_SHAPE;
   // every GEMM grid (256-token by 128- or 256-column tiles) fits a 31-bit count
   if (cdiv(T, 256) * cdiv(2 * std::max(k, n), 128) >= ((int64_t)1 << 31)) return LORA_ERR_BAD_SHAPE;
   if (dtype == LORA_BF16 && ((k % 8) || (n % 8))) return LORA_ERR_BAD_SHAPE;
@@ -507,13 +517,30 @@ void set_b(GemmArgs &a, const WeightView &w0, const WeightView &w1) {
   a.doff0 = w0.absmax.offset; a.doff1 = w1.absmax.offset;
 }
 
+// GEMM classes (the benchmark build's timing hook names them)
+enum GemmClass {
+  KC_GATEUP_FWD = 0, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX,
+  KC_QKV_FWD, KC_QKV_DX, KC_COUNT
+};
+#ifdef LORA_TIMING_HOOKS
+static_assert(KC_COUNT == LORA_KC_COUNT && KC_QKV_DX == LORA_KC_QKV_DX, "class numbering");
+// armed events, per host thread (liblora_timing.h)
 struct TimerSlot { hipEvent_t start = nullptr, stop = nullptr; };
-TimerSlot g_timer[LORA_KC_COUNT];
+thread_local TimerSlot t_timer[KC_COUNT];
+#endif
 
 int run_gemm(int kc, bool nn, bool q4, int epi, const GemmArgs &a, hipStream_t st) {
-  TimerSlot ts = g_timer[kc];
-  g_timer[kc] = TimerSlot{};
+  // The token operand's second source (columns >= ksplit) is addressed
+  // through the first source's buffer descriptor with the constant offset
+  // (A1 - A0) - ksplit elements; every caller lays the two out as column
+  // ranges of one matrix, so that offset is 0.  Anything else could reach
+  // past the descriptor's 2^31-byte range: refuse it.
+  if (!(a.A1 - a.A0 == a.ksplit || (a.A1 == a.A0 && a.ksplit >= a.K))) return LORA_ERR_BAD_SHAPE;
+#ifdef LORA_TIMING_HOOKS
+  const TimerSlot ts = t_timer[kc];
+  t_timer[kc] = TimerSlot{};
   if (ts.start) HIP_TRY(hipEventRecord(ts.start, st));
+#endif
   hipError_t e;
   // 4-bit operands with double-quantised constants carry their 8-bit codes
   const bool dq = q4 && a.D0 != nullptr;
@@ -524,7 +551,22 @@ int run_gemm(int kc, bool nn, bool q4, int epi, const GemmArgs &a, hipStream_t s
     e = !q4 ? launch_gemm_nn(epi, a, st) : dq ? launch_gemm_nn_q4dq(epi, a, st)
                                               : launch_gemm_nn_q4(epi, a, st);
   if (e != hipSuccess) return LORA_ERR_HIP;
+#ifdef LORA_TIMING_HOOKS
   if (ts.stop) HIP_TRY(hipEventRecord(ts.stop, st));
+#endif
+  return LORA_OK;
+}
+
+// every argument of lora_linear_bwd but the workspace
+int check_lin_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, const void *X,
+                  const lora_weight *W, const void *A, const void *B, const void *dY, void *dX,
+                  void *dA, void *dB, uint32_t flags, WeightView &wv) {
+  LORA_TRY(check_dims(dtype, T, k, n, r));
+  LORA_TRY(check_weight(W, dtype, k, wv));
+  LORA_TRY(check_ptrs({A, B, dA, dB}));
+  LORA_TRY(check_tok_ptrs(T, {X, dY}));
+  if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
+  if (flags & ~(uint32_t)LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 
@@ -572,11 +614,13 @@ extern "C" {
 
 int lora_abi_version(void) { return LORA_ABI_VERSION; }
 
+#ifdef LORA_TIMING_HOOKS
 int lora_debug_time_next(int which, void *start, void *stop) {
-  if (which < 0 || which >= LORA_KC_COUNT) return LORA_ERR_BAD_SHAPE;
-  g_timer[which] = TimerSlot{(hipEvent_t)start, (hipEvent_t)stop};
+  if (which < 0 || which >= KC_COUNT) return LORA_ERR_BAD_SHAPE;
+  t_timer[which] = TimerSlot{(hipEvent_t)start, (hipEvent_t)stop};
   return LORA_OK;
 }
+#endif
 
 const char *lora_strerror(int status) {
   switch (status) {
@@ -655,20 +699,15 @@ int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
   LORA_TRY(skinny_nt(RS, false, T, k, (const bf16_t *)X, (const bf16_t *)X, k, k, nullptr,
                      nullptr, side, (float *)(w + pl.hpart), nullptr, hbf, s, st));
   a.hglob = hbf;
-  return run_gemm(LORA_KC_LINEAR_FWD, false, wv.q4, EPI_STORE, a, st);
+  return run_gemm(KC_LINEAR_FWD, false, wv.q4, EPI_STORE, a, st);
 }
 
 int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float alpha,
                     const void *X, const lora_weight *W, const void *A, const void *B,
                     const void *dY, void *dX, void *dA, void *dB, uint32_t flags, void *ws,
                     size_t ws_bytes, void *stream) {
-  LORA_TRY(check_dims(dtype, T, k, n, r));
   WeightView wv;
-  LORA_TRY(check_weight(W, dtype, k, wv));
-  LORA_TRY(check_ptrs({A, B, dA, dB}));
-  LORA_TRY(check_tok_ptrs(T, {X, dY}));
-  if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
-  if (flags & ~(uint32_t)LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
+  LORA_TRY(check_lin_bwd(dtype, T, k, n, r, X, W, A, B, dY, dX, dA, dB, flags, wv));
   bool fast;
   LORA_TRY(check_ws(LORA_OP_LINEAR_BWD, dtype, W->fmt, T, k, n, r, ws, ws_bytes, fast));
   hipStream_t st = (hipStream_t)stream;
@@ -717,7 +756,7 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
       a.accumulate = acc; a.C = (bf16_t *)dX; a.ldc = k;
       a.hglob = gbf;
       a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
-      LORA_TRY(run_gemm(LORA_KC_LINEAR_DX, nn, q4, EPI_STORE, a, st));
+      LORA_TRY(run_gemm(KC_LINEAR_DX, nn, q4, EPI_STORE, a, st));
     }
     LORA_TRY(skinny_nt(RS, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,
                        nullptr, 1.f, st));
@@ -797,7 +836,7 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
                      hbf, s, st));
   a.hglob = hbf;
-  LORA_TRY(run_gemm(LORA_KC_GATEUP_FWD, false, wg.q4, EPI_SWIGLU_FWD, a, st));
+  LORA_TRY(run_gemm(KC_GATEUP_FWD, false, wg.q4, EPI_SWIGLU_FWD, a, st));
 
   // down
   if (wcopy && wd.q4) {   // reuses the buffer once the gate/up GEMM is done
@@ -815,7 +854,7 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(skinny_nt(RS2, false, T, f, h, h, f, f, nullptr, nullptr, side_d, hpart, nullptr, hbf,
                      s, st));
   b.hglob = hbf;
-  return run_gemm(LORA_KC_DOWN_FWD, false, wd.q4, EPI_STORE, b, st);
+  return run_gemm(KC_DOWN_FWD, false, wd.q4, EPI_STORE, b, st);
 }
 
 int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
@@ -920,10 +959,10 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
       set_b(a, wd, wd); a.ldb = f;
     }
     a.rs = RS2; a.epi = epi_d_nn;
-    a.Ein = eb; a.Gin = gb; a.DE = de; a.DG = dg;
+    a.Ein = eb; a.Gin = gb; a.DE = de; a.DG = dg; a.ldd = 2 * f;
     a.hglob = gdbf;
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
-    LORA_TRY(run_gemm(LORA_KC_DOWN_BWD, nn, q4, EPI_SWIGLU_BWD, a, st));
+    LORA_TRY(run_gemm(KC_DOWN_BWD, nn, q4, EPI_SWIGLU_BWD, a, st));
   }
   // 2. one pass over h = silu(e) g (recomputed): H_d = h Ad^T (fp32, for dBd)
   //    and dAd = s G_d^T h
@@ -953,21 +992,21 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   // 5. G_gu = [de Bg | dg Bu] (fp32 for dA_gu, s G_gu in bf16 for the dX
   //    epilogue) and dBg = s de^T H_g, dBu = s dg^T H_u: one pass over [de | dg]
   if (dual) {
-    LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, f, de, dg, nullptr, nullptr, side_g, side_u,
+    LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, 2 * f, de, dg, nullptr, nullptr, side_g, side_u,
                          pt_g, pt_u, part_u, part_v, r, RS1, s, ggu32, ggubf, s, 1, (bf16_t *)dBg,
                          (bf16_t *)dBu, st));
   } else {
     if (T > 0)
-      LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, f, nullptr, nullptr, side_gu_nn, ntpart,
+      LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, 2 * f, nullptr, nullptr, side_gu_nn, ntpart,
                          ggu32, ggubf, s, st));
-    LORA_TRY(skinny_tn(RS1, false, T, 2 * f, hgu32, de, dg, f, f, nullptr, nullptr, tnpart, r, s,
+    LORA_TRY(skinny_tn(RS1, false, T, 2 * f, hgu32, de, dg, f, 2 * f, nullptr, nullptr, tnpart, r, s,
                        1, (bf16_t *)dBg, (bf16_t *)dBu, f, st));
   }
   if (T > 0 && dX) {
     // 6. dX = de Wg + dg Wu + s [de Bg | dg Bu] [Ag; Au]
     GemmArgs b = gemm_base();
     b.M = (int)T; b.N = (int)d; b.K = (int)(2 * f); b.ksplit = (int)f;
-    b.A0 = de; b.A1 = dg; b.lda = f;
+    b.A0 = de; b.A1 = dg; b.lda = 2 * f;
     bool nn = true, q4 = wg.q4;
     if (wcopy) {   // decoded [Wg^T | Wu^T] [d x 2f], over Wd^T (its GEMM is done)
       LORA_TRY(transpose_w(wt, 2 * f, wg, f, d, st));
@@ -982,7 +1021,7 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     b.C = (bf16_t *)dX; b.ldc = d;
     b.hglob = ggubf;
     b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
-    LORA_TRY(run_gemm(LORA_KC_GATEUP_BWD, nn, q4, EPI_STORE, b, st));
+    LORA_TRY(run_gemm(KC_GATEUP_BWD, nn, q4, EPI_STORE, b, st));
   }
   // 7. [dAg; dAu] = s G_gu^T X
   LORA_TRY(skinny_tn(RS1, false, T, d, ggu32, Xb, Xb, d, d, nullptr, nullptr, tnpart, r, s, 0,
@@ -1077,7 +1116,7 @@ int lora_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64
   a.C1 = (bf16_t *)K; a.ldc1 = nkv;
   a.C2 = (bf16_t *)V; a.ldc2 = nkv;
   a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)(N / BN);
-  return run_gemm(LORA_KC_QKV_FWD, false, false, EPI_STORE, a, st);
+  return run_gemm(KC_QKV_FWD, false, false, EPI_STORE, a, st);
 }
 
 int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
@@ -1153,7 +1192,7 @@ int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64
       a.rs = RS3; a.epi = epi_nn; a.hglob = gbf;
       a.accumulate = acc; a.C = (bf16_t *)dX; a.ldc = k;
       a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
-      LORA_TRY(run_gemm(LORA_KC_QKV_DX, false, false, EPI_STORE, a, st));
+      LORA_TRY(run_gemm(KC_QKV_DX, false, false, EPI_STORE, a, st));
     }
     // H = X [Aq; Ak; Av]^T
     LORA_TRY(skinny_nt(RS3, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,

@@ -20,12 +20,12 @@ inline hipError_t ensure_lds(Kern kern, size_t bytes, std::atomic<uint64_t> &don
   return e;
 }
 
-template <int BMODE, int EPI, int PF = 0>
+// the four-wave kernel with a 4-bit weight decoded in its LDS fill
+template <int BMODE, int EPI>
 inline hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t st) {
   static std::atomic<uint64_t> done{0};
-  constexpr int BK = gemm_bk<BMODE>(), NS = gemm_nstage<BMODE>();
-  constexpr size_t lds = gemm_lds_bytes<BMODE, PF, BK, NS>();
-  auto kern = k_lora_gemm<BMODE, EPI, PF, BK, NS>;
+  constexpr size_t lds = gemm_lds_bytes<BMODE>();
+  auto kern = k_lora_gemm<BMODE, EPI>;
   hipError_t e = ensure_lds(kern, lds, done);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
@@ -34,11 +34,6 @@ inline hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// dense NT with a K step of 64: loops of at least this many K elements also
-// prefetch one step further into L2 (measured: helps K = 14336 and 28672,
-// hurts K = 4096); the K-step-32 pipeline runs three steps ahead instead
-constexpr int kPrefetchMinK = 8192;
-constexpr bool kNtPrefetch = gemm_bk<B_NT>() == 64;
 hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nt_q4(int epi, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nn(int epi, const GemmArgs &a, hipStream_t st);

@@ -7,13 +7,13 @@
 // second MFMA pass with K = rs in the epilogue ("Unsloth deep-dive", 1.3: the
 // layer is the frozen base linear plus x A^T B^T * alpha/r).
 //
-// Operand B comes in four forms:
-//   B_NT     dense [N x K] rows (forward: W of an nn.Linear, K-contiguous)
-//   B_NT_Q4  4-bit codes of the same [N x K] weight, decoded while filling LDS
-//   B_NN     dense [K x N] rows (backward dX = dY W: W is N-contiguous), kept
-//            in natural layout in LDS; MFMA fragments are read with the LDS
-//            transpose read ds_read_b64_tr_b16
-//   B_NN_Q4  4-bit codes of the [K x N] weight, decoded into that layout
+// This four-wave kernel takes 4-bit weights, decoded while their LDS tiles
+// fill (dense bf16 weights go through the eight-wave k_lora_gemm_pp):
+//   B_NT_Q4  4-bit codes of an [N x K] weight (forward: W of an nn.Linear,
+//            K-contiguous)
+//   B_NN_Q4  4-bit codes of the [K x N] weight (backward dX = dY W: W is
+//            N-contiguous), decoded into that natural layout in LDS; MFMA
+//            fragments are read with the LDS transpose read ds_read_b64_tr_b16
 //   B_NT_Q4DQ, B_NN_Q4DQ  the same with double-quantised block constants
 //            (8-bit absmax codes decoded through a 256-level table, a scale
 //            per 256 blocks and an offset: "Unsloth deep-dive", 1.4)
@@ -33,12 +33,11 @@
 // "B" operand the A_op fragment, so each lane ends with 4 consecutive output
 // columns of one output row (8-byte stores).
 //
-// Pipeline: global tiles go straight to LDS with buffer_load ... lds.  Dense
-// NT: K step 32 over 4 LDS stages of 32 KB, loads three steps ahead, the A
-// tile's loads spread over the first 16-K sub-step and the B tile's over the
-// second; other forms: K step 64 over 2 stages of 64 KB, one step ahead.  The
-// barrier of each step sits before its last 16-K sub-step, so the next
-// stage's first fragment reads overlap the current stage's last 16 MFMAs.
+// Pipeline: token tiles go straight to LDS with buffer_load ... lds; 4-bit
+// codes and block constants go to registers one step ahead and are decoded
+// into the LDS stage.  K step 64 over 2 stages of 64 KB.  The barrier of each
+// step sits before its last 16-K sub-step, so the next stage's first fragment
+// reads overlap the current stage's last 16 MFMAs.
 #pragma once
 #include <type_traits>
 
@@ -55,25 +54,13 @@ constexpr int BM = 256, BN = 256, NTHREADS = 256;
 #ifndef LORA_GEMM_NSTAGE
 #define LORA_GEMM_NSTAGE 2
 #endif
-// the dense NT form: K step 32 over four stages with its DMA split in two
-// (measured faster than K step 64 over two stages; the other forms are not)
-#ifndef LORA_GEMM_BK_NT
-#define LORA_GEMM_BK_NT 32
-#endif
-#ifndef LORA_GEMM_NSTAGE_NT
-#define LORA_GEMM_NSTAGE_NT 4
-#endif
-#ifndef LORA_DMA_SPLIT
-#define LORA_DMA_SPLIT 1
-#endif
 constexpr int kBK = LORA_GEMM_BK, kNSTAGE = LORA_GEMM_NSTAGE;
-constexpr int kBK_NT = LORA_GEMM_BK_NT, kNSTAGE_NT = LORA_GEMM_NSTAGE_NT;
 static_assert(kBK == 32 || kBK == 64, "K step must be 32 or 64");
 static_assert(kNSTAGE >= 2 && kNSTAGE <= 4, "2 to 4 pipeline stages");
-static_assert(kBK_NT == 32 || kBK_NT == 64, "K step must be 32 or 64");
-static_assert(kNSTAGE_NT >= 2 && kNSTAGE_NT <= 5, "2 to 5 pipeline stages");
 
-enum BMode { B_NT = 0, B_NT_Q4 = 1, B_NN = 2, B_NN_Q4 = 3, B_NT_Q4DQ = 4, B_NN_Q4DQ = 5 };
+// 4-bit operand forms of the four-wave kernel (the values 0 and 2 were its
+// retired dense forms)
+enum BMode { B_NT_Q4 = 1, B_NN_Q4 = 3, B_NT_Q4DQ = 4, B_NN_Q4DQ = 5 };
 constexpr bool bmode_nt_q4(int m) { return m == B_NT_Q4 || m == B_NT_Q4DQ; }
 constexpr bool bmode_nn_q4(int m) { return m == B_NN_Q4 || m == B_NN_Q4DQ; }
 constexpr bool bmode_q4(int m) { return bmode_nt_q4(m) || bmode_nn_q4(m); }
@@ -104,7 +91,8 @@ struct GemmArgs {
   int64_t ldc;
   bf16_t *E, *G, *H;            // SwiGLU forward outputs [M x f]
   const bf16_t *Ein, *Gin;      // SwiGLU backward saved activations [M x N]
-  bf16_t *DE, *DG;              // SwiGLU backward outputs [M x N]
+  bf16_t *DE, *DG;              // SwiGLU backward outputs [M x N], row stride ldd
+  int64_t ldd;
   int tiles_m, tiles_n;
   // dense NT store form with N split into up to three segments (fused
   // q/k/v projections): columns [0, nseg1) use B0 / C, [nseg1, nseg2) B1 / C1,
@@ -170,48 +158,9 @@ __device__ __forceinline__ void sched_pairs() {
   }
 }
 
-// 16 - READS MFMAs each followed by an equal share of the DMAS VMEM loads
-// (the next stage's DMA), then READS pairs of (MFMA, LDS read).  The LDS
-// reads stay after the DMA: the compiler cannot tell the DMA's LDS writes
-// from the reads' addresses.
-template <int READS, int DMAS>
-__device__ __forceinline__ void sched_mfma_read_dma() {
-#pragma unroll
-  for (int i = 0; i < 16 - READS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, DMAS / (16 - READS), 0);
-  }
-#pragma unroll
-  for (int i = 0; i < READS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
-// READS pairs of (MFMA, LDS read), then 16 - READS MFMAs with DMAS VMEM loads
-// spread evenly over them (I: compile-time position)
-template <int READS, int DMAS, int I = 0>
-__device__ __forceinline__ void sched_dma_tail() {
-  if constexpr (I < 16 - READS) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr int n = DMAS * (I + 1) / (16 - READS) - DMAS * I / (16 - READS);
-    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
-    sched_dma_tail<READS, DMAS, I + 1>();
-  }
-}
-template <int READS, int DMAS>
-__device__ __forceinline__ void sched_reads_then_dma() {
-#pragma unroll
-  for (int i = 0; i < READS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  sched_dma_tail<READS, DMAS>();
-}
-
 template <int BMODE>
 struct Stage {  // sized for BK <= 64
-  // register-staged 4-bit B operand (the dense forms go straight to LDS)
+  // register-staged 4-bit B operand
   u32x4 qc[2];                           // NT: BK/2 code bytes; NN: 16 per row
   float qs[bmode_nn_q4(BMODE) ? 2 : 1];   // absmax, or the 256-block scale (DQ)
   // NN: bit i = row i comes from the second weight; DQ: bits 8 + i = row i
@@ -220,15 +169,14 @@ struct Stage {  // sized for BK <= 64
   uint32_t q8;
 };
 
-// PF (dense NT form only): each K step also warms L2 for the step PF steps
-// after the one it loads (0 = off)
-template <int BMODE, int EPI, int PF = 0, int BK = kBK, int NSTAGE = kNSTAGE>
+template <int BMODE, int EPI, int BK = kBK, int NSTAGE = kNSTAGE>
 __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
   constexpr bool Q4 = bmode_q4(BMODE);
+  static_assert(Q4, "dense weights run in k_lora_gemm_pp");
   constexpr bool DQ = bmode_dq(BMODE);
-  constexpr bool NN = (BMODE == B_NN || bmode_nn_q4(BMODE));
+  constexpr bool NN = bmode_nn_q4(BMODE);
   constexpr int XS = BM * BK * 2, WS = BN * BK * 2;
   constexpr int STAGE = XS + WS;
   constexpr int kReads = NN ? 12 : 8;   // LDS reads per 16-K sub-step
@@ -278,46 +226,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
     const int row = dma_row(u);
     aoff[u] = (m0 + row < M) ? (uint32_t)(row * p.lda * 2 + dma_chunk(u) * 16) : kOOB;
   }
-  uint32_t boff[NDMA];
+  uint32_t boff[2];
   __amdgpu_buffer_rsrc_t rsB0, rsB1;
-  if constexpr (BMODE == B_NT) {
-    if constexpr (GU) {
-      rsB0 = make_rsrc(p.B0 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
-      rsB1 = make_rsrc(p.B1 + (int64_t)tn * 128 * p.ldb, kMaxRecords);
-    } else {
-      const bf16_t *bseg = p.B0;
-      int nsb = 0;
-      if (p.nseg1 > 0 && n0 >= p.nseg1) {
-        const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
-        bseg = s2 ? p.B2 : p.B1;
-        nsb = s2 ? p.nseg2 : p.nseg1;
-      }
-      rsB0 = rsB1 = make_rsrc(bseg + (int64_t)(n0 - nsb) * p.ldb, kMaxRecords);
-    }
-#pragma unroll
-    for (int u = 0; u < NDMA; ++u) {
-      const int row = dma_row(u), c = dma_chunk(u);
-      if constexpr (GU) {
-        // tile rows: [64 gate | 64 up] for each wave column half
-        const int jl = (row >> 7) * 64 + (row & 63);
-        boff[u] = (tn * 128 + jl < p.gu_f) ? (uint32_t)(jl * p.ldb * 2 + c * 16) : kOOB;
-      } else {
-        boff[u] = (n0 + row < N) ? (uint32_t)(row * p.ldb * 2 + c * 16) : kOOB;
-      }
-    }
-  } else if constexpr (BMODE == B_NN) {
-    // DMA instruction u of wave w fills K-rows 2b, 2b+1 (b = 4u + w); lane l
-    // lands in row 2b + l/32 at chunk l%32, holding logical chunk
-    // (l%32) ^ 4 (row%4).  Rows >= ksplit come from B1.
-    rsB0 = make_rsrc(p.B0 + n0, kMaxRecords);
-    rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
-#pragma unroll
-    for (int u = 0; u < BK / 8; ++u) {
-      const int row = 2 * (4 * u + wave) + (lane >> 5);
-      const int c = (lane & 31) ^ ((row & 3) << 2);
-      boff[u] = (n0 + 8 * c < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + c * 16) : kOOB;
-    }
-  } else if constexpr (bmode_nt_q4(BMODE)) {
+  if constexpr (bmode_nt_q4(BMODE)) {
     // one weight row per thread; gate rows for waves 0, 2 and up rows for
     // waves 1, 3 when the tile interleaves gate/up
     const int row = tid;
@@ -356,48 +267,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   }
 
   const int nkt = (K + BK - 1) / BK;
-  // ------------------------------------------------ L2 prefetch (dense NT)
-  // Every operand row of a K step is one 128-byte line per operand.  Lane
-  // (wave, l) touches the line of tile row 64 wave + l of A_op and of B_op
-  // with a 4-byte LDS-DMA load into a scratch slot nobody reads, PF steps
-  // before the step's real DMA; the loads ride in the same in-order vmcnt
-  // queue as the stage loads.
-  constexpr bool DOPF = (BMODE == B_NT) && (BK == 64) && (PF > 0);
-  char *pf_lds = smem + NSTAGE * STAGE + wave * 512;
-  uint32_t pfa = kOOB, pfb = kOOB;
-  __amdgpu_buffer_rsrc_t rsPB;
-  if constexpr (DOPF) {
-    const int pr = wave * 64 + lane;
-    if (m0 + pr < M) pfa = (uint32_t)(pr * p.lda * 2);
-    if constexpr (GU) {
-      const int jl = (pr >> 7) * 64 + (pr & 63);
-      if (tn * 128 + jl < p.gu_f) pfb = (uint32_t)(jl * p.ldb * 2);
-      rsPB = (wave & 1) ? rsB1 : rsB0;
-    } else {
-      if (n0 + pr < N) pfb = (uint32_t)(pr * p.ldb * 2);
-      rsPB = rsB0;
-    }
-  }
-  auto issue_pf = [&](int kt) {
-    if constexpr (DOPF) {
-      const int k0 = kt * BK;
-      const bool live = kt < nkt;
-      const uint32_t sa = live ? 2u * (uint32_t)k0 + (k0 >= ksplit ? dA1 : 0u) : 0u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsA, (__attribute__((address_space(3))) void *)pf_lds, 4, live ? pfa : kOOB, sa, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsPB, (__attribute__((address_space(3))) void *)(pf_lds + 256), 4, live ? pfb : kOOB,
-          live ? 2u * (uint32_t)k0 : 0u, 0, 0);
-    }
-  };
-
   // ---------------------------------------- DMA of K step kt into a stage
   // Steps past the end issue loads whose lanes are all out of range (they
   // write zeros into a stage nobody reads), which keeps the per-wave count
   // of outstanding loads uniform for the vmcnt waits.
   auto issue_dma = [&](int kt, char *stage) {
     const int k0 = kt * BK;
-    char *Xs = stage, *Ws = stage + XS;
+    char *Xs = stage;
     const bool live = kt < nkt;
     const bool full = live && (k0 + BK <= K) && (k0 + BK <= ksplit || k0 >= ksplit);
     if (full) {
@@ -412,83 +288,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
                                ? aoff[u] + 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u)
                                : kOOB;
         dma16(rsA, Xs + (4 * u + wave) * 1024, v, 0);
-      }
-    }
-    const bool kfull = live && k0 + BK <= K;
-    if constexpr (BMODE == B_NT) {
-#pragma unroll
-      for (int u = 0; u < NDMA; ++u) {
-        const int b = 4 * u + wave;
-        // rows RPI b .. : gate rows for (RPI b) % 128 < 64, up rows otherwise
-        const __amdgpu_buffer_rsrc_t r = (GU && (((RPI * b) >> 6) & 1)) ? rsB1 : rsB0;
-        uint32_t v = boff[u];
-        if (!kfull && (!live || k0 + 8 * dma_chunk(u) >= K)) v = kOOB;
-        dma16(r, Ws + b * 1024, v, live ? 2u * (uint32_t)k0 : 0u);
-      }
-    } else if constexpr (BMODE == B_NN) {
-#pragma unroll
-      for (int u = 0; u < BK / 8; ++u) {
-        const int b = 4 * u + wave;
-        const int kr = k0 + 2 * b;            // first of the two rows (even)
-        const bool second = kr >= ksplit;     // ksplit is even: no straddle
-        uint32_t v = boff[u];
-        if (!kfull && (!live || kr + (lane >> 5) >= K)) v = kOOB;
-        dma16(second ? rsB1 : rsB0, Ws + b * 1024, v,
-              live ? (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2) : 0u);
-      }
-    }
-  };
-
-  // DMA of a step that lies inside K and inside one of the two K sources:
-  // no per-lane or per-step conditions (rows past the end carry kOOB)
-  auto issue_dma_fast = [&](int kt, char *stage) {
-    const int k0 = kt * BK;
-    char *Xs = stage, *Ws = stage + XS;
-    const uint32_t sa = 2u * (uint32_t)k0 + (k0 >= ksplit ? dA1 : 0u);
-#pragma unroll
-    for (int u = 0; u < NDMA; ++u) dma16(rsA, Xs + (4 * u + wave) * 1024, aoff[u], sa);
-    if constexpr (BMODE == B_NT) {
-#pragma unroll
-      for (int u = 0; u < NDMA; ++u) {
-        const int b = 4 * u + wave;
-        const __amdgpu_buffer_rsrc_t r = (GU && (((RPI * b) >> 6) & 1)) ? rsB1 : rsB0;
-        dma16(r, Ws + b * 1024, boff[u], 2u * (uint32_t)k0);
-      }
-    } else if constexpr (BMODE == B_NN) {
-      const bool second = k0 >= ksplit;
-      const __amdgpu_buffer_rsrc_t r = second ? rsB1 : rsB0;
-#pragma unroll
-      for (int u = 0; u < BK / 8; ++u) {
-        const int b = 4 * u + wave;
-        const int kr = k0 + 2 * b - (second ? ksplit : 0);
-        dma16(r, Ws + b * 1024, boff[u], (uint32_t)(kr * p.ldb * 2));
-      }
-    }
-  };
-
-  // the same as issue_dma_fast in two parts: part 0 the A tile, part 1 the B tile
-  auto issue_dma_part = [&](int kt, char *stage, int part) {
-    const int k0 = kt * BK;
-    char *Xs = stage, *Ws = stage + XS;
-    if (part == 0) {
-      const uint32_t sa = 2u * (uint32_t)k0 + (k0 >= ksplit ? dA1 : 0u);
-#pragma unroll
-      for (int u = 0; u < NDMA; ++u) dma16(rsA, Xs + (4 * u + wave) * 1024, aoff[u], sa);
-    } else if constexpr (BMODE == B_NT) {
-#pragma unroll
-      for (int u = 0; u < NDMA; ++u) {
-        const int b = 4 * u + wave;
-        const __amdgpu_buffer_rsrc_t r = (GU && (((RPI * b) >> 6) & 1)) ? rsB1 : rsB0;
-        dma16(r, Ws + b * 1024, boff[u], 2u * (uint32_t)k0);
-      }
-    } else if constexpr (BMODE == B_NN) {
-      const bool second = k0 >= ksplit;
-      const __amdgpu_buffer_rsrc_t r = second ? rsB1 : rsB0;
-#pragma unroll
-      for (int u = 0; u < BK / 8; ++u) {
-        const int b = 4 * u + wave;
-        const int kr = k0 + 2 * b - (second ? ksplit : 0);
-        dma16(r, Ws + b * 1024, boff[u], (uint32_t)(kr * p.ldb * 2));
       }
     }
   };
@@ -629,110 +428,53 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
 
   // ---------------------------------------------------------- prologue
   Stage<BMODE> st;
-  if (Q4) __syncthreads();  // pair table visible before the first decode
-  if constexpr (Q4) load_q4(st, 0);
+  __syncthreads();  // pair table visible before the first decode
+  load_q4(st, 0);
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i) issue_dma(i, smem + i * STAGE);
-  if constexpr (DOPF) {
-#pragma unroll
-    for (int i = NSTAGE; i < NSTAGE - 1 + PF; ++i) issue_pf(i);
-  }
   wait_vmem();
-  if constexpr (Q4) commit_q4(st, smem);
+  commit_q4(st, smem);
   __syncthreads();
   read_frags(smem, 0, 0);
 
   // ------------------------------------------------------------ K loop
   // A wave's loads, oldest first, when it reaches the wait before the
-  // step's barrier:
-  //   dense:  DMA(kt+1) .. DMA(kt+NSTAGE-1)
-  //   4-bit:  DMA(kt+1) .. DMA(kt+NSTAGE-2), q4(kt+1), DMA(kt+NSTAGE-1)
-  // Waiting until only the youngest DMA steps remain completes DMA(kt+1)
-  // (and the 4-bit registers of step kt+1).  The barrier sits before the
+  // step's barrier: DMA(kt+1) .. DMA(kt+NSTAGE-2), q4(kt+1), DMA(kt+NSTAGE-1).
+  // Waiting until only the youngest DMA step remains completes DMA(kt+1)
+  // and the 4-bit registers of step kt+1.  The barrier sits before the
   // step's last 16-K sub-step, whose MFMAs overlap the next stage's first
   // fragment reads.
-  constexpr int kDmaPerStep = NDMA + ((BMODE == B_NT || BMODE == B_NN) ? NDMA : 0);
-  constexpr int kWaitDense = (NSTAGE - 2) * kDmaPerStep + (DOPF ? 2 : 0);
-  constexpr int kWaitQ4 = NSTAGE == 2 ? 0 : kDmaPerStep;
-  // Steps whose DMA target lies inside K and inside one K source run a
-  // branch-free body with the DMA interleaved into the first sub-step's
-  // MFMAs; the rest (tails, a source boundary inside a step, 4-bit forms)
-  // take the general loads.
-  int nfast = 0;
-  if constexpr (!Q4) {
-    int s_end = K / BK;                       // first step reaching past K
-    if ((ksplit % BK) != 0 && ksplit < K) s_end = min(s_end, ksplit / BK);
-    nfast = max(0, min(nkt, s_end - (NSTAGE - 1)));
-  }
-  // Split DMA (three or more stages, dense forms): the A part of a step's
-  // DMA goes out in its first sub-step and the B part in its last, each
-  // spread over the MFMAs that follow the sub-step's fragment reads, so the
-  // loads never queue up in front of the MFMAs; the wait then lets the
-  // younger B part stay in flight.
-  constexpr bool kSplit = LORA_DMA_SPLIT && NSTAGE >= 3 && !Q4 && !DOPF;
-  constexpr int kDmaA = NDMA, kDmaB = kDmaPerStep - NDMA;
-  // at the wait of step kt the loads of stage kt+1 (step kt+2-NSTAGE, its B
-  // part last) are followed by NSTAGE-3 whole steps and this step's A part
-  constexpr int kWaitSplit = kSplit ? (NSTAGE - 3) * kDmaPerStep + kDmaA : 0;
-  auto step = [&](int kt, auto fast_tag) {
-    constexpr bool FAST = decltype(fast_tag)::value;
-    constexpr bool SPLIT = FAST && kSplit;
+  constexpr int kWaitQ4 = NSTAGE == 2 ? 0 : NDMA;
+  auto step = [&](int kt) {
     const char *cur = smem + (kt % NSTAGE) * STAGE;
     char *nxt = smem + ((kt + 1) % NSTAGE) * STAGE;
     char *tgt = smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE;
-    if constexpr (Q4) load_q4(st, kt + 1);
-    if constexpr (SPLIT) {
-      // issued inside the sub-steps below
-    } else if constexpr (FAST) {
-      issue_dma_fast(kt + NSTAGE - 1, tgt);
-    } else {
-      issue_dma(kt + NSTAGE - 1, tgt);
-    }
-    issue_pf(kt + NSTAGE - 1 + PF);
+    load_q4(st, kt + 1);
+    issue_dma(kt + NSTAGE - 1, tgt);
 #pragma unroll
     for (int kk = 0; kk + 1 < KSUB; ++kk) {
       // sub-step kk: MFMAs on fragment set kk&1, reads of kk+1 interleaved
       read_frags(cur, kk + 1, (kk + 1) & 1);
-      if (SPLIT && kk == 0) issue_dma_part(kt + NSTAGE - 1, tgt, 0);
       mfmas(kk & 1);
-      if (SPLIT && kk == 0) {
-        sched_reads_then_dma<kReads, kDmaA>();
-      } else if (FAST && !SPLIT && kk == 0 && kDmaPerStep % (16 - kReads) == 0) {
-        sched_mfma_read_dma<kReads, kDmaPerStep>();
-      } else {
-        sched_pairs<kReads>();
-        sched_group<0x008, 16 - kReads>();
-      }
+      sched_pairs<kReads>();
+      sched_group<0x008, 16 - kReads>();
     }
     // keep every MFMA of the earlier sub-steps ahead of the wait: the
-    // longer the DMA has, the less the wait stalls
+    // longer the loads have, the less the wait stalls
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (Q4) {
-      vm_wait<kWaitQ4>();
-      commit_q4(st, nxt);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    } else if constexpr (SPLIT) {
-      vm_wait<kWaitSplit>();
-    } else {
-      vm_wait<kWaitDense>();
-    }
+    vm_wait<kWaitQ4>();
+    commit_q4(st, nxt);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier_only();
     __builtin_amdgcn_sched_barrier(0);
     // last sub-step: MFMAs on its fragment set, the next stage's first
     // reads interleaved (on the last step they read a stage nobody uses)
     read_frags(nxt, 0, 0);
-    if constexpr (SPLIT) issue_dma_part(kt + NSTAGE - 1, tgt, 1);
     mfmas((KSUB - 1) & 1);
-    if constexpr (SPLIT) {
-      sched_reads_then_dma<kReads, kDmaB>();
-    } else {
-      sched_pairs<kReads>();
-      sched_group<0x008, 16 - kReads>();
-    }
+    sched_pairs<kReads>();
+    sched_group<0x008, 16 - kReads>();
   };
-  int kt = 0;
-  for (; kt < nfast; ++kt) step(kt, std::true_type{});
-  for (; kt < nkt; ++kt) step(kt, std::false_type{});
+  for (int kt = 0; kt < nkt; ++kt) step(kt);
   wait_vmem();
 
   // ------------------------------------------------ LoRA epilogue pass
@@ -911,8 +653,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
             dew[t] = pack_bf16x2(de[0], de[1]);
             dgw[t] = pack_bf16x2(dg[0], dg[1]);
           }
-          gstore16(p.DE + off, dew);
-          gstore16(p.DG + off, dgw);
+          const int64_t doff = (int64_t)m * p.ldd + n;
+          gstore16(p.DE + doff, dew);
+          gstore16(p.DG + doff, dgw);
         }
       }
     }
@@ -921,22 +664,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_lora_gemm(const GemmArgs p) {
   }
 }
 
-// K step and pipeline depth of each B form
-template <int BMODE>
-constexpr int gemm_bk() { return BMODE == B_NT ? kBK_NT : kBK; }
-template <int BMODE>
-constexpr int gemm_nstage() { return BMODE == B_NT ? kNSTAGE_NT : kNSTAGE; }
-
-template <int BMODE, int PF = 0, int BK = kBK, int NSTAGE = kNSTAGE>
+template <int BMODE, int BK = kBK, int NSTAGE = kNSTAGE>
 constexpr size_t gemm_lds_bytes() {
-  if constexpr (BMODE == B_NT && BK == 64 && PF > 0)   // + prefetch scratch
-    return (NSTAGE * (BM * BK * 2 + BN * BK * 2) > 4 * 32768 ? (size_t)NSTAGE * (BM * BK * 2 + BN * BK * 2)
-                                                             : (size_t)4 * 32768) + 2048;
-  // pipeline stages, at least the 4 x 32 KB the output staging uses
+  // pipeline stages (at least the 4 x 32 KB the output staging uses), then
+  // the two weights' 4-bit pair tables and (double-quantised) 256-level
+  // block-constant tables
   return (NSTAGE * (BM * BK * 2 + BN * BK * 2) > 4 * 32768 ? (size_t)NSTAGE * (BM * BK * 2 + BN * BK * 2)
                                                            : (size_t)4 * 32768) +
-         (bmode_q4(BMODE) ? 2 * 256 * sizeof(float2) + (bmode_dq(BMODE) ? 2 * 256 * sizeof(float) : 0)
-                          : 0);
+         2 * 256 * sizeof(float2) + (bmode_dq(BMODE) ? 2 * 256 * sizeof(float) : 0);
 }
 
 }  // namespace lora

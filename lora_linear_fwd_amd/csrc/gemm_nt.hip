@@ -1,14 +1,10 @@
-// LoRA GEMM instantiations for the B_NT operand form.
+// Dense NT LoRA GEMM instantiations (eight-wave k_lora_gemm_pp): the
+// forwards (store and SwiGLU epilogues) and the backward dX products that
+// read a decoded, transposed copy of a 4-bit weight.
 #include "gemm_launch.hpp"
 #include "gemm_pp.hpp"
 
-// 1: the eight-wave ping-pong kernel (default); 0: the four-wave kernel
-#ifndef LORA_GEMM_PP
-#define LORA_GEMM_PP 1
-#endif
-
 namespace lora {
-#if LORA_GEMM_PP
 template <int EPI>
 static hipError_t launch_pp(const GemmArgs &a, hipStream_t st) {
   static std::atomic<uint64_t> done{0};
@@ -26,19 +22,4 @@ hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st) {
   if (epi == EPI_SWIGLU_BWD) return launch_pp<EPI_SWIGLU_BWD>(a, st);
   return hipErrorInvalidValue;
 }
-#else
-template <int PF>
-static hipError_t launch_nt_pf(int epi, const GemmArgs &a, hipStream_t st) {
-  if (epi == EPI_STORE) return launch_gemm_t<B_NT, EPI_STORE, PF>(a, st);
-  if (epi == EPI_SWIGLU_FWD) return launch_gemm_t<B_NT, EPI_SWIGLU_FWD, PF>(a, st);
-  if (epi == EPI_SWIGLU_BWD) return launch_gemm_t<B_NT, EPI_SWIGLU_BWD, PF>(a, st);
-  return hipErrorInvalidValue;
-}
-hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st) {
-  if constexpr (kNtPrefetch) {
-    if (a.K >= kPrefetchMinK) return launch_nt_pf<1>(epi, a, st);
-  }
-  return launch_nt_pf<0>(epi, a, st);
-}
-#endif
 }  // namespace lora

@@ -1,6 +1,7 @@
-// Eight-wave ("ping-pong") form of the dense NT LoRA GEMM, for gfx950.
+// Eight-wave ("ping-pong") dense LoRA GEMM for gfx950: every bf16-weight
+// product of the library.
 //
-// Same contract as k_lora_gemm<B_NT, EPI> (GemmArgs; 256 x 256 output tile;
+// Contract as documented at GemmArgs (256 x 256 output tile;
 // K = rs LoRA epilogue pass adding S . E^T, "Unsloth deep-dive" 1.3; store,
 // SwiGLU and SwiGLU' epilogues), run by 512 threads: two waves per SIMD, in
 // two groups of four (waves 0-3 and 4-7, one of each on every SIMD).  The
@@ -121,9 +122,15 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     // row%4 does not depend on u
     const int krow = 2 * b0 + (lane >> 5);
     const int cn = (lane & 31) ^ ((krow & 3) << 2);
-    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.B0 + n0, kMaxRecords);
-    const __amdgpu_buffer_rsrc_t rsB1 = make_rsrc(p.B1 + n0, kMaxRecords);
-    const uint32_t boff0 = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * p.ldb * 2 + cn * 16) : kOOB;
+    // The weight descriptors are rebased on every K step (row k0 of the
+    // step, in each source's own row numbering), so every offset stays
+    // inside one step's 64 rows whatever the weight's size.  A row kr >= ksplit
+    // of a step that starts in the first source sits at (kr - k0) rows from
+    // the second source's base for that step, as it does in the first.
+    const int64_t ldb2 = 2 * p.ldb;
+    const char *const wbase0 = (const char *)(p.B0 + n0);
+    const char *const wbase1 = (const char *)(p.B1 + n0) - (int64_t)ksplit * ldb2;
+    const uint32_t boff0 = (n0 + 8 * cn < N) ? (uint32_t)((lane >> 5) * ldb2 + cn * 16) : kOOB;
     const int nk = (K + BK - 1) / BK;
     constexpr int STAGE = XS + WS;
     auto dma = [&](auto ni_tag, int kt, int stg) {
@@ -138,14 +145,15 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         const bool ok = kin && 32 * u < arem;
         dma16(rsA, Xs + (b0 + 4 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
       }
+      const __amdgpu_buffer_rsrc_t rsB = make_rsrc(wbase0 + (int64_t)k0 * ldb2, kMaxRecords);
+      const __amdgpu_buffer_rsrc_t rsB1 = make_rsrc(wbase1 + (int64_t)k0 * ldb2, kMaxRecords);
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
         const int b = b0 + 4 * u;
         const int kr = k0 + 2 * b;          // first of the two K rows (even)
         const bool second = kr >= ksplit;   // ksplit is even: no straddle
         const bool ok = kr + (lane >> 5) < K;
-        dma16(second ? rsB1 : rsB, Ws + b * 1024, ok ? boff0 : kOOB,
-              (uint32_t)((kr - (second ? ksplit : 0)) * p.ldb * 2));
+        dma16(second ? rsB1 : rsB, Ws + b * 1024, ok ? boff0 : kOOB, (uint32_t)(2 * b * ldb2));
       }
     };
     // byte offset of this lane's transpose-read row for column block i at K
@@ -576,8 +584,9 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
             dew[t] = pack_bf16x2(de[0], de[1]);
             dgw[t] = pack_bf16x2(dg[0], dg[1]);
           }
-          gstore16(p.DE + off, dew);
-          gstore16(p.DG + off, dgw);
+          const int64_t doff = (int64_t)m * p.ldd + n;
+          gstore16(p.DE + doff, dew);
+          gstore16(p.DG + doff, dgw);
         }
       }
     }

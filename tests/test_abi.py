@@ -12,14 +12,21 @@ import lora_linear_fwd_amd as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "liblora.h")
+TIMING_HEADER = os.path.join(ROOT, "include", "liblora_timing.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="liblora not built")
 
 
-def header_functions():
-    txt = open(HEADER).read()
+def header_functions(path=HEADER):
+    txt = open(path).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", txt)))
+
+
+def exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                         text=True, check=True).stdout
+    return set(re.findall(r"\bT\s+(lora_[a-z0-9_]+)$", out, flags=re.M))
 
 
 def test_header_declares_the_entry_points():
@@ -32,13 +39,31 @@ def test_header_declares_the_entry_points():
 
 
 def test_library_exports_every_declared_symbol():
-    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
-                         text=True, check=True).stdout
-    exported = set(re.findall(r"\bT\s+(lora_[a-z0-9_]+)$", out, flags=re.M))
-    assert set(header_functions()) <= exported
+    assert set(header_functions()) <= exported(L.LIB_PATH)
     lib = L.lib()
     for name in header_functions():
         assert hasattr(lib, name)
+
+
+def test_timing_hook_only_in_the_timing_build():
+    # the production library carries no instrumentation state or symbol; the
+    # benchmark's build exports everything liblora.h declares plus the hook
+    timing = header_functions(TIMING_HEADER)
+    assert timing == sorted(L.TIMING_EXPORTS)
+    assert not set(timing) & exported(L.LIB_PATH)
+    assert set(header_functions()) | set(timing) <= exported(L.TIMED_LIB_PATH)
+    with pytest.raises(RuntimeError):
+        L.time_next(L.KC_GATEUP_FWD, None, None)
+
+
+def test_timing_build_has_the_same_kernels():
+    # only the host dispatch object differs: every GPU kernel symbol is shared
+    def kernels(path):
+        out = subprocess.run(["nm", "--defined-only", path], capture_output=True, text=True,
+                             check=True).stdout
+        return set(re.findall(r"\s(_Z\S*k_\w+)$", out, flags=re.M))
+    a, b = kernels(L.LIB_PATH), kernels(L.TIMED_LIB_PATH)
+    assert a and a == b
 
 
 def test_version_and_strerror():
@@ -265,6 +290,17 @@ def test_rmsnorm_validation_codes():
     assert bwd(dY=None) == 1
     assert bwd(dX=P_MIS) == 5
     assert bwd(dt=0, d=60, dX=None) == 1   # fp32 takes any width: the null dX is what fails
+
+
+def test_feature_size_limit():
+    # feature sizes up to 2^20: a GEMM tile's 256 rows then span < 2^31 bytes
+    # (one buffer descriptor); larger sizes are refused before any HIP call
+    assert fwd(k=(1 << 20) + 8) == 2
+    assert fwd(n=(1 << 20) + 8) == 2
+    W = _w()
+    args = [1, 16, 64, (1 << 20) + 64, 8, 16.0, P, ctypes.byref(W), P, P, ctypes.byref(W), P, P,
+            ctypes.byref(W), P, P]
+    assert L.lib().lora_swiglu_mlp_fwd(*args, P, P, P, P, 1 << 40, None) == 2
 
 
 def test_grid_size_limits():

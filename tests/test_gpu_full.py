@@ -1,11 +1,14 @@
 """GPU parity at the benchmark workloads' full sizes, in the launch
 configuration bench.py times (the same C-ABI calls on full tensors).
 
-Outputs that are local to a token row (Y, e, g, dX) are checked on a sample
-of rows that the oracle computes one by one (first, last, and seeded random
-rows); the adapter gradients reduce over all tokens and are checked in full
-against the float64 oracle.  Tolerance: 2e-2 relative Frobenius error per
-tensor (bf16 storage, fp32 accumulation)."""
+Outputs that are local to a token row (Y, e, g, dX) are checked on rows
+that the oracle computes one by one: three whole 256-token tile bands (the
+first, a seeded middle one and the last, which is the ragged one when T is
+not a multiple of 256) over every column, plus seeded random rows; the
+adapter gradients reduce over all tokens and are checked in full against
+the float64 oracle.  Tolerance: 2e-2 relative Frobenius error per tensor
+(bf16 storage, fp32 accumulation) and the element-wise bound of
+gpu_helpers.check."""
 import numpy as np
 import pytest
 
@@ -18,9 +21,13 @@ from gpu_helpers import check, dev, host, log, mlp_weights
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def sample_rows(T, n=40, seed=0):
+def sample_rows(T, n=40, seed=0, band=256):
+    """Whole tile bands (first, a seeded middle one, last) plus n random rows."""
     r = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, 1, T - 2, T - 1], r.integers(0, T, n)]))
+    nb = (T + band - 1) // band
+    mid = int(r.integers(1, nb - 1)) if nb > 2 else 0
+    bands = [np.arange(b * band, min(T, (b + 1) * band)) for b in sorted({0, mid, nb - 1})]
+    rows = np.unique(np.concatenate(bands + [r.integers(0, T, n)]))
     return rows
 
 
@@ -56,6 +63,13 @@ def run_full_mlp(cfg, q4=None, minimal=False):
 @pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_full_mlp(cfg):
     run_full_mlp(cfg)
+
+
+def test_full_mlp_q4_minimal():
+    """The 4-bit 8B MLP in the minimal workspace: every 4-bit GEMM decodes its
+    codes inside the LDS fill (forward NT, backward NN with the K split
+    between the gate and up weights)."""
+    run_full_mlp(5, minimal=True)
 
 
 @pytest.mark.parametrize("minimal", [False, True], ids=["fast", "minimal"])
