@@ -187,6 +187,32 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r,
                     void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * lora_linear_bwd without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments (minus ws/ws_bytes), results and errors as lora_linear_bwd run
+ * with the minimal workspace (4-bit weights are decoded inside the GEMM).
+ * Its scratch memory is a static device array of LORA_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) per GPU, held from the library's first use on that GPU until the
+ * process ends; a call whose minimal workspace would exceed it returns
+ * LORA_ERR_WORKSPACE before any HIP call.  The need is
+ * lora_workspace_bytes(LORA_OP_LINEAR_BWD | LORA_WS_MINIMAL, ...): with
+ * k = n = 4096, 23 MiB at T = 16384, r = 16 and 92 MiB at T = 16384, r = 64
+ * (the 8B model's projections fit); r = 128 with T = 4096 needs 152 MiB
+ * and is refused.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams, or host
+ * threads) race and must be serialised by the caller.  No part of the array
+ * needs to start at zero: every kernel writes its scratch before reading it.
+ * The first call on a device looks up the array's device address (a HIP
+ * call); make it once outside graph capture.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int lora_linear_bwd_noalloc(int dtype, int64_t T, int64_t k, int64_t n, int64_t r,
+                            float alpha, const void *X, const lora_weight *W,
+                            const void *A, const void *B, const void *dY, void *dX,
+                            void *dA, void *dB, uint32_t flags, void *stream);
+
+/*
  * LoRA-SwiGLU MLP forward ([CR] 2.3, 4; SwiGLU per [HF]-blog section 1):
  *   e = lin(X; gate), g = lin(X; up), h = silu(e) * g, Y = lin(h; down),
  * each lin a LoRA linear with the same r and alpha.  silu(z) = z/(1+e^-z).

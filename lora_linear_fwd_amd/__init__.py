@@ -10,7 +10,7 @@ assumes row-major contiguous tensors of the stated shapes.
 Entry points mirror the C ABI in include/liblora.h:
   lora_linear_fwd, lora_linear_bwd, lora_swiglu_mlp_fwd, lora_swiglu_mlp_bwd,
   lora_dequant4, lora_decode_weight, lora_merge, lora_qkv_fwd, lora_qkv_bwd,
-  lora_rmsnorm_fwd, lora_rmsnorm_bwd,
+  lora_rmsnorm_fwd, lora_rmsnorm_bwd, lora_linear_bwd_noalloc,
   lora_workspace_bytes, lora_qkv_workspace_bytes, lora_strerror,
   lora_abi_version.
 """
@@ -39,7 +39,7 @@ EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_sw
            "lora_dequant4", "lora_workspace_bytes", "lora_strerror", "lora_abi_version",
            "lora_merge", "lora_qkv_fwd", "lora_qkv_bwd",
            "lora_qkv_workspace_bytes", "lora_decode_weight", "lora_rmsnorm_fwd",
-           "lora_rmsnorm_bwd"]
+           "lora_rmsnorm_bwd", "lora_linear_bwd_noalloc"]
 TIMING_EXPORTS = ["lora_debug_time_next"]
 (KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX,
  KC_QKV_FWD, KC_QKV_DX) = range(8)
@@ -92,6 +92,8 @@ def lib():
                                       vp, vp, vp, vp, vp, vp, sz, vp]
     L.lora_swiglu_mlp_bwd.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W,
                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lora_linear_bwd_noalloc.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, vp, vp,
+                                          vp, vp, u32, vp]
     L.lora_dequant4.argtypes = [i64, i64, vp, vp, vp, i32, i32, vp, vp]
     L.lora_merge.argtypes = [i32, i64, i64, i64, f32, i32, W, vp, vp, vp, vp]
     L.lora_decode_weight.argtypes = [i64, i64, W, i32, vp, vp]
@@ -114,7 +116,7 @@ def lib():
     for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
                  "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version", "lora_merge",
                  "lora_qkv_fwd", "lora_qkv_bwd", "lora_decode_weight", "lora_rmsnorm_fwd",
-                 "lora_rmsnorm_bwd"):
+                 "lora_rmsnorm_bwd", "lora_linear_bwd_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -399,6 +401,37 @@ def lora_linear_bwd(X, W: Weight, A, B, alpha: float, dY, need_dx=True, dX=None,
                                  _ptr(A), _ptr(B), _ptr(dY), _ptr(dX), _ptr(dA), _ptr(dB),
                                  flags, wsp, wsn, _stream(stream)),
            "lora_linear_bwd")
+    return dX, dA, dB
+
+
+LORA_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def lora_linear_bwd_noalloc(X, W: Weight, A, B, alpha: float, dY, dX, dA, dB,
+                            accumulate_dx=False, stream=None):
+    """lora_linear_bwd without a workspace: the library's static per-GPU
+    scratch array (LORA_NOALLOC_SCRATCH_BYTES) holds its scratch memory.  The
+    caller passes every output (dX may be None); nothing is allocated."""
+    where = "lora_linear_bwd_noalloc"
+    T, k = _x(X, where)
+    r = _rank(A, where)
+    n = W.shape[0]
+    _weight(W, "W", n, k, X.dtype, X.device, where)
+    _adapter(A, B, n, k, r, X.dtype, X.device, where)
+    _tensor(dY, "dY", (T, n), X.dtype, X.device, where)
+    _need(not accumulate_dx or dX is not None, f"{where}: accumulate_dx needs dX")
+    if dX is not None:
+        _tensor(dX, "dX", (T, k), X.dtype, X.device, where)
+    _tensor(dA, "dA", (r, k), X.dtype, X.device, where)
+    _tensor(dB, "dB", (n, r), X.dtype, X.device, where)
+    _on_gpu(X, where)
+    dt = _dtype_code(X)
+    wst = _wstruct(W)
+    flags = LORA_FLAG_ACCUMULATE_DX if accumulate_dx else 0
+    _check(lib().lora_linear_bwd_noalloc(dt, T, k, n, r, float(alpha), _ptr(X),
+                                         ctypes.byref(wst), _ptr(A), _ptr(B), _ptr(dY),
+                                         _ptr(dX), _ptr(dA), _ptr(dB), flags, _stream(stream)),
+           where)
     return dX, dA, dB
 
 

@@ -769,6 +769,42 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
   return LORA_OK;
 }
 
+// The allocation-free variant of lora_linear_bwd keeps its scratch memory in
+// this array: one copy per GPU, held from the library's load on that device
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device memory: its device address is looked up once per device
+// (with that device current) and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+int lora_linear_bwd_noalloc(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float alpha,
+                            const void *X, const lora_weight *W, const void *A, const void *B,
+                            const void *dY, void *dX, void *dA, void *dB, uint32_t flags,
+                            void *stream) {
+  WeightView wv;
+  LORA_TRY(check_lin_bwd(dtype, T, k, n, r, X, W, A, B, dY, dX, dA, dB, flags, wv));
+  // the minimal strategy's size (4-bit weights decoded inside the GEMM)
+  const size_t need =
+      lora_workspace_bytes(LORA_OP_LINEAR_BWD | LORA_WS_MINIMAL, dtype, W->fmt, T, k, n, r);
+  if (need > (size_t)LORA_NOALLOC_SCRATCH_BYTES) return LORA_ERR_WORKSPACE;
+  void *ptr = nullptr;
+  if (need > 0) {
+    static std::atomic<void *> dev_scratch[kMaxDevices];
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return LORA_ERR_HIP;
+    ptr = dev_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+      // the same address on every lookup for this device: a race between two
+      // first calls stores it twice
+      HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+      if (!ptr) return LORA_ERR_HIP;
+      dev_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  return lora_linear_bwd(dtype, T, k, n, r, alpha, X, W, A, B, dY, dX, dA, dB, flags, ptr, need,
+                         stream);
+}
+
 int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
                         const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
                         const lora_weight *Wu, const void *Au, const void *Bu,

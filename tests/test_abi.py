@@ -310,3 +310,22 @@ def test_grid_size_limits():
     assert lib.lora_decode_weight(1 << 24, 1 << 24, ctypes.byref(_w(1, 64, None, P, P, P)), 1, P,
                                   None) == 2
     assert lib.lora_dequant4(1 << 24, 1 << 24, P, P, P, 64, 1, P, None) == 2
+
+
+def test_noalloc_validation_before_any_hip_call():
+    # the allocation-free linear backward checks its arguments, then the size
+    # of its static scratch array, before it touches the GPU
+    lib = L.lib()
+    W = _w()
+    call = lambda T=16, k=64, n=64, r=8, **kw: lib.lora_linear_bwd_noalloc(
+        kw.get("dtype", 1), T, k, n, r, 16.0, kw.get("X", P), ctypes.byref(W), P, P,
+        kw.get("dY", P), kw.get("dX", P), kw.get("dA", P), P, kw.get("flags", 0), None)
+    assert call(dY=None) == 1
+    assert call(dA=None) == 1
+    assert call(dX=P_MIS) == 5
+    assert call(k=60) == 2
+    assert call(r=129) == 3
+    assert call(flags=2) == 3
+    big = L.workspace_bytes(L.OP_LINEAR_BWD | L.LORA_WS_MINIMAL, 1, 0, 4096, 4096, 4096, 128)
+    assert big > L.LORA_NOALLOC_SCRATCH_BYTES
+    assert call(T=4096, k=4096, n=4096, r=128) == 4
