@@ -243,6 +243,63 @@ def time_rmsnorm(T, d, reps=20):
     return out
 
 
+def time_norm_mlp(L, X, W, A, B, alpha, dY, ws_fwd, ws_bwd, stream, steps=5):
+    """RMSNorm + LoRA-SwiGLU MLP, forward + backward, outside the timed
+    region: the norm fused into the gate/up projections (folded weights, no
+    normalised rows in memory) against the same step as a chain of the
+    standalone norm kernels and the MLP calls.  X stands for the raw rows."""
+    import numpy as np
+    import torch
+    T, d = X.shape
+    g = np.random.default_rng(6)
+    w = torch.from_numpy((1.0 + 0.1 * g.standard_normal(d)).astype(np.float32)).to(
+        torch.bfloat16).to(X.device)
+    Wf = dict(W, gate=L.lora_fold_norm_weight(W["gate"], w), up=L.lora_fold_norm_weight(W["up"], w))
+    f = W["gate"].shape[0]
+    r = A["gate"].shape[0]
+    Xn = torch.empty_like(X)
+    rstd = torch.empty((T,), dtype=torch.float32, device=X.device)
+    e = torch.empty((T, f), dtype=X.dtype, device=X.device)
+    g_ = torch.empty_like(e)
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    out = {"dX": torch.empty_like(X)}
+    nf = L.workspace_bytes(L.OP_RMSNORM_MLP_FWD, L.LORA_BF16, 0, T, d, f, r)
+    nb = L.workspace_bytes(L.OP_RMSNORM_MLP_BWD, L.LORA_BF16, 0, T, d, f, r)
+    ws = torch.empty(max(nf, nb), dtype=torch.uint8, device=X.device)
+
+    def chain():
+        L.lora_rmsnorm_fwd(X, w, 1e-5, Y=Xn, rstd=rstd, stream=stream)
+        L.lora_swiglu_mlp_fwd(Xn, W, A, B, alpha, Y=Y, e=e, g=g_, workspace=ws_fwd, stream=stream)
+        L.lora_swiglu_mlp_bwd(Xn, W, A, B, alpha, e, g_, dY, out=out, workspace=ws_bwd,
+                              stream=stream)
+        L.lora_rmsnorm_bwd(X, w, rstd, out["dX"], dX=dX, stream=stream)
+
+    def fused():
+        L.lora_rmsnorm_swiglu_mlp_fwd(X, w, 1e-5, Wf, A, B, alpha, Y=Y, e=e, g=g_, rstd=rstd,
+                                      workspace=ws[:nf], stream=stream)
+        L.lora_rmsnorm_swiglu_mlp_bwd(X, w, rstd, Wf, A, B, alpha, e, g_, dY,
+                                      out=dict(out, dX=dX), workspace=ws[:nb], stream=stream)
+
+    res = {}
+    for name, fn in (("chain_ms", chain), ("fused_ms", fused)):
+        fn()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        res[name] = round(float(np.median(ts)), 4)
+    res["saved_ms"] = round(res["chain_ms"] - res["fused_ms"], 4)
+    res["source"] = (f"HIP events around each step, median of {steps}, after the timed region; "
+                     "chain = lora_rmsnorm_fwd + MLP fwd + MLP bwd + lora_rmsnorm_bwd, fused = "
+                     "lora_rmsnorm_swiglu_mlp_fwd + _bwd on norm-folded gate/up weights")
+    return res
+
+
 def bench_attn_mlp(args):
     """Config 4: q, k, v (shared input, dX summed) and o LoRA projections plus
     the LoRA-SwiGLU MLP, forward + backward, T = 16384, r = 64."""
@@ -489,6 +546,8 @@ def main():
     }
     # the RMSNorm in front of the MLP, timed on its own (not part of value)
     line["rmsnorm_before_mlp"] = time_rmsnorm(T, d)
+    if not q4:
+        line["rmsnorm_mlp_step"] = time_norm_mlp(L, X, W, A, B, alpha, dY, ws_fwd, ws_bwd, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens, mi)
     print(json.dumps(line), flush=True)

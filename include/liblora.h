@@ -151,6 +151,8 @@ typedef struct {
 #define LORA_OP_MLP_BWD    3
 #define LORA_OP_QKV_FWD    4   /* lora_qkv_workspace_bytes only */
 #define LORA_OP_QKV_BWD    5
+#define LORA_OP_RMSNORM_MLP_FWD 6   /* lora_rmsnorm_swiglu_mlp_fwd */
+#define LORA_OP_RMSNORM_MLP_BWD 7   /* lora_rmsnorm_swiglu_mlp_bwd */
 /* or-ed into `op`: size of the minimal-memory strategy */
 #define LORA_WS_MINIMAL    0x100
 
@@ -244,6 +246,63 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r,
                         void *dX, void *dAg, void *dBg, void *dAu, void *dBu,
                         void *dAd, void *dBd,
                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * RMSNorm fused into the gate/up projections of the LoRA-SwiGLU MLP
+ * ([HF]-blog section 1: RMSNorm fused with the linear projections; [TB] 3.2
+ * the RMSNorm kernel), forward:
+ *   rstd[t] = 1 / sqrt(sum_j X[t,j]^2 / d + eps),  Xn = X rstd diag(w),
+ *   (Y, e, g) = lora_swiglu_mlp_fwd(Xn, ...)
+ * without forming Xn: the norm weight w is frozen like the base weights, so
+ * the caller passes the gate and up base weights ALREADY FOLDED,
+ * Wg' = Wg diag(w) and Wu' = Wu diag(w) (lora_fold_norm_weight, once), and
+ * the GEMMs read the raw rows X and scale each output row by rstd (an exact
+ * row factor of every term); the adapters A stay the trainable parameters
+ * and A diag(w) is formed per call.  X is the raw [T x d] input (the residual
+ * stream), norm_w [d], rstd [T] fp32 is written for the backward.  bf16 and
+ * dense weights only (LORA_ERR_UNSUPPORTED otherwise: a 4-bit weight cannot
+ * hold W diag(w); use lora_rmsnorm_fwd in front of lora_swiglu_mlp_fwd).
+ * eps finite and >= 0.  Workspace: LORA_OP_RMSNORM_MLP_FWD.
+ */
+int lora_rmsnorm_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r,
+                                float alpha, float eps, const void *X, const void *norm_w,
+                                const lora_weight *Wg, const void *Ag, const void *Bg,
+                                const lora_weight *Wu, const void *Au, const void *Bu,
+                                const lora_weight *Wd, const void *Ad, const void *Bd,
+                                void *Y, void *e_saved, void *g_saved, float *rstd,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of lora_rmsnorm_swiglu_mlp_fwd from X, rstd, e, g and dY (same
+ * folded gate/up weights): the adapter gradients of lora_swiglu_mlp_bwd
+ * taken at Xn, and dX the gradient with respect to the RAW input X,
+ *   dX = rstd gn - rstd^3 X (sum_j gn_j X_j) / d,   gn = dXn diag(w),
+ * where dXn is the MLP's input gradient (the folded projections return gn
+ * directly).  The row sum comes from the down backward's epilogue
+ * (sum_j gn_j X_j = sum_k (de e + dg g) / rstd over the ffn features) and
+ * dX is written by the dX GEMM's epilogue, so neither Xn nor gn is ever
+ * stored.  LORA_FLAG_ACCUMULATE_DX adds dX to the caller's dX (the residual
+ * branch's gradient).  dX NULL skips it.  Workspace: LORA_OP_RMSNORM_MLP_BWD.
+ */
+int lora_rmsnorm_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r,
+                                float alpha, const void *X, const void *norm_w,
+                                const float *rstd,
+                                const lora_weight *Wg, const void *Ag, const void *Bg,
+                                const lora_weight *Wu, const void *Au, const void *Bu,
+                                const lora_weight *Wd, const void *Ad, const void *Bd,
+                                const void *e_saved, const void *g_saved, const void *dY,
+                                void *dX, void *dAg, void *dBg, void *dAu, void *dBu,
+                                void *dAd, void *dBd, uint32_t flags,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * out[i][j] = bf16_rne(W[i][j] * w[j]) (one fp32 multiply): a frozen RMSNorm
+ * weight w [k] folded into a frozen base weight W [n x k] that reads the
+ * norm's output, for lora_rmsnorm_swiglu_mlp_fwd/bwd.  bf16, k % 8 == 0;
+ * out may be W itself (in place).  No workspace.
+ */
+int lora_fold_norm_weight(int dtype, int64_t n, int64_t k, const void *W, const void *norm_w,
+                          void *out, void *stream);
 
 /*
  * Standalone 4-bit decode ([CR] 2.1 fast_dequantize; [DD] 1.4):

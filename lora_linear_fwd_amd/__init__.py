@@ -11,6 +11,7 @@ Entry points mirror the C ABI in include/liblora.h:
   lora_linear_fwd, lora_linear_bwd, lora_swiglu_mlp_fwd, lora_swiglu_mlp_bwd,
   lora_dequant4, lora_decode_weight, lora_merge, lora_qkv_fwd, lora_qkv_bwd,
   lora_rmsnorm_fwd, lora_rmsnorm_bwd, lora_linear_bwd_noalloc,
+  lora_rmsnorm_swiglu_mlp_fwd, lora_rmsnorm_swiglu_mlp_bwd, lora_fold_norm_weight,
   lora_workspace_bytes, lora_qkv_workspace_bytes, lora_strerror,
   lora_abi_version.
 """
@@ -30,6 +31,7 @@ LORA_F32, LORA_BF16 = 0, 1
 LORA_W_DENSE, LORA_W_Q4, LORA_W_Q4_DQ = 0, 1, 2
 LORA_FLAG_ACCUMULATE_DX = 1
 OP_LINEAR_FWD, OP_LINEAR_BWD, OP_MLP_FWD, OP_MLP_BWD, OP_QKV_FWD, OP_QKV_BWD = 0, 1, 2, 3, 4, 5
+OP_RMSNORM_MLP_FWD, OP_RMSNORM_MLP_BWD = 6, 7
 LORA_WS_MINIMAL = 0x100
 STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
           3: "LORA_ERR_UNSUPPORTED", 4: "LORA_ERR_WORKSPACE", 5: "LORA_ERR_MISALIGNED",
@@ -39,7 +41,8 @@ EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_sw
            "lora_dequant4", "lora_workspace_bytes", "lora_strerror", "lora_abi_version",
            "lora_merge", "lora_qkv_fwd", "lora_qkv_bwd",
            "lora_qkv_workspace_bytes", "lora_decode_weight", "lora_rmsnorm_fwd",
-           "lora_rmsnorm_bwd", "lora_linear_bwd_noalloc"]
+           "lora_rmsnorm_bwd", "lora_linear_bwd_noalloc", "lora_rmsnorm_swiglu_mlp_fwd",
+           "lora_rmsnorm_swiglu_mlp_bwd", "lora_fold_norm_weight"]
 TIMING_EXPORTS = ["lora_debug_time_next"]
 (KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX,
  KC_QKV_FWD, KC_QKV_DX) = range(8)
@@ -95,6 +98,12 @@ def lib():
     L.lora_linear_bwd_noalloc.argtypes = [i32, i64, i64, i64, i64, f32, vp, W, vp, vp, vp, vp,
                                           vp, vp, u32, vp]
     L.lora_dequant4.argtypes = [i64, i64, vp, vp, vp, i32, i32, vp, vp]
+    L.lora_rmsnorm_swiglu_mlp_fwd.argtypes = [i32, i64, i64, i64, i64, f32, f32, vp, vp, W, vp, vp,
+                                              W, vp, vp, W, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lora_rmsnorm_swiglu_mlp_bwd.argtypes = [i32, i64, i64, i64, i64, f32, vp, vp, vp, W, vp, vp,
+                                              W, vp, vp, W, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, u32, vp, sz, vp]
+    L.lora_fold_norm_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp]
     L.lora_merge.argtypes = [i32, i64, i64, i64, f32, i32, W, vp, vp, vp, vp]
     L.lora_decode_weight.argtypes = [i64, i64, W, i32, vp, vp]
     L.lora_rmsnorm_fwd.argtypes = [i32, i64, i64, f32, vp, vp, vp, vp, vp]
@@ -116,7 +125,8 @@ def lib():
     for name in ("lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd",
                  "lora_swiglu_mlp_bwd", "lora_dequant4", "lora_abi_version", "lora_merge",
                  "lora_qkv_fwd", "lora_qkv_bwd", "lora_decode_weight", "lora_rmsnorm_fwd",
-                 "lora_rmsnorm_bwd", "lora_linear_bwd_noalloc"):
+                 "lora_rmsnorm_bwd", "lora_linear_bwd_noalloc", "lora_rmsnorm_swiglu_mlp_fwd",
+                 "lora_rmsnorm_swiglu_mlp_bwd", "lora_fold_norm_weight"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -523,6 +533,106 @@ def lora_swiglu_mlp_bwd(X, W: Dict[str, Weight], A, B, alpha: float, e, g, dY, n
         _ptr(o["dA_down"]), _ptr(o["dB_down"]),
         wsp, wsn, _stream(stream)),
         "lora_swiglu_mlp_bwd")
+    return o
+
+
+def lora_fold_norm_weight(W, w, out=None, stream=None):
+    """W diag(w) for a frozen base weight W [n, k] that reads the output of an
+    RMSNorm with frozen weight w [k] (bf16; out may be W itself)."""
+    torch = _torch()
+    where = "lora_fold_norm_weight"
+    _need(isinstance(W, torch.Tensor) and W.dim() == 2, f"{where}: W must be a 2-D tensor")
+    n, k = W.shape
+    _tensor(W, "W", (n, k), torch.bfloat16, W.device, where)
+    _tensor(w, "w", (k,), torch.bfloat16, W.device, where)
+    if out is not None:
+        _tensor(out, "out", (n, k), torch.bfloat16, W.device, where)
+    _on_gpu(W, where)
+    if out is None:
+        out = torch.empty_like(W)
+    _check(lib().lora_fold_norm_weight(LORA_BF16, n, k, _ptr(W), _ptr(w), _ptr(out),
+                                       _stream(stream)), where)
+    return out
+
+
+def lora_rmsnorm_swiglu_mlp_fwd(X, norm_w, eps: float, W: Dict[str, Weight], A, B, alpha: float,
+                                Y=None, e=None, g=None, rstd=None, workspace=None, stream=None):
+    """RMSNorm of the raw rows X fused into the LoRA-SwiGLU MLP.  W["gate"]
+    and W["up"] must be folded with the norm weight (lora_fold_norm_weight).
+    Returns (Y, e, g, rstd)."""
+    torch = _torch()
+    where = "lora_rmsnorm_swiglu_mlp_fwd"
+    T, d, f, r = _mlp_check(X, W, A, B, where)
+    _tensor(norm_w, "norm_w", (d,), X.dtype, X.device, where)
+    for t, name, shp, dt_ in ((Y, "Y", (T, d), X.dtype), (e, "e", (T, f), X.dtype),
+                              (g, "g", (T, f), X.dtype), (rstd, "rstd", (T,), torch.float32)):
+        if t is not None:
+            _tensor(t, name, shp, dt_, X.device, where)
+    _on_gpu(X, where)
+    dt = _dtype_code(X)
+    Y = torch.empty((T, d), dtype=X.dtype, device=X.device) if Y is None else Y
+    e = torch.empty((T, f), dtype=X.dtype, device=X.device) if e is None else e
+    g = torch.empty((T, f), dtype=X.dtype, device=X.device) if g is None else g
+    rstd = torch.empty((T,), dtype=torch.float32, device=X.device) if rstd is None else rstd
+    wsp, wsn = _workspace(OP_RMSNORM_MLP_FWD, dt, _wfmt(W["gate"]), (T, d, f, r), X.device,
+                          workspace, False, stream)
+    ws_ = [_wstruct(W[p]) for p in ("gate", "up", "down")]
+    _check(lib().lora_rmsnorm_swiglu_mlp_fwd(
+        dt, T, d, f, r, float(alpha), float(eps), _ptr(X), _ptr(norm_w),
+        ctypes.byref(ws_[0]), _ptr(A["gate"]), _ptr(B["gate"]),
+        ctypes.byref(ws_[1]), _ptr(A["up"]), _ptr(B["up"]),
+        ctypes.byref(ws_[2]), _ptr(A["down"]), _ptr(B["down"]),
+        _ptr(Y), _ptr(e), _ptr(g), _ptr(rstd), wsp, wsn, _stream(stream)), where)
+    return Y, e, g, rstd
+
+
+def lora_rmsnorm_swiglu_mlp_bwd(X, norm_w, rstd, W: Dict[str, Weight], A, B, alpha: float, e, g,
+                                dY, need_dx=True, accumulate_dx=False, out: Optional[dict] = None,
+                                workspace=None, stream=None):
+    """Backward of lora_rmsnorm_swiglu_mlp_fwd: dict with dX (gradient of
+    the raw rows; added to out["dX"] when accumulate_dx) and dA_*/dB_*."""
+    torch = _torch()
+    where = "lora_rmsnorm_swiglu_mlp_bwd"
+    T, d, f, r = _mlp_check(X, W, A, B, where)
+    _tensor(norm_w, "norm_w", (d,), X.dtype, X.device, where)
+    _tensor(rstd, "rstd", (T,), torch.float32, X.device, where)
+    _tensor(e, "e", (T, f), X.dtype, X.device, where)
+    _tensor(g, "g", (T, f), X.dtype, X.device, where)
+    _tensor(dY, "dY", (T, d), X.dtype, X.device, where)
+    o = dict(out or {})
+    if need_dx and o.get("dX") is not None:
+        _tensor(o["dX"], "dX", (T, d), X.dtype, X.device, where)
+    _need(not accumulate_dx or (need_dx and o.get("dX") is not None),
+          f"{where}: accumulate_dx needs out['dX']")
+    for p, shp in _MLP_SHAPES.items():
+        n, k = shp(d, f)
+        if o.get("dA_" + p) is not None:
+            _tensor(o["dA_" + p], "dA_" + p, (r, k), X.dtype, X.device, where)
+        if o.get("dB_" + p) is not None:
+            _tensor(o["dB_" + p], "dB_" + p, (n, r), X.dtype, X.device, where)
+    _on_gpu(X, where)
+    dt = _dtype_code(X)
+    if need_dx and o.get("dX") is None:
+        o["dX"] = torch.empty((T, d), dtype=X.dtype, device=X.device)
+    if not need_dx:
+        o["dX"] = None
+    for p in ("gate", "up", "down"):
+        if o.get("dA_" + p) is None:
+            o["dA_" + p] = torch.empty_like(A[p])
+        if o.get("dB_" + p) is None:
+            o["dB_" + p] = torch.empty_like(B[p])
+    wsp, wsn = _workspace(OP_RMSNORM_MLP_BWD, dt, _wfmt(W["gate"]), (T, d, f, r), X.device,
+                          workspace, False, stream)
+    ws_ = [_wstruct(W[p]) for p in ("gate", "up", "down")]
+    flags = LORA_FLAG_ACCUMULATE_DX if accumulate_dx else 0
+    _check(lib().lora_rmsnorm_swiglu_mlp_bwd(
+        dt, T, d, f, r, float(alpha), _ptr(X), _ptr(norm_w), _ptr(rstd),
+        ctypes.byref(ws_[0]), _ptr(A["gate"]), _ptr(B["gate"]),
+        ctypes.byref(ws_[1]), _ptr(A["up"]), _ptr(B["up"]),
+        ctypes.byref(ws_[2]), _ptr(A["down"]), _ptr(B["down"]),
+        _ptr(e), _ptr(g), _ptr(dY), _ptr(o["dX"]),
+        _ptr(o["dA_gate"]), _ptr(o["dB_gate"]), _ptr(o["dA_up"]), _ptr(o["dB_up"]),
+        _ptr(o["dA_down"]), _ptr(o["dB_down"]), flags, wsp, wsn, _stream(stream)), where)
     return o
 
 

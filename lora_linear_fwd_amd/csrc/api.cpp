@@ -141,10 +141,14 @@ inline bool mlp_bwd_dual(int64_t r) { return rs_of(r) <= 32; }
 struct MlpBwdPlan {
   size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, epi_gu_nn, side_gu_nt, side_gu_nn;
   size_t side_g, side_u, pt_d, pt_g, pt_u, part_u, part_v;
-  size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, total;
+  size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, cpart, nkk, total;
 };
-MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) {
+MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, bool norm = false) {
   Bump b; MlpBwdPlan p{};
+  if (norm) {   // folded RMSNorm: row partials per 64-column block of the down backward
+    p.cpart = b.take((size_t)cdiv(f, 256) * 4 * T * 4);
+    p.nkk = b.take((size_t)T * 4);
+  }
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   if (wcopy) p.wbuf = b.take((size_t)2 * d * f * 2);   // Wd^T, later [Wg^T | Wu^T]
   // de and dg interleaved as one [T x 2f] matrix (dg = de + f): the dX
@@ -329,25 +333,28 @@ struct Prep {
   PrepBatch b{};
   unsigned blocks = 0;
   void add(int kind, bf16_t *dst, int64_t a, int64_t bb, const void *src0, const void *src1,
-           int64_t r, int64_t split, int tr, const void *src2 = nullptr, int64_t split2 = 0) {
+           int64_t r, int64_t split, int tr, const void *src2 = nullptr, int64_t split2 = 0,
+           const void *cs = nullptr) {
     const int64_t cnt = a * bb;
     if (cnt == 0) return;
     PrepJob &j = b.job[b.njobs];
     j = PrepJob{dst, (const bf16_t *)src0, (const bf16_t *)src1, (const bf16_t *)src2, kind,
-                (int)a, (int)bb, (int)r, (int)split, (int)split2, tr};
+                (int)a, (int)bb, (int)r, (int)split, (int)split2, tr, (const bf16_t *)cs};
     b.start[b.njobs] = blocks;
     blocks += (unsigned)cdiv(cnt, 256);
     ++b.njobs;
   }
   // side[q][k], q < RS, k < K
   void side(bf16_t *dst, int RS, int64_t K, const void *s0, const void *s1, int64_t r,
-            int64_t ksplit, int tr, const void *s2 = nullptr, int64_t ksplit2 = 0) {
-    add(0, dst, RS, K, s0, s1, r, ksplit, tr, s2, ksplit2);
+            int64_t ksplit, int tr, const void *s2 = nullptr, int64_t ksplit2 = 0,
+            const void *cs = nullptr) {
+    add(0, dst, RS, K, s0, s1, r, ksplit, tr, s2, ksplit2, cs);
   }
   // epi[row][q], row < rows, q < RS
   void epi(bf16_t *dst, int64_t rows, int RS, const void *s0, const void *s1, int64_t r,
-           int64_t rsplit, int tr, const void *s2 = nullptr, int64_t rsplit2 = 0) {
-    add(1, dst, rows, RS, s0, s1, r, rsplit, tr, s2, rsplit2);
+           int64_t rsplit, int tr, const void *s2 = nullptr, int64_t rsplit2 = 0,
+           const void *cs = nullptr) {
+    add(1, dst, rows, RS, s0, s1, r, rsplit, tr, s2, rsplit2, cs);
   }
   int launch(hipStream_t st) {
     if (!b.njobs) return LORA_OK;
@@ -361,7 +368,8 @@ struct Prep {
 // out = Z . SIDE^T over all K (deterministic split-K); fp32 and/or scaled bf16
 int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, const bf16_t *Z1,
               int64_t ksplit, int64_t ldz, const bf16_t *E, const bf16_t *G, const bf16_t *side,
-              float *part, float *out32, bf16_t *outbf, float scale, hipStream_t st) {
+              float *part, float *out32, bf16_t *outbf, float scale, hipStream_t st,
+              const float *rowscale = nullptr) {
   if (T == 0) return LORA_OK;
   const NTSplit sp = nt_split(T, K);
   SkinnyNTArgs a{(int)T, (int)K, (int)ksplit, sp.kchunk, Z0, Z1, ldz, E, G, side, part};
@@ -380,7 +388,7 @@ int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, cons
   HIP_TRY(hipGetLastError());
   const int64_t cnt = T * RS;
   hipLaunchKernelGGL(k_reduce_side, dim3(blocks_for(cnt)), dim3(256), 0, st, part, sp.ks, cnt,
-                     scale, out32, outbf);
+                     scale, out32, outbf, rowscale, RS);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
 }
@@ -390,7 +398,7 @@ int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const 
               const bf16_t *Z1, int64_t nsplit, int64_t ldz, const bf16_t *E, const bf16_t *G,
               float *part, int64_t r, float scale, int transposed, bf16_t *out0, bf16_t *out1,
               int64_t out_nsplit, hipStream_t st, bf16_t *out2 = nullptr,
-              int64_t out_nsplit2 = 0) {
+              int64_t out_nsplit2 = 0, const bf16_t *colscale = nullptr) {
   const TNSplit sp = tn_split(T, N);
   SkinnyTNArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, P, Z0, Z1, ldz, E, G, part};
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)sp.ts);
@@ -407,7 +415,7 @@ int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const 
 #undef STN
   HIP_TRY(hipGetLastError());
   ReduceTNArgs ra{part,       sp.ts, RS, (int)N, (int)r, (int)out_nsplit, scale, transposed, out0,
-                  out1,       (int)r, out2, (int)out_nsplit2, (int)(2 * r)};
+                  out1,       (int)r, out2, (int)out_nsplit2, (int)(2 * r), colscale};
   hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)RS * N)), dim3(256), 0, st, ra);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
@@ -460,7 +468,7 @@ int skinny_dual(int RS, bool zswiglu, int64_t T, int64_t N, int64_t nsplit, int6
                 const bf16_t *S0, const bf16_t *S1, const bf16_t *P0, const bf16_t *P1,
                 float *part_u, float *part_v, int64_t r, int RSout, float uscale, float *uout32,
                 bf16_t *uoutbf, float vscale, int transposed, bf16_t *vout0, bf16_t *vout1,
-                hipStream_t st) {
+                hipStream_t st, const float *urowscale = nullptr) {
   const DualSplit sp = dual_split(T, N, nsplit);
   DualArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, sp.nb0, ldz, Z0, Z1, E, G, S0, S1, P0, P1,
              (int)ldp_of(T), part_u, part_v};
@@ -478,12 +486,12 @@ int skinny_dual(int RS, bool zswiglu, int64_t T, int64_t N, int64_t nsplit, int6
 #undef SDU
     HIP_TRY(hipGetLastError());
     ReduceUArgs ru{part_u, (int)T, RS, RSout, (int)r, sp.nb1 ? 2 : 1, sp.nb0, sp.nb1, uscale,
-                   uout32, uoutbf};
+                   uout32, uoutbf, urowscale};
     hipLaunchKernelGGL(k_reduce_dual_u, dim3(blocks_for(T * RSout)), dim3(256), 0, st, ru);
     HIP_TRY(hipGetLastError());
   }
   ReduceTNArgs rv{part_v, T > 0 ? sp.ts : 0, RS, (int)N, (int)r, (int)nsplit, vscale, transposed,
-                  vout0, vout1, 0, nullptr, 0, 0};
+                  vout0, vout1, 0, nullptr, 0, 0, nullptr};
   hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)RS * N)), dim3(256), 0, st, rv);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
@@ -642,7 +650,9 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, 
   op &= 0xFF;
   if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4 && wfmt != LORA_W_Q4_DQ) return 0;
   if (T < 0 || kd <= 0 || nf <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
-  if (dtype == LORA_F32) return plan_f32(op, T, kd, nf, r);
+  if (dtype == LORA_F32)
+    return (op == LORA_OP_RMSNORM_MLP_FWD || op == LORA_OP_RMSNORM_MLP_BWD) ? 0
+                                                                            : plan_f32(op, T, kd, nf, r);
   if (dtype != LORA_BF16) return 0;
   // only 4-bit weights are copied: decoded for the forwards, decoded and
   // transposed for the backwards (dense weights are read in place: the NN
@@ -653,6 +663,11 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, 
     case LORA_OP_LINEAR_BWD: return plan_lin_bwd(T, kd, nf, r, bwd_copy).total;
     case LORA_OP_MLP_FWD: return plan_mlp_fwd(T, kd, nf, r, fwd_copy).total;
     case LORA_OP_MLP_BWD: return plan_mlp_bwd(T, kd, nf, r, bwd_copy).total;
+    // the folded-norm MLP takes dense weights only
+    case LORA_OP_RMSNORM_MLP_FWD:
+      return wfmt == LORA_W_DENSE ? plan_mlp_fwd(T, kd, nf, r, false).total : 0;
+    case LORA_OP_RMSNORM_MLP_BWD:
+      return wfmt == LORA_W_DENSE ? plan_mlp_bwd(T, kd, nf, r, false, true).total : 0;
   }
   return 0;
 }
@@ -805,11 +820,34 @@ int lora_linear_bwd_noalloc(int dtype, int64_t T, int64_t k, int64_t n, int64_t 
                          stream);
 }
 
-int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+// An RMSNorm folded into the gate/up projections: the caller's gate/up
+// weights are W diag(w) (lora_fold_norm_weight), the GEMMs read the raw rows
+// X and scale each output row by rstd; the adapters' A become A diag(w) per
+// call.  rstd is written by the forward and read by the backward.
+struct NormFuse {
+  const bf16_t *w;
+  float eps;
+  float *rstd;
+  bool accumulate;   // backward: dX += the norm's input gradient
+};
+
+// every RMSNorm-specific argument; the fused path takes bf16 and dense
+// weights only (a 4-bit weight cannot hold W diag(w))
+static int check_norm(int dtype, int64_t T, const NormFuse &nf, const WeightView &wg,
+               const WeightView &wu, const WeightView &wd) {
+  if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (wg.q4 || wu.q4 || wd.q4) return LORA_ERR_UNSUPPORTED;
+  if (!(nf.eps >= 0.f) || !std::isfinite(nf.eps)) return LORA_ERR_UNSUPPORTED;
+  LORA_TRY(check_ptrs({nf.w}));
+  LORA_TRY(check_tok_ptrs(T, {nf.rstd}));
+  return LORA_OK;
+}
+
+static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
                         const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
-                        const lora_weight *Wu, const void *Au, const void *Bu,
-                        const lora_weight *Wd, const void *Ad, const void *Bd, void *Y,
-                        void *e_saved, void *g_saved, void *ws, size_t ws_bytes, void *stream) {
+                 const lora_weight *Wu, const void *Au, const void *Bu, const lora_weight *Wd,
+                 const void *Ad, const void *Bd, void *Y, void *e_saved, void *g_saved, void *ws,
+                 size_t ws_bytes, void *stream, const NormFuse *nf) {
   LORA_TRY(check_dims(dtype, T, d, f, r));
   WeightView wg, wu, wd;
   LORA_TRY(check_weight(Wg, dtype, d, wg));
@@ -818,8 +856,10 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   if (wg.fmt != wu.fmt) return LORA_ERR_UNSUPPORTED;
   LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd}));
   LORA_TRY(check_tok_ptrs(T, {X, Y, e_saved, g_saved}));
+  if (nf) LORA_TRY(check_norm(dtype, T, *nf, wg, wu, wd));
   bool fast;
-  LORA_TRY(check_ws(LORA_OP_MLP_FWD, dtype, Wg->fmt, T, d, f, r, ws, ws_bytes, fast));
+  LORA_TRY(check_ws(nf ? LORA_OP_RMSNORM_MLP_FWD : LORA_OP_MLP_FWD, dtype, Wg->fmt, T, d, f, r, ws,
+                    ws_bytes, fast));
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
   if (T == 0) return LORA_OK;
@@ -852,12 +892,17 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   bf16_t *hbf = (bf16_t *)(w + pl.hbf);
   float *hpart = (float *)(w + pl.hpart);
   Prep prep;
-  prep.side(side_gu, RS1, d, Ag, Au, r, d, 0);
+  prep.side(side_gu, RS1, d, Ag, Au, r, d, 0, nullptr, 0, nf ? nf->w : nullptr);   // [Ag; Au] (diag w)
   prep.epi(epi_gu, 2 * f, RS1, Bg, Bu, r, f, 0);
   prep.side(side_d, RS2, f, Ad, nullptr, r, f, 0);
   prep.epi(epi_d, d, RS2, Bd, nullptr, r, d, 0);
   LORA_TRY(prep.launch(st));
   const bf16_t *Xb = (const bf16_t *)X;
+  if (nf) {   // the rows' rstd only: the normalised rows are never formed
+    hipLaunchKernelGGL(k_rmsnorm_fwd<false>, dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, X,
+                       (const void *)nf->w, nf->eps, (int)T, (int)d, (void *)nullptr, nf->rstd);
+    HIP_TRY(hipGetLastError());
+  }
 
   // gate + up with the SwiGLU epilogue
   GemmArgs a = gemm_base();
@@ -867,6 +912,7 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   a.gu_f = (int)f;
   a.rs = RS1; a.epi = epi_gu;
   a.E = (bf16_t *)e_saved; a.G = (bf16_t *)g_saved; a.H = h;
+  if (nf) a.rowscale = nf->rstd;
   a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, 128);
   // [s X Ag^T | s X Au^T], once per call
   LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
@@ -893,13 +939,12 @@ int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   return run_gemm(KC_DOWN_FWD, false, wd.q4, EPI_STORE, b, st);
 }
 
-int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
-                        const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
-                        const lora_weight *Wu, const void *Au, const void *Bu,
-                        const lora_weight *Wd, const void *Ad, const void *Bd,
-                        const void *e_saved, const void *g_saved, const void *dY, void *dX,
-                        void *dAg, void *dBg, void *dAu, void *dBu, void *dAd, void *dBd,
-                        void *ws, size_t ws_bytes, void *stream) {
+static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+                 const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
+                 const lora_weight *Wu, const void *Au, const void *Bu, const lora_weight *Wd,
+                 const void *Ad, const void *Bd, const void *e_saved, const void *g_saved,
+                 const void *dY, void *dX, void *dAg, void *dBg, void *dAu, void *dBu, void *dAd,
+                 void *dBd, void *ws, size_t ws_bytes, void *stream, const NormFuse *nf) {
   LORA_TRY(check_dims(dtype, T, d, f, r));
   WeightView wg, wu, wd;
   LORA_TRY(check_weight(Wg, dtype, d, wg));
@@ -909,8 +954,10 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(check_ptrs({Ag, Bg, Au, Bu, Ad, Bd, dAg, dBg, dAu, dBu, dAd, dBd}));
   LORA_TRY(check_tok_ptrs(T, {X, e_saved, g_saved, dY}));
   if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
+  if (nf) LORA_TRY(check_norm(dtype, T, *nf, wg, wu, wd));
   bool fast;
-  LORA_TRY(check_ws(LORA_OP_MLP_BWD, dtype, Wg->fmt, T, d, f, r, ws, ws_bytes, fast));
+  LORA_TRY(check_ws(nf ? LORA_OP_RMSNORM_MLP_BWD : LORA_OP_MLP_BWD, dtype, Wg->fmt, T, d, f, r, ws,
+                    ws_bytes, fast));
   hipStream_t st = (hipStream_t)stream;
   const float s = alpha / (float)r;
   char *w = (char *)ws;
@@ -942,7 +989,7 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   // 4-bit gate/up weights (the format the workspace was sized for): a decoded,
   // transposed copy per dX GEMM; dense weights are read in place (NN GEMM)
   const bool wcopy = fast && wg.q4;
-  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r, wcopy);
+  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r, wcopy, nf != nullptr);
   bf16_t *wt = (bf16_t *)(w + pl.wbuf);
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   bf16_t *de = (bf16_t *)(w + pl.de), *dg = (bf16_t *)(w + pl.dg);
@@ -973,9 +1020,16 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   } else {
     prep.side(side_gu_nn, RS1, 2 * f, Bg, Bu, r, f, 1);     // blockdiag(Bg, Bu)^T
   }
-  prep.epi(epi_gu_nn, d, RS1, Ag, Au, r, d, 1);             // [Ag;Au]^T [d x RS1]
-  prep.side(side_gu_nt, RS1, d, Ag, Au, r, d, 0);           // [Ag;Au] [RS1 x d]
+  // [Ag;Au]^T [d x RS1] and [Ag;Au] [RS1 x d], times diag(w) under a folded norm
+  const bf16_t *nw = nf ? nf->w : nullptr;
+  prep.epi(epi_gu_nn, d, RS1, Ag, Au, r, d, 1, nullptr, 0, nw);
+  prep.side(side_gu_nt, RS1, d, Ag, Au, r, d, 0, nullptr, 0, nw);
   LORA_TRY(prep.launch(st));
+  // folded norm: per-row sums of de e + dg g per 64-column block of the down
+  // backward, then the coefficient of x in the norm's input gradient
+  float *cpart = nf ? (float *)(w + pl.cpart) : nullptr;
+  float *nkk = nf ? (float *)(w + pl.nkk) : nullptr;
+  const float *rstd = nf ? nf->rstd : nullptr;
 
   if (T > 0) {
     // 1. dh = dY Wd + s (dY Bd) Ad with the SwiGLU-derivative epilogue -> de, dg
@@ -997,8 +1051,14 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     a.rs = RS2; a.epi = epi_d_nn;
     a.Ein = eb; a.Gin = gb; a.DE = de; a.DG = dg; a.ldd = 2 * f;
     a.hglob = gdbf;
+    a.cpart = cpart;
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
     LORA_TRY(run_gemm(KC_DOWN_BWD, nn, q4, EPI_SWIGLU_BWD, a, st));
+    if (nf) {
+      hipLaunchKernelGGL(k_norm_coef, dim3(blocks_for(T)), dim3(256), 0, st, cpart,
+                         (int)(a.tiles_n * 4), (int)T, rstd, 1.0f / (float)d, nkk);
+      HIP_TRY(hipGetLastError());
+    }
   }
   // 2. one pass over h = silu(e) g (recomputed): H_d = h Ad^T (fp32, for dBd)
   //    and dAd = s G_d^T h
@@ -1019,7 +1079,7 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   if (T > 0) {
     // 4. H_gu = X [Ag; Au]^T (fp32), its two halves transposed to bf16
     LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,
-                       nullptr, 1.f, st));
+                       nullptr, 1.f, st, rstd));
     if (dual) {
       LORA_TRY(pack_pt(hgu32, T, RS1, 0, (int)r, RS2, pt_g, st));
       LORA_TRY(pack_pt(hgu32, T, RS1, (int)r, (int)r, RS2, pt_u, st));
@@ -1030,11 +1090,11 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   if (dual) {
     LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, 2 * f, de, dg, nullptr, nullptr, side_g, side_u,
                          pt_g, pt_u, part_u, part_v, r, RS1, s, ggu32, ggubf, s, 1, (bf16_t *)dBg,
-                         (bf16_t *)dBu, st));
+                         (bf16_t *)dBu, st, rstd));
   } else {
     if (T > 0)
       LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, 2 * f, nullptr, nullptr, side_gu_nn, ntpart,
-                         ggu32, ggubf, s, st));
+                         ggu32, ggubf, s, st, rstd));
     LORA_TRY(skinny_tn(RS1, false, T, 2 * f, hgu32, de, dg, f, 2 * f, nullptr, nullptr, tnpart, r, s,
                        1, (bf16_t *)dBg, (bf16_t *)dBu, f, st));
   }
@@ -1056,12 +1116,77 @@ int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     b.rs = RS1; b.epi = epi_gu_nn;
     b.C = (bf16_t *)dX; b.ldc = d;
     b.hglob = ggubf;
+    if (nf) {   // dX = rstd gn - kk x (+ the residual stream's gradient)
+      b.nrm_x = Xb; b.nrm_rs = rstd; b.nrm_kk = nkk;
+      b.accumulate = nf->accumulate;
+    }
     b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
     LORA_TRY(run_gemm(KC_GATEUP_BWD, nn, q4, EPI_STORE, b, st));
   }
-  // 7. [dAg; dAu] = s G_gu^T X
+  // 7. [dAg; dAu] = s G_gu^T X  (folded norm: G_gu rows scaled by rstd, the
+  //    result's columns by w, so X stands in for the normalised rows)
   LORA_TRY(skinny_tn(RS1, false, T, d, ggu32, Xb, Xb, d, d, nullptr, nullptr, tnpart, r, s, 0,
-                     (bf16_t *)dAg, (bf16_t *)dAu, d, st));
+                     (bf16_t *)dAg, (bf16_t *)dAu, d, st, nullptr, 0, nw));
+  return LORA_OK;
+}
+
+int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+                        const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
+                        const lora_weight *Wu, const void *Au, const void *Bu,
+                        const lora_weight *Wd, const void *Ad, const void *Bd, void *Y,
+                        void *e_saved, void *g_saved, void *ws, size_t ws_bytes, void *stream) {
+  return mlp_fwd_impl(dtype, T, d, f, r, alpha, X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, Y, e_saved,
+                      g_saved, ws, ws_bytes, stream, nullptr);
+}
+
+int lora_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+                        const void *X, const lora_weight *Wg, const void *Ag, const void *Bg,
+                        const lora_weight *Wu, const void *Au, const void *Bu,
+                        const lora_weight *Wd, const void *Ad, const void *Bd,
+                        const void *e_saved, const void *g_saved, const void *dY, void *dX,
+                        void *dAg, void *dBg, void *dAu, void *dBu, void *dAd, void *dBd,
+                        void *ws, size_t ws_bytes, void *stream) {
+  return mlp_bwd_impl(dtype, T, d, f, r, alpha, X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, e_saved,
+                      g_saved, dY, dX, dAg, dBg, dAu, dBu, dAd, dBd, ws, ws_bytes, stream, nullptr);
+}
+
+int lora_rmsnorm_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+                                float eps, const void *X, const void *norm_w,
+                                const lora_weight *Wg, const void *Ag, const void *Bg,
+                                const lora_weight *Wu, const void *Au, const void *Bu,
+                                const lora_weight *Wd, const void *Ad, const void *Bd, void *Y,
+                                void *e_saved, void *g_saved, float *rstd, void *ws,
+                                size_t ws_bytes, void *stream) {
+  const NormFuse nf{(const bf16_t *)norm_w, eps, rstd, false};
+  return mlp_fwd_impl(dtype, T, d, f, r, alpha, X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, Y, e_saved,
+                      g_saved, ws, ws_bytes, stream, &nf);
+}
+
+int lora_rmsnorm_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, float alpha,
+                                const void *X, const void *norm_w, const float *rstd,
+                                const lora_weight *Wg, const void *Ag, const void *Bg,
+                                const lora_weight *Wu, const void *Au, const void *Bu,
+                                const lora_weight *Wd, const void *Ad, const void *Bd,
+                                const void *e_saved, const void *g_saved, const void *dY, void *dX,
+                                void *dAg, void *dBg, void *dAu, void *dBu, void *dAd, void *dBd,
+                                uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  if (flags & ~(uint32_t)LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
+  const NormFuse nf{(const bf16_t *)norm_w, 0.f, const_cast<float *>(rstd),
+                    (flags & LORA_FLAG_ACCUMULATE_DX) != 0};
+  return mlp_bwd_impl(dtype, T, d, f, r, alpha, X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, e_saved,
+                      g_saved, dY, dX, dAg, dBg, dAu, dBu, dAd, dBd, ws, ws_bytes, stream, &nf);
+}
+
+int lora_fold_norm_weight(int dtype, int64_t n, int64_t k, const void *W, const void *norm_w,
+                          void *out, void *stream) {
+  if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (n <= 0 || k <= 0 || n > kMaxFeatures || k > kMaxFeatures || (k % 8)) return LORA_ERR_BAD_SHAPE;
+  LORA_TRY(check_ptrs({W, norm_w, out}));
+  if (n * k == 0) return LORA_OK;
+  hipLaunchKernelGGL(k_fold_colscale, dim3(blocks_for(n * k / 8)), dim3(256), 0,
+                     (hipStream_t)stream, (const bf16_t *)W, (const bf16_t *)norm_w, n, k,
+                     (bf16_t *)out);
+  HIP_TRY(hipGetLastError());
   return LORA_OK;
 }
 

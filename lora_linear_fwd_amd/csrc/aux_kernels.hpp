@@ -115,14 +115,16 @@ __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
   }
 }
 
-// out32[i] = sum_ks part[ks][i] (fixed order); outbf[i] = bf16(scale * out32[i])
+// out32[i] = sum_ks part[ks][i] (fixed order); outbf[i] = bf16(scale * out32[i]).
+// With rowscale (rows of RS values), out32 is multiplied by rowscale[i / RS]
+// (the bf16 copy is not).
 __global__ void k_reduce_side(const float *part, int ks, int64_t count, float scale,
-                              float *out32, bf16_t *outbf) {
+                              float *out32, bf16_t *outbf, const float *rowscale, int RS) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   float s = 0.f;
   for (int k = 0; k < ks; ++k) s += part[(int64_t)k * count + i];
-  if (out32) out32[i] = s;
+  if (out32) out32[i] = rowscale ? s * rowscale[i / RS] : s;
   if (outbf) {
     const uint32_t w = pack_bf16x2(scale * s, 0.f);
     outbf[i] = (bf16_t)(w & 0xFFFFu);
@@ -264,6 +266,8 @@ struct ReduceTNArgs {
   // n >= nsplit2 with q in [q2, q2 + r)
   bf16_t *out2;
   int nsplit2, q2;
+  // optional bf16 column scale (row-major layout: out[q][n] *= colscale[n])
+  const bf16_t *colscale;
 };
 __global__ void k_reduce_tn(const ReduceTNArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -293,8 +297,10 @@ __global__ void k_reduce_tn(const ReduceTNArgs a) {
     for (int u = 0; u < 4; ++u) s4[u] += a.part[(int64_t)(k + u) * count + i];
   }
   for (int u = 0; k < a.ts; ++k, ++u) s4[u] += a.part[(int64_t)k * count + i];
-  const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-  const uint32_t w = pack_bf16x2(a.scale * s, 0.f);
+  float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  s *= a.scale;
+  if (a.colscale && !a.transposed) s *= bf16_to_f32(a.colscale[n]);
+  const uint32_t w = pack_bf16x2(s, 0.f);
   *dst = (bf16_t)(w & 0xFFFFu);
 }
 
@@ -470,6 +476,7 @@ struct ReduceUArgs {
   float scale;
   float *out32;
   bf16_t *outbf;
+  const float *rowscale;   // optional: out32[t][.] *= rowscale[t] (not outbf)
 };
 __global__ void k_reduce_dual_u(const ReduceUArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -497,7 +504,7 @@ __global__ void k_reduce_dual_u(const ReduceUArgs a) {
     for (int u = 0; jj < je; ++jj, ++u) s4[u] += src[(int64_t)jj * stride];
   }
   const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-  if (a.out32) a.out32[i] = s;
+  if (a.out32) a.out32[i] = a.rowscale ? s * a.rowscale[t] : s;
   if (a.outbf) {
     const uint32_t w = pack_bf16x2(a.scale * s, 0.f);
     a.outbf[i] = (bf16_t)(w & 0xFFFFu);
@@ -538,6 +545,10 @@ struct PrepJob {
   const bf16_t *src0, *src1, *src2;
   int kind;            // 0: side [a = RS x b = K], 1: epi [a = rows x b = RS]
   int a, b, r, split, split2, tr;
+  // optional bf16 scale per in_feature of an adapter A (side !tr: per k;
+  // epi tr: per row), applied as one fp32 multiply rounded to bf16: the
+  // operand becomes A diag(colscale)
+  const bf16_t *colscale;
 };
 constexpr int kMaxPrepJobs = 8;
 struct PrepBatch {
@@ -560,6 +571,8 @@ __global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
     if (blk < 3 && src[blk]) {
       if (!jb.tr) {
         v = src[blk][(int64_t)(q - blk * r) * K + k];
+        if (jb.colscale)
+          v = (bf16_t)(pack_bf16x2(bf16_to_f32(v) * bf16_to_f32(jb.colscale[k]), 0.f) & 0xFFFFu);
       } else {
         const int lo = blk == 0 ? 0 : (blk == 1 ? jb.split : jb.split2);
         const int hi = blk == 0 ? jb.split : (blk == 1 ? (jb.src2 ? jb.split2 : K) : K);
@@ -576,6 +589,8 @@ __global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
         if (row >= lo && row < hi) v = src[blk][(int64_t)(row - lo) * r + (q - blk * r)];
       } else {
         v = src[blk][(int64_t)(q - blk * r) * rows + row];
+        if (jb.colscale)
+          v = (bf16_t)(pack_bf16x2(bf16_to_f32(v) * bf16_to_f32(jb.colscale[row]), 0.f) & 0xFFFFu);
       }
     }
   }
@@ -832,6 +847,46 @@ __global__ void k_swiglu_bwd_f32(const float *e, const float *g, const float *dh
   const float z = e[i], sg = 1.0f / (1.0f + expf(-z));
   de[i] = dh[i] * g[i] * sg * (1.0f + z * (1.0f - sg));
   dg[i] = dh[i] * z * sg;
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm folded into the projections that follow it
+// ---------------------------------------------------------------------------
+// out[i][j] = bf16(W[i][j] * w[j]): the frozen norm weight folded into a
+// frozen base weight [n x k] (one fp32 multiply, rounded once).  8 elements
+// per thread.
+__global__ __launch_bounds__(256) void k_fold_colscale(const bf16_t *W, const bf16_t *w, int64_t n,
+                                                       int64_t k, bf16_t *out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // 8-element group
+  if (g * 8 >= n * k) return;
+  const int64_t j0 = (g * 8) % k;   // k % 8 == 0: a group stays inside one row
+  const u32x4 a = gload16(W + g * 8), b = gload16(w + j0);
+  u32x4 o;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    o[t] = pack_bf16x2(bf16lo(a[t]) * bf16lo(b[t]), bf16hi(a[t]) * bf16hi(b[t]));
+  gstore16(out + g * 8, o);
+}
+
+// Coefficient of x in the RMSNorm input gradient, from the down-projection
+// backward's per-row partial sums S_p[t] of de e + dg g over column blocks:
+//   kk[t] = rstd[t]^2 (sum_p S_p[t]) / d     (fixed summation order)
+// (sum_j gn_j x_j = S / rstd with gn = dXn w the gradient the folded
+// projections return, so rstd^3 x (gn . x) / d = kk x.)
+__global__ void k_norm_coef(const float *part, int np, int T, const float *rstd, float inv_d,
+                            float *kk) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  int p = 0;
+  for (; p + 4 <= np; p += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s4[u] += part[(int64_t)(p + u) * T + t];
+  }
+  for (int u = 0; p < np; ++p, ++u) s4[u] += part[(int64_t)p * T + t];
+  const float S = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  const float r = rstd[t];
+  kk[t] = r * r * S * inv_d;
 }
 
 }  // namespace lora

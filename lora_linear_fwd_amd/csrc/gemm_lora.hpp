@@ -102,6 +102,18 @@ struct GemmArgs {
   const bf16_t *B2;
   bf16_t *C1, *C2;
   int64_t ldc1, ldc2;
+  // RMSNorm folded into the projections that follow it (eight-wave kernel):
+  //   rowscale  SwiGLU forward: e, g of row m are scaled by rowscale[m]
+  //             (rstd; the GEMM reads the raw rows and weights W diag(w))
+  //   cpart     SwiGLU backward: cpart[(tile column * 4 + 64-column block) *
+  //             M + m] = sum over the block's columns of de e + dg g
+  //             (de, dg as stored); nullptr: not formed
+  //   nrm_x     store: C = nrm_rs[m] acc - nrm_kk[m] nrm_x[m][n] (before any
+  //             accumulation), the RMSNorm input gradient; nrm_x is [M x N]
+  const float *rowscale;
+  float *cpart;
+  const bf16_t *nrm_x;
+  const float *nrm_rs, *nrm_kk;
 };
 
 // XCD-aware, grouped tile order.  Workgroups are dispatched round-robin over

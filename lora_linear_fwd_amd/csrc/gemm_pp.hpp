@@ -508,12 +508,20 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         const u32x4 e0 = lds_read16(reg, ep_off(r, 2 * q)), e1 = lds_read16(reg, ep_off(r, 2 * q + 1));
         const u32x4 g0 = lds_read16(reg, ep_off(r, 8 + 2 * q)), g1 = lds_read16(reg, ep_off(r, 9 + 2 * q));
         if (m < M && jf < f) {
-          const float ev[8] = {__uint_as_float(e0[0]), __uint_as_float(e0[1]), __uint_as_float(e0[2]),
-                               __uint_as_float(e0[3]), __uint_as_float(e1[0]), __uint_as_float(e1[1]),
-                               __uint_as_float(e1[2]), __uint_as_float(e1[3])};
-          const float gv[8] = {__uint_as_float(g0[0]), __uint_as_float(g0[1]), __uint_as_float(g0[2]),
-                               __uint_as_float(g0[3]), __uint_as_float(g1[0]), __uint_as_float(g1[1]),
-                               __uint_as_float(g1[2]), __uint_as_float(g1[3])};
+          float ev[8] = {__uint_as_float(e0[0]), __uint_as_float(e0[1]), __uint_as_float(e0[2]),
+                         __uint_as_float(e0[3]), __uint_as_float(e1[0]), __uint_as_float(e1[1]),
+                         __uint_as_float(e1[2]), __uint_as_float(e1[3])};
+          float gv[8] = {__uint_as_float(g0[0]), __uint_as_float(g0[1]), __uint_as_float(g0[2]),
+                         __uint_as_float(g0[3]), __uint_as_float(g1[0]), __uint_as_float(g1[1]),
+                         __uint_as_float(g1[2]), __uint_as_float(g1[3])};
+          if (p.rowscale) {   // folded RMSNorm: the row's rstd
+            const float rs = p.rowscale[m];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              ev[t] *= rs;
+              gv[t] *= rs;
+            }
+          }
           u32x4 ew, gw, hw;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -538,11 +546,21 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         const int r = it * 8 + (lane >> 3);
         const int m = mrow0 + r;
         const u32x4 a0 = lds_read16(reg, ep_off(r, 2 * q)), a1 = lds_read16(reg, ep_off(r, 2 * q + 1));
-        if (m >= M || n >= N) continue;
+        const bool valid = m < M && n < N;
         float v[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
                       __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
                       __uint_as_float(a1[2]), __uint_as_float(a1[3])};
         if constexpr (EPI == EPI_STORE) {
+          if (!valid) continue;
+          if (p.nrm_x) {   // RMSNorm input gradient from the folded projections' output
+            const u32x4 xv = gload16(p.nrm_x + (int64_t)m * N + n);
+            const float rs = p.nrm_rs[m], kk = p.nrm_kk[m];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              v[2 * t] = rs * v[2 * t] - kk * bf16lo(xv[t]);
+              v[2 * t + 1] = rs * v[2 * t + 1] - kk * bf16hi(xv[t]);
+            }
+          }
           bf16_t *cb = p.C;
           int64_t ldc = p.ldc;
           int ncs = 0;
@@ -566,27 +584,42 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
           gstore16(dst, w);
         } else {  // EPI_SWIGLU_BWD: v = dh
-          const int64_t off = (int64_t)m * N + n;
-          const u32x4 ev = ein[it], gv = gin[it];
-          u32x4 dew, dgw;
+          float csum = 0.f;
+          if (valid) {
+            const u32x4 ev = ein[it], gv = gin[it];
+            u32x4 dew, dgw;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float de[2], dg[2];
+            for (int t = 0; t < 4; ++t) {
+              float de[2], dg[2];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
-              const float gg = h2 ? bf16hi(gv[t]) : bf16lo(gv[t]);
-              const float dh = v[2 * t + h2];
-              const float sg = sigmoidf_fast(e);
-              dg[h2] = dh * e * sg;
-              de[h2] = dh * gg * sg * (1.0f + e * (1.0f - sg));
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
+                const float gg = h2 ? bf16hi(gv[t]) : bf16lo(gv[t]);
+                const float dh = v[2 * t + h2];
+                const float sg = sigmoidf_fast(e);
+                dg[h2] = dh * e * sg;
+                de[h2] = dh * gg * sg * (1.0f + e * (1.0f - sg));
+              }
+              dew[t] = pack_bf16x2(de[0], de[1]);
+              dgw[t] = pack_bf16x2(dg[0], dg[1]);
+              // de e + dg g with de, dg as stored (a folded RMSNorm's row
+              // coefficient; unused otherwise)
+              if (p.cpart)
+                csum += bf16lo(dew[t]) * bf16lo(ev[t]) + bf16hi(dew[t]) * bf16hi(ev[t]) +
+                        bf16lo(dgw[t]) * bf16lo(gv[t]) + bf16hi(dgw[t]) * bf16hi(gv[t]);
             }
-            dew[t] = pack_bf16x2(de[0], de[1]);
-            dgw[t] = pack_bf16x2(dg[0], dg[1]);
+            const int64_t doff = (int64_t)m * p.ldd + n;
+            gstore16(p.DE + doff, dew);
+            gstore16(p.DG + doff, dgw);
           }
-          const int64_t doff = (int64_t)m * p.ldd + n;
-          gstore16(p.DE + doff, dew);
-          gstore16(p.DG + doff, dgw);
+          if (p.cpart) {
+            // the 8 lanes of one row (lanes 8j .. 8j+7) add their sums in a
+            // fixed butterfly; every lane takes part (invalid ones add 0)
+            csum += __shfl_xor(csum, 1, 64);
+            csum += __shfl_xor(csum, 2, 64);
+            csum += __shfl_xor(csum, 4, 64);
+            if (q == 0 && m < M) p.cpart[(int64_t)(tn * 4 + wn) * M + m] = csum;
+          }
         }
       }
     }

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const void *Xv, const void 
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
     if (lane == 0) rstd[row] = r;
+    if (Yv == nullptr) return;   // statistics only (the norm folded into the projections)
     auto out = [&](int c, const u32x4 &xc) {
       float v[8], g[8];
       unpack8(xc, v);

@@ -329,3 +329,35 @@ def test_noalloc_validation_before_any_hip_call():
     big = L.workspace_bytes(L.OP_LINEAR_BWD | L.LORA_WS_MINIMAL, 1, 0, 4096, 4096, 4096, 128)
     assert big > L.LORA_NOALLOC_SCRATCH_BYTES
     assert call(T=4096, k=4096, n=4096, r=128) == 4
+
+
+def test_fused_norm_validation_codes():
+    lib = L.lib()
+    W = _w()
+    q4 = _w(1, 64, None, P, P, P)
+    def fwd_(dtype=1, eps=1e-5, nw=P, rstd=P, Wg=W, wsb=1 << 30):
+        return lib.lora_rmsnorm_swiglu_mlp_fwd(dtype, 16, 64, 128, 8, 16.0, eps, P, nw,
+                                               ctypes.byref(Wg), P, P, ctypes.byref(Wg), P, P,
+                                               ctypes.byref(W), P, P, P, P, P, rstd, P, wsb, None)
+    assert fwd_(nw=None) == 1
+    assert fwd_(rstd=None) == 1
+    assert fwd_(dtype=0) == 3           # bf16 only
+    assert fwd_(Wg=q4) == 3             # a 4-bit weight cannot hold W diag(w)
+    assert fwd_(eps=-1.0) == 3
+    assert fwd_(eps=float("nan")) == 3
+    assert fwd_(wsb=16) == 4
+    def bwd_(flags=0, rstd=P):
+        return lib.lora_rmsnorm_swiglu_mlp_bwd(1, 16, 64, 128, 8, 16.0, P, P, rstd,
+                                               ctypes.byref(W), P, P, ctypes.byref(W), P, P,
+                                               ctypes.byref(W), P, P, P, P, P, P,
+                                               P, P, P, P, P, P, flags, P, 1 << 30, None)
+    assert bwd_(flags=2) == 3
+    assert bwd_(rstd=None) == 1
+    # the fused backward needs room for the per-row partials of the norm
+    assert L.workspace_bytes(L.OP_RMSNORM_MLP_BWD, 1, 0, 8192, 4096, 14336, 16) > \
+        L.workspace_bytes(L.OP_MLP_BWD, 1, 0, 8192, 4096, 14336, 16)
+    assert L.workspace_bytes(L.OP_RMSNORM_MLP_FWD, 1, 1, 8192, 4096, 14336, 16) == 0
+    assert L.workspace_bytes(L.OP_RMSNORM_MLP_FWD, 0, 0, 8192, 4096, 14336, 16) == 0
+    assert lib.lora_fold_norm_weight(1, 16, 60, P, P, P, None) == 2
+    assert lib.lora_fold_norm_weight(0, 16, 64, P, P, P, None) == 3
+    assert lib.lora_fold_norm_weight(1, 16, 64, P, None, P, None) == 1
