@@ -189,12 +189,19 @@ def cpu_baseline(cfg, tokens, mi, reps=2):
     Af = {p: np.asarray(v, np.float64) for p, v in mi.A.items()}
     Bf = {p: np.asarray(v, np.float64) for p, v in mi.B.items()}
     oracle.mlp_bwd(X[:512], Wf, Af, Bf, s, dY[:512])       # warm-up
-    t0 = time.perf_counter()
+    tf = tb = 0.0
     for _ in range(reps):
+        t0 = time.perf_counter()
         oracle.mlp_fwd(X, Wf, Af, Bf, s)
+        t1 = time.perf_counter()
         oracle.mlp_bwd(X, Wf, Af, Bf, s, dY)
-    dt = (time.perf_counter() - t0) / reps
+        t2 = time.perf_counter()
+        tf += t1 - t0
+        tb += t2 - t1
+    tf, tb = tf / reps, tb / reps
+    dt = tf + tb
     fl = mlp_flops(tokens, c["d"], c["f"], c["r"])
+    ffl, bfl = mlp_phase_flops(tokens, c["d"], c["f"], c["r"])
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -203,7 +210,22 @@ def cpu_baseline(cfg, tokens, mi, reps=2):
             "sample": f"float64 NumPy oracle, MLP fwd+bwd on {tokens} of {c['T']} tokens "
                       f"(d={c['d']}, f={c['f']}, r={c['r']}), mean of {reps} timed reps after "
                       f"a 512-token warm-up, {dt:.2f} s per rep",
-            "tokens_per_s": tokens / dt, "seconds_per_rep": dt}
+            "tokens_per_s": tokens / dt, "seconds_per_rep": dt,
+            "fwd_s": round(tf, 3), "bwd_s": round(tb, 3),
+            "fwd_tflops": round(ffl / tf / 1e12, 4), "bwd_tflops": round(bfl / tb / 1e12, 4),
+            "blas": blas_vendor()}
+
+
+def blas_vendor():
+    """The BLAS library NumPy's matmul runs on, from numpy.show_config."""
+    import numpy as np
+    try:
+        cfg = np.show_config(mode="dicts")
+        deps = cfg.get("Build Dependencies", {})
+        b = deps.get("blas", {})
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:   # older NumPy: no dict mode
+        return "unknown"
 
 
 def time_rmsnorm(T, d, reps=20):
