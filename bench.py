@@ -43,6 +43,9 @@ def parse():
                     help="workload 5 with double-quantised 4-bit block constants")
     ap.add_argument("--minimal-ws", action="store_true",
                     help="minimal workspace (no weight copies; 4-bit decoded inside the GEMMs)")
+    ap.add_argument("--weights-as-stored", action="store_true",
+                    help="dense weights without a caller-kept transpose (the backward dX GEMMs "
+                         "then read W as stored); default: W^T is kept next to each frozen W")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle baseline runs on")
@@ -441,6 +444,12 @@ def main():
         W = {p: L.to_device_q4(mi.q4[p]) for p in mi.q4}
     else:
         W = {p: up(mi.W[p]) for p in mi.W}
+    W_stored = W
+    # frozen dense weights: a transposed copy is made once, at setup, like the
+    # weights themselves; the backward dX GEMMs then read W^T K-contiguously
+    keep_wt = not q4 and not args.weights_as_stored
+    if keep_wt:
+        W = {p: L.with_transpose(v) for p, v in W.items()}
     A = {p: up(mi.A[p]) for p in mi.A}
     B = {p: up(mi.B[p]) for p in mi.B}
     X, dY = up(mi.X), up(mi.dY)
@@ -505,6 +514,26 @@ def main():
     _, _, kms = timed_steps(min(args.steps, 5), kcs)
     kms[dom] = live[dom]
 
+    # with dense weights, the same step reading W as stored (no transposed
+    # copy), in a pass after the timed region
+    alt = None
+    if keep_wt:
+        def step_stored():
+            L.lora_swiglu_mlp_fwd(X, W_stored, A, B, alpha, Y=Y, e=e, g=g, workspace=ws_fwd,
+                                  stream=stream)
+            L.lora_swiglu_mlp_bwd(X, W_stored, A, B, alpha, e, g, dY, out=out, workspace=ws_bwd,
+                                  stream=stream)
+        step_stored()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nalt = max(3, min(args.steps, 10))
+        a_.record(stream)
+        for _ in range(nalt):
+            step_stored()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        alt = {"ms_per_step": round(a_.elapsed_time(b_) / nalt, 4),
+               "source": f"{nalt} steps after the timed region, HIP events around them"}
+
     # forward and backward separately, in another pass after the timed region:
     # HIP events around each call on the same stream
     nph = max(3, min(args.steps, 10))
@@ -551,12 +580,15 @@ def main():
                                f"{('4-bit (double-quantised constants)' if args.dq else '4-bit') if q4 else 'bf16'} "
                                f"base weights, bf16 adapters",
                    "config_id": args.config, "T": T, "d": d, "f": f, "r": r,
-                   "workspace": "minimal" if args.minimal_ws else "fast"},
+                   "workspace": "minimal" if args.minimal_ws else "fast",
+                   "weights": ("W with a caller-kept W^T (made once at setup; the backward dX "
+                               "GEMMs read W^T)") if keep_wt else "as stored"},
         "wall_s_timed": round(wall, 3),
         "kernels_ms": {names[kc]: round(kms[kc], 4) for kc in kcs},
         "kernels_ms_source": "roofline kernel: HIP events in the timed region; the others: "
                              "a separate pass of up to 5 steps after it",
         "phases_ms": phase,
+        "weights_as_stored": alt,
         "phases_ms_source": f"HIP events around each call, {nph} steps after the timed region",
         "roofline": {"bound": "mfma", "kernel": names[dom], "achieved": round(dom_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -569,7 +601,8 @@ def main():
     # the RMSNorm in front of the MLP, timed on its own (not part of value)
     line["rmsnorm_before_mlp"] = time_rmsnorm(T, d)
     if not q4:
-        line["rmsnorm_mlp_step"] = time_norm_mlp(L, X, W, A, B, alpha, dY, ws_fwd, ws_bwd, stream)
+        line["rmsnorm_mlp_step"] = time_norm_mlp(L, X, W_stored, A, B, alpha, dY, ws_fwd, ws_bwd,
+                                                 stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens, mi)
     print(json.dumps(line), flush=True)

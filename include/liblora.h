@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 2
+#define LORA_ABI_VERSION 3
 #define LORA_MAX_RANK 128
 
 /* status codes */
@@ -127,8 +127,16 @@ typedef enum { LORA_W_DENSE = 0, LORA_W_Q4 = 1, LORA_W_Q4_DQ = 2 } lora_wfmt;
  *     first-level blocks and one fp32 offset are this library's reading.
  *     absmax_codes:    n*k/64 bytes;  absmax_codebook: 256 fp32 (device);
  *     absmax_scale:    ceil(n*k/64 / 256) fp32;  absmax_blocksize: 256.
- *   Fields after `codebook` are read only for Q4_DQ.  All device pointers
- *   16-byte aligned.  The library never writes through any of them.
+ *   Fields `absmax_codes` .. `absmax_blocksize` are read only for Q4_DQ.
+ *   DENSE, optional `wt`: the same weight transposed, W^T [k x n] row-major
+ *     (bf16 only; NULL: none).  A frozen weight may keep this copy next to W
+ *     (made once, e.g. at load time); the backward dX products dY W then run
+ *     the K-contiguous (NT) GEMM form on it, measured faster than reading W
+ *     as stored.  The MLP's gate/up backward uses the gate and up copies as
+ *     the two K halves of one product and needs f % 64 == 0 for that (other
+ *     shapes read W as stored).  Its contents must equal W^T.
+ *   All device pointers 16-byte aligned.  The library never writes through
+ *   any of them.
  */
 typedef struct {
   int32_t fmt;              /* lora_wfmt */
@@ -142,6 +150,7 @@ typedef struct {
   const float *absmax_scale;       /* Q4_DQ */
   float absmax_offset;             /* Q4_DQ */
   int32_t absmax_blocksize;        /* Q4_DQ; must be 256 */
+  const void *wt;                  /* DENSE, optional: W^T [k x n] */
 } lora_weight;
 
 /* ops for lora_workspace_bytes */

@@ -60,7 +60,7 @@ class LoraWeightC(ctypes.Structure):
                 ("absmax", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
                 ("absmax_codes", ctypes.c_void_p), ("absmax_codebook", ctypes.c_void_p),
                 ("absmax_scale", ctypes.c_void_p), ("absmax_offset", ctypes.c_float),
-                ("absmax_blocksize", ctypes.c_int32)]
+                ("absmax_blocksize", ctypes.c_int32), ("wt", ctypes.c_void_p)]
 
 
 _lib = None
@@ -241,6 +241,9 @@ def _weight(W, name, n, k, dtype, device, where):
         else:
             _tensor(W.absmax.reshape(-1) if W.absmax.is_contiguous() else W.absmax,
                     name + ".absmax", (nblk,), torch.float32, device, where)
+    elif isinstance(W, DenseWeight):
+        _tensor(W.w, name, (n, k), dtype, device, where)
+        _tensor(W.wt, name + ".wt", (k, n), dtype, device, where)
     else:
         _tensor(W, name, (n, k), dtype, device, where)
 
@@ -293,7 +296,25 @@ class Q4Weight:
         return (self.n, self.k)
 
 
-Weight = Union["torch.Tensor", Q4Weight]
+@dataclass
+class DenseWeight:
+    """A dense frozen base weight w [n, k] with a copy of its transpose wt
+    [k, n] kept next to it (made once): the backward dX products then run the
+    K-contiguous GEMM form on wt.  Build with with_transpose(w)."""
+    w: object
+    wt: object
+
+    @property
+    def shape(self):
+        return tuple(self.w.shape)
+
+
+def with_transpose(w):
+    """DenseWeight(w, w^T as a contiguous copy)."""
+    return DenseWeight(w, w.t().contiguous())
+
+
+Weight = Union["torch.Tensor", Q4Weight, DenseWeight]
 
 
 def _wstruct(W) -> LoraWeightC:
@@ -305,6 +326,9 @@ def _wstruct(W) -> LoraWeightC:
                                float(W.absmax_offset), W.absmax_blocksize)
         return LoraWeightC(LORA_W_Q4, W.blocksize, None, W.codes.data_ptr(),
                            W.absmax.data_ptr(), W.codebook.data_ptr())
+    if isinstance(W, DenseWeight):
+        return LoraWeightC(LORA_W_DENSE, 0, W.w.data_ptr(), None, None, None, None, None, None,
+                           0.0, 0, W.wt.data_ptr())
     return LoraWeightC(LORA_W_DENSE, 0, W.data_ptr(), None, None, None)
 
 

@@ -242,14 +242,17 @@ struct WeightView {
   const uint8_t *codes;
   AbsmaxSrc absmax;       // plain or double-quantised block constants
   const float *codebook;
+  const bf16_t *wt;       // dense, optional: W^T [k x n] kept by the caller
 };
 
 int check_weight(const lora_weight *W, int dtype, int64_t k_in, WeightView &out) {
   if (!W) return LORA_ERR_NULL_POINTER;
   if (W->fmt == LORA_W_DENSE) {
     if (!W->w) return LORA_ERR_NULL_POINTER;
-    if (!aligned16(W->w)) return LORA_ERR_MISALIGNED;
-    out = {false, LORA_W_DENSE, (const bf16_t *)W->w, nullptr, AbsmaxSrc{}, nullptr};
+    if (!aligned16(W->w) || (W->wt && !aligned16(W->wt))) return LORA_ERR_MISALIGNED;
+    // the transposed copy serves the bf16 GEMMs only
+    const bf16_t *wt = dtype == LORA_BF16 ? (const bf16_t *)W->wt : nullptr;
+    out = {false, LORA_W_DENSE, (const bf16_t *)W->w, nullptr, AbsmaxSrc{}, nullptr, wt};
     return LORA_OK;
   }
   if (W->fmt != LORA_W_Q4 && W->fmt != LORA_W_Q4_DQ) return LORA_ERR_UNSUPPORTED;
@@ -274,7 +277,7 @@ int check_weight(const lora_weight *W, int dtype, int64_t k_in, WeightView &out)
     am.scale = W->absmax_scale;
     am.offset = W->absmax_offset;
   }
-  out = {true, W->fmt, nullptr, W->codes, am, W->codebook};
+  out = {true, W->fmt, nullptr, W->codes, am, W->codebook, nullptr};
   return LORA_OK;
 }
 
@@ -445,7 +448,7 @@ int transpose_w(bf16_t *out, int64_t ld_out, const WeightView &w, int64_t rows, 
   return LORA_OK;
 }
 inline WeightView dense_view(const bf16_t *p) {
-  return {false, LORA_W_DENSE, p, nullptr, AbsmaxSrc{}, nullptr};
+  return {false, LORA_W_DENSE, p, nullptr, AbsmaxSrc{}, nullptr, nullptr};
 }
 
 // workspace check shared by the entry points; `fast` = room for the
@@ -758,9 +761,9 @@ int lora_linear_bwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
       a.M = (int)T; a.N = (int)k; a.K = (int)n; a.ksplit = (int)n;
       a.A0 = a.A1 = dYb; a.lda = n;
       bool nn = true, q4 = wv.q4;
-      if (wcopy) {   // decoded W^T [k x n]: the NT GEMM reads it K-contiguous
-        bf16_t *wt = (bf16_t *)(w + pl.wbuf);
-        LORA_TRY(transpose_w(wt, n, wv, n, k, st));
+      if (wcopy || wv.wt) {   // W^T [k x n] (decoded, or the caller's): NT GEMM, K-contiguous
+        bf16_t *wt = wv.wt ? const_cast<bf16_t *>(wv.wt) : (bf16_t *)(w + pl.wbuf);
+        if (!wv.wt) LORA_TRY(transpose_w(wt, n, wv, n, k, st));
         const WeightView tv = dense_view(wt);
         set_b(a, tv, tv); a.ldb = n;
         nn = false; q4 = false;
@@ -1040,9 +1043,10 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     a.M = (int)T; a.N = (int)f; a.K = (int)d; a.ksplit = (int)d;
     a.A0 = a.A1 = dYb; a.lda = d;
     bool nn = true, q4 = wd.q4;
-    if (wcopy && wd.q4) {   // decoded Wd^T [f x d]
-      LORA_TRY(transpose_w(wt, d, wd, d, f, st));
-      const WeightView tv = dense_view(wt);
+    if ((wcopy && wd.q4) || wd.wt) {   // Wd^T [f x d] (decoded, or the caller's)
+      const bf16_t *wdt = wd.wt ? wd.wt : wt;
+      if (!wd.wt) LORA_TRY(transpose_w(wt, d, wd, d, f, st));
+      const WeightView tv = dense_view(wdt);
       set_b(a, tv, tv); a.ldb = d;
       nn = false; q4 = false;
     } else {
@@ -1110,6 +1114,12 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
       const WeightView tv = dense_view(wt);
       set_b(b, tv, tv); b.ldb = 2 * f;
       nn = false; q4 = false;
+    } else if (wg.wt && wu.wt && f % 64 == 0) {
+      // the caller's Wg^T, Wu^T [d x f]: the K halves of one NT product
+      const WeightView tv = dense_view(wg.wt);
+      set_b(b, tv, tv); b.ldb = f;
+      b.Bk1 = wu.wt; b.kbsplit = (int)f;
+      nn = false;
     } else {
       set_b(b, wg, wu); b.ldb = d;
     }

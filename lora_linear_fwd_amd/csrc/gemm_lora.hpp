@@ -114,6 +114,11 @@ struct GemmArgs {
   float *cpart;
   const bf16_t *nrm_x;
   const float *nrm_rs, *nrm_kk;
+  // dense NT (eight-wave, no gate/up interleave): K columns >= kbsplit of the
+  // weight operand come from Bk1 (same ldb), kbsplit a multiple of 64;
+  // nullptr: one source
+  const bf16_t *Bk1;
+  int kbsplit;
 };
 
 // XCD-aware, grouped tile order.  Workgroups are dispatched round-robin over

@@ -291,6 +291,11 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       boff0 = (uint32_t)(r0 * p.ldb * 2 + cA * 16);
       brem = N - n0 - r0;
     }
+    // a second K source for K columns >= kbsplit (a multiple of the K step):
+    // its base is shifted back by kbsplit columns, so a step's offsets are
+    // the same expression for either source and only the base changes
+    const char *const bk1base =
+        p.Bk1 ? (const char *)(p.Bk1 + (int64_t)n0 * p.ldb) - 2 * (int64_t)p.kbsplit : nullptr;
     const uint32_t bstep32 = (uint32_t)(32 * p.ldb * 2);
     const int nk = (K + BK - 1) / BK;
     // A tile of K step kt (< nk) into A stage sa (group 0): 8 loads per wave;
@@ -313,6 +318,9 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       const int k0 = kt * BK;
       const int col = k0 + kcol;
       const bool kin = col < K;
+      // the whole step lies in one K source (kbsplit % BK == 0)
+      __amdgpu_buffer_rsrc_t rsK = rsB;
+      if (!GU && bk1base != nullptr && k0 >= p.kbsplit) rsK = make_rsrc(bk1base, kMaxRecords);
   #pragma unroll
       for (int u = 0; u < NI; ++u) {
         const int b = w4 + 4 * u;
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
                 ok ? boff0 + (uint32_t)v * bstep32 + 2u * (uint32_t)k0 : kOOB, 0);
         } else {
           const bool ok = kin && 32 * u < brem;
-          dma16(rsB, Ws + b * 1024, ok ? boff0 + (uint32_t)u * bstep32 + 2u * (uint32_t)k0 : kOOB, 0);
+          dma16(rsK, Ws + b * 1024, ok ? boff0 + (uint32_t)u * bstep32 + 2u * (uint32_t)k0 : kOOB, 0);
         }
       }
     };

@@ -67,7 +67,7 @@ def test_timing_build_has_the_same_kernels():
 
 
 def test_version_and_strerror():
-    assert L.abi_version() == 2
+    assert L.abi_version() == 3
     assert L.strerror(0) == "ok"
     for s in range(1, 7):
         assert L.strerror(s) and L.strerror(s) != "unknown status"

@@ -25,16 +25,22 @@ def _same(outs, ref, rep):
         assert torch.equal(a, b), f"rep {rep}: {k} differs in {(a != b).sum().item()} elements"
 
 
-@pytest.mark.parametrize("ws", ["fast", "minimal"])
-@pytest.mark.parametrize("shape", [(300, 256, 576, 16, 8, False), (8192, 4096, 14336, 16, 6, False),
-                                   (8192, 4096, 14336, 16, 4, True)],
-                         ids=["small", "llama3_8b_mlp", "llama3_8b_mlp_4bit"])
-def test_mlp_step_bitwise_reproducible(shape, ws):
+_SHAPES = {"small": (300, 256, 576, 16, 8, False), "llama3_8b_mlp": (8192, 4096, 14336, 16, 6, False),
+           "llama3_8b_mlp_4bit": (8192, 4096, 14336, 16, 4, True)}
+# ws "wt": the caller keeps W^T next to each dense weight
+_CASES = [(n, ws) for n in _SHAPES for ws in ("fast", "minimal", "wt")
+          if not (_SHAPES[n][5] and ws == "wt")]
+
+
+@pytest.mark.parametrize("name,ws", _CASES, ids=[f"{n}-{w}" for n, w in _CASES])
+def test_mlp_step_bitwise_reproducible(name, ws):
     import torch
-    T, d, f, r, reps, q4 = shape
+    T, d, f, r, reps, q4 = _SHAPES[name]
     log(f"determinism: T={T} d={d} f={f} r={r} ws={ws} reps={reps} q4={q4}")
     mi = gen_mlp(T, d, f, r, 16.0, "bf16", seed=51, q4=q4)
     W, _ = mlp_weights(mi)
+    if ws == "wt":
+        W = {p: L.with_transpose(v) for p, v in W.items()}
     wfmt = L._wfmt(W["gate"])
     A = {p: dev(mi.A[p], "bf16") for p in mi.A}
     B = {p: dev(mi.B[p], "bf16") for p in mi.B}

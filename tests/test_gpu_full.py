@@ -31,12 +31,15 @@ def sample_rows(T, n=40, seed=0, band=256):
     return rows
 
 
-def run_full_mlp(cfg, q4=None, minimal=False):
+def run_full_mlp(cfg, q4=None, minimal=False, transposed=False):
     import torch
-    log(f"config {cfg} (4-bit form {q4}, minimal workspace {minimal}): generating inputs")
+    log(f"config {cfg} (4-bit form {q4}, minimal workspace {minimal}, caller-kept W^T "
+        f"{transposed}): generating inputs")
     mi = gen_config(cfg, q4=q4)
     s = oracle.scaling(mi.alpha, mi.r)
     Wd, Wref = mlp_weights(mi)
+    if transposed:
+        Wd = {p: L.with_transpose(v) for p, v in Wd.items()}
     X, dY = dev(mi.X, "bf16"), dev(mi.dY, "bf16")
     A = {p: dev(mi.A[p], "bf16") for p in mi.A}
     B = {p: dev(mi.B[p], "bf16") for p in mi.B}
@@ -63,6 +66,13 @@ def run_full_mlp(cfg, q4=None, minimal=False):
 @pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_full_mlp(cfg):
     run_full_mlp(cfg)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_mlp_transposed_weights(cfg):
+    """The caller keeps W^T next to each frozen weight (the benchmark's
+    default): both backward dX GEMMs run the K-contiguous form on it."""
+    run_full_mlp(cfg, transposed=True)
 
 
 def test_full_mlp_q4_minimal():

@@ -22,12 +22,16 @@ def _sync():
 
 # the two workspace strategies: "fast" (weight copied transposed / decoded
 # into the workspace, NT GEMMs) and "minimal" (weight read in place: NN
-# GEMMs for dX, 4-bit codes decoded inside the GEMM)
+# GEMMs for dX, 4-bit codes decoded inside the GEMM); for dense weights also
+# "wt": the caller keeps W^T next to W (the backward runs the NT form on it)
 WS_MODES = ["fast", "minimal"]
+DENSE_MODES = WS_MODES + ["wt"]
 
 
 def run_linear(li, need_dx=True, ws="fast"):
     Wd, Wref = linear_weight(li)
+    if ws == "wt":
+        Wd = L.with_transpose(Wd)
     X, A, B, dY = (dev(v, li.dtype) for v in (li.X, li.A, li.B, li.dY))
     mw = ws == "minimal"
     Y = L.lora_linear_fwd(X, Wd, A, B, li.alpha, minimal_workspace=mw)
@@ -60,7 +64,7 @@ LINEAR_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("ws", WS_MODES)
+@pytest.mark.parametrize("ws", DENSE_MODES)
 @pytest.mark.parametrize("shape", LINEAR_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_linear_bf16(shape, ws):
     T, k, n, r = shape
@@ -149,6 +153,8 @@ def test_linear_deterministic():
 # ------------------------------------------------------------------ MLP
 def run_mlp(mi, need_dx=True, ws="fast"):
     Wd, Wref = mlp_weights(mi)
+    if ws == "wt":
+        Wd = {p: L.with_transpose(v) for p, v in Wd.items()}
     X, dY = dev(mi.X, mi.dtype), dev(mi.dY, mi.dtype)
     A = {p: dev(mi.A[p], mi.dtype) for p in mi.A}
     B = {p: dev(mi.B[p], mi.dtype) for p in mi.B}
@@ -175,8 +181,10 @@ def check_mlp(mi, need_dx=True, ws="fast"):
 
 
 MLP_SHAPES = [
-    # T, d, f, r
+    # T, d, f, r  (with "wt", f % 64 == 0 runs the gate/up backward as one NT
+    # product over [Wg^T | Wu^T]; other f read the gate/up weights as stored)
     (300, 256, 520, 16),
+    (300, 264, 512, 16),
     (37, 64, 72, 3),
     (260, 128, 264, 64),
     (513, 136, 256, 8),
@@ -184,7 +192,7 @@ MLP_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("ws", WS_MODES)
+@pytest.mark.parametrize("ws", DENSE_MODES)
 @pytest.mark.parametrize("shape", MLP_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_mlp_bf16(shape, ws):
     T, d, f, r = shape
@@ -192,9 +200,10 @@ def test_mlp_bf16(shape, ws):
     check_mlp(gen_mlp(T, d, f, r, 16.0, "bf16", seed=T + d + f + r), ws=ws)
 
 
-def test_mlp_bf16_lora_dominant():
-    log("mlp bf16 lora-dominant")
-    check_mlp(gen_mlp(300, 256, 520, 16, 16.0, "bf16", seed=21, b_std=1.0))
+@pytest.mark.parametrize("ws", ["fast", "wt"])
+def test_mlp_bf16_lora_dominant(ws):
+    log(f"mlp bf16 lora-dominant ws={ws}")
+    check_mlp(gen_mlp(300, 256, 512, 16, 16.0, "bf16", seed=21, b_std=1.0), ws=ws)
 
 
 def test_mlp_bf16_without_dx():
