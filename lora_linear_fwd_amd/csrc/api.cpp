@@ -1059,7 +1059,7 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
     LORA_TRY(run_gemm(KC_DOWN_BWD, nn, q4, EPI_SWIGLU_BWD, a, st));
     if (nf) {
-      hipLaunchKernelGGL(k_norm_coef, dim3(blocks_for(T)), dim3(256), 0, st, cpart,
+      hipLaunchKernelGGL(k_norm_coef, dim3(blocks_for(T, 64)), dim3(1024), 0, st, cpart,
                          (int)(a.tiles_n * 4), (int)T, rstd, 1.0f / (float)d, nkk);
       HIP_TRY(hipGetLastError());
     }

@@ -338,6 +338,8 @@ __global__ __launch_bounds__(256, (RSU <= 32 && RSV <= 32) ? 4 : 1) void k_skinn
   constexpr int SL = (RSU * 32 + 255) / 256;   // side chunks per thread
   __shared__ __attribute__((aligned(16))) char zs[64 * 512];
   __shared__ __attribute__((aligned(16))) char ss[RSU * 512];
+  // the P tile of the step: [RSV x 64 tokens], 128-byte rows, chunk ^ (q % 8)
+  __shared__ __attribute__((aligned(16))) char ps[RSV * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int j = blockIdx.x;
@@ -365,33 +367,52 @@ __global__ __launch_bounds__(256, (RSU <= 32 && RSV <= 32) ? 4 : 1) void k_skinn
       lds_write16(ss, soff(q, lc), v);
     }
   }
+  // Z tile rows (raw e and g for ZSWIGLU: silu is applied when the tile is
+  // written to LDS, so the loads stay in flight behind the step's MFMAs)
   u32x4 zr[8];
+  u32x4 gr[ZSWIGLU ? 8 : 1];
+  // P tile chunk of this thread: row q = tid / 8, tokens 8 (tid % 8) .. +7
+  constexpr int PCH = RSV * 8;   // 16-byte chunks of the P tile
+  u32x4 pr = {0, 0, 0, 0};
   auto load = [&](int t0) {
     const int k = c0 + 8 * lc;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = t0 + lr + 8 * i;
-      u32x4 v = {0, 0, 0, 0};
+      u32x4 v = {0, 0, 0, 0}, w = {0, 0, 0, 0};
       if (t < tend && k < ncol) {
         if constexpr (ZSWIGLU) {
-          const u32x4 e = gload16(a.E + (int64_t)t * a.ldz + k);
-          const u32x4 g = gload16(a.G + (int64_t)t * a.ldz + k);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float e0 = bf16lo(e[w]), e1 = bf16hi(e[w]);
-            v[w] = pack_bf16x2(e0 * sigmoidf_fast(e0) * bf16lo(g[w]),
-                               e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
-          }
+          v = gload16(a.E + (int64_t)t * a.ldz + k);
+          w = gload16(a.G + (int64_t)t * a.ldz + k);
         } else {
           v = gload16((seg1 ? a.Z1 : a.Z0) + (int64_t)t * a.ldz + k);
         }
       }
       zr[i] = v;
+      if constexpr (ZSWIGLU) gr[i] = w;
     }
+    // P rows are zero past T up to ldp (a multiple of 64), so the whole
+    // 64-token tile is in bounds
+    if (tid < PCH) pr = gload16(P + (int64_t)(tid >> 3) * a.ldp + t0 + 8 * (tid & 7));
   };
   auto store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lds_write16(zs, zoff(lr + 8 * i, lc), zr[i]);
+    for (int i = 0; i < 8; ++i) {
+      u32x4 v = zr[i];
+      if constexpr (ZSWIGLU) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = bf16lo(zr[i][w]), e1 = bf16hi(zr[i][w]);
+          v[w] = pack_bf16x2(e0 * sigmoidf_fast(e0) * bf16lo(gr[i][w]),
+                             e1 * sigmoidf_fast(e1) * bf16hi(gr[i][w]));
+        }
+      }
+      lds_write16(zs, zoff(lr + 8 * i, lc), v);
+    }
+    if (tid < PCH) {
+      const int q = tid >> 3, c = tid & 7;
+      lds_write16(ps, (uint32_t)(q * 128 + ((c ^ (q & 7)) << 4)), pr);
+    }
   };
 
   f32x4 vacc[4][NQV];
@@ -422,8 +443,10 @@ __global__ __launch_bounds__(256, (RSU <= 32 && RSV <= 32) ? 4 : 1) void k_skinn
     for (int kb = 0; kb < 2; ++kb) {
       u32x4 pf[NQV];
 #pragma unroll
-      for (int qb = 0; qb < NQV; ++qb)
-        pf[qb] = gload16(P + (int64_t)(qb * 16 + l16) * a.ldp + t0 + 32 * kb + 8 * g4);
+      for (int qb = 0; qb < NQV; ++qb) {
+        const int q = qb * 16 + l16, c = 4 * kb + g4;
+        pf[qb] = lds_read16(ps, (uint32_t)(q * 128 + ((c ^ (q & 7)) << 4)));
+      }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         // lane l16 of group g4: column 64 wave + 16 nb + l16, tokens
@@ -873,20 +896,25 @@ __global__ __launch_bounds__(256) void k_fold_colscale(const bf16_t *W, const bf
 //   kk[t] = rstd[t]^2 (sum_p S_p[t]) / d     (fixed summation order)
 // (sum_j gn_j x_j = S / rstd with gn = dXn w the gradient the folded
 // projections return, so rstd^3 x (gn . x) / d = kk x.)
-__global__ void k_norm_coef(const float *part, int np, int T, const float *rstd, float inv_d,
-                            float *kk) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
-  int p = 0;
-  for (; p + 4 <= np; p += 4) {
+// Block: 64 rows, 16 waves; wave w adds the partials p = w (mod 16) of its
+// lane's row, the 16 wave sums are then added in wave order.
+__global__ __launch_bounds__(1024) void k_norm_coef(const float *part, int np, int T,
+                                                    const float *rstd, float inv_d, float *kk) {
+  __shared__ float red[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 64 + lane;
+  float s = 0.f;
+  if (t < T)
+    for (int p = w; p < np; p += 16) s += part[(int64_t)p * T + t];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && t < T) {
+    float S = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s4[u] += part[(int64_t)(p + u) * T + t];
+    for (int i = 0; i < 16; ++i) S += red[i][lane];
+    const float r = rstd[t];
+    kk[t] = r * r * S * inv_d;
   }
-  for (int u = 0; p < np; ++p, ++u) s4[u] += part[(int64_t)p * T + t];
-  const float S = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-  const float r = rstd[t];
-  kk[t] = r * r * S * inv_d;
 }
 
 }  // namespace lora
