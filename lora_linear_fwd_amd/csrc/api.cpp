@@ -141,8 +141,14 @@ inline bool mlp_bwd_dual(int64_t r) { return rs_of(r) <= 32; }
 struct MlpBwdPlan {
   size_t de, dg, side_d_nn, epi_d_nn, side_d_nt, epi_gu_nn, side_gu_nt, side_gu_nn;
   size_t side_g, side_u, pt_d, pt_g, pt_u, part_u, part_v;
-  size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, cpart, nkk, total;
+  size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, cpart, nkk;
+  size_t fu_d, fu_gu, fv_d, fv_gu;   // per-tile partials of the rank-fused SwiGLU' GEMM
+  size_t total;
 };
+// The down-projection backward forms the four rank-r products of the
+// backward in its SwiGLU' epilogue (EPI_SWIGLU_BWD_RANK) when the rank fits
+// one 16-wide MFMA block
+inline bool mlp_bwd_rank_fused(int64_t r) { return rs_of(r) == 16; }
 MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, bool norm = false) {
   Bump b; MlpBwdPlan p{};
   if (norm) {   // folded RMSNorm: row partials per 64-column block of the down backward
@@ -177,6 +183,13 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, 
     p.pt_u = b.take(ptb);
     p.part_u = b.take(std::max(dual_u_bytes(T, f, f, RS2), dual_u_bytes(T, 2 * f, f, RS2)));
     p.part_v = b.take(std::max(dual_v_bytes(T, f, f, RS2), dual_v_bytes(T, 2 * f, f, RS2)));
+    if (mlp_bwd_rank_fused(r)) {
+      const int64_t tn = cdiv(f, 256), tm = cdiv(T, 256);
+      p.fu_d = b.take((size_t)tn * T * 16 * 4);
+      p.fu_gu = b.take((size_t)2 * tn * T * 16 * 4);
+      p.fv_d = b.take((size_t)tm * 16 * f * 4);
+      p.fv_gu = b.take((size_t)tm * 16 * 2 * f * 4);
+    }
   } else {
     p.side_gu_nn = b.take((size_t)RS1 * 2 * f * 2);
     p.ntpart = b.take(std::max({nt_part_bytes(T, d, RS2), nt_part_bytes(T, d, RS1),
@@ -1034,11 +1047,25 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   float *nkk = nf ? (float *)(w + pl.nkk) : nullptr;
   const float *rstd = nf ? nf->rstd : nullptr;
 
+  // rank-fused: every rank-r product but dBd and dA_gu comes out of the
+  // down-projection backward's epilogue (the Q4 minimal strategy's four-wave
+  // GEMM has no such epilogue)
+  const bool rankf = dual && mlp_bwd_rank_fused(r) && !(wd.q4 && !wcopy);
+  const int64_t ftn = cdiv(f, BN), ftm = cdiv(T, BM);
   if (T > 0) {
     // 1. dh = dY Wd + s (dY Bd) Ad with the SwiGLU-derivative epilogue -> de, dg
     // G_d = dY Bd (fp32 for dAd, s G_d in bf16 for the epilogue)
     LORA_TRY(skinny_nt(RS2, false, T, d, dYb, dYb, d, d, nullptr, nullptr, side_d_nn, ntpart,
                        gd32, gdbf, s, st));
+    if (rankf) {
+      // the epilogue's token-contraction operands: G_d^T, and H_g^T, H_u^T
+      // from H_gu = X [Ag; Au]^T
+      LORA_TRY(pack_pt(gd32, T, RS2, 0, (int)r, RS2, pt_d, st));
+      LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart,
+                         hgu32, nullptr, 1.f, st, rstd));
+      LORA_TRY(pack_pt(hgu32, T, RS1, 0, (int)r, RS2, pt_g, st));
+      LORA_TRY(pack_pt(hgu32, T, RS1, (int)r, (int)r, RS2, pt_u, st));
+    }
     GemmArgs a = gemm_base();
     a.M = (int)T; a.N = (int)f; a.K = (int)d; a.ksplit = (int)d;
     a.A0 = a.A1 = dYb; a.lda = d;
@@ -1057,16 +1084,49 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     a.hglob = gdbf;
     a.cpart = cpart;
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
-    LORA_TRY(run_gemm(KC_DOWN_BWD, nn, q4, EPI_SWIGLU_BWD, a, st));
+    if (rankf) {
+      a.fr_sd = side_d_nt; a.fr_sg = side_g; a.fr_su = side_u;
+      a.fr_pd = pt_d; a.fr_pg = pt_g; a.fr_pu = pt_u; a.fr_ldp = (int)ldp_of(T);
+      a.fr_ud = (float *)(w + pl.fu_d); a.fr_ugu = (float *)(w + pl.fu_gu);
+      a.fr_vd = (float *)(w + pl.fv_d); a.fr_vgu = (float *)(w + pl.fv_gu);
+    }
+    LORA_TRY(run_gemm(KC_DOWN_BWD, nn, q4, rankf ? EPI_SWIGLU_BWD_RANK : EPI_SWIGLU_BWD, a, st));
     if (nf) {
       hipLaunchKernelGGL(k_norm_coef, dim3(blocks_for(T, 64)), dim3(1024), 0, st, cpart,
                          (int)(a.tiles_n * 4), (int)T, rstd, 1.0f / (float)d, nkk);
       HIP_TRY(hipGetLastError());
     }
   }
+  if (rankf) {
+    // the per-tile partials, reduced in a fixed order:
+    //   H_d = sum over feature tiles (fp32, for dBd); dAd = s sum over token tiles;
+    //   G_gu = [de Bg | dg Bu] (fp32 for dA_gu with the folded norm's rstd,
+    //   s G_gu in bf16 for the dX epilogue); dBg, dBu = s sums over token tiles
+    if (T > 0) {
+      ReduceUArgs rd{(const float *)(w + pl.fu_d), (int)T, 16, RS2, (int)r, 1, (int)ftn, 0, 1.f,
+                     hd32, nullptr, nullptr};
+      hipLaunchKernelGGL(k_reduce_dual_u, dim3(blocks_for(T * RS2)), dim3(256), 0, st, rd);
+      HIP_TRY(hipGetLastError());
+      ReduceUArgs rg{(const float *)(w + pl.fu_gu), (int)T, 16, RS1, (int)r, 2, (int)ftn, (int)ftn,
+                     s, ggu32, ggubf, rstd};
+      hipLaunchKernelGGL(k_reduce_dual_u, dim3(blocks_for(T * RS1)), dim3(256), 0, st, rg);
+      HIP_TRY(hipGetLastError());
+    }
+    const int tsv = T > 0 ? (int)ftm : 0;
+    ReduceTNArgs vd{(const float *)(w + pl.fv_d), tsv, 16, (int)f, (int)r, (int)f, s, 0,
+                    (bf16_t *)dAd, nullptr, 0, nullptr, 0, 0, nullptr};
+    hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)16 * f)), dim3(256), 0, st, vd);
+    HIP_TRY(hipGetLastError());
+    ReduceTNArgs vg{(const float *)(w + pl.fv_gu), tsv, 16, (int)(2 * f), (int)r, (int)f, s, 1,
+                    (bf16_t *)dBg, (bf16_t *)dBu, 0, nullptr, 0, 0, nullptr};
+    hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)16 * 2 * f)), dim3(256), 0, st, vg);
+    HIP_TRY(hipGetLastError());
+  }
   // 2. one pass over h = silu(e) g (recomputed): H_d = h Ad^T (fp32, for dBd)
   //    and dAd = s G_d^T h
-  if (dual) {
+  if (rankf) {
+    // formed by the down backward's epilogue
+  } else if (dual) {
     if (T > 0) LORA_TRY(pack_pt(gd32, T, RS2, 0, (int)r, RS2, pt_d, st));   // G_d^T bf16
     LORA_TRY(skinny_dual(RS2, true, T, f, f, f, nullptr, nullptr, eb, gb, side_d_nt, nullptr,
                          pt_d, nullptr, part_u, part_v, r, RS2, 1.f, hd32, nullptr, s, 0,
@@ -1080,7 +1140,7 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   // 3. dBd = s dY^T H_d
   LORA_TRY(skinny_tn(RS2, false, T, d, hd32, dYb, dYb, d, d, nullptr, nullptr, tnpart, r, s, 1,
                      (bf16_t *)dBd, nullptr, d, st));
-  if (T > 0) {
+  if (T > 0 && !rankf) {
     // 4. H_gu = X [Ag; Au]^T (fp32), its two halves transposed to bf16
     LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,
                        nullptr, 1.f, st, rstd));
@@ -1091,7 +1151,9 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   }
   // 5. G_gu = [de Bg | dg Bu] (fp32 for dA_gu, s G_gu in bf16 for the dX
   //    epilogue) and dBg = s de^T H_g, dBu = s dg^T H_u: one pass over [de | dg]
-  if (dual) {
+  if (rankf) {
+    // formed by the down backward's epilogue
+  } else if (dual) {
     LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, 2 * f, de, dg, nullptr, nullptr, side_g, side_u,
                          pt_g, pt_u, part_u, part_v, r, RS1, s, ggu32, ggubf, s, 1, (bf16_t *)dBg,
                          (bf16_t *)dBu, st, rstd));

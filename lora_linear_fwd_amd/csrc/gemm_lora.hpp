@@ -65,7 +65,10 @@ constexpr bool bmode_nt_q4(int m) { return m == B_NT_Q4 || m == B_NT_Q4DQ; }
 constexpr bool bmode_nn_q4(int m) { return m == B_NN_Q4 || m == B_NN_Q4DQ; }
 constexpr bool bmode_q4(int m) { return bmode_nt_q4(m) || bmode_nn_q4(m); }
 constexpr bool bmode_dq(int m) { return m == B_NT_Q4DQ || m == B_NN_Q4DQ; }
-enum Epi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
+// EPI_SWIGLU_BWD_RANK (eight-wave kernel, rank-r width 16): the SwiGLU'
+// epilogue that also forms the tile's shares of the four rank-r products of
+// the MLP backward (see GemmArgs::fr_*)
+enum Epi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_SWIGLU_BWD_RANK = 3 };
 
 struct GemmArgs {
   int M, N, K;
@@ -119,6 +122,20 @@ struct GemmArgs {
   // nullptr: one source
   const bf16_t *Bk1;
   int kbsplit;
+  // EPI_SWIGLU_BWD_RANK: with h = silu(e) g, de, dg as stored, per tile
+  //   fr_ud[tn][t][q]       += sum_n h[t][n] Ad[q][n]          (H_d = h Ad^T)
+  //   fr_ugu[tn][t][q]      += sum_n de[t][n] Bg[n][q], and at block
+  //   fr_ugu[tiles_n + tn]      the same with dg and Bu        ([de Bg | dg Bu])
+  //   fr_vd[tm][q][n]       += sum_t G_d[t][q] h[t][n]         (dAd / s)
+  //   fr_vgu[tm][q][n], [tm][q][N + n]  sums of H_g[t][q] de[t][n] and
+  //                            H_u[t][q] dg[t][n]              (dBg, dBu / s)
+  // over the tile's 256 features (tn) or tokens (tm), q < 16, so fixed-order
+  // sums over the tiles give the products.  Operands: fr_sd, fr_sg, fr_su
+  // [16 x N] bf16 (Ad, Bg^T, Bu^T padded), fr_pd, fr_pg, fr_pu [16 x fr_ldp]
+  // bf16 (G_d^T, H_g^T, H_u^T, zero for t >= M; fr_ldp a multiple of 64).
+  const bf16_t *fr_sd, *fr_sg, *fr_su, *fr_pd, *fr_pg, *fr_pu;
+  int fr_ldp;
+  float *fr_ud, *fr_ugu, *fr_vd, *fr_vgu;
 };
 
 // XCD-aware, grouped tile order.  Workgroups are dispatched round-robin over

@@ -478,161 +478,378 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     }
   }
 
-  // ------------------------------------------------ output
-  // A lane holds 4 consecutive output columns of one token row per MFMA
-  // block.  Each wave passes its 128 x 64 sub-tile through a private 16 KB
-  // LDS region, 64 token rows (fp32) at a time, then reads and writes global
-  // memory in 16-byte pieces along rows.  Region row r (0..63) is 256 bytes;
-  // 16-byte chunk c (columns 4c .. 4c+3) sits at chunk c ^ (r % 16).
-  char *reg = smem + wave * 16384;
-  auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); };
+  if constexpr (EPI == EPI_SWIGLU_BWD_RANK) {
+    // ---------------------------------- SwiGLU' with the rank-r products
+    // Per wave (128 tokens x 64 features), four quarters of 32 tokens: the
+    // quarter's dh goes through a private fp32 staging area (8 KB), de, dg
+    // and h = silu(e) g are stored and also written as bf16 tiles [32 x 64]
+    // (4 KB each, 128-byte rows, chunk ^ (r ^ r / 8) % 8), and 16x16x32
+    // MFMAs contract them: over the wave's 64 features with Ad, Bg^T, Bu^T
+    // (row reads) and over the quarter's 32 tokens with G_d^T, H_g^T, H_u^T
+    // (transpose reads).  Feature sums of the 4 waves that share tokens, and
+    // token sums of the 2 waves that share features, are added through LDS
+    // in a fixed order and written once per tile.
+    constexpr int WREG = 20480;
+    char *stg = smem + wave * WREG;
+    char *const tl0 = stg + 8192, *const tl1 = stg + 12288, *const tl2 = stg + 16384;
+    auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); };
+    auto tb_off = [](int r, int c) -> uint32_t {
+      return (uint32_t)(r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4));
+    };
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int fcol0 = n0 + wn * 64, trow0 = m0 + wm * 128;
+    const int tiles_n = p.tiles_n;
+    f32x4 vd[4], vg[4], vu[4];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    load_eg(half);
-    // region rows jj * 32 + l32 hold token block j = 2 half + jj
+    for (int nb = 0; nb < 4; ++nb) vd[nb] = vg[nb] = vu[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int q = lane & 7;                       // 8-column group
+    const int n = fcol0 + 8 * q;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jq = 0; jq < 4; ++jq) {
+      // the quarter's dh (token block jq) into the staging area first: its
+      // accumulators are free before the quarter's operands are loaded
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x16 &a = acc[i][2 * half + jj];
+          const f32x16 &a = acc[i][jq];
           const u32x4 v = {__float_as_uint(a[4 * g]), __float_as_uint(a[4 * g + 1]),
                            __float_as_uint(a[4 * g + 2]), __float_as_uint(a[4 * g + 3])};
-          lds_write16(reg, ep_off(jj * 32 + l32, 8 * i + 2 * g + hi32), v);
+          lds_write16(stg, ep_off(l32, 8 * i + 2 * g + hi32), v);
         }
-    lgkm0();
-    __builtin_amdgcn_wave_barrier();
-    const int mrow0 = m0 + wm * 128 + half * 64;   // token of region row 0
-    if constexpr (GU) {
-      // region columns 0..31: gate, 32..63: up, features tn*128 + wn*32 + c
-      const int f = p.gu_f;
-      const int q = lane & 3;                       // 8-feature group
+      u32x4 ein[4], gin[4];
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int r = it * 16 + (lane >> 2);
-        const int m = mrow0 + r;
-        const int jf = tn * 128 + wn * 32 + 8 * q;
-        const u32x4 e0 = lds_read16(reg, ep_off(r, 2 * q)), e1 = lds_read16(reg, ep_off(r, 2 * q + 1));
-        const u32x4 g0 = lds_read16(reg, ep_off(r, 8 + 2 * q)), g1 = lds_read16(reg, ep_off(r, 9 + 2 * q));
-        if (m < M && jf < f) {
-          float ev[8] = {__uint_as_float(e0[0]), __uint_as_float(e0[1]), __uint_as_float(e0[2]),
-                         __uint_as_float(e0[3]), __uint_as_float(e1[0]), __uint_as_float(e1[1]),
-                         __uint_as_float(e1[2]), __uint_as_float(e1[3])};
-          float gv[8] = {__uint_as_float(g0[0]), __uint_as_float(g0[1]), __uint_as_float(g0[2]),
-                         __uint_as_float(g0[3]), __uint_as_float(g1[0]), __uint_as_float(g1[1]),
-                         __uint_as_float(g1[2]), __uint_as_float(g1[3])};
-          if (p.rowscale) {   // folded RMSNorm: the row's rstd
-            const float rs = p.rowscale[m];
+        const int m = trow0 + jq * 32 + it * 8 + (lane >> 3);
+        u32x4 e = {0, 0, 0, 0}, g = {0, 0, 0, 0};
+        if (m < M && n < N) {
+          const int64_t off = (int64_t)m * N + n;
+          e = gload16(p.Ein + off);
+          g = gload16(p.Gin + off);
+        }
+        ein[it] = e;
+        gin[it] = g;
+      }
+      const int tk = trow0 + jq * 32 + 8 * g4;    // token-contraction K block
+      u32x4 pd = {0, 0, 0, 0}, pg = pd, pu = pd;
+      if (tk < p.fr_ldp) {
+        const int64_t o = (int64_t)l16 * p.fr_ldp + tk;
+        pd = gload16(p.fr_pd + o);
+        pg = gload16(p.fr_pg + o);
+        pu = gload16(p.fr_pu + o);
+      }
+      lgkm0();
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              ev[t] *= rs;
-              gv[t] *= rs;
-            }
-          }
-          u32x4 ew, gw, hw;
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int m = trow0 + jq * 32 + r;
+        const u32x4 a0 = lds_read16(stg, ep_off(r, 2 * q)), a1 = lds_read16(stg, ep_off(r, 2 * q + 1));
+        const bool valid = m < M && n < N;
+        const float v[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
+                            __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
+                            __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+        u32x4 dew = {0, 0, 0, 0}, dgw = dew, hw = dew;
+        float csum = 0.f;
+        if (valid) {
+          const u32x4 ev = ein[it], gv = gin[it];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            ew[t] = pack_bf16x2(ev[2 * t], ev[2 * t + 1]);
-            gw[t] = pack_bf16x2(gv[2 * t], gv[2 * t + 1]);
-            // h from the rounded e, g: the same values the backward reloads
-            const float ea = bf16lo(ew[t]), eb = bf16hi(ew[t]);
-            const float ga = bf16lo(gw[t]), gb = bf16hi(gw[t]);
-            hw[t] = pack_bf16x2(ea * sigmoidf_fast(ea) * ga, eb * sigmoidf_fast(eb) * gb);
+            float de[2], dg[2], hh[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
+              const float gg = h2 ? bf16hi(gv[t]) : bf16lo(gv[t]);
+              const float dh = v[2 * t + h2];
+              const float sgm = sigmoidf_fast(e);
+              dg[h2] = dh * e * sgm;
+              de[h2] = dh * gg * sgm * (1.0f + e * (1.0f - sgm));
+              hh[h2] = e * sgm * gg;
+            }
+            dew[t] = pack_bf16x2(de[0], de[1]);
+            dgw[t] = pack_bf16x2(dg[0], dg[1]);
+            hw[t] = pack_bf16x2(hh[0], hh[1]);
+            if (p.cpart)
+              csum += bf16lo(dew[t]) * bf16lo(ev[t]) + bf16hi(dew[t]) * bf16hi(ev[t]) +
+                      bf16lo(dgw[t]) * bf16lo(gv[t]) + bf16hi(dgw[t]) * bf16hi(gv[t]);
           }
-          const int64_t off = (int64_t)m * f + jf;
-          gstore16(p.E + off, ew);
-          gstore16(p.G + off, gw);
-          gstore16(p.H + off, hw);
+          const int64_t doff = (int64_t)m * p.ldd + n;
+          gstore16(p.DE + doff, dew);
+          gstore16(p.DG + doff, dgw);
+        }
+        if (p.cpart) {   // folded RMSNorm: see EPI_SWIGLU_BWD
+          csum += __shfl_xor(csum, 1, 64);
+          csum += __shfl_xor(csum, 2, 64);
+          csum += __shfl_xor(csum, 4, 64);
+          if (q == 0 && m < M) p.cpart[(int64_t)(tn * 4 + wn) * M + m] = csum;
+        }
+        lds_write16(tl0, tb_off(r, q), hw);
+        lds_write16(tl1, tb_off(r, q), dew);
+        lds_write16(tl2, tb_off(r, q), dgw);
+      }
+      lgkm0();
+      __builtin_amdgcn_wave_barrier();
+      // feature-contraction operands (rows q = l16 of Ad, Bg^T, Bu^T over the
+      // wave's features), in flight behind the token contractions
+      u32x4 sd[2], sg[2], su[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int nk = fcol0 + 32 * ks + 8 * g4;
+        const u32x4 z = {0, 0, 0, 0};
+        const bool ok = nk < N;
+        const int64_t o = (int64_t)l16 * N + nk;
+        sd[ks] = ok ? gload16(p.fr_sd + o) : z;
+        sg[ks] = ok ? gload16(p.fr_sg + o) : z;
+        su[ks] = ok ? gload16(p.fr_su + o) : z;
+      }
+      // token contractions: D[q][n] of the wave's four 16-feature blocks
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int col = nb * 16 + 4 * (l16 & 3);
+        const int r0 = 8 * g4 + (l16 >> 2);
+        const uint32_t o0 = tb_off(r0, col >> 3) + (col & 7) * 2;
+        const uint32_t o1 = tb_off(r0 + 4, col >> 3) + (col & 7) * 2;
+        const u32x2 h0 = lds_read_tr8(tl0, o0), h1 = lds_read_tr8(tl0, o1);
+        const u32x2 d0 = lds_read_tr8(tl1, o0), d1 = lds_read_tr8(tl1, o1);
+        const u32x2 x0 = lds_read_tr8(tl2, o0), x1 = lds_read_tr8(tl2, o1);
+        vd[nb] = mfma16(pd, u32x4{h0[0], h0[1], h1[0], h1[1]}, vd[nb]);
+        vg[nb] = mfma16(pg, u32x4{d0[0], d0[1], d1[0], d1[1]}, vg[nb]);
+        vu[nb] = mfma16(pu, u32x4{x0[0], x0[1], x1[0], x1[1]}, vu[nb]);
+      }
+      // feature contractions: D[q][t] of the quarter's two 16-token blocks
+      f32x4 uh[2], ug[2], uu[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        uh[tb] = ug[tb] = uu[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint32_t o = tb_off(tb * 16 + l16, 4 * ks + g4);
+          uh[tb] = mfma16(sd[ks], lds_read16(tl0, o), uh[tb]);
+          ug[tb] = mfma16(sg[ks], lds_read16(tl1, o), ug[tb]);
+          uu[tb] = mfma16(su[ks], lds_read16(tl2, o), uu[tb]);
         }
       }
-    } else {
-      const int q = lane & 7;                       // 8-column group
-      const int n = n0 + wn * 64 + 8 * q;
+      // the 4 waves of this token half add their feature sums: product
+      // slot (p, tb) of every wave, then wave (wm, wn < 3) sums product wn
+      lgkm0();
+      auto red_off = [&](int w, int pr, int tb) -> uint32_t {
+        return (uint32_t)(w * WREG + ((pr * 2 + tb) * 64 + lane) * 16);
+      };
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int r = it * 8 + (lane >> 3);
-        const int m = mrow0 + r;
-        const u32x4 a0 = lds_read16(reg, ep_off(r, 2 * q)), a1 = lds_read16(reg, ep_off(r, 2 * q + 1));
-        const bool valid = m < M && n < N;
-        float v[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
-                      __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
-                      __uint_as_float(a1[2]), __uint_as_float(a1[3])};
-        if constexpr (EPI == EPI_STORE) {
-          if (!valid) continue;
-          if (p.nrm_x) {   // RMSNorm input gradient from the folded projections' output
-            const u32x4 xv = gload16(p.nrm_x + (int64_t)m * N + n);
-            const float rs = p.nrm_rs[m], kk = p.nrm_kk[m];
+      for (int tb = 0; tb < 2; ++tb) {
+        *reinterpret_cast<f32x4 *>(smem + red_off(wave, 0, tb)) = uh[tb];
+        *reinterpret_cast<f32x4 *>(smem + red_off(wave, 1, tb)) = ug[tb];
+        *reinterpret_cast<f32x4 *>(smem + red_off(wave, 2, tb)) = uu[tb];
+      }
+      __syncthreads();
+      if (wn < 3) {
+        const int pr = wn;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              v[2 * t] = rs * v[2 * t] - kk * bf16lo(xv[t]);
-              v[2 * t + 1] = rs * v[2 * t + 1] - kk * bf16hi(xv[t]);
-            }
+        for (int tb = 0; tb < 2; ++tb) {
+          f32x4 sum = *reinterpret_cast<const f32x4 *>(smem + red_off(wm, pr, tb));
+#pragma unroll
+          for (int w2 = 1; w2 < 4; ++w2) {
+            const f32x4 o = *reinterpret_cast<const f32x4 *>(smem + red_off(w2 * 2 + wm, pr, tb));
+            sum = f32x4{sum[0] + o[0], sum[1] + o[1], sum[2] + o[2], sum[3] + o[3]};
           }
-          bf16_t *cb = p.C;
-          int64_t ldc = p.ldc;
-          int ncs = 0;
-          if (p.nseg1 > 0 && n0 >= p.nseg1) {
-            const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
-            cb = s2 ? p.C2 : p.C1;
-            ldc = s2 ? p.ldc2 : p.ldc1;
-            ncs = s2 ? p.nseg2 : p.nseg1;
+          const int t = trow0 + jq * 32 + tb * 16 + l16;
+          if (t < M) {
+            float *dst = pr == 0 ? p.fr_ud + ((int64_t)tn * M + t) * 16
+                                 : p.fr_ugu + ((int64_t)((pr == 2 ? tiles_n : 0) + tn) * M + t) * 16;
+            *reinterpret_cast<f32x4 *>(dst + 4 * g4) = sum;
           }
-          bf16_t *dst = cb + (int64_t)m * ldc + (n - ncs);
-          if (p.accumulate) {
-            const u32x4 o = gload16(dst);
+        }
+      }
+      __syncthreads();   // staging areas free for the next quarter
+    }
+    // the 2 waves of this feature block add their token sums: wave wm = 0
+    // writes dAd and dBg, wave wm = 1 dBu
+    auto vred_off = [&](int w, int pr, int nb) -> uint32_t {
+      return (uint32_t)(w * WREG + ((pr * 4 + nb) * 64 + lane) * 16);
+    };
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              v[2 * t] += bf16lo(o[t]);
-              v[2 * t + 1] += bf16hi(o[t]);
-            }
-          }
-          u32x4 w;
+    for (int nb = 0; nb < 4; ++nb) {
+      *reinterpret_cast<f32x4 *>(smem + vred_off(wave, 0, nb)) = vd[nb];
+      *reinterpret_cast<f32x4 *>(smem + vred_off(wave, 1, nb)) = vg[nb];
+      *reinterpret_cast<f32x4 *>(smem + vred_off(wave, 2, nb)) = vu[nb];
+    }
+    __syncthreads();
+    const int w0 = wn * 2, w1 = wn * 2 + 1;      // the two waves of this feature block
 #pragma unroll
-          for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
-          gstore16(dst, w);
-        } else {  // EPI_SWIGLU_BWD: v = dh
-          float csum = 0.f;
-          if (valid) {
-            const u32x4 ev = ein[it], gv = gin[it];
-            u32x4 dew, dgw;
+    for (int pr = 0; pr < 3; ++pr) {
+      if ((pr < 2) != (wm == 0)) continue;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              float de[2], dg[2];
+      for (int nb = 0; nb < 4; ++nb) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(smem + vred_off(w0, pr, nb));
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(smem + vred_off(w1, pr, nb));
+        const int ng = fcol0 + nb * 16 + l16;
+        if (ng >= N) continue;
 #pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2) {
-                const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
-                const float gg = h2 ? bf16hi(gv[t]) : bf16lo(gv[t]);
-                const float dh = v[2 * t + h2];
-                const float sg = sigmoidf_fast(e);
-                dg[h2] = dh * e * sg;
-                de[h2] = dh * gg * sg * (1.0f + e * (1.0f - sg));
-              }
-              dew[t] = pack_bf16x2(de[0], de[1]);
-              dgw[t] = pack_bf16x2(dg[0], dg[1]);
-              // de e + dg g with de, dg as stored (a folded RMSNorm's row
-              // coefficient; unused otherwise)
-              if (p.cpart)
-                csum += bf16lo(dew[t]) * bf16lo(ev[t]) + bf16hi(dew[t]) * bf16hi(ev[t]) +
-                        bf16lo(dgw[t]) * bf16lo(gv[t]) + bf16hi(dgw[t]) * bf16hi(gv[t]);
-            }
-            const int64_t doff = (int64_t)m * p.ldd + n;
-            gstore16(p.DE + doff, dew);
-            gstore16(p.DG + doff, dgw);
-          }
-          if (p.cpart) {
-            // the 8 lanes of one row (lanes 8j .. 8j+7) add their sums in a
-            // fixed butterfly; every lane takes part (invalid ones add 0)
-            csum += __shfl_xor(csum, 1, 64);
-            csum += __shfl_xor(csum, 2, 64);
-            csum += __shfl_xor(csum, 4, 64);
-            if (q == 0 && m < M) p.cpart[(int64_t)(tn * 4 + wn) * M + m] = csum;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int qq = 4 * g4 + e;
+          const float v = a[e] + b[e];
+          if (pr == 0) p.fr_vd[((int64_t)tm * 16 + qq) * N + ng] = v;
+          else p.fr_vgu[((int64_t)tm * 16 + qq) * 2 * N + (pr == 2 ? N : 0) + ng] = v;
         }
       }
     }
-    lgkm0();
-    __builtin_amdgcn_wave_barrier();
+  } else {
+  // ------------------------------------------------ output
+    // A lane holds 4 consecutive output columns of one token row per MFMA
+    // block.  Each wave passes its 128 x 64 sub-tile through a private 16 KB
+    // LDS region, 64 token rows (fp32) at a time, then reads and writes global
+    // memory in 16-byte pieces along rows.  Region row r (0..63) is 256 bytes;
+    // 16-byte chunk c (columns 4c .. 4c+3) sits at chunk c ^ (r % 16).
+    char *reg = smem + wave * 16384;
+    auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); };
+  #pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      load_eg(half);
+      // region rows jj * 32 + l32 hold token block j = 2 half + jj
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+  #pragma unroll
+        for (int i = 0; i < 2; ++i)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16 &a = acc[i][2 * half + jj];
+            const u32x4 v = {__float_as_uint(a[4 * g]), __float_as_uint(a[4 * g + 1]),
+                             __float_as_uint(a[4 * g + 2]), __float_as_uint(a[4 * g + 3])};
+            lds_write16(reg, ep_off(jj * 32 + l32, 8 * i + 2 * g + hi32), v);
+          }
+      lgkm0();
+      __builtin_amdgcn_wave_barrier();
+      const int mrow0 = m0 + wm * 128 + half * 64;   // token of region row 0
+      if constexpr (GU) {
+        // region columns 0..31: gate, 32..63: up, features tn*128 + wn*32 + c
+        const int f = p.gu_f;
+        const int q = lane & 3;                       // 8-feature group
+  #pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = it * 16 + (lane >> 2);
+          const int m = mrow0 + r;
+          const int jf = tn * 128 + wn * 32 + 8 * q;
+          const u32x4 e0 = lds_read16(reg, ep_off(r, 2 * q)), e1 = lds_read16(reg, ep_off(r, 2 * q + 1));
+          const u32x4 g0 = lds_read16(reg, ep_off(r, 8 + 2 * q)), g1 = lds_read16(reg, ep_off(r, 9 + 2 * q));
+          if (m < M && jf < f) {
+            float ev[8] = {__uint_as_float(e0[0]), __uint_as_float(e0[1]), __uint_as_float(e0[2]),
+                           __uint_as_float(e0[3]), __uint_as_float(e1[0]), __uint_as_float(e1[1]),
+                           __uint_as_float(e1[2]), __uint_as_float(e1[3])};
+            float gv[8] = {__uint_as_float(g0[0]), __uint_as_float(g0[1]), __uint_as_float(g0[2]),
+                           __uint_as_float(g0[3]), __uint_as_float(g1[0]), __uint_as_float(g1[1]),
+                           __uint_as_float(g1[2]), __uint_as_float(g1[3])};
+            if (p.rowscale) {   // folded RMSNorm: the row's rstd
+              const float rs = p.rowscale[m];
+  #pragma unroll
+              for (int t = 0; t < 8; ++t) {
+                ev[t] *= rs;
+                gv[t] *= rs;
+              }
+            }
+            u32x4 ew, gw, hw;
+  #pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              ew[t] = pack_bf16x2(ev[2 * t], ev[2 * t + 1]);
+              gw[t] = pack_bf16x2(gv[2 * t], gv[2 * t + 1]);
+              // h from the rounded e, g: the same values the backward reloads
+              const float ea = bf16lo(ew[t]), eb = bf16hi(ew[t]);
+              const float ga = bf16lo(gw[t]), gb = bf16hi(gw[t]);
+              hw[t] = pack_bf16x2(ea * sigmoidf_fast(ea) * ga, eb * sigmoidf_fast(eb) * gb);
+            }
+            const int64_t off = (int64_t)m * f + jf;
+            gstore16(p.E + off, ew);
+            gstore16(p.G + off, gw);
+            gstore16(p.H + off, hw);
+          }
+        }
+      } else {
+        const int q = lane & 7;                       // 8-column group
+        const int n = n0 + wn * 64 + 8 * q;
+  #pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int r = it * 8 + (lane >> 3);
+          const int m = mrow0 + r;
+          const u32x4 a0 = lds_read16(reg, ep_off(r, 2 * q)), a1 = lds_read16(reg, ep_off(r, 2 * q + 1));
+          const bool valid = m < M && n < N;
+          float v[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
+                        __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
+                        __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+          if constexpr (EPI == EPI_STORE) {
+            if (!valid) continue;
+            if (p.nrm_x) {   // RMSNorm input gradient from the folded projections' output
+              const u32x4 xv = gload16(p.nrm_x + (int64_t)m * N + n);
+              const float rs = p.nrm_rs[m], kk = p.nrm_kk[m];
+  #pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                v[2 * t] = rs * v[2 * t] - kk * bf16lo(xv[t]);
+                v[2 * t + 1] = rs * v[2 * t + 1] - kk * bf16hi(xv[t]);
+              }
+            }
+            bf16_t *cb = p.C;
+            int64_t ldc = p.ldc;
+            int ncs = 0;
+            if (p.nseg1 > 0 && n0 >= p.nseg1) {
+              const bool s2 = p.nseg2 > 0 && n0 >= p.nseg2;
+              cb = s2 ? p.C2 : p.C1;
+              ldc = s2 ? p.ldc2 : p.ldc1;
+              ncs = s2 ? p.nseg2 : p.nseg1;
+            }
+            bf16_t *dst = cb + (int64_t)m * ldc + (n - ncs);
+            if (p.accumulate) {
+              const u32x4 o = gload16(dst);
+  #pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                v[2 * t] += bf16lo(o[t]);
+                v[2 * t + 1] += bf16hi(o[t]);
+              }
+            }
+            u32x4 w;
+  #pragma unroll
+            for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
+            gstore16(dst, w);
+          } else {  // EPI_SWIGLU_BWD: v = dh
+            float csum = 0.f;
+            if (valid) {
+              const u32x4 ev = ein[it], gv = gin[it];
+              u32x4 dew, dgw;
+  #pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                float de[2], dg[2];
+  #pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                  const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
+                  const float gg = h2 ? bf16hi(gv[t]) : bf16lo(gv[t]);
+                  const float dh = v[2 * t + h2];
+                  const float sg = sigmoidf_fast(e);
+                  dg[h2] = dh * e * sg;
+                  de[h2] = dh * gg * sg * (1.0f + e * (1.0f - sg));
+                }
+                dew[t] = pack_bf16x2(de[0], de[1]);
+                dgw[t] = pack_bf16x2(dg[0], dg[1]);
+                // de e + dg g with de, dg as stored (a folded RMSNorm's row
+                // coefficient; unused otherwise)
+                if (p.cpart)
+                  csum += bf16lo(dew[t]) * bf16lo(ev[t]) + bf16hi(dew[t]) * bf16hi(ev[t]) +
+                          bf16lo(dgw[t]) * bf16lo(gv[t]) + bf16hi(dgw[t]) * bf16hi(gv[t]);
+              }
+              const int64_t doff = (int64_t)m * p.ldd + n;
+              gstore16(p.DE + doff, dew);
+              gstore16(p.DG + doff, dgw);
+            }
+            if (p.cpart) {
+              // the 8 lanes of one row (lanes 8j .. 8j+7) add their sums in a
+              // fixed butterfly; every lane takes part (invalid ones add 0)
+              csum += __shfl_xor(csum, 1, 64);
+              csum += __shfl_xor(csum, 2, 64);
+              csum += __shfl_xor(csum, 4, 64);
+              if (q == 0 && m < M) p.cpart[(int64_t)(tn * 4 + wn) * M + m] = csum;
+            }
+          }
+        }
+      }
+      lgkm0();
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
