@@ -674,23 +674,32 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       *reinterpret_cast<f32x4 *>(smem + vred_off(wave, 2, nb)) = vu[nb];
     }
     __syncthreads();
+    // Each lane then writes 16 bytes: row q = 4 (l / 16) + e_q of a product,
+    // columns nb * 16 + 4 (l % 4) .. +3 for e_q = (l / 4) % 4 -- values of
+    // lanes 4 (l % 4) .. +3 of the MFMA layout (lane (n, g) holds q = 4 g ..
+    // 4 g + 3 of column n), read back from LDS with one word per lane.
     const int w0 = wn * 2, w1 = wn * 2 + 1;      // the two waves of this feature block
+    const int vq = 4 * (lane >> 4) + ((lane >> 2) & 3);   // row q
+    const int vc = 4 * (lane & 3);                         // first of 4 columns in the block
 #pragma unroll
     for (int pr = 0; pr < 3; ++pr) {
       if ((pr < 2) != (wm == 0)) continue;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(smem + vred_off(w0, pr, nb));
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(smem + vred_off(w1, pr, nb));
-        const int ng = fcol0 + nb * 16 + l16;
-        if (ng >= N) continue;
+        const int ng = fcol0 + nb * 16 + vc;
+        f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qq = 4 * g4 + e;
-          const float v = a[e] + b[e];
-          if (pr == 0) p.fr_vd[((int64_t)tm * 16 + qq) * N + ng] = v;
-          else p.fr_vgu[((int64_t)tm * 16 + qq) * 2 * N + (pr == 2 ? N : 0) + ng] = v;
+        for (int c = 0; c < 4; ++c) {
+          // source lane: column vc + c, group vq / 4, element vq % 4
+          const int sl = (vq >> 2) * 16 + vc + c;
+          const uint32_t o = (uint32_t)(((pr * 4 + nb) * 64 + sl) * 16 + (vq & 3) * 4);
+          v[c] = *reinterpret_cast<const float *>(smem + w0 * WREG + o) +
+                 *reinterpret_cast<const float *>(smem + w1 * WREG + o);
         }
+        if (ng >= N) continue;   // N % 8 == 0: a 4-column group is all in or all out
+        float *dst = pr == 0 ? p.fr_vd + ((int64_t)tm * 16 + vq) * N + ng
+                             : p.fr_vgu + ((int64_t)tm * 16 + vq) * 2 * N + (pr == 2 ? N : 0) + ng;
+        *reinterpret_cast<f32x4 *>(dst) = v;
       }
     }
   } else {
