@@ -57,6 +57,12 @@ def parse():
                     help="print the HBM-traffic summary (markdown) of the GEMM classes from "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection CSVs of "
                          "bench.py and of --calibrate-copy")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("SQ_CSV_1", "SQ_CSV_2"),
+                    help="print the GEMM classes' shader-engine counter table from the two "
+                         "rocprofv3 --pmc counter_collection CSVs of bench.py")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "STEP"),
+                    help="print the kernel table and one step's dispatches from a "
+                         "rocprofv3 --kernel-trace --stats output folder of bench.py")
     return ap.parse_args()
 
 
@@ -80,24 +86,63 @@ def _counter_rows(path):
     return rows
 
 
+# A profiled `bench.py --steps 1 --warmup 1` runs the step form that `value`
+# times in its first five steps (warm-up, two probe steps, the timed step, the
+# per-class pass); later passes use other forms (weights as stored, the norm
+# comparisons).  Summaries average steps 2-5 of the run.
+PROFILED_STEPS = range(1, 5)
+
+
+def _step_starts(names):
+    """Index of each step's first dispatch: the forward opens with k_prep
+    followed by the rank-r pass over X (or by the norm's rstd pass)."""
+    return [i for i in range(len(names) - 1) if "k_prep" in names[i]
+            and ("k_skinny_nt<32" in names[i + 1] or "k_rmsnorm_fwd" in names[i + 1])]
+
+
+def _steps(rows):
+    """rows sorted by dispatch -> list of steps, each a list of rows."""
+    names = [r[1] for r in rows]
+    st = _step_starts(names) + [len(rows)]
+    return [rows[st[i]:st[i + 1]] for i in range(len(st) - 1)]
+
+
 def _gemm_class_values(rows):
-    """Counter value (KiB) per dispatch of each GEMM class: a step launches
-    the GEMMs in the order gate/up fwd, down fwd, down bwd, gate/up bwd."""
-    gem = [v for _, name, v in rows if "k_lora_gemm" in name]
+    """Counter value (KiB) per dispatch of each GEMM class over the profiled
+    steps: a step launches the GEMMs in the order gate/up fwd, down fwd,
+    down bwd, gate/up bwd."""
     out = {i: [] for i in range(4)}
-    for j, v in enumerate(gem):
-        out[j % 4].append(v)
+    steps = _steps(rows)
+    for k in PROFILED_STEPS:
+        gem = [v for _, name, v in steps[k] if "k_lora_gemm" in name]
+        assert len(gem) == 4, f"step {k}: {len(gem)} GEMM dispatches"
+        for j, v in enumerate(gem):
+            out[j].append(v)
     return out
 
 
+def _short(name, width=72):
+    name = name.replace("lora::", "").replace("void ", "")
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def traffic_path(cfg):
+    from lora_inputs import CONFIGS
+    c = CONFIGS[cfg]
+    shape = "T%d_d%d_f%d_r%d" % (c["T"], c["d"], c["f"], c["r"])
+    return TRAFFIC_SUMMARY.format(shape=shape + ("_q4" if c.get("q4") else ""))
+
+
 def summarize_counters(fetch_csv, write_csv, cf_csv, cw_csv, cfg):
-    """Markdown summary with a machine-readable line read back by bench.py."""
+    """Markdown summary with a machine-readable line read back by bench.py:
+    per GEMM class and, for one step, per dispatch."""
     copy_bytes = 256 << 20
     cf = [v for _, n, v in _counter_rows(cf_csv) if "copyBuffer" in n]
     cw = [v for _, n, v in _counter_rows(cw_csv) if "copyBuffer" in n]
     f_fac = copy_bytes / (sum(cf) / len(cf) * 1024)
     w_fac = copy_bytes / (sum(cw) / len(cw) * 1024)
-    fv, wv = _gemm_class_values(_counter_rows(fetch_csv)), _gemm_class_values(_counter_rows(write_csv))
+    frows, wrows = _counter_rows(fetch_csv), _counter_rows(write_csv)
+    fv, wv = _gemm_class_values(frows), _gemm_class_values(wrows)
     per = {}
     for i in range(4):
         fb = sum(fv[i]) / len(fv[i]) * 1024 * f_fac
@@ -110,24 +155,104 @@ def summarize_counters(fetch_csv, write_csv, cf_csv, cw_csv, cfg):
     for k, v in per.items():
         lines.append(f"| {k} | {v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.1f} | "
                      f"{v['traffic_bytes'] / 1e6:.1f} |")
+    k = PROFILED_STEPS[0]
+    fs, ws = _steps(frows)[k], _steps(wrows)[k]
+    lines += ["", f"Every dispatch of step {k + 1} (scaled MB):", "",
+              "| # | kernel | FETCH MB | WRITE MB |", "|---|---|---|---|"]
+    for i, ((_, n, fv_), (_, n2, wv_)) in enumerate(zip(fs, ws)):
+        assert n == n2, (n, n2)
+        lines.append(f"| {i} | `{_short(n)}` | {fv_ * 1024 * f_fac / 1e6:.1f} | "
+                     f"{wv_ * 1024 * w_fac / 1e6:.1f} |")
     return "\n".join(lines) + "\n\ntraffic-record: " + json.dumps(rec) + "\n"
+
+
+def summarize_sq(csv1, csv2):
+    """Shader-engine counters of the four GEMM classes (medians over the
+    profiled steps) from two --pmc runs: clock, achieved MFMA rate, MFMA-busy
+    fraction, LDS bank conflicts and the share of wave time waiting on LDS."""
+    import csv
+    import statistics
+
+    def load(path):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            rows.setdefault(key, {"dur": dur})[r["Counter_Name"]] = float(r["Counter_Value"])
+        disp = sorted(rows)
+        steps = _steps([(i, n, 0.0) for i, n in disp])
+        out = {i: [] for i in range(4)}
+        for k in PROFILED_STEPS:
+            gem = [(i, n) for i, n, _ in steps[k] if "k_lora_gemm" in n]
+            assert len(gem) == 4
+            for j, key in enumerate(gem):
+                out[j].append(rows[key])
+        return out
+
+    a, b = load(csv1), load(csv2)
+    med = statistics.median
+    lines = ["| GEMM | dispatches | duration ms | clock GHz | TFLOP/s | peak at that clock "
+             "| MFMA busy | LDS bank conflicts | wave time waiting on LDS issue |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for i in range(4):
+        A, B = a[i], b[i]
+        clk = med([x["GRBM_GUI_ACTIVE"] / 8 / x["dur"] for x in B])   # one GRBM per XCD
+        dur = med([x["dur"] for x in B])
+        tf = med([x["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / x["dur"] for x in A]) / 1e12
+        busy = med([x["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (clk * x["dur"]) for x in A])
+        bc = med([x["SQ_LDS_BANK_CONFLICT"] for x in A])
+        wl = med([x["SQ_WAIT_INST_LDS"] / x["SQ_WAVE_CYCLES"] for x in A])
+        lines.append(f"| {KC_NAMES[i]} | {len(B)} | {dur * 1e3:.3f} | {clk / 1e9:.2f} | "
+                     f"{tf:.0f} | {256 * 4096 * clk / 1e12:.0f} | {busy * 100:.0f} % | "
+                     f"{bc:.0f} | {wl * 100:.1f} % |")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_trace(trace_dir, step):
+    """rocprofv3 --kernel-trace --stats output of a bench.py run: the stats
+    table as written, and every dispatch of step `step` (0-based) with its
+    start offset, the gap before it and its duration."""
+    import csv
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    lines = ["| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        if "copyBuffer" in r["Name"]:
+            continue
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} "
+                     f"| {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    tr = sorted(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))),
+                key=lambda r: int(r["Start_Timestamp"]))
+    rows = [(int(r["Start_Timestamp"]), r["Kernel_Name"], int(r["End_Timestamp"])) for r in tr]
+    steps = _steps(rows)
+    one = steps[step]
+    t0 = prev = one[0][0]
+    lines += ["", f"Step {step + 1} of {len(steps)} found in the trace (offset / gap before / "
+                  "duration, us):", "", "```"]
+    for s, n, e in one:
+        lines.append(f"{(s - t0) / 1e3:8.1f} gap {max(0, s - prev) / 1e3:5.1f} "
+                     f"dur {(e - s) / 1e3:8.1f}  {_short(n, 64)}")
+        prev = e
+    lines += [f"step span {(prev - t0) / 1e3:.1f} us", "```"]
+    return "\n".join(lines) + "\n"
 
 
 def stored_traffic(cfg, kernel_name):
     """HBM bytes per launch of `kernel_name` from the committed counter
     summary, or None when there is none or the HIP sources changed since."""
     from lora_inputs import CONFIGS
-    c = CONFIGS[cfg]
-    if c.get("kind") != "mlp":
+    if CONFIGS[cfg].get("kind") != "mlp":
         return None
-    path = TRAFFIC_SUMMARY.format(shape="T%d_d%d_f%d_r%d" % (c["T"], c["d"], c["f"], c["r"]))
+    path = traffic_path(cfg)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         for line in fh:
             if line.startswith("traffic-record: "):
                 rec = json.loads(line[len("traffic-record: "):])
-                if rec.get("source_sha256") != kernel_source_digest():
+                if rec.get("source_sha256") != kernel_source_digest() or \
+                        rec.get("config_id") != cfg:
                     return None
                 v = rec["per_launch"].get(kernel_name)
                 return None if v is None else v["traffic_bytes"]
@@ -416,6 +541,12 @@ def main():
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.config), end="")
+        return
+    if args.summarize_sq:
+        print(summarize_sq(*args.summarize_sq), end="")
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace[0], int(args.summarize_trace[1])), end="")
         return
     if args.config == 4:
         bench_attn_mlp(args)

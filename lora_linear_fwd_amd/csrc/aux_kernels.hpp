@@ -621,8 +621,11 @@ __global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
 }
 
 // ---------------------------------------------------------------------------
-// standalone 4-bit decode: each thread decodes 32 consecutive elements
-// (16 code bytes) and writes 64 bytes of bf16.  HBM-bound.
+// standalone 4-bit decode.  A wave decodes 2048 consecutive elements in
+// four passes; in each pass lane l takes code bytes 4 l .. 4 l + 3 of the
+// pass's 256 (8 elements, one 64-element block constant) and stores their
+// 16 bytes of bf16, so every load instruction covers 256 contiguous bytes
+// and every store 1 KB.  total is a multiple of 64.  HBM-bound.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_dequant4(const uint8_t *codes, const AbsmaxSrc absmax,
                                                   const float *codebook, int64_t total,
@@ -630,20 +633,27 @@ __global__ __launch_bounds__(256) void k_dequant4(const uint8_t *codes, const Ab
   __shared__ float2 cbt[256];
   cbt[threadIdx.x] = make_float2(codebook[threadIdx.x & 15], codebook[threadIdx.x >> 4]);
   __syncthreads();
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 32-element group
-  if (g * 32 >= total) return;
-  const u32x4 c = gload16(codes + g * 16);
-  const float am = absmax_at(absmax, (g * 32) >> 6);
-  u32x4 o[4];
+  const int lane = threadIdx.x & 63;
+  const int64_t e0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2048 + lane * 8;
+  uint32_t c[4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
+  for (int w = 0; w < 4; ++w) {
+    const int64_t e = e0 + w * 512;
+    c[w] = e < total ? *reinterpret_cast<const uint32_t *>(codes + e / 2) : 0u;
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int64_t e = e0 + w * 512;
+    if (e >= total) break;
+    const float am = absmax_at(absmax, e >> 6);
+    u32x4 o;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const float2 cv = cbt[(c[w] >> (8 * b)) & 0xFFu];
-      o[w][b] = pack_bf16x2(cv.x * am, cv.y * am);
+      o[b] = pack_bf16x2(cv.x * am, cv.y * am);
     }
-#pragma unroll
-  for (int w = 0; w < 4; ++w) gstore16(out + g * 32 + 8 * w, o[w]);
+    gstore16(out + e, o);
+  }
 }
 
 // ---------------------------------------------------------------------------
