@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 
 #include "aux_kernels.hpp"
 #include "gemm_launch.hpp"
@@ -513,13 +514,14 @@ int skinny_dual(int RS, bool zswiglu, int64_t T, int64_t N, int64_t nsplit, int6
   return LORA_OK;
 }
 
-// [RSout x ldp_of(T)] bf16 transposed copy of columns qoff .. qoff+nq-1 of a
-// [T x ldin] fp32 matrix, zero elsewhere
-int pack_pt(const float *in, int64_t T, int ldin, int qoff, int nq, int RSout, bf16_t *out,
-            hipStream_t st) {
-  const int64_t ldp = ldp_of(T);
-  hipLaunchKernelGGL(k_pack_pt, dim3(blocks_for(RSout * ldp)), dim3(256), 0, st, in, (int)T, ldin,
-                     qoff, nq, RSout, (int)ldp, out);
+// up to three [RSout x ldp_of(T)] bf16 transposed copies, each of columns
+// qoff .. qoff+nq-1 of a [T x ldin] fp32 matrix, zero elsewhere, in one launch
+int pack_pt(std::initializer_list<PackJob> jobs, int64_t T, int RSout, hipStream_t st) {
+  PackBatch b{};
+  if (jobs.size() > 3) return LORA_ERR_UNSUPPORTED;
+  for (const PackJob &j : jobs) b.j[b.n++] = j;
+  b.T = (int)T; b.RSout = RSout; b.ldp = (int)ldp_of(T);
+  hipLaunchKernelGGL(k_pack_pt, dim3(blocks_for((int64_t)b.n * RSout * b.ldp)), dim3(256), 0, st, b);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
 }
@@ -1060,11 +1062,10 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     if (rankf) {
       // the epilogue's token-contraction operands: G_d^T, and H_g^T, H_u^T
       // from H_gu = X [Ag; Au]^T
-      LORA_TRY(pack_pt(gd32, T, RS2, 0, (int)r, RS2, pt_d, st));
       LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart,
                          hgu32, nullptr, 1.f, st, rstd));
-      LORA_TRY(pack_pt(hgu32, T, RS1, 0, (int)r, RS2, pt_g, st));
-      LORA_TRY(pack_pt(hgu32, T, RS1, (int)r, (int)r, RS2, pt_u, st));
+      LORA_TRY(pack_pt({{gd32, RS2, 0, (int)r, pt_d}, {hgu32, RS1, 0, (int)r, pt_g},
+                        {hgu32, RS1, (int)r, (int)r, pt_u}}, T, RS2, st));
     }
     GemmArgs a = gemm_base();
     a.M = (int)T; a.N = (int)f; a.K = (int)d; a.ksplit = (int)d;
@@ -1102,24 +1103,29 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     //   H_d = sum over feature tiles (fp32, for dBd); dAd = s sum over token tiles;
     //   G_gu = [de Bg | dg Bu] (fp32 for dA_gu with the folded norm's rstd,
     //   s G_gu in bf16 for the dX epilogue); dBg, dBu = s sums over token tiles
+    // (one launch; with T = 0 only the gradients, as zeros)
+    ReduceBatch rb{};
     if (T > 0) {
-      ReduceUArgs rd{(const float *)(w + pl.fu_d), (int)T, 16, RS2, (int)r, 1, (int)ftn, 0, 1.f,
-                     hd32, nullptr, nullptr};
-      hipLaunchKernelGGL(k_reduce_dual_u, dim3(blocks_for(T * RS2)), dim3(256), 0, st, rd);
-      HIP_TRY(hipGetLastError());
-      ReduceUArgs rg{(const float *)(w + pl.fu_gu), (int)T, 16, RS1, (int)r, 2, (int)ftn, (int)ftn,
-                     s, ggu32, ggubf, rstd};
-      hipLaunchKernelGGL(k_reduce_dual_u, dim3(blocks_for(T * RS1)), dim3(256), 0, st, rg);
-      HIP_TRY(hipGetLastError());
+      rb.u[0] = ReduceUArgs{(const float *)(w + pl.fu_d), (int)T, 16, RS2, (int)r, 1, (int)ftn, 0,
+                            1.f, hd32, nullptr, nullptr};
+      rb.u[1] = ReduceUArgs{(const float *)(w + pl.fu_gu), (int)T, 16, RS1, (int)r, 2, (int)ftn,
+                            (int)ftn, s, ggu32, ggubf, rstd};
+      rb.nu = 2;
     }
     const int tsv = T > 0 ? (int)ftm : 0;
-    ReduceTNArgs vd{(const float *)(w + pl.fv_d), tsv, 16, (int)f, (int)r, (int)f, s, 0,
-                    (bf16_t *)dAd, nullptr, 0, nullptr, 0, 0, nullptr};
-    hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)16 * f)), dim3(256), 0, st, vd);
-    HIP_TRY(hipGetLastError());
-    ReduceTNArgs vg{(const float *)(w + pl.fv_gu), tsv, 16, (int)(2 * f), (int)r, (int)f, s, 1,
-                    (bf16_t *)dBg, (bf16_t *)dBu, 0, nullptr, 0, 0, nullptr};
-    hipLaunchKernelGGL(k_reduce_tn, dim3(blocks_for((int64_t)16 * 2 * f)), dim3(256), 0, st, vg);
+    rb.v[0] = ReduceTNArgs{(const float *)(w + pl.fv_d), tsv, 16, (int)f, (int)r, (int)f, s, 0,
+                           (bf16_t *)dAd, nullptr, 0, nullptr, 0, 0, nullptr};
+    rb.v[1] = ReduceTNArgs{(const float *)(w + pl.fv_gu), tsv, 16, (int)(2 * f), (int)r, (int)f, s,
+                           1, (bf16_t *)dBg, (bf16_t *)dBu, 0, nullptr, 0, 0, nullptr};
+    rb.nv = 2;
+    const int64_t cnt[4] = {T * RS2, T * RS1, (int64_t)16 * f, (int64_t)16 * 2 * f};
+    int64_t nblk = 0;
+    for (int j = 0, c = rb.nu ? 0 : 2; c < 4; ++j, ++c) {
+      rb.start[j] = nblk;
+      nblk += blocks_for(cnt[c]);
+    }
+    rb.start[rb.nu + rb.nv] = nblk;
+    hipLaunchKernelGGL(k_reduce_batch, dim3((unsigned)nblk), dim3(256), 0, st, rb);
     HIP_TRY(hipGetLastError());
   }
   // 2. one pass over h = silu(e) g (recomputed): H_d = h Ad^T (fp32, for dBd)
@@ -1127,7 +1133,7 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   if (rankf) {
     // formed by the down backward's epilogue
   } else if (dual) {
-    if (T > 0) LORA_TRY(pack_pt(gd32, T, RS2, 0, (int)r, RS2, pt_d, st));   // G_d^T bf16
+    if (T > 0) LORA_TRY(pack_pt({{gd32, RS2, 0, (int)r, pt_d}}, T, RS2, st));   // G_d^T bf16
     LORA_TRY(skinny_dual(RS2, true, T, f, f, f, nullptr, nullptr, eb, gb, side_d_nt, nullptr,
                          pt_d, nullptr, part_u, part_v, r, RS2, 1.f, hd32, nullptr, s, 0,
                          (bf16_t *)dAd, nullptr, st));
@@ -1145,8 +1151,8 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu_nt, ntpart, hgu32,
                        nullptr, 1.f, st, rstd));
     if (dual) {
-      LORA_TRY(pack_pt(hgu32, T, RS1, 0, (int)r, RS2, pt_g, st));
-      LORA_TRY(pack_pt(hgu32, T, RS1, (int)r, (int)r, RS2, pt_u, st));
+      LORA_TRY(pack_pt({{hgu32, RS1, 0, (int)r, pt_g}, {hgu32, RS1, (int)r, (int)r, pt_u}}, T,
+                       RS2, st));
     }
   }
   // 5. G_gu = [de Bg | dg Bu] (fp32 for dA_gu, s G_gu in bf16 for the dX

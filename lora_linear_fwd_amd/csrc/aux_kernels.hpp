@@ -269,8 +269,7 @@ struct ReduceTNArgs {
   // optional bf16 column scale (row-major layout: out[q][n] *= colscale[n])
   const bf16_t *colscale;
 };
-__global__ void k_reduce_tn(const ReduceTNArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void reduce_tn_at(const ReduceTNArgs &a, int64_t i) {
   const int64_t count = (int64_t)a.RS * a.N;
   if (i >= count) return;
   const int q = (int)(i / a.N), n = (int)(i % a.N);
@@ -302,6 +301,9 @@ __global__ void k_reduce_tn(const ReduceTNArgs a) {
   if (a.colscale && !a.transposed) s *= bf16_to_f32(a.colscale[n]);
   const uint32_t w = pack_bf16x2(s, 0.f);
   *dst = (bf16_t)(w & 0xFFFFu);
+}
+__global__ void k_reduce_tn(const ReduceTNArgs a) {
+  reduce_tn_at(a, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -501,8 +503,7 @@ struct ReduceUArgs {
   bf16_t *outbf;
   const float *rowscale;   // optional: out32[t][.] *= rowscale[t] (not outbf)
 };
-__global__ void k_reduce_dual_u(const ReduceUArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void reduce_dual_u_at(const ReduceUArgs &a, int64_t i) {
   if (i >= (int64_t)a.T * a.RSout) return;
   const int t = (int)(i / a.RSout), qo = (int)(i % a.RSout);
   int q = qo, jb = 0, je = a.nb0;
@@ -533,18 +534,50 @@ __global__ void k_reduce_dual_u(const ReduceUArgs a) {
     a.outbf[i] = (bf16_t)(w & 0xFFFFu);
   }
 }
+__global__ void k_reduce_dual_u(const ReduceUArgs a) {
+  reduce_dual_u_at(a, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// Independent reductions in one launch (each a launch of its own costs more
+// than its few microseconds of work): the U-type jobs first, then the TN-type
+// jobs, job j on blocks [start[j], start[j + 1]).
+struct ReduceBatch {
+  ReduceUArgs u[2];
+  ReduceTNArgs v[2];
+  int nu, nv;
+  int64_t start[5];
+};
+__global__ void k_reduce_batch(const ReduceBatch b) {
+  int j = 0;
+  while (j + 1 < b.nu + b.nv && (int64_t)blockIdx.x >= b.start[j + 1]) ++j;
+  const int64_t i = ((int64_t)blockIdx.x - b.start[j]) * blockDim.x + threadIdx.x;
+  if (j < b.nu) reduce_dual_u_at(b.u[j], i);
+  else reduce_tn_at(b.v[j - b.nu], i);
+}
 
 // out[q][t] = bf16(in[t][qoff + q]) for q < nq, t < T; 0 elsewhere in
-// [RSout x ldp]
-__global__ void k_pack_pt(const float *in, int T, int ldin, int qoff, int nq, int RSout, int ldp,
-                          bf16_t *out) {
+// [RSout x ldp]; up to three such copies (same T, RSout, ldp) in one launch,
+// copy c on elements [c RSout ldp, (c + 1) RSout ldp)
+struct PackJob {
+  const float *in;
+  int ldin, qoff, nq;
+  bf16_t *out;
+};
+struct PackBatch {
+  PackJob j[3];
+  int n, T, RSout, ldp;
+};
+__global__ void k_pack_pt(const PackBatch b) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)RSout * ldp) return;
-  const int q = (int)(i / ldp), t = (int)(i % ldp);
+  const int64_t per = (int64_t)b.RSout * b.ldp;
+  if (i >= b.n * per) return;
+  const PackJob &jb = b.j[i / per];
+  const int64_t e = i % per;
+  const int q = (int)(e / b.ldp), t = (int)(e % b.ldp);
   float v = 0.f;
-  if (q < nq && t < T) v = in[(int64_t)t * ldin + qoff + q];
+  if (q < jb.nq && t < b.T) v = jb.in[(int64_t)t * jb.ldin + jb.qoff + q];
   const uint32_t w = pack_bf16x2(v, 0.f);
-  out[i] = (bf16_t)(w & 0xFFFFu);
+  jb.out[e] = (bf16_t)(w & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------------------
