@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 3
+#define LORA_ABI_VERSION 4
 #define LORA_MAX_RANK 128
 
 /* status codes */
@@ -162,6 +162,8 @@ typedef struct {
 #define LORA_OP_QKV_BWD    5
 #define LORA_OP_RMSNORM_MLP_FWD 6   /* lora_rmsnorm_swiglu_mlp_fwd */
 #define LORA_OP_RMSNORM_MLP_BWD 7   /* lora_rmsnorm_swiglu_mlp_bwd */
+#define LORA_OP_RMSNORM_QKV_FWD 8   /* lora_rmsnorm_qkv_fwd (lora_qkv_workspace_bytes) */
+#define LORA_OP_RMSNORM_QKV_BWD 9   /* lora_rmsnorm_qkv_bwd (lora_qkv_workspace_bytes) */
 /* or-ed into `op`: size of the minimal-memory strategy */
 #define LORA_WS_MINIMAL    0x100
 
@@ -307,7 +309,7 @@ int lora_rmsnorm_swiglu_mlp_bwd(int dtype, int64_t T, int64_t d, int64_t f, int6
 /*
  * out[i][j] = bf16_rne(W[i][j] * w[j]) (one fp32 multiply): a frozen RMSNorm
  * weight w [k] folded into a frozen base weight W [n x k] that reads the
- * norm's output, for lora_rmsnorm_swiglu_mlp_fwd/bwd.  bf16, k % 8 == 0;
+ * norm's output, for lora_rmsnorm_swiglu_mlp_fwd/bwd and lora_rmsnorm_qkv_fwd/bwd.  bf16, k % 8 == 0;
  * out may be W itself (in place).  No workspace.
  */
 int lora_fold_norm_weight(int dtype, int64_t n, int64_t k, const void *W, const void *norm_w,
@@ -395,9 +397,56 @@ int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64
                  uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes of lora_qkv_fwd / lora_qkv_bwd (op LORA_OP_QKV_FWD or
- * LORA_OP_QKV_BWD, optionally | LORA_WS_MINIMAL); 0 for invalid arguments. */
+ * LORA_OP_QKV_BWD, optionally | LORA_WS_MINIMAL) and of lora_rmsnorm_qkv_fwd
+ * / _bwd (LORA_OP_RMSNORM_QKV_FWD / _BWD, one strategy); 0 for invalid
+ * arguments or shapes the op does not take. */
 size_t lora_qkv_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t k, int64_t nq,
                                 int64_t nkv, int64_t r);
+
+/*
+ * RMSNorm fused into the q/k/v projections ([HF]-blog section 1: RMSNorm
+ * fused with the linear projections; [TB] 3.2 the RMSNorm kernel), forward:
+ *   rstd[t] = 1 / sqrt(sum_j X[t,j]^2 / k + eps),  Xn = X rstd diag(w),
+ *   (Q, K, V) = lora_qkv_fwd(Xn, ...)
+ * without forming Xn, as lora_rmsnorm_swiglu_mlp_fwd does for the MLP: the
+ * caller passes the three base weights folded with the frozen norm weight,
+ * Wp' = Wp diag(w) (lora_fold_norm_weight), the stacked GEMM reads the raw
+ * rows X and its store epilogue scales each output row by rstd; A diag(w)
+ * is formed per call.  X [T x k] raw rows, norm_w [k], rstd [T] fp32
+ * written for the backward.  bf16, dense weights, nq and nkv multiples of
+ * 256 and 3r <= 256 (LORA_ERR_UNSUPPORTED otherwise; lora_rmsnorm_fwd in
+ * front of lora_qkv_fwd takes every shape).  eps finite and >= 0.
+ * Workspace: lora_qkv_workspace_bytes(LORA_OP_RMSNORM_QKV_FWD, ...).
+ */
+int lora_rmsnorm_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                         float alpha, float eps, const void *X, const void *norm_w,
+                         const lora_weight *Wq, const void *Aq, const void *Bq,
+                         const lora_weight *Wk, const void *Ak, const void *Bk,
+                         const lora_weight *Wv, const void *Av, const void *Bv,
+                         void *Q, void *K, void *V, float *rstd,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of lora_rmsnorm_qkv_fwd from X, rstd and dQ, dK, dV (same folded
+ * weights): the adapter gradients of lora_qkv_bwd taken at Xn (formed from
+ * X with the rstd row and w column factors, Xn never stored), and dX the
+ * gradient with respect to the RAW input X,
+ *   dX = rstd gn - rstd^3 X (sum_j gn_j X_j) / k,   gn = dXn diag(w),
+ * where the folded projections' dX GEMM returns gn directly.  Unlike the
+ * MLP, no earlier step of this backward holds partial sums that give
+ * sum_j gn_j X_j, so gn goes through the workspace once and one row pass
+ * applies the norm's gradient.  LORA_FLAG_ACCUMULATE_DX adds dX to the
+ * caller's dX (the residual branch's gradient); dX NULL skips it.
+ * Workspace: lora_qkv_workspace_bytes(LORA_OP_RMSNORM_QKV_BWD, ...).
+ */
+int lora_rmsnorm_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                         float alpha, const void *X, const void *norm_w, const float *rstd,
+                         const lora_weight *Wq, const void *Aq, const void *Bq,
+                         const lora_weight *Wk, const void *Ak, const void *Bk,
+                         const lora_weight *Wv, const void *Av, const void *Bv,
+                         const void *dQ, const void *dK, const void *dV, void *dX,
+                         void *dAq, void *dBq, void *dAk, void *dBk, void *dAv, void *dBv,
+                         uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Merged weight out = W + sign * s * B A, s = alpha / r ([DD] 1.2: the

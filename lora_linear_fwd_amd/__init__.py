@@ -32,6 +32,7 @@ LORA_W_DENSE, LORA_W_Q4, LORA_W_Q4_DQ = 0, 1, 2
 LORA_FLAG_ACCUMULATE_DX = 1
 OP_LINEAR_FWD, OP_LINEAR_BWD, OP_MLP_FWD, OP_MLP_BWD, OP_QKV_FWD, OP_QKV_BWD = 0, 1, 2, 3, 4, 5
 OP_RMSNORM_MLP_FWD, OP_RMSNORM_MLP_BWD = 6, 7
+OP_RMSNORM_QKV_FWD, OP_RMSNORM_QKV_BWD = 8, 9
 LORA_WS_MINIMAL = 0x100
 STATUS = {0: "LORA_OK", 1: "LORA_ERR_NULL_POINTER", 2: "LORA_ERR_BAD_SHAPE",
           3: "LORA_ERR_UNSUPPORTED", 4: "LORA_ERR_WORKSPACE", 5: "LORA_ERR_MISALIGNED",
@@ -42,7 +43,8 @@ EXPORTS = ["lora_linear_fwd", "lora_linear_bwd", "lora_swiglu_mlp_fwd", "lora_sw
            "lora_merge", "lora_qkv_fwd", "lora_qkv_bwd",
            "lora_qkv_workspace_bytes", "lora_decode_weight", "lora_rmsnorm_fwd",
            "lora_rmsnorm_bwd", "lora_linear_bwd_noalloc", "lora_rmsnorm_swiglu_mlp_fwd",
-           "lora_rmsnorm_swiglu_mlp_bwd", "lora_fold_norm_weight"]
+           "lora_rmsnorm_swiglu_mlp_bwd", "lora_fold_norm_weight", "lora_rmsnorm_qkv_fwd",
+           "lora_rmsnorm_qkv_bwd"]
 TIMING_EXPORTS = ["lora_debug_time_next"]
 (KC_GATEUP_FWD, KC_DOWN_FWD, KC_DOWN_BWD, KC_GATEUP_BWD, KC_LINEAR_FWD, KC_LINEAR_DX,
  KC_QKV_FWD, KC_QKV_DX) = range(8)
@@ -112,6 +114,11 @@ def lib():
                                vp, vp, vp, vp, vp, sz, vp]
     L.lora_qkv_bwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, W, vp, vp, W, vp, vp, W, vp,
                                vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, sz, vp]
+    L.lora_rmsnorm_qkv_fwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, f32, vp, vp, W, vp, vp,
+                                       W, vp, vp, W, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lora_rmsnorm_qkv_bwd.argtypes = [i32, i64, i64, i64, i64, i64, f32, vp, vp, vp, W, vp, vp,
+                                       W, vp, vp, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, u32, vp, sz, vp]
     L.lora_qkv_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i64, i64, i64]
     L.lora_qkv_workspace_bytes.restype = sz
     L.lora_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i64, i64]
@@ -354,7 +361,7 @@ def _workspace(op, dt, wfmt, dims, device, workspace=None, minimal=False, stream
               "workspace must be a contiguous tensor on the inputs' device")
         return _ptr(workspace), workspace.numel() * workspace.element_size()
     flag = LORA_WS_MINIMAL if minimal else 0
-    if op in (OP_QKV_FWD, OP_QKV_BWD):
+    if op in (OP_QKV_FWD, OP_QKV_BWD, OP_RMSNORM_QKV_FWD, OP_RMSNORM_QKV_BWD):
         nbytes = int(lib().lora_qkv_workspace_bytes(op | flag, dt, wfmt, *dims))
     else:
         nbytes = workspace_bytes(op | flag, dt, wfmt, *dims)
@@ -748,6 +755,87 @@ def lora_qkv_bwd(X, W: Dict[str, Weight], A, B, alpha: float, dY: Dict[str, obje
         _ptr(dY["q"]), _ptr(dY["k"]), _ptr(dY["v"]), _ptr(o["dX"]),
         _ptr(o["dA_q"]), _ptr(o["dB_q"]), _ptr(o["dA_k"]), _ptr(o["dB_k"]),
         _ptr(o["dA_v"]), _ptr(o["dB_v"]), flags, wsp, wsn, _stream(stream)), "lora_qkv_bwd")
+    return o
+
+
+def lora_rmsnorm_qkv_fwd(X, norm_w, eps: float, W: Dict[str, Weight], A, B, alpha: float,
+                         out: Optional[dict] = None, rstd=None, workspace=None, stream=None):
+    """RMSNorm of the raw rows X fused into the q/k/v LoRA projections.
+    W["q"], W["k"], W["v"] must be folded with the norm weight
+    (lora_fold_norm_weight).  Returns (dict q, k, v; rstd)."""
+    torch = _torch()
+    where = "lora_rmsnorm_qkv_fwd"
+    T, k, nq, nkv, r = _qkv_check(X, W, A, B, where)
+    _tensor(norm_w, "norm_w", (k,), X.dtype, X.device, where)
+    o = dict(out or {})
+    for p, n in (("q", nq), ("k", nkv), ("v", nkv)):
+        if o.get(p) is not None:
+            _tensor(o[p], p, (T, n), X.dtype, X.device, where)
+    if rstd is not None:
+        _tensor(rstd, "rstd", (T,), torch.float32, X.device, where)
+    _on_gpu(X, where)
+    dt = _dtype_code(X)
+    for p, n in (("q", nq), ("k", nkv), ("v", nkv)):
+        if o.get(p) is None:
+            o[p] = torch.empty((T, n), dtype=X.dtype, device=X.device)
+    rstd = torch.empty((T,), dtype=torch.float32, device=X.device) if rstd is None else rstd
+    wsp, wsn = _workspace(OP_RMSNORM_QKV_FWD, dt, _wfmt(W["q"]), (T, k, nq, nkv, r), X.device,
+                          workspace, False, stream)
+    ws_ = [_wstruct(W[p]) for p in ("q", "k", "v")]
+    _check(lib().lora_rmsnorm_qkv_fwd(
+        dt, T, k, nq, nkv, r, float(alpha), float(eps), _ptr(X), _ptr(norm_w),
+        ctypes.byref(ws_[0]), _ptr(A["q"]), _ptr(B["q"]),
+        ctypes.byref(ws_[1]), _ptr(A["k"]), _ptr(B["k"]),
+        ctypes.byref(ws_[2]), _ptr(A["v"]), _ptr(B["v"]),
+        _ptr(o["q"]), _ptr(o["k"]), _ptr(o["v"]), _ptr(rstd), wsp, wsn, _stream(stream)), where)
+    return o, rstd
+
+
+def lora_rmsnorm_qkv_bwd(X, norm_w, rstd, W: Dict[str, Weight], A, B, alpha: float,
+                         dY: Dict[str, object], need_dx=True, accumulate_dx=False,
+                         out: Optional[dict] = None, workspace=None, stream=None):
+    """Backward of lora_rmsnorm_qkv_fwd: dict with dX (gradient of the raw
+    rows; added to out["dX"] when accumulate_dx) and dA_p / dB_p."""
+    torch = _torch()
+    where = "lora_rmsnorm_qkv_bwd"
+    T, k, nq, nkv, r = _qkv_check(X, W, A, B, where)
+    _tensor(norm_w, "norm_w", (k,), X.dtype, X.device, where)
+    _tensor(rstd, "rstd", (T,), torch.float32, X.device, where)
+    for p, n in (("q", nq), ("k", nkv), ("v", nkv)):
+        _tensor(dY[p], "d" + p.upper(), (T, n), X.dtype, X.device, where)
+    o = dict(out or {})
+    if need_dx and o.get("dX") is not None:
+        _tensor(o["dX"], "dX", (T, k), X.dtype, X.device, where)
+    _need(not accumulate_dx or (need_dx and o.get("dX") is not None),
+          f"{where}: accumulate_dx needs out['dX']")
+    for p, n in (("q", nq), ("k", nkv), ("v", nkv)):
+        if o.get("dA_" + p) is not None:
+            _tensor(o["dA_" + p], "dA_" + p, (r, k), X.dtype, X.device, where)
+        if o.get("dB_" + p) is not None:
+            _tensor(o["dB_" + p], "dB_" + p, (n, r), X.dtype, X.device, where)
+    _on_gpu(X, where)
+    dt = _dtype_code(X)
+    if need_dx and o.get("dX") is None:
+        o["dX"] = torch.empty((T, k), dtype=X.dtype, device=X.device)
+    if not need_dx:
+        o["dX"] = None
+    for p in ("q", "k", "v"):
+        if o.get("dA_" + p) is None:
+            o["dA_" + p] = torch.empty_like(A[p])
+        if o.get("dB_" + p) is None:
+            o["dB_" + p] = torch.empty_like(B[p])
+    wsp, wsn = _workspace(OP_RMSNORM_QKV_BWD, dt, _wfmt(W["q"]), (T, k, nq, nkv, r), X.device,
+                          workspace, False, stream)
+    ws_ = [_wstruct(W[p]) for p in ("q", "k", "v")]
+    flags = LORA_FLAG_ACCUMULATE_DX if accumulate_dx else 0
+    _check(lib().lora_rmsnorm_qkv_bwd(
+        dt, T, k, nq, nkv, r, float(alpha), _ptr(X), _ptr(norm_w), _ptr(rstd),
+        ctypes.byref(ws_[0]), _ptr(A["q"]), _ptr(B["q"]),
+        ctypes.byref(ws_[1]), _ptr(A["k"]), _ptr(B["k"]),
+        ctypes.byref(ws_[2]), _ptr(A["v"]), _ptr(B["v"]),
+        _ptr(dY["q"]), _ptr(dY["k"]), _ptr(dY["v"]), _ptr(o["dX"]),
+        _ptr(o["dA_q"]), _ptr(o["dB_q"]), _ptr(o["dA_k"]), _ptr(o["dB_k"]),
+        _ptr(o["dA_v"]), _ptr(o["dB_v"]), flags, wsp, wsn, _stream(stream)), where)
     return o
 
 

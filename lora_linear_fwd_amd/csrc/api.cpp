@@ -205,6 +205,11 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, 
 // fused q/k/v projections: N = nq + 2 nkv output columns, rank products of
 // width RS3 = 3r rounded up to 16 (q, k, v blocks stacked)
 inline bool qkv_rank_ok(int64_t r) { return rs_of(3 * r) <= 256; }
+// shapes the stacked q/k/v GEMM takes: every tile's columns in one projection
+inline bool qkv_shapes_ok(int64_t k, int64_t nq, int64_t nkv, int64_t r) {
+  return r > 0 && r <= LORA_MAX_RANK && qkv_rank_ok(r) && k > 0 && nq > 0 && nkv > 0 &&
+         nq % BN == 0 && nkv % BN == 0 && k <= kMaxFeatures && nq + 2 * nkv <= kMaxFeatures;
+}
 struct QkvFwdPlan { size_t side, epi, hpart, hbf, wbuf, total; };
 QkvFwdPlan plan_qkv_fwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r, bool wcopy) {
   Bump b; QkvFwdPlan p{};
@@ -218,12 +223,16 @@ QkvFwdPlan plan_qkv_fwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r
   p.total = b.cur;
   return p;
 }
-struct QkvBwdPlan { size_t dyc, side_nn, epi_nn, side_nt, g32, gbf, h32, ntpart, tnpart, wbuf, total; };
-QkvBwdPlan plan_qkv_bwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r) {
+struct QkvBwdPlan { size_t dyc, side_nn, epi_nn, side_nt, g32, gbf, h32, ntpart, tnpart, wbuf, gn, total; };
+// norm: an RMSNorm folded into the projections (lora_rmsnorm_qkv_bwd) adds a
+// [T x k] bf16 buffer for the projections' input gradient
+QkvBwdPlan plan_qkv_bwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                        bool norm = false) {
   Bump b; QkvBwdPlan p{};
   const int64_t N = nq + 2 * nkv;
   const int RS3 = rs_of(3 * r);
   p.wbuf = b.take((size_t)k * N * 2);
+  if (norm) p.gn = b.take((size_t)T * k * 2);
   p.dyc = b.take((size_t)T * N * 2);
   p.side_nn = b.take((size_t)RS3 * N * 2);
   p.epi_nn = b.take((size_t)k * RS3 * 2);
@@ -1273,6 +1282,13 @@ size_t lora_qkv_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t 
   if (op & ~(0xFF | LORA_WS_MINIMAL)) return 0;
   const bool minimal = (op & LORA_WS_MINIMAL) != 0;
   const int base = op & 0xFF;
+  if (base == LORA_OP_RMSNORM_QKV_FWD || base == LORA_OP_RMSNORM_QKV_BWD) {
+    // one strategy (bf16, dense weights, the stacked GEMM's shapes)
+    if (dtype != LORA_BF16 || wfmt != LORA_W_DENSE || !qkv_shapes_ok(k, nq, nkv, r)) return 0;
+    if (T < 0 || T > ((int64_t)1 << 30)) return 0;
+    return base == LORA_OP_RMSNORM_QKV_FWD ? plan_qkv_fwd(T, k, nq, nkv, r, false).total
+                                           : plan_qkv_bwd(T, k, nq, nkv, r, true).total;
+  }
   if (base != LORA_OP_QKV_FWD && base != LORA_OP_QKV_BWD) return 0;
   if (wfmt != LORA_W_DENSE && wfmt != LORA_W_Q4 && wfmt != LORA_W_Q4_DQ) return 0;
   if (T < 0 || k <= 0 || nq <= 0 || nkv <= 0 || r <= 0 || r > LORA_MAX_RANK) return 0;
@@ -1291,6 +1307,58 @@ size_t lora_qkv_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t 
       need = std::max(need, plan_qkv_bwd(T, k, nq, nkv, r).total);
   }
   return need;
+}
+
+// The stacked q/k/v forward (bf16, nq and nkv multiples of the tile width,
+// 3r <= 256): one rank-3r pass over X and one GEMM over [Wq; Wk; Wv] whose
+// store epilogue writes Q, K, V.  With a folded norm the GEMM reads the raw
+// rows and scales each output row by rstd.
+static int qkv_fwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r, float alpha,
+                         const void *X, WeightView wq, WeightView wk, WeightView wv,
+                         const void *Aq, const void *Bq, const void *Ak, const void *Bk,
+                         const void *Av, const void *Bv, void *Q, void *K, void *V, void *ws,
+                         hipStream_t st, const NormFuse *nf) {
+  const int64_t N = nq + 2 * nkv;
+  const int RS3 = rs_of(3 * r);
+  const float s = alpha / (float)r;
+  char *w = (char *)ws;
+  const QkvFwdPlan pl = plan_qkv_fwd(T, k, nq, nkv, r, wq.q4);
+  bf16_t *side = (bf16_t *)(w + pl.side), *epi = (bf16_t *)(w + pl.epi);
+  bf16_t *hbf = (bf16_t *)(w + pl.hbf);
+  if (wq.q4) {   // decode the three weights once, stacked [Wq; Wk; Wv]
+    bf16_t *wb = (bf16_t *)(w + pl.wbuf);
+    LORA_TRY(decode_w(wb, wq, nq, k, st));
+    LORA_TRY(decode_w(wb + nq * k, wk, nkv, k, st));
+    LORA_TRY(decode_w(wb + (nq + nkv) * k, wv, nkv, k, st));
+    wq = dense_view(wb);
+    wk = dense_view(wb + nq * k);
+    wv = dense_view(wb + (nq + nkv) * k);
+  }
+  Prep prep;
+  // [Aq; Ak; Av], times diag(w) under a folded norm
+  prep.side(side, RS3, k, Aq, Ak, r, k, 0, Av, k, nf ? nf->w : nullptr);
+  prep.epi(epi, N, RS3, Bq, Bk, r, nq, 0, Bv, nq + nkv);            // blockdiag(Bq, Bk, Bv)
+  LORA_TRY(prep.launch(st));
+  const bf16_t *Xb = (const bf16_t *)X;
+  if (nf) {   // the rows' rstd only: the normalised rows are never formed
+    hipLaunchKernelGGL(k_rmsnorm_fwd<false>, dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, X,
+                       (const void *)nf->w, nf->eps, (int)T, (int)k, (void *)nullptr, nf->rstd);
+    HIP_TRY(hipGetLastError());
+  }
+  LORA_TRY(skinny_nt(RS3, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side,
+                     (float *)(w + pl.hpart), nullptr, hbf, s, st));
+  GemmArgs a = gemm_base();
+  a.M = (int)T; a.N = (int)N; a.K = (int)k; a.ksplit = (int)k;
+  a.A0 = a.A1 = Xb; a.lda = k;
+  a.B0 = wq.w; a.B1 = wk.w; a.B2 = wv.w; a.ldb = k;
+  a.nseg1 = (int)nq; a.nseg2 = (int)(nq + nkv);
+  a.rs = RS3; a.epi = epi; a.hglob = hbf;
+  if (nf) a.rowscale = nf->rstd;
+  a.C = (bf16_t *)Q; a.ldc = nq;
+  a.C1 = (bf16_t *)K; a.ldc1 = nkv;
+  a.C2 = (bf16_t *)V; a.ldc2 = nkv;
+  a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)(N / BN);
+  return run_gemm(KC_QKV_FWD, false, false, EPI_STORE, a, st);
 }
 
 int lora_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
@@ -1322,40 +1390,86 @@ int lora_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64
     LORA_TRY(lora_linear_fwd(dtype, T, k, nkv, r, alpha, X, Wk, Ak, Bk, K, ws, ws_bytes, stream));
     return lora_linear_fwd(dtype, T, k, nkv, r, alpha, X, Wv, Av, Bv, V, ws, ws_bytes, stream);
   }
+  return qkv_fwd_fused(T, k, nq, nkv, r, alpha, X, wq, wk, wv, Aq, Bq, Ak, Bk, Av, Bv, Q, K, V, ws,
+                       st, nullptr);
+}
+
+// The stacked q/k/v backward (bf16, fast workspace, 3r <= 256): [dQ | dK | dV]
+// packed once, one rank-3r pass for G, one dX GEMM with K = nq + 2 nkv over
+// the transposed stacked weights, one pass for H and the two adapter-gradient
+// passes.  With a folded norm the adapters' A become A diag(w), the rank-r
+// products carry rstd, and dX is the raw rows' gradient.
+static int qkv_bwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r, float alpha,
+                         const void *X, WeightView wq, WeightView wk, WeightView wv,
+                         const void *Aq, const void *Bq, const void *Ak, const void *Bk,
+                         const void *Av, const void *Bv, const void *dQ, const void *dK,
+                         const void *dV, void *dX, void *dAq, void *dBq, void *dAk, void *dBk,
+                         void *dAv, void *dBv, bool acc, void *ws, hipStream_t st,
+                         const NormFuse *nf) {
   const int64_t N = nq + 2 * nkv;
   const int RS3 = rs_of(3 * r);
   const float s = alpha / (float)r;
   char *w = (char *)ws;
-  const QkvFwdPlan pl = plan_qkv_fwd(T, k, nq, nkv, r, wq.q4);
-  bf16_t *side = (bf16_t *)(w + pl.side), *epi = (bf16_t *)(w + pl.epi);
-  bf16_t *hbf = (bf16_t *)(w + pl.hbf);
-  if (wq.q4) {   // decode the three weights once, stacked [Wq; Wk; Wv]
-    bf16_t *wb = (bf16_t *)(w + pl.wbuf);
-    LORA_TRY(decode_w(wb, wq, nq, k, st));
-    LORA_TRY(decode_w(wb + nq * k, wk, nkv, k, st));
-    LORA_TRY(decode_w(wb + (nq + nkv) * k, wv, nkv, k, st));
-    wq = dense_view(wb);
-    wk = dense_view(wb + nq * k);
-    wv = dense_view(wb + (nq + nkv) * k);
-  }
-  Prep prep;
-  prep.side(side, RS3, k, Aq, Ak, r, k, 0, Av, k);                  // [Aq; Ak; Av]
-  prep.epi(epi, N, RS3, Bq, Bk, r, nq, 0, Bv, nq + nkv);            // blockdiag(Bq, Bk, Bv)
-  LORA_TRY(prep.launch(st));
+  const QkvBwdPlan pl = plan_qkv_bwd(T, k, nq, nkv, r, nf != nullptr);
+  const bf16_t *nw = nf ? nf->w : nullptr;
+  const float *rstd = nf ? nf->rstd : nullptr;
+  bf16_t *dyc = (bf16_t *)(w + pl.dyc), *wt = (bf16_t *)(w + pl.wbuf);
+  bf16_t *side_nn = (bf16_t *)(w + pl.side_nn), *epi_nn = (bf16_t *)(w + pl.epi_nn);
+  bf16_t *side_nt = (bf16_t *)(w + pl.side_nt), *gbf = (bf16_t *)(w + pl.gbf);
+  float *g32 = (float *)(w + pl.g32), *h32 = (float *)(w + pl.h32);
+  float *ntpart = (float *)(w + pl.ntpart), *tnpart = (float *)(w + pl.tnpart);
   const bf16_t *Xb = (const bf16_t *)X;
-  LORA_TRY(skinny_nt(RS3, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side,
-                     (float *)(w + pl.hpart), nullptr, hbf, s, st));
-  GemmArgs a = gemm_base();
-  a.M = (int)T; a.N = (int)N; a.K = (int)k; a.ksplit = (int)k;
-  a.A0 = a.A1 = Xb; a.lda = k;
-  a.B0 = wq.w; a.B1 = wk.w; a.B2 = wv.w; a.ldb = k;
-  a.nseg1 = (int)nq; a.nseg2 = (int)(nq + nkv);
-  a.rs = RS3; a.epi = epi; a.hglob = hbf;
-  a.C = (bf16_t *)Q; a.ldc = nq;
-  a.C1 = (bf16_t *)K; a.ldc1 = nkv;
-  a.C2 = (bf16_t *)V; a.ldc2 = nkv;
-  a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)(N / BN);
-  return run_gemm(KC_QKV_FWD, false, false, EPI_STORE, a, st);
+  Prep prep;
+  prep.side(side_nn, RS3, N, Bq, Bk, r, nq, 1, Bv, nq + nkv);       // blockdiag(Bq,Bk,Bv)^T
+  // [Aq; Ak; Av]^T and [Aq; Ak; Av], times diag(w) under a folded norm
+  prep.epi(epi_nn, k, RS3, Aq, Ak, r, k, 1, Av, k, nw);
+  prep.side(side_nt, RS3, k, Aq, Ak, r, k, 0, Av, k, nw);
+  LORA_TRY(prep.launch(st));
+  if (T > 0) {
+    // [dQ | dK | dV] as one [T x N] operand
+    hipLaunchKernelGGL(k_concat3, dim3(blocks_for(T * (N / 8))), dim3(256), 0, st,
+                       (const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV, (int)nq,
+                       (int)nkv, (int)nkv, T, dyc);
+    HIP_TRY(hipGetLastError());
+    // G = [dQ Bq | dK Bk | dV Bv] (fp32 for dA, rows times rstd under a
+    // folded norm; s G in bf16 for the dX epilogue)
+    LORA_TRY(skinny_nt(RS3, false, T, N, dyc, dyc, N, N, nullptr, nullptr, side_nn, ntpart, g32,
+                       gbf, s, st, rstd));
+    if (dX) {
+      // dX (+)= [dQ | dK | dV] [Wq; Wk; Wv] + s G [Aq; Ak; Av]: one GEMM, K = N
+      LORA_TRY(transpose_w(wt, N, wq, nq, k, st));
+      LORA_TRY(transpose_w(wt + nq, N, wk, nkv, k, st));
+      LORA_TRY(transpose_w(wt + nq + nkv, N, wv, nkv, k, st));
+      GemmArgs a = gemm_base();
+      a.M = (int)T; a.N = (int)k; a.K = (int)N; a.ksplit = (int)N;
+      a.A0 = a.A1 = dyc; a.lda = N;
+      const WeightView tv = dense_view(wt);
+      set_b(a, tv, tv); a.ldb = N;
+      a.rs = RS3; a.epi = epi_nn; a.hglob = gbf;
+      // folded norm: the GEMM gives gn, the gradient with respect to X rstd
+      bf16_t *gn = nf ? (bf16_t *)(w + pl.gn) : (bf16_t *)dX;
+      a.accumulate = !nf && acc; a.C = gn; a.ldc = k;
+      a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
+      LORA_TRY(run_gemm(KC_QKV_DX, false, false, EPI_STORE, a, st));
+      if (nf) {   // dX (+)= rstd gn - rstd^3 X (sum_j gn_j X_j) / k (unit norm weight)
+        hipLaunchKernelGGL(k_rmsnorm_bwd<false>, dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, X,
+                           (const void *)nullptr, rstd, (const void *)gn, (int)T, (int)k, dX,
+                           acc ? 1 : 0);
+        HIP_TRY(hipGetLastError());
+      }
+    }
+    // H = X [Aq; Ak; Av]^T (folded norm: rstd X [Aq; Ak; Av]^T diag(w), the
+    // normalised rows' product)
+    LORA_TRY(skinny_nt(RS3, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,
+                       nullptr, 1.f, st, rstd));
+  }
+  // [dAq; dAk; dAv] = s G^T X ;  dBq = s dQ^T H_q, dBk = s dK^T H_k, dBv = s dV^T H_v
+  //   (folded norm: G rows scaled by rstd, the result's columns by w)
+  LORA_TRY(skinny_tn(RS3, false, T, k, g32, Xb, Xb, k, k, nullptr, nullptr, tnpart, r, s, 0,
+                     (bf16_t *)dAq, (bf16_t *)dAk, k, st, (bf16_t *)dAv, 0, nw));
+  LORA_TRY(skinny_tn(RS3, false, T, N, h32, dyc, dyc, N, N, nullptr, nullptr, tnpart, r, s, 1,
+                     (bf16_t *)dBq, (bf16_t *)dBk, nq, st, (bf16_t *)dBv, nq + nkv));
+  return LORA_OK;
 }
 
 int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
@@ -1392,57 +1506,71 @@ int lora_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64
     return lora_linear_bwd(dtype, T, k, nkv, r, alpha, X, Wv, Av, Bv, dV, dX, dAv, dBv,
                            LORA_FLAG_ACCUMULATE_DX, ws, ws_bytes, stream);
   }
-  const int64_t N = nq + 2 * nkv;
-  const int RS3 = rs_of(3 * r);
-  const float s = alpha / (float)r;
-  const bool acc = (flags & LORA_FLAG_ACCUMULATE_DX) != 0;
-  char *w = (char *)ws;
-  const QkvBwdPlan pl = plan_qkv_bwd(T, k, nq, nkv, r);
-  bf16_t *dyc = (bf16_t *)(w + pl.dyc), *wt = (bf16_t *)(w + pl.wbuf);
-  bf16_t *side_nn = (bf16_t *)(w + pl.side_nn), *epi_nn = (bf16_t *)(w + pl.epi_nn);
-  bf16_t *side_nt = (bf16_t *)(w + pl.side_nt), *gbf = (bf16_t *)(w + pl.gbf);
-  float *g32 = (float *)(w + pl.g32), *h32 = (float *)(w + pl.h32);
-  float *ntpart = (float *)(w + pl.ntpart), *tnpart = (float *)(w + pl.tnpart);
-  const bf16_t *Xb = (const bf16_t *)X;
-  Prep prep;
-  prep.side(side_nn, RS3, N, Bq, Bk, r, nq, 1, Bv, nq + nkv);       // blockdiag(Bq,Bk,Bv)^T
-  prep.epi(epi_nn, k, RS3, Aq, Ak, r, k, 1, Av, k);                 // [Aq; Ak; Av]^T
-  prep.side(side_nt, RS3, k, Aq, Ak, r, k, 0, Av, k);               // [Aq; Ak; Av]
-  LORA_TRY(prep.launch(st));
-  if (T > 0) {
-    // [dQ | dK | dV] as one [T x N] operand
-    hipLaunchKernelGGL(k_concat3, dim3(blocks_for(T * (N / 8))), dim3(256), 0, st,
-                       (const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV, (int)nq,
-                       (int)nkv, (int)nkv, T, dyc);
-    HIP_TRY(hipGetLastError());
-    // G = [dQ Bq | dK Bk | dV Bv] (fp32 for dA, s G in bf16 for the dX epilogue)
-    LORA_TRY(skinny_nt(RS3, false, T, N, dyc, dyc, N, N, nullptr, nullptr, side_nn, ntpart, g32,
-                       gbf, s, st));
-    if (dX) {
-      // dX (+)= [dQ | dK | dV] [Wq; Wk; Wv] + s G [Aq; Ak; Av]: one GEMM, K = N
-      LORA_TRY(transpose_w(wt, N, wq, nq, k, st));
-      LORA_TRY(transpose_w(wt + nq, N, wk, nkv, k, st));
-      LORA_TRY(transpose_w(wt + nq + nkv, N, wv, nkv, k, st));
-      GemmArgs a = gemm_base();
-      a.M = (int)T; a.N = (int)k; a.K = (int)N; a.ksplit = (int)N;
-      a.A0 = a.A1 = dyc; a.lda = N;
-      const WeightView tv = dense_view(wt);
-      set_b(a, tv, tv); a.ldb = N;
-      a.rs = RS3; a.epi = epi_nn; a.hglob = gbf;
-      a.accumulate = acc; a.C = (bf16_t *)dX; a.ldc = k;
-      a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(k, BN);
-      LORA_TRY(run_gemm(KC_QKV_DX, false, false, EPI_STORE, a, st));
-    }
-    // H = X [Aq; Ak; Av]^T
-    LORA_TRY(skinny_nt(RS3, false, T, k, Xb, Xb, k, k, nullptr, nullptr, side_nt, ntpart, h32,
-                       nullptr, 1.f, st));
-  }
-  // [dAq; dAk; dAv] = s G^T X ;  dBq = s dQ^T H_q, dBk = s dK^T H_k, dBv = s dV^T H_v
-  LORA_TRY(skinny_tn(RS3, false, T, k, g32, Xb, Xb, k, k, nullptr, nullptr, tnpart, r, s, 0,
-                     (bf16_t *)dAq, (bf16_t *)dAk, k, st, (bf16_t *)dAv, 0));
-  LORA_TRY(skinny_tn(RS3, false, T, N, h32, dyc, dyc, N, N, nullptr, nullptr, tnpart, r, s, 1,
-                     (bf16_t *)dBq, (bf16_t *)dBk, nq, st, (bf16_t *)dBv, nq + nkv));
+  return qkv_bwd_fused(T, k, nq, nkv, r, alpha, X, wq, wk, wv, Aq, Bq, Ak, Bk, Av, Bv, dQ, dK, dV,
+                       dX, dAq, dBq, dAk, dBk, dAv, dBv, (flags & LORA_FLAG_ACCUMULATE_DX) != 0,
+                       ws, st, nullptr);
+}
+
+// checks shared by the norm-fused q/k/v entry points: bf16, dense weights and
+// the shapes of the stacked GEMM (the projections one by one cannot take a
+// folded norm: their per-call rank products carry no rstd)
+static int check_qkv_norm(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                          const lora_weight *Wq, const lora_weight *Wk, const lora_weight *Wv,
+                          WeightView &wq, WeightView &wk, WeightView &wv) {
+  LORA_TRY(check_dims(dtype, T, k, nq, r));
+  LORA_TRY(check_dims(dtype, T, k, nkv, r));
+  LORA_TRY(check_weight(Wq, dtype, k, wq));
+  LORA_TRY(check_weight(Wk, dtype, k, wk));
+  LORA_TRY(check_weight(Wv, dtype, k, wv));
+  if (dtype != LORA_BF16 || wq.q4 || wk.q4 || wv.q4) return LORA_ERR_UNSUPPORTED;
+  if (!qkv_shapes_ok(k, nq, nkv, r)) return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
+}
+
+int lora_rmsnorm_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                         float alpha, float eps, const void *X, const void *norm_w,
+                         const lora_weight *Wq, const void *Aq, const void *Bq,
+                         const lora_weight *Wk, const void *Ak, const void *Bk,
+                         const lora_weight *Wv, const void *Av, const void *Bv, void *Q, void *K,
+                         void *V, float *rstd, void *ws, size_t ws_bytes, void *stream) {
+  WeightView wq, wk, wv;
+  LORA_TRY(check_qkv_norm(dtype, T, k, nq, nkv, r, Wq, Wk, Wv, wq, wk, wv));
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return LORA_ERR_UNSUPPORTED;
+  LORA_TRY(check_ptrs({Aq, Bq, Ak, Bk, Av, Bv, norm_w}));
+  LORA_TRY(check_tok_ptrs(T, {X, Q, K, V, rstd}));
+  const size_t need = lora_qkv_workspace_bytes(LORA_OP_RMSNORM_QKV_FWD, dtype, LORA_W_DENSE, T, k,
+                                               nq, nkv, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  if (T == 0) return LORA_OK;
+  const NormFuse nf{(const bf16_t *)norm_w, eps, rstd, false};
+  return qkv_fwd_fused(T, k, nq, nkv, r, alpha, X, wq, wk, wv, Aq, Bq, Ak, Bk, Av, Bv, Q, K, V, ws,
+                       (hipStream_t)stream, &nf);
+}
+
+int lora_rmsnorm_qkv_bwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
+                         float alpha, const void *X, const void *norm_w, const float *rstd,
+                         const lora_weight *Wq, const void *Aq, const void *Bq,
+                         const lora_weight *Wk, const void *Ak, const void *Bk,
+                         const lora_weight *Wv, const void *Av, const void *Bv, const void *dQ,
+                         const void *dK, const void *dV, void *dX, void *dAq, void *dBq,
+                         void *dAk, void *dBk, void *dAv, void *dBv, uint32_t flags, void *ws,
+                         size_t ws_bytes, void *stream) {
+  WeightView wq, wk, wv;
+  LORA_TRY(check_qkv_norm(dtype, T, k, nq, nkv, r, Wq, Wk, Wv, wq, wk, wv));
+  LORA_TRY(check_ptrs({Aq, Bq, Ak, Bk, Av, Bv, dAq, dBq, dAk, dBk, dAv, dBv, norm_w}));
+  LORA_TRY(check_tok_ptrs(T, {X, dQ, dK, dV, rstd}));
+  if (dX && !aligned16(dX)) return LORA_ERR_MISALIGNED;
+  if (flags & ~(uint32_t)LORA_FLAG_ACCUMULATE_DX) return LORA_ERR_UNSUPPORTED;
+  const size_t need = lora_qkv_workspace_bytes(LORA_OP_RMSNORM_QKV_BWD, dtype, LORA_W_DENSE, T, k,
+                                               nq, nkv, r);
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (need && (!ws || !aligned16(ws))) return ws ? LORA_ERR_MISALIGNED : LORA_ERR_NULL_POINTER;
+  const NormFuse nf{(const bf16_t *)norm_w, 0.f, const_cast<float *>(rstd),
+                    (flags & LORA_FLAG_ACCUMULATE_DX) != 0};
+  return qkv_bwd_fused(T, k, nq, nkv, r, alpha, X, wq, wk, wv, Aq, Bq, Ak, Bk, Av, Bv, dQ, dK, dV,
+                       dX, dAq, dBq, dAk, dBk, dAv, dBv, nf.accumulate, ws, (hipStream_t)stream,
+                       &nf);
 }
 
 int lora_merge(int dtype, int64_t n, int64_t k, int64_t r, float alpha, int sign,

@@ -106,7 +106,8 @@ struct GemmArgs {
   bf16_t *C1, *C2;
   int64_t ldc1, ldc2;
   // RMSNorm folded into the projections that follow it (eight-wave kernel):
-  //   rowscale  SwiGLU forward: e, g of row m are scaled by rowscale[m]
+  //   rowscale  SwiGLU forward: e, g of row m are scaled by rowscale[m];
+  //             store: row m of C is (before any accumulation)
   //             (rstd; the GEMM reads the raw rows and weights W diag(w))
   //   cpart     SwiGLU backward: cpart[(tile column * 4 + 64-column block) *
   //             M + m] = sum over the block's columns of de e + dg g

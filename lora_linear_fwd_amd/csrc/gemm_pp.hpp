@@ -785,6 +785,11 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
                         __uint_as_float(a1[2]), __uint_as_float(a1[3])};
           if constexpr (EPI == EPI_STORE) {
             if (!valid) continue;
+            if (p.rowscale) {   // folded RMSNorm: the row's rstd
+              const float rs = p.rowscale[m];
+  #pragma unroll
+              for (int t = 0; t < 8; ++t) v[t] *= rs;
+            }
             if (p.nrm_x) {   // RMSNorm input gradient from the folded projections' output
               const u32x4 xv = gload16(p.nrm_x + (int64_t)m * N + n);
               const float rs = p.nrm_rs[m], kk = p.nrm_kk[m];

@@ -102,7 +102,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const void *Xv, const void 
   }
 }
 
-// dX = (or +=, accumulate != 0) the input gradient of k_rmsnorm_fwd
+// dX = (or +=, accumulate != 0) the input gradient of k_rmsnorm_fwd; wv
+// NULL stands for a unit weight (dY is then already the gradient with
+// respect to X rstd diag(w), as a folded projection returns it)
 template <bool F32>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const void *Xv, const void *wv,
                                                      const float *rstd, const void *dYv, int T,
@@ -117,11 +119,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const void *Xv, const void 
     const float *dy = reinterpret_cast<const float *>(dYv) + (int64_t)row * d;
     float *dx = reinterpret_cast<float *>(dXv) + (int64_t)row * d;
     float dot = 0.f;
-    for (int j = lane; j < d; j += 64) dot = fmaf(dy[j] * w[j], x[j], dot);
+    for (int j = lane; j < d; j += 64) dot = fmaf(dy[j] * (w ? w[j] : 1.f), x[j], dot);
     dot = wave_sum(dot);
     const float cx = r * r * r * dot / (float)d;   // coefficient of x_i
     for (int j = lane; j < d; j += 64) {
-      const float v = r * (dy[j] * w[j]) - cx * x[j];
+      const float v = r * (dy[j] * (w ? w[j] : 1.f)) - cx * x[j];
       dx[j] = accumulate ? dx[j] + v : v;
     }
   } else {
@@ -135,10 +137,18 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const void *Xv, const void 
     const bool resident = nch <= 64 * RC;
     u32x4 xr[RC], gr[RC];
     float dot = 0.f;
+    auto wload = [&](int c, float *wv8) {
+      if (w) {
+        unpack8(gload16(w + 8 * c), wv8);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv8[i] = 1.f;
+      }
+    };
     auto add_dot = [&](int c, const u32x4 &xc, const u32x4 &gc) {
       float xv[8], wv8[8], gv[8];
       unpack8(xc, xv);
-      unpack8(gload16(w + 8 * c), wv8);
+      wload(c, wv8);
       unpack8(gc, gv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) dot = fmaf(gv[i] * wv8[i], xv[i], dot);
@@ -161,7 +171,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const void *Xv, const void 
     auto out = [&](int c, const u32x4 &xc, const u32x4 &gc) {
       float xv[8], wv8[8], gv[8], o8[8];
       unpack8(xc, xv);
-      unpack8(gload16(w + 8 * c), wv8);
+      wload(c, wv8);
       unpack8(gc, gv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o8[i] = r * (gv[i] * wv8[i]) - cx * xv[i];

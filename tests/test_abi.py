@@ -67,7 +67,7 @@ def test_timing_build_has_the_same_kernels():
 
 
 def test_version_and_strerror():
-    assert L.abi_version() == 3
+    assert L.abi_version() == 4
     assert L.strerror(0) == "ok"
     for s in range(1, 7):
         assert L.strerror(s) and L.strerror(s) != "unknown status"
@@ -361,3 +361,38 @@ def test_fused_norm_validation_codes():
     assert lib.lora_fold_norm_weight(1, 16, 60, P, P, P, None) == 2
     assert lib.lora_fold_norm_weight(0, 16, 64, P, P, P, None) == 3
     assert lib.lora_fold_norm_weight(1, 16, 64, P, None, P, None) == 1
+
+
+def test_fused_norm_qkv_validation_codes():
+    lib = L.lib()
+    W = _w()
+    q4 = _w(1, 64, None, P, P, P)
+    def fwd_(dtype=1, k=64, nq=256, nkv=256, r=8, eps=1e-5, nw=P, rstd=P, Wq=W, wsb=1 << 30):
+        return lib.lora_rmsnorm_qkv_fwd(dtype, 16, k, nq, nkv, r, 16.0, eps, P, nw,
+                                        ctypes.byref(Wq), P, P, ctypes.byref(W), P, P,
+                                        ctypes.byref(W), P, P, P, P, P, rstd, P, wsb, None)
+    assert fwd_(nw=None) == 1
+    assert fwd_(rstd=None) == 1
+    assert fwd_(dtype=0) == 3           # bf16 only
+    assert fwd_(Wq=q4) == 3             # a 4-bit weight cannot hold W diag(w)
+    assert fwd_(nkv=136) == 3           # the stacked GEMM's shapes only
+    assert fwd_(r=100) == 3             # 3r > 256
+    assert fwd_(k=60) == 2
+    assert fwd_(eps=float("inf")) == 3
+    assert fwd_(wsb=16) == 4
+    def bwd_(flags=0, rstd=P, dA=P):
+        return lib.lora_rmsnorm_qkv_bwd(1, 16, 64, 256, 256, 8, 16.0, P, P, rstd,
+                                        ctypes.byref(W), P, P, ctypes.byref(W), P, P,
+                                        ctypes.byref(W), P, P, P, P, P, P,
+                                        dA, P, P, P, P, P, flags, P, 1 << 30, None)
+    assert bwd_(flags=2) == 3
+    assert bwd_(rstd=None) == 1
+    assert bwd_(dA=None) == 1
+    ws = lambda op, dt=1, fmt=0, nkv=1024: int(lib.lora_qkv_workspace_bytes(op, dt, fmt, 8192, 4096,
+                                                                          4096, nkv, 16))
+    # the fused backward keeps the projections' input gradient for the row pass
+    assert ws(L.OP_RMSNORM_QKV_BWD) == ws(L.OP_QKV_BWD) + 8192 * 4096 * 2
+    assert ws(L.OP_RMSNORM_QKV_FWD) == ws(L.OP_QKV_FWD)
+    assert ws(L.OP_RMSNORM_QKV_FWD, fmt=1) == 0
+    assert ws(L.OP_RMSNORM_QKV_FWD, dt=0) == 0
+    assert ws(L.OP_RMSNORM_QKV_BWD, nkv=1000) == 0
