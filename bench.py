@@ -57,6 +57,9 @@ def parse():
                     help="print the HBM-traffic summary (markdown) of the GEMM classes from "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection CSVs of "
                          "bench.py and of --calibrate-copy")
+    ap.add_argument("--with-trace", nargs=2, metavar=("TRACE_DIR", "STEP"),
+                    help="with --summarize-counters: durations from one step of a rocprofv3 "
+                         "--kernel-trace output folder of the same workload, and HBM rates")
     ap.add_argument("--summarize-sq", nargs=2, metavar=("SQ_CSV_1", "SQ_CSV_2"),
                     help="print the GEMM classes' shader-engine counter table from the two "
                          "rocprofv3 --pmc counter_collection CSVs of bench.py")
@@ -95,9 +98,16 @@ PROFILED_STEPS = range(1, 5)
 
 def _step_starts(names):
     """Index of each step's first dispatch: the forward opens with k_prep
-    followed by the rank-r pass over X (or by the norm's rstd pass)."""
-    return [i for i in range(len(names) - 1) if "k_prep" in names[i]
-            and ("k_skinny_nt<32" in names[i + 1] or "k_rmsnorm_fwd" in names[i + 1])]
+    followed by the rank-r pass over X (or by the norm's rstd pass), after
+    the 4-bit decodes of the gate and up weights when it has them."""
+    out = []
+    for i in range(len(names) - 1):
+        if "k_prep" in names[i] and ("k_skinny_nt<32" in names[i + 1]
+                                     or "k_rmsnorm_fwd" in names[i + 1]):
+            while i > 0 and "k_dequant4(" in names[i - 1]:
+                i -= 1
+            out.append(i)
+    return out
 
 
 def _steps(rows):
@@ -133,9 +143,33 @@ def traffic_path(cfg):
     return TRAFFIC_SUMMARY.format(shape=shape + ("_q4" if c.get("q4") else ""))
 
 
-def summarize_counters(fetch_csv, write_csv, cf_csv, cw_csv, cfg):
+def _trace_rows(trace_dir):
+    import csv
+    tr = sorted(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))),
+                key=lambda r: int(r["Start_Timestamp"]))
+    return [(int(r["Start_Timestamp"]), r["Kernel_Name"], int(r["End_Timestamp"])) for r in tr]
+
+
+def _longest_runs(names):
+    """name -> (start, length) of its longest run of consecutive dispatches."""
+    out, i = {}, 0
+    while i < len(names):
+        j = i
+        while j < len(names) and names[j] == names[i]:
+            j += 1
+        if j - i > out.get(names[i], (0, 0))[1]:
+            out[names[i]] = (i, j - i)
+        i = j
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, cf_csv, cw_csv, cfg, trace=None):
     """Markdown summary with a machine-readable line read back by bench.py:
-    per GEMM class and, for one step, per dispatch."""
+    per GEMM class and, for one step, per dispatch.  With trace = (folder of
+    a kernel trace of the same workload, step index), each dispatch also gets
+    its traced duration and the HBM rate of its counted bytes, and kernels
+    launched in timing loops of their own (RMSNorm) get a row each."""
+    import statistics
     copy_bytes = 256 << 20
     cf = [v for _, n, v in _counter_rows(cf_csv) if "copyBuffer" in n]
     cw = [v for _, n, v in _counter_rows(cw_csv) if "copyBuffer" in n]
@@ -157,12 +191,45 @@ def summarize_counters(fetch_csv, write_csv, cf_csv, cw_csv, cfg):
                      f"{v['traffic_bytes'] / 1e6:.1f} |")
     k = PROFILED_STEPS[0]
     fs, ws = _steps(frows)[k], _steps(wrows)[k]
-    lines += ["", f"Every dispatch of step {k + 1} (scaled MB):", "",
-              "| # | kernel | FETCH MB | WRITE MB |", "|---|---|---|---|"]
+    durs = None
+    if trace is not None:
+        tsteps = _steps(_trace_rows(trace[0]))
+        tstep = tsteps[int(trace[1])]
+        assert [n for _, n, _ in tstep] == [n for _, n, _ in fs], "trace step differs"
+        durs = [(e - b) / 1e3 for b, _, e in tstep]
+    head = "| # | kernel | FETCH MB | WRITE MB |"
+    if durs:
+        head += " us | GB/s | of 8 TB/s |"
+    lines += ["", f"Every dispatch of step {k + 1} (scaled MB" +
+              (f"; duration from step {int(trace[1]) + 1} of the kernel trace" if durs else "") +
+              "):", "", head, "|---" * (head.count("|") - 1) + "|"]
     for i, ((_, n, fv_), (_, n2, wv_)) in enumerate(zip(fs, ws)):
         assert n == n2, (n, n2)
-        lines.append(f"| {i} | `{_short(n)}` | {fv_ * 1024 * f_fac / 1e6:.1f} | "
-                     f"{wv_ * 1024 * w_fac / 1e6:.1f} |")
+        fb, wb = fv_ * 1024 * f_fac, wv_ * 1024 * w_fac
+        row = f"| {i} | `{_short(n)}` | {fb / 1e6:.1f} | {wb / 1e6:.1f} |"
+        if durs:
+            gbs = (fb + wb) / (durs[i] * 1e-6) / 1e9
+            row += f" {durs[i]:.1f} | {gbs:.0f} | {gbs / PEAK_HBM_GBS:.2f} |"
+        lines.append(row)
+    if durs:
+        fn, wn = [n for _, n, _ in frows], [n for _, n, _ in wrows]
+        tr = _trace_rows(trace[0])
+        tn = [n for _, n, _ in tr]
+        fr, wr, trr = _longest_runs(fn), _longest_runs(wn), _longest_runs(tn)
+        loops = [n for n, (_, ln) in fr.items() if ln >= 10 and "k_lora_gemm" not in n]
+        if loops:
+            lines += ["", "Kernels launched in timing loops of their own (medians over the "
+                      "longest run of consecutive dispatches of each):", "",
+                      "| kernel | dispatches | FETCH MB | WRITE MB | us | GB/s | of 8 TB/s |",
+                      "|---|---|---|---|---|---|---|"]
+            for n in loops:
+                (a0, la), (b0, lb), (c0, lc) = fr[n], wr[n], trr[n]
+                fb = statistics.median(v for _, _, v in frows[a0:a0 + la]) * 1024 * f_fac
+                wb = statistics.median(v for _, _, v in wrows[b0:b0 + lb]) * 1024 * w_fac
+                us = statistics.median((e - b) / 1e3 for b, _, e in tr[c0:c0 + lc])
+                gbs = (fb + wb) / (us * 1e-6) / 1e9
+                lines.append(f"| `{_short(n)}` | {la} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                             f"{us:.1f} | {gbs:.0f} | {gbs / PEAK_HBM_GBS:.2f} |")
     return "\n".join(lines) + "\n\ntraffic-record: " + json.dumps(rec) + "\n"
 
 
@@ -450,6 +517,54 @@ def time_norm_mlp(L, X, W, A, B, alpha, dY, ws_fwd, ws_bwd, stream, steps=5):
     return res
 
 
+def time_norm_qkv(L, X, W, A, B, alpha, dY, stream, steps=5):
+    """RMSNorm + fused q/k/v LoRA projections, forward + backward, outside
+    the timed region: the norm folded into the projections (no normalised
+    rows in memory) against the chain of the standalone norm kernels and the
+    q/k/v calls.  X stands for the raw rows."""
+    import numpy as np
+    import torch
+    T, k = X.shape
+    g = np.random.default_rng(7)
+    w = torch.from_numpy((1.0 + 0.1 * g.standard_normal(k)).astype(np.float32)).to(
+        torch.bfloat16).to(X.device)
+    Wf = {p: L.lora_fold_norm_weight(W[p], w) for p in "qkv"}
+    Xn = torch.empty_like(X)
+    rstd = torch.empty((T,), dtype=torch.float32, device=X.device)
+    dX = torch.empty_like(X)
+    outs = {p: torch.empty((T, W[p].shape[0]), dtype=X.dtype, device=X.device) for p in "qkv"}
+    grads = {"dX": torch.empty_like(X)}
+
+    def chain():
+        L.lora_rmsnorm_fwd(X, w, 1e-5, Y=Xn, rstd=rstd, stream=stream)
+        L.lora_qkv_fwd(Xn, W, A, B, alpha, out=outs, stream=stream)
+        L.lora_qkv_bwd(Xn, W, A, B, alpha, dY, out=grads, stream=stream)
+        L.lora_rmsnorm_bwd(X, w, rstd, grads["dX"], dX=dX, stream=stream)
+
+    def fused():
+        L.lora_rmsnorm_qkv_fwd(X, w, 1e-5, Wf, A, B, alpha, out=outs, rstd=rstd, stream=stream)
+        L.lora_rmsnorm_qkv_bwd(X, w, rstd, Wf, A, B, alpha, dY, out=dict(grads, dX=dX),
+                               stream=stream)
+
+    res = {}
+    for name, fn in (("chain_ms", chain), ("fused_ms", fused)):
+        fn()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        res[name] = round(float(np.median(ts)), 4)
+    res["saved_ms"] = round(res["chain_ms"] - res["fused_ms"], 4)
+    res["source"] = (f"HIP events around each step, median of {steps}, after the timed region; "
+                     "chain = lora_rmsnorm_fwd + lora_qkv_fwd + lora_qkv_bwd + lora_rmsnorm_bwd, "
+                     "fused = lora_rmsnorm_qkv_fwd + _bwd on norm-folded q/k/v weights")
+    return res
+
+
 def bench_attn_mlp(args):
     """Config 4: q, k, v (shared input, dX summed) and o LoRA projections plus
     the LoRA-SwiGLU MLP, forward + backward, T = 16384, r = 64."""
@@ -527,6 +642,9 @@ def bench_attn_mlp(args):
         "wall_s_timed": round(wall, 3), "flops_per_step": flops,
         "roofline": None, "cpu_baseline": None,
     }
+    # the RMSNorm in front of q/k/v, fused into them against the chain (not part of value)
+    line["rmsnorm_qkv_step"] = time_norm_qkv(L, Xa, {p: Wa[p] for p in qkv}, Aa, Ba, alpha,
+                                             {p: dYa[p] for p in qkv}, stream)
     print(json.dumps(line), flush=True)
 
 
@@ -540,7 +658,8 @@ def main():
         calibrate_copy()
         return
     if args.summarize_counters:
-        print(summarize_counters(*args.summarize_counters, args.config), end="")
+        print(summarize_counters(*args.summarize_counters, args.config, trace=args.with_trace),
+              end="")
         return
     if args.summarize_sq:
         print(summarize_sq(*args.summarize_sq), end="")

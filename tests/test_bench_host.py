@@ -178,3 +178,28 @@ def test_source_digest_covers_every_hip_source(tmp_path, monkeypatch):
     assert bench.kernel_source_digest() == d0
     os.remove(tmp_path / "a.hip")
     assert bench.kernel_source_digest() != d0
+
+
+def test_counter_summary_pairs_dispatches_with_traced_durations(tmp_path):
+    copy_kib = (256 << 20) / 1024
+    _write_counters(tmp_path / "cf.csv", [("copyBuffer", copy_kib / 2)] * 3)
+    _write_counters(tmp_path / "cw.csv", [("copyBuffer", copy_kib)] * 3)
+    loop = [("k_rmsnorm_fwd<false>", 1000.0)] * 12
+    rows = sum((_step([100.0] * 4) for _ in range(6)), []) + loop
+    _write_counters(tmp_path / "f.csv", rows)
+    _write_counters(tmp_path / "w.csv", rows)
+    # a trace of the same dispatches, 2 us each
+    with open(tmp_path / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for i, (n, _) in enumerate(rows):
+            w.writerow([n, 3000 * i, 3000 * i + 2000])
+    md = bench.summarize_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                  str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 3,
+                                  trace=(str(tmp_path), "3"))
+    # GEMM 3 of the step: 100 KiB fetched (x2 by the copy scale) + 100 KiB written in 2 us
+    gb = (100 * 1024 * 2 + 100 * 1024) / 2e-6 / 1e9
+    assert f"| 2.0 | {gb:.0f} | {gb / 8000:.2f} |" in md
+    # the norm loop: 12 dispatches, 1000 KiB x 3 per 2 us
+    gl = 3000 * 1024 / 2e-6 / 1e9
+    assert f"| `k_rmsnorm_fwd<false>` | 12 | 2.0 | 1.0 | 2.0 | {gl:.0f} |" in md
