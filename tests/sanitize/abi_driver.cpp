@@ -60,6 +60,14 @@ int main() {
   EXPECT(lora_qkv_fwd(LORA_BF16, 16, 64, 64, 32, 8, 16.f, P, &W, P, P, &W, P, P, &Q, P, P, P, P, P, P, 1 << 30, nullptr), LORA_ERR_UNSUPPORTED);
   EXPECT(lora_qkv_bwd(LORA_BF16, 16, 64, 64, 32, 8, 16.f, P, &W, P, P, &W, P, P, &W, P, P, P, P, nullptr, P, P, P, P, P, P, P, 0, P, 1 << 30, nullptr), LORA_ERR_NULL_POINTER);
 
+  // RMSNorm folded into the q/k/v projections: bf16, dense, the stacked GEMM's shapes
+  EXPECT(lora_rmsnorm_qkv_fwd(LORA_BF16, 16, 64, 256, 136, 8, 16.f, 1e-5f, P, P, &W, P, P, &W, P, P, &W, P, P, P, P, P, (float *)P, P, 1 << 30, nullptr), LORA_ERR_UNSUPPORTED);
+  EXPECT(lora_rmsnorm_qkv_fwd(LORA_BF16, 16, 64, 256, 256, 8, 16.f, 1e-5f, P, P, &Q, P, P, &Q, P, P, &Q, P, P, P, P, P, (float *)P, P, 1 << 30, nullptr), LORA_ERR_UNSUPPORTED);
+  EXPECT(lora_rmsnorm_qkv_fwd(LORA_BF16, 16, 64, 256, 256, 8, 16.f, 1e-5f, P, P, &W, P, P, &W, P, P, &W, P, P, P, P, P, nullptr, P, 1 << 30, nullptr), LORA_ERR_NULL_POINTER);
+  EXPECT(lora_rmsnorm_qkv_fwd(LORA_BF16, 16, 64, 256, 256, 8, 16.f, 1e-5f, P, P, &W, P, P, &W, P, P, &W, P, P, P, P, P, (float *)P, P, 16, nullptr), LORA_ERR_WORKSPACE);
+  EXPECT(lora_rmsnorm_qkv_bwd(LORA_BF16, 16, 64, 256, 256, 8, 16.f, P, P, (const float *)P, &W, P, P, &W, P, P, &W, P, P, P, P, P, P, P, P, P, P, P, P, 2, P, 1 << 30, nullptr), LORA_ERR_UNSUPPORTED);
+  EXPECT(lora_rmsnorm_qkv_bwd(LORA_BF16, 16, 64, 256, 256, 8, 16.f, P, P, nullptr, &W, P, P, &W, P, P, &W, P, P, P, P, P, P, P, P, P, P, P, P, 0, P, 1 << 30, nullptr), LORA_ERR_NULL_POINTER);
+
   // standalone kernels
   EXPECT(lora_dequant4(16, 60, (const uint8_t *)P, (const float *)P, (const float *)P, 64, LORA_BF16, P, nullptr), LORA_ERR_BAD_SHAPE);
   EXPECT(lora_decode_weight(16, 64, &W, LORA_BF16, P, nullptr), LORA_ERR_UNSUPPORTED);
@@ -76,12 +84,19 @@ int main() {
     for (int64_t k : Ks)
       for (int64_t n : Ks)
         for (int64_t r : Rs)
-          for (int op = 0; op <= LORA_OP_RMSNORM_MLP_BWD; ++op)
+          for (int op = 0; op <= LORA_OP_RMSNORM_QKV_BWD; ++op)
             for (int dt = 0; dt < 2; ++dt)
               for (int wf = 0; wf < 3; ++wf) {
                 const size_t fast = lora_workspace_bytes(op, dt, wf, T, k, n, r);
                 const size_t mini = lora_workspace_bytes(op | LORA_WS_MINIMAL, dt, wf, T, k, n, r);
-                if (op == LORA_OP_QKV_FWD || op == LORA_OP_QKV_BWD) {
+                if (op == LORA_OP_RMSNORM_QKV_FWD || op == LORA_OP_RMSNORM_QKV_BWD) {
+                  EXPECT(fast, 0);
+                  EXPECT(mini, 0);
+                  const size_t q = lora_qkv_workspace_bytes(op, dt, wf, T, k, n, n, r);
+                  // one strategy: the minimal flag asks for the same size
+                  EXPECT(lora_qkv_workspace_bytes(op | LORA_WS_MINIMAL, dt, wf, T, k, n, n, r), q);
+                  if (q) EXPECT(dt == LORA_BF16 && wf == LORA_W_DENSE, 1);
+                } else if (op == LORA_OP_QKV_FWD || op == LORA_OP_QKV_BWD) {
                   EXPECT(fast, 0);   // lora_qkv_workspace_bytes answers those
                   const size_t q = lora_qkv_workspace_bytes(op, dt, wf, T, k, n, n / 2 + 8, r);
                   const size_t qm = lora_qkv_workspace_bytes(op | LORA_WS_MINIMAL, dt, wf, T, k, n, n / 2 + 8, r);
