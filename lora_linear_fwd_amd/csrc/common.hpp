@@ -67,6 +67,16 @@ __device__ __forceinline__ void gstore8(void *p, const u32x2 &v) {
 __device__ __forceinline__ void gstore16(void *p, const u32x4 &v) {
   *reinterpret_cast<u32x4 *>(p) = v;
 }
+// Streaming (non-temporal) forms for data touched once per pass that would
+// only displace reusable lines from L2 and the MALL: the SwiGLU-derivative
+// epilogue's e, g reads and de, dg writes.  (The SwiGLU forward's e, g, h
+// stores stay cached: h is read again right after.)
+__device__ __forceinline__ void gstore16_nt(void *p, const u32x4 &v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ u32x4 gload16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 // ----------------------------------------------------- buffer resources ----
 // Raw buffer descriptor (gfx9 layout) over `base`, `bytes` long.  Loads at

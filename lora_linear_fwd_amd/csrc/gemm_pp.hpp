@@ -423,8 +423,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         u32x4 e = {0, 0, 0, 0}, g = {0, 0, 0, 0};
         if (m < M && n < N) {
           const int64_t off = (int64_t)m * N + n;
-          e = gload16(p.Ein + off);
-          g = gload16(p.Gin + off);
+          e = gload16_nt(p.Ein + off);
+          g = gload16_nt(p.Gin + off);
         }
         ein[it] = e;
         gin[it] = g;
@@ -524,8 +524,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         u32x4 e = {0, 0, 0, 0}, g = {0, 0, 0, 0};
         if (m < M && n < N) {
           const int64_t off = (int64_t)m * N + n;
-          e = gload16(p.Ein + off);
-          g = gload16(p.Gin + off);
+          e = gload16_nt(p.Ein + off);
+          g = gload16_nt(p.Gin + off);
         }
         ein[it] = e;
         gin[it] = g;
@@ -574,8 +574,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
                       bf16lo(dgw[t]) * bf16lo(gv[t]) + bf16hi(dgw[t]) * bf16hi(gv[t]);
           }
           const int64_t doff = (int64_t)m * p.ldd + n;
-          gstore16(p.DE + doff, dew);
-          gstore16(p.DG + doff, dgw);
+          gstore16_nt(p.DE + doff, dew);
+          gstore16_nt(p.DG + doff, dgw);
         }
         if (p.cpart) {   // folded RMSNorm: see EPI_SWIGLU_BWD
           csum += __shfl_xor(csum, 1, 64);
@@ -847,8 +847,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
                           bf16lo(dgw[t]) * bf16lo(gv[t]) + bf16hi(dgw[t]) * bf16hi(gv[t]);
               }
               const int64_t doff = (int64_t)m * p.ldd + n;
-              gstore16(p.DE + doff, dew);
-              gstore16(p.DG + doff, dgw);
+              gstore16_nt(p.DE + doff, dew);
+              gstore16_nt(p.DG + doff, dgw);
             }
             if (p.cpart) {
               // the 8 lanes of one row (lanes 8j .. 8j+7) add their sums in a
