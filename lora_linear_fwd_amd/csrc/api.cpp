@@ -682,8 +682,9 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, 
                                                                             : plan_f32(op, T, kd, nf, r);
   if (dtype != LORA_BF16) return 0;
   // only 4-bit weights are copied: decoded for the forwards, decoded and
-  // transposed for the backwards (dense weights are read in place: the NN
-  // GEMM on W as stored is as fast as a transposed copy plus the NT GEMM)
+  // transposed for the backwards (dense weights are read in place: the NT
+  // GEMM over a caller-kept W^T, else the NN GEMM over W as stored, which
+  // costs what a per-call transposed copy would save)
   const bool fwd_copy = !minimal && wfmt != LORA_W_DENSE, bwd_copy = fwd_copy;
   switch (op) {
     case LORA_OP_LINEAR_FWD: return plan_lin_fwd(T, kd, nf, r, fwd_copy).total;
