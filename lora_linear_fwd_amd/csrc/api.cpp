@@ -946,7 +946,7 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
                      hbf, s, st));
   a.hglob = hbf;
-  LORA_TRY(run_gemm(KC_GATEUP_FWD, false, wg.q4, EPI_SWIGLU_FWD, a, st));
+  LORA_TRY(run_gemm(KC_GATEUP_FWD, false, wg.q4, nf ? EPI_SWIGLU_FWD_NORM : EPI_SWIGLU_FWD, a, st));
 
   // down
   if (wcopy && wd.q4) {   // reuses the buffer once the gate/up GEMM is done
@@ -1209,7 +1209,7 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
       b.accumulate = nf->accumulate;
     }
     b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
-    LORA_TRY(run_gemm(KC_GATEUP_BWD, nn, q4, EPI_STORE, b, st));
+    LORA_TRY(run_gemm(KC_GATEUP_BWD, nn, q4, nf ? EPI_STORE_NORM : EPI_STORE, b, st));
   }
   // 7. [dAg; dAu] = s G_gu^T X  (folded norm: G_gu rows scaled by rstd, the
   //    result's columns by w, so X stands in for the normalised rows)
@@ -1359,7 +1359,7 @@ static int qkv_fwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t 
   a.C1 = (bf16_t *)K; a.ldc1 = nkv;
   a.C2 = (bf16_t *)V; a.ldc2 = nkv;
   a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)(N / BN);
-  return run_gemm(KC_QKV_FWD, false, false, EPI_STORE, a, st);
+  return run_gemm(KC_QKV_FWD, false, false, nf ? EPI_STORE_NORM : EPI_STORE, a, st);
 }
 
 int lora_qkv_fwd(int dtype, int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,

@@ -164,6 +164,18 @@ __device__ __forceinline__ float absmax_at(const AbsmaxSrc &s, int64_t b) {
   return absmax_dq(s.table[s.codes[b]], s.scale[b >> 8], s.offset);
 }
 
+// Sum of x over the 8 lanes 8j .. 8j+7, valid in lane 8j, added as
+// ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7)): DPP lane moves inside
+// the VALU, no round trip through the LDS unit.  quad_perm [1,0,3,2] reads
+// lane ^ 1, quad_perm [2,3,0,1] lane ^ 2; row_ror:n reads lane (i - n) mod
+// 16 of the 16-lane row, so row_ror:12 reads lane (i + 4) mod 16.
+__device__ __forceinline__ float sum8_lanes(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x12C, 0xF, 0xF, false));
+  return x;
+}
+
 // fast logistic with the hardware exp2 / reciprocal
 __device__ __forceinline__ float sigmoidf_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));

@@ -68,7 +68,15 @@ constexpr bool bmode_dq(int m) { return m == B_NT_Q4DQ || m == B_NN_Q4DQ; }
 // EPI_SWIGLU_BWD_RANK (eight-wave kernel, rank-r width 16): the SwiGLU'
 // epilogue that also forms the tile's shares of the four rank-r products of
 // the MLP backward (see GemmArgs::fr_*)
-enum Epi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_SWIGLU_BWD_RANK = 3 };
+// EPI_STORE_NORM is the store epilogue with per-row factors of a folded
+// RMSNorm (rowscale, or nrm_x / nrm_rs / nrm_kk; not both), requested before
+// each half of the tile is staged; EPI_SWIGLU_FWD_NORM the SwiGLU forward with
+// rowscale, requested before the LoRA pass.  EPI_STORE and EPI_SWIGLU_FWD
+// ignore those fields.  (Eight-wave kernel only.)
+enum Epi {
+  EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_SWIGLU_BWD_RANK = 3,
+  EPI_STORE_NORM = 4, EPI_SWIGLU_FWD_NORM = 5
+};
 
 struct GemmArgs {
   int M, N, K;
@@ -106,13 +114,13 @@ struct GemmArgs {
   bf16_t *C1, *C2;
   int64_t ldc1, ldc2;
   // RMSNorm folded into the projections that follow it (eight-wave kernel):
-  //   rowscale  SwiGLU forward: e, g of row m are scaled by rowscale[m];
-  //             store: row m of C is (before any accumulation)
+  //   rowscale  EPI_SWIGLU_FWD_NORM: e, g of row m are scaled by rowscale[m];
+  //             EPI_STORE_NORM: row m of C is (before any accumulation)
   //             (rstd; the GEMM reads the raw rows and weights W diag(w))
   //   cpart     SwiGLU backward: cpart[(tile column * 4 + 64-column block) *
   //             M + m] = sum over the block's columns of de e + dg g
   //             (de, dg as stored); nullptr: not formed
-  //   nrm_x     store: C = nrm_rs[m] acc - nrm_kk[m] nrm_x[m][n] (before any
+  //   nrm_x     EPI_STORE_NORM: C = nrm_rs[m] acc - nrm_kk[m] nrm_x[m][n] (before any
   //             accumulation), the RMSNorm input gradient; nrm_x is [M x N]
   const float *rowscale;
   float *cpart;

@@ -20,6 +20,7 @@ static hipError_t launch_pp_nn(const GemmArgs &a, hipStream_t st) {
 }
 hipError_t launch_gemm_nn(int epi, const GemmArgs &a, hipStream_t st) {
   if (epi == EPI_STORE) return launch_pp_nn<EPI_STORE>(a, st);
+  if (epi == EPI_STORE_NORM) return launch_pp_nn<EPI_STORE_NORM>(a, st);
   if (epi == EPI_SWIGLU_BWD) return launch_pp_nn<EPI_SWIGLU_BWD>(a, st);
   if (epi == EPI_SWIGLU_BWD_RANK) return launch_pp_nn<EPI_SWIGLU_BWD_RANK>(a, st);
   return hipErrorInvalidValue;

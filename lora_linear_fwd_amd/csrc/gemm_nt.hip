@@ -18,7 +18,9 @@ static hipError_t launch_pp(const GemmArgs &a, hipStream_t st) {
 }
 hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st) {
   if (epi == EPI_STORE) return launch_pp<EPI_STORE>(a, st);
+  if (epi == EPI_STORE_NORM) return launch_pp<EPI_STORE_NORM>(a, st);
   if (epi == EPI_SWIGLU_FWD) return launch_pp<EPI_SWIGLU_FWD>(a, st);
+  if (epi == EPI_SWIGLU_FWD_NORM) return launch_pp<EPI_SWIGLU_FWD_NORM>(a, st);
   if (epi == EPI_SWIGLU_BWD) return launch_pp<EPI_SWIGLU_BWD>(a, st);
   if (epi == EPI_SWIGLU_BWD_RANK) return launch_pp<EPI_SWIGLU_BWD_RANK>(a, st);
   return hipErrorInvalidValue;

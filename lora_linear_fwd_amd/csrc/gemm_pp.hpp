@@ -60,7 +60,7 @@ __device__ __forceinline__ void pp_barrier() {
 template <int EPI, bool NN = false>
 __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr bool GU = (EPI == EPI_SWIGLU_FWD);
+  constexpr bool GU = (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_FWD_NORM);
   static_assert(!(NN && GU), "the gate/up forward reads its weights K-contiguous");
   constexpr int BK = 64, XS = BM * BK * 2, WS = BN * BK * 2;
 
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         // token stage s & 1 was last read in the phase before, so its loads
         // may go first: the store form issues them ahead of the fragment
         // reads (3 % faster there), the SwiGLU forms after them (1 % faster)
-        if constexpr (EPI == EPI_STORE) {
+        if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_NORM) {
           if (s + 2 < nk) dma_a(s + 2, s & 1);
           if (s + 1 < nk) rd(s + 1);
         } else {
@@ -411,6 +411,35 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   wait_vmem();
   __syncthreads();         // stages free for the epilogue
 
+  // SwiGLU forward with a folded norm: the rows' rstd, requested before the
+  // LoRA pass so the epilogue does not wait on them
+  float grs[2][4];
+  if constexpr (EPI == EPI_SWIGLU_FWD_NORM) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int m = m0 + wm * 128 + h * 64 + it * 16 + (lane >> 2);
+        grs[h][it] = m < M ? p.rowscale[m] : 1.f;
+      }
+  }
+  // store with a folded norm: a half's row factors (and raw rows) are all
+  // requested before the half is staged
+  u32x4 nxv[8];
+  float nrs[8], nkk[8];
+  auto load_norm = [&](int half) {
+    if constexpr (EPI == EPI_STORE_NORM) {
+      const int q = lane & 7, n = n0 + wn * 64 + 8 * q;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int m = m0 + wm * 128 + half * 64 + it * 8 + (lane >> 3);
+        const bool ok = m < M && n < N;
+        nrs[it] = !ok ? 0.f : p.nrm_x ? p.nrm_rs[m] : p.rowscale ? p.rowscale[m] : 1.f;
+        nkk[it] = ok && p.nrm_x ? p.nrm_kk[m] : 0.f;
+        nxv[it] = ok && p.nrm_x ? gload16(p.nrm_x + (int64_t)m * N + n) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
   // SwiGLU backward: a half's saved e, g are all requested before the half
   // is staged
   u32x4 ein[8], gin[8];
@@ -578,9 +607,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           gstore16_nt(p.DG + doff, dgw);
         }
         if (p.cpart) {   // folded RMSNorm: see EPI_SWIGLU_BWD
-          csum += __shfl_xor(csum, 1, 64);
-          csum += __shfl_xor(csum, 2, 64);
-          csum += __shfl_xor(csum, 4, 64);
+          csum = sum8_lanes(csum);
           if (q == 0 && m < M) p.cpart[(int64_t)(tn * 4 + wn) * M + m] = csum;
         }
         lds_write16(tl0, tb_off(r, q), hw);
@@ -714,6 +741,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   #pragma unroll
     for (int half = 0; half < 2; ++half) {
       load_eg(half);
+      load_norm(half);
       // region rows jj * 32 + l32 hold token block j = 2 half + jj
   #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
@@ -747,8 +775,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
             float gv[8] = {__uint_as_float(g0[0]), __uint_as_float(g0[1]), __uint_as_float(g0[2]),
                            __uint_as_float(g0[3]), __uint_as_float(g1[0]), __uint_as_float(g1[1]),
                            __uint_as_float(g1[2]), __uint_as_float(g1[3])};
-            if (p.rowscale) {   // folded RMSNorm: the row's rstd
-              const float rs = p.rowscale[m];
+            if constexpr (EPI == EPI_SWIGLU_FWD_NORM) {   // folded RMSNorm: the row's rstd
+              const float rs = grs[half][it];
   #pragma unroll
               for (int t = 0; t < 8; ++t) {
                 ev[t] *= rs;
@@ -783,20 +811,22 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           float v[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
                         __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
                         __uint_as_float(a1[2]), __uint_as_float(a1[3])};
-          if constexpr (EPI == EPI_STORE) {
+          if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_NORM) {
             if (!valid) continue;
-            if (p.rowscale) {   // folded RMSNorm: the row's rstd
-              const float rs = p.rowscale[m];
+            if constexpr (EPI == EPI_STORE_NORM) {
+              if (!p.nrm_x && p.rowscale) {   // folded RMSNorm: the row's rstd
+                const float rs = nrs[it];
   #pragma unroll
-              for (int t = 0; t < 8; ++t) v[t] *= rs;
-            }
-            if (p.nrm_x) {   // RMSNorm input gradient from the folded projections' output
-              const u32x4 xv = gload16(p.nrm_x + (int64_t)m * N + n);
-              const float rs = p.nrm_rs[m], kk = p.nrm_kk[m];
+                for (int t = 0; t < 8; ++t) v[t] *= rs;
+              }
+              if (p.nrm_x) {   // RMSNorm input gradient from the folded projections' output
+                const u32x4 xv = nxv[it];
+                const float rs = nrs[it], kk = nkk[it];
   #pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                v[2 * t] = rs * v[2 * t] - kk * bf16lo(xv[t]);
-                v[2 * t + 1] = rs * v[2 * t + 1] - kk * bf16hi(xv[t]);
+                for (int t = 0; t < 4; ++t) {
+                  v[2 * t] = rs * v[2 * t] - kk * bf16lo(xv[t]);
+                  v[2 * t + 1] = rs * v[2 * t + 1] - kk * bf16hi(xv[t]);
+                }
               }
             }
             bf16_t *cb = p.C;
@@ -852,10 +882,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
             }
             if (p.cpart) {
               // the 8 lanes of one row (lanes 8j .. 8j+7) add their sums in a
-              // fixed butterfly; every lane takes part (invalid ones add 0)
-              csum += __shfl_xor(csum, 1, 64);
-              csum += __shfl_xor(csum, 2, 64);
-              csum += __shfl_xor(csum, 4, 64);
+              // fixed order; every lane takes part (invalid ones add 0)
+              csum = sum8_lanes(csum);
               if (q == 0 && m < M) p.cpart[(int64_t)(tn * 4 + wn) * M + m] = csum;
             }
           }
