@@ -461,27 +461,29 @@ def time_rmsnorm(T, d, reps=20):
 
 
 def _chain_vs_fused(chain, fused, stream, steps):
-    """Median step time of two forms of the same work, timed alternately
-    (one warm-up each first) so that clock or thermal drift affects both."""
+    """Per-step time of two forms of the same work: blocks of `steps`
+    back-to-back steps of each form, alternated three times after one
+    untimed block each (so clock or thermal drift affects both); the median
+    over the blocks."""
     import numpy as np
     import torch
-    chain()
-    fused()
     ts = {"chain_ms": [], "fused_ms": []}
-    for _ in range(steps):
+    for rep in range(4):
         for name, fn in (("chain_ms", chain), ("fused_ms", fused)):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            fn()
+            for _ in range(steps):
+                fn()
             b.record(stream)
             torch.cuda.synchronize()
-            ts[name].append(a.elapsed_time(b))
+            if rep:
+                ts[name].append(a.elapsed_time(b) / steps)
     res = {k: round(float(np.median(v)), 4) for k, v in ts.items()}
     res["saved_ms"] = round(res["chain_ms"] - res["fused_ms"], 4)
     return res
 
 
-def time_norm_mlp(L, X, W, A, B, alpha, dY, ws_fwd, ws_bwd, stream, steps=9):
+def time_norm_mlp(L, X, W, A, B, alpha, dY, ws_fwd, ws_bwd, stream, steps=5):
     """RMSNorm + LoRA-SwiGLU MLP, forward + backward, outside the timed
     region: the norm fused into the gate/up projections (folded weights, no
     normalised rows in memory) against the same step as a chain of the
@@ -520,14 +522,15 @@ def time_norm_mlp(L, X, W, A, B, alpha, dY, ws_fwd, ws_bwd, stream, steps=9):
                                       out=dict(out, dX=dX), workspace=ws[:nb], stream=stream)
 
     res = _chain_vs_fused(chain, fused, stream, steps)
-    res["source"] = (f"HIP events around each step, chain and fused steps alternating, median "
-                     f"of {steps} each, after the timed region; chain = lora_rmsnorm_fwd + MLP fwd "
-                     "+ MLP bwd + lora_rmsnorm_bwd, fused = lora_rmsnorm_swiglu_mlp_fwd + _bwd on "
-                     "norm-folded gate/up weights")
+    res["source"] = (f"HIP events around blocks of {steps} back-to-back steps of each form, "
+                     "alternated three times after an untimed block each, median per-step time, "
+                     "after the timed region; chain = lora_rmsnorm_fwd + MLP fwd + MLP bwd + "
+                     "lora_rmsnorm_bwd, fused = lora_rmsnorm_swiglu_mlp_fwd + _bwd on norm-folded "
+                     "gate/up weights")
     return res
 
 
-def time_norm_qkv(L, X, W, A, B, alpha, dY, stream, steps=9):
+def time_norm_qkv(L, X, W, A, B, alpha, dY, stream, steps=5):
     """RMSNorm + fused q/k/v LoRA projections, forward + backward, outside
     the timed region: the norm folded into the projections (no normalised
     rows in memory) against the chain of the standalone norm kernels and the
@@ -557,10 +560,11 @@ def time_norm_qkv(L, X, W, A, B, alpha, dY, stream, steps=9):
                                stream=stream)
 
     res = _chain_vs_fused(chain, fused, stream, steps)
-    res["source"] = (f"HIP events around each step, chain and fused steps alternating, median "
-                     f"of {steps} each, after the timed region; chain = lora_rmsnorm_fwd + "
-                     "lora_qkv_fwd + lora_qkv_bwd + lora_rmsnorm_bwd, fused = lora_rmsnorm_qkv_fwd "
-                     "+ _bwd on norm-folded q/k/v weights")
+    res["source"] = (f"HIP events around blocks of {steps} back-to-back steps of each form, "
+                     "alternated three times after an untimed block each, median per-step time, "
+                     "after the timed region; chain = lora_rmsnorm_fwd + lora_qkv_fwd + "
+                     "lora_qkv_bwd + lora_rmsnorm_bwd, fused = lora_rmsnorm_qkv_fwd + _bwd on "
+                     "norm-folded q/k/v weights")
     return res
 
 
