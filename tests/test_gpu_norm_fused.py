@@ -72,6 +72,7 @@ def run_fused(mi, w, x_scale=1.0, accumulate=False, rows=None, full_grads=True):
     (300, 320, 520, 16, 0.02, 1.0),     # ragged in every dimension, the dual rank-r pass
     (256, 256, 512, 8, 1.0, 1.0),       # LoRA-dominant adapters
     (200, 256, 768, 64, 0.5, 30.0),     # wide rank (separate rank-r passes), large activations
+    (264, 192, 392, 32, 0.3, 1.0),      # the dual rank-r passes
     (37, 72, 40, 3, 0.5, 1.0),          # below one tile
 ], ids=lambda v: str(v))
 def test_fused_norm_mlp(T, d, f, r, bstd, xs):

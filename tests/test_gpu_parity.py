@@ -188,6 +188,8 @@ MLP_SHAPES = [
     (37, 64, 72, 3),
     (260, 128, 264, 64),
     (513, 136, 256, 8),
+    (200, 192, 392, 24),    # 16 < r <= 32: the dual rank-r passes, not the fused epilogue
+    (130, 256, 512, 32),
     (70, 64, 136, 128),     # widest side operands (2 r = 256)
 ]
 
