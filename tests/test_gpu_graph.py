@@ -113,3 +113,83 @@ def test_qkv_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         for i, t in enumerate(tensors):
             assert np.array_equal(_bits(t), ref[i]), f"replay {rep}, tensor {i}"
+
+
+@pytest.mark.parametrize("part", ["mlp", "qkv"])
+def test_norm_fused_step_graph_replays_match_eager(part):
+    """The norm-fused MLP and q/k/v steps (rstd-only norm pass, row-scaled
+    epilogues, the norm coefficient and the raw rows' gradient) under graph
+    capture, residual-gradient accumulation included."""
+    import torch
+    log(f"graph: norm-fused {part}")
+    g = np.random.default_rng(71)
+    if part == "mlp":
+        T, d, f, r = 300, 256, 576, 16
+        mi = gen_mlp(T, d, f, r, 16.0, "bf16", seed=72)
+        Wd, _ = mlp_weights(mi)
+        w = dev(1.0 + 0.1 * g.standard_normal(d), "bf16")
+        W = dict(Wd, gate=L.lora_fold_norm_weight(Wd["gate"], w),
+                 up=L.lora_fold_norm_weight(Wd["up"], w))
+        A = {p: dev(mi.A[p], "bf16") for p in mi.A}
+        B = {p: dev(mi.B[p], "bf16") for p in mi.B}
+        X, dY = dev(mi.X, "bf16"), dev(mi.dY, "bf16")
+        nb = max(L.workspace_bytes(op, L.LORA_BF16, 0, T, d, f, r)
+                 for op in (L.OP_RMSNORM_MLP_FWD, L.OP_RMSNORM_MLP_BWD))
+        wsb = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        Y, e, gg, rstd = L.lora_rmsnorm_swiglu_mlp_fwd(X, w, 1e-5, W, A, B, 16.0, workspace=wsb)
+        R = dev(g.standard_normal((T, d)), "bf16")
+        out = {"dX": torch.empty_like(X)}
+        for p in ("gate", "up", "down"):
+            out["dA_" + p] = torch.empty_like(A[p])
+            out["dB_" + p] = torch.empty_like(B[p])
+
+        def step(stream):
+            out["dX"].copy_(R)     # the residual branch's gradient, accumulated into
+            L.lora_rmsnorm_swiglu_mlp_fwd(X, w, 1e-5, W, A, B, 16.0, Y=Y, e=e, g=gg, rstd=rstd,
+                                          workspace=wsb, stream=stream)
+            L.lora_rmsnorm_swiglu_mlp_bwd(X, w, rstd, W, A, B, 16.0, e, gg, dY,
+                                          accumulate_dx=True, out=out, workspace=wsb,
+                                          stream=stream)
+        outs = lambda: [Y, e, gg, rstd] + [out[k] for k in sorted(out)]
+    else:
+        T, k, nq, nkv, r = 130, 256, 512, 256, 16
+        lis = {p: gen_linear(T, k, n, r, 16.0, "bf16", seed=80 + i)
+               for i, (p, n) in enumerate((("q", nq), ("k", nkv), ("v", nkv)))}
+        X = dev(lis["q"].X, "bf16")
+        w = dev(1.0 + 0.1 * g.standard_normal(k), "bf16")
+        W = {p: L.lora_fold_norm_weight(dev(li.W, "bf16"), w) for p, li in lis.items()}
+        A = {p: dev(li.A, "bf16") for p, li in lis.items()}
+        B = {p: dev(li.B, "bf16") for p, li in lis.items()}
+        dY = {p: dev(li.dY, "bf16") for p, li in lis.items()}
+        nb = max(int(L.lib().lora_qkv_workspace_bytes(op, L.LORA_BF16, 0, T, k, nq, nkv, r))
+                 for op in (L.OP_RMSNORM_QKV_FWD, L.OP_RMSNORM_QKV_BWD))
+        wsb = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        o, rstd = L.lora_rmsnorm_qkv_fwd(X, w, 1e-5, W, A, B, 16.0, workspace=wsb)
+        gr = L.lora_rmsnorm_qkv_bwd(X, w, rstd, W, A, B, 16.0, dY, workspace=wsb)
+
+        def step(stream):
+            L.lora_rmsnorm_qkv_fwd(X, w, 1e-5, W, A, B, 16.0, out=o, rstd=rstd, workspace=wsb,
+                                   stream=stream)
+            L.lora_rmsnorm_qkv_bwd(X, w, rstd, W, A, B, 16.0, dY, out=gr, workspace=wsb,
+                                   stream=stream)
+        outs = lambda: [o[p] for p in ("q", "k", "v")] + [rstd] + [gr[kk] for kk in sorted(gr)]
+
+    bits = lambda t: t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [bits(t).copy() for t in outs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs():
+            t.fill_(5.0)              # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, t in enumerate(outs()):
+            assert np.array_equal(bits(t), ref[i]), f"replay {rep}, output {i}"
