@@ -230,7 +230,10 @@ int lora_linear_bwd_noalloc(int dtype, int64_t T, int64_t k, int64_t n, int64_t 
  *   e = lin(X; gate), g = lin(X; up), h = silu(e) * g, Y = lin(h; down),
  * each lin a LoRA linear with the same r and alpha.  silu(z) = z/(1+e^-z).
  * Out: Y [T x d]; e_saved, g_saved [T x f] (the activations the backward
- * needs; X is the caller's).  h lives in the workspace.
+ * needs; X is the caller's).  h lives in the workspace.  The down
+ * projection's rank-r product s (h Ad^T) comes, for r <= 16 with dense or
+ * decoded weights, from the gate/up GEMM's epilogue (per-tile sums over its
+ * features, added in a fixed order) instead of a second pass over h.
  */
 int lora_swiglu_mlp_fwd(int dtype, int64_t T, int64_t d, int64_t f, int64_t r,
                         float alpha, const void *X,

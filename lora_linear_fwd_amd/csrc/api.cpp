@@ -119,8 +119,15 @@ LinBwdPlan plan_lin_bwd(int64_t T, int64_t k, int64_t n, int64_t r, bool wcopy) 
   return p;
 }
 
+// The gate/up forward's SwiGLU epilogue forms H_d = h Ad^T as per-tile
+// partials (one 16-wide MFMA block of rank) when it runs in the eight-wave
+// kernel, instead of a separate pass over h
+inline bool mlp_fwd_hd_fused(int64_t r) { return rs_of(r) == 16; }
+inline int64_t gu_tiles_n(int64_t f) { return cdiv(f, 128); }
 struct MlpFwdPlan { size_t h, side_gu, epi_gu, side_d, epi_d, hpart, hbf, wbuf, total; };
-MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) {
+// hd: H_d from the gate/up epilogue; its partials [gu_tiles_n(f) x T x 16]
+// fp32 share hpart with the pass over X, which is done by then
+MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, bool hd) {
   Bump b; MlpFwdPlan p{};
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   if (wcopy) p.wbuf = b.take((size_t)2 * f * d * 2);   // Wg | Wu, later Wd
@@ -129,7 +136,8 @@ MlpFwdPlan plan_mlp_fwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy) 
   p.epi_gu = b.take((size_t)2 * f * RS1 * 2);
   p.side_d = b.take((size_t)RS2 * f * 2);
   p.epi_d = b.take((size_t)d * RS2 * 2);
-  p.hpart = b.take(std::max(nt_part_bytes(T, d, RS1), nt_part_bytes(T, f, RS2)));
+  p.hpart = b.take(std::max(nt_part_bytes(T, d, RS1),
+                            hd ? (size_t)gu_tiles_n(f) * T * 16 * 4 : nt_part_bytes(T, f, RS2)));
   p.hbf = b.take((size_t)T * std::max(RS1, RS2) * 2);
   p.total = b.cur;
   return p;
@@ -689,11 +697,13 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, 
   switch (op) {
     case LORA_OP_LINEAR_FWD: return plan_lin_fwd(T, kd, nf, r, fwd_copy).total;
     case LORA_OP_LINEAR_BWD: return plan_lin_bwd(T, kd, nf, r, bwd_copy).total;
-    case LORA_OP_MLP_FWD: return plan_mlp_fwd(T, kd, nf, r, fwd_copy).total;
+    case LORA_OP_MLP_FWD:
+      return plan_mlp_fwd(T, kd, nf, r, fwd_copy,
+                          mlp_fwd_hd_fused(r) && (wfmt == LORA_W_DENSE || fwd_copy)).total;
     case LORA_OP_MLP_BWD: return plan_mlp_bwd(T, kd, nf, r, bwd_copy).total;
     // the folded-norm MLP takes dense weights only
     case LORA_OP_RMSNORM_MLP_FWD:
-      return wfmt == LORA_W_DENSE ? plan_mlp_fwd(T, kd, nf, r, false).total : 0;
+      return wfmt == LORA_W_DENSE ? plan_mlp_fwd(T, kd, nf, r, false, mlp_fwd_hd_fused(r)).total : 0;
     case LORA_OP_RMSNORM_MLP_BWD:
       return wfmt == LORA_W_DENSE ? plan_mlp_bwd(T, kd, nf, r, false, true).total : 0;
   }
@@ -905,7 +915,9 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
                        (const float *)Bd, (float *)Y, H, st);
   }
   const bool wcopy = fast && wg.q4;   // the plan holds a weight buffer
-  const MlpFwdPlan pl = plan_mlp_fwd(T, d, f, r, wcopy);
+  // H_d from the gate/up epilogue (eight-wave kernel: dense or decoded weights)
+  const bool hdf = mlp_fwd_hd_fused(r) && (!wg.q4 || wcopy);
+  const MlpFwdPlan pl = plan_mlp_fwd(T, d, f, r, wcopy, hdf);
   bf16_t *wb = (bf16_t *)(w + pl.wbuf);
   if (wcopy) {   // decode Wg, Wu once, then the dense GEMM
     LORA_TRY(decode_w(wb, wg, f, d, st));
@@ -941,12 +953,19 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   a.rs = RS1; a.epi = epi_gu;
   a.E = (bf16_t *)e_saved; a.G = (bf16_t *)g_saved; a.H = h;
   if (nf) a.rowscale = nf->rstd;
-  a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, 128);
+  a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)gu_tiles_n(f);
+  if (hdf) { a.fr_sd = side_d; a.fr_ud = hpart; }
   // [s X Ag^T | s X Au^T], once per call
   LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
                      hbf, s, st));
   a.hglob = hbf;
   LORA_TRY(run_gemm(KC_GATEUP_FWD, false, wg.q4, nf ? EPI_SWIGLU_FWD_NORM : EPI_SWIGLU_FWD, a, st));
+  if (hdf) {   // s H_d in bf16: the epilogue's partials summed over the tiles in a fixed order
+    const ReduceUArgs ru{hpart, (int)T, 16, RS2, (int)r, 1, (int)gu_tiles_n(f), 0, s, nullptr, hbf,
+                         nullptr};
+    hipLaunchKernelGGL(k_reduce_dual_u, dim3(blocks_for(T * RS2)), dim3(256), 0, st, ru);
+    HIP_TRY(hipGetLastError());
+  }
 
   // down
   if (wcopy && wd.q4) {   // reuses the buffer once the gate/up GEMM is done
@@ -961,8 +980,9 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   b.C = (bf16_t *)Y; b.ldc = d;
   b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
   // s h Ad^T, once per call
-  LORA_TRY(skinny_nt(RS2, false, T, f, h, h, f, f, nullptr, nullptr, side_d, hpart, nullptr, hbf,
-                     s, st));
+  if (!hdf)
+    LORA_TRY(skinny_nt(RS2, false, T, f, h, h, f, f, nullptr, nullptr, side_d, hpart, nullptr, hbf,
+                       s, st));
   b.hglob = hbf;
   return run_gemm(KC_DOWN_FWD, false, wd.q4, EPI_STORE, b, st);
 }

@@ -460,6 +460,17 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       }
     }
   };
+  // SwiGLU forward with fr_ud: the lane's Ad operand for the H_d partials
+  // (row l % 16, the wave's features 8 (l / 16) ..), requested without a
+  // branch ahead of the LoRA pass, whose own waits then cover it (a zero
+  // operand where it does not apply)
+  u32x4 sdh = {0, 0, 0, 0};
+  bool sdh_ok = false;
+  if constexpr (GU) {
+    const int jf = tn * 128 + wn * 32 + 8 * (lane >> 4);
+    sdh_ok = p.fr_ud != nullptr && jf < p.gu_f;
+    sdh = gload16(sdh_ok ? p.fr_sd + (int64_t)(lane & 15) * p.gu_f + jf : p.epi);
+  }
   // ------------------------------------------------ LoRA epilogue pass
   // acc += S . E^T with K = rs: S = s (A_op SIDE^T) [M x rs], E [N x rs]
   // Two 16-column slices per round trip: every load of the pair is issued
@@ -505,6 +516,13 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(ea[h][i], hb[h][j], acc[i][j]);
       }
     }
+  }
+
+  if constexpr (GU) {
+    // the Ad operand settled here, where no store is in flight yet (a use in
+    // the epilogue would otherwise wait for the epilogue's own stores)
+    if (!sdh_ok) sdh = u32x4{0, 0, 0, 0};
+    asm volatile("" : "+v"(sdh));
   }
 
   if constexpr (EPI == EPI_SWIGLU_BWD_RANK) {
@@ -569,6 +587,11 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       }
       lgkm0();
       __builtin_amdgcn_wave_barrier();
+      // the quarter's loads are settled here, ahead of the row loop: a first
+      // use inside the loop's per-lane branches would leave the later rows
+      // waiting for the rows' stores as well
+      asm volatile("" ::"v"(ein[0]), "v"(ein[1]), "v"(ein[2]), "v"(ein[3]), "v"(gin[0]), "v"(gin[1]),
+                   "v"(gin[2]), "v"(gin[3]), "v"(pd), "v"(pg), "v"(pu));
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int r = it * 8 + (lane >> 3);
@@ -738,6 +761,17 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     // 16-byte chunk c (columns 4c .. 4c+3) sits at chunk c ^ (r % 16).
     char *reg = smem + wave * 16384;
     auto ep_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); };
+    // SwiGLU forward with fr_ud: the tile's share of H_d = h Ad^T.  Each wave
+    // writes its half's h [64 tokens x 32 features] as a bf16 LDS tile (4 KB
+    // past the staging regions, 64-byte rows, chunk c at c ^ (r / 4) % 4) and
+    // contracts it over its 32 features with one 16x16x32 MFMA per 16 tokens
+    // against Ad; the 4 waves of a token half then add their sums in a fixed
+    // order and write them once.
+    const bool hd_on = GU && p.fr_ud != nullptr;
+    char *const htl = smem + 8 * 16384 + wave * 4096;
+    auto ht_off = [](int r, int c) -> uint32_t { return (uint32_t)(r * 64 + ((c ^ ((r >> 2) & 3)) << 4)); };
+    const int l16 = lane & 15, g4 = lane >> 4;
+    f32x4 uhd[2][4];
   #pragma unroll
     for (int half = 0; half < 2; ++half) {
       load_eg(half);
@@ -756,6 +790,18 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           }
       lgkm0();
       __builtin_amdgcn_wave_barrier();
+      // the half's loads are settled here, ahead of the row loop: a first use
+      // inside the loop's per-lane branches would leave the later rows
+      // waiting for the rows' stores as well
+      if constexpr (EPI == EPI_SWIGLU_BWD)
+        asm volatile("" ::"v"(ein[0]), "v"(ein[1]), "v"(ein[2]), "v"(ein[3]), "v"(ein[4]), "v"(ein[5]),
+                     "v"(ein[6]), "v"(ein[7]), "v"(gin[0]), "v"(gin[1]), "v"(gin[2]), "v"(gin[3]),
+                     "v"(gin[4]), "v"(gin[5]), "v"(gin[6]), "v"(gin[7]));
+      if constexpr (EPI == EPI_STORE_NORM)
+        asm volatile("" ::"v"(nxv[0]), "v"(nxv[1]), "v"(nxv[2]), "v"(nxv[3]), "v"(nxv[4]), "v"(nxv[5]),
+                     "v"(nxv[6]), "v"(nxv[7]), "v"(nrs[0]), "v"(nrs[1]), "v"(nrs[2]), "v"(nrs[3]),
+                     "v"(nrs[4]), "v"(nrs[5]), "v"(nrs[6]), "v"(nrs[7]), "v"(nkk[0]), "v"(nkk[1]),
+                     "v"(nkk[2]), "v"(nkk[3]), "v"(nkk[4]), "v"(nkk[5]), "v"(nkk[6]), "v"(nkk[7]));
       const int mrow0 = m0 + wm * 128 + half * 64;   // token of region row 0
       if constexpr (GU) {
         // region columns 0..31: gate, 32..63: up, features tn*128 + wn*32 + c
@@ -768,6 +814,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           const int jf = tn * 128 + wn * 32 + 8 * q;
           const u32x4 e0 = lds_read16(reg, ep_off(r, 2 * q)), e1 = lds_read16(reg, ep_off(r, 2 * q + 1));
           const u32x4 g0 = lds_read16(reg, ep_off(r, 8 + 2 * q)), g1 = lds_read16(reg, ep_off(r, 9 + 2 * q));
+          u32x4 hw = {0, 0, 0, 0};
           if (m < M && jf < f) {
             float ev[8] = {__uint_as_float(e0[0]), __uint_as_float(e0[1]), __uint_as_float(e0[2]),
                            __uint_as_float(e0[3]), __uint_as_float(e1[0]), __uint_as_float(e1[1]),
@@ -783,7 +830,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
                 gv[t] *= rs;
               }
             }
-            u32x4 ew, gw, hw;
+            u32x4 ew, gw;
   #pragma unroll
             for (int t = 0; t < 4; ++t) {
               ew[t] = pack_bf16x2(ev[2 * t], ev[2 * t + 1]);
@@ -798,6 +845,15 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
             gstore16(p.G + off, gw);
             gstore16(p.H + off, hw);
           }
+          if (hd_on) lds_write16(htl, ht_off(r, q), hw);   // zeros outside M x f
+        }
+        if (hd_on) {
+          lgkm0();
+          __builtin_amdgcn_wave_barrier();
+  #pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+            uhd[half][tb] = mfma16(sdh, lds_read16(htl, ht_off(tb * 16 + l16, g4)),
+                                   f32x4{0.f, 0.f, 0.f, 0.f});
         }
       } else {
         const int q = lane & 7;                       // 8-column group
@@ -891,6 +947,30 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       }
       lgkm0();
       __builtin_amdgcn_wave_barrier();
+    }
+    if constexpr (GU) {
+      if (hd_on) {
+        // block b = 4 half + tb of wave w at w * 16 KB + (b * 64 + lane) * 16;
+        // wave (wm, wn) sums blocks 2 wn, 2 wn + 1 over the waves wn' * 2 + wm
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          *reinterpret_cast<f32x4 *>(smem + wave * 16384 + (b * 64 + lane) * 16) = uhd[b >> 2][b & 3];
+        __syncthreads();
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int b = 2 * wn + bb;
+          f32x4 sum = *reinterpret_cast<const f32x4 *>(smem + wm * 16384 + (b * 64 + lane) * 16);
+#pragma unroll
+          for (int w2 = 1; w2 < 4; ++w2) {
+            const f32x4 o =
+                *reinterpret_cast<const f32x4 *>(smem + (w2 * 2 + wm) * 16384 + (b * 64 + lane) * 16);
+            sum = f32x4{sum[0] + o[0], sum[1] + o[1], sum[2] + o[2], sum[3] + o[3]};
+          }
+          const int t = m0 + wm * 128 + (b >> 2) * 64 + (b & 3) * 16 + l16;
+          if (t < M)
+            *reinterpret_cast<f32x4 *>(p.fr_ud + ((int64_t)tn * M + t) * 16 + 4 * g4) = sum;
+        }
+      }
     }
   }
 }
