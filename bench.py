@@ -594,6 +594,15 @@ def bench_attn_mlp(args):
     Bm = {p: up(mi.B[p]) for p in mi.B}
     Xm, dYm = up(mi.X), up(mi.dY)
     del inp, att, mi
+    # frozen dense weights keep a transposed copy made once (as for the MLP
+    # workload), so the backward dX GEMMs run over W^T; the fused q/k/v
+    # backward stacks its own transposed copy per call and takes W as stored
+    keep_wt = not args.weights_as_stored
+    Wqkv = {p: Wa[p] for p in ("q", "k", "v")}   # as stored, for the folded-norm timing
+    if keep_wt:
+        Wm = {p: L.with_transpose(v) for p, v in Wm.items()}
+        for p in (("o", "q", "k", "v") if args.qkv_separate else ("o",)):
+            Wa[p] = L.with_transpose(Wa[p])
     stream = torch.cuda.current_stream()
     qkv = ("q", "k", "v")
 
@@ -641,12 +650,14 @@ def bench_attn_mlp(args):
         "config": {"workload": f"q/k/v/o LoRA projections (d={d}, d_kv={dkv}, q/k/v "
                                f"{'separate' if args.qkv_separate else 'fused'}) + LoRA-SwiGLU "
                                f"MLP (f={f}), T={T}, r={r}, alpha={alpha:g}, bf16",
-                   "config_id": 4, "T": T, "d": d, "d_kv": dkv, "f": f, "r": r},
+                   "config_id": 4, "T": T, "d": d, "d_kv": dkv, "f": f, "r": r,
+                   "base_weights": ("W and a caller-kept W^T (backward dX GEMMs read W^T)"
+                                    if keep_wt else "as stored")},
         "wall_s_timed": round(wall, 3), "flops_per_step": flops,
         "roofline": None, "cpu_baseline": None,
     }
     # the RMSNorm in front of q/k/v, fused into them against the chain (not part of value)
-    line["rmsnorm_qkv_step"] = time_norm_qkv(L, Xa, {p: Wa[p] for p in qkv}, Aa, Ba, alpha,
+    line["rmsnorm_qkv_step"] = time_norm_qkv(L, Xa, Wqkv, Aa, Ba, alpha,
                                              {p: dYa[p] for p in qkv}, stream)
     print(json.dumps(line), flush=True)
 
