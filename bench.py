@@ -98,11 +98,14 @@ PROFILED_STEPS = range(1, 5)
 
 def _step_starts(names):
     """Index of each step's first dispatch: the forward opens with k_prep
-    followed by the rank-r pass over X (or by the norm's rstd pass), after
-    the 4-bit decodes of the gate and up weights when it has them."""
+    followed by the rank-r pass over X (width 2r = 32 for the MLP workloads,
+    3r = 192 for the attention workload's fused q/k/v) or by the norm's rstd
+    pass, after the 4-bit decodes of the gate and up weights when it has
+    them."""
     out = []
     for i in range(len(names) - 1):
         if "k_prep" in names[i] and ("k_skinny_nt<32" in names[i + 1]
+                                     or "k_skinny_nt<192" in names[i + 1]
                                      or "k_rmsnorm_fwd" in names[i + 1]):
             while i > 0 and "k_dequant4(" in names[i - 1]:
                 i -= 1

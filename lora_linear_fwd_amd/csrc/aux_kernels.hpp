@@ -288,15 +288,18 @@ __device__ __forceinline__ void reduce_tn_at(const ReduceTNArgs &a, int64_t i) {
     }
   }
   if (!dst) return;
-  // four interleaved partial sums (a fixed order) keep several loads in flight
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  // eight interleaved partial sums (a fixed order) keep eight loads in flight
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int k = 0;
-  for (; k + 4 <= a.ts; k += 4) {
+  for (; k + 8 <= a.ts; k += 8) {
+    float v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s4[u] += a.part[(int64_t)(k + u) * count + i];
+    for (int u = 0; u < 8; ++u) v[u] = a.part[(int64_t)(k + u) * count + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s8[u] += v[u];
   }
-  for (int u = 0; k < a.ts; ++k, ++u) s4[u] += a.part[(int64_t)k * count + i];
-  float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  for (int u = 0; k < a.ts; ++k, ++u) s8[u] += a.part[(int64_t)k * count + i];
+  float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   s *= a.scale;
   if (a.colscale && !a.transposed) s *= bf16_to_f32(a.colscale[n]);
   const uint32_t w = pack_bf16x2(s, 0.f);
@@ -515,19 +518,24 @@ __device__ __forceinline__ void reduce_dual_u_at(const ReduceUArgs &a, int64_t i
     je = s1 ? a.nb0 + a.nb1 : a.nb0;
     ok = qo < 2 * a.r;
   }
-  // four interleaved partial sums (a fixed order) keep several loads in flight
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  // eight interleaved partial sums (a fixed order): a thread has eight loads
+  // in flight, which the long sums (one partial per 128- or 256-column tile)
+  // need to approach the HBM rate
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (ok) {
     const float *src = a.part + (int64_t)t * a.RSU + q;
     const int64_t stride = (int64_t)a.T * a.RSU;
     int jj = jb;
-    for (; jj + 4 <= je; jj += 4) {
+    for (; jj + 8 <= je; jj += 8) {
+      float v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) s4[u] += src[(int64_t)(jj + u) * stride];
+      for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(jj + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s8[u] += v[u];
     }
-    for (int u = 0; jj < je; ++jj, ++u) s4[u] += src[(int64_t)jj * stride];
+    for (int u = 0; jj < je; ++jj, ++u) s8[u] += src[(int64_t)jj * stride];
   }
-  const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  const float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   if (a.out32) a.out32[i] = a.rowscale ? s * a.rowscale[t] : s;
   if (a.outbf) {
     const uint32_t w = pack_bf16x2(a.scale * s, 0.f);

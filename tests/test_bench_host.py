@@ -119,6 +119,18 @@ def test_steps_start_at_the_forward_and_its_4bit_decodes():
         assert len(st) == len(_step([1] * 4, q4=True))
 
 
+def test_steps_of_the_attention_workload_open_at_the_fused_qkv():
+    """q/k/v forward (k_prep, then the rank-3r pass over X), o, MLP: one step
+    per q/k/v opener; the MLP's own k_prep inside the step opens nothing."""
+    one = ["k_prep", "k_skinny_nt<192, false>", "k_reduce_side", "k_lora_gemm_pp<0, false>",
+           "k_prep", "k_skinny_nt<64, false>", "k_reduce_side", "k_lora_gemm_pp<0, false>",
+           "k_prep", "k_skinny_nt<128, false>", "k_reduce_side", "k_lora_gemm_pp<1, false>",
+           "k_reduce_tn"]
+    rows = [(i, n, 0.0) for i, n in enumerate(one * 3)]
+    steps = bench._steps(rows)
+    assert [len(st) for st in steps] == [len(one)] * 3
+
+
 def test_sq_summary_medians_per_class(tmp_path):
     """Clock, TFLOP/s and MFMA-busy fraction from two counter sets."""
     dur_ns = 1_000_000                                   # 1 ms per GEMM dispatch
