@@ -979,7 +979,7 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   b.rs = RS2; b.epi = epi_d;
   b.C = (bf16_t *)Y; b.ldc = d;
   b.tiles_m = (int)cdiv(T, BM); b.tiles_n = (int)cdiv(d, BN);
-  // s h Ad^T, once per call
+  // s h Ad^T, once per call, where the gate/up epilogue did not form it
   if (!hdf)
     LORA_TRY(skinny_nt(RS2, false, T, f, h, h, f, f, nullptr, nullptr, side_d, hpart, nullptr, hbf,
                        s, st));

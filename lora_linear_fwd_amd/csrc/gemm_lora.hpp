@@ -142,6 +142,10 @@ struct GemmArgs {
   // sums over the tiles give the products.  Operands: fr_sd, fr_sg, fr_su
   // [16 x N] bf16 (Ad, Bg^T, Bu^T padded), fr_pd, fr_pg, fr_pu [16 x fr_ldp]
   // bf16 (G_d^T, H_g^T, H_u^T, zero for t >= M; fr_ldp a multiple of 64).
+  // EPI_SWIGLU_FWD(_NORM) with fr_ud (else nullptr): with h as stored, per
+  // tile of 128 features (tn < tiles_n = ceil(gu_f / 128))
+  //   fr_ud[tn][t][q]        = sum over the tile's features n of h[t][n] Ad[q][n]
+  // with fr_sd = Ad [16 x gu_f] bf16 (rows >= r zero).
   const bf16_t *fr_sd, *fr_sg, *fr_su, *fr_pd, *fr_pg, *fr_pu;
   int fr_ldp;
   float *fr_ud, *fr_ugu, *fr_vd, *fr_vgu;
