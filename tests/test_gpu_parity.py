@@ -102,6 +102,19 @@ def test_linear_q4(ws):
     check_linear(gen_linear(77, 128, 136, 16, 16.0, "bf16", seed=12, q4=True, b_std=1.0), ws=ws)
 
 
+# one token and the narrowest features the bf16 path takes (multiples of 8):
+# every GEMM, rank-r and reduction kernel runs on a single partial tile
+TINY_LINEAR = [(1, 8, 8, 1), (1, 8, 16, 2), (3, 24, 8, 5)]
+
+
+@pytest.mark.parametrize("ws", DENSE_MODES)
+@pytest.mark.parametrize("shape", TINY_LINEAR, ids=lambda s: "x".join(map(str, s)))
+def test_linear_bf16_tiny(shape, ws):
+    T, k, n, r = shape
+    log(f"linear bf16 tiny T={T} k={k} n={n} r={r} ws={ws}")
+    check_linear(gen_linear(T, k, n, r, 16.0, "bf16", seed=T + k + n + r), ws=ws)
+
+
 def test_linear_B_zero_is_base_layer():
     li = gen_linear(300, 320, 264, 16, 16.0, "bf16", seed=5)
     li.B = np.zeros_like(li.B)
@@ -222,6 +235,17 @@ def test_mlp_q4(ws):
     log(f"mlp q4 T=300 d=256 f=576 r=16 ws={ws}")
     check_mlp(gen_mlp(300, 256, 576, 16, 16.0, "bf16", seed=24, q4=True), ws=ws)
     check_mlp(gen_mlp(70, 128, 192, 16, 16.0, "bf16", seed=25, q4=True, b_std=1.0), ws=ws)
+
+
+TINY_MLP = [(1, 8, 8, 1), (2, 16, 24, 2), (5, 8, 136, 16)]
+
+
+@pytest.mark.parametrize("ws", DENSE_MODES)
+@pytest.mark.parametrize("shape", TINY_MLP, ids=lambda s: "x".join(map(str, s)))
+def test_mlp_bf16_tiny(shape, ws):
+    T, d, f, r = shape
+    log(f"mlp bf16 tiny T={T} d={d} f={f} r={r} ws={ws}")
+    check_mlp(gen_mlp(T, d, f, r, 16.0, "bf16", seed=T + d + f + r), ws=ws)
 
 
 def test_mlp_T_zero():
