@@ -152,13 +152,19 @@ struct MlpBwdPlan {
   size_t side_g, side_u, pt_d, pt_g, pt_u, part_u, part_v;
   size_t gd32, gdbf, hd32, ggu32, ggubf, hgu32, ntpart, tnpart, wbuf, cpart, nkk;
   size_t fu_d, fu_gu, fv_d, fv_gu;   // per-tile partials of the rank-fused SwiGLU' GEMM
+  size_t hsv;                        // h = silu(e) g from the SwiGLU' epilogue (wide ranks)
   size_t total;
 };
 // The down-projection backward forms the four rank-r products of the
 // backward in its SwiGLU' epilogue (EPI_SWIGLU_BWD_RANK) when the rank fits
 // one 16-wide MFMA block
 inline bool mlp_bwd_rank_fused(int64_t r) { return rs_of(r) == 16; }
-MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, bool norm = false) {
+// Wide ranks (separate rank-r passes) with the eight-wave down backward: its
+// SwiGLU' epilogue also writes h, which the two passes for H_d and dAd then
+// read instead of e and g (half the bytes, no recomputation)
+inline bool mlp_bwd_hsave(int64_t r, bool eight_wave) { return !mlp_bwd_dual(r) && eight_wave; }
+MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, bool norm = false,
+                        bool hsave = false) {
   Bump b; MlpBwdPlan p{};
   if (norm) {   // folded RMSNorm: row partials per 64-column block of the down backward
     p.cpart = b.take((size_t)cdiv(f, 256) * 4 * T * 4);
@@ -200,6 +206,7 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, 
       p.fv_gu = b.take((size_t)tm * 16 * 2 * f * 4);
     }
   } else {
+    if (hsave) p.hsv = b.take((size_t)T * f * 2);
     p.side_gu_nn = b.take((size_t)RS1 * 2 * f * 2);
     p.ntpart = b.take(std::max({nt_part_bytes(T, d, RS2), nt_part_bytes(T, d, RS1),
                                 nt_part_bytes(T, f, RS2), nt_part_bytes(T, 2 * f, RS1)}));
@@ -700,12 +707,16 @@ size_t lora_workspace_bytes(int op, int dtype, int wfmt, int64_t T, int64_t kd, 
     case LORA_OP_MLP_FWD:
       return plan_mlp_fwd(T, kd, nf, r, fwd_copy,
                           mlp_fwd_hd_fused(r) && (wfmt == LORA_W_DENSE || fwd_copy)).total;
-    case LORA_OP_MLP_BWD: return plan_mlp_bwd(T, kd, nf, r, bwd_copy).total;
+    case LORA_OP_MLP_BWD:
+      return plan_mlp_bwd(T, kd, nf, r, bwd_copy, false,
+                          mlp_bwd_hsave(r, wfmt == LORA_W_DENSE || bwd_copy)).total;
     // the folded-norm MLP takes dense weights only
     case LORA_OP_RMSNORM_MLP_FWD:
       return wfmt == LORA_W_DENSE ? plan_mlp_fwd(T, kd, nf, r, false, mlp_fwd_hd_fused(r)).total : 0;
     case LORA_OP_RMSNORM_MLP_BWD:
-      return wfmt == LORA_W_DENSE ? plan_mlp_bwd(T, kd, nf, r, false, true).total : 0;
+      return wfmt == LORA_W_DENSE
+                 ? plan_mlp_bwd(T, kd, nf, r, false, true, mlp_bwd_hsave(r, true)).total
+                 : 0;
   }
   return 0;
 }
@@ -1037,7 +1048,11 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   // 4-bit gate/up weights (the format the workspace was sized for): a decoded,
   // transposed copy per dX GEMM; dense weights are read in place (NN GEMM)
   const bool wcopy = fast && wg.q4;
-  const MlpBwdPlan pl = plan_mlp_bwd(T, d, f, r, wcopy, nf != nullptr);
+  const MlpBwdPlan pl =
+      plan_mlp_bwd(T, d, f, r, wcopy, nf != nullptr, mlp_bwd_hsave(r, !wg.q4 || wcopy));
+  // h from the down backward's epilogue: planned, and that GEMM is the
+  // eight-wave kernel (a 4-bit down weight decoded in the GEMM is not)
+  bf16_t *hsv = pl.hsv && !(wd.q4 && !wcopy) ? (bf16_t *)(w + pl.hsv) : nullptr;
   bf16_t *wt = (bf16_t *)(w + pl.wbuf);
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   bf16_t *de = (bf16_t *)(w + pl.de), *dg = (bf16_t *)(w + pl.dg);
@@ -1112,6 +1127,7 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     }
     a.rs = RS2; a.epi = epi_d_nn;
     a.Ein = eb; a.Gin = gb; a.DE = de; a.DG = dg; a.ldd = 2 * f;
+    a.H = rankf ? nullptr : hsv;
     a.hglob = gdbf;
     a.cpart = cpart;
     a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)cdiv(f, BN);
@@ -1167,6 +1183,11 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     LORA_TRY(skinny_dual(RS2, true, T, f, f, f, nullptr, nullptr, eb, gb, side_d_nt, nullptr,
                          pt_d, nullptr, part_u, part_v, r, RS2, 1.f, hd32, nullptr, s, 0,
                          (bf16_t *)dAd, nullptr, st));
+  } else if (hsv) {   // over h as the down backward's epilogue stored it
+    LORA_TRY(skinny_nt(RS2, false, T, f, hsv, hsv, f, f, nullptr, nullptr, side_d_nt, ntpart, hd32,
+                       nullptr, 1.f, st));
+    LORA_TRY(skinny_tn(RS2, false, T, f, gd32, hsv, hsv, f, f, nullptr, nullptr, tnpart, r, s, 0,
+                       (bf16_t *)dAd, nullptr, f, st));
   } else {
     LORA_TRY(skinny_nt(RS2, true, T, f, nullptr, nullptr, f, f, eb, gb, side_d_nt, ntpart, hd32,
                        nullptr, 1.f, st));

@@ -100,7 +100,8 @@ struct GemmArgs {
   int accumulate;               // EPI_STORE: C += result
   bf16_t *C;
   int64_t ldc;
-  bf16_t *E, *G, *H;            // SwiGLU forward outputs [M x f]
+  bf16_t *E, *G, *H;            // SwiGLU forward outputs [M x f]; eight-wave
+                                // EPI_SWIGLU_BWD: H (optional) gets h = silu(e) g [M x N]
   const bf16_t *Ein, *Gin;      // SwiGLU backward saved activations [M x N]
   bf16_t *DE, *DG;              // SwiGLU backward outputs [M x N], row stride ldd
   int64_t ldd;

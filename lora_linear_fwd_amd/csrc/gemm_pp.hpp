@@ -911,10 +911,10 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
             float csum = 0.f;
             if (valid) {
               const u32x4 ev = ein[it], gv = gin[it];
-              u32x4 dew, dgw;
+              u32x4 dew, dgw, hw;
   #pragma unroll
               for (int t = 0; t < 4; ++t) {
-                float de[2], dg[2];
+                float de[2], dg[2], hh[2];
   #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                   const float e = h2 ? bf16hi(ev[t]) : bf16lo(ev[t]);
@@ -923,9 +923,11 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
                   const float sg = sigmoidf_fast(e);
                   dg[h2] = dh * e * sg;
                   de[h2] = dh * gg * sg * (1.0f + e * (1.0f - sg));
+                  hh[h2] = e * sg * gg;
                 }
                 dew[t] = pack_bf16x2(de[0], de[1]);
                 dgw[t] = pack_bf16x2(dg[0], dg[1]);
+                hw[t] = pack_bf16x2(hh[0], hh[1]);
                 // de e + dg g with de, dg as stored (a folded RMSNorm's row
                 // coefficient; unused otherwise)
                 if (p.cpart)
@@ -935,6 +937,9 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
               const int64_t doff = (int64_t)m * p.ldd + n;
               gstore16_nt(p.DE + doff, dew);
               gstore16_nt(p.DG + doff, dgw);
+              // h = silu(e) g for the rank-r passes that follow (read again
+              // right after: a plain store)
+              if (p.H) gstore16(p.H + (int64_t)m * N + n, hw);
             }
             if (p.cpart) {
               // the 8 lanes of one row (lanes 8j .. 8j+7) add their sums in a
