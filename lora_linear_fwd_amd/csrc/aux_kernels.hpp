@@ -150,6 +150,12 @@ struct SkinnyTNArgs {
 template <int RS, bool ZSWIGLU>
 __global__ __launch_bounds__(256) void k_skinny_tn(const SkinnyTNArgs a) {
   constexpr int NQB = RS / 16;
+  // Wide ranks run one wave per SIMD (the accumulators take the register
+  // file), so the loop is latency-bound unless the next step's Z rows are in
+  // flight during the current step's contractions: those instances keep the
+  // raw loads of step t0 + 64 in registers across the step.
+  constexpr bool PF = RS >= 64;
+  constexpr int NZ = ZSWIGLU ? 2 : 1;        // loaded vectors per row: e, g or z
   __shared__ __attribute__((aligned(16))) char zs[256 * 128];
   __shared__ __attribute__((aligned(16))) char ps[RS * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -163,50 +169,85 @@ __global__ __launch_bounds__(256) void k_skinny_tn(const SkinnyTNArgs a) {
 #pragma unroll
     for (int j = 0; j < NQB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int kb = tid >> 5, nb = tid & 31;
-  for (int t0 = tbeg; t0 < tend; t0 += 64) {
-    u32x4 rows[8], cols[8];
+  // the raw 16-byte pieces of the thread's 8 rows of step t0 (zero outside)
+  auto load_rows = [&](int t0, u32x4 (&raw)[NZ][8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = t0 + kb * 8 + i, n = n0 + nb * 8;
-      u32x4 v = {0, 0, 0, 0};
+      u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
       if (t < tend && n < a.N) {
         if constexpr (ZSWIGLU) {
-          const u32x4 e = gload16(a.E + (int64_t)t * a.ldz + n);
-          const u32x4 g = gload16(a.G + (int64_t)t * a.ldz + n);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float e0 = bf16lo(e[w]), e1 = bf16hi(e[w]);
-            v[w] = pack_bf16x2(e0 * sigmoidf_fast(e0) * bf16lo(g[w]),
-                               e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
-          }
+          v0 = gload16(a.E + (int64_t)t * a.ldz + n);
+          v1 = gload16(a.G + (int64_t)t * a.ldz + n);
         } else {
           const bf16_t *src = n < a.nsplit ? a.Z0 + (int64_t)t * a.ldz + n
                                            : a.Z1 + (int64_t)t * a.ldz + (n - a.nsplit);
-          v = gload16(src);
+          v0 = gload16(src);
         }
       }
-      rows[i] = v;
+      raw[0][i] = v0;
+      if constexpr (ZSWIGLU) raw[NZ - 1][i] = v1;
     }
-    transpose8x8(rows, cols);
-    // P tile [64 tokens x RS] fp32 in units of 4 tokens x 4 ranks: four
-    // 16-byte row loads, transposed into four 8-byte runs of 4 tokens
-    constexpr int NPU = (RS * 4 + 255) / 256;   // units per thread
-    u32x2 pv[NPU][4];
+  };
+  // P tile [64 tokens x RS] fp32 in units of 4 tokens x 4 ranks: four
+  // 16-byte row loads per unit, later transposed into four 8-byte runs of 4
+  // tokens
+  constexpr int NPU = (RS * 4 + 255) / 256;   // units per thread
+  auto load_p = [&](int t0, f32x4 (&pr)[NPU][4]) {
 #pragma unroll
     for (int u = 0; u < NPU; ++u) {
       const int idx = tid + 256 * u;
       const int qq = idx >> 4, tq = idx & 15;   // rank quad, token quad
-      f32x4 pr[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const int t = t0 + 4 * tq + h;
-        pr[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pr[u][h] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (qq < RS / 4 && t < tend)
-          pr[h] = *reinterpret_cast<const f32x4 *>(a.P + (int64_t)t * RS + 4 * qq);
+          pr[u][h] = *reinterpret_cast<const f32x4 *>(a.P + (int64_t)t * RS + 4 * qq);
       }
+    }
+  };
+  u32x4 raw[NZ][8];
+  f32x4 pr[NPU][4];
+  if constexpr (PF) {
+    if (tbeg < tend) {
+      load_rows(tbeg, raw);
+      load_p(tbeg, pr);
+    }
+  }
+  for (int t0 = tbeg; t0 < tend; t0 += 64) {
+    if constexpr (!PF) {
+      load_rows(t0, raw);
+      load_p(t0, pr);
+    }
+    u32x4 rows[8], cols[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (ZSWIGLU) {
+        const u32x4 e = raw[0][i], g = raw[NZ - 1][i];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = bf16lo(e[w]), e1 = bf16hi(e[w]);
+          rows[i][w] = pack_bf16x2(e0 * sigmoidf_fast(e0) * bf16lo(g[w]),
+                                   e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
+        }
+      } else {
+        rows[i] = raw[0][i];
+      }
+    }
+    transpose8x8(rows, cols);
+    u32x2 pv[NPU][4];
+#pragma unroll
+    for (int u = 0; u < NPU; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        pv[u][i] = u32x2{pack_bf16x2(pr[0][i], pr[1][i]), pack_bf16x2(pr[2][i], pr[3][i])};
+        pv[u][i] = u32x2{pack_bf16x2(pr[u][0][i], pr[u][1][i]), pack_bf16x2(pr[u][2][i], pr[u][3][i])};
+    // the next step's operands, in flight during this step's contractions
+    if constexpr (PF) {
+      if (t0 + 64 < tend) {
+        load_rows(t0 + 64, raw);
+        load_p(t0 + 64, pr);
+      }
     }
     __syncthreads();
 #pragma unroll
