@@ -239,6 +239,11 @@ QkvFwdPlan plan_qkv_fwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r
   return p;
 }
 struct QkvBwdPlan { size_t dyc, side_nn, epi_nn, side_nt, g32, gbf, h32, ntpart, tnpart, wbuf, gn, total; };
+// The products with dQ, dK, dV (G and dB) are block-diagonal in the rank:
+// with r a multiple of 16 each block is its own rank-r pass over its own
+// gradient (a third of the contraction work of one 3r-wide pass each, and no
+// packed [dQ | dK | dV] for them)
+inline bool qkv_bwd_segmented(int64_t r) { return r % 16 == 0; }
 // norm: an RMSNorm folded into the projections (lora_rmsnorm_qkv_bwd) adds a
 // [T x k] bf16 buffer for the projections' input gradient
 QkvBwdPlan plan_qkv_bwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r,
@@ -255,8 +260,14 @@ QkvBwdPlan plan_qkv_bwd(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t r
   p.g32 = b.take((size_t)T * RS3 * 4);
   p.gbf = b.take((size_t)T * RS3 * 2);
   p.h32 = b.take((size_t)T * RS3 * 4);
-  p.ntpart = b.take(std::max(nt_part_bytes(T, N, RS3), nt_part_bytes(T, k, RS3)));
-  p.tnpart = b.take(std::max(tn_part_bytes(T, k, RS3), tn_part_bytes(T, N, RS3)));
+  size_t ntb = std::max(nt_part_bytes(T, N, RS3), nt_part_bytes(T, k, RS3));
+  size_t tnb = std::max(tn_part_bytes(T, k, RS3), tn_part_bytes(T, N, RS3));
+  if (qkv_bwd_segmented(r)) {
+    ntb = std::max({ntb, nt_part_bytes(T, nq, (int)r), nt_part_bytes(T, nkv, (int)r)});
+    tnb = std::max({tnb, tn_part_bytes(T, nq, (int)r), tn_part_bytes(T, nkv, (int)r)});
+  }
+  p.ntpart = b.take(ntb);
+  p.tnpart = b.take(tnb);
   p.total = b.cur;
   return p;
 }
@@ -407,13 +418,16 @@ struct Prep {
 };
 
 // out = Z . SIDE^T over all K (deterministic split-K); fp32 and/or scaled bf16
+// side [RS x K] with row stride lds (0: K); outputs [T x RS] with row
+// stride ldo (0: RS)
 int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, const bf16_t *Z1,
               int64_t ksplit, int64_t ldz, const bf16_t *E, const bf16_t *G, const bf16_t *side,
               float *part, float *out32, bf16_t *outbf, float scale, hipStream_t st,
-              const float *rowscale = nullptr) {
+              const float *rowscale = nullptr, int64_t lds = 0, int ldo = 0) {
   if (T == 0) return LORA_OK;
   const NTSplit sp = nt_split(T, K);
-  SkinnyNTArgs a{(int)T, (int)K, (int)ksplit, sp.kchunk, Z0, Z1, ldz, E, G, side, part};
+  SkinnyNTArgs a{(int)T, (int)K, (int)ksplit, sp.kchunk, Z0, Z1, ldz, E, G, side, part,
+                 lds ? lds : K};
   dim3 grid((unsigned)cdiv(T, 64), (unsigned)sp.ks);
 #define SNT(R)                                                                          \
   case R:                                                                               \
@@ -429,7 +443,7 @@ int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, cons
   HIP_TRY(hipGetLastError());
   const int64_t cnt = T * RS;
   hipLaunchKernelGGL(k_reduce_side, dim3(blocks_for(cnt)), dim3(256), 0, st, part, sp.ks, cnt,
-                     scale, out32, outbf, rowscale, RS);
+                     scale, out32, outbf, rowscale, RS, ldo ? ldo : RS);
   HIP_TRY(hipGetLastError());
   return LORA_OK;
 }
@@ -439,9 +453,10 @@ int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const 
               const bf16_t *Z1, int64_t nsplit, int64_t ldz, const bf16_t *E, const bf16_t *G,
               float *part, int64_t r, float scale, int transposed, bf16_t *out0, bf16_t *out1,
               int64_t out_nsplit, hipStream_t st, bf16_t *out2 = nullptr,
-              int64_t out_nsplit2 = 0, const bf16_t *colscale = nullptr) {
+              int64_t out_nsplit2 = 0, const bf16_t *colscale = nullptr, int64_t ldp = 0) {
   const TNSplit sp = tn_split(T, N);
-  SkinnyTNArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, P, Z0, Z1, ldz, E, G, part};
+  SkinnyTNArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, P, Z0, Z1, ldz, E, G, part,
+                 ldp ? ldp : RS};
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)sp.ts);
 #define STN(R)                                                                          \
   case R:                                                                               \
@@ -1461,6 +1476,10 @@ static int qkv_bwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t 
   float *g32 = (float *)(w + pl.g32), *h32 = (float *)(w + pl.h32);
   float *ntpart = (float *)(w + pl.ntpart), *tnpart = (float *)(w + pl.tnpart);
   const bf16_t *Xb = (const bf16_t *)X;
+  // the three gradients as they are, their widths and first columns in [dQ | dK | dV]
+  const bool seg = qkv_bwd_segmented(r);
+  const bf16_t *sd[3] = {(const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV};
+  const int64_t sn[3] = {nq, nkv, nkv}, sc[3] = {0, nq, nq + nkv};
   Prep prep;
   prep.side(side_nn, RS3, N, Bq, Bk, r, nq, 1, Bv, nq + nkv);       // blockdiag(Bq,Bk,Bv)^T
   // [Aq; Ak; Av]^T and [Aq; Ak; Av], times diag(w) under a folded norm
@@ -1468,15 +1487,25 @@ static int qkv_bwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t 
   prep.side(side_nt, RS3, k, Aq, Ak, r, k, 0, Av, k, nw);
   LORA_TRY(prep.launch(st));
   if (T > 0) {
-    // [dQ | dK | dV] as one [T x N] operand
-    hipLaunchKernelGGL(k_concat3, dim3(blocks_for(T * (N / 8))), dim3(256), 0, st,
-                       (const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV, (int)nq,
-                       (int)nkv, (int)nkv, T, dyc);
-    HIP_TRY(hipGetLastError());
+    // [dQ | dK | dV] as one [T x N] operand (for the dX GEMM, and for the
+    // rank passes unless they run block by block)
+    if (dX || !seg) {
+      hipLaunchKernelGGL(k_concat3, dim3(blocks_for(T * (N / 8))), dim3(256), 0, st,
+                         (const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV, (int)nq,
+                         (int)nkv, (int)nkv, T, dyc);
+      HIP_TRY(hipGetLastError());
+    }
     // G = [dQ Bq | dK Bk | dV Bv] (fp32 for dA, rows times rstd under a
     // folded norm; s G in bf16 for the dX epilogue)
-    LORA_TRY(skinny_nt(RS3, false, T, N, dyc, dyc, N, N, nullptr, nullptr, side_nn, ntpart, g32,
-                       gbf, s, st, rstd));
+    if (seg) {   // block by block: the rows of blockdiag(Bq, Bk, Bv)^T that are not zero
+      for (int j = 0; j < 3; ++j)
+        LORA_TRY(skinny_nt((int)r, false, T, sn[j], sd[j], sd[j], sn[j], sn[j], nullptr, nullptr,
+                           side_nn + (int64_t)j * r * N + sc[j], ntpart, g32 + j * r, gbf + j * r, s,
+                           st, rstd, N, RS3));
+    } else {
+      LORA_TRY(skinny_nt(RS3, false, T, N, dyc, dyc, N, N, nullptr, nullptr, side_nn, ntpart, g32,
+                         gbf, s, st, rstd));
+    }
     if (dX) {
       // dX (+)= [dQ | dK | dV] [Wq; Wk; Wv] + s G [Aq; Ak; Av]: one GEMM, K = N
       LORA_TRY(transpose_w(wt, N, wq, nq, k, st));
@@ -1509,8 +1538,16 @@ static int qkv_bwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t 
   //   (folded norm: G rows scaled by rstd, the result's columns by w)
   LORA_TRY(skinny_tn(RS3, false, T, k, g32, Xb, Xb, k, k, nullptr, nullptr, tnpart, r, s, 0,
                      (bf16_t *)dAq, (bf16_t *)dAk, k, st, (bf16_t *)dAv, 0, nw));
-  LORA_TRY(skinny_tn(RS3, false, T, N, h32, dyc, dyc, N, N, nullptr, nullptr, tnpart, r, s, 1,
-                     (bf16_t *)dBq, (bf16_t *)dBk, nq, st, (bf16_t *)dBv, nq + nkv));
+  if (seg) {   // dB_j = s dY_j^T H_j, each over its own gradient and rank block of H
+    bf16_t *dBs[3] = {(bf16_t *)dBq, (bf16_t *)dBk, (bf16_t *)dBv};
+    for (int j = 0; j < 3; ++j)
+      LORA_TRY(skinny_tn((int)r, false, T, sn[j], h32 + j * r, sd[j], sd[j], sn[j], sn[j], nullptr,
+                         nullptr, tnpart, r, s, 1, dBs[j], nullptr, sn[j], st, nullptr, 0, nullptr,
+                         RS3));
+  } else {
+    LORA_TRY(skinny_tn(RS3, false, T, N, h32, dyc, dyc, N, N, nullptr, nullptr, tnpart, r, s, 1,
+                       (bf16_t *)dBq, (bf16_t *)dBk, nq, st, (bf16_t *)dBv, nq + nkv));
+  }
   return LORA_OK;
 }
 

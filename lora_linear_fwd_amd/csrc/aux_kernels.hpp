@@ -18,8 +18,9 @@ struct SkinnyNTArgs {
   const bf16_t *Z0, *Z1;
   int64_t ldz;
   const bf16_t *E, *G;      // ZSWIGLU sources, ld = ldz
-  const bf16_t *side;       // [RS x K]
+  const bf16_t *side;       // [RS x K], row stride lds (>= K)
   float *part;              // [KS x T x RS]
+  int64_t lds;
 };
 
 // Block: 64 tokens x one K chunk, stepping 128 columns at a time.  Each
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
     for (int i = 0; i < SL; ++i) {
       const int q = rb + 16 * i;
       u32x4 v = {0, 0, 0, 0};
-      if (kin && q < RS) v = gload16(a.side + (int64_t)q * a.K + k);
+      if (kin && q < RS) v = gload16(a.side + (int64_t)q * a.lds + k);
       sr[i] = v;
     }
   };
@@ -115,19 +116,22 @@ __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
   }
 }
 
-// out32[i] = sum_ks part[ks][i] (fixed order); outbf[i] = bf16(scale * out32[i]).
-// With rowscale (rows of RS values), out32 is multiplied by rowscale[i / RS]
-// (the bf16 copy is not).
+// For i = t RS + q: out32[t ldo + q] = sum_ks part[ks][i] (fixed order),
+// outbf[t ldo + q] = bf16(scale * that sum) (ldo = RS: the [T x RS] layout;
+// larger: a column slice of a wider output).  With rowscale, out32 is
+// multiplied by rowscale[t] (the bf16 copy is not).
 __global__ void k_reduce_side(const float *part, int ks, int64_t count, float scale,
-                              float *out32, bf16_t *outbf, const float *rowscale, int RS) {
+                              float *out32, bf16_t *outbf, const float *rowscale, int RS,
+                              int ldo) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   float s = 0.f;
   for (int k = 0; k < ks; ++k) s += part[(int64_t)k * count + i];
-  if (out32) out32[i] = rowscale ? s * rowscale[i / RS] : s;
+  const int64_t t = i / RS, o = t * ldo + (i - t * RS);
+  if (out32) out32[o] = rowscale ? s * rowscale[t] : s;
   if (outbf) {
     const uint32_t w = pack_bf16x2(scale * s, 0.f);
-    outbf[i] = (bf16_t)(w & 0xFFFFu);
+    outbf[o] = (bf16_t)(w & 0xFFFFu);
   }
 }
 
@@ -140,11 +144,12 @@ __global__ void k_reduce_side(const float *part, int ks, int64_t count, float sc
 // ---------------------------------------------------------------------------
 struct SkinnyTNArgs {
   int T, N, nsplit, tchunk;
-  const float *P;
+  const float *P;           // [T x RS], row stride ldp (>= RS)
   const bf16_t *Z0, *Z1;
   int64_t ldz;
   const bf16_t *E, *G;
   float *part;              // [TS x RS x N]
+  int64_t ldp;
 };
 
 template <int RS, bool ZSWIGLU>
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(256) void k_skinny_tn(const SkinnyTNArgs a) {
         const int t = t0 + 4 * tq + h;
         pr[u][h] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (qq < RS / 4 && t < tend)
-          pr[u][h] = *reinterpret_cast<const f32x4 *>(a.P + (int64_t)t * RS + 4 * qq);
+          pr[u][h] = *reinterpret_cast<const f32x4 *>(a.P + (int64_t)t * a.ldp + 4 * qq);
       }
     }
   };
