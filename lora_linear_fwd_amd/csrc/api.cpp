@@ -1410,6 +1410,7 @@ static int qkv_fwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t 
   a.B0 = wq.w; a.B1 = wk.w; a.B2 = wv.w; a.ldb = k;
   a.nseg1 = (int)nq; a.nseg2 = (int)(nq + nkv);
   a.rs = RS3; a.epi = epi; a.hglob = hbf;
+  if (r % 16 == 0) a.rs_seg = (int)r;   // blockdiag(Bq, Bk, Bv): one block per tile
   if (nf) a.rowscale = nf->rstd;
   a.C = (bf16_t *)Q; a.ldc = nq;
   a.C1 = (bf16_t *)K; a.ldc1 = nkv;

@@ -475,13 +475,22 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   // acc += S . E^T with K = rs: S = s (A_op SIDE^T) [M x rs], E [N x rs]
   // Two 16-column slices per round trip: every load of the pair is issued
   // before its MFMAs (the fragment registers are free by now).
-  const int rs = p.rs, nq = rs / 16;
-  for (int kq0 = 0; kq0 < nq; kq0 += 2) {
+  // With rs_seg (fused q/k/v, rank blocks of whole 16-column groups) the
+  // epilogue operand is block-diagonal: a tile's columns lie in one
+  // projection, whose rows of it are zero outside that projection's block
+  const int rs = p.rs;
+  int kqb = 0, kqe = rs / 16;
+  if (p.rs_seg > 0) {
+    const int sgi = (p.nseg2 > 0 && n0 >= p.nseg2) ? 2 : (n0 >= p.nseg1 ? 1 : 0);
+    kqb = sgi * (p.rs_seg / 16);
+    kqe = kqb + p.rs_seg / 16;
+  }
+  for (int kq0 = kqb; kq0 < kqe; kq0 += 2) {
     u32x4 ea[2][2], hb[2][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kq = kq0 + h;
-      const bool qok = kq < nq;
+      const bool qok = kq < kqe;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         int64_t erow;
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (kq0 + h < nq) {
+      if (kq0 + h < kqe) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
