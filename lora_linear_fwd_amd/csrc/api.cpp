@@ -393,7 +393,8 @@ struct Prep {
     j = PrepJob{dst, (const bf16_t *)src0, (const bf16_t *)src1, (const bf16_t *)src2, kind,
                 (int)a, (int)bb, (int)r, (int)split, (int)split2, tr, (const bf16_t *)cs};
     b.start[b.njobs] = blocks;
-    blocks += (unsigned)cdiv(cnt, 256);
+    // 8 elements per thread for rows of a multiple of 8 (see k_prep)
+    blocks += (unsigned)cdiv(bb % 8 == 0 ? cnt / 8 : cnt, 256);
     ++b.njobs;
   }
   // side[q][k], q < RS, k < K

@@ -666,12 +666,7 @@ struct PrepBatch {
   unsigned start[kMaxPrepJobs + 1];
   int njobs;
 };
-__global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
-  int j = 0;
-  while (j + 1 < pb.njobs && blockIdx.x >= pb.start[j + 1]) ++j;
-  const PrepJob &jb = pb.job[j];
-  const int64_t i = (int64_t)(blockIdx.x - pb.start[j]) * 256 + threadIdx.x;
-  if (i >= (int64_t)jb.a * jb.b) return;
+__device__ __forceinline__ bf16_t prep_at(const PrepJob &jb, int64_t i) {
   const int r = jb.r;
   const bf16_t *src[3] = {jb.src0, jb.src1, jb.src2};
   bf16_t v = 0;
@@ -704,7 +699,28 @@ __global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
       }
     }
   }
-  jb.dst[i] = v;
+  return v;
+}
+// A thread writes 8 consecutive elements of a row (one 16-byte store) when
+// the row length b is a multiple of 8, else one element.
+__global__ __launch_bounds__(256) void k_prep(const PrepBatch pb) {
+  int j = 0;
+  while (j + 1 < pb.njobs && blockIdx.x >= pb.start[j + 1]) ++j;
+  const PrepJob &jb = pb.job[j];
+  const int64_t u = (int64_t)(blockIdx.x - pb.start[j]) * 256 + threadIdx.x;
+  const int64_t cnt = (int64_t)jb.a * jb.b;
+  if (jb.b % 8 == 0) {
+    const int64_t i = u * 8;
+    if (i >= cnt) return;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)prep_at(jb, i + 2 * e) | ((uint32_t)prep_at(jb, i + 2 * e + 1) << 16);
+    gstore16(jb.dst + i, u32x4{w[0], w[1], w[2], w[3]});
+  } else {
+    if (u >= cnt) return;
+    jb.dst[u] = prep_at(jb, u);
+  }
 }
 
 // ---------------------------------------------------------------------------
