@@ -163,6 +163,10 @@ inline bool mlp_bwd_rank_fused(int64_t r) { return rs_of(r) == 16; }
 // SwiGLU' epilogue also writes h, which the two passes for H_d and dAd then
 // read instead of e and g (half the bytes, no recomputation)
 inline bool mlp_bwd_hsave(int64_t r, bool eight_wave) { return !mlp_bwd_dual(r) && eight_wave; }
+// Wide ranks that fill whole 16-column groups: G_gu and dBg, dBu are
+// block-diagonal in the rank (de pairs with Bg and H_g, dg with Bu and H_u),
+// so they run as two r-wide passes instead of one 2r-wide pass over [de | dg]
+inline bool mlp_bwd_gu_segmented(int64_t r) { return !mlp_bwd_dual(r) && r % 16 == 0; }
 MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, bool norm = false,
                         bool hsave = false) {
   Bump b; MlpBwdPlan p{};
@@ -208,6 +212,7 @@ MlpBwdPlan plan_mlp_bwd(int64_t T, int64_t d, int64_t f, int64_t r, bool wcopy, 
   } else {
     if (hsave) p.hsv = b.take((size_t)T * f * 2);
     p.side_gu_nn = b.take((size_t)RS1 * 2 * f * 2);
+    // (the r-wide passes of the segmented form are within the f-wide sizes)
     p.ntpart = b.take(std::max({nt_part_bytes(T, d, RS2), nt_part_bytes(T, d, RS1),
                                 nt_part_bytes(T, f, RS2), nt_part_bytes(T, 2 * f, RS1)}));
     p.tnpart = b.take(std::max({tn_part_bytes(T, d, RS2), tn_part_bytes(T, d, RS1),
@@ -1230,6 +1235,19 @@ static int mlp_bwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
     LORA_TRY(skinny_dual(RS2, false, T, 2 * f, f, 2 * f, de, dg, nullptr, nullptr, side_g, side_u,
                          pt_g, pt_u, part_u, part_v, r, RS1, s, ggu32, ggubf, s, 1, (bf16_t *)dBg,
                          (bf16_t *)dBu, st, rstd));
+  } else if (mlp_bwd_gu_segmented(r)) {
+    // block-diagonal in the rank: de with Bg and H_g, dg with Bu and H_u,
+    // each an r-wide pass over its half of [de | dg]
+    const bf16_t *zs[2] = {de, dg};
+    bf16_t *dbs[2] = {(bf16_t *)dBg, (bf16_t *)dBu};
+    for (int j = 0; j < 2; ++j) {
+      if (T > 0)
+        LORA_TRY(skinny_nt((int)r, false, T, f, zs[j], zs[j], f, 2 * f, nullptr, nullptr,
+                           side_gu_nn + (int64_t)j * r * 2 * f + j * f, ntpart, ggu32 + j * r,
+                           ggubf + j * r, s, st, rstd, 2 * f, RS1));
+      LORA_TRY(skinny_tn((int)r, false, T, f, hgu32 + j * r, zs[j], zs[j], f, 2 * f, nullptr, nullptr,
+                         tnpart, r, s, 1, dbs[j], nullptr, f, st, nullptr, 0, nullptr, RS1));
+    }
   } else {
     if (T > 0)
       LORA_TRY(skinny_nt(RS1, false, T, 2 * f, de, dg, f, 2 * f, nullptr, nullptr, side_gu_nn, ntpart,

@@ -204,6 +204,7 @@ MLP_SHAPES = [
     (200, 192, 392, 24),    # 16 < r <= 32: the dual rank-r passes, not the fused epilogue
     (130, 256, 512, 32),
     (70, 64, 136, 128),     # widest side operands (2 r = 256)
+    (130, 128, 200, 40),    # wide rank not a multiple of 16: one 2r-wide pass over [de | dg]
 ]
 
 
