@@ -987,6 +987,7 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   if (nf) a.rowscale = nf->rstd;
   a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)gu_tiles_n(f);
   if (hdf) { a.fr_sd = side_d; a.fr_ud = hpart; }
+  if (r % 16 == 0) a.rs_seg = (int)r;   // blockdiag(Bg, Bu): gate and up rows one block each
   // [s X Ag^T | s X Au^T], once per call
   LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
                      hbf, s, st));

@@ -111,9 +111,10 @@ struct GemmArgs {
   // [nseg2, N) B2 / C2; boundaries are multiples of the 256-column tile.
   // nseg1 = 0: one segment.
   int nseg1, nseg2;
-  // eight-wave kernel, nseg1 > 0: the epilogue operand is block-diagonal with
-  // rs_seg columns per segment (a multiple of 16), and a tile of segment j
-  // runs the LoRA pass over columns [j rs_seg, (j + 1) rs_seg) only; 0: all rs
+  // eight-wave kernel: the epilogue operand is block-diagonal with rs_seg
+  // columns per block (a multiple of 16).  nseg1 > 0: a tile of segment j
+  // runs the LoRA pass over columns [j rs_seg, (j + 1) rs_seg) only; SwiGLU
+  // forward: gate rows over block 0, up rows over block 1.  0: all rs columns
   int rs_seg;
   const bf16_t *B2;
   bf16_t *C1, *C2;

@@ -475,16 +475,20 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   // acc += S . E^T with K = rs: S = s (A_op SIDE^T) [M x rs], E [N x rs]
   // Two 16-column slices per round trip: every load of the pair is issued
   // before its MFMAs (the fragment registers are free by now).
-  // With rs_seg (fused q/k/v, rank blocks of whole 16-column groups) the
-  // epilogue operand is block-diagonal: a tile's columns lie in one
-  // projection, whose rows of it are zero outside that projection's block
+  // With rs_seg (rank blocks of whole 16-column groups) the epilogue operand
+  // is block-diagonal.  Fused q/k/v: a tile's columns lie in one projection,
+  // whose rows of it are zero outside that projection's block.  Gate/up: the
+  // gate rows (i = 0) are zero outside block 0, the up rows outside block 1.
   const int rs = p.rs;
   int kqb = 0, kqe = rs / 16;
-  if (p.rs_seg > 0) {
+  const int kqs = GU ? p.rs_seg / 16 : 0;   // gate/up: first column group of block 1
+  if (!GU && p.rs_seg > 0) {
     const int sgi = (p.nseg2 > 0 && n0 >= p.nseg2) ? 2 : (n0 >= p.nseg1 ? 1 : 0);
     kqb = sgi * (p.rs_seg / 16);
     kqe = kqb + p.rs_seg / 16;
   }
+  // gate/up with blocks: does row group i take column group kq
+  auto gu_takes = [&](int i, int kq) { return kqs == 0 || (kq < kqs) == (i == 0); };
   for (int kq0 = kqb; kq0 < kqe; kq0 += 2) {
     u32x4 ea[2][2], hb[2][4];
 #pragma unroll
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
           erow = n;
         }
         u32x4 v = {0, 0, 0, 0};
-        if (ok && qok) v = gload16(p.epi + erow * rs + kq * 16 + 8 * hi32);
+        if (ok && qok && gu_takes(i, kq)) v = gload16(p.epi + erow * rs + kq * 16 + 8 * hi32);
         ea[h][i] = v;
       }
 #pragma unroll
@@ -520,9 +524,11 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
     for (int h = 0; h < 2; ++h) {
       if (kq0 + h < kqe) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+          if (!gu_takes(i, kq0 + h)) continue;
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(ea[h][i], hb[h][j], acc[i][j]);
+        }
       }
     }
   }
