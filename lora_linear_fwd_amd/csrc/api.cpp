@@ -51,9 +51,13 @@ inline NTSplit nt_split(int64_t T, int64_t K) {
   return {(int)ks, (int)kchunk};
 }
 struct TNSplit { int ts; int tchunk; };
-inline TNSplit tn_split(int64_t T, int64_t N) {
+// Token chunks so that the grid about fills the workgroups resident at once:
+// four per CU for narrow ranks, fewer where the accumulators take the
+// register file (two per CU from 64 rank columns, one from 128)
+inline TNSplit tn_split(int64_t T, int64_t N, int RS) {
   const int64_t gx = cdiv(N, 256);
-  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, gx), cdiv(T, 64)));
+  const int64_t slots = RS >= 128 ? 256 : (RS >= 64 ? 512 : 1024);
+  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(slots, gx), cdiv(T, 64)));
   int64_t tchunk = std::max<int64_t>(64, cdiv(cdiv(T, ts), 64) * 64);
   ts = std::max<int64_t>(1, cdiv(T, tchunk));
   return {(int)ts, (int)tchunk};
@@ -62,7 +66,7 @@ inline size_t nt_part_bytes(int64_t T, int64_t K, int RS) {
   return (size_t)nt_split(T, K).ks * T * RS * 4;
 }
 inline size_t tn_part_bytes(int64_t T, int64_t N, int RS) {
-  return (size_t)tn_split(T, N).ts * RS * N * 4;
+  return (size_t)tn_split(T, N, RS).ts * RS * N * 4;
 }
 // dual pass: 256-column blocks per segment x token chunks (multiples of 64)
 struct DualSplit { int nb0, nb1, ts, tchunk; };
@@ -460,7 +464,7 @@ int skinny_tn(int RS, bool zswiglu, int64_t T, int64_t N, const float *P, const 
               float *part, int64_t r, float scale, int transposed, bf16_t *out0, bf16_t *out1,
               int64_t out_nsplit, hipStream_t st, bf16_t *out2 = nullptr,
               int64_t out_nsplit2 = 0, const bf16_t *colscale = nullptr, int64_t ldp = 0) {
-  const TNSplit sp = tn_split(T, N);
+  const TNSplit sp = tn_split(T, N, RS);
   SkinnyTNArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, P, Z0, Z1, ldz, E, G, part,
                  ldp ? ldp : RS};
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)sp.ts);
