@@ -40,12 +40,13 @@ struct Bump {
 
 // split choices shared by the planner and the launchers
 struct NTSplit { int ks; int kchunk; };
-#ifndef LORA_NT_SLOTS
-#define LORA_NT_SLOTS 1024
-#endif
-inline NTSplit nt_split(int64_t T, int64_t K) {
+// K chunks so that the grid about fills the workgroups resident at once for
+// the rank width (the skinny NT kernel's occupancy falls from four
+// workgroups per CU at narrow ranks to one at the widest)
+inline NTSplit nt_split(int64_t T, int64_t K, int RS) {
   const int64_t gx = std::max<int64_t>(1, cdiv(T, 64));
-  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(LORA_NT_SLOTS, gx), cdiv(K, 512)));
+  const int64_t slots = RS >= 208 ? 256 : (RS >= 128 ? 512 : (RS >= 80 ? 768 : 1024));
+  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(slots, gx), cdiv(K, 512)));
   int64_t kchunk = cdiv(cdiv(K, ks), 128) * 128;
   ks = std::max<int64_t>(1, cdiv(K, kchunk));
   return {(int)ks, (int)kchunk};
@@ -63,7 +64,7 @@ inline TNSplit tn_split(int64_t T, int64_t N, int RS) {
   return {(int)ts, (int)tchunk};
 }
 inline size_t nt_part_bytes(int64_t T, int64_t K, int RS) {
-  return (size_t)nt_split(T, K).ks * T * RS * 4;
+  return (size_t)nt_split(T, K, RS).ks * T * RS * 4;
 }
 inline size_t tn_part_bytes(int64_t T, int64_t N, int RS) {
   return (size_t)tn_split(T, N, RS).ts * RS * N * 4;
@@ -435,7 +436,7 @@ int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, cons
               float *part, float *out32, bf16_t *outbf, float scale, hipStream_t st,
               const float *rowscale = nullptr, int64_t lds = 0, int ldo = 0) {
   if (T == 0) return LORA_OK;
-  const NTSplit sp = nt_split(T, K);
+  const NTSplit sp = nt_split(T, K, RS);
   SkinnyNTArgs a{(int)T, (int)K, (int)ksplit, sp.kchunk, Z0, Z1, ldz, E, G, side, part,
                  lds ? lds : K};
   dim3 grid((unsigned)cdiv(T, 64), (unsigned)sp.ks);
