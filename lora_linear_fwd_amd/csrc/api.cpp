@@ -53,11 +53,11 @@ inline NTSplit nt_split(int64_t T, int64_t K, int RS) {
 }
 struct TNSplit { int ts; int tchunk; };
 // Token chunks so that the grid about fills the workgroups resident at once:
-// four per CU for narrow ranks, fewer where the accumulators take the
-// register file (two per CU from 64 rank columns, one from 128)
+// four per CU for the narrowest ranks, fewer as the accumulators take more
+// of the register file (three from 32 rank columns, two from 64, one from 128)
 inline TNSplit tn_split(int64_t T, int64_t N, int RS) {
   const int64_t gx = cdiv(N, 256);
-  const int64_t slots = RS >= 128 ? 256 : (RS >= 64 ? 512 : 1024);
+  const int64_t slots = RS >= 128 ? 256 : (RS >= 64 ? 512 : (RS >= 32 ? 768 : 1024));
   int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(slots, gx), cdiv(T, 64)));
   int64_t tchunk = std::max<int64_t>(64, cdiv(cdiv(T, ts), 64) * 64);
   ts = std::max<int64_t>(1, cdiv(T, tchunk));
