@@ -46,7 +46,7 @@ int main() {
   EXPECT(lora_linear_fwd(LORA_BF16, 16, ((int64_t)1 << 20) + 8, 64, 8, 16.f, P, &W, P, P, P, P, 1 << 30, nullptr), LORA_ERR_BAD_SHAPE);
   EXPECT(lora_linear_bwd(LORA_BF16, 16, 64, 64, 8, 16.f, P, &W, P, P, nullptr, P, P, P, 0, P, 1 << 30, nullptr), LORA_ERR_NULL_POINTER);
   EXPECT(lora_linear_bwd(LORA_BF16, 16, 64, 64, 8, 16.f, P, &W, P, P, P, P, P, P, 4, P, 1 << 30, nullptr), LORA_ERR_UNSUPPORTED);
-  EXPECT(lora_linear_bwd_noalloc(LORA_BF16, 4096, 4096, 4096, 128, 16.f, P, &W, P, P, P, P, P, P, 0, nullptr), LORA_ERR_WORKSPACE);
+  EXPECT(lora_linear_bwd_noalloc(LORA_BF16, 65536, 4096, 4096, 128, 16.f, P, &W, P, P, P, P, P, P, 0, nullptr), LORA_ERR_WORKSPACE);
   EXPECT(lora_linear_bwd_noalloc(LORA_BF16, 16, 64, 64, 8, 16.f, P, &W, P, P, P, MIS, P, P, 0, nullptr), LORA_ERR_MISALIGNED);
 
   // MLP, fused norm, q/k/v

@@ -331,9 +331,9 @@ def test_noalloc_validation_before_any_hip_call():
     assert call(k=60) == 2
     assert call(r=129) == 3
     assert call(flags=2) == 3
-    big = L.workspace_bytes(L.OP_LINEAR_BWD | L.LORA_WS_MINIMAL, 1, 0, 4096, 4096, 4096, 128)
+    big = L.workspace_bytes(L.OP_LINEAR_BWD | L.LORA_WS_MINIMAL, 1, 0, 65536, 4096, 4096, 128)
     assert big > L.LORA_NOALLOC_SCRATCH_BYTES
-    assert call(T=4096, k=4096, n=4096, r=128) == 4
+    assert call(T=65536, k=4096, n=4096, r=128) == 4
 
 
 def test_fused_norm_validation_codes():

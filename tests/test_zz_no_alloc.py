@@ -50,7 +50,7 @@ def test_noalloc_matches_workspace_call_twice(dtype, q4):
 
 def test_noalloc_refuses_oversize():
     import torch
-    T, k, n, r = 4096, 4096, 4096, 128
+    T, k, n, r = 65536, 4096, 4096, 128
     need = L.workspace_bytes(L.OP_LINEAR_BWD | L.LORA_WS_MINIMAL, L.LORA_BF16, 0, T, k, n, r)
     assert need > L.LORA_NOALLOC_SCRATCH_BYTES
     p = ctypes.c_void_p(1 << 20)
