@@ -71,25 +71,28 @@ inline size_t tn_part_bytes(int64_t T, int64_t N, int RS) {
 }
 // dual pass: 256-column blocks per segment x token chunks (multiples of 64)
 struct DualSplit { int nb0, nb1, ts, tchunk; };
-inline DualSplit dual_split(int64_t T, int64_t N, int64_t nsplit) {
+// Fill the workgroups resident at once (three per CU for the 16-wide pass
+// over a stored operand, two otherwise: registers and LDS) in one round
+// rather than spill a partial second round
+inline int64_t dual_slots(int RS, bool zswiglu) { return RS <= 16 && !zswiglu ? 768 : 512; }
+inline DualSplit dual_split(int64_t T, int64_t N, int64_t nsplit, int64_t slots) {
   DualSplit d;
   d.nb0 = (int)cdiv(nsplit, 256);
   d.nb1 = (int)cdiv(N - nsplit, 256);
-  // the narrow kernels run 4 workgroups on each of the 256 CUs: fill those
-  // 1024 slots once rather than spill a partial second round
   const int64_t nbc = std::max<int64_t>(1, d.nb0 + d.nb1);
-  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(T, 64), 1024 / nbc));
+  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(T, 64), slots / nbc));
   const int64_t tchunk = std::max<int64_t>(64, cdiv(cdiv(T, ts), 64) * 64);
   d.tchunk = (int)tchunk;
   d.ts = (int)std::max<int64_t>(1, cdiv(T, tchunk));
   return d;
 }
 inline size_t dual_u_bytes(int64_t T, int64_t N, int64_t nsplit, int RS) {
-  const DualSplit d = dual_split(T, N, nsplit);
+  const DualSplit d = dual_split(T, N, nsplit, dual_slots(RS, false));
   return (size_t)(d.nb0 + d.nb1) * T * RS * 4;
 }
 inline size_t dual_v_bytes(int64_t T, int64_t N, int64_t nsplit, int RS) {
-  return (size_t)dual_split(T, N, nsplit).ts * RS * N * 4;
+  // the larger slot count of the two forms: the most token chunks
+  return (size_t)dual_split(T, N, nsplit, dual_slots(RS, false)).ts * RS * N * 4;
 }
 inline int64_t ldp_of(int64_t T) { return std::max<int64_t>(64, cdiv(T, 64) * 64); }
 
@@ -536,7 +539,7 @@ int skinny_dual(int RS, bool zswiglu, int64_t T, int64_t N, int64_t nsplit, int6
                 float *part_u, float *part_v, int64_t r, int RSout, float uscale, float *uout32,
                 bf16_t *uoutbf, float vscale, int transposed, bf16_t *vout0, bf16_t *vout1,
                 hipStream_t st, const float *urowscale = nullptr) {
-  const DualSplit sp = dual_split(T, N, nsplit);
+  const DualSplit sp = dual_split(T, N, nsplit, dual_slots(RS, zswiglu));
   DualArgs a{(int)T, (int)N, (int)nsplit, sp.tchunk, sp.nb0, ldz, Z0, Z1, E, G, S0, S1, P0, P1,
              (int)ldp_of(T), part_u, part_v};
   if (T > 0) {
