@@ -40,12 +40,16 @@ struct Bump {
 
 // split choices shared by the planner and the launchers
 struct NTSplit { int ks; int kchunk; };
+// Token block of the skinny NT kernel: from 64 rank columns on, 128 tokens in
+// eight waves, which halves the side tile's re-reads per Z byte at the same
+// per-wave registers; 64 tokens in four waves for narrower ranks.
+constexpr int nt_tb(int RS) { return RS >= 64 ? 128 : 64; }
 // K chunks so that the grid about fills the workgroups resident at once for
-// the rank width (the skinny NT kernel's occupancy falls from four
-// workgroups per CU at narrow ranks to one at the widest)
+// the rank width: four 64-token workgroups per CU below 64 rank columns, two
+// 128-token ones up to 144 and one from 160 (the accumulators' registers)
 inline NTSplit nt_split(int64_t T, int64_t K, int RS) {
-  const int64_t gx = std::max<int64_t>(1, cdiv(T, 64));
-  const int64_t slots = RS >= 208 ? 256 : (RS >= 128 ? 512 : (RS >= 80 ? 768 : 1024));
+  const int64_t gx = std::max<int64_t>(1, cdiv(T, nt_tb(RS)));
+  const int64_t slots = RS < 64 ? 1024 : (RS < 160 ? 512 : 256);
   int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(slots, gx), cdiv(K, 512)));
   int64_t kchunk = cdiv(cdiv(K, ks), 128) * 128;
   ks = std::max<int64_t>(1, cdiv(K, kchunk));
@@ -442,11 +446,13 @@ int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, cons
   const NTSplit sp = nt_split(T, K, RS);
   SkinnyNTArgs a{(int)T, (int)K, (int)ksplit, sp.kchunk, Z0, Z1, ldz, E, G, side, part,
                  lds ? lds : K};
-  dim3 grid((unsigned)cdiv(T, 64), (unsigned)sp.ks);
-#define SNT(R)                                                                          \
-  case R:                                                                               \
-    if (zswiglu) hipLaunchKernelGGL((k_skinny_nt<R, true>), grid, dim3(256), 0, st, a);  \
-    else hipLaunchKernelGGL((k_skinny_nt<R, false>), grid, dim3(256), 0, st, a);         \
+  dim3 grid((unsigned)cdiv(T, nt_tb(RS)), (unsigned)sp.ks);
+#define SNT(R)                                                                    \
+  case R:                                                                         \
+    if (zswiglu)                                                                  \
+      hipLaunchKernelGGL((k_skinny_nt<R, true, nt_tb(R)>), grid, dim3(nt_tb(R) * 4), 0, st, a); \
+    else                                                                          \
+      hipLaunchKernelGGL((k_skinny_nt<R, false, nt_tb(R)>), grid, dim3(nt_tb(R) * 4), 0, st, a); \
     break;
   switch (RS) {
     SNT(16) SNT(32) SNT(48) SNT(64) SNT(80) SNT(96) SNT(112) SNT(128)

@@ -23,21 +23,27 @@ struct SkinnyNTArgs {
   int64_t lds;
 };
 
-// Block: 64 tokens x one K chunk, stepping 128 columns at a time.  Each
-// step's Z tile (64 x 128) and SIDE tile (RS x 128) are loaded with
-// row-contiguous 16-byte lanes (a wave instruction covers 4 rows x 256 B),
-// kept in registers while the previous step's tiles are contracted from LDS,
-// then written to LDS.  Wave w contracts tokens 16 w .. 16 w + 15.
+// Block: TB tokens (64 or 128) x one K chunk, stepping 128 columns at a
+// time, TB / 16 waves.  Each step's Z tile (TB x 128) and SIDE tile
+// (RS x 128) are loaded with row-contiguous 16-byte lanes (a wave
+// instruction covers 4 rows x 256 B), kept in registers while the previous
+// step's tiles are contracted from LDS, then written to LDS.  Wave w
+// contracts tokens 16 w .. 16 w + 15, so the per-wave registers do not
+// depend on TB, while the SIDE tile, read once per block and step, costs
+// RS / TB of its bytes per Z byte.
 // LDS rows are 256 B (16 chunks of 16 B), chunk index XOR (row % 16).
-template <int RS, bool ZSWIGLU>
-__global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
+template <int RS, bool ZSWIGLU, int TB = 64>
+__global__ __launch_bounds__(TB * 4) void k_skinny_nt(const SkinnyNTArgs a) {
+  static_assert(TB == 64 || TB == 128, "64- or 128-token blocks");
+  constexpr int NTH = TB * 4;                    // threads
+  constexpr int RPI = NTH / 16;                  // rows per load round
   constexpr int NQ = RS / 16;
-  constexpr int SL = (RS * 16 + 255) / 256;   // side chunks per thread
-  __shared__ __attribute__((aligned(16))) char zs[64 * 256];
+  constexpr int SL = (RS * 16 + NTH - 1) / NTH;  // side chunks per thread
+  __shared__ __attribute__((aligned(16))) char zs[TB * 256];
   __shared__ __attribute__((aligned(16))) char ss[RS * 256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, hi16 = lane >> 4;
-  const int t0 = blockIdx.x * 64;
+  const int t0 = blockIdx.x * TB;
   const int kbeg = blockIdx.y * a.kchunk;
   const int kend = min(a.K, kbeg + a.kchunk);
   const int c = tid & 15, rb = tid >> 4;      // load chunk column, first row
@@ -50,7 +56,7 @@ __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
     const bool kin = k < kend;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + rb + 16 * i;
+      const int t = t0 + rb + RPI * i;
       u32x4 v = {0, 0, 0, 0};
       if (kin && t < a.T) {
         if constexpr (ZSWIGLU) {
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
-      const int q = rb + 16 * i;
+      const int q = rb + RPI * i;
       u32x4 v = {0, 0, 0, 0};
       if (kin && q < RS) v = gload16(a.side + (int64_t)q * a.lds + k);
       sr[i] = v;
@@ -79,10 +85,10 @@ __global__ __launch_bounds__(256) void k_skinny_nt(const SkinnyNTArgs a) {
   };
   auto store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_write16(zs, off(rb + 16 * i, c), zr[i]);
+    for (int i = 0; i < 4; ++i) lds_write16(zs, off(rb + RPI * i, c), zr[i]);
 #pragma unroll
     for (int i = 0; i < SL; ++i)
-      if (rb + 16 * i < RS) lds_write16(ss, off(rb + 16 * i, c), sr[i]);
+      if (rb + RPI * i < RS) lds_write16(ss, off(rb + RPI * i, c), sr[i]);
   };
   f32x4 acc[NQ];
 #pragma unroll
