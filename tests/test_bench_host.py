@@ -57,10 +57,10 @@ GEMS = ["k_lora_gemm_pp<1, false>", "k_lora_gemm_pp<0, false>", "k_lora_gemm_pp<
 def _step(values, q4=False):
     """One MLP step's dispatches in launch order, the GEMMs carrying `values`."""
     pre = [("k_dequant4(unsigned char const*)", 0.5)] * 2 if q4 else []
-    fwd = pre + [("k_prep(PrepBatch)", 1.0), ("k_skinny_nt<32, false>(SkinnyNTArgs)", 2.0),
+    fwd = pre + [("k_prep(PrepBatch)", 1.0), ("k_skinny_nt<32, false, 64>(SkinnyNTArgs)", 2.0),
                  ("k_reduce_side", 0.1), (GEMS[0], values[0]),
-                 ("k_skinny_nt<16, false>(SkinnyNTArgs)", 3.0), (GEMS[1], values[1])]
-    bwd = [("k_prep(PrepBatch)", 1.0), ("k_skinny_nt<16, false>(SkinnyNTArgs)", 2.0),
+                 ("k_skinny_nt<16, false, 64>(SkinnyNTArgs)", 3.0), (GEMS[1], values[1])]
+    bwd = [("k_prep(PrepBatch)", 1.0), ("k_skinny_nt<16, false, 64>(SkinnyNTArgs)", 2.0),
            (GEMS[2], values[2]), ("k_reduce_batch", 0.2), (GEMS[3], values[3]),
            ("k_reduce_tn", 0.3)]
     return fwd + bwd
@@ -122,9 +122,9 @@ def test_steps_start_at_the_forward_and_its_4bit_decodes():
 def test_steps_of_the_attention_workload_open_at_the_fused_qkv():
     """q/k/v forward (k_prep, then the rank-3r pass over X), o, MLP: one step
     per q/k/v opener; the MLP's own k_prep inside the step opens nothing."""
-    one = ["k_prep", "k_skinny_nt<192, false>", "k_reduce_side", "k_lora_gemm_pp<0, false>",
-           "k_prep", "k_skinny_nt<64, false>", "k_reduce_side", "k_lora_gemm_pp<0, false>",
-           "k_prep", "k_skinny_nt<128, false>", "k_reduce_side", "k_lora_gemm_pp<1, false>",
+    one = ["k_prep", "k_skinny_nt<192, false, 128>", "k_reduce_side", "k_lora_gemm_pp<0, false>",
+           "k_prep", "k_skinny_nt<64, false, 128>", "k_reduce_side", "k_lora_gemm_pp<0, false>",
+           "k_prep", "k_skinny_nt<128, false, 128>", "k_reduce_side", "k_lora_gemm_pp<1, false>",
            "k_reduce_tn"]
     rows = [(i, n, 0.0) for i, n in enumerate(one * 3)]
     steps = bench._steps(rows)
