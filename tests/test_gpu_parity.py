@@ -103,8 +103,9 @@ def test_linear_q4(ws):
 
 
 # one token and the narrowest features the bf16 path takes (multiples of 8):
-# every GEMM, rank-r and reduction kernel runs on a single partial tile
-TINY_LINEAR = [(1, 8, 8, 1), (1, 8, 16, 2), (3, 24, 8, 5)]
+# every GEMM, rank-r and reduction kernel runs on a single partial tile (the
+# last shape: a wide rank, whose rank-r passes take the 128-token blocks)
+TINY_LINEAR = [(1, 8, 8, 1), (1, 8, 16, 2), (3, 24, 8, 5), (2, 64, 72, 64)]
 
 
 @pytest.mark.parametrize("ws", DENSE_MODES)
@@ -238,7 +239,9 @@ def test_mlp_q4(ws):
     check_mlp(gen_mlp(70, 128, 192, 16, 16.0, "bf16", seed=25, q4=True, b_std=1.0), ws=ws)
 
 
-TINY_MLP = [(1, 8, 8, 1), (2, 16, 24, 2), (5, 8, 136, 16)]
+# the same for the MLP; the last two: wide ranks (saved h, 128-token rank-r
+# blocks; a multiple of 16 with the block-by-block passes, and one that is not)
+TINY_MLP = [(1, 8, 8, 1), (2, 16, 24, 2), (5, 8, 136, 16), (3, 16, 64, 64), (2, 8, 72, 40)]
 
 
 @pytest.mark.parametrize("ws", DENSE_MODES)
