@@ -437,15 +437,16 @@ struct Prep {
 
 // out = Z . SIDE^T over all K (deterministic split-K); fp32 and/or scaled bf16
 // side [RS x K] with row stride lds (0: K); outputs [T x RS] with row
-// stride ldo (0: RS)
+// stride ldo (0: RS); with side1, side rows >= rsplit come from side1
 int skinny_nt(int RS, bool zswiglu, int64_t T, int64_t K, const bf16_t *Z0, const bf16_t *Z1,
               int64_t ksplit, int64_t ldz, const bf16_t *E, const bf16_t *G, const bf16_t *side,
               float *part, float *out32, bf16_t *outbf, float scale, hipStream_t st,
-              const float *rowscale = nullptr, int64_t lds = 0, int ldo = 0) {
+              const float *rowscale = nullptr, int64_t lds = 0, int ldo = 0,
+              const bf16_t *side1 = nullptr, int rsplit = 0) {
   if (T == 0) return LORA_OK;
   const NTSplit sp = nt_split(T, K, RS);
   SkinnyNTArgs a{(int)T, (int)K, (int)ksplit, sp.kchunk, Z0, Z1, ldz, E, G, side, part,
-                 lds ? lds : K};
+                 lds ? lds : K, side1, side1 ? rsplit : RS};
   dim3 grid((unsigned)cdiv(T, nt_tb(RS)), (unsigned)sp.ks);
 #define SNT(R)                                                                    \
   case R:                                                                         \
@@ -963,6 +964,11 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   const bool wcopy = fast && wg.q4;   // the plan holds a weight buffer
   // H_d from the gate/up epilogue (eight-wave kernel: dense or decoded weights)
   const bool hdf = mlp_fwd_hd_fused(r) && (!wg.q4 || wcopy);
+  // r a multiple of 16 (no padding), no folded norm and the eight-wave
+  // gate/up GEMM (dense or decoded weights): every rank-r operand is an
+  // adapter as it is ([Ag; Au] as two side sources, Bg / Bu read by the gate
+  // and up rows, Ad, Bd), so no operand copies are made
+  const bool inplace = r % 16 == 0 && !nf && (!wg.q4 || wcopy);
   const MlpFwdPlan pl = plan_mlp_fwd(T, d, f, r, wcopy, hdf);
   bf16_t *wb = (bf16_t *)(w + pl.wbuf);
   if (wcopy) {   // decode Wg, Wu once, then the dense GEMM
@@ -977,12 +983,17 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   bf16_t *side_d = (bf16_t *)(w + pl.side_d), *epi_d = (bf16_t *)(w + pl.epi_d);
   bf16_t *hbf = (bf16_t *)(w + pl.hbf);
   float *hpart = (float *)(w + pl.hpart);
-  Prep prep;
-  prep.side(side_gu, RS1, d, Ag, Au, r, d, 0, nullptr, 0, nf ? nf->w : nullptr);   // [Ag; Au] (diag w)
-  prep.epi(epi_gu, 2 * f, RS1, Bg, Bu, r, f, 0);
-  prep.side(side_d, RS2, f, Ad, nullptr, r, f, 0);
-  prep.epi(epi_d, d, RS2, Bd, nullptr, r, d, 0);
-  LORA_TRY(prep.launch(st));
+  if (inplace) {
+    side_d = (bf16_t *)Ad;
+    epi_d = (bf16_t *)Bd;
+  } else {
+    Prep prep;
+    prep.side(side_gu, RS1, d, Ag, Au, r, d, 0, nullptr, 0, nf ? nf->w : nullptr);   // [Ag; Au] (diag w)
+    prep.epi(epi_gu, 2 * f, RS1, Bg, Bu, r, f, 0);
+    prep.side(side_d, RS2, f, Ad, nullptr, r, f, 0);
+    prep.epi(epi_d, d, RS2, Bd, nullptr, r, d, 0);
+    LORA_TRY(prep.launch(st));
+  }
   const bf16_t *Xb = (const bf16_t *)X;
   if (nf) {   // the rows' rstd only: the normalised rows are never formed
     hipLaunchKernelGGL(k_rmsnorm_fwd<false>, dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, X,
@@ -997,14 +1008,19 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   set_b(a, wg, wu); a.ldb = d;
   a.gu_f = (int)f;
   a.rs = RS1; a.epi = epi_gu;
+  if (inplace) { a.epi = (const bf16_t *)Bg; a.epi_u = (const bf16_t *)Bu; }
   a.E = (bf16_t *)e_saved; a.G = (bf16_t *)g_saved; a.H = h;
   if (nf) a.rowscale = nf->rstd;
   a.tiles_m = (int)cdiv(T, BM); a.tiles_n = (int)gu_tiles_n(f);
   if (hdf) { a.fr_sd = side_d; a.fr_ud = hpart; }
   if (r % 16 == 0) a.rs_seg = (int)r;   // blockdiag(Bg, Bu): gate and up rows one block each
   // [s X Ag^T | s X Au^T], once per call
-  LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
-                     hbf, s, st));
+  if (inplace)
+    LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, (const bf16_t *)Ag, hpart,
+                       nullptr, hbf, s, st, nullptr, d, 0, (const bf16_t *)Au, (int)r));
+  else
+    LORA_TRY(skinny_nt(RS1, false, T, d, Xb, Xb, d, d, nullptr, nullptr, side_gu, hpart, nullptr,
+                       hbf, s, st));
   a.hglob = hbf;
   LORA_TRY(run_gemm(KC_GATEUP_FWD, false, wg.q4, nf ? EPI_SWIGLU_FWD_NORM : EPI_SWIGLU_FWD, a, st));
   if (hdf) {   // s H_d in bf16: the epilogue's partials summed over the tiles in a fixed order

@@ -21,6 +21,10 @@ struct SkinnyNTArgs {
   const bf16_t *side;       // [RS x K], row stride lds (>= K)
   float *part;              // [KS x T x RS]
   int64_t lds;
+  // SIDE rows q >= rsplit come from side1 row q - rsplit (same stride): the
+  // two adapters of a gate/up pair read in place
+  const bf16_t *side1;
+  int rsplit;
 };
 
 // Block: TB tokens (64 or 128) x one K chunk, stepping 128 columns at a
@@ -79,7 +83,9 @@ __global__ __launch_bounds__(TB * 4) void k_skinny_nt(const SkinnyNTArgs a) {
     for (int i = 0; i < SL; ++i) {
       const int q = rb + RPI * i;
       u32x4 v = {0, 0, 0, 0};
-      if (kin && q < RS) v = gload16(a.side + (int64_t)q * a.lds + k);
+      if (kin && q < RS)
+        v = gload16(q < a.rsplit ? a.side + (int64_t)q * a.lds + k
+                                 : a.side1 + (int64_t)(q - a.rsplit) * a.lds + k);
       sr[i] = v;
     }
   };

@@ -97,6 +97,10 @@ struct GemmArgs {
   const bf16_t *hglob;          // s * (A_op SIDE^T), [M x rs] bf16
   int rs;                       // rank padded to a multiple of 16
   const bf16_t *epi;            // [rows x rs] bf16 epilogue LoRA operand
+  // eight-wave SwiGLU forward with rs_seg > 0: when set, the gate rows read
+  // epi as Bg [gu_f x rs_seg] and the up rows read epi_u as Bu [gu_f x rs_seg]
+  // (the adapters in place, not the interleaved copy)
+  const bf16_t *epi_u;
   int accumulate;               // EPI_STORE: C += result
   bf16_t *C;
   int64_t ldc;

@@ -497,19 +497,20 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       const bool qok = kq < kqe;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        int64_t erow;
+        const bf16_t *src;
         bool ok;
         if constexpr (GU) {
           const int j = tn * 128 + wn * 32 + l32;
           ok = j < p.gu_f;
-          erow = (i ? p.gu_f : 0) + j;
+          src = p.epi_u ? (i ? p.epi_u : p.epi) + (int64_t)j * p.rs_seg + (kq - (i ? kqs : 0)) * 16
+                        : p.epi + (int64_t)((i ? p.gu_f : 0) + j) * rs + kq * 16;
         } else {
           const int n = n0 + wn * 64 + i * 32 + l32;
           ok = n < N;
-          erow = n;
+          src = p.epi + (int64_t)n * rs + kq * 16;
         }
         u32x4 v = {0, 0, 0, 0};
-        if (ok && qok && gu_takes(i, kq)) v = gload16(p.epi + erow * rs + kq * 16 + 8 * hi32);
+        if (ok && qok && gu_takes(i, kq)) v = gload16(src + 8 * hi32);
         ea[h][i] = v;
       }
 #pragma unroll
