@@ -783,10 +783,15 @@ int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
     LORA_TRY(decode_w(wb, wv, n, k, st));
     wv = dense_view(wb);
   }
-  Prep prep;
-  prep.side(side, RS, k, A, nullptr, r, k, 0);
-  prep.epi(epi, n, RS, B, nullptr, r, n, 0);
-  LORA_TRY(prep.launch(st));
+  if (RS == r) {   // no padding: the side pass and the epilogue read A and B as they are
+    side = (bf16_t *)A;
+    epi = (bf16_t *)B;
+  } else {
+    Prep prep;
+    prep.side(side, RS, k, A, nullptr, r, k, 0);
+    prep.epi(epi, n, RS, B, nullptr, r, n, 0);
+    LORA_TRY(prep.launch(st));
+  }
   GemmArgs a = gemm_base();
   a.M = (int)T; a.N = (int)n; a.K = (int)k; a.ksplit = (int)k;
   a.A0 = a.A1 = (const bf16_t *)X; a.lda = k;
