@@ -97,19 +97,26 @@ PROFILED_STEPS = range(1, 5)
 
 
 def _step_starts(names):
-    """Index of each step's first dispatch: the forward opens with k_prep
-    followed by the rank-r pass over X (width 2r = 32 for the MLP workloads,
-    3r = 192 for the attention workload's fused q/k/v) or by the norm's rstd
-    pass, after the 4-bit decodes of the gate and up weights when it has
-    them."""
+    """Index of each step's first dispatch.  The forward opens with the
+    rank-r pass over X (width 2r = 32 for the MLP workloads, 3r = 192 for the
+    attention workload's fused q/k/v) or the norm's rstd pass, preceded by
+    the operand copies (k_prep) where the call makes them, and by the 4-bit
+    decodes of the gate and up weights when it has them.  (In the MLP
+    backward the 32-wide pass over X follows a reduction, never k_prep.)"""
     out = []
     for i in range(len(names) - 1):
-        if "k_prep" in names[i] and ("k_skinny_nt<32" in names[i + 1]
-                                     or "k_skinny_nt<192" in names[i + 1]
-                                     or "k_rmsnorm_fwd" in names[i + 1]):
-            while i > 0 and "k_dequant4(" in names[i - 1]:
-                i -= 1
-            out.append(i)
+        opener = ("k_skinny_nt<32" in names[i + 1] or "k_skinny_nt<192" in names[i + 1]
+                  or "k_rmsnorm_fwd" in names[i + 1])
+        if "k_prep" in names[i] and opener:
+            j = i
+        elif ("k_skinny_nt<32" in names[i] and (i == 0 or not any(
+                k in names[i - 1] for k in ("k_reduce_side", "k_prep")))):
+            j = i
+        else:
+            continue
+        while j > 0 and "k_dequant4(" in names[j - 1]:
+            j -= 1
+        out.append(j)
     return out
 
 

@@ -54,15 +54,19 @@ GEMS = ["k_lora_gemm_pp<1, false>", "k_lora_gemm_pp<0, false>", "k_lora_gemm_pp<
         "k_lora_gemm_pp<0, false>"]
 
 
-def _step(values, q4=False):
-    """One MLP step's dispatches in launch order, the GEMMs carrying `values`."""
+def _step(values, q4=False, prep=False):
+    """One MLP step's dispatches in launch order, the GEMMs carrying `values`.
+    prep: the forward makes operand copies first (padded ranks, folded norm);
+    at r = 16 it reads the adapters in place and opens with the pass over X."""
     pre = [("k_dequant4(unsigned char const*)", 0.5)] * 2 if q4 else []
-    fwd = pre + [("k_prep(PrepBatch)", 1.0), ("k_skinny_nt<32, false, 64>(SkinnyNTArgs)", 2.0),
-                 ("k_reduce_side", 0.1), (GEMS[0], values[0]),
-                 ("k_skinny_nt<16, false, 64>(SkinnyNTArgs)", 3.0), (GEMS[1], values[1])]
+    pre += [("k_prep(PrepBatch)", 1.0)] if prep else []
+    fwd = pre + [("k_skinny_nt<32, false, 64>(SkinnyNTArgs)", 2.0),
+                 ("k_reduce_side", 0.1), (GEMS[0], values[0]), ("k_reduce_dual_u", 0.1),
+                 (GEMS[1], values[1])]
     bwd = [("k_prep(PrepBatch)", 1.0), ("k_skinny_nt<16, false, 64>(SkinnyNTArgs)", 2.0),
-           (GEMS[2], values[2]), ("k_reduce_batch", 0.2), (GEMS[3], values[3]),
-           ("k_reduce_tn", 0.3)]
+           ("k_reduce_side", 0.1), ("k_skinny_nt<32, false, 64>(SkinnyNTArgs)", 2.0),
+           ("k_reduce_side", 0.1), (GEMS[2], values[2]), ("k_reduce_batch", 0.2),
+           (GEMS[3], values[3]), ("k_reduce_tn", 0.3)]
     return fwd + bwd
 
 
@@ -109,14 +113,26 @@ def test_summary_scales_by_the_copy_and_reads_back(tmp_path, monkeypatch):
     assert bench.stored_traffic(3, name) is None
 
 
-def test_steps_start_at_the_forward_and_its_4bit_decodes():
+@pytest.mark.parametrize("prep", [False, True], ids=["in-place", "prep"])
+def test_steps_start_at_the_forward_and_its_4bit_decodes(prep):
     rows = [(i, n, 0.0) for i, (n, _) in enumerate(
-        [("k_reduce_tn", 0)] + _step([1] * 4, q4=True) + _step([1] * 4, q4=True))]
+        [("k_reduce_tn", 0)] + _step([1] * 4, q4=True, prep=prep)
+        + _step([1] * 4, q4=True, prep=prep))]
     steps = bench._steps(rows)
     assert len(steps) == 2
     for st in steps:
-        assert "k_dequant4(" in st[0][1] and "k_prep" in st[2][1]
-        assert len(st) == len(_step([1] * 4, q4=True))
+        assert "k_dequant4(" in st[0][1] and "k_dequant4(" in st[1][1]
+        assert ("k_prep" in st[2][1]) == prep
+        assert len(st) == len(_step([1] * 4, q4=True, prep=prep))
+
+
+@pytest.mark.parametrize("prep", [False, True], ids=["in-place", "prep"])
+def test_steps_of_a_dense_mlp_skip_the_backward_pass_over_x(prep):
+    """The backward's 32-wide pass over X follows a reduction: no step opens
+    there, with or without the forward's operand copies."""
+    seq = sum((_step([1] * 4, prep=prep) for _ in range(3)), [])
+    starts = bench._step_starts([n for n, _ in seq])
+    assert starts == [i * len(_step([1] * 4, prep=prep)) for i in range(3)]
 
 
 def test_steps_of_the_attention_workload_open_at_the_fused_qkv():
