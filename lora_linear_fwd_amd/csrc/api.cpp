@@ -777,19 +777,20 @@ int lora_linear_fwd(int dtype, int64_t T, int64_t k, int64_t n, int64_t r, float
 
   const LinFwdPlan pl = plan_lin_fwd(T, k, n, r, fast && wv.q4);
   const int RS = rs_of(r);
-  bf16_t *side = (bf16_t *)(w + pl.side), *epi = (bf16_t *)(w + pl.epi);
+  bf16_t *side_c = (bf16_t *)(w + pl.side), *epi_c = (bf16_t *)(w + pl.epi);
+  // no padding: the side pass and the epilogue read A and B as they are
+  const bool inplace = RS == r;
+  const bf16_t *side = inplace ? (const bf16_t *)A : side_c;
+  const bf16_t *epi = inplace ? (const bf16_t *)B : epi_c;
   if (fast && wv.q4) {   // decode once, then the dense GEMM
     bf16_t *wb = (bf16_t *)(w + pl.wbuf);
     LORA_TRY(decode_w(wb, wv, n, k, st));
     wv = dense_view(wb);
   }
-  if (RS == r) {   // no padding: the side pass and the epilogue read A and B as they are
-    side = (bf16_t *)A;
-    epi = (bf16_t *)B;
-  } else {
+  if (!inplace) {
     Prep prep;
-    prep.side(side, RS, k, A, nullptr, r, k, 0);
-    prep.epi(epi, n, RS, B, nullptr, r, n, 0);
+    prep.side(side_c, RS, k, A, nullptr, r, k, 0);
+    prep.epi(epi_c, n, RS, B, nullptr, r, n, 0);
     LORA_TRY(prep.launch(st));
   }
   GemmArgs a = gemm_base();
@@ -985,18 +986,18 @@ static int mlp_fwd_impl(int dtype, int64_t T, int64_t d, int64_t f, int64_t r, f
   const int RS1 = rs_of(2 * r), RS2 = rs_of(r);
   bf16_t *h = (bf16_t *)(w + pl.h);
   bf16_t *side_gu = (bf16_t *)(w + pl.side_gu), *epi_gu = (bf16_t *)(w + pl.epi_gu);
-  bf16_t *side_d = (bf16_t *)(w + pl.side_d), *epi_d = (bf16_t *)(w + pl.epi_d);
+  bf16_t *side_dc = (bf16_t *)(w + pl.side_d), *epi_dc = (bf16_t *)(w + pl.epi_d);
+  // the down projection's rank-r operands: the copies, or Ad and Bd as they are
+  const bf16_t *side_d = inplace ? (const bf16_t *)Ad : side_dc;
+  const bf16_t *epi_d = inplace ? (const bf16_t *)Bd : epi_dc;
   bf16_t *hbf = (bf16_t *)(w + pl.hbf);
   float *hpart = (float *)(w + pl.hpart);
-  if (inplace) {
-    side_d = (bf16_t *)Ad;
-    epi_d = (bf16_t *)Bd;
-  } else {
+  if (!inplace) {
     Prep prep;
     prep.side(side_gu, RS1, d, Ag, Au, r, d, 0, nullptr, 0, nf ? nf->w : nullptr);   // [Ag; Au] (diag w)
     prep.epi(epi_gu, 2 * f, RS1, Bg, Bu, r, f, 0);
-    prep.side(side_d, RS2, f, Ad, nullptr, r, f, 0);
-    prep.epi(epi_d, d, RS2, Bd, nullptr, r, d, 0);
+    prep.side(side_dc, RS2, f, Ad, nullptr, r, f, 0);
+    prep.epi(epi_dc, d, RS2, Bd, nullptr, r, d, 0);
     LORA_TRY(prep.launch(st));
   }
   const bf16_t *Xb = (const bf16_t *)X;
