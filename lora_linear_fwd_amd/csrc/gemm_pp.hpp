@@ -478,7 +478,8 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
   // With rs_seg (rank blocks of whole 16-column groups) the epilogue operand
   // is block-diagonal.  Fused q/k/v: a tile's columns lie in one projection,
   // whose rows of it are zero outside that projection's block.  Gate/up: the
-  // gate rows (i = 0) are zero outside block 0, the up rows outside block 1.
+  // gate rows (i = 0) are zero outside block 0, the up rows outside block 1
+  // (with epi_u the two blocks are Bg and Bu as they are).
   const int rs = p.rs;
   int kqb = 0, kqe = rs / 16;
   const int kqs = GU ? p.rs_seg / 16 : 0;   // gate/up: first column group of block 1
