@@ -50,7 +50,9 @@ constexpr int nt_tb(int RS) { return RS >= 64 ? 128 : 64; }
 inline NTSplit nt_split(int64_t T, int64_t K, int RS) {
   const int64_t gx = std::max<int64_t>(1, cdiv(T, nt_tb(RS)));
   const int64_t slots = RS < 64 ? 1024 : (RS < 160 ? 512 : 256);
-  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(slots, gx), cdiv(K, 512)));
+  // at most one round of resident workgroups: a second round that holds a
+  // few workgroups would take as long as the first
+  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(slots / gx, cdiv(K, 512)));
   int64_t kchunk = cdiv(cdiv(K, ks), 128) * 128;
   ks = std::max<int64_t>(1, cdiv(K, kchunk));
   return {(int)ks, (int)kchunk};
@@ -62,7 +64,8 @@ struct TNSplit { int ts; int tchunk; };
 inline TNSplit tn_split(int64_t T, int64_t N, int RS) {
   const int64_t gx = cdiv(N, 256);
   const int64_t slots = RS >= 128 ? 256 : (RS >= 64 ? 512 : (RS >= 32 ? 768 : 1024));
-  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(cdiv(slots, gx), cdiv(T, 64)));
+  // at most one round of resident workgroups (as for the NT split)
+  int64_t ts = std::max<int64_t>(1, std::min<int64_t>(slots / gx, cdiv(T, 64)));
   int64_t tchunk = std::max<int64_t>(64, cdiv(cdiv(T, ts), 64) * 64);
   ts = std::max<int64_t>(1, cdiv(T, tchunk));
   return {(int)ts, (int)tchunk};
