@@ -73,8 +73,14 @@ __global__ __launch_bounds__(TB * 4) void k_skinny_nt(const SkinnyNTArgs a) {
                                e1 * sigmoidf_fast(e1) * bf16hi(g[w]));
           }
         } else {
-          v = gload16(k < a.ksplit ? a.Z0 + (int64_t)t * a.ldz + k
-                                   : a.Z1 + (int64_t)t * a.ldz + (k - a.ksplit));
+          // wide ranks stream Z past the caches (a wide pass reads it once,
+          // and at the attention workload's [T x f] operands this took the
+          // forward's pass over h from 152 to 115 us); narrow ranks keep the
+          // cached load, whose operands (X, dY) are read again later
+          const bf16_t *src = k < a.ksplit ? a.Z0 + (int64_t)t * a.ldz + k
+                                           : a.Z1 + (int64_t)t * a.ldz + (k - a.ksplit);
+          if constexpr (RS >= 64) v = gload16_nt(src);
+          else v = gload16(src);
         }
       }
       zr[i] = v;
