@@ -605,13 +605,13 @@ def bench_attn_mlp(args):
     Xm, dYm = up(mi.X), up(mi.dY)
     del inp, att, mi
     # frozen dense weights keep a transposed copy made once (as for the MLP
-    # workload), so the backward dX GEMMs run over W^T; the fused q/k/v
-    # backward stacks its own transposed copy per call and takes W as stored
+    # workload), so the backward dX GEMMs run over W^T (the fused q/k/v
+    # backward reads the three as the K sources of one GEMM)
     keep_wt = not args.weights_as_stored
     Wqkv = {p: Wa[p] for p in ("q", "k", "v")}   # as stored, for the folded-norm timing
     if keep_wt:
         Wm = {p: L.with_transpose(v) for p, v in Wm.items()}
-        for p in (("o", "q", "k", "v") if args.qkv_separate else ("o",)):
+        for p in ("o", "q", "k", "v"):
             Wa[p] = L.with_transpose(Wa[p])
     stream = torch.cuda.current_stream()
     qkv = ("q", "k", "v")

@@ -624,7 +624,11 @@ int run_gemm(int kc, bool nn, bool q4, int epi, const GemmArgs &a, hipStream_t s
   // (A1 - A0) - ksplit elements; every caller lays the two out as column
   // ranges of one matrix, so that offset is 0.  Anything else could reach
   // past the descriptor's 2^31-byte range: refuse it.
-  if (!(a.A1 - a.A0 == a.ksplit || (a.A1 == a.A0 && a.ksplit >= a.K))) return LORA_ERR_BAD_SHAPE;
+  // (The three-source form addresses each source through its own descriptor.)
+  const bool mk = a.mk_a[0] != nullptr;
+  if (mk ? (nn || q4 || epi != EPI_STORE || a.mk_kb[0] != 0 || a.mk_kb[3] != a.K)
+         : !(a.A1 - a.A0 == a.ksplit || (a.A1 == a.A0 && a.ksplit >= a.K)))
+    return LORA_ERR_BAD_SHAPE;
 #ifdef LORA_TIMING_HOOKS
   const TimerSlot ts = t_timer[kc];
   t_timer[kc] = TimerSlot{};
@@ -633,7 +637,9 @@ int run_gemm(int kc, bool nn, bool q4, int epi, const GemmArgs &a, hipStream_t s
   hipError_t e;
   // 4-bit operands with double-quantised constants carry their 8-bit codes
   const bool dq = q4 && a.D0 != nullptr;
-  if (!nn)
+  if (mk)
+    e = launch_gemm_nt_mk(a, st);
+  else if (!nn)
     e = !q4 ? launch_gemm_nt(epi, a, st) : dq ? launch_gemm_nt_q4dq(epi, a, st)
                                               : launch_gemm_nt_q4(epi, a, st);
   else
@@ -1547,9 +1553,12 @@ static int qkv_bwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t 
   prep.side(side_nt, RS3, k, Aq, Ak, r, k, 0, Av, k, nw);
   LORA_TRY(prep.launch(st));
   if (T > 0) {
-    // [dQ | dK | dV] as one [T x N] operand (for the dX GEMM, and for the
-    // rank passes unless they run block by block)
-    if (dX || !seg) {
+    // the dX GEMM reads dQ, dK, dV and the three W^T as three K sources when
+    // the projection widths are multiples of the K step
+    const bool mk = nq % 64 == 0 && nkv % 64 == 0;
+    // [dQ | dK | dV] as one [T x N] operand (for the dX GEMM over one K source,
+    // and for the rank passes unless they run block by block)
+    if ((dX && !mk) || !seg) {
       hipLaunchKernelGGL(k_concat3, dim3(blocks_for(T * (N / 8))), dim3(256), 0, st,
                          (const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV, (int)nq,
                          (int)nkv, (int)nkv, T, dyc);
@@ -1567,15 +1576,32 @@ static int qkv_bwd_fused(int64_t T, int64_t k, int64_t nq, int64_t nkv, int64_t 
                          gbf, s, st, rstd));
     }
     if (dX) {
-      // dX (+)= [dQ | dK | dV] [Wq; Wk; Wv] + s G [Aq; Ak; Av]: one GEMM, K = N
-      LORA_TRY(transpose_w(wt, N, wq, nq, k, st));
-      LORA_TRY(transpose_w(wt + nq, N, wk, nkv, k, st));
-      LORA_TRY(transpose_w(wt + nq + nkv, N, wv, nkv, k, st));
+      // dX (+)= [dQ | dK | dV] [Wq; Wk; Wv] + s G [Aq; Ak; Av]: one GEMM, K = N,
+      // over the three W^T (the caller's, else transposed here, stacked)
+      const bool kept = mk && wq.wt && wk.wt && wv.wt;
+      if (!kept) {
+        LORA_TRY(transpose_w(wt, N, wq, nq, k, st));
+        LORA_TRY(transpose_w(wt + nq, N, wk, nkv, k, st));
+        LORA_TRY(transpose_w(wt + nq + nkv, N, wv, nkv, k, st));
+      }
       GemmArgs a = gemm_base();
       a.M = (int)T; a.N = (int)k; a.K = (int)N; a.ksplit = (int)N;
-      a.A0 = a.A1 = dyc; a.lda = N;
-      const WeightView tv = dense_view(wt);
-      set_b(a, tv, tv); a.ldb = N;
+      if (mk) {
+        const bf16_t *gs[3] = {(const bf16_t *)dQ, (const bf16_t *)dK, (const bf16_t *)dV};
+        const bf16_t *ws3[3] = {wq.wt, wk.wt, wv.wt};
+        for (int j = 0; j < 3; ++j) {
+          a.mk_a[j] = gs[j];
+          a.mk_lda[j] = sn[j];
+          a.mk_b[j] = kept ? ws3[j] : wt + sc[j];
+          a.mk_ldb[j] = kept ? sn[j] : N;
+          a.mk_kb[j] = (int)sc[j];
+        }
+        a.mk_kb[3] = (int)N;
+      } else {
+        a.A0 = a.A1 = dyc; a.lda = N;
+        const WeightView tv = dense_view(wt);
+        set_b(a, tv, tv); a.ldb = N;
+      }
       a.rs = RS3; a.epi = epi_nn; a.hglob = gbf;
       // folded norm: the GEMM gives gn, the gradient with respect to X rstd
       bf16_t *gn = nf ? (bf16_t *)(w + pl.gn) : (bf16_t *)dX;

@@ -35,6 +35,7 @@ inline hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_nt(int epi, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_nt_mk(const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nt_q4(int epi, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nn(int epi, const GemmArgs &a, hipStream_t st);
 hipError_t launch_gemm_nn_q4(int epi, const GemmArgs &a, hipStream_t st);

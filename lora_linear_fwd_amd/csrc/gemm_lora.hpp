@@ -141,6 +141,16 @@ struct GemmArgs {
   // nullptr: one source
   const bf16_t *Bk1;
   int kbsplit;
+  // eight-wave NT store form with three K sources for both operands (the
+  // fused q/k/v backward's dX read from dQ, dK, dV and Wq^T, Wk^T, Wv^T in
+  // place): K columns [mk_kb[j], mk_kb[j + 1]) of the token operand come from
+  // mk_a[j] (row stride mk_lda[j]) and of the weight operand from mk_b[j]
+  // (row stride mk_ldb[j]); mk_kb[0] = 0, mk_kb[3] = K, every boundary a
+  // multiple of the K step (64).  Launched as its own instance; A0, B0, ...
+  // are not read then.
+  const bf16_t *mk_a[3], *mk_b[3];
+  int64_t mk_lda[3], mk_ldb[3];
+  int mk_kb[4];
   // EPI_SWIGLU_BWD_RANK: with h = silu(e) g, de, dg as stored, per tile
   //   fr_ud[tn][t][q]       += sum_n h[t][n] Ad[q][n]          (H_d = h Ad^T)
   //   fr_ugu[tn][t][q]      += sum_n de[t][n] Bg[n][q], and at block

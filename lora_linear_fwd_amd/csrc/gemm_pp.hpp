@@ -57,11 +57,12 @@ __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int EPI, bool NN = false>
+template <int EPI, bool NN = false, bool MK = false>
 __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool GU = (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_FWD_NORM);
   static_assert(!(NN && GU), "the gate/up forward reads its weights K-contiguous");
+  static_assert(!MK || (EPI == EPI_STORE && !NN), "three K sources: the NT store form only");
   constexpr int BK = 64, XS = BM * BK * 2, WS = BN * BK * 2;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -298,6 +299,17 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
         p.Bk1 ? (const char *)(p.Bk1 + (int64_t)n0 * p.ldb) - 2 * (int64_t)p.kbsplit : nullptr;
     const uint32_t bstep32 = (uint32_t)(32 * p.ldb * 2);
     const int nk = (K + BK - 1) / BK;
+    // three K sources (MK): the step's source j, whose K columns start at
+    // mk_kb[j]; a step lies in one source (the boundaries are multiples of
+    // BK).  Base, row stride and first column are picked with uniform selects;
+    // the lane's offset is one 24-bit multiply-add (rows < 256, strides < 2^20).
+    struct MkSrc { const bf16_t *base; uint32_t ld; int kb; };
+    auto mk_src = [&](int k0, const bf16_t *const *b3, const int64_t *ld3) -> MkSrc {
+      const bool s2 = k0 >= p.mk_kb[2], s1 = k0 >= p.mk_kb[1];
+      return {s2 ? b3[2] : (s1 ? b3[1] : b3[0]),
+              (uint32_t)(s2 ? ld3[2] : (s1 ? ld3[1] : ld3[0])),
+              s2 ? p.mk_kb[2] : (s1 ? p.mk_kb[1] : 0)};
+    };
     // A tile of K step kt (< nk) into A stage sa (group 0): 8 loads per wave;
     // lanes past M or K read zeros.  No load is issued for steps past the end.
     auto dma_a = [&](int kt, int sa) {
@@ -305,11 +317,23 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       const int k0 = kt * BK;
       const int col = k0 + kcol;
       const bool kin = col < K;
-      const uint32_t ka = 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u);
+      if constexpr (MK) {
+        const MkSrc sj = mk_src(k0, p.mk_a, p.mk_lda);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sj.base + (int64_t)m0 * sj.ld, kMaxRecords);
+        const uint32_t base = (uint32_t)(2 * r0) * sj.ld + (uint32_t)(cA * 16) + 2u * (uint32_t)(k0 - sj.kb);
+        const uint32_t step = 64u * sj.ld;
   #pragma unroll
-      for (int u = 0; u < NI; ++u) {
-        const bool ok = kin && 32 * u < arem;
-        dma16(rsA, Xs + (w4 + 4 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
+        for (int u = 0; u < NI; ++u) {
+          const bool ok = kin && 32 * u < arem;
+          dma16(rs, Xs + (w4 + 4 * u) * 1024, ok ? base + (uint32_t)u * step : kOOB, 0);
+        }
+      } else {
+        const uint32_t ka = 2u * (uint32_t)k0 + (col >= ksplit ? dA1 : 0u);
+  #pragma unroll
+        for (int u = 0; u < NI; ++u) {
+          const bool ok = kin && 32 * u < arem;
+          dma16(rsA, Xs + (w4 + 4 * u) * 1024, ok ? aoff0 + (uint32_t)u * astep + ka : kOOB, 0);
+        }
       }
     };
     // B tile of K step kt (< nk) into B stage sb (group 1): 8 loads per wave
@@ -318,6 +342,18 @@ __global__ __launch_bounds__(PP_THREADS, 1) void k_lora_gemm_pp(const GemmArgs p
       const int k0 = kt * BK;
       const int col = k0 + kcol;
       const bool kin = col < K;
+      if constexpr (MK) {
+        const MkSrc sj = mk_src(k0, p.mk_b, p.mk_ldb);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sj.base + (int64_t)n0 * sj.ld, kMaxRecords);
+        const uint32_t base = (uint32_t)(2 * r0) * sj.ld + (uint32_t)(cA * 16) + 2u * (uint32_t)(k0 - sj.kb);
+        const uint32_t step = 64u * sj.ld;
+  #pragma unroll
+        for (int u = 0; u < NI; ++u) {
+          const bool ok = kin && 32 * u < brem;
+          dma16(rs, Ws + (w4 + 4 * u) * 1024, ok ? base + (uint32_t)u * step : kOOB, 0);
+        }
+        return;
+      }
       // the whole step lies in one K source (kbsplit % BK == 0)
       __amdgpu_buffer_rsrc_t rsK = rsB;
       if (!GU && bk1base != nullptr && k0 >= p.kbsplit) rsK = make_rsrc(bk1base, kMaxRecords);

@@ -1,7 +1,10 @@
 """GPU parity of the fused q/k/v LoRA projections (lora_qkv_fwd / _bwd)
 against the float64 oracle applied to each projection: the fused GEMM path
-(bf16, nq and nkv multiples of 256, 3r <= 256), the packed-dY backward, and
-the per-projection paths (other shapes, large r, fp32, minimal workspace)."""
+(bf16, nq and nkv multiples of 256, 3r <= 256), whose backward dX GEMM reads
+dQ, dK, dV and the three W^T (the caller's, or transposed per call) as three
+K sources where the widths are multiples of 64 and a packed [dQ | dK | dV]
+otherwise, and the per-projection paths (other shapes, large r, fp32,
+minimal workspace)."""
 import numpy as np
 import pytest
 
@@ -32,6 +35,8 @@ def run_and_check(lis, ws="fast", accumulate=False):
         W[p], Wref[p] = linear_weight(li)
         A[p], B[p], dY[p] = dev(li.A, dt), dev(li.B, dt), dev(li.dY, dt)
     mw = ws == "minimal"
+    if ws == "wt":   # caller-kept transposes next to the dense weights
+        W = {p: L.with_transpose(w) for p, w in W.items()}
     out = L.lora_qkv_fwd(X, W, A, B, li0.alpha, minimal_workspace=mw)
     dX0 = None
     if accumulate:
@@ -53,7 +58,7 @@ def run_and_check(lis, ws="fast", accumulate=False):
     check("dX", host(g["dX"]), dX_ref, dt)
 
 
-@pytest.mark.parametrize("ws", ["fast", "minimal"])
+@pytest.mark.parametrize("ws", ["fast", "minimal", "wt"])
 @pytest.mark.parametrize("shape", [(300, 320, 512, 256, 16), (130, 256, 256, 256, 64),
                                    (37, 72, 264, 136, 3), (70, 128, 256, 256, 100)],
                          ids=lambda s: "x".join(map(str, s)))
